@@ -1,0 +1,334 @@
+/*
+ * ce_oracle.c -- plain, slow, FP64 CPU oracle for fused (vocabulary-parallel)
+ * cross-entropy over language-model logits.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the yardstick that the GPU library is
+ * measured against.  Only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark may load it; the product path never does.  It shares no
+ * code, header, table or helper with the HIP library.
+ *
+ * What it computes (plain definitions, FP64 accumulation, rows one by one):
+ *
+ *   Cross-entropy of row i with target t_i over V classes, label smoothing a:
+ *     softmax_ij = exp(x_ij) / sum_k exp(x_ik)
+ *     q_ij       = a/V + (1 - a) [j == t_i]      (smoothed target distribution)
+ *     loss_i     = - sum_j q_ij log softmax_ij
+ *   The fused method rests on log softmax_ij = x_ij - lse_i with
+ *   lse_i = log sum_k exp(x_ik), so no N x V intermediate is needed
+ *   ("CANN ops-nn CE fusion" page, section "fusion scheme: log_softmax + NLL").
+ *   lse is evaluated with the row maximum taken out first, the standard guard
+ *   against exp overflow (same page, "pitfall 1: exp overflow").
+ *   The smoothing convention is the uniform a/V one of torch's
+ *   F.cross_entropy, which the TransformerEngineNPU issue #29 page names as the
+ *   precision baseline (section 4); the page's ops-nn listing spreads a over
+ *   the V-1 non-target classes instead -- that variant is not computed here.
+ *
+ *   Rows whose target equals ignore_idx have loss 0 and gradient 0
+ *   (ops-nn page, both kernels; default ignore_idx -100 per issue #29 section 1
+ *   and the hyper-parallel issue #269 section 3.1).
+ *
+ *   Gradient (ops-nn page, section "backward"; smoothing correction from its
+ *   "pitfall 3", read with the uniform a/V convention):
+ *     grad_ij = s_i (softmax_ij - q_ij)
+ *   with s_i = g_i (per-row upstream gradient) when the loss is not reduced,
+ *   and s_i = g / n when reduce_loss asks for the mean over the n rows whose
+ *   target is not ignored (issue #29 section 1 "reduce_loss"; section 7 counts
+ *   n_non_ignore).
+ *
+ *   Vocabulary shards (hyper-parallel issue #269, section 3.1: forward is a
+ *   MAX all-reduce, a SUM all-reduce and a gather of the target logit;
+ *   issue #29 section 6 gathers the per-rank (m, d, X_y) triple):
+ *     shard k holds global columns [o_k, o_k + V_k)
+ *     m_k = max_j x_j,  d_k = sum_j exp(x_j - m_k),
+ *     y_k = x[t - o_k] if o_k <= t < o_k + V_k else 0,  r_k = sum_j x_j
+ *     M = max_k m_k,  D = sum_k d_k exp(m_k - M),  lse = M + log D,
+ *     x_t = sum_k y_k,  R = sum_k r_k,
+ *     loss = lse - (1 - a) x_t - (a / V) R
+ *   The last line is the expanded form of -sum_j q_j (x_j - lse); the row sum
+ *   r_k is the extra statistic that a > 0 needs.
+ *
+ * Inputs are read as the exact stored bits: BF16 is widened to FP32 by a
+ * 16-bit shift and then to double, FP32 is widened to double.  Logical row
+ * r = i0 * d1 + i1 lives at element offset i0 * s0 + i1 * s1; columns are
+ * contiguous.  Targets are int64 at i0 * ts0 + i1 * ts1.
+ *
+ * Every function returns 0 on success and a negative code on bad input:
+ *   -1  a non-ignored target outside [0, V)
+ *   -2  bad argument (sizes, dtype, NULL)
+ *
+ * Pins (tests/test_oracle_pins.py): decimal brute force of the unfused
+ * softmax -> log -> NLL chain, the closed form loss = ln V for uniform logits
+ * and the ops-nn page's worked lse value, torch's float64 F.cross_entropy and
+ * its autograd gradient, central finite differences, shift invariance,
+ * gradient rows summing to zero, and sharded == unsharded.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+
+#define OR_EBADTARGET (-1)
+#define OR_EINVAL (-2)
+
+typedef struct or_logits {
+  const void* data;
+  int32_t dtype;       /* OR_F32 or OR_BF16 */
+  int32_t pad_;
+  int64_t d0, d1;      /* logical leading dims; rows = d0 * d1 */
+  int64_t s0, s1;      /* element strides of the two leading dims */
+  int64_t v_local;     /* columns present in this buffer */
+  int64_t vocab_start; /* global index of local column 0 */
+  int64_t vocab_total; /* global vocabulary size V */
+} or_logits;
+
+typedef struct or_targets {
+  const int64_t* data;
+  int64_t s0, s1;
+} or_targets;
+
+/* Exact widening of one stored logit to double. */
+static double or_elem(const or_logits* x, int64_t off) {
+  if (x->dtype == OR_F32) return (double)((const float*)x->data)[off];
+  uint32_t bits = (uint32_t)((const uint16_t*)x->data)[off] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static int64_t or_row_offset(const or_logits* x, int64_t r) {
+  int64_t i0 = r / x->d1, i1 = r % x->d1;
+  return i0 * x->s0 + i1 * x->s1;
+}
+
+static int64_t or_target(const or_targets* t, int64_t d1, int64_t r) {
+  int64_t i0 = r / d1, i1 = r % d1;
+  return t->data[i0 * t->s0 + i1 * t->s1];
+}
+
+static int or_check(const or_logits* x) {
+  if (!x || !x->data) return OR_EINVAL;
+  if (x->dtype != OR_F32 && x->dtype != OR_BF16) return OR_EINVAL;
+  if (x->d0 < 0 || x->d1 <= 0 || x->v_local <= 0) return OR_EINVAL;
+  if (x->vocab_start < 0 || x->vocab_start + x->v_local > x->vocab_total) return OR_EINVAL;
+  return 0;
+}
+
+/* n = number of rows whose target is not ignore_idx. */
+int64_t or_count_valid(const or_targets* t, int64_t d0, int64_t d1, int64_t ignore_idx) {
+  int64_t n = 0;
+  for (int64_t r = 0; r < d0 * d1; ++r)
+    if (or_target(t, d1, r) != ignore_idx) ++n;
+  return n;
+}
+
+/* lse of one full row: m + log sum_j exp(x_j - m). */
+static double or_row_lse(const or_logits* x, int64_t off) {
+  int64_t V = x->v_local;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < V; ++j) {
+    double v = or_elem(x, off + j);
+    if (v > m) m = v;
+  }
+  double s = 0.0;
+  for (int64_t j = 0; j < V; ++j) s += exp(or_elem(x, off + j) - m);
+  return m + log(s);
+}
+
+/*
+ * Loss (and lse) of the listed logical rows of an unsharded row set
+ * (v_local == vocab_total).  loss_i = -sum_j q_ij (x_ij - lse_i).
+ * lse_out may be NULL; for ignored rows it receives NAN (not defined).
+ */
+int or_loss_rows(const or_logits* x, const or_targets* t, double alpha, int64_t ignore_idx,
+                 const int64_t* rows, int64_t nrows, double* loss_out, double* lse_out) {
+  if (or_check(x) || x->v_local != x->vocab_total || !t || !rows || !loss_out) return OR_EINVAL;
+  const int64_t V = x->v_local;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t k = 0; k < nrows; ++k) {
+    int64_t r = rows[k];
+    int64_t tgt = or_target(t, x->d1, r);
+    if (tgt == ignore_idx) {
+      loss_out[k] = 0.0;
+      if (lse_out) lse_out[k] = NAN;
+      continue;
+    }
+    if (tgt < 0 || tgt >= V) {
+      bad = 1;
+      continue;
+    }
+    int64_t off = or_row_offset(x, r);
+    double lse = or_row_lse(x, off);
+    double loss = 0.0;
+    for (int64_t j = 0; j < V; ++j) {
+      double q = alpha / (double)V + (j == tgt ? 1.0 - alpha : 0.0);
+      loss -= q * (or_elem(x, off + j) - lse);
+    }
+    loss_out[k] = loss;
+    if (lse_out) lse_out[k] = lse;
+  }
+  return bad ? OR_EBADTARGET : 0;
+}
+
+/*
+ * Gradient of the listed rows, unrounded FP64, written as grad_out[k * V + j].
+ * s_i = g_row[r] (or 1 when g_row is NULL) if !reduce_loss,
+ * s_i = g_scalar / n_valid if reduce_loss.  Ignored rows get 0.
+ */
+int or_grad_rows(const or_logits* x, const or_targets* t, double alpha, int64_t ignore_idx,
+                 int32_t reduce_loss, const double* g_row, double g_scalar, int64_t n_valid,
+                 const int64_t* rows, int64_t nrows, double* grad_out) {
+  if (or_check(x) || x->v_local != x->vocab_total || !t || !rows || !grad_out) return OR_EINVAL;
+  const int64_t V = x->v_local;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t k = 0; k < nrows; ++k) {
+    int64_t r = rows[k];
+    double* gout = grad_out + k * V;
+    int64_t tgt = or_target(t, x->d1, r);
+    if (tgt == ignore_idx) {
+      for (int64_t j = 0; j < V; ++j) gout[j] = 0.0;
+      continue;
+    }
+    if (tgt < 0 || tgt >= V) {
+      bad = 1;
+      continue;
+    }
+    double s = reduce_loss ? g_scalar / (double)n_valid : (g_row ? g_row[r] : 1.0);
+    int64_t off = or_row_offset(x, r);
+    double lse = or_row_lse(x, off);
+    for (int64_t j = 0; j < V; ++j) {
+      double p = exp(or_elem(x, off + j) - lse);
+      double q = alpha / (double)V + (j == tgt ? 1.0 - alpha : 0.0);
+      gout[j] = s * (p - q);
+    }
+  }
+  return bad ? OR_EBADTARGET : 0;
+}
+
+/* Mean of per-row losses over the n non-ignored rows: sum_i loss_i / n. */
+double or_mean_loss(const double* loss, int64_t nrows, int64_t n_valid) {
+  double s = 0.0;
+  for (int64_t i = 0; i < nrows; ++i) s += loss[i];
+  return s / (double)n_valid;
+}
+
+/*
+ * Per-shard statistics of the listed rows: stats_out[k*4 + {0,1,2,3}] =
+ * (m, d, y, r) as defined in the header comment.  Targets are global.
+ * Ignored rows get (0, 0, 0, 0).
+ */
+int or_shard_stats(const or_logits* x, const or_targets* t, int64_t ignore_idx,
+                   const int64_t* rows, int64_t nrows, double* stats_out) {
+  if (or_check(x) || !t || !rows || !stats_out) return OR_EINVAL;
+  const int64_t V = x->v_local, o = x->vocab_start;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t k = 0; k < nrows; ++k) {
+    int64_t r = rows[k];
+    double* st = stats_out + 4 * k;
+    int64_t tgt = or_target(t, x->d1, r);
+    if (tgt == ignore_idx) {
+      st[0] = st[1] = st[2] = st[3] = 0.0;
+      continue;
+    }
+    int64_t off = or_row_offset(x, r);
+    double m = -INFINITY;
+    for (int64_t j = 0; j < V; ++j) {
+      double v = or_elem(x, off + j);
+      if (v > m) m = v;
+    }
+    double d = 0.0, rs = 0.0;
+    for (int64_t j = 0; j < V; ++j) {
+      double v = or_elem(x, off + j);
+      d += exp(v - m);
+      rs += v;
+    }
+    st[0] = m;
+    st[1] = d;
+    st[2] = (tgt >= o && tgt < o + V) ? or_elem(x, off + (tgt - o)) : 0.0;
+    st[3] = rs;
+  }
+  return 0;
+}
+
+/*
+ * Combine S shards' statistics (stats[s][k][4], k over the listed rows) into
+ * loss and lse for those rows.  V in a/V is vocab_total.
+ */
+int or_shard_combine(const double* stats, int32_t S, int64_t nrows, int64_t vocab_total,
+                     const or_targets* t, int64_t d1, double alpha, int64_t ignore_idx,
+                     const int64_t* rows, double* loss_out, double* lse_out) {
+  if (!stats || S <= 0 || vocab_total <= 0 || !t || !rows || !loss_out) return OR_EINVAL;
+  int bad = 0;
+  for (int64_t k = 0; k < nrows; ++k) {
+    int64_t tgt = or_target(t, d1, rows[k]);
+    if (tgt == ignore_idx) {
+      loss_out[k] = 0.0;
+      if (lse_out) lse_out[k] = NAN;
+      continue;
+    }
+    if (tgt < 0 || tgt >= vocab_total) {
+      bad = 1;
+      continue;
+    }
+    double M = -INFINITY;
+    for (int32_t s = 0; s < S; ++s) {
+      double m = stats[((int64_t)s * nrows + k) * 4 + 0];
+      if (m > M) M = m;
+    }
+    double D = 0.0, xt = 0.0, R = 0.0;
+    for (int32_t s = 0; s < S; ++s) {
+      const double* st = stats + ((int64_t)s * nrows + k) * 4;
+      D += st[1] * exp(st[0] - M);
+      xt += st[2];
+      R += st[3];
+    }
+    double lse = M + log(D);
+    loss_out[k] = lse - (1.0 - alpha) * xt - (alpha / (double)vocab_total) * R;
+    if (lse_out) lse_out[k] = lse;
+  }
+  return bad ? OR_EBADTARGET : 0;
+}
+
+/*
+ * Gradient of the listed rows of one shard, given the combined lse of each
+ * listed row (lse[k]).  Column j of the shard is global column o + j.
+ * grad_out[k * V_local + j]; scale s_i as in or_grad_rows.
+ */
+int or_shard_grad(const or_logits* x, const or_targets* t, double alpha, int64_t ignore_idx,
+                  int32_t reduce_loss, const double* g_row, double g_scalar, int64_t n_valid,
+                  const int64_t* rows, int64_t nrows, const double* lse, double* grad_out) {
+  if (or_check(x) || !t || !rows || !lse || !grad_out) return OR_EINVAL;
+  const int64_t V = x->v_local, o = x->vocab_start, Vt = x->vocab_total;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t k = 0; k < nrows; ++k) {
+    int64_t r = rows[k];
+    double* gout = grad_out + k * V;
+    int64_t tgt = or_target(t, x->d1, r);
+    if (tgt == ignore_idx) {
+      for (int64_t j = 0; j < V; ++j) gout[j] = 0.0;
+      continue;
+    }
+    double s = reduce_loss ? g_scalar / (double)n_valid : (g_row ? g_row[r] : 1.0);
+    int64_t off = or_row_offset(x, r);
+    for (int64_t j = 0; j < V; ++j) {
+      double p = exp(or_elem(x, off + j) - lse[k]);
+      double q = alpha / (double)Vt + (o + j == tgt ? 1.0 - alpha : 0.0);
+      gout[j] = s * (p - q);
+    }
+  }
+  return 0;
+}
+
+/* Threads the OpenMP runtime would use for the parallel loops above. */
+int or_max_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

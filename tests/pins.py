@@ -1,0 +1,270 @@
+"""Pins of the FP64 oracle against facts fixed outside it.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with what the pages or the mathematics fix.  They
+run against the real oracle (tests/test_oracle_pins.py) and against copies of
+it with planted mistakes (tests/test_oracle_mutants.py), where at least one
+pin must fail for every mistake.
+
+What each pin rests on:
+  * brute force -- the unfused softmax -> log -> NLL chain of the CANN ops-nn
+    fusion page ("standard approach: three kernels"), run in 50-digit decimal;
+  * closed form -- uniform logits give softmax 1/V, so the loss is ln V for
+    any smoothing and any target, and the gradient is s (1 - a)(1/V - [j = t]);
+  * the ops-nn page's worked number ("pitfall 1"): logits all 100, V = 32000,
+    lse = 100 + ln 32000, printed as 110.4 (tests/golden/p4_uniform_lse.json);
+  * library special case -- torch's float64 F.cross_entropy with
+    ignore_index and label_smoothing (the precision baseline named on the
+    TransformerEngineNPU issue #29 page, section 4) and its autograd gradient;
+  * finite differences -- the gradient is the derivative of the loss;
+  * invariants -- a row shift leaves loss and gradient unchanged, and
+    non-ignored gradient rows sum to zero;
+  * sharded == unsharded -- the vocabulary-parallel combine (hyper-parallel
+    issue #269 page, section 3.1) is an identity.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import workloads
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _close(a, b, rtol, atol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = np.abs(a - b)
+    bound = atol + rtol * np.abs(b)
+    bad = ~(err <= bound)
+    assert not bad.any(), f"{what}: max err {err.max():.3e} (worst at {np.unravel_index(np.argmax(err - bound), err.shape)})"
+
+
+def _tiny_case(seed, N, V, dtype, alpha, ignore_frac=0.25, swapped=False):
+    g = torch.Generator().manual_seed(seed)
+    A, B = (2, N // 2) if N % 2 == 0 else (1, N)
+    phys = (torch.randn((A, B, V), generator=g) * 3).to(dtype)
+    t = torch.randint(0, V, (A, B), generator=g)
+    k = int(round(ignore_frac * A * B))
+    if k:
+        t.view(-1)[torch.randperm(A * B, generator=g)[:k]] = workloads.IGNORE_IDX
+    if swapped:
+        return phys.transpose(0, 1), t.transpose(0, 1)
+    return phys, t
+
+
+def _rows_of(x):
+    """Logical rows as lists of Python floats (exact values of the stored bits)."""
+    d0, d1, V = x.shape
+    xd = x.to(torch.float64)
+    return [[float(v) for v in xd[i0, i1]] for i0 in range(d0) for i1 in range(d1)]
+
+
+def _targets_of(t):
+    d0, d1 = t.shape
+    return [int(t[i0, i1]) for i0 in range(d0) for i1 in range(d1)]
+
+
+# ----------------------------------------------------------------------------
+def pin_brute_force(orc):
+    """Oracle loss == 50-digit softmax -> log -> NLL, tiny inputs, all layouts."""
+    cases = 0
+    for seed, (N, V) in enumerate([(4, 1), (4, 2), (4, 5), (6, 8), (3, 7), (8, 16)]):
+        for dtype in (torch.float32, torch.bfloat16):
+            for alpha in (0.0, 0.1, 0.7):
+                for swapped in (False, True):
+                    x, t = _tiny_case(100 + seed, N, V, dtype, alpha, swapped=swapped)
+                    loss, _ = orc.loss_rows(x, t, alpha=alpha)
+                    ref = brute.loss_rows(_rows_of(x), _targets_of(t), alpha=alpha)
+                    _close(loss, [float(r) for r in ref], 1e-12, 1e-15, f"brute N={N} V={V} {dtype} a={alpha}")
+                    cases += 1
+    assert cases == 72
+
+
+def pin_closed_form_uniform(orc):
+    """Uniform logits: loss = ln V for every smoothing; grad = s(1-a)(1/V - onehot).
+
+    c = 1000 overflows exp() in FP64 unless the row maximum is taken out first."""
+    for V in (1, 7, 4096, 32000):
+        for c in (0.0, -37.5, 100.0, 1000.0):
+            for alpha in (0.0, 0.1, 0.5):
+                x = torch.full((1, 3, V), c, dtype=torch.float32)
+                t = torch.tensor([[0, V - 1, V // 2]])
+                loss, lse = orc.loss_rows(x, t, alpha=alpha)
+                _close(loss, [math.log(V)] * 3, 1e-12, 1e-12, f"ln V, V={V} c={c} a={alpha}")
+                _close(lse, [c + math.log(V)] * 3, 1e-13, 1e-12, f"lse V={V} c={c}")
+                if V <= 4096:
+                    g = np.array([0.5, 2.0, -1.0])
+                    grad = orc.grad_rows(x, t, alpha=alpha, g=g)
+                    ref = np.empty_like(grad)
+                    for k in range(3):
+                        ref[k] = g[k] * (1 - alpha) * (1.0 / V - (np.arange(V) == int(t[0, k])))
+                    _close(grad, ref, 1e-12, 1e-15, f"uniform grad V={V} c={c} a={alpha}")
+
+
+def pin_golden_p4_worked_lse(orc):
+    """The ops-nn page's worked value: all logits 100, V = 32000, lse ~ 110.4."""
+    with open(os.path.join(GOLDEN, "p4_uniform_lse.json")) as f:
+        gold = json.load(f)
+    V, c = gold["V"], gold["logit"]
+    x = torch.full((1, 1, V), c, dtype=torch.float32)
+    t = torch.tensor([[gold["target"]]])
+    _, lse = orc.loss_rows(x, t)
+    printed = gold["lse_printed"]
+    assert abs(lse[0] - printed) <= gold["printed_half_unit"], (lse[0], printed)
+    assert abs((lse[0] - c) - gold["log_v_printed"]) <= gold["printed_half_unit"]
+
+
+def pin_torch_cross_entropy(orc):
+    """Oracle loss, mean and gradient == torch float64 F.cross_entropy + autograd."""
+    for seed, (N, V) in enumerate([(8, 3), (12, 50), (6, 257), (16, 1000)]):
+        for dtype in (torch.float32, torch.bfloat16):
+            for alpha in (0.0, 0.1, 0.3):
+                for swapped in (False, True):
+                    x, t = _tiny_case(200 + seed, N, V, dtype, alpha, ignore_frac=0.2, swapped=swapped)
+                    d0, d1, _ = x.shape
+                    xd = x.to(torch.float64).reshape(d0 * d1, V).clone().requires_grad_(True)
+                    tf = t.reshape(d0 * d1)
+                    ref = F.cross_entropy(xd, tf, ignore_index=-100, label_smoothing=alpha, reduction="none")
+                    loss, _ = orc.loss_rows(x, t, alpha=alpha)
+                    _close(loss, ref.detach().numpy(), 1e-12, 1e-14, f"torch loss {N}x{V} a={alpha}")
+                    g = torch.linspace(-1.5, 2.0, d0 * d1, dtype=torch.float64)
+                    (gx,) = torch.autograd.grad(ref, xd, g)
+                    grad = orc.grad_rows(x, t, alpha=alpha, g=g.numpy())
+                    _close(grad, gx.numpy(), 1e-11, 1e-15, f"torch grad (none) {N}x{V} a={alpha}")
+                    # mean over non-ignored rows, upstream scalar g = 0.75
+                    xm = x.to(torch.float64).reshape(d0 * d1, V).clone().requires_grad_(True)
+                    refm = F.cross_entropy(xm, tf, ignore_index=-100, label_smoothing=alpha, reduction="mean")
+                    n = orc.count_valid(t)
+                    _close([orc.mean_loss(loss, n)], [float(refm.detach())], 1e-12, 1e-14, "torch mean")
+                    (gm,) = torch.autograd.grad(refm, xm, torch.tensor(0.75, dtype=torch.float64))
+                    gradm = orc.grad_rows(x, t, alpha=alpha, reduce_loss=True, g=0.75)
+                    _close(gradm, gm.numpy(), 1e-11, 1e-15, f"torch grad (mean) {N}x{V} a={alpha}")
+
+
+def pin_mean_all_ignored_is_nan(orc):
+    """Mean over zero non-ignored rows is 0/0 = NaN, as torch's mean reduction."""
+    x = torch.randn((2, 3, 5), generator=torch.Generator().manual_seed(7))
+    t = torch.full((2, 3), -100)
+    loss, _ = orc.loss_rows(x, t)
+    n = orc.count_valid(t)
+    ref = F.cross_entropy(x.double().reshape(6, 5), t.reshape(6), ignore_index=-100, reduction="mean")
+    assert n == 0 and math.isnan(orc.mean_loss(loss, n)) and math.isnan(float(ref))
+    assert np.all(loss == 0.0)
+
+
+def pin_finite_differences(orc):
+    """grad == central differences of sum_i g_i loss_i (and of g * mean).
+
+    Logits sit on the 2^-10 grid and the step is 2^-10, so x +- h is exact in
+    FP32 and the only error is the O(h^2) truncation."""
+    h = 2.0 ** -10
+    for alpha in (0.0, 0.2):
+        for reduce_loss in (False, True):
+            g = torch.Generator().manual_seed(31 + int(reduce_loss))
+            x = (torch.randint(-2048, 2048, (2, 2, 6), generator=g).double() * h).float()
+            t = torch.tensor([[1, -100], [5, 0]])
+            gr = np.array([0.7, -1.3, 2.0, 0.4])
+            gs = 1.7
+            n = orc.count_valid(t)
+
+            def objective(xx):
+                loss, _ = orc.loss_rows(xx, t, alpha=alpha)
+                return gs * orc.mean_loss(loss, n) if reduce_loss else float(np.dot(gr, loss))
+
+            grad = orc.grad_rows(x, t, alpha=alpha, reduce_loss=reduce_loss, g=gs if reduce_loss else gr)
+            fd = np.zeros_like(grad)
+            for r in range(4):
+                i0, i1 = divmod(r, 2)
+                for j in range(6):
+                    xp, xm = x.clone(), x.clone()
+                    xp[i0, i1, j] += h
+                    xm[i0, i1, j] -= h
+                    fd[r, j] = (objective(xp) - objective(xm)) / (2 * h)
+            _close(grad, fd, 1e-4, 1e-7, f"finite differences a={alpha} reduce={reduce_loss}")
+
+
+def pin_shift_invariance(orc):
+    """x -> x + c per row leaves loss and gradient unchanged (grid-exact shift)."""
+    for dtype in (torch.float32, torch.bfloat16):
+        x = workloads.grid_logits((3, 4, 37), dtype, seed=5)
+        t = workloads.random_targets((3, 4), 37, seed=6, ignore_frac=0.25)
+        xs = (x.double() + 4.0).to(dtype)
+        assert torch.equal(xs.double() - 4.0, x.double())
+        for alpha in (0.0, 0.3):
+            l0, _ = orc.loss_rows(x, t, alpha=alpha)
+            l1, _ = orc.loss_rows(xs, t, alpha=alpha)
+            _close(l1, l0, 1e-12, 1e-13, "shift loss")
+            g0 = orc.grad_rows(x, t, alpha=alpha)
+            g1 = orc.grad_rows(xs, t, alpha=alpha)
+            _close(g1, g0, 1e-11, 1e-15, "shift grad")
+
+
+def pin_grad_rows_sum_to_zero(orc):
+    """sum_j grad_ij = s (1 - (1-a) - a) = 0 for kept rows; ignored rows are exactly 0."""
+    inp = workloads.generate(workloads.WORKLOADS[2].scaled(phys=(4, 8), V=300))
+    for alpha in (0.0, 0.1):
+        for reduce_loss in (False, True):
+            grad = orc.grad_rows(inp.logits, inp.targets, alpha=alpha, reduce_loss=reduce_loss,
+                                 g=0.9 if reduce_loss else None)
+            t = inp.targets.reshape(-1).numpy()
+            kept = t != -100
+            assert np.all(grad[~kept] == 0.0)
+            sums = grad[kept].sum(axis=1)
+            scale = np.abs(grad[kept]).sum(axis=1)
+            assert np.all(np.abs(sums) <= 1e-13 * np.maximum(scale, 1e-300)), np.abs(sums).max()
+
+
+def pin_sharded_equals_unsharded(orc):
+    """Per-shard (m, d, y, r) then combine == the unsharded loss, lse and grad."""
+    for V, shards in ((1000, 4), (1001, 4), (65, 3), (5, 5)):
+        w = workloads.WORKLOADS[4].scaled(phys=(2, 5), V=V)
+        inp = workloads.generate(w)
+        x, t = inp.logits, inp.targets
+        bounds = workloads.shard_bounds(V, shards)
+        assert bounds[-1][1] == V
+        for alpha in (0.0, 0.1):
+            full_loss, full_lse = orc.loss_rows(x, t, alpha=alpha)
+            stats = np.stack([orc.shard_stats(x[..., a:b].contiguous(), t, a, V) for a, b in bounds])
+            loss, lse = orc.shard_combine(stats, t, V, alpha=alpha)
+            kept = t.reshape(-1).numpy() != -100
+            _close(loss, full_loss, 1e-12, 1e-13, f"shard loss V={V} S={shards}")
+            _close(lse[kept], full_lse[kept], 1e-13, 1e-13, "shard lse")
+            full_grad = orc.grad_rows(x, t, alpha=alpha, g=np.linspace(0.5, 1.5, 10))
+            parts = [orc.shard_grad(x[..., a:b].contiguous(), t, a, V, np.where(kept, lse, 0.0), alpha=alpha,
+                                    g=np.linspace(0.5, 1.5, 10)) for a, b in bounds]
+            _close(np.concatenate(parts, axis=1), full_grad, 1e-12, 1e-16, f"shard grad V={V} S={shards}")
+
+
+def pin_count_and_rows(orc):
+    """n equals the rows the generator kept, and sampled rows equal full rows."""
+    for k in (1, 2, 3, 4):
+        w = workloads.WORKLOADS[k].scaled(phys=(2, 16), V=64)
+        inp = workloads.generate(w)
+        assert orc.count_valid(inp.targets) == w.rows - w.n_ignored
+        rows = np.array([w.rows - 1, 0, 7, 3])
+        full, _ = orc.loss_rows(inp.logits, inp.targets, alpha=w.alpha)
+        part, _ = orc.loss_rows(inp.logits, inp.targets, alpha=w.alpha, rows=rows)
+        assert np.array_equal(part, full[rows])
+
+
+ALL_PINS = [
+    pin_brute_force,
+    pin_closed_form_uniform,
+    pin_golden_p4_worked_lse,
+    pin_torch_cross_entropy,
+    pin_mean_all_ignored_is_nan,
+    pin_finite_differences,
+    pin_shift_invariance,
+    pin_grad_rows_sum_to_zero,
+    pin_sharded_equals_unsharded,
+    pin_count_and_rows,
+]

@@ -1,0 +1,66 @@
+"""Plant plausible mistakes in a copy of the oracle and check that a pin fails.
+
+Each mutant is a textual edit of oracle/ce_oracle.c compiled into a temporary
+library on the CPU; the real oracle is never modified.  A mutant that every pin
+lets through would mean the pins cannot tell that mistake from the truth.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ce_oracle.c")
+
+# (name, text in ce_oracle.c, replacement, expected number of occurrences)
+MUTANTS = [
+    ("loss_drops_smoothing_mass",
+     "double q = alpha / (double)V + (j == tgt ? 1.0 - alpha : 0.0);\n      loss -= q",
+     "double q = (j == tgt ? 1.0 - alpha : 0.0);\n      loss -= q", 1),
+    ("grad_sign_flipped", "gout[j] = s * (p - q);\n    }\n  }\n  return bad", "gout[j] = s * (q - p);\n    }\n  }\n  return bad", 1),
+    ("grad_target_off_by_one",
+     "double q = alpha / (double)V + (j == tgt ? 1.0 - alpha : 0.0);\n      gout",
+     "double q = alpha / (double)V + (j == tgt + 1 ? 1.0 - alpha : 0.0);\n      gout", 1),
+    ("grad_smoothing_over_v_minus_1",
+     "double q = alpha / (double)V + (j == tgt ? 1.0 - alpha : 0.0);\n      gout",
+     "double q = (j == tgt ? 1.0 - alpha : alpha / (double)(V - 1));\n      gout", 1),
+    ("row_strides_swapped", "return i0 * x->s0 + i1 * x->s1;", "return i0 * x->s1 + i1 * x->s0;", 1),
+    ("target_strides_swapped", "return t->data[i0 * t->s0 + i1 * t->s1];", "return t->data[i0 * t->s1 + i1 * t->s0];", 1),
+    ("no_max_shift", "s += exp(or_elem(x, off + j) - m);\n  return m + log(s);",
+     "s += exp(or_elem(x, off + j));\n  return log(s);", 1),
+    ("mean_divides_by_rows", "return s / (double)n_valid;", "return s / (double)nrows;", 1),
+    ("mean_grad_ignores_n",
+     "double s = reduce_loss ? g_scalar / (double)n_valid : (g_row ? g_row[r] : 1.0);\n    int64_t off = or_row_offset(x, r);\n    double lse",
+     "double s = reduce_loss ? g_scalar : (g_row ? g_row[r] : 1.0);\n    int64_t off = or_row_offset(x, r);\n    double lse", 1),
+    ("bf16_widened_wrong", "<< 16;", "<< 15;", 1),
+    ("combine_no_rescale", "D += st[1] * exp(st[0] - M);", "D += st[1];", 1),
+    ("combine_drops_target_gather", "xt += st[2];", "xt = st[2];", 1),
+    ("shard_grad_uses_local_v", "alpha / (double)Vt", "alpha / (double)V", 1),
+    ("shard_target_column_unshifted", "or_elem(x, off + (tgt - o))", "or_elem(x, off + tgt % V)", 1),
+    ("ignored_row_not_zeroed", "loss_out[k] = 0.0;\n      if (lse_out) lse_out[k] = NAN;\n      continue;\n    }\n    if (tgt < 0 || tgt >= V)",
+     "if (lse_out) lse_out[k] = NAN;\n    }\n    if (tgt < 0 || tgt >= V)", 1),
+    ("count_counts_ignored", "if (or_target(t, d1, r) != ignore_idx) ++n;", "++n;", 1),
+]
+
+
+@pytest.mark.parametrize("name,old,new,count", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_some_pin_catches(tmp_path, name, old, new, count):
+    src = open(SRC).read()
+    assert src.count(old) == count, f"mutation anchor for {name} not found {count}x"
+    mutated = src.replace(old, new)
+    c_path = tmp_path / "mutant.c"
+    so_path = tmp_path / "libmutant.so"
+    c_path.write_text(mutated)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-w", "-o", str(so_path),
+                    str(c_path), "-lm"], check=True)
+    orc = oracle.Oracle(oracle.load(str(so_path)))
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, oracle.OracleError) as e:  # a pin failed: the mistake is seen
+            caught.append((pin.__name__, str(e)[:80]))
+            break
+    assert caught, f"no pin catches mutant {name}"
