@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused cross-entropy hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 5] [--gpus 1]
+
+A step is one pass of the whole path over one batch of synthetic input
+already resident in HBM: for the default workload (4 x 2048 rows of 128000
+BF16 logits, label smoothing 0.1, mean over the 7782 non-ignored rows) that is
+ce_fwd_bwd_fused = count kernel + fused kernel (one read of the logits, the
+gradient written over them) + mean kernel.  Each timed step works on its own
+pre-generated copy of the logits from a pool in HBM (the call overwrites its
+input with the gradient; once the pool wraps, a step runs on a previous
+step's gradient, which costs the same work).
+
+Printed: one JSON line with the whole-step throughput (formula bytes
+N*V*b read + N*V*b written, per step), the roofline of the fused kernel
+(its own average duration from HIP events recorded by the library on the
+same stream), HBM traffic from committed rocprofv3 counter runs when they
+match the current kernel source, and the FP64 oracle timed on a bounded
+sample of rows on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused CE fwd+bwd achieved HBM GB/s (% of peak) and rows/sec at V=128000 bf16"
+PEAK_GBPS = 8000.0  # MI355X HBM3E peak, AMD public specification
+KERNEL_SRC = os.path.join(ROOT, "vocab_cross_entropy_amd", "csrc", "ce_kernels.hip")
+PMC_FILE = os.path.join(ROOT, "profiles", "fused_bf16_v128000_pmc.json")
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_profiles(workload_name: str):
+    """HBM bytes per launch of the fused kernel from committed rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter reads
+    for a plain copy kernel of known size.  None when absent or stale."""
+    try:
+        with open(PMC_FILE) as f:
+            pmc = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter file"
+    if pmc.get("kernel_source_sha256") != kernel_source_sha():
+        return None, "kernel changed since the counters were taken"
+    if pmc.get("workload") != workload_name:
+        return None, "counters are for another workload"
+    c = pmc["copy"]
+    fetch_scale = c["bytes"] / (c["fetch_kib"] * 1024.0)
+    write_scale = c["bytes"] / (c["write_kib"] * 1024.0)
+    t = pmc["fetch_kib"] * 1024.0 * fetch_scale + pmc["write_kib"] * 1024.0 * write_scale
+    return t, f"fetch x{fetch_scale:.3f}, write x{write_scale:.3f} (copy calibration)"
+
+
+def cpu_baseline(w, inputs, sample_rows: int):
+    """The FP64 oracle (as it is) on the first `sample_rows` rows: loss and
+    gradient, the same work per row as the GPU step."""
+    import numpy as np
+
+    import oracle
+
+    orc = oracle.default()
+    N = w.rows
+    rows = np.arange(min(sample_rows, N), dtype=np.int64)
+    n_valid = orc.count_valid(inputs.targets)
+    t0 = time.perf_counter()
+    for b in range(0, rows.size, 256):
+        blk = rows[b:b + 256]
+        orc.loss_rows(inputs.logits, inputs.targets, w.alpha, rows=blk)
+        orc.grad_rows(inputs.logits, inputs.targets, w.alpha, reduce_loss=w.reduce_loss,
+                      g=1.0 if w.reduce_loss else None, rows=blk, n_valid=n_valid)
+    dt = time.perf_counter() - t0
+    nbytes = 2 * rows.size * w.V * w.elem_bytes
+    return {
+        "value": nbytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": orc.max_threads(),
+        "kind": "oracle",
+        "sample": f"first {rows.size} of {N} rows (loss + gradient, FP64), {dt:.2f} s wall",
+        "rows_per_s": rows.size / dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--pool", type=int, default=8, help="device copies of the input (HBM)")
+    ap.add_argument("--cpu-sample-rows", type=int, default=1536)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-chunks", type=int, default=0, help="tuning: force the fused kernel's split")
+    ap.add_argument("--json-out", default=None)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU (vocabulary- or row-sharded) path is not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import vocab_cross_entropy_amd as vce
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    inputs = workloads.generate(w)
+    gen_s = time.perf_counter() - t_gen
+    print(f"[bench] generated {w.name} in {gen_s:.1f} s", file=sys.stderr, flush=True)
+
+    N, V, b = w.rows, w.V, w.elem_bytes
+    formula_bytes = 2 * N * V * b  # N*V*b read + N*V*b gradient written
+
+    phys_dev = inputs.logits_phys.to(dev)
+    targets_dev = inputs.targets_phys.to(dev)
+    view = (lambda p: p.transpose(0, 1)) if w.swapped else (lambda p: p)
+    t_view = view(targets_dev)
+    P = max(1, min(args.pool, args.steps + args.warmup))
+    pool = [phys_dev] + [phys_dev.clone() for _ in range(P - 1)]
+    torch.cuda.synchronize()
+
+    loss = torch.empty(1 if w.reduce_loss else N, dtype=torch.float32, device=dev)
+    n_valid = torch.empty(1, dtype=torch.int32, device=dev)
+    calls_per_step = 1
+    if w.calls == "fused":
+        ws = torch.empty(vce.ce_workspace_bytes(view(pool[0]), w.alpha, w.reduce_loss, split_chunks=args.split_chunks),
+                         dtype=torch.uint8, device=dev)
+
+        def step(p):
+            vce.ce_fwd_bwd_fused(view(p), t_view, w.alpha, w.reduce_loss, loss=loss, n_valid=n_valid, ws=ws,
+                                 split_chunks=args.split_chunks)
+    elif w.calls == "split":
+        ws = torch.empty(vce.ce_workspace_bytes(view(pool[0]), w.alpha, w.reduce_loss), dtype=torch.uint8, device=dev)
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        g = torch.ones(N, dtype=torch.float32, device=dev)
+        calls_per_step = 2
+
+        def step(p):
+            x = view(p)
+            vce.ce_forward(x, t_view, w.alpha, w.reduce_loss, loss=loss, lse=lse, n_valid=n_valid, ws=ws)
+            vce.ce_backward_inplace(x, t_view, lse, w.alpha, w.reduce_loss, grad_out=g, n_valid=n_valid)
+    else:  # vocabulary shards: S partial-stat calls, one combine, S backward calls
+        bounds = workloads.shard_bounds(V, w.shards)
+        shard_pool = [[p[..., a:c].contiguous() for a, c in bounds] for p in pool]
+        del pool
+        pool = shard_pool
+        stats = torch.empty((len(bounds), N, 4), dtype=torch.float32, device=dev)
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        ws = torch.empty(vce.ce_combine_workspace_bytes(N, w.reduce_loss), dtype=torch.uint8, device=dev)
+        g = torch.ones(N, dtype=torch.float32, device=dev)
+        calls_per_step = 2 * len(bounds)
+
+        def step(shards):
+            for s, (a, c) in enumerate(bounds):
+                vce.ce_shard_partial_stats(shards[s], t_view, a, V, stats=stats[s])
+            vce.ce_shard_combine(stats, t_view, V, w.alpha, w.reduce_loss, loss=loss, lse=lse, n_valid=n_valid, ws=ws)
+            for s, (a, c) in enumerate(bounds):
+                vce.ce_backward_inplace(shards[s], t_view, lse, w.alpha, w.reduce_loss, grad_out=g, n_valid=n_valid,
+                                        vocab_start=a, vocab_total=V)
+
+    for i in range(args.warmup):
+        step(pool[i % P])
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with vce.Profiler(args.steps * calls_per_step) as prof:
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        e0.record()
+        for i in range(args.steps):
+            step(pool[(args.warmup + i) % P])
+        e1.record()
+        torch.cuda.synchronize()
+        h1 = time.perf_counter()
+    step_ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {step_ms * 1e3:.1f} us/step (host {1e6 * (h1 - h0) / args.steps:.1f})",
+          file=sys.stderr, flush=True)
+
+    # plain device copy of the same byte count, for context (achievable read+write rate)
+    src = pool[0] if w.calls != "shard" else pool[0][0]
+    flat = phys_dev.view(-1)
+    dst = torch.empty_like(flat)
+    for _ in range(3):
+        dst.copy_(flat)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(flat)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * flat.numel() * flat.element_size() / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+    del dst, src
+
+    main_ms = prof.ms
+    roofline = None
+    if w.calls == "fused" and main_ms:
+        k_ms = sum(main_ms) / len(main_ms)
+        achieved = formula_bytes / (k_ms * 1e-3) / 1e9
+        traffic, traffic_note = traffic_from_profiles(w.name)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+                    "kernel": "k_fused", "kernel_avg_us": round(k_ms * 1e3, 2),
+                    "algorithmic_bytes": formula_bytes, "traffic_note": traffic_note}
+
+    value = formula_bytes / (step_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {**w.describe(), "io_dtype": "bf16" if w.elem_bytes == 2 else "f32", "calls": w.calls,
+                   "split_chunks": args.split_chunks, "pool": P},
+        "rows_per_s": round(N / (step_ms * 1e-3), 1),
+        "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
+        "formula_bytes_per_step": formula_bytes,
+        "copy_ref_GBps": round(copy_gbps, 1),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if w.calls != "fused":
+        moved = 3 * N * V * b
+        out["moved_bytes_per_step"] = moved
+        out["moved_GBps"] = round(moved / (step_ms * 1e-3) / 1e9, 1)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_sample_rows)
+    line = json.dumps(out)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
+
+
+if __name__ == "__main__":
+    main()

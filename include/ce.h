@@ -1,0 +1,210 @@
+/*
+ * ce.h -- C ABI of the MI355X (gfx950) fused cross-entropy library (libce.so).
+ *
+ * The library computes, for each row i of language-model logits x[N, V]
+ * (FP32 or BF16, accumulated in FP32):
+ *
+ *   lse_i  = log sum_j exp(x_ij)
+ *   loss_i = lse_i - (1 - a) x_i,t_i - (a / V) sum_j x_ij
+ *   grad_ij = s_i (exp(x_ij - lse_i) - a / V - (1 - a) [j == t_i])
+ *
+ * with label smoothing a, target t_i (a global vocabulary index), rows whose
+ * target equals ignore_idx contributing loss 0 and gradient 0, and
+ * s_i = g_i (per-row upstream gradient) or g / n when the loss is reduced to
+ * the mean over the n non-ignored rows.
+ *
+ * Sources, by the pages' titles and sections:
+ *  - interface and semantics: TransformerEngineNPU issue #29 "Parallel Cross
+ *    Entropy (Triton)", section 1 (parallel_cross_entropy(inp, target,
+ *    label_smoothing, reduce_loss, dist_process_group, ignore_idx=-100);
+ *    (B, SQ, V) or (SQ, B, V) input; FP32 accumulation; FP32 loss; gradient
+ *    written back in the input dtype) and section 6 (the gradient is staged
+ *    in place in the input; the only extra buffers are loss[N] and, under
+ *    vocabulary parallelism, the gathered per-rank (m, d, X_y) statistics);
+ *  - the log_softmax + NLL identity and the softmax-minus-onehot gradient:
+ *    CANN ops-nn page "cross-entropy fusion: three kernel launches to one",
+ *    sections "fusion scheme" and "backward";
+ *  - vocabulary shards: hyper-parallel issue #269, section 3.1 (forward is a
+ *    MAX all-reduce, a SUM all-reduce and a target-logit gather; backward
+ *    needs no collective; shards of ceil(V / tp) columns; ignore_index -100).
+ *  Label smoothing follows the uniform a/V convention of torch's
+ *  F.cross_entropy, the precision baseline named in issue #29 section 4.
+ *
+ * Conventions for every call:
+ *  - All pointers named "device" are HIP device (or managed) memory owned by
+ *    the caller; the library allocates nothing on these calls and keeps no
+ *    pointer after it returns.
+ *  - Calls are asynchronous on `stream` (NULL = the null stream); results are
+ *    valid once the stream has reached the enqueued work.  No call
+ *    synchronises the host, so the sequence can be captured in a HIP graph.
+ *  - Arguments are checked on the host before any HIP call.  On an argument
+ *    error the call returns a non-zero ce_status, enqueues nothing and leaves
+ *    every buffer untouched; ce_last_error() then describes the problem.
+ *  - A non-ignored target outside [0, vocab_total) violates the calls'
+ *    precondition: no kernel reads out of bounds because of it, and that
+ *    row's loss, lse and gradient are NaN.
+ *  - Logical row r = i0 * d1 + i1 (0 <= i0 < d0, 0 <= i1 < d1) starts at
+ *    element offset i0 * s0 + i1 * s1 of `data`; its V columns are
+ *    contiguous.  (B, SQ, V) is s0 = SQ * V, s1 = V; the transposed (SQ, B, V)
+ *    view of (B, SQ, V) storage is s0 = V, s1 = SQ * V.  Loss and lse are
+ *    indexed by logical row.  Rows must not overlap in memory.
+ */
+#ifndef VCE_CE_H
+#define VCE_CE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CE_ABI_VERSION 1
+
+typedef enum ce_status {
+  CE_OK = 0,
+  CE_EINVAL = 1,      /* NULL pointer, negative size, smoothing outside [0, 1], ... */
+  CE_EDTYPE = 2,      /* logits dtype is not CE_F32 or CE_BF16 */
+  CE_ELAYOUT = 3,     /* strides, alignment or shard bounds not supported */
+  CE_EWORKSPACE = 4,  /* workspace NULL or smaller than required */
+  CE_EHIP = 5,        /* a HIP runtime call or kernel launch failed */
+  CE_EDEADLOCK = 6    /* a split row's statistics exchange exceeded its wait bound */
+} ce_status;
+
+enum { CE_F32 = 0, CE_BF16 = 1 };
+
+/* Logits (or one vocabulary shard of them). */
+typedef struct ce_logits {
+  void* data;          /* device pointer to logical element (0, 0, 0); aligned to its dtype */
+  int32_t dtype;       /* CE_F32 or CE_BF16 */
+  int32_t reserved;    /* must be 0 */
+  int64_t d0, d1;      /* logical leading dims, d0 >= 0, d1 >= 1; N = d0 * d1 rows */
+  int64_t s0, s1;      /* element strides of d0 and d1 (>= 0); the column stride is 1 */
+  int64_t v_local;     /* columns present in `data` (>= 1) */
+  int64_t vocab_start; /* global index of local column 0 (0 when unsharded) */
+  int64_t vocab_total; /* global vocabulary size V; vocab_start + v_local <= V */
+} ce_logits;
+
+/* Targets: int64 global vocabulary indices over the same logical (d0, d1). */
+typedef struct ce_targets {
+  const int64_t* data; /* device pointer to target (0, 0) */
+  int64_t s0, s1;      /* element strides (>= 0) */
+} ce_targets;
+
+typedef struct ce_params {
+  float label_smoothing; /* a in [0, 1] */
+  int32_t reduce_loss;   /* 0: per-row loss[N]; 1: mean over non-ignored rows, loss[1] */
+  int64_t ignore_idx;    /* rows whose target equals this are skipped (conventionally -100) */
+  int32_t split_chunks;  /* 0: automatic.  > 0: ce_fwd_bwd_fused splits each row over this many
+                            cooperating workgroups (tuning and testing; at most 64) */
+  int32_t reserved;      /* must be 0 */
+} ce_params;
+
+/*
+ * Workspace bytes that ce_forward and ce_fwd_bwd_fused need for logits
+ * described by `x` and parameters `p`.  Returns 0 (and sets ce_last_error)
+ * if the arguments are invalid.  The content of the workspace needs no
+ * initialisation; the calls clear what they use.  Two calls must not use one
+ * workspace concurrently.
+ */
+size_t ce_workspace_bytes(const ce_logits* x, const ce_params* p);
+
+/* Workspace bytes that ce_shard_combine needs for `rows` rows. */
+size_t ce_combine_workspace_bytes(int64_t rows, const ce_params* p);
+
+/*
+ * Forward only (issue #29 section 1 forward; ops-nn "fusion scheme").
+ * Unsharded logits (vocab_start == 0, v_local == vocab_total); read once.
+ *   loss    [N] (reduce_loss 0) or [1] (reduce_loss 1), device FP32, written
+ *   lse     [N] device FP32 or NULL; ignored rows get 0
+ *   n_valid [1] device int32 or NULL: number of non-ignored rows
+ *   ws      device workspace of at least ce_workspace_bytes(x, p) bytes
+ */
+ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p, float* loss, float* lse,
+                     int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward, gradient written in place over the logits in their own dtype
+ * (issue #29 section 6; ops-nn "backward", smoothing per "pitfall 3" read
+ * with a/V).  `x` may be a vocabulary shard: column j is global column
+ * vocab_start + j and a/V uses vocab_total (hyper-parallel #269 section 3.1:
+ * the backward needs no collective).
+ *   lse       [N] device FP32 from ce_forward or ce_shard_combine
+ *   grad_out  device FP32: [N] per-row upstream gradient (reduce_loss 0) or
+ *             [1] (reduce_loss 1); NULL means 1
+ *   n_valid   [1] device int32, required when reduce_loss is 1
+ * Ignored rows are set to +0.0 without being read.
+ */
+ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* lse,
+                              const float* grad_out, const int32_t* n_valid, hipStream_t stream);
+
+/*
+ * Fused forward + backward: one read of the logits, the gradient written
+ * over them once (ops-nn page, fused rows of its comparison table; issue #29
+ * section 6 in-place staging).  Unsharded logits.  Rows that do not fit one
+ * workgroup's registers are split over cooperating workgroups that exchange
+ * (max, sum-exp, target logit, row sum) through the workspace.
+ *   grad_out  as for ce_backward_inplace (known before the call); NULL = 1
+ *   loss      [N] or [1] device FP32, written
+ *   n_valid   [1] device int32 or NULL
+ *   ws        device workspace of at least ce_workspace_bytes(x, p) bytes
+ */
+ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* grad_out,
+                           float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Per-shard partial statistics (issue #29 section 6 gathers (m, d, X_y);
+ * hyper-parallel #269 section 3.1 reduces MAX and SUM and gathers the target
+ * logit).  For every logical row of the shard:
+ *   stats[r*4 + 0] = m = max_j x_rj                      (natural units)
+ *   stats[r*4 + 1] = d = sum_j exp(x_rj - m)
+ *   stats[r*4 + 2] = y = x_r,(t_r - vocab_start) if the shard holds t_r, else 0
+ *   stats[r*4 + 3] = r = sum_j x_rj
+ * Ignored rows are not read and get (0, 0, 0, 0).  `stats` is device FP32 [N][4].
+ */
+ce_status ce_shard_partial_stats(const ce_logits* shard, const ce_targets* t, const ce_params* p, float* stats,
+                                 hipStream_t stream);
+
+/*
+ * Combine S shards' statistics stats[S][N][4] (device FP32, shard-major) into
+ * per-row loss and lse over the full vocabulary of vocab_total columns:
+ *   M = max_s m_s, D = sum_s d_s exp(m_s - M) (s ascending), lse = M + log D,
+ *   loss = lse - (1 - a) sum_s y_s - (a / V) sum_s r_s.
+ * This is the point where a multi-GPU run would exchange the statistics.
+ *   loss [N] or [1], lse [N] (may be NULL), n_valid [1] (may be NULL),
+ *   ws of at least ce_combine_workspace_bytes(d0 * d1, p) bytes.
+ */
+ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1, int64_t vocab_total,
+                           const ce_targets* t, const ce_params* p, float* loss, float* lse, int32_t* n_valid,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Waits for `stream` and reports whether a split-row exchange in the last call
+ * that used `ws` gave up waiting (CE_EDEADLOCK) -- a diagnostic, never needed
+ * for correct results. */
+ce_status ce_workspace_check(const void* ws, hipStream_t stream);
+
+/*
+ * Kernel timing for benchmarks.  After ce_profile_start(capacity), each of
+ * the next `capacity` calls of ce_forward, ce_backward_inplace,
+ * ce_fwd_bwd_fused or ce_shard_partial_stats records a pair of HIP events on
+ * its stream around its main (bandwidth-dominant) kernel.
+ * ce_profile_stop(ms, cap, count) waits for those events, writes up to `cap`
+ * durations in milliseconds to host array `ms`, the number recorded to
+ * *count, and releases the events.  Not thread-safe; adds no synchronisation
+ * to the timed calls.
+ */
+ce_status ce_profile_start(int32_t capacity);
+ce_status ce_profile_stop(float* ms, int32_t cap, int32_t* count);
+
+const char* ce_status_string(ce_status s);
+/* Detail of the last non-OK status returned on the calling thread. */
+const char* ce_last_error(void);
+int32_t ce_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VCE_CE_H */

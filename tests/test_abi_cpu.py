@@ -1,0 +1,200 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments on the host before any HIP call (nothing is enqueued and
+no buffer is touched).  No compute call is made here.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from vocab_cross_entropy_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ce.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ce_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("ce_forward", "ce_backward_inplace", "ce_fwd_bwd_fused", "ce_shard_partial_stats",
+              "ce_shard_combine"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _abi.SIGNATURES, f"binding lacks {name}"
+
+
+def test_version_and_strings(lib):
+    assert lib.ce_abi_version() == _abi.CE_ABI_VERSION
+    for s in range(7):
+        assert lib.ce_status_string(s).startswith(b"CE_")
+
+
+# -- host-side validation with host buffers (never dereferenced) ------------
+class Host:
+    """Host stand-ins for device buffers; validation must reject the call
+    before anything reads or writes them."""
+
+    def __init__(self, N=6, V=16, dtype=_abi.CE_BF16):
+        self.x = np.zeros(N * V * 2, np.uint16 if dtype == _abi.CE_BF16 else np.float32)
+        self.t = np.zeros(N, np.int64)
+        self.loss = np.full(N, 7.0, np.float32)
+        self.lse = np.full(N, 7.0, np.float32)
+        self.n = np.full(1, 7, np.int32)
+        self.stats = np.full(N * 4, 7.0, np.float32)
+        self.ws = np.zeros(1 << 16, np.uint8)
+        self.N, self.V, self.dtype = N, V, dtype
+
+    def logits(self, **kw):
+        d = dict(data=self.x.ctypes.data, dtype=self.dtype, reserved=0, d0=2, d1=self.N // 2, s0=self.N // 2 * self.V,
+                 s1=self.V, v_local=self.V, vocab_start=0, vocab_total=self.V)
+        d.update(kw)
+        return _abi.CeLogits(**d)
+
+    def targets(self, **kw):
+        d = dict(data=self.t.ctypes.data, s0=self.N // 2, s1=1)
+        d.update(kw)
+        return _abi.CeTargets(**d)
+
+    @staticmethod
+    def params(**kw):
+        d = dict(label_smoothing=0.0, reduce_loss=0, ignore_idx=-100, split_chunks=0, reserved=0)
+        d.update(kw)
+        return _abi.CeParams(**d)
+
+    def untouched(self):
+        return (np.all(self.loss == 7.0) and np.all(self.lse == 7.0) and self.n[0] == 7
+                and np.all(self.stats == 7.0) and not self.x.any())
+
+
+def _fused(lib, h, x=None, t=None, p=None, ws=True, ws_bytes=None):
+    x = x or h.logits()
+    t = t or h.targets()
+    p = p or h.params()
+    return lib.ce_fwd_bwd_fused(ctypes.byref(x), ctypes.byref(t), ctypes.byref(p), None, h.loss.ctypes.data,
+                                h.n.ctypes.data, h.ws.ctypes.data if ws else None,
+                                h.ws.nbytes if ws_bytes is None else ws_bytes, None)
+
+
+BAD_FUSED = [
+    ("dtype", dict(x=dict(dtype=7)), _abi.CE_EDTYPE),
+    ("reserved", dict(x=dict(reserved=1)), _abi.CE_EINVAL),
+    ("v_local_zero", dict(x=dict(v_local=0, vocab_total=0)), _abi.CE_EINVAL),
+    ("d1_zero", dict(x=dict(d1=0)), _abi.CE_EINVAL),
+    ("d0_negative", dict(x=dict(d0=-1)), _abi.CE_EINVAL),
+    ("null_data", dict(x=dict(data=None)), _abi.CE_EINVAL),
+    ("misaligned_bf16", dict(x=dict(data="odd")), _abi.CE_ELAYOUT),
+    ("negative_stride", dict(x=dict(s0=-16)), _abi.CE_ELAYOUT),
+    ("rows_overlap", dict(x=dict(s1=8)), _abi.CE_ELAYOUT),
+    ("rows_overlap_outer", dict(x=dict(s0=16)), _abi.CE_ELAYOUT),
+    ("sharded_for_fused", dict(x=dict(vocab_start=16, vocab_total=32)), _abi.CE_ELAYOUT),
+    ("shard_past_vocab", dict(x=dict(vocab_start=8, vocab_total=20)), _abi.CE_ELAYOUT),
+    ("smoothing_negative", dict(p=dict(label_smoothing=-0.1)), _abi.CE_EINVAL),
+    ("smoothing_above_one", dict(p=dict(label_smoothing=1.5)), _abi.CE_EINVAL),
+    ("smoothing_nan", dict(p=dict(label_smoothing=float("nan"))), _abi.CE_EINVAL),
+    ("reduce_not_bool", dict(p=dict(reduce_loss=2)), _abi.CE_EINVAL),
+    ("split_chunks_too_many", dict(p=dict(split_chunks=65)), _abi.CE_EINVAL),
+    ("params_reserved", dict(p=dict(reserved=3)), _abi.CE_EINVAL),
+    ("null_targets", dict(t=dict(data=None)), _abi.CE_EINVAL),
+    ("target_negative_stride", dict(t=dict(s1=-1)), _abi.CE_ELAYOUT),
+    ("no_workspace", dict(ws=False), _abi.CE_EWORKSPACE),
+    ("small_workspace", dict(ws_bytes=16), _abi.CE_EWORKSPACE),
+]
+
+
+@pytest.mark.parametrize("name,change,status", BAD_FUSED, ids=[b[0] for b in BAD_FUSED])
+def test_fused_rejects_before_any_hip_call(lib, name, change, status):
+    h = Host()
+    xkw = dict(change.get("x", {}))
+    if xkw.get("data") == "odd":
+        xkw["data"] = h.x.ctypes.data + 1
+    x = h.logits(**xkw)
+    t = h.targets(**change.get("t", {}))
+    p = h.params(**change.get("p", {}))
+    rc = _fused(lib, h, x, t, p, ws=change.get("ws", True), ws_bytes=change.get("ws_bytes"))
+    assert rc == status, (rc, lib.ce_last_error())
+    assert lib.ce_last_error()
+    assert h.untouched()
+
+
+def test_other_calls_reject(lib):
+    h = Host()
+    p = h.params()
+    bad_x = h.logits(dtype=5)
+    t = h.targets()
+    assert lib.ce_forward(ctypes.byref(bad_x), ctypes.byref(t), ctypes.byref(p), h.loss.ctypes.data, None, None,
+                          h.ws.ctypes.data, h.ws.nbytes, None) == _abi.CE_EDTYPE
+    # forward needs unsharded logits
+    sx = h.logits(vocab_start=16, vocab_total=64)
+    assert lib.ce_forward(ctypes.byref(sx), ctypes.byref(t), ctypes.byref(p), h.loss.ctypes.data, None, None,
+                          h.ws.ctypes.data, h.ws.nbytes, None) == _abi.CE_ELAYOUT
+    # backward: lse required, n_valid required when reducing
+    x = h.logits()
+    assert lib.ce_backward_inplace(ctypes.byref(x), ctypes.byref(t), ctypes.byref(p), None, None, None,
+                                   None) == _abi.CE_EINVAL
+    pr = h.params(reduce_loss=1)
+    assert lib.ce_backward_inplace(ctypes.byref(x), ctypes.byref(t), ctypes.byref(pr), h.lse.ctypes.data, None,
+                                   None, None) == _abi.CE_EINVAL
+    # shard stats: misaligned stats, shard past the vocabulary
+    assert lib.ce_shard_partial_stats(ctypes.byref(x), ctypes.byref(t), ctypes.byref(p), h.stats.ctypes.data + 4,
+                                      None) == _abi.CE_ELAYOUT
+    bad_shard = h.logits(vocab_start=60, vocab_total=64)
+    assert lib.ce_shard_partial_stats(ctypes.byref(bad_shard), ctypes.byref(t), ctypes.byref(p),
+                                      h.stats.ctypes.data, None) == _abi.CE_ELAYOUT
+    # combine: S < 1, vocab_total < 1, small workspace
+    assert lib.ce_shard_combine(h.stats.ctypes.data, 0, 2, 3, 64, ctypes.byref(t), ctypes.byref(p),
+                                h.loss.ctypes.data, None, None, h.ws.ctypes.data, h.ws.nbytes, None) == _abi.CE_EINVAL
+    assert lib.ce_shard_combine(h.stats.ctypes.data, 1, 2, 3, 0, ctypes.byref(t), ctypes.byref(p),
+                                h.loss.ctypes.data, None, None, h.ws.ctypes.data, h.ws.nbytes, None) == _abi.CE_EINVAL
+    assert lib.ce_shard_combine(h.stats.ctypes.data, 1, 2, 3, 64, ctypes.byref(t), ctypes.byref(p),
+                                h.loss.ctypes.data, None, None, h.ws.ctypes.data, 8, None) == _abi.CE_EWORKSPACE
+    assert h.untouched()
+
+
+def test_workspace_sizes(lib):
+    h = Host(N=8192, V=128000)
+    x = h.logits(d0=4, d1=2048, s0=2048 * 128000, s1=128000)
+    p = h.params(reduce_loss=1, label_smoothing=0.1)
+    n = lib.ce_workspace_bytes(ctypes.byref(x), ctypes.byref(p))
+    # header + per-row losses + 2 chunks x 4 tagged words per row
+    assert n == 256 + 8192 * 4 + 8192 * 2 * 4 * 8
+    p0 = h.params()
+    x1 = h.logits(d0=2, d1=512, s0=512 * 32000, s1=32000, v_local=32000, vocab_total=32000)
+    assert lib.ce_workspace_bytes(ctypes.byref(x1), ctypes.byref(p0)) == 256
+    assert lib.ce_workspace_bytes(ctypes.byref(h.logits(dtype=9)), ctypes.byref(p0)) == 0
+    assert lib.ce_combine_workspace_bytes(512, ctypes.byref(h.params(reduce_loss=1))) == 256 + 2048
+    # forced split: chunks of at most one workgroup
+    p3 = h.params(split_chunks=3)
+    x2 = h.logits(d0=1, d1=10, s0=40960, s1=4096, v_local=4096, vocab_total=4096)
+    assert lib.ce_workspace_bytes(ctypes.byref(x2), ctypes.byref(p3)) == 256 + (10 * 3 * 4 * 8 + 255) // 256 * 256
+
+
+def test_split_chunks_too_few_rejected(lib):
+    # V = 256000 BF16 rows need at least 4 chunks of 8192 vectors; 2 cannot hold them
+    h = Host()
+    x = h.logits(d0=1, d1=2, s0=512000, s1=256000, v_local=256000, vocab_total=256000)
+    p = h.params(split_chunks=2)
+    rc = lib.ce_fwd_bwd_fused(ctypes.byref(x), ctypes.byref(h.targets()), ctypes.byref(p), None,
+                              h.loss.ctypes.data, None, h.ws.ctypes.data, h.ws.nbytes, None)
+    assert rc == _abi.CE_ELAYOUT
+    assert h.untouched()
+
+
+def test_profile_calls_validate(lib):
+    assert lib.ce_profile_stop(None, 0, None) == _abi.CE_EINVAL
+    assert lib.ce_profile_start(0) == _abi.CE_EINVAL

@@ -1,0 +1,219 @@
+"""MI355X-native fused (vocabulary-parallel) cross-entropy.
+
+Thin Python binding of the C ABI in ``include/ce.h`` (``libce.so``, built by
+``vocab_cross_entropy_amd/csrc/build.py``).  The functions below only marshal torch
+device tensors into the ABI's descriptors and pass torch's current HIP stream;
+every step of the computation runs in the library's gfx950 kernels.  PyTorch
+provides device memory and streams.
+
+Entry points with the C names:
+    ce_forward, ce_backward_inplace, ce_fwd_bwd_fused,
+    ce_shard_partial_stats, ce_shard_combine
+and the interface of the TransformerEngineNPU issue #29 page (section 1):
+    parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False,
+                           dist_process_group=None, ignore_idx=-100)
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+from ._abi import CE_BF16, CE_F32, CeArgumentError, CeError
+
+__all__ = [
+    "ce_forward", "ce_backward_inplace", "ce_fwd_bwd_fused", "ce_shard_partial_stats", "ce_shard_combine",
+    "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_check", "parallel_cross_entropy",
+    "Profiler", "CeError", "CeArgumentError", "lib",
+]
+
+lib = _abi.load()
+
+_ARG_ERRORS = {_abi.CE_EINVAL, _abi.CE_EDTYPE, _abi.CE_ELAYOUT, _abi.CE_EWORKSPACE}
+
+
+def _check(status: int):
+    if status != _abi.CE_OK:
+        detail = lib.ce_last_error().decode(errors="replace")
+        cls = CeArgumentError if status in _ARG_ERRORS else CeError
+        raise cls(status, detail)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return CE_F32
+    if x.dtype == torch.bfloat16:
+        return CE_BF16
+    return -1  # rejected by the library with CE_EDTYPE
+
+
+def logits_desc(x: torch.Tensor, vocab_start: int = 0, vocab_total: int | None = None) -> _abi.CeLogits:
+    """Descriptor of a (d0, d1, V) logits view; columns must be contiguous."""
+    if x.dim() != 3:
+        raise CeArgumentError(_abi.CE_EINVAL, "logits must be a 3-d (d0, d1, V) tensor")
+    if x.stride(2) != 1 and x.shape[2] > 1:
+        raise CeArgumentError(_abi.CE_ELAYOUT, "logits columns must be contiguous (stride 1)")
+    d0, d1, v = x.shape
+    return _abi.CeLogits(x.data_ptr(), _dtype_code(x), 0, d0, d1, x.stride(0), x.stride(1), v, vocab_start,
+                         v if vocab_total is None else vocab_total)
+
+
+def targets_desc(t: torch.Tensor) -> _abi.CeTargets:
+    if t.dim() != 2 or t.dtype != torch.int64:
+        raise CeArgumentError(_abi.CE_EINVAL, "targets must be a 2-d int64 tensor")
+    return _abi.CeTargets(t.data_ptr(), t.stride(0), t.stride(1))
+
+
+def params(label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, split_chunks=0) -> _abi.CeParams:
+    return _abi.CeParams(float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx), int(split_chunks), 0)
+
+
+def _f32(n, device):
+    return torch.empty(n, dtype=torch.float32, device=device)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def ce_workspace_bytes(x: torch.Tensor, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100,
+                       split_chunks=0) -> int:
+    n = lib.ce_workspace_bytes(ctypes.byref(logits_desc(x)),
+                               ctypes.byref(params(label_smoothing, reduce_loss, ignore_idx, split_chunks)))
+    if n == 0:
+        _check(_abi.CE_EINVAL)
+    return int(n)
+
+
+def ce_combine_workspace_bytes(rows: int, reduce_loss=False) -> int:
+    n = lib.ce_combine_workspace_bytes(int(rows), ctypes.byref(params(reduce_loss=reduce_loss)))
+    if n == 0:
+        _check(_abi.CE_EINVAL)
+    return int(n)
+
+
+def ce_forward(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, loss=None, lse=None,
+               n_valid=None, ws=None, want_lse=True):
+    """Forward only.  Returns (loss [N] or [1], lse [N] or None, n_valid [1])."""
+    N = x.shape[0] * x.shape[1]
+    dev = x.device
+    p = params(label_smoothing, reduce_loss, ignore_idx)
+    loss = _f32(1 if reduce_loss else N, dev) if loss is None else loss
+    if lse is None and want_lse:
+        lse = _f32(N, dev)
+    n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
+    xd = logits_desc(x)
+    if ws is None:
+        ws = _workspace(lib.ce_workspace_bytes(ctypes.byref(xd), ctypes.byref(p)), dev)
+    _check(lib.ce_forward(ctypes.byref(xd), ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(loss), _ptr(lse),
+                          _ptr(n_valid), _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, lse, n_valid
+
+
+def ce_backward_inplace(x, t, lse, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, grad_out=None,
+                        n_valid=None, vocab_start=0, vocab_total=None):
+    """Writes the gradient over ``x`` (which may be a vocabulary shard)."""
+    p = params(label_smoothing, reduce_loss, ignore_idx)
+    _check(lib.ce_backward_inplace(ctypes.byref(logits_desc(x, vocab_start, vocab_total)),
+                                   ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(lse), _ptr(grad_out),
+                                   _ptr(n_valid), _stream(x.device)))
+    return x
+
+
+def ce_fwd_bwd_fused(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, grad_out=None, loss=None,
+                     n_valid=None, ws=None, split_chunks=0):
+    """Loss and, in place over ``x``, the gradient.  Returns (loss, n_valid)."""
+    N = x.shape[0] * x.shape[1]
+    dev = x.device
+    p = params(label_smoothing, reduce_loss, ignore_idx, split_chunks)
+    loss = _f32(1 if reduce_loss else N, dev) if loss is None else loss
+    n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
+    xd = logits_desc(x)
+    if ws is None:
+        nb = lib.ce_workspace_bytes(ctypes.byref(xd), ctypes.byref(p))
+        if nb == 0:
+            _check(_abi.CE_EINVAL)
+        ws = _workspace(nb, dev)
+    _check(lib.ce_fwd_bwd_fused(ctypes.byref(xd), ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(grad_out),
+                                _ptr(loss), _ptr(n_valid), _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, n_valid
+
+
+def ce_shard_partial_stats(shard, t, vocab_start, vocab_total, ignore_idx=-100, *, stats=None):
+    """(m, d, y, r) per row of one vocabulary shard, as a [N, 4] FP32 tensor."""
+    N = shard.shape[0] * shard.shape[1]
+    stats = torch.empty((N, 4), dtype=torch.float32, device=shard.device) if stats is None else stats
+    p = params(ignore_idx=ignore_idx)
+    _check(lib.ce_shard_partial_stats(ctypes.byref(logits_desc(shard, vocab_start, vocab_total)),
+                                      ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(stats),
+                                      _stream(shard.device)))
+    return stats
+
+
+def ce_shard_combine(stats, t, vocab_total, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, loss=None,
+                     lse=None, n_valid=None, ws=None):
+    """Combine stats [S, N, 4] into (loss, lse [N], n_valid [1])."""
+    S = stats.shape[0]
+    d0, d1 = t.shape
+    N = d0 * d1
+    dev = stats.device
+    p = params(label_smoothing, reduce_loss, ignore_idx)
+    loss = _f32(1 if reduce_loss else N, dev) if loss is None else loss
+    lse = _f32(N, dev) if lse is None else lse
+    n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
+    if ws is None:
+        ws = _workspace(ce_combine_workspace_bytes(N, reduce_loss), dev)
+    if not stats.is_contiguous():
+        raise CeArgumentError(_abi.CE_ELAYOUT, "stats must be a contiguous [S, N, 4] tensor")
+    _check(lib.ce_shard_combine(_ptr(stats), S, d0, d1, int(vocab_total), ctypes.byref(targets_desc(t)),
+                                ctypes.byref(p), _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(ws), ws.numel(),
+                                _stream(dev)))
+    return loss, lse, n_valid
+
+
+def ce_workspace_check(ws: torch.Tensor):
+    """Raises CeError(CE_EDEADLOCK) if a split row of the last call gave up waiting."""
+    _check(lib.ce_workspace_check(_ptr(ws), _stream(ws.device)))
+
+
+def parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False, dist_process_group=None,
+                           ignore_idx=-100):
+    """The issue #29 interface: FP32 loss; the gradient for an upstream
+    gradient of 1 is staged in place in ``inp`` (in its dtype).
+
+    ``inp`` is (B, SQ, V) or (SQ, B, V) (any row strides, contiguous
+    columns); ``target`` the matching (B, SQ) / (SQ, B) int64 global indices.
+    """
+    if dist_process_group is not None:
+        raise NotImplementedError("vocabulary-parallel process groups need more than one GPU; use "
+                                  "ce_shard_partial_stats / ce_shard_combine / ce_backward_inplace per shard")
+    loss, _ = ce_fwd_bwd_fused(inp, target, label_smoothing, reduce_loss, ignore_idx)
+    return loss[0] if reduce_loss else loss.view(target.shape)
+
+
+class Profiler:
+    """Collects the main-kernel duration (ms) of each of the next calls."""
+
+    def __init__(self, capacity: int):
+        self.capacity = capacity
+        self.ms: list[float] = []
+
+    def __enter__(self):
+        _check(lib.ce_profile_start(self.capacity))
+        return self
+
+    def __exit__(self, *exc):
+        buf = (ctypes.c_float * self.capacity)()
+        n = ctypes.c_int32(0)
+        _check(lib.ce_profile_stop(buf, self.capacity, ctypes.byref(n)))
+        self.ms = [buf[i] for i in range(n.value)]
+        return False

@@ -1,0 +1,55 @@
+"""Build libce.so (the C-ABI library) for gfx950 with hipcc, in-tree.
+
+    python vocab_cross_entropy_amd/csrc/build.py
+
+Objects go to _build/ at the repository root; the shared library lands next
+to this file so that it travels with the source tree.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+CSRC = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.dirname(CSRC)
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libce.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+ARCH = "gfx950"
+COMMON = ["-std=c++17", "-fPIC", "-O3", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall"]
+# Packed FP32 VALU forms are kept out of the device code.
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l and "not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    kobj = os.path.join(BUILD, "ce_kernels.o")
+    aobj = os.path.join(BUILD, "ce_api.o")
+    steps = [
+        [HIPCC, *DEVICE, *COMMON, "-c", os.path.join(CSRC, "ce_kernels.hip"), "-o", kobj],
+        [HIPCC, *COMMON, "-c", os.path.join(CSRC, "ce_api.cpp"), "-o", aobj],
+    ]
+    for cmd in steps:
+        out = _run(cmd)
+        if verbose and out.strip():
+            print(out)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, aobj, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

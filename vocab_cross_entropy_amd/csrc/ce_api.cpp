@@ -1,0 +1,420 @@
+// C ABI of the fused cross-entropy library: argument checks, workspace
+// layout, and the sequence of kernel launches for each entry point.
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and touches no buffer.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "ce.h"
+#include "ce_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ce_status fail(ce_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ce_status hip_fail(hipError_t e, const char* what) {
+  return fail(CE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(int32_t dtype) { return dtype == CE_BF16 ? 2 : 4; }
+
+constexpr int64_t kMaxChunks = 64;
+constexpr int64_t kMaxGrid = 0x7fffffffLL;
+
+// Rows are addressed at i0*s0 + i1*s1; the gradient is written in place, so
+// distinct rows must not overlap: with the non-trivial dims sorted by stride,
+// each stride must clear the extent of everything below it.
+bool rows_disjoint(int64_t d0, int64_t d1, int64_t s0, int64_t s1, int64_t V) {
+  struct Dim {
+    int64_t n, s;
+  } dims[2];
+  int nd = 0;
+  if (d0 > 1) dims[nd++] = {d0, s0};
+  if (d1 > 1) dims[nd++] = {d1, s1};
+  if (nd == 2 && dims[0].s > dims[1].s) {
+    Dim tmp = dims[0];
+    dims[0] = dims[1];
+    dims[1] = tmp;
+  }
+  int64_t extent = V;  // elements spanned by one row
+  for (int i = 0; i < nd; ++i) {
+    if (dims[i].s < extent) return false;
+    if (dims[i].n - 1 > (INT64_MAX - extent) / dims[i].s) return false;
+    extent = dims[i].s * (dims[i].n - 1) + extent;
+  }
+  return true;
+}
+
+ce_status check_params(const ce_params* p) {
+  if (!p) return fail(CE_EINVAL, "params is NULL");
+  const float a = p->label_smoothing;
+  if (!(a >= 0.f && a <= 1.f)) return fail(CE_EINVAL, "label_smoothing %g is outside [0, 1]", (double)a);
+  if (p->reduce_loss != 0 && p->reduce_loss != 1) return fail(CE_EINVAL, "reduce_loss must be 0 or 1");
+  if (p->split_chunks < 0 || p->split_chunks > kMaxChunks)
+    return fail(CE_EINVAL, "split_chunks %d outside [0, %lld]", p->split_chunks, (long long)kMaxChunks);
+  if (p->reserved != 0) return fail(CE_EINVAL, "params.reserved must be 0");
+  return CE_OK;
+}
+
+ce_status check_logits(const ce_logits* x, bool unsharded) {
+  if (!x) return fail(CE_EINVAL, "logits descriptor is NULL");
+  if (x->dtype != CE_F32 && x->dtype != CE_BF16) return fail(CE_EDTYPE, "unsupported logits dtype %d", x->dtype);
+  if (x->reserved != 0) return fail(CE_EINVAL, "logits.reserved must be 0");
+  if (x->d0 < 0 || x->d1 < 1) return fail(CE_EINVAL, "need d0 >= 0 and d1 >= 1 (got %lld, %lld)",
+                                          (long long)x->d0, (long long)x->d1);
+  if (x->v_local < 1) return fail(CE_EINVAL, "v_local must be >= 1");
+  if (x->vocab_start < 0 || x->vocab_total < 1 || x->vocab_start > x->vocab_total - x->v_local)
+    return fail(CE_ELAYOUT, "shard [%lld, %lld) does not fit a vocabulary of %lld", (long long)x->vocab_start,
+                (long long)(x->vocab_start + x->v_local), (long long)x->vocab_total);
+  if (unsharded && (x->vocab_start != 0 || x->v_local != x->vocab_total))
+    return fail(CE_ELAYOUT, "this call needs unsharded logits (vocab_start 0, v_local == vocab_total)");
+  if (x->d0 > 0 && x->d1 > INT64_MAX / x->d0) return fail(CE_EINVAL, "row count overflows");
+  const int64_t N = x->d0 * x->d1;
+  if (N > 0x7fffffffLL) return fail(CE_EINVAL, "more than 2^31-1 rows");
+  if (N > 0 && !x->data) return fail(CE_EINVAL, "logits data is NULL");
+  if (((uintptr_t)x->data) % (uintptr_t)elem_bytes(x->dtype) != 0)
+    return fail(CE_ELAYOUT, "logits pointer is not aligned to its dtype");
+  if (x->s0 < 0 || x->s1 < 0) return fail(CE_ELAYOUT, "negative strides are not supported");
+  if (!rows_disjoint(x->d0, x->d1, x->s0, x->s1, x->v_local))
+    return fail(CE_ELAYOUT, "rows overlap in memory (strides %lld, %lld with %lld columns)", (long long)x->s0,
+                (long long)x->s1, (long long)x->v_local);
+  return CE_OK;
+}
+
+ce_status check_targets(const ce_targets* t, int64_t N) {
+  if (!t) return fail(CE_EINVAL, "targets descriptor is NULL");
+  if (N > 0 && !t->data) return fail(CE_EINVAL, "targets data is NULL");
+  if (((uintptr_t)t->data) % 8u != 0) return fail(CE_ELAYOUT, "targets pointer is not 8-byte aligned");
+  if (t->s0 < 0 || t->s1 < 0) return fail(CE_ELAYOUT, "negative target strides are not supported");
+  return CE_OK;
+}
+
+struct WsLayout {
+  size_t row_loss = 0;  // offset of [N] FP32 per-row losses (reduce only)
+  size_t slots = 0;     // offset of [N][K][4] u64 exchange words (K > 1)
+  int64_t nslots = 0;
+  size_t total = 0;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int64_t N, int32_t K, bool reduce) {
+  WsLayout w;
+  size_t off = vce::kWsHeaderBytes;
+  if (reduce) {
+    w.row_loss = off;
+    off = align256(off + (size_t)N * 4u);
+  }
+  if (K > 1) {
+    w.slots = off;
+    w.nslots = N * K * 4;
+    off = align256(off + (size_t)w.nslots * 8u);
+  }
+  w.total = off;
+  return w;
+}
+
+int32_t chunks_for(const ce_logits* x, const ce_params* p) {
+  int32_t K = p->split_chunks > 0 ? p->split_chunks : vce::fused_auto_chunks(x->dtype, x->v_local);
+  return K < 1 ? 1 : K;
+}
+
+vce::RowLayout row_layout(const ce_logits* x, const ce_targets* t, const ce_params* p) {
+  vce::RowLayout L;
+  L.x = static_cast<char*>(x->data);
+  L.dtype = x->dtype;
+  L.d1 = x->d1;
+  L.s0 = x->s0;
+  L.s1 = x->s1;
+  L.N = x->d0 * x->d1;
+  L.V = x->v_local;
+  L.vocab_start = x->vocab_start;
+  L.vocab_total = x->vocab_total;
+  L.tgt = t->data;
+  L.ts0 = t->s0;
+  L.ts1 = t->s1;
+  L.ignore_idx = p->ignore_idx;
+  L.alpha = p->label_smoothing;
+  return L;
+}
+
+// ---- profiling state (instrumentation only)
+std::mutex g_prof_mu;
+std::vector<hipEvent_t> g_prof_ev;  // pairs
+int32_t g_prof_cap = 0, g_prof_used = 0;
+
+void prof_next(hipEvent_t* e0, hipEvent_t* e1) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  *e0 = *e1 = nullptr;
+  if (g_prof_used < g_prof_cap) {
+    *e0 = g_prof_ev[2 * g_prof_used];
+    *e1 = g_prof_ev[2 * g_prof_used + 1];
+    ++g_prof_used;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ce_abi_version(void) { return CE_ABI_VERSION; }
+
+const char* ce_last_error(void) { return g_err; }
+
+const char* ce_status_string(ce_status s) {
+  switch (s) {
+    case CE_OK: return "CE_OK";
+    case CE_EINVAL: return "CE_EINVAL: invalid argument";
+    case CE_EDTYPE: return "CE_EDTYPE: unsupported dtype";
+    case CE_ELAYOUT: return "CE_ELAYOUT: unsupported layout";
+    case CE_EWORKSPACE: return "CE_EWORKSPACE: workspace missing or too small";
+    case CE_EHIP: return "CE_EHIP: HIP runtime error";
+    case CE_EDEADLOCK: return "CE_EDEADLOCK: split-row exchange gave up waiting";
+  }
+  return "unknown ce_status";
+}
+
+size_t ce_workspace_bytes(const ce_logits* x, const ce_params* p) {
+  if (check_params(p) != CE_OK || check_logits(x, false) != CE_OK) return 0;
+  return ws_layout(x->d0 * x->d1, chunks_for(x, p), p->reduce_loss != 0).total;
+}
+
+size_t ce_combine_workspace_bytes(int64_t rows, const ce_params* p) {
+  if (check_params(p) != CE_OK) return 0;
+  if (rows < 0 || rows > 0x7fffffffLL) {
+    fail(CE_EINVAL, "rows %lld out of range", (long long)rows);
+    return 0;
+  }
+  return ws_layout(rows, 1, p->reduce_loss != 0).total;
+}
+
+ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p, float* loss, float* lse,
+                     int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ce_status st;
+  if ((st = check_params(p)) || (st = check_logits(x, true))) return st;
+  const int64_t N = x->d0 * x->d1;
+  if ((st = check_targets(t, N))) return st;
+  if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
+  const WsLayout w = ws_layout(N, 1, p->reduce_loss != 0);
+  if (!ws || ws_bytes < w.total)
+    return fail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
+  if (((uintptr_t)ws) % 256u) return fail(CE_EWORKSPACE, "workspace must be 256-byte aligned");
+
+  char* wsb = static_cast<char*>(ws);
+  auto* hdr = reinterpret_cast<vce::WsHeader*>(wsb);
+  int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
+  hipError_t e;
+  if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
+    return hip_fail(e, "prologue launch");
+  vce::StatsArgs a;
+  a.L = row_layout(x, t, p);
+  a.mode = vce::kStatsForward;
+  a.row_loss = p->reduce_loss ? reinterpret_cast<float*>(wsb + w.row_loss) : loss;
+  a.lse = lse;
+  a.stats = nullptr;
+  hipEvent_t e0, e1;
+  prof_next(&e0, &e1);
+  if ((e = vce::launch_stats(a, stream, e0, e1))) return hip_fail(e, "forward launch");
+  if (p->reduce_loss && (e = vce::launch_mean(a.row_loss, N, n_out, loss, stream)))
+    return hip_fail(e, "mean launch");
+  return CE_OK;
+}
+
+ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* lse,
+                              const float* grad_out, const int32_t* n_valid, hipStream_t stream) {
+  ce_status st;
+  if ((st = check_params(p)) || (st = check_logits(x, false))) return st;
+  const int64_t N = x->d0 * x->d1;
+  if ((st = check_targets(t, N))) return st;
+  if (N > 0 && !lse) return fail(CE_EINVAL, "lse is NULL");
+  if (p->reduce_loss && !n_valid) return fail(CE_EINVAL, "reduce_loss needs n_valid");
+  vce::BackwardArgs a;
+  a.L = row_layout(x, t, p);
+  a.lse = lse;
+  a.reduce = p->reduce_loss;
+  a.g = grad_out;
+  a.n_valid = n_valid;
+  hipEvent_t e0, e1;
+  prof_next(&e0, &e1);
+  hipError_t e;
+  if ((e = vce::launch_backward(a, stream, e0, e1))) return hip_fail(e, "backward launch");
+  return CE_OK;
+}
+
+ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* grad_out,
+                           float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ce_status st;
+  if ((st = check_params(p)) || (st = check_logits(x, true))) return st;
+  const int64_t N = x->d0 * x->d1;
+  if ((st = check_targets(t, N))) return st;
+  if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
+  const int32_t K = chunks_for(x, p);
+  if (K > kMaxChunks)
+    return fail(CE_ELAYOUT, "rows of %lld columns need %d chunks (at most %lld)", (long long)x->v_local, K,
+                (long long)kMaxChunks);
+  const int64_t nvmax = vce::max_body_vecs(x->dtype, x->v_local);
+  const int64_t C = (nvmax + K - 1) / K;
+  const vce::FusedShape shape = vce::fused_shape_for(C);
+  if (shape.threads == 0)
+    return fail(CE_ELAYOUT, "split_chunks %d leaves %lld vectors per chunk, above one workgroup's %d",
+                p->split_chunks, (long long)C, 512 * 16);
+  if (N * K > kMaxGrid) return fail(CE_EINVAL, "rows x chunks exceeds the launch grid");
+  const WsLayout w = ws_layout(N, K, p->reduce_loss != 0);
+  if (!ws || ws_bytes < w.total)
+    return fail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
+  if (((uintptr_t)ws) % 256u) return fail(CE_EWORKSPACE, "workspace must be 256-byte aligned");
+
+  char* wsb = static_cast<char*>(ws);
+  auto* hdr = reinterpret_cast<vce::WsHeader*>(wsb);
+  int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
+  auto* slots = K > 1 ? reinterpret_cast<unsigned long long*>(wsb + w.slots) : nullptr;
+  hipError_t e;
+  if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, slots, w.nslots,
+                                stream)))
+    return hip_fail(e, "prologue launch");
+  vce::FusedArgs a;
+  a.L = row_layout(x, t, p);
+  a.K = K;
+  a.C = C;
+  a.reduce = p->reduce_loss;
+  a.g = grad_out;
+  a.n_valid = n_out;
+  a.row_loss = p->reduce_loss ? reinterpret_cast<float*>(wsb + w.row_loss) : loss;
+  a.hdr = hdr;
+  a.slots = slots;
+  hipEvent_t e0, e1;
+  prof_next(&e0, &e1);
+  if ((e = vce::launch_fused(a, shape, stream, e0, e1))) return hip_fail(e, "fused launch");
+  if (p->reduce_loss && (e = vce::launch_mean(a.row_loss, N, n_out, loss, stream)))
+    return hip_fail(e, "mean launch");
+  return CE_OK;
+}
+
+ce_status ce_shard_partial_stats(const ce_logits* shard, const ce_targets* t, const ce_params* p, float* stats,
+                                 hipStream_t stream) {
+  ce_status st;
+  if ((st = check_params(p)) || (st = check_logits(shard, false))) return st;
+  const int64_t N = shard->d0 * shard->d1;
+  if ((st = check_targets(t, N))) return st;
+  if (N > 0 && !stats) return fail(CE_EINVAL, "stats is NULL");
+  if (((uintptr_t)stats) % 16u) return fail(CE_ELAYOUT, "stats must be 16-byte aligned");
+  vce::StatsArgs a;
+  a.L = row_layout(shard, t, p);
+  a.mode = vce::kStatsShard;
+  a.row_loss = nullptr;
+  a.lse = nullptr;
+  a.stats = stats;
+  hipEvent_t e0, e1;
+  prof_next(&e0, &e1);
+  hipError_t e;
+  if ((e = vce::launch_stats(a, stream, e0, e1))) return hip_fail(e, "shard stats launch");
+  return CE_OK;
+}
+
+ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1, int64_t vocab_total,
+                           const ce_targets* t, const ce_params* p, float* loss, float* lse, int32_t* n_valid,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  ce_status st;
+  if ((st = check_params(p))) return st;
+  if (S < 1) return fail(CE_EINVAL, "S must be >= 1");
+  if (d0 < 0 || d1 < 1) return fail(CE_EINVAL, "need d0 >= 0 and d1 >= 1");
+  if (vocab_total < 1) return fail(CE_EINVAL, "vocab_total must be >= 1");
+  if (d0 > 0 && d1 > 0x7fffffffLL / d0) return fail(CE_EINVAL, "more than 2^31-1 rows");
+  const int64_t N = d0 * d1;
+  if ((st = check_targets(t, N))) return st;
+  if (N > 0 && !stats) return fail(CE_EINVAL, "stats is NULL");
+  if (((uintptr_t)stats) % 16u) return fail(CE_ELAYOUT, "stats must be 16-byte aligned");
+  if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
+  const WsLayout w = ws_layout(N, 1, p->reduce_loss != 0);
+  if (!ws || ws_bytes < w.total)
+    return fail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
+  if (((uintptr_t)ws) % 256u) return fail(CE_EWORKSPACE, "workspace must be 256-byte aligned");
+
+  char* wsb = static_cast<char*>(ws);
+  auto* hdr = reinterpret_cast<vce::WsHeader*>(wsb);
+  int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
+  hipError_t e;
+  if ((e = vce::launch_prologue(t->data, t->s0, t->s1, d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
+    return hip_fail(e, "prologue launch");
+  vce::CombineArgs a;
+  a.stats = stats;
+  a.S = S;
+  a.N = N;
+  a.d1 = d1;
+  a.vocab_total = vocab_total;
+  a.tgt = t->data;
+  a.ts0 = t->s0;
+  a.ts1 = t->s1;
+  a.ignore_idx = p->ignore_idx;
+  a.alpha = p->label_smoothing;
+  a.row_loss = p->reduce_loss ? reinterpret_cast<float*>(wsb + w.row_loss) : loss;
+  a.lse = lse;
+  if ((e = vce::launch_combine(a, stream))) return hip_fail(e, "combine launch");
+  if (p->reduce_loss && (e = vce::launch_mean(a.row_loss, N, n_out, loss, stream)))
+    return hip_fail(e, "mean launch");
+  return CE_OK;
+}
+
+ce_status ce_workspace_check(const void* ws, hipStream_t stream) {
+  if (!ws) return fail(CE_EINVAL, "workspace is NULL");
+  hipError_t e;
+  if ((e = hipStreamSynchronize(stream))) return hip_fail(e, "stream synchronize");
+  vce::WsHeader h;
+  if ((e = hipMemcpy(&h, ws, sizeof h, hipMemcpyDeviceToHost))) return hip_fail(e, "workspace read");
+  if (h.status) return fail(CE_EDEADLOCK, "a split row gave up waiting for its partner chunks");
+  return CE_OK;
+}
+
+ce_status ce_profile_start(int32_t capacity) {
+  if (capacity < 1 || capacity > (1 << 20)) return fail(CE_EINVAL, "capacity out of range");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (g_prof_cap) return fail(CE_EINVAL, "profiling already started");
+  g_prof_ev.assign(2 * (size_t)capacity, nullptr);
+  for (auto& ev : g_prof_ev) {
+    hipError_t e = hipEventCreate(&ev);
+    if (e) {
+      for (auto& x : g_prof_ev)
+        if (x) (void)hipEventDestroy(x);
+      g_prof_ev.clear();
+      return hip_fail(e, "event create");
+    }
+  }
+  g_prof_cap = capacity;
+  g_prof_used = 0;
+  return CE_OK;
+}
+
+ce_status ce_profile_stop(float* ms, int32_t cap, int32_t* count) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_cap) return fail(CE_EINVAL, "profiling was not started");
+  ce_status st = CE_OK;
+  int32_t n = 0;
+  for (int32_t i = 0; i < g_prof_used; ++i) {
+    hipError_t e = hipEventSynchronize(g_prof_ev[2 * i + 1]);
+    float v = 0.f;
+    if (!e) e = hipEventElapsedTime(&v, g_prof_ev[2 * i], g_prof_ev[2 * i + 1]);
+    if (e && st == CE_OK) st = hip_fail(e, "event elapsed time");
+    if (ms && n < cap) ms[n++] = v;
+  }
+  for (auto& ev : g_prof_ev) (void)hipEventDestroy(ev);
+  g_prof_ev.clear();
+  g_prof_cap = g_prof_used = 0;
+  if (count) *count = n;
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal interface between the C ABI layer (ce_api.cpp) and the gfx950
+// kernels (ce_kernels.hip).  Host-side only types; no torch, no allocation.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace vce {
+
+// Workspace header (first 256 bytes of every workspace).
+struct WsHeader {
+  unsigned long long ticket;  // split rows: next (row, chunk) work item
+  uint32_t status;            // nonzero: an exchange wait gave up
+  int32_t n_valid;            // count of non-ignored rows when the caller passed no n_valid
+};
+constexpr size_t kWsHeaderBytes = 256;
+
+// Which template instance of the fused kernel a plan uses.
+struct FusedShape {
+  int threads;      // workgroup size T
+  int vecs;         // 16-byte vectors held per thread P
+};
+
+struct RowLayout {
+  char* x;                 // logits base (element (0,0,0))
+  int32_t dtype;           // CE_F32 / CE_BF16
+  int64_t d1, s0, s1;      // logical dim and element strides
+  int64_t N;               // rows
+  int64_t V;               // columns in this buffer (v_local)
+  int64_t vocab_start, vocab_total;
+  const int64_t* tgt;
+  int64_t ts0, ts1;
+  int64_t ignore_idx;
+  float alpha;
+};
+
+struct FusedArgs {
+  RowLayout L;
+  int32_t K;               // chunks per row
+  int64_t C;               // body vectors per chunk
+  int32_t reduce;          // mean over non-ignored rows
+  const float* g;          // upstream gradient ([N] or [1]); NULL = 1
+  const int32_t* n_valid;  // device count (read when reduce)
+  float* row_loss;         // [N]: loss output (reduce 0) or per-row scratch (reduce 1)
+  WsHeader* hdr;
+  unsigned long long* slots;  // [N][K][4] tagged exchange words (K > 1)
+};
+
+enum StatsMode { kStatsForward = 0, kStatsShard = 1 };
+
+struct StatsArgs {
+  RowLayout L;
+  int32_t mode;
+  float* row_loss;  // forward: loss [N] or per-row scratch
+  float* lse;       // forward: may be NULL
+  float* stats;     // shard: [N][4]
+};
+
+struct BackwardArgs {
+  RowLayout L;
+  const float* lse;
+  int32_t reduce;
+  const float* g;
+  const int32_t* n_valid;
+};
+
+struct CombineArgs {
+  const float* stats;
+  int32_t S;
+  int64_t N, d1, vocab_total;
+  const int64_t* tgt;
+  int64_t ts0, ts1, ignore_idx;
+  float alpha;
+  float* row_loss;
+  float* lse;
+};
+
+// Shape choice for the fused kernel (host side, no HIP calls).
+FusedShape fused_shape_for(int64_t body_vecs_per_chunk);
+int64_t max_body_vecs(int32_t dtype, int64_t V);
+int32_t fused_auto_chunks(int32_t dtype, int64_t V);
+
+// Launchers: enqueue on `stream`, return the hipError_t of the launch.
+hipError_t launch_prologue(const int64_t* tgt, int64_t ts0, int64_t ts1, int64_t d1, int64_t N,
+                           int64_t ignore_idx, int32_t* n_out, WsHeader* hdr, unsigned long long* slots,
+                           int64_t nslots, hipStream_t stream);
+hipError_t launch_fused(const FusedArgs& a, FusedShape shape, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_stats(const StatsArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out, hipStream_t stream);
+
+}  // namespace vce

@@ -1,0 +1,794 @@
+// gfx950 kernels of the fused (vocabulary-parallel) cross-entropy library.
+//
+// Arithmetic (per row of logits x, target t, smoothing a, V = vocab_total):
+//   lse  = log sum_j exp(x_j)                       (FP32 accumulation)
+//   loss = lse - (1 - a) x_t - (a / V) sum_j x_j
+//   grad_j = s (exp(x_j - lse) - a / V - (1 - a) [j == t])
+// -- the log_softmax + NLL identity and the softmax-minus-onehot gradient of
+// the CANN ops-nn fusion page ("fusion scheme", "backward", smoothing per its
+// "pitfall 3" read with the uniform a/V of torch's F.cross_entropy), the
+// in-place gradient staging of TransformerEngineNPU issue #29 (section 6),
+// and the per-shard (max, sum-exp, target logit) exchange of hyper-parallel
+// issue #269 (section 3.1) extended with the row sum that a > 0 needs.
+//
+// Exponentials are taken in base 2 on the hardware v_exp_f32: with
+// u = x * log2(e), lse = ln2 * (m2 + log2 sum_j 2^(u_j - m2)) for any m2, and
+// m2 = fl(max_j x_j * log2 e) keeps every term <= 1 (the max-shift of the
+// ops-nn page's "pitfall 1").
+//
+// Layout: logical row r = i0 * d1 + i1 starts at element i0*s0 + i1*s1; its
+// columns are contiguous.  Each row is cut into a head of up to 15 bytes that
+// precedes the first 16-byte boundary, a body of 16-byte vectors and a tail
+// of fewer than 16 bytes, so every body access is one coalesced 128-bit load
+// or store whatever the row's alignment.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ce.h"
+#include "ce_internal.h"
+
+namespace vce {
+namespace {
+
+constexpr float kL = 1.44269504088896340736f;     // log2(e)
+constexpr float kLn2 = 0.69314718055994530942f;  // ln(2)
+// High half of a published exchange word; a cleared word never carries it.
+constexpr uint32_t kTagHi = 0x5EEDC0DEu;
+// Bound on polling iterations of one lane waiting for a partner chunk
+// (each iteration sleeps ~128 cycles: ~0.2 s in total), after which the
+// row is finished with NaN and the workspace status word is set.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+template <int DT>
+struct ElemT;
+template <>
+struct ElemT<CE_BF16> {
+  static constexpr int E = 8;   // elements per 16-byte vector
+  static constexpr int EB = 2;  // bytes per element
+};
+template <>
+struct ElemT<CE_F32> {
+  static constexpr int E = 4;
+  static constexpr int EB = 4;
+};
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// FP32 pair -> packed BF16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  f2 in = {lo, hi};
+  b2 out = __builtin_convertvector(in, b2);
+  return __builtin_bit_cast(uint32_t, out);
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack(const uint4& v, float (&f)[ElemT<DT>::E]) {
+  if constexpr (DT == CE_BF16) {
+    f[0] = bf_lo(v.x); f[1] = bf_hi(v.x);
+    f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+    f[4] = bf_lo(v.z); f[5] = bf_hi(v.z);
+    f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+  } else {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 pack(const float (&f)[ElemT<DT>::E]) {
+  if constexpr (DT == CE_BF16) {
+    return make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
+  } else {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+}
+
+// A vector whose elements are all -inf (neutral for max and for sum-exp).
+template <int DT>
+__device__ __forceinline__ uint4 neg_inf_vec() {
+  const uint32_t w = (DT == CE_BF16) ? 0xFF80FF80u : 0xFF800000u;
+  return make_uint4(w, w, w, w);
+}
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const char* base, int64_t j) {
+  if constexpr (DT == CE_BF16) {
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[j] << 16);
+  } else {
+    return reinterpret_cast<const float*>(base)[j];
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(char* base, int64_t j, float g) {
+  if constexpr (DT == CE_BF16) {
+    reinterpret_cast<uint16_t*>(base)[j] = (uint16_t)(pack_bf16(g, 0.f) & 0xffffu);
+  } else {
+    reinterpret_cast<float*>(base)[j] = g;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float extract(const uint4& v, int e) {
+  float f[ElemT<DT>::E];
+  unpack<DT>(v, f);
+  float r = f[0];
+#pragma unroll
+  for (int i = 1; i < ElemT<DT>::E; ++i) r = (e == i) ? f[i] : r;
+  return r;
+}
+
+// exp(x - lse) from the base-2 lse split c_hi + c_lo.  For BF16 gradients the
+// low part is far below their rounding and is dropped.
+template <int DT>
+__device__ __forceinline__ float softmax_term(float x, float c_hi, float c_lo) {
+  if constexpr (DT == CE_BF16) {
+    return ex2(__builtin_fmaf(x, kL, -c_hi));
+  } else {
+    return ex2(__builtin_fmaf(x, kL, -c_hi) - c_lo);
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Workgroup reductions in a fixed order (deterministic, uniform result).
+template <int T>
+__device__ __forceinline__ float block_max(float v, float (*sh)[4]) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh[w][0] = v;
+  __syncthreads();
+  float r = sh[0][0];
+#pragma unroll
+  for (int i = 1; i < T / 64; ++i) r = fmaxf(r, sh[i][0]);
+  __syncthreads();
+  return r;
+}
+
+template <int T>
+__device__ __forceinline__ void block_sum3(float& a, float& b, float& c, float (*sh)[4]) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  c = wave_sum(c);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sh[w][0] = a;
+    sh[w][1] = b;
+    sh[w][2] = c;
+  }
+  __syncthreads();
+  a = sh[0][0];
+  b = sh[0][1];
+  c = sh[0][2];
+#pragma unroll
+  for (int i = 1; i < T / 64; ++i) {
+    a += sh[i][0];
+    b += sh[i][1];
+    c += sh[i][2];
+  }
+  __syncthreads();
+}
+
+// Geometry of one logical row.
+template <int DT>
+struct Row {
+  char* base;     // element 0
+  int64_t h;      // head elements before the first 16-byte boundary
+  int64_t nv;     // body vectors
+  int tn;         // tail elements
+  uint4* body;    // first body vector
+  char* tail;     // first tail element
+  int64_t t;      // target (global index)
+};
+
+template <int DT>
+__device__ __forceinline__ Row<DT> row_geometry(const RowLayout& L, int64_t r) {
+  constexpr int E = ElemT<DT>::E, EB = ElemT<DT>::EB;
+  Row<DT> g;
+  const int64_t i0 = r / L.d1, i1 = r - i0 * L.d1;
+  g.t = L.tgt[i0 * L.ts0 + i1 * L.ts1];
+  g.base = L.x + (i0 * L.s0 + i1 * L.s1) * EB;
+  int64_t h = (int64_t)(((16u - ((uint32_t)(uintptr_t)g.base & 15u)) & 15u) / EB);
+  g.h = h > L.V ? L.V : h;
+  g.nv = (L.V - g.h) / E;
+  g.tn = (int)(L.V - g.h - g.nv * E);
+  g.body = reinterpret_cast<uint4*>(g.base + g.h * EB);
+  g.tail = g.base + (g.h + g.nv * E) * EB;
+  return g;
+}
+
+// Upstream gradient scale s of row r.
+__device__ __forceinline__ float grad_scale(int32_t reduce, const float* g, const int32_t* n_valid, int64_t r) {
+  if (reduce) return (g ? g[0] : 1.f) / (float)(*n_valid);
+  return g ? g[r] : 1.f;
+}
+
+// --------------------------------------------------------------------------
+// Prologue: n = #{rows with target != ignore_idx} (block 0), and clearing of
+// the split-row exchange words and the ticket counter (other blocks).
+__global__ __launch_bounds__(1024) void k_prologue(const int64_t* tgt, int64_t ts0, int64_t ts1, int64_t d1,
+                                                   int64_t N, int64_t ignore_idx, int32_t* n_out, WsHeader* hdr,
+                                                   unsigned long long* slots, int64_t nslots) {
+  if (blockIdx.x == 0) {
+    __shared__ int sh[16];
+    int cnt = 0;
+    for (int64_t r = threadIdx.x; r < N; r += 1024) {
+      const int64_t i0 = r / d1, i1 = r - i0 * d1;
+      cnt += tgt[i0 * ts0 + i1 * ts1] != ignore_idx;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int n = 0;
+      for (int i = 0; i < 16; ++i) n += sh[i];
+      *n_out = n;
+      if (hdr) {
+        hdr->ticket = 0ull;
+        hdr->status = 0u;
+      }
+    }
+  } else {
+    const int64_t stride = (int64_t)(gridDim.x - 1) * 1024;
+    for (int64_t i = (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x; i < nslots; i += stride) slots[i] = 0ull;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Fused forward + backward.  One workgroup per (row, chunk); the chunk's
+// body vectors live in registers (P per thread) between the statistics pass
+// and the gradient pass, so the logits are read from HBM once and the
+// gradient is written once.  With K > 1 chunks per row, every chunk publishes
+// (m2, d_excl, y, r) as tagged 64-bit words, waits for its partners, and all
+// chunks combine the K tuples in chunk order, so they agree bit for bit on
+// the row's lse.  Work items come from an atomic ticket, so the chunks of a
+// row are claimed by workgroups that are already running: every chunk a
+// workgroup waits for is held by a running workgroup or will be claimed by
+// the next one to start, which keeps the wait finite.
+template <int DT, int T, int P>
+__global__ __launch_bounds__(T) void k_fused(FusedArgs a) {
+  constexpr int E = ElemT<DT>::E;
+  __shared__ float sh[T / 64][4];
+  __shared__ float xs[64 * 4];
+  __shared__ unsigned long long s_item;
+  const int tid = threadIdx.x;
+  const RowLayout& L = a.L;
+  const int K = a.K;
+
+  int64_t item = blockIdx.x;
+  if (K > 1) {
+    if (tid == 0) s_item = atomicAdd(&a.hdr->ticket, 1ull);
+    __syncthreads();
+    item = (int64_t)s_item;
+  }
+  const int64_t r = item / K;
+  const int k = (int)(item - r * K);
+  if (r >= L.N) return;
+
+  const Row<DT> g = row_geometry<DT>(L, r);
+  const int64_t cb = (int64_t)k * a.C;
+  const int64_t cend = g.nv < cb + a.C ? g.nv : cb + a.C;
+  const int nvc = cend > cb ? (int)(cend - cb) : 0;
+  uint4* body = g.body + cb;
+  const bool first = (k == 0), last = (k == K - 1);
+
+  if (g.t == L.ignore_idx) {  // ignored row: +0.0 gradient, loss 0, nothing read
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < nvc; i += T) body[i] = z;
+    if (first && tid < g.h) store_elem<DT>(g.base, tid, 0.f);
+    if (last && tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
+    if (first && tid == 0) a.row_loss[r] = 0.f;
+    return;
+  }
+
+  // ---- the single read of this chunk
+  uint4 v[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int i = j * T + tid;
+    v[j] = (i < nvc) ? body[i] : neg_inf_vec<DT>();
+  }
+  const bool hv = first && tid < g.h, tv = last && tid < g.tn;
+  const float hx = hv ? load_elem<DT>(g.base, tid) : -INFINITY;
+  const float tx = tv ? load_elem<DT>(g.tail, tid) : -INFINITY;
+
+  // ---- which thread / vector / element of this chunk holds the target
+  const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
+  int own_tid = -1, own_j = -1, own_e = 0, own_where = 0;  // 1 head, 2 body, 3 tail
+  if (tvalid) {
+    const int64_t tl = g.t - L.vocab_start;
+    if (tl < g.h) {
+      if (first) {
+        own_where = 1;
+        own_tid = (int)tl;
+      }
+    } else {
+      const int64_t c = tl - g.h;
+      if (c < g.nv * E) {
+        const int64_t vec = c / E;
+        if (vec >= cb && vec < cend) {
+          const int vi = (int)(vec - cb);
+          own_where = 2;
+          own_j = vi / T;
+          own_tid = vi - own_j * T;
+          own_e = (int)(c - vec * E);
+        }
+      } else if (last) {
+        own_where = 3;
+        own_tid = (int)(c - g.nv * E);
+      }
+    }
+  }
+  float y = 0.f;
+  if (tid == own_tid) {
+    if (own_where == 1) {
+      y = hx;
+    } else if (own_where == 3) {
+      y = tx;
+    } else {
+#pragma unroll
+      for (int j = 0; j < P; ++j)
+        if (j == own_j) y = extract<DT>(v[j], own_e);
+    }
+  }
+
+  // ---- statistics: max, then sum of 2^(x log2e - m2), row sum
+  float m = fmaxf(hx, tx);
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    float f[E];
+    unpack<DT>(v[j], f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) m = fmaxf(m, f[e]);
+  }
+  m = block_max<T>(m, sh);
+  const float m2 = m * kL;
+  const float msub = (m == -INFINITY) ? 0.f : m2;
+
+  // The target's own term is left out of the sum (and rebuilt from its logit
+  // after the reduction), so that 1 - p_t = D_excl / D stays accurate when
+  // the target holds almost all of the probability.
+  const bool own_head = (own_where == 1 && tid == own_tid), own_tail = (own_where == 3 && tid == own_tid);
+  float d0 = own_head ? 0.f : ex2(__builtin_fmaf(hx, kL, -msub));
+  float d1 = own_tail ? 0.f : ex2(__builtin_fmaf(tx, kL, -msub));
+  float rs = 0.f;
+  const bool smooth = L.alpha != 0.f;
+  if (smooth) rs = (hv ? hx : 0.f) + (tv ? tx : 0.f);
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    float f[E];
+    unpack<DT>(v[j], f);
+    float tm[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) tm[e] = ex2(__builtin_fmaf(f[e], kL, -msub));
+    if (j == own_j && tid == own_tid) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) tm[e] = (e == own_e) ? 0.f : tm[e];
+    }
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      d0 += tm[e];
+      d1 += tm[e + 1];
+    }
+    if (smooth) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) part += f[e];
+      rs += (j * T + tid < nvc) ? part : 0.f;
+    }
+  }
+  float d = d0 + d1;
+  block_sum3<T>(d, y, rs, sh);
+
+  // ---- exchange between the chunks of a split row
+  float M2 = m2, D = d, Y = y, R = rs;
+  if (K > 1) {
+    unsigned long long* row_slots = a.slots + (size_t)r * (size_t)K * 4u;
+    if (tid == 0) {
+      const float mine[4] = {m2, d, y, rs};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __hip_atomic_store(row_slots + 4 * k + q, ((unsigned long long)kTagHi << 32) | __float_as_uint(mine[q]),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid < 64) {
+      uint32_t spins = 0;
+      bool gave_up = false;
+      for (int w = tid; w < 4 * K; w += 64) {
+        unsigned long long val = 0ull;
+        for (;;) {
+          val = __hip_atomic_load(row_slots + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((uint32_t)(val >> 32) == kTagHi) break;
+          if (++spins > kSpinLimit) {
+            gave_up = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        xs[w] = gave_up ? __uint_as_float(0x7fc00000u) : __uint_as_float((uint32_t)val);
+      }
+      if (gave_up) atomicOr(&a.hdr->status, 1u);
+    }
+    __syncthreads();
+    M2 = -INFINITY;
+    for (int q = 0; q < K; ++q) M2 = fmaxf(M2, xs[4 * q]);
+    D = 0.f;
+    Y = 0.f;
+    R = 0.f;
+    for (int q = 0; q < K; ++q) {
+      const float mq = xs[4 * q];
+      D += (mq == -INFINITY) ? 0.f : xs[4 * q + 1] * ex2(mq - M2);
+      Y += xs[4 * q + 2];
+      R += xs[4 * q + 3];
+    }
+  }
+
+  // ---- sum with the target term restored, lse (base 2, split into hi + lo
+  // by an exact two-sum), loss
+  const float e_t = tvalid ? ex2(__builtin_fmaf(Y, kL, -M2)) : 0.f;
+  const float Dt = D + e_t;
+  const float lgD = lg2(Dt);
+  const float c_hi = M2 + lgD;
+  const float bb = c_hi - M2;
+  const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
+  const float inv_v = 1.f / (float)L.vocab_total;
+  if (first && tid == 0) {
+    const float lse = c_hi * kLn2 + c_lo * kLn2;
+    float loss = lse - (1.f - L.alpha) * Y - (L.alpha * inv_v) * R;
+    a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
+  }
+
+  // ---- gradient from the registers, written over the logits
+  float s = grad_scale(a.reduce, a.g, a.n_valid, r);
+  if (!tvalid) s = __uint_as_float(0x7fc00000u);
+  const float b = -s * (L.alpha * inv_v);
+  // target element: s (p_t - a/V - (1 - a)) = s ((a - a/V) - (1 - p_t)), 1 - p_t = D_excl / D
+  const float g_t = s * ((L.alpha - L.alpha * inv_v) - D / Dt);
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int i = j * T + tid;
+    float f[E];
+    unpack<DT>(v[j], f);
+    float gr[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(softmax_term<DT>(f[e], c_hi, c_lo), s, b);
+    if (j == own_j && tid == own_tid) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) gr[e] = (e == own_e) ? g_t : gr[e];
+    }
+    if (i < nvc) body[i] = pack<DT>(gr);
+  }
+  if (hv) store_elem<DT>(g.base, tid, own_head ? g_t : __builtin_fmaf(softmax_term<DT>(hx, c_hi, c_lo), s, b));
+  if (tv) store_elem<DT>(g.tail, tid, own_tail ? g_t : __builtin_fmaf(softmax_term<DT>(tx, c_hi, c_lo), s, b));
+}
+
+// --------------------------------------------------------------------------
+// Streaming statistics of whole rows (forward) or of shard rows.  Each thread
+// keeps an online (max, sum) pair, rescaled once per batch of PB vectors.
+template <int DT, int T, int PB>
+__global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
+  constexpr int E = ElemT<DT>::E;
+  __shared__ float sh[T / 64][4];
+  const int tid = threadIdx.x;
+  const RowLayout& L = a.L;
+  for (int64_t r = blockIdx.x; r < L.N; r += gridDim.x) {
+    const Row<DT> g = row_geometry<DT>(L, r);
+    if (g.t == L.ignore_idx) {
+      if (tid == 0) {
+        if (a.mode == kStatsForward) {
+          a.row_loss[r] = 0.f;
+          if (a.lse) a.lse[r] = 0.f;
+        } else {
+          reinterpret_cast<float4*>(a.stats)[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+      continue;
+    }
+    const bool hv = tid < g.h, tv = tid < g.tn;
+    const float hx = hv ? load_elem<DT>(g.base, tid) : -INFINITY;
+    const float tx = tv ? load_elem<DT>(g.tail, tid) : -INFINITY;
+    float m = fmaxf(hx, tx);
+    float m2 = m * kL;
+    float msub = (m == -INFINITY) ? 0.f : m2;
+    float d = ex2(__builtin_fmaf(hx, kL, -msub)) + ex2(__builtin_fmaf(tx, kL, -msub));
+    float rs = (hv ? hx : 0.f) + (tv ? tx : 0.f);
+    for (int64_t base = 0; base < g.nv; base += (int64_t)T * PB) {
+      uint4 v[PB];
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const int64_t i = base + j * T + tid;
+        v[j] = (i < g.nv) ? g.body[i] : neg_inf_vec<DT>();
+      }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        float f[E];
+        unpack<DT>(v[j], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) bm = fmaxf(bm, f[e]);
+      }
+      if (bm > m) {
+        const float bm2 = bm * kL;
+        d *= ex2(m2 - bm2);
+        m = bm;
+        m2 = bm2;
+        msub = m2;
+      }
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        float f[E];
+        unpack<DT>(v[j], f);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          d += ex2(__builtin_fmaf(f[e], kL, -msub));
+          part += f[e];
+        }
+        rs += (base + j * T + tid < g.nv) ? part : 0.f;
+      }
+    }
+    const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
+    const int64_t tl = g.t - L.vocab_start;
+    const bool owns = tvalid && tl >= 0 && tl < L.V;
+    float y = (tid == 0 && owns) ? load_elem<DT>(g.base, tl) : 0.f;
+
+    const float M = block_max<T>(m, sh);
+    const float M2 = M * kL;
+    float dadj = (m == -INFINITY) ? 0.f : d * ex2(m2 - M2);
+    block_sum3<T>(dadj, y, rs, sh);
+    if (tid == 0) {
+      if (a.mode == kStatsForward) {
+        const float lgD = lg2(dadj);
+        const float c_hi = M2 + lgD;
+        const float bb = c_hi - M2;
+        const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
+        const float lse = c_hi * kLn2 + c_lo * kLn2;
+        const float loss = lse - (1.f - L.alpha) * y - (L.alpha / (float)L.vocab_total) * rs;
+        a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
+        if (a.lse) a.lse[r] = tvalid ? lse : __uint_as_float(0x7fc00000u);
+      } else {
+        // natural-units sum: sum exp(x - M) = dadj * 2^(M2 - M log2e)
+        const float dn = (M == -INFINITY) ? 0.f : dadj * ex2(-__builtin_fmaf(M, kL, -M2));
+        reinterpret_cast<float4*>(a.stats)[r] = make_float4(M, dn, y, rs);
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Streaming in-place backward from a given lse[N]; works on shards.
+template <int DT, int T, int PB>
+__global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
+  constexpr int E = ElemT<DT>::E;
+  const int tid = threadIdx.x;
+  const RowLayout& L = a.L;
+  const float inv_v = 1.f / (float)L.vocab_total;
+  for (int64_t r = blockIdx.x; r < L.N; r += gridDim.x) {
+    const Row<DT> g = row_geometry<DT>(L, r);
+    if (g.t == L.ignore_idx) {
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      for (int64_t i = tid; i < g.nv; i += T) g.body[i] = z;
+      if (tid < g.h) store_elem<DT>(g.base, tid, 0.f);
+      if (tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
+      continue;
+    }
+    const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
+    const int64_t tl = tvalid ? g.t - L.vocab_start : -1;  // may fall outside this shard
+    const float lse = a.lse[r];
+    const float c_hi = lse * kL;
+    const float c_lo = __builtin_fmaf(lse, kL, -c_hi);
+    float s = grad_scale(a.reduce, a.g, a.n_valid, r);
+    if (!tvalid) s = __uint_as_float(0x7fc00000u);
+    const float b = -s * (L.alpha * inv_v);
+    const float a_rest = L.alpha - L.alpha * inv_v;
+    if (tid < g.h) {
+      const float xv = load_elem<DT>(g.base, tid);
+      float gg = __builtin_fmaf(ex2(__builtin_fmaf(xv, kL, -c_hi) - c_lo), s, b);
+      if (tl == tid) gg = s * (expm1f(xv - lse) + a_rest);
+      store_elem<DT>(g.base, tid, gg);
+    }
+    if (tid < g.tn) {
+      const float xv = load_elem<DT>(g.tail, tid);
+      float gg = __builtin_fmaf(ex2(__builtin_fmaf(xv, kL, -c_hi) - c_lo), s, b);
+      if (tl == g.h + g.nv * E + tid) gg = s * (expm1f(xv - lse) + a_rest);
+      store_elem<DT>(g.tail, tid, gg);
+    }
+    for (int64_t base = 0; base < g.nv; base += (int64_t)T * PB) {
+      uint4 v[PB];
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const int64_t i = base + j * T + tid;
+        if (i < g.nv) v[j] = g.body[i];
+      }
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        const int64_t i = base + j * T + tid;
+        if (i < g.nv) {
+          float f[E];
+          unpack<DT>(v[j], f);
+          float gr[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(ex2(__builtin_fmaf(f[e], kL, -c_hi) - c_lo), s, b);
+          const uint64_t off = (uint64_t)(tl - (g.h + i * E));
+          if (off < (uint64_t)E) {
+            // target: s (p_t - 1 + a - a/V) with p_t - 1 = expm1(x_t - lse), no rounding of p_t first
+#pragma unroll
+            for (int e = 0; e < E; ++e) gr[e] = (e == (int)off) ? s * (expm1f(f[e] - lse) + a_rest) : gr[e];
+          }
+          g.body[i] = pack<DT>(gr);
+        }
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Combine of S shards' (m, d, y, r): one thread per row, shards in order.
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= a.N) return;
+  const int64_t i0 = r / a.d1, i1 = r - i0 * a.d1;
+  const int64_t t = a.tgt[i0 * a.ts0 + i1 * a.ts1];
+  if (t == a.ignore_idx) {
+    a.row_loss[r] = 0.f;
+    if (a.lse) a.lse[r] = 0.f;
+    return;
+  }
+  const float4* st = reinterpret_cast<const float4*>(a.stats);
+  float M = -INFINITY;
+  for (int s = 0; s < a.S; ++s) M = fmaxf(M, st[(int64_t)s * a.N + r].x);
+  float D = 0.f, Y = 0.f, R = 0.f;
+  for (int s = 0; s < a.S; ++s) {
+    const float4 q = st[(int64_t)s * a.N + r];
+    D += (q.x == -INFINITY) ? 0.f : q.y * ex2((q.x - M) * kL);
+    Y += q.z;
+    R += q.w;
+  }
+  const float lse = M + lg2(D) * kLn2;
+  const float loss = lse - (1.f - a.alpha) * Y - (a.alpha / (float)a.vocab_total) * R;
+  const bool tvalid = t >= 0 && t < a.vocab_total;
+  a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
+  if (a.lse) a.lse[r] = tvalid ? lse : __uint_as_float(0x7fc00000u);
+}
+
+// --------------------------------------------------------------------------
+// Mean over non-ignored rows: sum of per-row losses in FP64, fixed order.
+__global__ __launch_bounds__(1024) void k_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out) {
+  __shared__ double sh[16];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < N; i += 1024) s += (double)row_loss[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int i = 0; i < 16; ++i) tot += sh[i];
+    out[0] = (float)(tot / (double)(*n_valid));  // n = 0 gives 0/0 = NaN
+  }
+}
+
+template <int DT, int T, int P>
+hipError_t launch_fused_t(const FusedArgs& a, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((k_fused<DT, T, P>), dim3((uint32_t)grid), dim3(T), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_fused_dt(const FusedArgs& a, FusedShape shape, int64_t grid, hipStream_t stream) {
+  if (shape.threads == 512 && shape.vecs == 16) return launch_fused_t<DT, 512, 16>(a, grid, stream);
+  if (shape.threads == 256) {
+    switch (shape.vecs) {
+      case 1: return launch_fused_t<DT, 256, 1>(a, grid, stream);
+      case 2: return launch_fused_t<DT, 256, 2>(a, grid, stream);
+      case 4: return launch_fused_t<DT, 256, 4>(a, grid, stream);
+      case 8: return launch_fused_t<DT, 256, 8>(a, grid, stream);
+      case 16: return launch_fused_t<DT, 256, 16>(a, grid, stream);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+constexpr int kStreamT = 256;
+constexpr int kStreamPB = 4;
+
+int64_t stream_grid(int64_t N) { return N < (1 << 20) ? N : (1 << 20); }
+
+}  // namespace
+
+// Shapes available to the fused kernel, smallest capacity first.
+static const FusedShape kShapes[] = {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {256, 16}, {512, 16}};
+
+FusedShape fused_shape_for(int64_t vecs) {
+  for (const FusedShape& s : kShapes)
+    if ((int64_t)s.threads * s.vecs >= vecs) return s;
+  return FusedShape{0, 0};
+}
+
+int64_t max_body_vecs(int32_t dtype, int64_t V) { return V / (dtype == CE_BF16 ? 8 : 4); }
+
+int32_t fused_auto_chunks(int32_t dtype, int64_t V) {
+  const int64_t cap = 512 * 16;
+  const int64_t nv = max_body_vecs(dtype, V);
+  return nv <= cap ? 1 : (int32_t)((nv + cap - 1) / cap);
+}
+
+hipError_t launch_prologue(const int64_t* tgt, int64_t ts0, int64_t ts1, int64_t d1, int64_t N, int64_t ignore_idx,
+                           int32_t* n_out, WsHeader* hdr, unsigned long long* slots, int64_t nslots,
+                           hipStream_t stream) {
+  int64_t clear_blocks = (nslots + 8 * 1024 - 1) / (8 * 1024);
+  if (clear_blocks > 1024) clear_blocks = 1024;
+  hipLaunchKernelGGL(k_prologue, dim3((uint32_t)(1 + clear_blocks)), dim3(1024), 0, stream, tgt, ts0, ts1, d1, N,
+                     ignore_idx, n_out, hdr, slots, nslots);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const FusedArgs& a, FusedShape shape, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  const int64_t grid = a.L.N * a.K;
+  if (grid == 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  e = (a.L.dtype == CE_BF16) ? launch_fused_dt<CE_BF16>(a, shape, grid, stream)
+                             : launch_fused_dt<CE_F32>(a, shape, grid, stream);
+  if (e != hipSuccess) return e;
+  if (ev1) e = hipEventRecord(ev1, stream);
+  return e;
+}
+
+hipError_t launch_stats(const StatsArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.L.N == 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  const dim3 grid((uint32_t)stream_grid(a.L.N));
+  if (a.L.dtype == CE_BF16)
+    hipLaunchKernelGGL((k_stats<CE_BF16, kStreamT, kStreamPB>), grid, dim3(kStreamT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_stats<CE_F32, kStreamT, kStreamPB>), grid, dim3(kStreamT), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev1) e = hipEventRecord(ev1, stream);
+  return e;
+}
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.L.N == 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  const dim3 grid((uint32_t)stream_grid(a.L.N));
+  if (a.L.dtype == CE_BF16)
+    hipLaunchKernelGGL((k_backward<CE_BF16, kStreamT, kStreamPB>), grid, dim3(kStreamT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_backward<CE_F32, kStreamT, kStreamPB>), grid, dim3(kStreamT), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev1) e = hipEventRecord(ev1, stream);
+  return e;
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  if (a.N == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine, dim3((uint32_t)((a.N + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_mean, dim3(1), dim3(1024), 0, stream, row_loss, N, n_valid, out);
+  return hipGetLastError();
+}
+
+}  // namespace vce
