@@ -67,6 +67,42 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, out);
 }
 
+// Raw buffer accesses with a byte range: a load past the range returns zero
+// and a store past it is dropped by the hardware, so partly filled vector
+// slots need no branch (a branch around each load would serialise them).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit element format
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void bstore16(const uint4& v, Rsrc r, uint32_t off) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, 0);
+}
+// one element (index j) of a range-checked buffer, widened to FP32 (0 outside)
+template <int DT>
+__device__ __forceinline__ float bload_elem(Rsrc r, int j) {
+  if constexpr (DT == CE_BF16) {
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, j * 2, 0, 0) << 16);
+  } else {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, j * 4, 0, 0));
+  }
+}
+template <int DT>
+__device__ __forceinline__ void bstore_elem(float g, Rsrc r, int j) {
+  if constexpr (DT == CE_BF16) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16(g, 0.f) & 0xffffu), r, j * 2, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), r, j * 4, 0, 0);
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void unpack(const uint4& v, float (&f)[ElemT<DT>::E]) {
   if constexpr (DT == CE_BF16) {
@@ -122,6 +158,63 @@ __device__ __forceinline__ float extract(const uint4& v, int e) {
 #pragma unroll
   for (int i = 1; i < ElemT<DT>::E; ++i) r = (e == i) ? f[i] : r;
   return r;
+}
+
+// Register barrier: the compiler must assume v changed, so the unpacked
+// floats of one sweep are recomputed (one shift or mask each) in the next
+// instead of being kept alive, which would double the registers a chunk
+// needs.  Emits no instruction.
+__device__ __forceinline__ void launder(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+// max(m, elements of v)
+template <int DT>
+__device__ __forceinline__ float vec_max(const uint4& v, float m) {
+  if constexpr (DT == CE_BF16) {
+    m = fmaxf(m, fmaxf(bf_lo(v.x), bf_hi(v.x)));
+    m = fmaxf(m, fmaxf(bf_lo(v.y), bf_hi(v.y)));
+    m = fmaxf(m, fmaxf(bf_lo(v.z), bf_hi(v.z)));
+    return fmaxf(m, fmaxf(bf_lo(v.w), bf_hi(v.w)));
+  } else {
+    m = fmaxf(m, fmaxf(__uint_as_float(v.x), __uint_as_float(v.y)));
+    return fmaxf(m, fmaxf(__uint_as_float(v.z), __uint_as_float(v.w)));
+  }
+}
+
+// sum of the elements of v (BF16 pairs through v_dot2_f32_bf16 with (1, 1))
+template <int DT>
+__device__ __forceinline__ float vec_sum(const uint4& v) {
+  if constexpr (DT == CE_BF16) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 one = __builtin_bit_cast(b2, 0x3f803f80u);
+    float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, v.x), one, 0.f, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, v.y), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, v.z), one, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, v.w), one, acc, false);
+  } else {
+    return (__uint_as_float(v.x) + __uint_as_float(v.y)) + (__uint_as_float(v.z) + __uint_as_float(v.w));
+  }
+}
+
+// v with element e replaced by -inf
+template <int DT>
+__device__ __forceinline__ uint4 with_neg_inf(uint4 v, int e) {
+  if constexpr (DT == CE_BF16) {
+    const int q = e >> 1;
+    const bool hi = e & 1;
+    auto put = [&](uint32_t w) { return hi ? ((w & 0x0000ffffu) | 0xff800000u) : ((w & 0xffff0000u) | 0x0000ff80u); };
+    if (q == 0) v.x = put(v.x);
+    if (q == 1) v.y = put(v.y);
+    if (q == 2) v.z = put(v.z);
+    if (q == 3) v.w = put(v.w);
+  } else {
+    if (e == 0) v.x = 0xff800000u;
+    if (e == 1) v.y = 0xff800000u;
+    if (e == 2) v.z = 0xff800000u;
+    if (e == 3) v.w = 0xff800000u;
+  }
+  return v;
 }
 
 // exp(x - lse) from the base-2 lse split c_hi + c_lo.  For BF16 gradients the
@@ -261,8 +354,14 @@ __global__ __launch_bounds__(1024) void k_prologue(const int64_t* tgt, int64_t t
 // row are claimed by workgroups that are already running: every chunk a
 // workgroup waits for is held by a running workgroup or will be claimed by
 // the next one to start, which keeps the wait finite.
+//
+// The target's own term is kept out of the sum-exp (its register copy is
+// set to -inf after the max pass and its term is rebuilt from the target
+// logit), so that 1 - p_t = D_excl / D stays accurate when the target holds
+// almost all of the probability; its gradient is stored separately after the
+// vector stores.
 template <int DT, int T, int P>
-__global__ __launch_bounds__(T) void k_fused(FusedArgs a) {
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_fused(FusedArgs a) {
   constexpr int E = ElemT<DT>::E;
   __shared__ float sh[T / 64][4];
   __shared__ float xs[64 * 4];
@@ -297,103 +396,106 @@ __global__ __launch_bounds__(T) void k_fused(FusedArgs a) {
     return;
   }
 
-  // ---- the single read of this chunk
+  // ---- the single read of this chunk (slots past the chunk read as zero
+  // and are masked below; their stores are dropped)
+  const Rsrc rb = make_rsrc(body, (int64_t)nvc * 16);
+  const Rsrc rh = make_rsrc(g.base, first ? g.h * ElemT<DT>::EB : 0);
+  const Rsrc rt = make_rsrc(g.tail, last ? (int64_t)g.tn * ElemT<DT>::EB : 0);
   uint4 v[P];
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const int i = j * T + tid;
-    v[j] = (i < nvc) ? body[i] : neg_inf_vec<DT>();
-  }
+  for (int j = 0; j < P; ++j) v[j] = bload16(rb, (uint32_t)(j * T + tid) * 16u);
   const bool hv = first && tid < g.h, tv = last && tid < g.tn;
-  const float hx = hv ? load_elem<DT>(g.base, tid) : -INFINITY;
-  const float tx = tv ? load_elem<DT>(g.tail, tid) : -INFINITY;
+  float hx = bload_elem<DT>(rh, tid);
+  float tx = bload_elem<DT>(rt, tid);
+  hx = hv ? hx : -INFINITY;
+  tx = tv ? tx : -INFINITY;
 
-  // ---- which thread / vector / element of this chunk holds the target
+  // ---- where the target sits (uniform): head, body (chunk, vector, lane,
+  // element) or tail; only the chunk that holds it has own_tid >= 0
   const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
-  int own_tid = -1, own_j = -1, own_e = 0, own_where = 0;  // 1 head, 2 body, 3 tail
+  const int64_t tl = g.t - L.vocab_start;
+  int own_tid = -1, own_j = 0, own_e = 0;
   if (tvalid) {
-    const int64_t tl = g.t - L.vocab_start;
     if (tl < g.h) {
-      if (first) {
-        own_where = 1;
-        own_tid = (int)tl;
-      }
+      if (first) own_tid = (int)tl;
     } else {
       const int64_t c = tl - g.h;
       if (c < g.nv * E) {
         const int64_t vec = c / E;
         if (vec >= cb && vec < cend) {
           const int vi = (int)(vec - cb);
-          own_where = 2;
           own_j = vi / T;
           own_tid = vi - own_j * T;
           own_e = (int)(c - vec * E);
         }
       } else if (last) {
-        own_where = 3;
         own_tid = (int)(c - g.nv * E);
       }
     }
   }
-  float y = 0.f;
-  if (tid == own_tid) {
-    if (own_where == 1) {
-      y = hx;
-    } else if (own_where == 3) {
-      y = tx;
-    } else {
-#pragma unroll
-      for (int j = 0; j < P; ++j)
-        if (j == own_j) y = extract<DT>(v[j], own_e);
-    }
-  }
+  const int own_where = own_tid < 0 ? 0 : (tl < g.h ? 1 : (tl - g.h < g.nv * E ? 2 : 3));
 
-  // ---- statistics: max, then sum of 2^(x log2e - m2), row sum
+  // ---- max, and the row sum that the smoothing term needs
+  const bool smooth = L.alpha != 0.f;
   float m = fmaxf(hx, tx);
+  float rs = (hv ? hx : 0.f) + (tv ? tx : 0.f);
+  if (smooth) {
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    float f[E];
-    unpack<DT>(v[j], f);
+    for (int j = 0; j < P; ++j) {
+      const float mj = vec_max<DT>(v[j], m);
+      m = (j * T + tid < nvc) ? mj : m;
+      rs += vec_sum<DT>(v[j]);  // slots past the chunk hold zeros
+    }
+  } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e) m = fmaxf(m, f[e]);
+    for (int j = 0; j < P; ++j) {
+      const float mj = vec_max<DT>(v[j], m);
+      m = (j * T + tid < nvc) ? mj : m;
+    }
   }
   m = block_max<T>(m, sh);
   const float m2 = m * kL;
   const float msub = (m == -INFINITY) ? 0.f : m2;
+#pragma unroll
+  for (int j = 0; j < P; ++j) launder(v[j]);
 
-  // The target's own term is left out of the sum (and rebuilt from its logit
-  // after the reduction), so that 1 - p_t = D_excl / D stays accurate when
-  // the target holds almost all of the probability.
-  const bool own_head = (own_where == 1 && tid == own_tid), own_tail = (own_where == 3 && tid == own_tid);
-  float d0 = own_head ? 0.f : ex2(__builtin_fmaf(hx, kL, -msub));
-  float d1 = own_tail ? 0.f : ex2(__builtin_fmaf(tx, kL, -msub));
-  float rs = 0.f;
-  const bool smooth = L.alpha != 0.f;
-  if (smooth) rs = (hv ? hx : 0.f) + (tv ? tx : 0.f);
+  // ---- the owning lane takes the target logit out of its registers
+  float y = 0.f;
+  if (own_tid >= 0 && (__builtin_amdgcn_readfirstlane(tid) >> 6) == (own_tid >> 6)) {  // the owning wave only
+    if (tid == own_tid) {
+      if (own_where == 1) {
+        y = hx;
+        hx = -INFINITY;
+      } else if (own_where == 3) {
+        y = tx;
+        tx = -INFINITY;
+      } else {
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+          if (j == own_j) {
+            y = extract<DT>(v[j], own_e);
+            v[j] = with_neg_inf<DT>(v[j], own_e);
+          }
+      }
+    }
+  }
+
+  // ---- sum of 2^(x log2e - m2) over everything but the target
+  float d0 = ex2(__builtin_fmaf(hx, kL, -msub)) + ex2(__builtin_fmaf(tx, kL, -msub)), d1 = 0.f;
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     float f[E];
     unpack<DT>(v[j], f);
-    float tm[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) tm[e] = ex2(__builtin_fmaf(f[e], kL, -msub));
-    if (j == own_j && tid == own_tid) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) tm[e] = (e == own_e) ? 0.f : tm[e];
-    }
+    const float mj = (j * T + tid < nvc) ? msub : INFINITY;  // 2^-inf = 0 for slots past the chunk
 #pragma unroll
     for (int e = 0; e < E; e += 2) {
-      d0 += tm[e];
-      d1 += tm[e + 1];
-    }
-    if (smooth) {
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) part += f[e];
-      rs += (j * T + tid < nvc) ? part : 0.f;
+      d0 += ex2(__builtin_fmaf(f[e], kL, -mj));
+      d1 += ex2(__builtin_fmaf(f[e + 1], kL, -mj));
     }
   }
   float d = d0 + d1;
+#pragma unroll
+  for (int j = 0; j < P; ++j) launder(v[j]);
   block_sum3<T>(d, y, rs, sh);
 
   // ---- exchange between the chunks of a split row
@@ -458,24 +560,28 @@ __global__ __launch_bounds__(T) void k_fused(FusedArgs a) {
   float s = grad_scale(a.reduce, a.g, a.n_valid, r);
   if (!tvalid) s = __uint_as_float(0x7fc00000u);
   const float b = -s * (L.alpha * inv_v);
-  // target element: s (p_t - a/V - (1 - a)) = s ((a - a/V) - (1 - p_t)), 1 - p_t = D_excl / D
-  const float g_t = s * ((L.alpha - L.alpha * inv_v) - D / Dt);
 #pragma unroll
   for (int j = 0; j < P; ++j) {
-    const int i = j * T + tid;
     float f[E];
     unpack<DT>(v[j], f);
     float gr[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(softmax_term<DT>(f[e], c_hi, c_lo), s, b);
-    if (j == own_j && tid == own_tid) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) gr[e] = (e == own_e) ? g_t : gr[e];
-    }
-    if (i < nvc) body[i] = pack<DT>(gr);
+    bstore16(pack<DT>(gr), rb, (uint32_t)(j * T + tid) * 16u);
   }
-  if (hv) store_elem<DT>(g.base, tid, own_head ? g_t : __builtin_fmaf(softmax_term<DT>(hx, c_hi, c_lo), s, b));
-  if (tv) store_elem<DT>(g.tail, tid, own_tail ? g_t : __builtin_fmaf(softmax_term<DT>(tx, c_hi, c_lo), s, b));
+  bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(hx, c_hi, c_lo), s, b), rh, tid);
+  bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(tx, c_hi, c_lo), s, b), rt, tid);
+  // target element: s (p_t - a/V - (1 - a)) = s ((a - a/V) - (1 - p_t)) with 1 - p_t = D_excl / D,
+  // stored by the lane that just wrote its vector (same-thread order keeps this store last)
+  if (tid == own_tid) {
+    const float g_t = s * ((L.alpha - L.alpha * inv_v) - D / Dt);
+    if (own_where == 1)
+      bstore_elem<DT>(g_t, rh, tid);
+    else if (own_where == 3)
+      bstore_elem<DT>(g_t, rt, tid);
+    else
+      bstore_elem<DT>(g_t, rb, (own_j * T + tid) * E + own_e);
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -483,7 +589,7 @@ __global__ __launch_bounds__(T) void k_fused(FusedArgs a) {
 // keeps an online (max, sum) pair, rescaled once per batch of PB vectors.
 template <int DT, int T, int PB>
 __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
-  constexpr int E = ElemT<DT>::E;
+  constexpr int E = ElemT<DT>::E, EB = ElemT<DT>::EB;
   __shared__ float sh[T / 64][4];
   const int tid = threadIdx.x;
   const RowLayout& L = a.L;
@@ -500,9 +606,19 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
       }
       continue;
     }
+    const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
+    const int64_t tl = g.t - L.vocab_start;
+    const bool owns = tvalid && tl >= 0 && tl < L.V;
+    const Rsrc rb = make_rsrc(g.body, g.nv * 16);
+    const Rsrc rh = make_rsrc(g.base, g.h * EB);
+    const Rsrc rt = make_rsrc(g.tail, (int64_t)g.tn * EB);
+    const Rsrc ry = make_rsrc(g.base, owns && tid == 0 ? L.V * EB : 0);
+    float y = bload_elem<DT>(ry, owns ? (int)tl : 0);
     const bool hv = tid < g.h, tv = tid < g.tn;
-    const float hx = hv ? load_elem<DT>(g.base, tid) : -INFINITY;
-    const float tx = tv ? load_elem<DT>(g.tail, tid) : -INFINITY;
+    float hx = bload_elem<DT>(rh, tid);
+    float tx = bload_elem<DT>(rt, tid);
+    hx = hv ? hx : -INFINITY;
+    tx = tv ? tx : -INFINITY;
     float m = fmaxf(hx, tx);
     float m2 = m * kL;
     float msub = (m == -INFINITY) ? 0.f : m2;
@@ -511,17 +627,13 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
     for (int64_t base = 0; base < g.nv; base += (int64_t)T * PB) {
       uint4 v[PB];
 #pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        const int64_t i = base + j * T + tid;
-        v[j] = (i < g.nv) ? g.body[i] : neg_inf_vec<DT>();
-      }
+      for (int j = 0; j < PB; ++j) v[j] = bload16(rb, (uint32_t)(base + j * T + tid) * 16u);
       float bm = -INFINITY;
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
-        float f[E];
-        unpack<DT>(v[j], f);
-#pragma unroll
-        for (int e = 0; e < E; ++e) bm = fmaxf(bm, f[e]);
+        const float mj = vec_max<DT>(v[j], bm);
+        bm = (base + j * T + tid < g.nv) ? mj : bm;
+        rs += vec_sum<DT>(v[j]);  // zeros past the row
       }
       if (bm > m) {
         const float bm2 = bm * kL;
@@ -534,20 +646,11 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
       for (int j = 0; j < PB; ++j) {
         float f[E];
         unpack<DT>(v[j], f);
-        float part = 0.f;
+        const float mj = (base + j * T + tid < g.nv) ? msub : INFINITY;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          d += ex2(__builtin_fmaf(f[e], kL, -msub));
-          part += f[e];
-        }
-        rs += (base + j * T + tid < g.nv) ? part : 0.f;
+        for (int e = 0; e < E; ++e) d += ex2(__builtin_fmaf(f[e], kL, -mj));
       }
     }
-    const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
-    const int64_t tl = g.t - L.vocab_start;
-    const bool owns = tvalid && tl >= 0 && tl < L.V;
-    float y = (tid == 0 && owns) ? load_elem<DT>(g.base, tl) : 0.f;
-
     const float M = block_max<T>(m, sh);
     const float M2 = M * kL;
     float dadj = (m == -INFINITY) ? 0.f : d * ex2(m2 - M2);
@@ -575,7 +678,7 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
 // Streaming in-place backward from a given lse[N]; works on shards.
 template <int DT, int T, int PB>
 __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
-  constexpr int E = ElemT<DT>::E;
+  constexpr int E = ElemT<DT>::E, EB = ElemT<DT>::EB;
   const int tid = threadIdx.x;
   const RowLayout& L = a.L;
   const float inv_v = 1.f / (float)L.vocab_total;
@@ -597,42 +700,39 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
     if (!tvalid) s = __uint_as_float(0x7fc00000u);
     const float b = -s * (L.alpha * inv_v);
     const float a_rest = L.alpha - L.alpha * inv_v;
-    if (tid < g.h) {
-      const float xv = load_elem<DT>(g.base, tid);
-      float gg = __builtin_fmaf(ex2(__builtin_fmaf(xv, kL, -c_hi) - c_lo), s, b);
-      if (tl == tid) gg = s * (expm1f(xv - lse) + a_rest);
-      store_elem<DT>(g.base, tid, gg);
-    }
-    if (tid < g.tn) {
-      const float xv = load_elem<DT>(g.tail, tid);
-      float gg = __builtin_fmaf(ex2(__builtin_fmaf(xv, kL, -c_hi) - c_lo), s, b);
-      if (tl == g.h + g.nv * E + tid) gg = s * (expm1f(xv - lse) + a_rest);
-      store_elem<DT>(g.tail, tid, gg);
+    const Rsrc rb = make_rsrc(g.body, g.nv * 16);
+    const Rsrc rh = make_rsrc(g.base, g.h * EB);
+    const Rsrc rt = make_rsrc(g.tail, (int64_t)g.tn * EB);
+    {
+      // head and tail elements (range-checked: lanes past them do nothing)
+      const float hx = bload_elem<DT>(rh, tid);
+      const float tx = bload_elem<DT>(rt, tid);
+      float gh = __builtin_fmaf(ex2(__builtin_fmaf(hx, kL, -c_hi) - c_lo), s, b);
+      float gt = __builtin_fmaf(ex2(__builtin_fmaf(tx, kL, -c_hi) - c_lo), s, b);
+      // target: s (p_t - 1 + a - a/V) with p_t - 1 = expm1(x_t - lse), p_t never rounded first
+      if (tl == tid) gh = s * (expm1f(hx - lse) + a_rest);
+      if (tl == g.h + g.nv * E + tid) gt = s * (expm1f(tx - lse) + a_rest);
+      bstore_elem<DT>(gh, rh, tid);
+      bstore_elem<DT>(gt, rt, tid);
     }
     for (int64_t base = 0; base < g.nv; base += (int64_t)T * PB) {
       uint4 v[PB];
 #pragma unroll
-      for (int j = 0; j < PB; ++j) {
-        const int64_t i = base + j * T + tid;
-        if (i < g.nv) v[j] = g.body[i];
-      }
+      for (int j = 0; j < PB; ++j) v[j] = bload16(rb, (uint32_t)(base + j * T + tid) * 16u);
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
         const int64_t i = base + j * T + tid;
-        if (i < g.nv) {
-          float f[E];
-          unpack<DT>(v[j], f);
-          float gr[E];
+        float f[E];
+        unpack<DT>(v[j], f);
+        float gr[E];
 #pragma unroll
-          for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(ex2(__builtin_fmaf(f[e], kL, -c_hi) - c_lo), s, b);
-          const uint64_t off = (uint64_t)(tl - (g.h + i * E));
-          if (off < (uint64_t)E) {
-            // target: s (p_t - 1 + a - a/V) with p_t - 1 = expm1(x_t - lse), no rounding of p_t first
+        for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(ex2(__builtin_fmaf(f[e], kL, -c_hi) - c_lo), s, b);
+        const uint64_t off = (uint64_t)(tl - (g.h + i * E));
+        if (off < (uint64_t)E) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) gr[e] = (e == (int)off) ? s * (expm1f(f[e] - lse) + a_rest) : gr[e];
-          }
-          g.body[i] = pack<DT>(gr);
+          for (int e = 0; e < E; ++e) gr[e] = (e == (int)off) ? s * (expm1f(f[e] - lse) + a_rest) : gr[e];
         }
+        bstore16(pack<DT>(gr), rb, (uint32_t)i * 16u);  // dropped past the row
       }
     }
   }
