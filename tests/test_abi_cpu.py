@@ -171,13 +171,13 @@ def test_workspace_sizes(lib):
     x = h.logits(d0=4, d1=2048, s0=2048 * 128000, s1=128000)
     p = h.params(reduce_loss=1, label_smoothing=0.1)
     n = lib.ce_workspace_bytes(ctypes.byref(x), ctypes.byref(p))
-    # header + per-row losses + 2 chunks x 4 tagged words per row
-    assert n == 256 + 8192 * 4 + 8192 * 2 * 4 * 8
+    # header + per-row tagged losses + 4 chunks (of at most 4096 vectors) x 4 tagged words per row
+    assert n == 256 + 8192 * 8 + 8192 * 4 * 4 * 8
     p0 = h.params()
     x1 = h.logits(d0=2, d1=512, s0=512 * 32000, s1=32000, v_local=32000, vocab_total=32000)
     assert lib.ce_workspace_bytes(ctypes.byref(x1), ctypes.byref(p0)) == 256
     assert lib.ce_workspace_bytes(ctypes.byref(h.logits(dtype=9)), ctypes.byref(p0)) == 0
-    assert lib.ce_combine_workspace_bytes(512, ctypes.byref(h.params(reduce_loss=1))) == 256 + 2048
+    assert lib.ce_combine_workspace_bytes(512, ctypes.byref(h.params(reduce_loss=1))) == 256 + 4096
     # forced split: chunks of at most one workgroup
     p3 = h.params(split_chunks=3)
     x2 = h.logits(d0=1, d1=10, s0=40960, s1=4096, v_local=4096, vocab_total=4096)
@@ -185,10 +185,10 @@ def test_workspace_sizes(lib):
 
 
 def test_split_chunks_too_few_rejected(lib):
-    # V = 256000 BF16 rows need at least 4 chunks of 8192 vectors; 2 cannot hold them
+    # V = 600000 BF16 rows need at least 5 chunks of 16384 vectors; 4 cannot hold them
     h = Host()
-    x = h.logits(d0=1, d1=2, s0=512000, s1=256000, v_local=256000, vocab_total=256000)
-    p = h.params(split_chunks=2)
+    x = h.logits(d0=1, d1=2, s0=1200000, s1=600000, v_local=600000, vocab_total=600000)
+    p = h.params(split_chunks=4)
     rc = lib.ce_fwd_bwd_fused(ctypes.byref(x), ctypes.byref(h.targets()), ctypes.byref(p), None,
                               h.loss.ctypes.data, None, h.ws.ctypes.data, h.ws.nbytes, None)
     assert rc == _abi.CE_ELAYOUT

@@ -112,12 +112,15 @@ struct WsLayout {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// header | per-row losses (8 bytes a row: FP32, or a tagged word in the fused
+// call) | split-row exchange words.  Everything after the header is cleared by
+// the fused call's prologue.
 WsLayout ws_layout(int64_t N, int32_t K, bool reduce) {
   WsLayout w;
   size_t off = vce::kWsHeaderBytes;
   if (reduce) {
     w.row_loss = off;
-    off = align256(off + (size_t)N * 4u);
+    off = align256(off + (size_t)N * 8u);
   }
   if (K > 1) {
     w.slots = off;
@@ -271,7 +274,7 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
   const vce::FusedShape shape = vce::fused_shape_for(C);
   if (shape.threads == 0)
     return fail(CE_ELAYOUT, "split_chunks %d leaves %lld vectors per chunk, above one workgroup's %d",
-                p->split_chunks, (long long)C, 512 * 16);
+                p->split_chunks, (long long)C, 1024 * 16);
   if (N * K > kMaxGrid) return fail(CE_EINVAL, "rows x chunks exceeds the launch grid");
   const WsLayout w = ws_layout(N, K, p->reduce_loss != 0);
   if (!ws || ws_bytes < w.total)
@@ -282,8 +285,11 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
   auto* hdr = reinterpret_cast<vce::WsHeader*>(wsb);
   int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
   auto* slots = K > 1 ? reinterpret_cast<unsigned long long*>(wsb + w.slots) : nullptr;
+  // the prologue clears everything after the header: tagged row losses and exchange words
+  auto* clear_begin = reinterpret_cast<unsigned long long*>(wsb + vce::kWsHeaderBytes);
+  const int64_t nclear = (int64_t)((w.total - vce::kWsHeaderBytes) / 8u);
   hipError_t e;
-  if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, slots, w.nslots,
+  if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, clear_begin, nclear,
                                 stream)))
     return hip_fail(e, "prologue launch");
   vce::FusedArgs a;
@@ -293,13 +299,16 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
   a.reduce = p->reduce_loss;
   a.g = grad_out;
   a.n_valid = n_out;
-  a.row_loss = p->reduce_loss ? reinterpret_cast<float*>(wsb + w.row_loss) : loss;
+  a.row_loss = p->reduce_loss ? nullptr : loss;
+  a.row_loss_tagged = p->reduce_loss ? reinterpret_cast<unsigned long long*>(wsb + w.row_loss) : nullptr;
+  a.mean_out = p->reduce_loss ? loss : nullptr;
   a.hdr = hdr;
   a.slots = slots;
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
   if ((e = vce::launch_fused(a, shape, stream, e0, e1))) return hip_fail(e, "fused launch");
-  if (p->reduce_loss && (e = vce::launch_mean(a.row_loss, N, n_out, loss, stream)))
+  // with rows, the fused kernel writes the mean itself; with none it is 0/0
+  if (p->reduce_loss && N == 0 && (e = vce::launch_mean(nullptr, 0, n_out, loss, stream)))
     return hip_fail(e, "mean launch");
   return CE_OK;
 }

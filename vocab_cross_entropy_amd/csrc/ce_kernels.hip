@@ -320,6 +320,7 @@ __global__ __launch_bounds__(1024) void k_prologue(const int64_t* tgt, int64_t t
   if (blockIdx.x == 0) {
     __shared__ int sh[16];
     int cnt = 0;
+#pragma unroll 8
     for (int64_t r = threadIdx.x; r < N; r += 1024) {
       const int64_t i0 = r / d1, i1 = r - i0 * d1;
       cnt += tgt[i0 * ts0 + i1 * ts1] != ignore_idx;
@@ -332,14 +333,66 @@ __global__ __launch_bounds__(1024) void k_prologue(const int64_t* tgt, int64_t t
       int n = 0;
       for (int i = 0; i < 16; ++i) n += sh[i];
       *n_out = n;
-      if (hdr) {
-        hdr->ticket = 0ull;
-        hdr->status = 0u;
-      }
+    }
+    if (hdr && threadIdx.x == 0) {
+      hdr->ticket = 0ull;
+      hdr->rows_done = 0ull;
+      hdr->status = 0u;
     }
   } else {
     const int64_t stride = (int64_t)(gridDim.x - 1) * 1024;
     for (int64_t i = (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x; i < nslots; i += stride) slots[i] = 0ull;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Publish a fused row's loss.  Without reduction it goes straight to
+// loss[r].  With the mean, chunk 0 of each row publishes a tagged word and
+// counts the row done; the workgroup that counts the last row waits for every
+// tag and sums the N losses in index order in FP64 (deterministic), so no
+// separate mean kernel runs after the fused one.
+template <int T>
+__device__ __forceinline__ void finish_row(const FusedArgs& a, int64_t r, float loss, bool chunk0) {
+  if (!chunk0) return;
+  if (!a.reduce) {
+    if (threadIdx.x == 0) a.row_loss[r] = loss;
+    return;
+  }
+  __shared__ int s_last;
+  __shared__ double s_sum[T / 64];
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(a.row_loss_tagged + r, ((unsigned long long)kTagHi << 32) | __float_as_uint(loss),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long done = atomicAdd(&a.hdr->rows_done, 1ull);
+    s_last = done == (unsigned long long)(a.L.N - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  double acc = 0.0;
+  uint32_t spins = 0;
+  bool gave_up = false;
+  for (int64_t i = threadIdx.x; i < a.L.N; i += T) {
+    unsigned long long w;
+    for (;;) {
+      w = __hip_atomic_load(a.row_loss_tagged + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((uint32_t)(w >> 32) == kTagHi) break;
+      if (++spins > kSpinLimit) {
+        gave_up = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    acc += gave_up ? __builtin_nan("") : (double)__uint_as_float((uint32_t)w);
+  }
+  if (gave_up) atomicOr(&a.hdr->status, 1u);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) s_sum[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int i = 0; i < T / 64; ++i) tot += s_sum[i];
+    a.mean_out[0] = (float)(tot / (double)(*a.n_valid));  // n = 0 cannot reach here (no rows)
   }
 }
 
@@ -351,9 +404,10 @@ __global__ __launch_bounds__(1024) void k_prologue(const int64_t* tgt, int64_t t
 // (m2, d_excl, y, r) as tagged 64-bit words, waits for its partners, and all
 // chunks combine the K tuples in chunk order, so they agree bit for bit on
 // the row's lse.  Work items come from an atomic ticket, so the chunks of a
-// row are claimed by workgroups that are already running: every chunk a
-// workgroup waits for is held by a running workgroup or will be claimed by
-// the next one to start, which keeps the wait finite.
+// row are claimed by workgroups that are already running: a chunk a workgroup
+// waits for is held by a running workgroup or will be claimed by one that
+// starts later (unclaimed items never outnumber unstarted workgroups), which
+// keeps the wait finite whatever order the hardware dispatches in.
 //
 // The target's own term is kept out of the sum-exp (its register copy is
 // set to -inf after the max pass and its term is rebuilt from the target
@@ -392,7 +446,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     for (int i = tid; i < nvc; i += T) body[i] = z;
     if (first && tid < g.h) store_elem<DT>(g.base, tid, 0.f);
     if (last && tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
-    if (first && tid == 0) a.row_loss[r] = 0.f;
+    finish_row<T>(a, r, 0.f, first);
     return;
   }
 
@@ -550,11 +604,8 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
   const float bb = c_hi - M2;
   const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
   const float inv_v = 1.f / (float)L.vocab_total;
-  if (first && tid == 0) {
-    const float lse = c_hi * kLn2 + c_lo * kLn2;
-    float loss = lse - (1.f - L.alpha) * Y - (L.alpha * inv_v) * R;
-    a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
-  }
+  const float lse = c_hi * kLn2 + c_lo * kLn2;
+  const float row_loss = tvalid ? lse - (1.f - L.alpha) * Y - (L.alpha * inv_v) * R : __uint_as_float(0x7fc00000u);
 
   // ---- gradient from the registers, written over the logits
   float s = grad_scale(a.reduce, a.g, a.n_valid, r);
@@ -582,6 +633,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     else
       bstore_elem<DT>(g_t, rb, (own_j * T + tid) * E + own_e);
   }
+  finish_row<T>(a, r, row_loss, first);
 }
 
 // --------------------------------------------------------------------------
@@ -772,6 +824,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 __global__ __launch_bounds__(1024) void k_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out) {
   __shared__ double sh[16];
   double s = 0.0;
+#pragma unroll 8
   for (int64_t i = threadIdx.x; i < N; i += 1024) s += (double)row_loss[i];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
@@ -792,6 +845,7 @@ hipError_t launch_fused_t(const FusedArgs& a, int64_t grid, hipStream_t stream) 
 
 template <int DT>
 hipError_t launch_fused_dt(const FusedArgs& a, FusedShape shape, int64_t grid, hipStream_t stream) {
+  if (shape.threads == 1024 && shape.vecs == 16) return launch_fused_t<DT, 1024, 16>(a, grid, stream);
   if (shape.threads == 512 && shape.vecs == 16) return launch_fused_t<DT, 512, 16>(a, grid, stream);
   if (shape.threads == 256) {
     switch (shape.vecs) {
@@ -814,7 +868,7 @@ int64_t stream_grid(int64_t N) { return N < (1 << 20) ? N : (1 << 20); }
 }  // namespace
 
 // Shapes available to the fused kernel, smallest capacity first.
-static const FusedShape kShapes[] = {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {256, 16}, {512, 16}};
+static const FusedShape kShapes[] = {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {256, 16}, {512, 16}, {1024, 16}};
 
 FusedShape fused_shape_for(int64_t vecs) {
   for (const FusedShape& s : kShapes)
@@ -824,8 +878,11 @@ FusedShape fused_shape_for(int64_t vecs) {
 
 int64_t max_body_vecs(int32_t dtype, int64_t V) { return V / (dtype == CE_BF16 ? 8 : 4); }
 
+// Rows are split into chunks of at most 256 threads x 16 vectors (64 KiB):
+// four such workgroups fit a CU at <= 128 VGPRs, which measured faster on the
+// 128000-column BF16 rows than two 512-thread or one 1024-thread workgroup.
 int32_t fused_auto_chunks(int32_t dtype, int64_t V) {
-  const int64_t cap = 512 * 16;
+  const int64_t cap = 256 * 16;
   const int64_t nv = max_body_vecs(dtype, V);
   return nv <= cap ? 1 : (int32_t)((nv + cap - 1) / cap);
 }
