@@ -59,6 +59,13 @@ bool rows_disjoint(int64_t d0, int64_t d1, int64_t s0, int64_t s1, int64_t V) {
   return true;
 }
 
+// Every row starts on a 16-byte boundary and spans whole 16-byte vectors.
+int32_t rows_aligned16(const ce_logits* x) {
+  const int64_t b = elem_bytes(x->dtype);
+  return ((uintptr_t)x->data % 16u == 0) && (x->d0 <= 1 || (x->s0 * b) % 16 == 0) &&
+         ((x->s1 * b) % 16 == 0 || x->d1 == 1) && ((x->v_local * b) % 16 == 0);
+}
+
 ce_status check_params(const ce_params* p) {
   if (!p) return fail(CE_EINVAL, "params is NULL");
   const float a = p->label_smoothing;
@@ -295,6 +302,7 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
   vce::FusedArgs a;
   a.L = row_layout(x, t, p);
   a.K = K;
+  a.aligned = rows_aligned16(x);
   a.C = C;
   a.reduce = p->reduce_loss;
   a.g = grad_out;

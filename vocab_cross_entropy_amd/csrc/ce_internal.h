@@ -39,6 +39,7 @@ struct RowLayout {
 struct FusedArgs {
   RowLayout L;
   int32_t K;               // chunks per row
+  int32_t aligned;         // every row starts and ends on a 16-byte boundary (no head/tail)
   int64_t C;               // body vectors per chunk
   int32_t reduce;          // mean over non-ignored rows
   const float* g;          // upstream gradient ([N] or [1]); NULL = 1

@@ -289,14 +289,14 @@ struct Row {
   int64_t t;      // target (global index)
 };
 
-template <int DT>
+template <int DT, bool HT = true>
 __device__ __forceinline__ Row<DT> row_geometry(const RowLayout& L, int64_t r) {
   constexpr int E = ElemT<DT>::E, EB = ElemT<DT>::EB;
   Row<DT> g;
   const int64_t i0 = r / L.d1, i1 = r - i0 * L.d1;
   g.t = L.tgt[i0 * L.ts0 + i1 * L.ts1];
   g.base = L.x + (i0 * L.s0 + i1 * L.s1) * EB;
-  int64_t h = (int64_t)(((16u - ((uint32_t)(uintptr_t)g.base & 15u)) & 15u) / EB);
+  int64_t h = HT ? (int64_t)(((16u - ((uint32_t)(uintptr_t)g.base & 15u)) & 15u) / EB) : 0;
   g.h = h > L.V ? L.V : h;
   g.nv = (L.V - g.h) / E;
   g.tn = (int)(L.V - g.h - g.nv * E);
@@ -414,7 +414,10 @@ __device__ __forceinline__ void finish_row(const FusedArgs& a, int64_t r, float 
 // logit), so that 1 - p_t = D_excl / D stays accurate when the target holds
 // almost all of the probability; its gradient is stored separately after the
 // vector stores.
-template <int DT, int T, int P>
+// HT: rows may have head/tail elements (a row start or end off a 16-byte
+// boundary).  When every row is aligned the host launches HT = false, which
+// keeps the two scalar element registers out of the chunk's register budget.
+template <int DT, int T, int P, bool HT>
 __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_fused(FusedArgs a) {
   constexpr int E = ElemT<DT>::E;
   __shared__ float sh[T / 64][4];
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
   const int k = (int)(item - r * K);
   if (r >= L.N) return;
 
-  const Row<DT> g = row_geometry<DT>(L, r);
+  const Row<DT> g = row_geometry<DT, HT>(L, r);
   const int64_t cb = (int64_t)k * a.C;
   const int64_t cend = g.nv < cb + a.C ? g.nv : cb + a.C;
   const int nvc = cend > cb ? (int)(cend - cb) : 0;
@@ -444,8 +447,10 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
   if (g.t == L.ignore_idx) {  // ignored row: +0.0 gradient, loss 0, nothing read
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     for (int i = tid; i < nvc; i += T) body[i] = z;
-    if (first && tid < g.h) store_elem<DT>(g.base, tid, 0.f);
-    if (last && tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
+    if (HT) {
+      if (first && tid < g.h) store_elem<DT>(g.base, tid, 0.f);
+      if (last && tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
+    }
     finish_row<T>(a, r, 0.f, first);
     return;
   }
@@ -453,16 +458,19 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
   // ---- the single read of this chunk (slots past the chunk read as zero
   // and are masked below; their stores are dropped)
   const Rsrc rb = make_rsrc(body, (int64_t)nvc * 16);
-  const Rsrc rh = make_rsrc(g.base, first ? g.h * ElemT<DT>::EB : 0);
-  const Rsrc rt = make_rsrc(g.tail, last ? (int64_t)g.tn * ElemT<DT>::EB : 0);
+  const Rsrc rh = make_rsrc(g.base, HT && first ? g.h * ElemT<DT>::EB : 0);
+  const Rsrc rt = make_rsrc(g.tail, HT && last ? (int64_t)g.tn * ElemT<DT>::EB : 0);
   uint4 v[P];
 #pragma unroll
   for (int j = 0; j < P; ++j) v[j] = bload16(rb, (uint32_t)(j * T + tid) * 16u);
-  const bool hv = first && tid < g.h, tv = last && tid < g.tn;
-  float hx = bload_elem<DT>(rh, tid);
-  float tx = bload_elem<DT>(rt, tid);
-  hx = hv ? hx : -INFINITY;
-  tx = tv ? tx : -INFINITY;
+  const bool hv = HT && first && tid < g.h, tv = HT && last && tid < g.tn;
+  float hx = -INFINITY, tx = -INFINITY;
+  if (HT) {
+    hx = bload_elem<DT>(rh, tid);
+    tx = bload_elem<DT>(rt, tid);
+    hx = hv ? hx : -INFINITY;
+    tx = tv ? tx : -INFINITY;
+  }
 
   // ---- where the target sits (uniform): head, body (chunk, vector, lane,
   // element) or tail; only the chunk that holds it has own_tid >= 0
@@ -620,8 +628,10 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(softmax_term<DT>(f[e], c_hi, c_lo), s, b);
     bstore16(pack<DT>(gr), rb, (uint32_t)(j * T + tid) * 16u);
   }
-  bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(hx, c_hi, c_lo), s, b), rh, tid);
-  bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(tx, c_hi, c_lo), s, b), rt, tid);
+  if (HT) {
+    bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(hx, c_hi, c_lo), s, b), rh, tid);
+    bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(tx, c_hi, c_lo), s, b), rt, tid);
+  }
   // target element: s (p_t - a/V - (1 - a)) = s ((a - a/V) - (1 - p_t)) with 1 - p_t = D_excl / D,
   // stored by the lane that just wrote its vector (same-thread order keeps this store last)
   if (tid == own_tid) {
@@ -839,7 +849,10 @@ __global__ __launch_bounds__(1024) void k_mean(const float* row_loss, int64_t N,
 
 template <int DT, int T, int P>
 hipError_t launch_fused_t(const FusedArgs& a, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((k_fused<DT, T, P>), dim3((uint32_t)grid), dim3(T), 0, stream, a);
+  if (a.aligned)
+    hipLaunchKernelGGL((k_fused<DT, T, P, false>), dim3((uint32_t)grid), dim3(T), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_fused<DT, T, P, true>), dim3((uint32_t)grid), dim3(T), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -847,13 +860,13 @@ template <int DT>
 hipError_t launch_fused_dt(const FusedArgs& a, FusedShape shape, int64_t grid, hipStream_t stream) {
   if (shape.threads == 1024 && shape.vecs == 16) return launch_fused_t<DT, 1024, 16>(a, grid, stream);
   if (shape.threads == 512 && shape.vecs == 16) return launch_fused_t<DT, 512, 16>(a, grid, stream);
+  if (shape.threads == 512 && shape.vecs == 8) return launch_fused_t<DT, 512, 8>(a, grid, stream);
   if (shape.threads == 256) {
     switch (shape.vecs) {
       case 1: return launch_fused_t<DT, 256, 1>(a, grid, stream);
       case 2: return launch_fused_t<DT, 256, 2>(a, grid, stream);
       case 4: return launch_fused_t<DT, 256, 4>(a, grid, stream);
       case 8: return launch_fused_t<DT, 256, 8>(a, grid, stream);
-      case 16: return launch_fused_t<DT, 256, 16>(a, grid, stream);
       default: break;
     }
   }
@@ -868,7 +881,9 @@ int64_t stream_grid(int64_t N) { return N < (1 << 20) ? N : (1 << 20); }
 }  // namespace
 
 // Shapes available to the fused kernel, smallest capacity first.
-static const FusedShape kShapes[] = {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {256, 16}, {512, 16}, {1024, 16}};
+// (512, 8) covers 2049..4096 vectors with 8 waves a workgroup at ~75 VGPRs
+// (6 waves per SIMD), which measured faster than (256, 16) at 128 VGPRs.
+static const FusedShape kShapes[] = {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {512, 8}, {512, 16}, {1024, 16}};
 
 FusedShape fused_shape_for(int64_t vecs) {
   for (const FusedShape& s : kShapes)
@@ -878,9 +893,9 @@ FusedShape fused_shape_for(int64_t vecs) {
 
 int64_t max_body_vecs(int32_t dtype, int64_t V) { return V / (dtype == CE_BF16 ? 8 : 4); }
 
-// Rows are split into chunks of at most 256 threads x 16 vectors (64 KiB):
-// four such workgroups fit a CU at <= 128 VGPRs, which measured faster on the
-// 128000-column BF16 rows than two 512-thread or one 1024-thread workgroup.
+// Rows are split into chunks of at most 4096 vectors (64 KiB), held by 512
+// threads x 8 vectors: on the 128000-column BF16 rows four such chunks per
+// row measured faster than 1, 2, 3, 6 or 8 chunks.
 int32_t fused_auto_chunks(int32_t dtype, int64_t V) {
   const int64_t cap = 256 * 16;
   const int64_t nv = max_body_vecs(dtype, V);
