@@ -69,12 +69,13 @@ def assert_loss(gpu, ref, what=""):
     assert not bad.any(), f"{what}: loss off at {np.flatnonzero(bad)[:5]} max err {np.nanmax(err):.3e}"
 
 
-def assert_grad(gpu, ref, dtype, what="", floor_scale=1.0):
+def assert_grad(gpu, ref, dtype, what="", floor_scale=1.0, extra_rtol=0.0):
     """Elementwise gradient bar; ``floor_scale`` < 1 tightens the absolute
-    floor (diagnostic check of g/s against ref/s)."""
+    floor (diagnostic check of g/s against ref/s), ``extra_rtol`` widens the
+    relative term of that diagnostic."""
     rtol, atol = GRAD_TOL[dtype]
     err = np.abs(gpu - ref)
-    tol = rtol * np.abs(ref) + atol * floor_scale
+    tol = (rtol + extra_rtol) * np.abs(ref) + atol * floor_scale
     bad = ~(err <= tol)
     if bad.any():
         i = np.argwhere(bad)[0]

@@ -71,8 +71,13 @@ def check_fused(x, t, alpha, reduce, g=None, split_chunks=0, sample=None, what="
     gpu = rows_f64(xd, rows)
     assert_grad(gpu, grad_ref, x.dtype, what)
     if diag and reduce and n_ref > 0:
+        # bug-catcher for small s, where the 1e-7 floor hides everything: the
+        # floor scaled by s, with 2^-11 |ref| more for BF16 (the kernel may stage
+        # exponentials in FP16 between its passes; the official bar above gates)
         s = _s_of(g, reduce, n_ref, N)
-        assert_grad(gpu, grad_ref, x.dtype, what + " (floor scaled by s)", floor_scale=min(1.0, abs(s)))
+        extra = 2.0 ** -11 if x.dtype == torch.bfloat16 else 0.0
+        assert_grad(gpu, grad_ref, x.dtype, what + " (floor scaled by s)", floor_scale=min(1.0, abs(s)),
+                    extra_rtol=extra)
     ign_rows = [k for k, r in enumerate(rows) if r in ign]
     if ign_rows:
         bits = raw_bits(xd, rows[ign_rows])

@@ -38,6 +38,18 @@ constexpr uint32_t kTagHi = 0x5EEDC0DEu;
 // (each iteration sleeps ~128 cycles: ~0.2 s in total), after which the
 // row is finished with NaN and the workspace status word is set.
 constexpr uint32_t kSpinLimit = 1u << 22;
+// Reuse path: the sum pass's terms (scaled by 2^kReuseShift to keep them in
+// FP16's normal range) are kept as FP16 for the BF16 gradient, relative
+// error 2^-11 next to the gradient's own 2^-9 rounding, inside the 2^-8 bar.
+// Near p = a/V the gradient s (p - a/V) cancels and that FP16 error is
+// absolute, s (a/V) 2^-11; the path is taken only while s (a/V) and a/V are
+// small enough that this stays well under the 1e-7 floor (scaled by s).
+constexpr int kReuseShift = 14;
+constexpr float kReuseUnscale = 1.f / 16384.f;
+constexpr float kReuseSA = 4e-5f;
+constexpr float kReuseA = 5e-5f;
+// and the FP16 error of a single term, |s| p 2^-11, stays below half the floor
+constexpr float kReuseAbs = 5e-8f;
 
 template <int DT>
 struct ElemT;
@@ -101,6 +113,26 @@ __device__ __forceinline__ void bstore_elem(float g, Rsrc r, int j) {
   } else {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g), r, j * 4, 0, 0);
   }
+}
+
+// FP32 pair -> packed FP16 pair, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  f2 in = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(in, h2));
+}
+// fma(FP16 half of w widened to FP32, k, c) in one v_fma_mix_f32
+// (op_sel_hi marks operand 0 as FP16, op_sel picks its high half).
+__device__ __forceinline__ float fma_mix_lo(uint32_t w, float k, float c) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(k), "v"(c));
+  return d;
+}
+__device__ __forceinline__ float fma_mix_hi(uint32_t w, float k, float c) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(k), "v"(c));
+  return d;
 }
 
 template <int DT>
@@ -336,7 +368,6 @@ __global__ __launch_bounds__(1024) void k_prologue(const int64_t* tgt, int64_t t
     }
     if (hdr && threadIdx.x == 0) {
       hdr->ticket = 0ull;
-      hdr->rows_done = 0ull;
       hdr->status = 0u;
     }
   } else {
@@ -347,42 +378,50 @@ __global__ __launch_bounds__(1024) void k_prologue(const int64_t* tgt, int64_t t
 
 // --------------------------------------------------------------------------
 // Publish a fused row's loss.  Without reduction it goes straight to
-// loss[r].  With the mean, chunk 0 of each row publishes a tagged word and
-// counts the row done; the workgroup that counts the last row waits for every
-// tag and sums the N losses in index order in FP64 (deterministic), so no
-// separate mean kernel runs after the fused one.
+// loss[r]; with the mean, chunk 0 of each row publishes a tagged word
+// (fire-and-forget, no round trip before the workgroup exits).
 template <int T>
-__device__ __forceinline__ void finish_row(const FusedArgs& a, int64_t r, float loss, bool chunk0) {
-  if (!chunk0) return;
-  if (!a.reduce) {
-    if (threadIdx.x == 0) a.row_loss[r] = loss;
-    return;
-  }
-  __shared__ int s_last;
-  __shared__ double s_sum[T / 64];
-  if (threadIdx.x == 0) {
+__device__ __forceinline__ void publish_row_loss(const FusedArgs& a, int64_t r, float loss, bool chunk0) {
+  if (!chunk0 || threadIdx.x != 0) return;
+  if (!a.reduce)
+    a.row_loss[r] = loss;
+  else
     __hip_atomic_store(a.row_loss_tagged + r, ((unsigned long long)kTagHi << 32) | __float_as_uint(loss),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long done = atomicAdd(&a.hdr->rows_done, 1ull);
-    s_last = done == (unsigned long long)(a.L.N - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
+}
+
+// The mean, computed by the workgroup that holds the last ticket once its own
+// item is done: by then every item is claimed by a running or finished
+// workgroup, none of which waits for this one, so every tag arrives.  The N
+// losses are summed in index order in FP64 (deterministic).
+template <int T>
+__device__ void fused_mean(const FusedArgs& a) {
+  __shared__ double s_sum[T / 64];
+  constexpr int U = 16;  // independent loads in flight per thread; missing words are polled again
   double acc = 0.0;
   uint32_t spins = 0;
   bool gave_up = false;
-  for (int64_t i = threadIdx.x; i < a.L.N; i += T) {
-    unsigned long long w;
-    for (;;) {
-      w = __hip_atomic_load(a.row_loss_tagged + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((uint32_t)(w >> 32) == kTagHi) break;
-      if (++spins > kSpinLimit) {
-        gave_up = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+  for (int64_t base = 0; base < a.L.N; base += (int64_t)T * U) {
+    unsigned long long w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + (int64_t)u * T + threadIdx.x;
+      w[u] = i < a.L.N ? __hip_atomic_load(a.row_loss_tagged + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : ((unsigned long long)kTagHi << 32);
     }
-    acc += gave_up ? __builtin_nan("") : (double)__uint_as_float((uint32_t)w);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + (int64_t)u * T + threadIdx.x;
+      while ((uint32_t)(w[u] >> 32) != kTagHi && !gave_up) {
+        if (++spins > kSpinLimit) {
+          gave_up = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        w[u] = __hip_atomic_load(a.row_loss_tagged + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      acc += gave_up ? __builtin_nan("") : (double)__uint_as_float((uint32_t)w[u]);
+    }
   }
   if (gave_up) atomicOr(&a.hdr->status, 1u);
 #pragma unroll
@@ -392,7 +431,7 @@ __device__ __forceinline__ void finish_row(const FusedArgs& a, int64_t r, float 
   if (threadIdx.x == 0) {
     double tot = 0.0;
     for (int i = 0; i < T / 64; ++i) tot += s_sum[i];
-    a.mean_out[0] = (float)(tot / (double)(*a.n_valid));  // n = 0 cannot reach here (no rows)
+    a.mean_out[0] = (float)(tot / (double)(*a.n_valid));  // N >= 1 here; n = 0 gives 0/0 = NaN
   }
 }
 
@@ -451,9 +490,13 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       if (first && tid < g.h) store_elem<DT>(g.base, tid, 0.f);
       if (last && tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
     }
-    finish_row<T>(a, r, 0.f, first);
+    publish_row_loss<T>(a, r, 0.f, first);
+    if (a.reduce && item == (int64_t)L.N * K - 1) fused_mean<T>(a);
     return;
   }
+
+  // the upstream gradient scale, loaded now so the round trip overlaps the chunk loads
+  const float s_up = grad_scale(a.reduce, a.g, a.n_valid, r);
 
   // ---- the single read of this chunk (slots past the chunk read as zero
   // and are masked below; their stores are dropped)
@@ -515,6 +558,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       m = (j * T + tid < nvc) ? mj : m;
     }
   }
+  const float m_loc = m;  // this thread's own maximum (bounds its largest softmax term)
   m = block_max<T>(m, sh);
   const float m2 = m * kL;
   const float msub = (m == -INFINITY) ? 0.f : m2;
@@ -542,17 +586,48 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     }
   }
 
-  // ---- sum of 2^(x log2e - m2) over everything but the target
+  // ---- sum of 2^(x log2e - m2) over everything but the target.
+  // On the reuse path (BF16 gradients, see kReuseSA) each term, scaled by
+  // 2^14, is also packed to FP16 into the registers that held the pair of
+  // logits, and the gradient pass reads it back instead of recomputing it.
+  // Per wave: every lane's largest term is below |s| p_max 2^-11 <= kReuseAbs, with
+  // p_j <= e^(x_j - chunk max) because lse >= every chunk's max; a wave
+  // holding a large softmax value keeps its logits and the exact path.
+  const bool reuse_row = DT == CE_BF16 && fabsf(s_up) * L.alpha * (1.f / (float)L.vocab_total) <= kReuseSA &&
+                         L.alpha * (1.f / (float)L.vocab_total) <= kReuseA;
+  const bool big_lane = fabsf(s_up) * ex2((m_loc - m) * kL) * (1.f / 2048.f) > kReuseAbs;
+  const bool reuse = reuse_row && !__any(big_lane);
   float d0 = ex2(__builtin_fmaf(hx, kL, -msub)) + ex2(__builtin_fmaf(tx, kL, -msub)), d1 = 0.f;
+  if (reuse) {
+    const float msc = msub - (float)kReuseShift;
+    float q0 = 0.f, q1 = 0.f;
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    float f[E];
-    unpack<DT>(v[j], f);
-    const float mj = (j * T + tid < nvc) ? msub : INFINITY;  // 2^-inf = 0 for slots past the chunk
+    for (int j = 0; j < P; ++j) {
+      float f[E];
+      unpack<DT>(v[j], f);
+      const float mj = (j * T + tid < nvc) ? msc : INFINITY;  // 2^-inf = 0 for slots past the chunk
+      float t[E];
 #pragma unroll
-    for (int e = 0; e < E; e += 2) {
-      d0 += ex2(__builtin_fmaf(f[e], kL, -mj));
-      d1 += ex2(__builtin_fmaf(f[e + 1], kL, -mj));
+      for (int e = 0; e < E; ++e) t[e] = ex2(__builtin_fmaf(f[e], kL, -mj));
+#pragma unroll
+      for (int e = 0; e < E; e += 2) {
+        q0 += t[e];
+        q1 += t[e + 1];
+      }
+      v[j] = make_uint4(pack_f16(t[0], t[1]), pack_f16(t[2], t[3]), pack_f16(t[4], t[5]), pack_f16(t[6], t[7]));
+    }
+    d0 += (q0 + q1) * kReuseUnscale;  // exact power-of-two rescale
+  } else {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      float f[E];
+      unpack<DT>(v[j], f);
+      const float mj = (j * T + tid < nvc) ? msub : INFINITY;  // 2^-inf = 0 for slots past the chunk
+#pragma unroll
+      for (int e = 0; e < E; e += 2) {
+        d0 += ex2(__builtin_fmaf(f[e], kL, -mj));
+        d1 += ex2(__builtin_fmaf(f[e + 1], kL, -mj));
+      }
     }
   }
   float d = d0 + d1;
@@ -616,17 +691,29 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
   const float row_loss = tvalid ? lse - (1.f - L.alpha) * Y - (L.alpha * inv_v) * R : __uint_as_float(0x7fc00000u);
 
   // ---- gradient from the registers, written over the logits
-  float s = grad_scale(a.reduce, a.g, a.n_valid, r);
-  if (!tvalid) s = __uint_as_float(0x7fc00000u);
+  const float s = tvalid ? s_up : __uint_as_float(0x7fc00000u);
   const float b = -s * (L.alpha * inv_v);
+  if (reuse) {
+    // p = 2^(x log2e - msub) / D * 2^(msub - M2); the registers hold that first factor times 2^14
+    const float kr = s * ex2(msub - M2 - (float)kReuseShift) / Dt;
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    float f[E];
-    unpack<DT>(v[j], f);
-    float gr[E];
+    for (int j = 0; j < P; ++j) {
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      uint32_t o[4];
 #pragma unroll
-    for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(softmax_term<DT>(f[e], c_hi, c_lo), s, b);
-    bstore16(pack<DT>(gr), rb, (uint32_t)(j * T + tid) * 16u);
+      for (int q = 0; q < 4; ++q) o[q] = pack_bf16(fma_mix_lo(w[q], kr, b), fma_mix_hi(w[q], kr, b));
+      bstore16(make_uint4(o[0], o[1], o[2], o[3]), rb, (uint32_t)(j * T + tid) * 16u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      float f[E];
+      unpack<DT>(v[j], f);
+      float gr[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(softmax_term<DT>(f[e], c_hi, c_lo), s, b);
+      bstore16(pack<DT>(gr), rb, (uint32_t)(j * T + tid) * 16u);
+    }
   }
   if (HT) {
     bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(hx, c_hi, c_lo), s, b), rh, tid);
@@ -643,7 +730,8 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     else
       bstore_elem<DT>(g_t, rb, (own_j * T + tid) * E + own_e);
   }
-  finish_row<T>(a, r, row_loss, first);
+  publish_row_loss<T>(a, r, row_loss, first);
+  if (a.reduce && item == (int64_t)L.N * K - 1) fused_mean<T>(a);
 }
 
 // --------------------------------------------------------------------------
