@@ -6,11 +6,14 @@
 A step is one pass of the whole path over one batch of synthetic input
 already resident in HBM: for the default workload (4 x 2048 rows of 128000
 BF16 logits, label smoothing 0.1, mean over the 7782 non-ignored rows) that is
-ce_fwd_bwd_fused = count kernel + fused kernel (one read of the logits, the
-gradient written over them) + mean kernel.  Each timed step works on its own
-pre-generated copy of the logits from a pool in HBM (the call overwrites its
-input with the gradient; once the pool wraps, a step runs on a previous
-step's gradient, which costs the same work).
+ce_fwd_bwd_fused = prologue kernel (count of non-ignored rows, workspace
+clear) + fused kernel (one read of the logits, the gradient written over them,
+the mean summed by the workgroup that finishes last).  The call overwrites its
+input with the gradient, so each timed step works on its own copy of the
+logits from a pool in HBM, refreshed from the generated batch just before the
+timed region: every timed step sees the logits as generated, never a previous
+step's gradient (on this chip the kernel's duration depends on the values it
+reads, since it runs near the power limit).  Warmup steps reuse the pool.
 
 Printed: one JSON line with the whole-step throughput (formula bytes
 N*V*b read + N*V*b written, per step), the roofline of the fused kernel
@@ -97,7 +100,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--pool", type=int, default=8, help="device copies of the input (HBM)")
+    ap.add_argument("--pool", type=int, default=0,
+                    help="device copies of the input (HBM); 0 = one per timed step, as memory allows")
     ap.add_argument("--cpu-sample-rows", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-chunks", type=int, default=0, help="tuning: force the fused kernel's split")
@@ -130,8 +134,14 @@ def main():
     targets_dev = inputs.targets_phys.to(dev)
     view = (lambda p: p.transpose(0, 1)) if w.swapped else (lambda p: p)
     t_view = view(targets_dev)
-    P = max(1, min(args.pool, args.steps + args.warmup))
-    pool = [phys_dev] + [phys_dev.clone() for _ in range(P - 1)]
+    want = args.pool if args.pool > 0 else args.steps
+    free_b, _ = torch.cuda.mem_get_info(dev)
+    fit = int(0.6 * free_b) // max(1, phys_dev.numel() * phys_dev.element_size())
+    P = max(1, min(want, fit))
+    if P < args.steps:
+        print(f"[bench] pool of {P} copies < {args.steps} steps: some timed steps reuse a gradient",
+              file=sys.stderr, flush=True)
+    pool = [phys_dev.clone() for _ in range(P)] if w.calls != "shard" else None
     torch.cuda.synchronize()
 
     loss = torch.empty(1 if w.reduce_loss else N, dtype=torch.float32, device=dev)
@@ -156,9 +166,7 @@ def main():
             vce.ce_backward_inplace(x, t_view, lse, w.alpha, w.reduce_loss, grad_out=g, n_valid=n_valid)
     else:  # vocabulary shards: S partial-stat calls, one combine, S backward calls
         bounds = workloads.shard_bounds(V, w.shards)
-        shard_pool = [[p[..., a:c].contiguous() for a, c in bounds] for p in pool]
-        del pool
-        pool = shard_pool
+        pool = [[phys_dev[..., a:c].contiguous() for a, c in bounds] for _ in range(P)]
         stats = torch.empty((len(bounds), N, 4), dtype=torch.float32, device=dev)
         lse = torch.empty(N, dtype=torch.float32, device=dev)
         ws = torch.empty(vce.ce_combine_workspace_bytes(N, w.reduce_loss), dtype=torch.uint8, device=dev)
@@ -173,10 +181,21 @@ def main():
                 vce.ce_backward_inplace(shards[s], t_view, lse, w.alpha, w.reduce_loss, grad_out=g, n_valid=n_valid,
                                         vocab_start=a, vocab_total=V)
 
+    def refresh():
+        """Every pool copy back to the generated logits (outside any timed region)."""
+        for p in pool:
+            if isinstance(p, list):
+                for (a, c), sh in zip(bounds, p):
+                    sh.copy_(phys_dev[..., a:c])
+            else:
+                p.copy_(phys_dev)
+        torch.cuda.synchronize()
+
     for i in range(args.warmup):
         step(pool[i % P])
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    refresh()
 
     # the timed steps: nothing but the calls themselves between the two events
     e0 = torch.cuda.Event(enable_timing=True)
@@ -185,22 +204,25 @@ def main():
     h0 = time.perf_counter()
     e0.record()
     for i in range(args.steps):
-        step(pool[(args.warmup + i) % P])
+        step(pool[i % P])
     e1.record()
     torch.cuda.synchronize()
     h1 = time.perf_counter()
     step_ms = e0.elapsed_time(e1) / args.steps
     print(f"[bench] timed {args.steps} steps: {step_ms * 1e3:.1f} us/step (host {1e6 * (h1 - h0) / args.steps:.1f})",
           file=sys.stderr, flush=True)
-    # the same steps again with the library recording HIP events around each
-    # call's main kernel on the call's stream, for the kernel's own duration
+    # the same steps again, on refreshed copies, with the library recording HIP
+    # events around each call's main kernel on the call's stream, for the
+    # kernel's own duration
+    refresh()
     with vce.Profiler(args.steps * calls_per_step) as prof:
         for i in range(args.steps):
-            step(pool[(args.warmup + args.steps + i) % P])
+            step(pool[i % P])
         torch.cuda.synchronize()
+    del pool
+    torch.cuda.empty_cache()
 
     # plain device copy of the same byte count, for context (achievable read+write rate)
-    src = pool[0] if w.calls != "shard" else pool[0][0]
     flat = phys_dev.view(-1)
     dst = torch.empty_like(flat)
     for _ in range(3):
@@ -212,7 +234,7 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * flat.numel() * flat.element_size() / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
-    del dst, src
+    del dst
 
     main_ms = prof.ms
     roofline = None
@@ -240,7 +262,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {**w.describe(), "io_dtype": "bf16" if w.elem_bytes == 2 else "f32", "calls": w.calls,
-                   "split_chunks": args.split_chunks, "pool": P},
+                   "split_chunks": args.split_chunks, "pool": P, "fresh_inputs": P >= args.steps},
         "rows_per_s": round(N / (step_ms * 1e-3), 1),
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
         "formula_bytes_per_step": formula_bytes,
