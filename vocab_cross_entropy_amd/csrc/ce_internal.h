@@ -10,9 +10,8 @@ namespace vce {
 
 // Workspace header (first 256 bytes of every workspace).
 struct WsHeader {
-  unsigned long long ticket;  // split rows: next (row, chunk) work item
-  uint32_t status;            // nonzero: an exchange or final wait gave up
-  int32_t n_valid;            // count of non-ignored rows when the caller passed no n_valid
+  uint32_t status;   // nonzero: an exchange or final wait gave up
+  int32_t n_valid;   // count of non-ignored rows when the caller passed no n_valid
 };
 constexpr size_t kWsHeaderBytes = 256;
 
@@ -45,7 +44,7 @@ struct FusedArgs {
   const int32_t* n_valid;  // device count (read when reduce)
   float* row_loss;         // [N] loss output (reduce 0)
   unsigned long long* row_loss_tagged;  // [N] tagged per-row losses (reduce 1)
-  float* mean_out;         // [1] mean loss (reduce 1), written by the workgroup holding the last ticket
+  float* mean_out;         // [1] mean loss (reduce 1), written by the workgroup of the last item
   WsHeader* hdr;
   unsigned long long* slots;  // [N][K][4] tagged exchange words (K > 1)
 };
