@@ -104,12 +104,23 @@ typedef struct ce_params {
 
 /*
  * Workspace bytes that ce_forward and ce_fwd_bwd_fused need for logits
- * described by `x` and parameters `p`.  Returns 0 (and sets ce_last_error)
- * if the arguments are invalid.  The content of the workspace needs no
- * initialisation; the calls clear what they use.  Two calls must not use one
- * workspace concurrently.
+ * described by `x` and parameters `p` (a multiple of 256).  Returns 0 (and
+ * sets ce_last_error) if the arguments are invalid.  Two calls must not use
+ * one workspace concurrently.  ce_fwd_bwd_fused needs the workspace prepared
+ * once by ce_workspace_init; ce_forward and ce_shard_combine need no
+ * preparation and leave a prepared workspace prepared.
  */
 size_t ce_workspace_bytes(const ce_logits* x, const ce_params* p);
+
+/*
+ * Prepares a workspace of `ws_bytes` bytes (256-byte aligned, a multiple of
+ * 8) for ce_fwd_bwd_fused: enqueues one fill kernel on `stream` that zeroes it
+ * and records the size in its header.  Once is enough for any number of
+ * later calls whose workspace need is at most `ws_bytes`: each fused call tags
+ * the words it exchanges with a fresh value, so words left by earlier calls
+ * never need clearing.  Graph-capturable (no memset node).
+ */
+ce_status ce_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes that ce_shard_combine needs for `rows` rows. */
 size_t ce_combine_workspace_bytes(int64_t rows, const ce_params* p);
@@ -149,7 +160,12 @@ ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_
  *   grad_out  as for ce_backward_inplace (known before the call); NULL = 1
  *   loss      [N] or [1] device FP32, written
  *   n_valid   [1] device int32 or NULL
- *   ws        device workspace of at least ce_workspace_bytes(x, p) bytes
+ *   ws        device workspace of at least ce_workspace_bytes(x, p) bytes,
+ *             prepared by ce_workspace_init.  On a workspace that was not
+ *             prepared (or prepared smaller) the loss and the gradient come
+ *             out NaN and the workspace status records it (ce_workspace_check).
+ * One kernel launch: the first workgroups also count the non-ignored rows,
+ * and the workgroup of the last (row, chunk) item writes n_valid and the mean.
  */
 ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* grad_out,
                            float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -180,10 +196,12 @@ ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1
                            const ce_targets* t, const ce_params* p, float* loss, float* lse, int32_t* n_valid,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Waits for `stream` and reports whether a split-row exchange in the last call
- * that used `ws` gave up waiting (CE_EDEADLOCK) -- a diagnostic, never needed
- * for correct results. */
-ce_status ce_workspace_check(const void* ws, hipStream_t stream);
+/* Waits for `stream` and reports whether any call that used `ws` since it was
+ * prepared or last checked gave up waiting in a split-row exchange or count
+ * (CE_EDEADLOCK; its results were NaN) or found the workspace unprepared
+ * (CE_EWORKSPACE), then clears that record.  A diagnostic: synchronises, so
+ * not for the hot path. */
+ce_status ce_workspace_check(void* ws, hipStream_t stream);
 
 /*
  * Kernel timing for benchmarks.  After ce_profile_start(capacity), each of

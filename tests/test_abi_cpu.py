@@ -171,17 +171,26 @@ def test_workspace_sizes(lib):
     x = h.logits(d0=4, d1=2048, s0=2048 * 128000, s1=128000)
     p = h.params(reduce_loss=1, label_smoothing=0.1)
     n = lib.ce_workspace_bytes(ctypes.byref(x), ctypes.byref(p))
-    # header + per-row tagged losses + 4 chunks (of at most 4096 vectors) x 4 tagged words per row
-    assert n == 256 + 8192 * 8 + 8192 * 4 * 4 * 8
+    # header + FP32 losses of the split calls + the fused call's tagged losses
+    # + 4 chunks (of at most 4096 vectors) x 4 tagged words per row
+    assert n == 256 + 8192 * 4 + 8192 * 8 + 8192 * 4 * 4 * 8
     p0 = h.params()
     x1 = h.logits(d0=2, d1=512, s0=512 * 32000, s1=32000, v_local=32000, vocab_total=32000)
     assert lib.ce_workspace_bytes(ctypes.byref(x1), ctypes.byref(p0)) == 256
     assert lib.ce_workspace_bytes(ctypes.byref(h.logits(dtype=9)), ctypes.byref(p0)) == 0
-    assert lib.ce_combine_workspace_bytes(512, ctypes.byref(h.params(reduce_loss=1))) == 256 + 4096
+    assert lib.ce_combine_workspace_bytes(512, ctypes.byref(h.params(reduce_loss=1))) == 256 + 2048
     # forced split: chunks of at most one workgroup
     p3 = h.params(split_chunks=3)
     x2 = h.logits(d0=1, d1=10, s0=40960, s1=4096, v_local=4096, vocab_total=4096)
     assert lib.ce_workspace_bytes(ctypes.byref(x2), ctypes.byref(p3)) == 256 + (10 * 3 * 4 * 8 + 255) // 256 * 256
+
+
+def test_workspace_init_validates(lib):
+    # rejected before any HIP call (no GPU needed): NULL, misaligned, too small, not a multiple of 8
+    assert lib.ce_workspace_init(None, 4096, None) == _abi.CE_EINVAL
+    assert lib.ce_workspace_init(ctypes.c_void_p(0x10000 + 8), 4096, None) == _abi.CE_EWORKSPACE
+    assert lib.ce_workspace_init(ctypes.c_void_p(0x10000), 128, None) == _abi.CE_EWORKSPACE
+    assert lib.ce_workspace_init(ctypes.c_void_p(0x10000), 4100, None) == _abi.CE_EWORKSPACE
 
 
 def test_split_chunks_too_few_rejected(lib):

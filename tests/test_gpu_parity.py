@@ -36,7 +36,7 @@ def _s_of(g, reduce, n, N):
     return 1.0
 
 
-def check_fused(x, t, alpha, reduce, g=None, split_chunks=0, sample=None, what="", diag=True):
+def check_fused(x, t, alpha, reduce, g=None, split_chunks=0, sample=None, what="", diag=True, ws=None):
     """Run ce_fwd_bwd_fused on a device copy of (x, t) and compare with the oracle.
     Returns the device logits (holding the gradient) and the loss tensor."""
     d0, d1, V = x.shape
@@ -44,7 +44,8 @@ def check_fused(x, t, alpha, reduce, g=None, split_chunks=0, sample=None, what="
     say(f"[fused] {what} shape={tuple(x.shape)} strides={x.stride()} off={x.storage_offset()} {x.dtype} "
         f"a={alpha} reduce={reduce} K={split_chunks}")
     xd, td = to_device_view(x), to_device_view(t)
-    loss, n = vce.ce_fwd_bwd_fused(xd, td, alpha, reduce, grad_out=_g_tensor(g, reduce), split_chunks=split_chunks)
+    loss, n = vce.ce_fwd_bwd_fused(xd, td, alpha, reduce, grad_out=_g_tensor(g, reduce), split_chunks=split_chunks,
+                                   ws=ws)
     torch.cuda.synchronize()
     o = orc()
     n_ref = o.count_valid(t)

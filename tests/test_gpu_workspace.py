@@ -1,0 +1,110 @@
+"""The fused call's workspace on the GPU, through the C ABI.
+
+ce_fwd_bwd_fused tags every word its workgroups exchange with a fresh
+per-call value, so one workspace prepared once by ce_workspace_init serves
+any sequence of calls with no clearing in between; a workspace that was never
+prepared (or prepared smaller) makes the call fail loudly: NaN loss and
+gradient, and CE_EWORKSPACE from ce_workspace_check.  The row count n that
+the mean divides by is counted inside the fused kernel, over up to 16 target
+slices of at least 2048 rows.
+"""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import vocab_cross_entropy_amd as vce
+import workloads
+from gpu_util import ignored_rows, orc, rows_f64, say, to_device_view
+from test_gpu_parity import check_fused
+
+pytestmark = pytest.mark.gpu
+
+
+def _logits(shape, dtype, seed, sigma=2.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * sigma).to(dtype)
+
+
+def _raw_fused(xd, td, alpha, reduce, ws, split_chunks=0):
+    """ce_fwd_bwd_fused through the C ABI, without the binding's preparation of ``ws``."""
+    N = xd.shape[0] * xd.shape[1]
+    loss = torch.empty(1 if reduce else N, dtype=torch.float32, device="cuda")
+    n = torch.empty(1, dtype=torch.int32, device="cuda")
+    p = vce.params(alpha, reduce, -100, split_chunks)
+    rc = vce.lib.ce_fwd_bwd_fused(ctypes.byref(vce.logits_desc(xd)), ctypes.byref(vce.targets_desc(td)),
+                                  ctypes.byref(p), None, ctypes.c_void_p(loss.data_ptr()),
+                                  ctypes.c_void_p(n.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0, vce.lib.ce_last_error()
+    torch.cuda.synchronize()
+    return loss, n
+
+
+def _expect_unprepared(ws):
+    with pytest.raises(vce.CeArgumentError) as e:
+        vce.ce_workspace_check(ws)
+    assert e.value.status == vce._abi.CE_EWORKSPACE
+    vce.ce_workspace_check(ws)  # the record was cleared
+
+
+def test_unprepared_workspace_fails_loudly():
+    x = _logits((2, 8, 4096), torch.bfloat16, seed=7)
+    t = workloads.random_targets((2, 8), 4096, seed=7, ignore_frac=0.25)
+    keep = np.setdiff1d(np.arange(16), ignored_rows(t))
+    nb = vce.ce_workspace_bytes(x.cuda(), 0.1, True, split_chunks=2)
+
+    say("[ws] garbage workspace, never prepared")
+    ws = torch.full((nb,), 0xAB, dtype=torch.uint8, device="cuda")
+    xd, td = to_device_view(x), to_device_view(t)
+    loss, n = _raw_fused(xd, td, 0.1, True, ws, split_chunks=2)
+    assert math.isnan(loss.item())
+    assert int(n.item()) == orc().count_valid(t)  # the count does not depend on the workspace
+    assert np.isnan(rows_f64(xd, keep)).all()
+    _expect_unprepared(ws)
+
+    say("[ws] workspace prepared smaller than the call needs")
+    vce.ce_workspace_init(ws[: nb - 256])
+    xd = to_device_view(x)
+    loss, _ = _raw_fused(xd, td, 0.1, True, ws, split_chunks=2)
+    assert math.isnan(loss.item())
+    _expect_unprepared(ws)
+
+    say("[ws] prepared: results match the oracle")
+    vce.ce_workspace_init(ws)
+    check_fused(x, t, 0.1, True, split_chunks=2, ws=ws, what="prepared")
+    vce.ce_workspace_check(ws)
+
+
+def test_one_workspace_serves_a_sequence_of_calls():
+    cases = [((2, 9, 4096), torch.bfloat16, 2, True, 0.1),
+             ((3, 5, 8192), torch.float32, 4, False, 0.0),
+             ((2, 9, 4096), torch.bfloat16, 2, True, 0.1),  # same shape again: last call's words are stale
+             ((1, 40, 1000), torch.bfloat16, 0, True, 0.0),
+             ((4, 4, 32003), torch.bfloat16, 3, False, 0.1),
+             ((2, 9, 4096), torch.bfloat16, 7, True, 0.1)]
+    nb = max(vce.ce_workspace_bytes(torch.empty(s, dtype=dt, device="cuda"), a, r, split_chunks=K)
+             for s, dt, K, r, a in cases)
+    ws = vce.ce_workspace_init(torch.empty(nb, dtype=torch.uint8, device="cuda"))
+    for i, (shape, dtype, K, reduce, alpha) in enumerate(cases):
+        x = _logits(shape, dtype, seed=100 + i)
+        t = workloads.random_targets(shape[:2], shape[2], seed=100 + i, ignore_frac=0.2)
+        check_fused(x, t, alpha, reduce, g=1.0 if reduce else None, split_chunks=K, ws=ws, what=f"sequence {i}")
+    vce.ce_workspace_check(ws)
+
+
+# rows around one slice (2048), several slices, and the 16-slice cap (slices grow past 2048 rows)
+@pytest.mark.parametrize("N", [1, 2047, 2049, 6000, 40000])
+@pytest.mark.parametrize("reduce", [False, True])
+def test_count_over_target_slices(N, reduce):
+    # physical (d1, d0) targets passed as the transposed (d0, d1) view: strided count
+    d0 = 8 if N % 8 == 0 else 1
+    d1 = N // d0
+    V = 64
+    phys = _logits((d1, d0, V), torch.bfloat16, seed=N)
+    x = phys.transpose(0, 1)
+    tp = workloads.random_targets((d1, d0), V, seed=N, ignore_frac=0.3)
+    t = tp.transpose(0, 1)
+    check_fused(x, t, 0.1, reduce, g=1.0 if reduce else None, what=f"count N={d0 * d1}")

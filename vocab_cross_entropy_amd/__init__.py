@@ -16,6 +16,7 @@ and the interface of the TransformerEngineNPU issue #29 page (section 1):
 from __future__ import annotations
 
 import ctypes
+import weakref
 
 import torch
 
@@ -24,7 +25,8 @@ from ._abi import CE_BF16, CE_F32, CeArgumentError, CeError
 
 __all__ = [
     "ce_forward", "ce_backward_inplace", "ce_fwd_bwd_fused", "ce_shard_partial_stats", "ce_shard_combine",
-    "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_check", "parallel_cross_entropy",
+    "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_init", "ce_workspace_check",
+    "parallel_cross_entropy",
     "Profiler", "CeError", "CeArgumentError", "lib",
 ]
 
@@ -85,6 +87,26 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+# Workspace tensors this binding has prepared with ce_workspace_init, by
+# object identity (id -> weak reference; a new tensor over reused memory is
+# prepared again).  Not a WeakSet: that compares tensors with ==.
+_prepared: dict[int, weakref.ref] = {}
+
+
+def _is_prepared(ws: torch.Tensor) -> bool:
+    r = _prepared.get(id(ws))
+    return r is not None and r() is ws
+
+
+def ce_workspace_init(ws: torch.Tensor) -> torch.Tensor:
+    """Prepare ``ws`` (uint8 device tensor) for ce_fwd_bwd_fused; once is enough."""
+    _check(lib.ce_workspace_init(_ptr(ws), ws.numel(), _stream(ws.device)))
+    for k in [k for k, r in _prepared.items() if r() is None]:
+        del _prepared[k]
+    _prepared[id(ws)] = weakref.ref(ws)
+    return ws
+
+
 def ce_workspace_bytes(x: torch.Tensor, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100,
                        split_chunks=0) -> int:
     n = lib.ce_workspace_bytes(ctypes.byref(logits_desc(x)),
@@ -143,6 +165,8 @@ def ce_fwd_bwd_fused(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-1
         if nb == 0:
             _check(_abi.CE_EINVAL)
         ws = _workspace(nb, dev)
+    if not _is_prepared(ws):
+        ce_workspace_init(ws)
     _check(lib.ce_fwd_bwd_fused(ctypes.byref(xd), ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(grad_out),
                                 _ptr(loss), _ptr(n_valid), _ptr(ws), ws.numel(), _stream(dev)))
     return loss, n_valid
@@ -181,7 +205,9 @@ def ce_shard_combine(stats, t, vocab_total, label_smoothing=0.0, reduce_loss=Fal
 
 
 def ce_workspace_check(ws: torch.Tensor):
-    """Raises CeError(CE_EDEADLOCK) if a split row of the last call gave up waiting."""
+    """Raises CeError(CE_EDEADLOCK) if a call since the last check gave up
+    waiting, CeArgumentError(CE_EWORKSPACE) if a fused call found ``ws``
+    unprepared; clears that record.  Synchronises the stream."""
     _check(lib.ce_workspace_check(_ptr(ws), _stream(ws.device)))
 
 

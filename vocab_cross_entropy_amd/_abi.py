@@ -59,6 +59,7 @@ SIGNATURES = {
     "ce_shard_partial_stats": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp]),
     "ce_shard_combine": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                         _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "ce_workspace_init": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp]),
     "ce_workspace_check": (ctypes.c_int, [_vp, _vp]),
     "ce_profile_start": (ctypes.c_int, [ctypes.c_int32]),
     "ce_profile_stop": (ctypes.c_int, [_vp, ctypes.c_int32, _P(ctypes.c_int32)]),

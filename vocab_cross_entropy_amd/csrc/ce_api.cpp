@@ -6,7 +6,12 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
 #include <mutex>
+#include <random>
 #include <vector>
 
 #include <hip/hip_runtime_api.h>
@@ -111,31 +116,56 @@ ce_status check_targets(const ce_targets* t, int64_t N) {
 }
 
 struct WsLayout {
-  size_t row_loss = 0;  // offset of [N] FP32 per-row losses (reduce only)
-  size_t slots = 0;     // offset of [N][K][4] u64 exchange words (K > 1)
-  int64_t nslots = 0;
+  size_t row_loss = 0;         // offset of [N] FP32 per-row losses (ce_forward / ce_shard_combine, reduce only)
+  size_t row_loss_tagged = 0;  // offset of [N] tagged per-row losses (ce_fwd_bwd_fused, reduce only)
+  size_t slots = 0;            // offset of [N][K][4] tagged exchange words (ce_fwd_bwd_fused, K > 1)
   size_t total = 0;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// header | per-row losses (8 bytes a row: FP32, or a tagged word in the fused
-// call) | split-row exchange words.  Everything after the header is cleared by
-// the fused call's prologue.
-WsLayout ws_layout(int64_t N, int32_t K, bool reduce) {
+// header | FP32 per-row losses of the split calls | the fused call's tagged
+// per-row losses | its split-row exchange words.  The fused call's regions
+// come after everything the other calls write, so a workspace shared by
+// several entry points never holds their values where the fused call looks
+// for its tags.
+WsLayout ws_layout(int64_t N, int32_t K, bool reduce, bool fused) {
   WsLayout w;
   size_t off = vce::kWsHeaderBytes;
   if (reduce) {
     w.row_loss = off;
+    off = align256(off + (size_t)N * 4u);
+  }
+  if (fused && reduce) {
+    w.row_loss_tagged = off;
     off = align256(off + (size_t)N * 8u);
   }
-  if (K > 1) {
+  if (fused && K > 1) {
     w.slots = off;
-    w.nslots = N * K * 4;
-    off = align256(off + (size_t)w.nslots * 8u);
+    off = align256(off + (size_t)N * (size_t)K * 4u * 8u);
   }
   w.total = off;
   return w;
+}
+
+// Tags of fused calls: consecutive values of a process-wide counter (low 32
+// bits, 0 skipped), so 2^32 - 1 calls in a row never share one.  The counter
+// starts at a random point, so a workspace that moved between processes
+// without ce_workspace_init is unlikely to hold a word with the next tag.
+std::atomic<uint64_t>& tag_counter() {
+  static std::atomic<uint64_t> c([] {
+    std::random_device rd;
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    return ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ t ^ ((uint64_t)getpid() << 16);
+  }());
+  return c;
+}
+
+uint32_t next_tag() {
+  for (;;) {
+    const uint32_t t = (uint32_t)tag_counter().fetch_add(1, std::memory_order_relaxed);
+    if (t) return t;
+  }
 }
 
 int32_t chunks_for(const ce_logits* x, const ce_params* p) {
@@ -200,7 +230,7 @@ const char* ce_status_string(ce_status s) {
 
 size_t ce_workspace_bytes(const ce_logits* x, const ce_params* p) {
   if (check_params(p) != CE_OK || check_logits(x, false) != CE_OK) return 0;
-  return ws_layout(x->d0 * x->d1, chunks_for(x, p), p->reduce_loss != 0).total;
+  return ws_layout(x->d0 * x->d1, chunks_for(x, p), p->reduce_loss != 0, true).total;
 }
 
 size_t ce_combine_workspace_bytes(int64_t rows, const ce_params* p) {
@@ -209,7 +239,7 @@ size_t ce_combine_workspace_bytes(int64_t rows, const ce_params* p) {
     fail(CE_EINVAL, "rows %lld out of range", (long long)rows);
     return 0;
   }
-  return ws_layout(rows, 1, p->reduce_loss != 0).total;
+  return ws_layout(rows, 1, p->reduce_loss != 0, false).total;
 }
 
 ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p, float* loss, float* lse,
@@ -219,7 +249,7 @@ ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p
   const int64_t N = x->d0 * x->d1;
   if ((st = check_targets(t, N))) return st;
   if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
-  const WsLayout w = ws_layout(N, 1, p->reduce_loss != 0);
+  const WsLayout w = ws_layout(N, 1, p->reduce_loss != 0, false);
   if (!ws || ws_bytes < w.total)
     return fail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
   if (((uintptr_t)ws) % 256u) return fail(CE_EWORKSPACE, "workspace must be 256-byte aligned");
@@ -283,41 +313,43 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
     return fail(CE_ELAYOUT, "split_chunks %d leaves %lld vectors per chunk, above one workgroup's %d",
                 p->split_chunks, (long long)C, 1024 * 16);
   if (N * K > kMaxGrid) return fail(CE_EINVAL, "rows x chunks exceeds the launch grid");
-  const WsLayout w = ws_layout(N, K, p->reduce_loss != 0);
+  const WsLayout w = ws_layout(N, K, p->reduce_loss != 0, true);
   if (!ws || ws_bytes < w.total)
     return fail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
   if (((uintptr_t)ws) % 256u) return fail(CE_EWORKSPACE, "workspace must be 256-byte aligned");
 
   char* wsb = static_cast<char*>(ws);
   auto* hdr = reinterpret_cast<vce::WsHeader*>(wsb);
-  int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
-  auto* slots = K > 1 ? reinterpret_cast<unsigned long long*>(wsb + w.slots) : nullptr;
-  // the prologue clears everything after the header: tagged row losses and exchange words
-  auto* clear_begin = reinterpret_cast<unsigned long long*>(wsb + vce::kWsHeaderBytes);
-  const int64_t nclear = (int64_t)((w.total - vce::kWsHeaderBytes) / 8u);
   hipError_t e;
-  if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, clear_begin, nclear,
-                                stream)))
-    return hip_fail(e, "prologue launch");
+  if (N == 0) {  // nothing to read: n = 0, and the mean of no rows is 0/0
+    int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
+    if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
+      return hip_fail(e, "prologue launch");
+    if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, n_out, loss, stream))) return hip_fail(e, "mean launch");
+    return CE_OK;
+  }
   vce::FusedArgs a;
   a.L = row_layout(x, t, p);
   a.K = K;
   a.aligned = rows_aligned16(x);
   a.C = C;
   a.reduce = p->reduce_loss;
+  a.tag = next_tag();
   a.g = grad_out;
-  a.n_valid = n_out;
+  a.n_out = n_valid;
   a.row_loss = p->reduce_loss ? nullptr : loss;
-  a.row_loss_tagged = p->reduce_loss ? reinterpret_cast<unsigned long long*>(wsb + w.row_loss) : nullptr;
+  a.row_loss_tagged = p->reduce_loss ? reinterpret_cast<unsigned long long*>(wsb + w.row_loss_tagged) : nullptr;
   a.mean_out = p->reduce_loss ? loss : nullptr;
   a.hdr = hdr;
-  a.slots = slots;
+  a.slots = K > 1 ? reinterpret_cast<unsigned long long*>(wsb + w.slots) : nullptr;
+  // at most kMaxSlices target slices of at least 2048 rows, counted by the first workgroups
+  a.slice_rows = (N + vce::kMaxSlices - 1) / vce::kMaxSlices;
+  if (a.slice_rows < 2048) a.slice_rows = 2048;
+  a.nslice = (int32_t)((N + a.slice_rows - 1) / a.slice_rows);
+  a.ws_bytes = w.total;
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
   if ((e = vce::launch_fused(a, shape, stream, e0, e1))) return hip_fail(e, "fused launch");
-  // with rows, the fused kernel writes the mean itself; with none it is 0/0
-  if (p->reduce_loss && N == 0 && (e = vce::launch_mean(nullptr, 0, n_out, loss, stream)))
-    return hip_fail(e, "mean launch");
   return CE_OK;
 }
 
@@ -356,7 +388,7 @@ ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1
   if (N > 0 && !stats) return fail(CE_EINVAL, "stats is NULL");
   if (((uintptr_t)stats) % 16u) return fail(CE_ELAYOUT, "stats must be 16-byte aligned");
   if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
-  const WsLayout w = ws_layout(N, 1, p->reduce_loss != 0);
+  const WsLayout w = ws_layout(N, 1, p->reduce_loss != 0, false);
   if (!ws || ws_bytes < w.total)
     return fail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
   if (((uintptr_t)ws) % 256u) return fail(CE_EWORKSPACE, "workspace must be 256-byte aligned");
@@ -386,14 +418,28 @@ ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1
   return CE_OK;
 }
 
-ce_status ce_workspace_check(const void* ws, hipStream_t stream) {
+ce_status ce_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws) return fail(CE_EINVAL, "workspace is NULL");
+  if (((uintptr_t)ws) % 256u) return fail(CE_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < vce::kWsHeaderBytes || ws_bytes % 8u)
+    return fail(CE_EWORKSPACE, "workspace of %zu bytes: need a multiple of 8, at least %zu", ws_bytes,
+                vce::kWsHeaderBytes);
+  hipError_t e;
+  if ((e = vce::launch_ws_init(ws, ws_bytes, stream))) return hip_fail(e, "workspace init launch");
+  return CE_OK;
+}
+
+ce_status ce_workspace_check(void* ws, hipStream_t stream) {
   if (!ws) return fail(CE_EINVAL, "workspace is NULL");
   hipError_t e;
   if ((e = hipStreamSynchronize(stream))) return hip_fail(e, "stream synchronize");
   vce::WsHeader h;
   if ((e = hipMemcpy(&h, ws, sizeof h, hipMemcpyDeviceToHost))) return hip_fail(e, "workspace read");
-  if (h.status) return fail(CE_EDEADLOCK, "a split row gave up waiting for its partner chunks");
-  return CE_OK;
+  if (!h.status) return CE_OK;
+  const uint32_t zero = 0;
+  if ((e = hipMemcpy(ws, &zero, sizeof zero, hipMemcpyHostToDevice))) return hip_fail(e, "workspace status clear");
+  if (h.status & 2u) return fail(CE_EWORKSPACE, "ce_fwd_bwd_fused ran on a workspace that ce_workspace_init has not prepared (or prepared smaller)");
+  return fail(CE_EDEADLOCK, "a split row gave up waiting for its partner chunks");
 }
 
 ce_status ce_profile_start(int32_t capacity) {

@@ -2,6 +2,7 @@
 // kernels (ce_kernels.hip).  Host-side only types; no torch, no allocation.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -9,11 +10,21 @@
 namespace vce {
 
 // Workspace header (first 256 bytes of every workspace).
+constexpr int kMaxSlices = 16;
 struct WsHeader {
-  uint32_t status;   // nonzero: an exchange or final wait gave up
-  int32_t n_valid;   // count of non-ignored rows when the caller passed no n_valid
+  uint32_t status;                 // bit 0: a wait gave up; bit 1: the workspace was not initialised
+  int32_t n_valid;                 // count of non-ignored rows when the caller passed no n_valid
+  unsigned long long magic;        // kWsMagic once ce_workspace_init has run
+  unsigned long long init_bytes;   // bytes ce_workspace_init cleared
+  unsigned long long reserved[13];
+  unsigned long long counts[kMaxSlices];  // fused call: tagged counts of non-ignored rows per target slice
 };
 constexpr size_t kWsHeaderBytes = 256;
+static_assert(sizeof(WsHeader) == kWsHeaderBytes, "workspace header is 256 bytes");
+// k_ws_init writes the header by word index: word 1 = magic, word 2 = init_bytes
+static_assert(offsetof(WsHeader, magic) == 8 && offsetof(WsHeader, init_bytes) == 16, "header word layout");
+static_assert(offsetof(WsHeader, counts) == 128, "header word layout");
+constexpr unsigned long long kWsMagic = 0x43452d5753304331ull;
 
 // Which template instance of the fused kernel a plan uses.
 struct FusedShape {
@@ -40,13 +51,17 @@ struct FusedArgs {
   int32_t aligned;         // every row starts and ends on a 16-byte boundary (no head/tail)
   int64_t C;               // body vectors per chunk
   int32_t reduce;          // mean over non-ignored rows
+  uint32_t tag;            // this call's tag: high half of every word it publishes (never 0)
   const float* g;          // upstream gradient ([N] or [1]); NULL = 1
-  const int32_t* n_valid;  // device count (read when reduce)
+  int32_t* n_out;          // [1] count of non-ignored rows (nullable), written by the last item's workgroup
   float* row_loss;         // [N] loss output (reduce 0)
   unsigned long long* row_loss_tagged;  // [N] tagged per-row losses (reduce 1)
   float* mean_out;         // [1] mean loss (reduce 1), written by the workgroup of the last item
   WsHeader* hdr;
   unsigned long long* slots;  // [N][K][4] tagged exchange words (K > 1)
+  int64_t slice_rows;      // rows per target slice; workgroup b < nslice counts slice b
+  unsigned long long ws_bytes;  // workspace bytes this call uses (checked against the initialised size)
+  int32_t nslice;
 };
 
 enum StatsMode { kStatsForward = 0, kStatsShard = 1 };
@@ -92,5 +107,6 @@ hipError_t launch_stats(const StatsArgs& a, hipStream_t stream, hipEvent_t ev0, 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out, hipStream_t stream);
+hipError_t launch_ws_init(void* ws, size_t bytes, hipStream_t stream);
 
 }  // namespace vce

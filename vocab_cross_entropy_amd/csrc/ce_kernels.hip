@@ -32,8 +32,6 @@ namespace {
 
 constexpr float kL = 1.44269504088896340736f;     // log2(e)
 constexpr float kLn2 = 0.69314718055994530942f;  // ln(2)
-// High half of a published exchange word; a cleared word never carries it.
-constexpr uint32_t kTagHi = 0x5EEDC0DEu;
 // Bound on polling iterations of one lane waiting for a partner chunk
 // (each iteration sleeps ~128 cycles: ~0.2 s in total), after which the
 // row is finished with NaN and the workspace status word is set.
@@ -374,6 +372,21 @@ __global__ __launch_bounds__(1024) void k_prologue(const int64_t* tgt, int64_t t
 }
 
 // --------------------------------------------------------------------------
+// Words the fused kernel's workgroups exchange are 64 bits: the call's tag
+// in the high half, a 32-bit payload in the low half, written and read with
+// relaxed agent-scope atomics.  Every call draws a fresh nonzero tag, so a
+// word left by an earlier call (or the zeros of ce_workspace_init) never
+// passes for this call's, and the workspace needs no clearing between calls.
+__device__ __forceinline__ unsigned long long tagged(uint32_t tag, uint32_t payload) {
+  return ((unsigned long long)tag << 32) | payload;
+}
+__device__ __forceinline__ void publish(unsigned long long* p, uint32_t tag, uint32_t payload) {
+  __hip_atomic_store(p, tagged(tag, payload), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long poll(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Publish a fused row's loss.  Without reduction it goes straight to
 // loss[r]; with the mean, chunk 0 of each row publishes a tagged word
 // (fire-and-forget, no round trip before the workgroup exits).
@@ -383,17 +396,78 @@ __device__ __forceinline__ void publish_row_loss(const FusedArgs& a, int64_t r, 
   if (!a.reduce)
     a.row_loss[r] = loss;
   else
-    __hip_atomic_store(a.row_loss_tagged + r, ((unsigned long long)kTagHi << 32) | __float_as_uint(loss),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    publish(a.row_loss_tagged + r, a.tag, __float_as_uint(loss));
 }
 
-// The mean, computed by the workgroup of the last item once its own item is
-// done: it starts after every other workgroup of the launch (in-order
-// dispatch, see k_fused), none of which waits for it, so every tag arrives.
-// The N losses are summed in index order in FP64 (deterministic).
+// n = #{rows whose target is not ignore_idx}, counted inside the fused kernel:
+// workgroup b < nslice counts rows [b * slice_rows, (b + 1) * slice_rows)
+// before anything else and publishes a tagged count in the header.  Those
+// workgroups start first and wait for nothing, so the counts always arrive.
 template <int T>
-__device__ void fused_mean(const FusedArgs& a) {
+__device__ void count_slice(const FusedArgs& a, int64_t b) {
+  __shared__ int csh[T / 64];
+  const RowLayout& L = a.L;
+  const int64_t r0 = b * a.slice_rows;
+  const int64_t r1 = r0 + a.slice_rows < L.N ? r0 + a.slice_rows : L.N;
+  int cnt = 0;
+  for (int64_t r = r0 + threadIdx.x; r < r1; r += T) {
+    const int64_t i0 = r / L.d1, i1 = r - i0 * L.d1;
+    cnt += L.tgt[i0 * L.ts0 + i1 * L.ts1] != L.ignore_idx;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  if ((threadIdx.x & 63) == 0) csh[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int i = 0; i < T / 64; ++i) n += csh[i];
+    publish(&a.hdr->counts[b], a.tag, (uint32_t)n);
+  }
+}
+
+// The slice counts as seen by one wave: lane q < nslice holds count q's word,
+// read with an agent-scope load (issued early, its round trip overlaps other
+// loads); lanes whose word does not carry this call's tag yet poll it again,
+// bounded.  (A plain, cached load could keep a stale line in an XCD's L2.)
+__device__ __forceinline__ unsigned long long count_word_early(const FusedArgs& a) {
+  const int lane = threadIdx.x & 63;
+  return lane < a.nslice ? poll(&a.hdr->counts[lane]) : 0ull;
+}
+__device__ int32_t wave_count(const FusedArgs& a, unsigned long long w, bool* ok) {
+  const int lane = threadIdx.x & 63;
+  const bool mine = lane < a.nslice;
+  bool ready = !mine || (uint32_t)(w >> 32) == a.tag;
+  uint32_t spins = 0;
+  while (!__all(ready) && spins <= kSpinLimit) {
+    if (!ready) {
+      w = poll(&a.hdr->counts[lane]);
+      ready = (uint32_t)(w >> 32) == a.tag;
+    }
+    ++spins;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  *ok = __all(ready);
+  int c = mine ? (int)(uint32_t)w : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  return c;
+}
+
+// The last item's workgroup finishes the call once its own item is done: it
+// starts after every other workgroup of the launch (in-order dispatch, see
+// k_fused), none of which waits for it, so every tagged word arrives.  It
+// writes n and, with the mean, sums the N losses in index order in FP64
+// (deterministic).
+template <int T>
+__device__ void fused_finish(const FusedArgs& a) {
   __shared__ double s_sum[T / 64];
+  bool cnt_ok = true;
+  const int32_t n = wave_count(a, count_word_early(a), &cnt_ok);
+  if (threadIdx.x == 0) {
+    if (!cnt_ok) atomicOr(&a.hdr->status, 1u);
+    if (a.n_out) a.n_out[0] = n;
+  }
+  if (!a.reduce) return;
   constexpr int U = 16;  // independent loads in flight per thread; missing words are polled again
   double acc = 0.0;
   uint32_t spins = 0;
@@ -403,19 +477,18 @@ __device__ void fused_mean(const FusedArgs& a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + (int64_t)u * T + threadIdx.x;
-      w[u] = i < a.L.N ? __hip_atomic_load(a.row_loss_tagged + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                       : ((unsigned long long)kTagHi << 32);
+      w[u] = i < a.L.N ? poll(a.row_loss_tagged + i) : tagged(a.tag, 0u);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + (int64_t)u * T + threadIdx.x;
-      while ((uint32_t)(w[u] >> 32) != kTagHi && !gave_up) {
+      while ((uint32_t)(w[u] >> 32) != a.tag && !gave_up) {
         if (++spins > kSpinLimit) {
           gave_up = true;
           break;
         }
         __builtin_amdgcn_s_sleep(2);
-        w[u] = __hip_atomic_load(a.row_loss_tagged + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w[u] = poll(a.row_loss_tagged + i);
       }
       acc += gave_up ? __builtin_nan("") : (double)__uint_as_float((uint32_t)w[u]);
     }
@@ -428,7 +501,8 @@ __device__ void fused_mean(const FusedArgs& a) {
   if (threadIdx.x == 0) {
     double tot = 0.0;
     for (int i = 0; i < T / 64; ++i) tot += s_sum[i];
-    a.mean_out[0] = (float)(tot / (double)(*a.n_valid));  // N >= 1 here; n = 0 gives 0/0 = NaN
+    // N >= 1 here; n = 0 gives 0/0 = NaN
+    a.mean_out[0] = cnt_ok ? (float)(tot / (double)n) : __builtin_nanf("");
   }
 }
 
@@ -463,11 +537,14 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
   constexpr int E = ElemT<DT>::E;
   __shared__ float sh[T / 64][4];
   __shared__ float xs[64 * 4];
+  __shared__ int sh_n;
   const int tid = threadIdx.x;
   const RowLayout& L = a.L;
   const int K = a.K;
 
   const int64_t item = blockIdx.x;
+  if (item < a.nslice) count_slice<T>(a, item);
+  const int64_t last_item = L.N * K - 1;
   const int64_t r = item / K;
   const int k = (int)(item - r * K);
   if (r >= L.N) return;
@@ -487,21 +564,31 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       if (last && tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
     }
     publish_row_loss<T>(a, r, 0.f, first);
-    if (a.reduce && item == (int64_t)L.N * K - 1) fused_mean<T>(a);
+    if (item == last_item) fused_finish<T>(a);
     return;
   }
 
-  // the upstream gradient scale, loaded now so the round trip overlaps the chunk loads
-  const float s_up = grad_scale(a.reduce, a.g, a.n_valid, r);
 
   // ---- the single read of this chunk (slots past the chunk read as zero
   // and are masked below; their stores are dropped)
   const Rsrc rb = make_rsrc(body, (int64_t)nvc * 16);
   const Rsrc rh = make_rsrc(g.base, HT && first ? g.h * ElemT<DT>::EB : 0);
   const Rsrc rt = make_rsrc(g.tail, HT && last ? (int64_t)g.tn * ElemT<DT>::EB : 0);
+  // The slice counts (wave 0, an agent-scope load to memory) go out before
+  // the chunk loads, so their round trip overlaps them; the upstream
+  // gradient after.  The workspace's initialisation record is read with
+  // scalar loads (constant address space: nothing writes it during the
+  // kernel), which keeps it out of the vector loads' in-order completion
+  // count, and is combined without branches, so no wait is placed before the
+  // chunk is in flight.
+  const unsigned long long cw = (a.reduce && tid < 64) ? count_word_early(a) : 0ull;
+  typedef const __attribute__((address_space(4))) unsigned long long* ConstU64;
+  const ConstU64 wsrec = (ConstU64)(&a.hdr->magic);
+  const bool ws_ok = (wsrec[0] == kWsMagic) & (wsrec[1] >= a.ws_bytes);
   uint4 v[P];
 #pragma unroll
   for (int j = 0; j < P; ++j) v[j] = bload16(rb, (uint32_t)(j * T + tid) * 16u);
+  const float g_up = a.g ? a.g[a.reduce ? 0 : r] : 1.f;
   const bool hv = HT && first && tid < g.h, tv = HT && last && tid < g.tn;
   float hx = -INFINITY, tx = -INFINITY;
   if (HT) {
@@ -555,7 +642,20 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     }
   }
   const float m_loc = m;  // this thread's own maximum (bounds its largest softmax term)
+  if (a.reduce && tid < 64) {  // n, handed to the other waves by block_max's barrier
+    bool ok;
+    const int32_t n = wave_count(a, cw, &ok);
+    if (tid == 0) sh_n = ok ? n : -1;
+  }
   m = block_max<T>(m, sh);
+  // s = g / n with the mean, g_r without; NaN (loud) when a count never
+  // arrived or the workspace was not initialised
+  float s_up = g_up;
+  if (a.reduce) s_up = sh_n >= 0 ? g_up / (float)sh_n : __builtin_nanf("");
+  if (!ws_ok) {
+    s_up = __builtin_nanf("");
+    if (tid == 0) atomicOr(&a.hdr->status, 2u);
+  }
   const float m2 = m * kL;
   const float msub = (m == -INFINITY) ? 0.f : m2;
 #pragma unroll
@@ -639,8 +739,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       const float mine[4] = {m2, d, y, rs};
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        __hip_atomic_store(row_slots + 4 * k + q, ((unsigned long long)kTagHi << 32) | __float_as_uint(mine[q]),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        publish(row_slots + 4 * k + q, a.tag, __float_as_uint(mine[q]));
     }
     if (tid < 64) {
       uint32_t spins = 0;
@@ -648,8 +747,8 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       for (int w = tid; w < 4 * K; w += 64) {
         unsigned long long val = 0ull;
         for (;;) {
-          val = __hip_atomic_load(row_slots + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if ((uint32_t)(val >> 32) == kTagHi) break;
+          val = poll(row_slots + w);
+          if ((uint32_t)(val >> 32) == a.tag) break;
           if (++spins > kSpinLimit) {
             gave_up = true;
             break;
@@ -684,7 +783,8 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
   const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
   const float inv_v = 1.f / (float)L.vocab_total;
   const float lse = c_hi * kLn2 + c_lo * kLn2;
-  const float row_loss = tvalid ? lse - (1.f - L.alpha) * Y - (L.alpha * inv_v) * R : __uint_as_float(0x7fc00000u);
+  const float row_loss = tvalid && ws_ok ? lse - (1.f - L.alpha) * Y - (L.alpha * inv_v) * R
+                                        : __uint_as_float(0x7fc00000u);
 
   // ---- gradient from the registers, written over the logits
   const float s = tvalid ? s_up : __uint_as_float(0x7fc00000u);
@@ -727,7 +827,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       bstore_elem<DT>(g_t, rb, (own_j * T + tid) * E + own_e);
   }
   publish_row_loss<T>(a, r, row_loss, first);
-  if (a.reduce && item == (int64_t)L.N * K - 1) fused_mean<T>(a);
+  if (item == last_item) fused_finish<T>(a);
 }
 
 // --------------------------------------------------------------------------
@@ -977,13 +1077,29 @@ FusedShape fused_shape_for(int64_t vecs) {
 
 int64_t max_body_vecs(int32_t dtype, int64_t V) { return V / (dtype == CE_BF16 ? 8 : 4); }
 
-// Rows are split into chunks of at most 4096 vectors (64 KiB), held by 512
-// threads x 8 vectors: on the 128000-column BF16 rows four such chunks per
-// row measured faster than 1, 2, 3, 6 or 8 chunks.
+// Rows of up to 4096 vectors stay whole.  Longer rows are split into K
+// chunks held by 256 x 8 (2048 vectors) or 512 x 8 (4096 vectors)
+// workgroups; K is the one between ceil(nv / 4096) and ceil(nv / 2048) whose
+// chunks fill their workgroup's registers best (the fewer chunks on a tie
+// within 1%).  Measured on 8192 BF16 rows: how full the registers are
+// matters most (V = 100000: 7 chunks at 87% beat 4 at 76% by 7%; V = 49152:
+// 3 at 100% beat 2 at 75% by 4%), and between equally full options the one
+// with fewer chunks was as fast or faster at 65536, 152064 and 256000
+// columns (at 128000, 4 and 8 chunks measured within 1%).
 int32_t fused_auto_chunks(int32_t dtype, int64_t V) {
-  const int64_t cap = 256 * 16;
   const int64_t nv = max_body_vecs(dtype, V);
-  return nv <= cap ? 1 : (int32_t)((nv + cap - 1) / cap);
+  if (nv <= 4096) return 1;
+  int64_t best_k = (nv + 4095) / 4096;
+  double best_fill = 0.0;
+  for (int64_t k = (nv + 4095) / 4096; k <= (nv + 2047) / 2048; ++k) {
+    const int64_t c = (nv + k - 1) / k;
+    const double fill = (double)c / (c <= 2048 ? 2048.0 : 4096.0);
+    if (fill > best_fill + 0.01) {
+      best_fill = fill;
+      best_k = k;
+    }
+  }
+  return (int32_t)best_k;
 }
 
 hipError_t launch_prologue(const int64_t* tgt, int64_t ts0, int64_t ts1, int64_t d1, int64_t N, int64_t ignore_idx,
@@ -1039,6 +1155,25 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, hipEvent_t
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.N == 0) return hipSuccess;
   hipLaunchKernelGGL(k_combine, dim3((uint32_t)((a.N + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Workspace initialisation: every word zero except the header's magic and
+// initialised size (each word written once with its final value, so no two
+// threads race on one word).  A fill kernel, not hipMemsetAsync, so that it
+// can sit in a captured graph.
+__global__ __launch_bounds__(1024) void k_ws_init(unsigned long long* p, int64_t nwords, unsigned long long bytes) {
+  const int64_t stride = (int64_t)gridDim.x * 1024;
+  for (int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x; i < nwords; i += stride)
+    p[i] = i == 1 ? kWsMagic : (i == 2 ? bytes : 0ull);
+}
+
+hipError_t launch_ws_init(void* ws, size_t bytes, hipStream_t stream) {
+  const int64_t nwords = (int64_t)(bytes / 8u);
+  int64_t blocks = (nwords + 1023) / 1024;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(k_ws_init, dim3((uint32_t)blocks), dim3(1024), 0, stream, static_cast<unsigned long long*>(ws),
+                     nwords, (unsigned long long)bytes);
   return hipGetLastError();
 }
 
