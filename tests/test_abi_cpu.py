@@ -176,13 +176,14 @@ def test_workspace_sizes(lib):
     assert n == 256 + 8192 * 4 + 8192 * 8 + 8192 * 4 * 4 * 8
     p0 = h.params()
     x1 = h.logits(d0=2, d1=512, s0=512 * 32000, s1=32000, v_local=32000, vocab_total=32000)
-    assert lib.ce_workspace_bytes(ctypes.byref(x1), ctypes.byref(p0)) == 256
+    # without the mean: header + the fused call's tagged losses (every call collects them)
+    assert lib.ce_workspace_bytes(ctypes.byref(x1), ctypes.byref(p0)) == 256 + 1024 * 8
     assert lib.ce_workspace_bytes(ctypes.byref(h.logits(dtype=9)), ctypes.byref(p0)) == 0
     assert lib.ce_combine_workspace_bytes(512, ctypes.byref(h.params(reduce_loss=1))) == 256 + 2048
     # forced split: chunks of at most one workgroup
     p3 = h.params(split_chunks=3)
     x2 = h.logits(d0=1, d1=10, s0=40960, s1=4096, v_local=4096, vocab_total=4096)
-    assert lib.ce_workspace_bytes(ctypes.byref(x2), ctypes.byref(p3)) == 256 + (10 * 3 * 4 * 8 + 255) // 256 * 256
+    assert lib.ce_workspace_bytes(ctypes.byref(x2), ctypes.byref(p3)) == 256 + 256 + (10 * 3 * 4 * 8 + 255) // 256 * 256
 
 
 def test_workspace_init_validates(lib):

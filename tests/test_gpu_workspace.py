@@ -108,3 +108,54 @@ def test_count_over_target_slices(N, reduce):
     tp = workloads.random_targets((d1, d0), V, seed=N, ignore_frac=0.3)
     t = tp.transpose(0, 1)
     check_fused(x, t, 0.1, reduce, g=1.0 if reduce else None, what=f"count N={d0 * d1}")
+
+
+@pytest.mark.parametrize("reduce", [False, True])
+def test_graph_replays_get_fresh_tags(reduce):
+    """A captured fused call replays with the kernel arguments frozen at
+    capture; the call's tag comes from the workspace's epoch, advanced by
+    every call, so each replay still sees only its own exchanged words.  Each
+    replay (the logits restored in between, eager calls on the same
+    workspace interleaved) must match an eager call bit for bit."""
+    A, B, V, K = 2, 9, 4096, 4  # split rows: the exchange is exercised
+    x = _logits((A, B, V), torch.bfloat16, seed=11)
+    t = workloads.random_targets((A, B), V, seed=11, ignore_frac=0.2)
+    xd, td = to_device_view(x), to_device_view(t)
+    pristine = xd.clone()
+    nb = vce.ce_workspace_bytes(xd, 0.1, reduce, split_chunks=K)
+    ws = vce.ce_workspace_init(torch.empty(nb, dtype=torch.uint8, device="cuda"))
+    loss = torch.empty(1 if reduce else A * B, dtype=torch.float32, device="cuda")
+    n = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    say(f"[graph] eager reference reduce={reduce}")
+    vce.ce_fwd_bwd_fused(xd, td, 0.1, reduce, loss=loss, n_valid=n, ws=ws, split_chunks=K)
+    torch.cuda.synchronize()
+    ref_grad, ref_loss = xd.clone(), loss.clone()
+    check_fused(x, t, 0.1, reduce, g=1.0 if reduce else None, split_chunks=K, what="graph reference")
+
+    say("[graph] capture")
+    xd.copy_(pristine)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            vce.ce_fwd_bwd_fused(xd, td, 0.1, reduce, loss=loss, n_valid=n, ws=ws, split_chunks=K)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say(f"[graph] replay {rep}")
+        xd.copy_(pristine)
+        loss.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(xd.view(torch.int16), ref_grad.view(torch.int16)), f"replay {rep}: gradient differs"
+        assert torch.equal(loss.view(torch.int32), ref_loss.view(torch.int32)), f"replay {rep}: loss differs"
+        if rep == 1:  # an eager call on the same workspace between replays
+            xd.copy_(pristine)
+            vce.ce_fwd_bwd_fused(xd, td, 0.1, reduce, loss=loss, n_valid=n, ws=ws, split_chunks=K)
+            torch.cuda.synchronize()
+            assert torch.equal(xd.view(torch.int16), ref_grad.view(torch.int16))
+    vce.ce_workspace_check(ws)

@@ -6,12 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <unistd.h>
-
-#include <atomic>
-#include <chrono>
 #include <mutex>
-#include <random>
 #include <vector>
 
 #include <hip/hip_runtime_api.h>
@@ -136,7 +131,7 @@ WsLayout ws_layout(int64_t N, int32_t K, bool reduce, bool fused) {
     w.row_loss = off;
     off = align256(off + (size_t)N * 4u);
   }
-  if (fused && reduce) {
+  if (fused) {
     w.row_loss_tagged = off;
     off = align256(off + (size_t)N * 8u);
   }
@@ -148,25 +143,6 @@ WsLayout ws_layout(int64_t N, int32_t K, bool reduce, bool fused) {
   return w;
 }
 
-// Tags of fused calls: consecutive values of a process-wide counter (low 32
-// bits, 0 skipped), so 2^32 - 1 calls in a row never share one.  The counter
-// starts at a random point, so a workspace that moved between processes
-// without ce_workspace_init is unlikely to hold a word with the next tag.
-std::atomic<uint64_t>& tag_counter() {
-  static std::atomic<uint64_t> c([] {
-    std::random_device rd;
-    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
-    return ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ t ^ ((uint64_t)getpid() << 16);
-  }());
-  return c;
-}
-
-uint32_t next_tag() {
-  for (;;) {
-    const uint32_t t = (uint32_t)tag_counter().fetch_add(1, std::memory_order_relaxed);
-    if (t) return t;
-  }
-}
 
 int32_t chunks_for(const ce_logits* x, const ce_params* p) {
   int32_t K = p->split_chunks > 0 ? p->split_chunks : vce::fused_auto_chunks(x->dtype, x->v_local);
@@ -334,11 +310,10 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
   a.aligned = rows_aligned16(x);
   a.C = C;
   a.reduce = p->reduce_loss;
-  a.tag = next_tag();
   a.g = grad_out;
   a.n_out = n_valid;
   a.row_loss = p->reduce_loss ? nullptr : loss;
-  a.row_loss_tagged = p->reduce_loss ? reinterpret_cast<unsigned long long*>(wsb + w.row_loss_tagged) : nullptr;
+  a.row_loss_tagged = reinterpret_cast<unsigned long long*>(wsb + w.row_loss_tagged);
   a.mean_out = p->reduce_loss ? loss : nullptr;
   a.hdr = hdr;
   a.slots = K > 1 ? reinterpret_cast<unsigned long long*>(wsb + w.slots) : nullptr;

@@ -16,14 +16,15 @@ struct WsHeader {
   int32_t n_valid;                 // count of non-ignored rows when the caller passed no n_valid
   unsigned long long magic;        // kWsMagic once ce_workspace_init has run
   unsigned long long init_bytes;   // bytes ce_workspace_init cleared
-  unsigned long long reserved[13];
+  unsigned long long epoch;        // fused call: its low 32 bits tag the call's words (1 after init, never 0)
+  unsigned long long reserved[12];
   unsigned long long counts[kMaxSlices];  // fused call: tagged counts of non-ignored rows per target slice
 };
 constexpr size_t kWsHeaderBytes = 256;
 static_assert(sizeof(WsHeader) == kWsHeaderBytes, "workspace header is 256 bytes");
-// k_ws_init writes the header by word index: word 1 = magic, word 2 = init_bytes
+// k_ws_init writes the header by word index: 1 = magic, 2 = init_bytes, 3 = epoch
 static_assert(offsetof(WsHeader, magic) == 8 && offsetof(WsHeader, init_bytes) == 16, "header word layout");
-static_assert(offsetof(WsHeader, counts) == 128, "header word layout");
+static_assert(offsetof(WsHeader, epoch) == 24 && offsetof(WsHeader, counts) == 128, "header word layout");
 constexpr unsigned long long kWsMagic = 0x43452d5753304331ull;
 
 // Which template instance of the fused kernel a plan uses.
@@ -51,11 +52,10 @@ struct FusedArgs {
   int32_t aligned;         // every row starts and ends on a 16-byte boundary (no head/tail)
   int64_t C;               // body vectors per chunk
   int32_t reduce;          // mean over non-ignored rows
-  uint32_t tag;            // this call's tag: high half of every word it publishes (never 0)
   const float* g;          // upstream gradient ([N] or [1]); NULL = 1
   int32_t* n_out;          // [1] count of non-ignored rows (nullable), written by the last item's workgroup
   float* row_loss;         // [N] loss output (reduce 0)
-  unsigned long long* row_loss_tagged;  // [N] tagged per-row losses (reduce 1)
+  unsigned long long* row_loss_tagged;  // [N] tagged per-row losses (workspace; both modes)
   float* mean_out;         // [1] mean loss (reduce 1), written by the workgroup of the last item
   WsHeader* hdr;
   unsigned long long* slots;  // [N][K][4] tagged exchange words (K > 1)

@@ -374,9 +374,12 @@ __global__ __launch_bounds__(1024) void k_prologue(const int64_t* tgt, int64_t t
 // --------------------------------------------------------------------------
 // Words the fused kernel's workgroups exchange are 64 bits: the call's tag
 // in the high half, a 32-bit payload in the low half, written and read with
-// relaxed agent-scope atomics.  Every call draws a fresh nonzero tag, so a
-// word left by an earlier call (or the zeros of ce_workspace_init) never
-// passes for this call's, and the workspace needs no clearing between calls.
+// relaxed agent-scope atomics.  The tag is the low half of the workspace's
+// epoch word, which the last workgroup of each call advances (never to a
+// value whose low half is 0), so a word left by an earlier call (or the
+// zeros of ce_workspace_init) never passes for this call's, the workspace
+// needs no clearing between calls, and a call replayed from a captured graph
+// (same kernel arguments) still gets a fresh tag.
 __device__ __forceinline__ unsigned long long tagged(uint32_t tag, uint32_t payload) {
   return ((unsigned long long)tag << 32) | payload;
 }
@@ -387,16 +390,17 @@ __device__ __forceinline__ unsigned long long poll(const unsigned long long* p) 
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Publish a fused row's loss.  Without reduction it goes straight to
-// loss[r]; with the mean, chunk 0 of each row publishes a tagged word
-// (fire-and-forget, no round trip before the workgroup exits).
+// Publish a fused row's loss: chunk 0 of each row publishes a tagged word
+// (fire-and-forget, no round trip before the workgroup exits), which the
+// last workgroup collects for the mean and, in both modes, as proof that
+// every workgroup has read the epoch; without reduction it also goes
+// straight to loss[r].
 template <int T>
-__device__ __forceinline__ void publish_row_loss(const FusedArgs& a, int64_t r, float loss, bool chunk0) {
+__device__ __forceinline__ void publish_row_loss(const FusedArgs& a, uint32_t tag, int64_t r, float loss,
+                                                 bool chunk0) {
   if (!chunk0 || threadIdx.x != 0) return;
-  if (!a.reduce)
-    a.row_loss[r] = loss;
-  else
-    publish(a.row_loss_tagged + r, a.tag, __float_as_uint(loss));
+  if (!a.reduce) a.row_loss[r] = loss;
+  publish(a.row_loss_tagged + r, tag, __float_as_uint(loss));
 }
 
 // n = #{rows whose target is not ignore_idx}, counted inside the fused kernel:
@@ -404,7 +408,7 @@ __device__ __forceinline__ void publish_row_loss(const FusedArgs& a, int64_t r, 
 // before anything else and publishes a tagged count in the header.  Those
 // workgroups start first and wait for nothing, so the counts always arrive.
 template <int T>
-__device__ void count_slice(const FusedArgs& a, int64_t b) {
+__device__ void count_slice(const FusedArgs& a, uint32_t tag, int64_t b) {
   __shared__ int csh[T / 64];
   const RowLayout& L = a.L;
   const int64_t r0 = b * a.slice_rows;
@@ -421,7 +425,7 @@ __device__ void count_slice(const FusedArgs& a, int64_t b) {
   if (threadIdx.x == 0) {
     int n = 0;
     for (int i = 0; i < T / 64; ++i) n += csh[i];
-    publish(&a.hdr->counts[b], a.tag, (uint32_t)n);
+    publish(&a.hdr->counts[b], tag, (uint32_t)n);
   }
 }
 
@@ -433,15 +437,15 @@ __device__ __forceinline__ unsigned long long count_word_early(const FusedArgs& 
   const int lane = threadIdx.x & 63;
   return lane < a.nslice ? poll(&a.hdr->counts[lane]) : 0ull;
 }
-__device__ int32_t wave_count(const FusedArgs& a, unsigned long long w, bool* ok) {
+__device__ int32_t wave_count(const FusedArgs& a, uint32_t tag, unsigned long long w, bool* ok) {
   const int lane = threadIdx.x & 63;
   const bool mine = lane < a.nslice;
-  bool ready = !mine || (uint32_t)(w >> 32) == a.tag;
+  bool ready = !mine || (uint32_t)(w >> 32) == tag;
   uint32_t spins = 0;
   while (!__all(ready) && spins <= kSpinLimit) {
     if (!ready) {
       w = poll(&a.hdr->counts[lane]);
-      ready = (uint32_t)(w >> 32) == a.tag;
+      ready = (uint32_t)(w >> 32) == tag;
     }
     ++spins;
     __builtin_amdgcn_s_sleep(2);
@@ -456,19 +460,17 @@ __device__ int32_t wave_count(const FusedArgs& a, unsigned long long w, bool* ok
 // The last item's workgroup finishes the call once its own item is done: it
 // starts after every other workgroup of the launch (in-order dispatch, see
 // k_fused), none of which waits for it, so every tagged word arrives.  It
-// writes n and, with the mean, sums the N losses in index order in FP64
-// (deterministic).
+// writes n and, with the mean, the N losses summed in index order in FP64
+// (deterministic).  Last, it advances the epoch: every workgroup that used
+// this call's tag has read it by then (its words fed a row loss, a count or
+// both), so the next call's tag is set only after this call is done with it.
+// Every row's tagged loss, summed in index order in FP64 by this workgroup
+// (thread-partial sums; the caller combines them in a fixed order).  Words
+// that have not arrived are polled again, bounded.
 template <int T>
-__device__ void fused_finish(const FusedArgs& a) {
-  __shared__ double s_sum[T / 64];
-  bool cnt_ok = true;
-  const int32_t n = wave_count(a, count_word_early(a), &cnt_ok);
-  if (threadIdx.x == 0) {
-    if (!cnt_ok) atomicOr(&a.hdr->status, 1u);
-    if (a.n_out) a.n_out[0] = n;
-  }
-  if (!a.reduce) return;
-  constexpr int U = 16;  // independent loads in flight per thread; missing words are polled again
+__device__ double poll_row_losses(const FusedArgs& a, uint32_t tag, bool* gave_up_out) {
+  // independent loads in flight per thread (more would raise the kernel's register need)
+  constexpr int U = 8;
   double acc = 0.0;
   uint32_t spins = 0;
   bool gave_up = false;
@@ -477,12 +479,12 @@ __device__ void fused_finish(const FusedArgs& a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + (int64_t)u * T + threadIdx.x;
-      w[u] = i < a.L.N ? poll(a.row_loss_tagged + i) : tagged(a.tag, 0u);
+      w[u] = i < a.L.N ? poll(a.row_loss_tagged + i) : tagged(tag, 0u);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + (int64_t)u * T + threadIdx.x;
-      while ((uint32_t)(w[u] >> 32) != a.tag && !gave_up) {
+      while ((uint32_t)(w[u] >> 32) != tag && !gave_up) {
         if (++spins > kSpinLimit) {
           gave_up = true;
           break;
@@ -493,6 +495,45 @@ __device__ void fused_finish(const FusedArgs& a) {
       acc += gave_up ? __builtin_nan("") : (double)__uint_as_float((uint32_t)w[u]);
     }
   }
+  *gave_up_out = gave_up;
+  return acc;
+}
+
+// Advance the workspace's epoch (skipping values whose low half is 0); the
+// caller has seen every word tagged with this call's tag.
+__device__ __forceinline__ void advance_epoch(const FusedArgs& a) {
+  unsigned long long next = a.hdr->epoch + 1;  // this call's epoch: nothing has written it since
+  if ((uint32_t)next == 0u) ++next;
+  __hip_atomic_store(&a.hdr->epoch, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The last item's workgroup finishes the call once its own item is done: it
+// starts after every other workgroup of the launch (in-order dispatch, see
+// k_fused), none of which waits for it, so every tagged word arrives.  It
+// writes n and, with the mean, the N losses summed in index order in FP64
+// (deterministic).  Last, it advances the epoch: every workgroup that used
+// this call's tag has read it by then (its words fed a row loss, a count or
+// both), so the next call's tag is set only after this call is done with it.
+// (The two modes keep separate tails: sharing the mean's tail measurably
+// raised the whole kernel's register allocation.)
+template <int T>
+__device__ void fused_finish(const FusedArgs& a, uint32_t tag) {
+  __shared__ double s_sum[T / 64];
+  bool cnt_ok = true;
+  const int32_t n = wave_count(a, tag, count_word_early(a), &cnt_ok);
+  if (threadIdx.x == 0) {
+    if (!cnt_ok) atomicOr(&a.hdr->status, 1u);
+    if (a.n_out) a.n_out[0] = n;
+  }
+  bool gave_up = false;
+  if (!a.reduce) {
+    (void)poll_row_losses<T>(a, tag, &gave_up);
+    if (gave_up) atomicOr(&a.hdr->status, 1u);
+    __syncthreads();
+    if (threadIdx.x == 0) advance_epoch(a);
+    return;
+  }
+  double acc = poll_row_losses<T>(a, tag, &gave_up);
   if (gave_up) atomicOr(&a.hdr->status, 1u);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
@@ -503,6 +544,7 @@ __device__ void fused_finish(const FusedArgs& a) {
     for (int i = 0; i < T / 64; ++i) tot += s_sum[i];
     // N >= 1 here; n = 0 gives 0/0 = NaN
     a.mean_out[0] = cnt_ok ? (float)(tot / (double)n) : __builtin_nanf("");
+    advance_epoch(a);
   }
 }
 
@@ -543,7 +585,13 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
   const int K = a.K;
 
   const int64_t item = blockIdx.x;
-  if (item < a.nslice) count_slice<T>(a, item);
+  // the workspace's init record and epoch, with scalar loads (constant
+  // address space: nothing writes them before this call's last workgroup
+  // finishes); the epoch's low half is this call's tag
+  typedef const __attribute__((address_space(4))) unsigned long long* ConstU64;
+  const ConstU64 wsrec = (ConstU64)(&a.hdr->magic);  // magic, init_bytes, epoch
+  const uint32_t tag = (uint32_t)wsrec[2];
+  if (item < a.nslice) count_slice<T>(a, tag, item);
   const int64_t last_item = L.N * K - 1;
   const int64_t r = item / K;
   const int k = (int)(item - r * K);
@@ -563,271 +611,273 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       if (first && tid < g.h) store_elem<DT>(g.base, tid, 0.f);
       if (last && tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
     }
-    publish_row_loss<T>(a, r, 0.f, first);
-    if (item == last_item) fused_finish<T>(a);
-    return;
-  }
-
-
-  // ---- the single read of this chunk (slots past the chunk read as zero
-  // and are masked below; their stores are dropped)
-  const Rsrc rb = make_rsrc(body, (int64_t)nvc * 16);
-  const Rsrc rh = make_rsrc(g.base, HT && first ? g.h * ElemT<DT>::EB : 0);
-  const Rsrc rt = make_rsrc(g.tail, HT && last ? (int64_t)g.tn * ElemT<DT>::EB : 0);
-  // The slice counts (wave 0, an agent-scope load to memory) go out before
-  // the chunk loads, so their round trip overlaps them; the upstream
-  // gradient after.  The workspace's initialisation record is read with
-  // scalar loads (constant address space: nothing writes it during the
-  // kernel), which keeps it out of the vector loads' in-order completion
-  // count, and is combined without branches, so no wait is placed before the
-  // chunk is in flight.
-  const unsigned long long cw = (a.reduce && tid < 64) ? count_word_early(a) : 0ull;
-  typedef const __attribute__((address_space(4))) unsigned long long* ConstU64;
-  const ConstU64 wsrec = (ConstU64)(&a.hdr->magic);
-  const bool ws_ok = (wsrec[0] == kWsMagic) & (wsrec[1] >= a.ws_bytes);
-  uint4 v[P];
-#pragma unroll
-  for (int j = 0; j < P; ++j) v[j] = bload16(rb, (uint32_t)(j * T + tid) * 16u);
-  const float g_up = a.g ? a.g[a.reduce ? 0 : r] : 1.f;
-  const bool hv = HT && first && tid < g.h, tv = HT && last && tid < g.tn;
-  float hx = -INFINITY, tx = -INFINITY;
-  if (HT) {
-    hx = bload_elem<DT>(rh, tid);
-    tx = bload_elem<DT>(rt, tid);
-    hx = hv ? hx : -INFINITY;
-    tx = tv ? tx : -INFINITY;
-  }
-
-  // ---- where the target sits (uniform): head, body (chunk, vector, lane,
-  // element) or tail; only the chunk that holds it has own_tid >= 0
-  const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
-  const int64_t tl = g.t - L.vocab_start;
-  int own_tid = -1, own_j = 0, own_e = 0;
-  if (tvalid) {
-    if (tl < g.h) {
-      if (first) own_tid = (int)tl;
-    } else {
-      const int64_t c = tl - g.h;
-      if (c < g.nv * E) {
-        const int64_t vec = c / E;
-        if (vec >= cb && vec < cend) {
-          const int vi = (int)(vec - cb);
-          own_j = vi / T;
-          own_tid = vi - own_j * T;
-          own_e = (int)(c - vec * E);
-        }
-      } else if (last) {
-        own_tid = (int)(c - g.nv * E);
-      }
-    }
-  }
-  const int own_where = own_tid < 0 ? 0 : (tl < g.h ? 1 : (tl - g.h < g.nv * E ? 2 : 3));
-
-  // ---- max, and the row sum that the smoothing term needs
-  const bool smooth = L.alpha != 0.f;
-  float m = fmaxf(hx, tx);
-  float rs = (hv ? hx : 0.f) + (tv ? tx : 0.f);
-  if (smooth) {
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const float mj = vec_max<DT>(v[j], m);
-      m = (j * T + tid < nvc) ? mj : m;
-      rs += vec_sum<DT>(v[j]);  // slots past the chunk hold zeros
-    }
+    publish_row_loss<T>(a, tag, r, 0.f, first);
   } else {
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const float mj = vec_max<DT>(v[j], m);
-      m = (j * T + tid < nvc) ? mj : m;
-    }
-  }
-  const float m_loc = m;  // this thread's own maximum (bounds its largest softmax term)
-  if (a.reduce && tid < 64) {  // n, handed to the other waves by block_max's barrier
-    bool ok;
-    const int32_t n = wave_count(a, cw, &ok);
-    if (tid == 0) sh_n = ok ? n : -1;
-  }
-  m = block_max<T>(m, sh);
-  // s = g / n with the mean, g_r without; NaN (loud) when a count never
-  // arrived or the workspace was not initialised
-  float s_up = g_up;
-  if (a.reduce) s_up = sh_n >= 0 ? g_up / (float)sh_n : __builtin_nanf("");
-  if (!ws_ok) {
-    s_up = __builtin_nanf("");
-    if (tid == 0) atomicOr(&a.hdr->status, 2u);
-  }
-  const float m2 = m * kL;
-  const float msub = (m == -INFINITY) ? 0.f : m2;
-#pragma unroll
-  for (int j = 0; j < P; ++j) launder(v[j]);
 
-  // ---- the owning lane takes the target logit out of its registers
-  float y = 0.f;
-  if (own_tid >= 0 && (__builtin_amdgcn_readfirstlane(tid) >> 6) == (own_tid >> 6)) {  // the owning wave only
-    if (tid == own_tid) {
-      if (own_where == 1) {
-        y = hx;
-        hx = -INFINITY;
-      } else if (own_where == 3) {
-        y = tx;
-        tx = -INFINITY;
+
+    // ---- the single read of this chunk (slots past the chunk read as zero
+    // and are masked below; their stores are dropped)
+    const Rsrc rb = make_rsrc(body, (int64_t)nvc * 16);
+    const Rsrc rh = make_rsrc(g.base, HT && first ? g.h * ElemT<DT>::EB : 0);
+    const Rsrc rt = make_rsrc(g.tail, HT && last ? (int64_t)g.tn * ElemT<DT>::EB : 0);
+    // The slice counts (wave 0, an agent-scope load to memory) go out before
+    // the chunk loads, so their round trip overlaps them; the upstream
+    // gradient after.  The initialisation record came in with scalar loads,
+    // which keeps it out of the vector loads' in-order completion count, and
+    // is combined without branches, so no wait is placed before the chunk is
+    // in flight.
+    const unsigned long long cw = (a.reduce && tid < 64) ? count_word_early(a) : 0ull;
+    const bool ws_ok = (wsrec[0] == kWsMagic) & (wsrec[1] >= a.ws_bytes);
+    uint4 v[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) v[j] = bload16(rb, (uint32_t)(j * T + tid) * 16u);
+    const float g_up = a.g ? a.g[a.reduce ? 0 : r] : 1.f;
+    const bool hv = HT && first && tid < g.h, tv = HT && last && tid < g.tn;
+    float hx = -INFINITY, tx = -INFINITY;
+    if (HT) {
+      hx = bload_elem<DT>(rh, tid);
+      tx = bload_elem<DT>(rt, tid);
+      hx = hv ? hx : -INFINITY;
+      tx = tv ? tx : -INFINITY;
+    }
+
+    // ---- where the target sits (uniform): head, body (chunk, vector, lane,
+    // element) or tail; only the chunk that holds it has own_tid >= 0
+    const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
+    const int64_t tl = g.t - L.vocab_start;
+    int own_tid = -1, own_j = 0, own_e = 0;
+    if (tvalid) {
+      if (tl < g.h) {
+        if (first) own_tid = (int)tl;
       } else {
-#pragma unroll
-        for (int j = 0; j < P; ++j)
-          if (j == own_j) {
-            y = extract<DT>(v[j], own_e);
-            v[j] = with_neg_inf<DT>(v[j], own_e);
+        const int64_t c = tl - g.h;
+        if (c < g.nv * E) {
+          const int64_t vec = c / E;
+          if (vec >= cb && vec < cend) {
+            const int vi = (int)(vec - cb);
+            own_j = vi / T;
+            own_tid = vi - own_j * T;
+            own_e = (int)(c - vec * E);
           }
-      }
-    }
-  }
-
-  // ---- sum of 2^(x log2e - m2) over everything but the target.
-  // On the reuse path (BF16 gradients, see kReuseSA) each term, scaled by
-  // 2^14, is also packed to FP16 into the registers that held the pair of
-  // logits, and the gradient pass reads it back instead of recomputing it.
-  // Per wave: every lane's largest term is below |s| p_max 2^-11 <= kReuseAbs, with
-  // p_j <= e^(x_j - chunk max) because lse >= every chunk's max; a wave
-  // holding a large softmax value keeps its logits and the exact path.
-  const bool reuse_row = DT == CE_BF16 && fabsf(s_up) * L.alpha * (1.f / (float)L.vocab_total) <= kReuseSA &&
-                         L.alpha * (1.f / (float)L.vocab_total) <= kReuseA;
-  const bool big_lane = fabsf(s_up) * ex2((m_loc - m) * kL) * (1.f / 2048.f) > kReuseAbs;
-  const bool reuse = reuse_row && !__any(big_lane);
-  float d0 = ex2(__builtin_fmaf(hx, kL, -msub)) + ex2(__builtin_fmaf(tx, kL, -msub)), d1 = 0.f;
-  if (reuse) {
-    const float msc = msub - (float)kReuseShift;
-    float q0 = 0.f, q1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      float f[E];
-      unpack<DT>(v[j], f);
-      const float mj = (j * T + tid < nvc) ? msc : INFINITY;  // 2^-inf = 0 for slots past the chunk
-      float t[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) t[e] = ex2(__builtin_fmaf(f[e], kL, -mj));
-#pragma unroll
-      for (int e = 0; e < E; e += 2) {
-        q0 += t[e];
-        q1 += t[e + 1];
-      }
-      v[j] = make_uint4(pack_f16(t[0], t[1]), pack_f16(t[2], t[3]), pack_f16(t[4], t[5]), pack_f16(t[6], t[7]));
-    }
-    d0 += (q0 + q1) * kReuseUnscale;  // exact power-of-two rescale
-  } else {
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      float f[E];
-      unpack<DT>(v[j], f);
-      const float mj = (j * T + tid < nvc) ? msub : INFINITY;  // 2^-inf = 0 for slots past the chunk
-#pragma unroll
-      for (int e = 0; e < E; e += 2) {
-        d0 += ex2(__builtin_fmaf(f[e], kL, -mj));
-        d1 += ex2(__builtin_fmaf(f[e + 1], kL, -mj));
-      }
-    }
-  }
-  float d = d0 + d1;
-#pragma unroll
-  for (int j = 0; j < P; ++j) launder(v[j]);
-  block_sum3<T>(d, y, rs, sh);
-
-  // ---- exchange between the chunks of a split row
-  float M2 = m2, D = d, Y = y, R = rs;
-  if (K > 1) {
-    unsigned long long* row_slots = a.slots + (size_t)r * (size_t)K * 4u;
-    if (tid == 0) {
-      const float mine[4] = {m2, d, y, rs};
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        publish(row_slots + 4 * k + q, a.tag, __float_as_uint(mine[q]));
-    }
-    if (tid < 64) {
-      uint32_t spins = 0;
-      bool gave_up = false;
-      for (int w = tid; w < 4 * K; w += 64) {
-        unsigned long long val = 0ull;
-        for (;;) {
-          val = poll(row_slots + w);
-          if ((uint32_t)(val >> 32) == a.tag) break;
-          if (++spins > kSpinLimit) {
-            gave_up = true;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
+        } else if (last) {
+          own_tid = (int)(c - g.nv * E);
         }
-        xs[w] = gave_up ? __uint_as_float(0x7fc00000u) : __uint_as_float((uint32_t)val);
       }
-      if (gave_up) atomicOr(&a.hdr->status, 1u);
     }
-    __syncthreads();
-    M2 = -INFINITY;
-    for (int q = 0; q < K; ++q) M2 = fmaxf(M2, xs[4 * q]);
-    D = 0.f;
-    Y = 0.f;
-    R = 0.f;
-    for (int q = 0; q < K; ++q) {
-      const float mq = xs[4 * q];
-      D += (mq == -INFINITY) ? 0.f : xs[4 * q + 1] * ex2(mq - M2);
-      Y += xs[4 * q + 2];
-      R += xs[4 * q + 3];
-    }
-  }
+    const int own_where = own_tid < 0 ? 0 : (tl < g.h ? 1 : (tl - g.h < g.nv * E ? 2 : 3));
 
-  // ---- sum with the target term restored, lse (base 2, split into hi + lo
-  // by an exact two-sum), loss
-  const float e_t = tvalid ? ex2(__builtin_fmaf(Y, kL, -M2)) : 0.f;
-  const float Dt = D + e_t;
-  const float lgD = lg2(Dt);
-  const float c_hi = M2 + lgD;
-  const float bb = c_hi - M2;
-  const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
-  const float inv_v = 1.f / (float)L.vocab_total;
-  const float lse = c_hi * kLn2 + c_lo * kLn2;
-  const float row_loss = tvalid && ws_ok ? lse - (1.f - L.alpha) * Y - (L.alpha * inv_v) * R
-                                        : __uint_as_float(0x7fc00000u);
+    // ---- max, and the row sum that the smoothing term needs
+    const bool smooth = L.alpha != 0.f;
+    float m = fmaxf(hx, tx);
+    float rs = (hv ? hx : 0.f) + (tv ? tx : 0.f);
+    if (smooth) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const float mj = vec_max<DT>(v[j], m);
+        m = (j * T + tid < nvc) ? mj : m;
+        rs += vec_sum<DT>(v[j]);  // slots past the chunk hold zeros
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const float mj = vec_max<DT>(v[j], m);
+        m = (j * T + tid < nvc) ? mj : m;
+      }
+    }
+    const float m_loc = m;  // this thread's own maximum (bounds its largest softmax term)
+    if (a.reduce && tid < 64) {  // n, handed to the other waves by block_max's barrier
+      bool ok;
+      const int32_t n = wave_count(a, tag, cw, &ok);
+      if (tid == 0) sh_n = ok ? n : -1;
+    }
+    m = block_max<T>(m, sh);
+    // s = g / n with the mean, g_r without; NaN (loud) when a count never
+    // arrived or the workspace was not initialised
+    float s_up = g_up;
+    if (a.reduce) s_up = sh_n >= 0 ? g_up / (float)sh_n : __builtin_nanf("");
+    if (!ws_ok) {
+      s_up = __builtin_nanf("");
+      if (tid == 0) atomicOr(&a.hdr->status, 2u);
+    }
+    const float m2 = m * kL;
+    const float msub = (m == -INFINITY) ? 0.f : m2;
+#pragma unroll
+    for (int j = 0; j < P; ++j) launder(v[j]);
 
-  // ---- gradient from the registers, written over the logits
-  const float s = tvalid ? s_up : __uint_as_float(0x7fc00000u);
-  const float b = -s * (L.alpha * inv_v);
-  if (reuse) {
-    // p = 2^(x log2e - msub) / D * 2^(msub - M2); the registers hold that first factor times 2^14
-    const float kr = s * ex2(msub - M2 - (float)kReuseShift) / Dt;
+    // ---- the owning lane takes the target logit out of its registers
+    float y = 0.f;
+    if (own_tid >= 0 && (__builtin_amdgcn_readfirstlane(tid) >> 6) == (own_tid >> 6)) {  // the owning wave only
+      if (tid == own_tid) {
+        if (own_where == 1) {
+          y = hx;
+          hx = -INFINITY;
+        } else if (own_where == 3) {
+          y = tx;
+          tx = -INFINITY;
+        } else {
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-      uint32_t o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf16(fma_mix_lo(w[q], kr, b), fma_mix_hi(w[q], kr, b));
-      bstore16(make_uint4(o[0], o[1], o[2], o[3]), rb, (uint32_t)(j * T + tid) * 16u);
+          for (int j = 0; j < P; ++j)
+            if (j == own_j) {
+              y = extract<DT>(v[j], own_e);
+              v[j] = with_neg_inf<DT>(v[j], own_e);
+            }
+        }
+      }
     }
-  } else {
+
+    // ---- sum of 2^(x log2e - m2) over everything but the target.
+    // On the reuse path (BF16 gradients, see kReuseSA) each term, scaled by
+    // 2^14, is also packed to FP16 into the registers that held the pair of
+    // logits, and the gradient pass reads it back instead of recomputing it.
+    // Per wave: every lane's largest term is below |s| p_max 2^-11 <= kReuseAbs, with
+    // p_j <= e^(x_j - chunk max) because lse >= every chunk's max; a wave
+    // holding a large softmax value keeps its logits and the exact path.
+    const bool reuse_row = DT == CE_BF16 && fabsf(s_up) * L.alpha * (1.f / (float)L.vocab_total) <= kReuseSA &&
+                           L.alpha * (1.f / (float)L.vocab_total) <= kReuseA;
+    const bool big_lane = fabsf(s_up) * ex2((m_loc - m) * kL) * (1.f / 2048.f) > kReuseAbs;
+    const bool reuse = reuse_row && !__any(big_lane);
+    float d0 = ex2(__builtin_fmaf(hx, kL, -msub)) + ex2(__builtin_fmaf(tx, kL, -msub)), d1 = 0.f;
+    if (reuse) {
+      const float msc = msub - (float)kReuseShift;
+      float q0 = 0.f, q1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      float f[E];
-      unpack<DT>(v[j], f);
-      float gr[E];
+      for (int j = 0; j < P; ++j) {
+        float f[E];
+        unpack<DT>(v[j], f);
+        const float mj = (j * T + tid < nvc) ? msc : INFINITY;  // 2^-inf = 0 for slots past the chunk
+        float t[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(softmax_term<DT>(f[e], c_hi, c_lo), s, b);
-      bstore16(pack<DT>(gr), rb, (uint32_t)(j * T + tid) * 16u);
+        for (int e = 0; e < E; ++e) t[e] = ex2(__builtin_fmaf(f[e], kL, -mj));
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          q0 += t[e];
+          q1 += t[e + 1];
+        }
+        v[j] = make_uint4(pack_f16(t[0], t[1]), pack_f16(t[2], t[3]), pack_f16(t[4], t[5]), pack_f16(t[6], t[7]));
+      }
+      d0 += (q0 + q1) * kReuseUnscale;  // exact power-of-two rescale
+    } else {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        float f[E];
+        unpack<DT>(v[j], f);
+        const float mj = (j * T + tid < nvc) ? msub : INFINITY;  // 2^-inf = 0 for slots past the chunk
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          d0 += ex2(__builtin_fmaf(f[e], kL, -mj));
+          d1 += ex2(__builtin_fmaf(f[e + 1], kL, -mj));
+        }
+      }
     }
+    float d = d0 + d1;
+#pragma unroll
+    for (int j = 0; j < P; ++j) launder(v[j]);
+    block_sum3<T>(d, y, rs, sh);
+
+    // ---- exchange between the chunks of a split row
+    float M2 = m2, D = d, Y = y, R = rs;
+    if (K > 1) {
+      unsigned long long* row_slots = a.slots + (size_t)r * (size_t)K * 4u;
+      if (tid == 0) {
+        const float mine[4] = {m2, d, y, rs};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          publish(row_slots + 4 * k + q, tag, __float_as_uint(mine[q]));
+      }
+      if (tid < 64) {
+        uint32_t spins = 0;
+        bool gave_up = false;
+        for (int w = tid; w < 4 * K; w += 64) {
+          unsigned long long val = 0ull;
+          for (;;) {
+            val = poll(row_slots + w);
+            if ((uint32_t)(val >> 32) == tag) break;
+            if (++spins > kSpinLimit) {
+              gave_up = true;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+          xs[w] = gave_up ? __uint_as_float(0x7fc00000u) : __uint_as_float((uint32_t)val);
+        }
+        if (gave_up) atomicOr(&a.hdr->status, 1u);
+      }
+      __syncthreads();
+      M2 = -INFINITY;
+      for (int q = 0; q < K; ++q) M2 = fmaxf(M2, xs[4 * q]);
+      D = 0.f;
+      Y = 0.f;
+      R = 0.f;
+      for (int q = 0; q < K; ++q) {
+        const float mq = xs[4 * q];
+        D += (mq == -INFINITY) ? 0.f : xs[4 * q + 1] * ex2(mq - M2);
+        Y += xs[4 * q + 2];
+        R += xs[4 * q + 3];
+      }
+    }
+
+    // ---- sum with the target term restored, lse (base 2, split into hi + lo
+    // by an exact two-sum), loss
+    const float e_t = tvalid ? ex2(__builtin_fmaf(Y, kL, -M2)) : 0.f;
+    const float Dt = D + e_t;
+    const float lgD = lg2(Dt);
+    const float c_hi = M2 + lgD;
+    const float bb = c_hi - M2;
+    const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
+    const float inv_v = 1.f / (float)L.vocab_total;
+    const float lse = c_hi * kLn2 + c_lo * kLn2;
+    const float row_loss = tvalid && ws_ok ? lse - (1.f - L.alpha) * Y - (L.alpha * inv_v) * R
+                                          : __uint_as_float(0x7fc00000u);
+
+    // ---- gradient from the registers, written over the logits.  The store
+    // offsets are recomputed from an opaque copy of the thread index, so the
+    // compiler does not keep the P load offsets alive through the passes.
+    int tid_st = tid;
+    asm volatile("" : "+v"(tid_st));
+    const float s = tvalid ? s_up : __uint_as_float(0x7fc00000u);
+    const float b = -s * (L.alpha * inv_v);
+    if (reuse) {
+      // p = 2^(x log2e - msub) / D * 2^(msub - M2); the registers hold that first factor times 2^14
+      const float kr = s * ex2(msub - M2 - (float)kReuseShift) / Dt;
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16(fma_mix_lo(w[q], kr, b), fma_mix_hi(w[q], kr, b));
+        bstore16(make_uint4(o[0], o[1], o[2], o[3]), rb, (uint32_t)(j * T + tid_st) * 16u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        float f[E];
+        unpack<DT>(v[j], f);
+        float gr[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(softmax_term<DT>(f[e], c_hi, c_lo), s, b);
+        bstore16(pack<DT>(gr), rb, (uint32_t)(j * T + tid_st) * 16u);
+      }
+    }
+    if (HT) {
+      bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(hx, c_hi, c_lo), s, b), rh, tid);
+      bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(tx, c_hi, c_lo), s, b), rt, tid);
+    }
+    // target element: s (p_t - a/V - (1 - a)) = s ((a - a/V) - (1 - p_t)) with 1 - p_t = D_excl / D,
+    // stored by the lane that just wrote its vector (same-thread order keeps this store last)
+    if (tid == own_tid) {
+      const float g_t = s * ((L.alpha - L.alpha * inv_v) - D / Dt);
+      if (own_where == 1)
+        bstore_elem<DT>(g_t, rh, tid);
+      else if (own_where == 3)
+        bstore_elem<DT>(g_t, rt, tid);
+      else
+        bstore_elem<DT>(g_t, rb, (own_j * T + tid) * E + own_e);
+    }
+    publish_row_loss<T>(a, tag, r, row_loss, first);
   }
-  if (HT) {
-    bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(hx, c_hi, c_lo), s, b), rh, tid);
-    bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(tx, c_hi, c_lo), s, b), rt, tid);
-  }
-  // target element: s (p_t - a/V - (1 - a)) = s ((a - a/V) - (1 - p_t)) with 1 - p_t = D_excl / D,
-  // stored by the lane that just wrote its vector (same-thread order keeps this store last)
-  if (tid == own_tid) {
-    const float g_t = s * ((L.alpha - L.alpha * inv_v) - D / Dt);
-    if (own_where == 1)
-      bstore_elem<DT>(g_t, rh, tid);
-    else if (own_where == 3)
-      bstore_elem<DT>(g_t, rt, tid);
-    else
-      bstore_elem<DT>(g_t, rb, (own_j * T + tid) * E + own_e);
-  }
-  publish_row_loss<T>(a, r, row_loss, first);
-  if (item == last_item) fused_finish<T>(a);
+  // one call site for both kinds of row (two inlined copies of the finish
+  // measurably raised the register allocation of the whole kernel)
+  if (item == last_item) fused_finish<T>(a, tag);
 }
 
 // --------------------------------------------------------------------------
@@ -1158,14 +1208,14 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Workspace initialisation: every word zero except the header's magic and
-// initialised size (each word written once with its final value, so no two
+// Workspace initialisation: every word zero except the header's magic,
+// initialised size and epoch (1) (each word written once with its final value, so no two
 // threads race on one word).  A fill kernel, not hipMemsetAsync, so that it
 // can sit in a captured graph.
 __global__ __launch_bounds__(1024) void k_ws_init(unsigned long long* p, int64_t nwords, unsigned long long bytes) {
   const int64_t stride = (int64_t)gridDim.x * 1024;
   for (int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x; i < nwords; i += stride)
-    p[i] = i == 1 ? kWsMagic : (i == 2 ? bytes : 0ull);
+    p[i] = i == 1 ? kWsMagic : (i == 2 ? bytes : (i == 3 ? 1ull : 0ull));
 }
 
 hipError_t launch_ws_init(void* ws, size_t bytes, hipStream_t stream) {
