@@ -171,6 +171,20 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
                            float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Deferred upstream gradient (TENPU #29 section 6 stages the gradient in the
+ * input; the autograd backward then applies the upstream gradient).  `x`
+ * holds a gradient written by ce_fwd_bwd_fused or ce_backward_inplace for an
+ * upstream gradient of 1; this multiplies row r by grad_out[r] (per_row = 1,
+ * grad_out device FP32 [N]) or every row by grad_out[0] (per_row = 0, [1]),
+ * in place, in x's dtype (FP32 multiply, then RNE to BF16: a second rounding
+ * of a BF16 gradient unless the factor is a power of two).  A row whose
+ * factor is exactly 1 is neither read nor written, so the common case costs
+ * one small launch and no traffic, with no host synchronisation.  Zeros stay
+ * +0.0, so ignored rows keep their bit pattern for any factor.
+ */
+ce_status ce_scale_grad_inplace(const ce_logits* x, const float* grad_out, int32_t per_row, hipStream_t stream);
+
+/*
  * Per-shard partial statistics (issue #29 section 6 gathers (m, d, X_y);
  * hyper-parallel #269 section 3.1 reduces MAX and SUM and gathers the target
  * logit).  For every logical row of the shard:

@@ -208,3 +208,14 @@ def test_split_chunks_too_few_rejected(lib):
 def test_profile_calls_validate(lib):
     assert lib.ce_profile_stop(None, 0, None) == _abi.CE_EINVAL
     assert lib.ce_profile_start(0) == _abi.CE_EINVAL
+
+
+def test_scale_grad_validates(lib):
+    # rejected before any HIP call: NULL factor with rows, bad mode, bad dtype, NULL descriptor
+    h = Host()
+    g = np.full(h.N, 2.0, np.float32)
+    assert lib.ce_scale_grad_inplace(ctypes.byref(h.logits()), None, 1, None) == _abi.CE_EINVAL
+    assert lib.ce_scale_grad_inplace(ctypes.byref(h.logits()), g.ctypes.data, 2, None) == _abi.CE_EINVAL
+    assert lib.ce_scale_grad_inplace(ctypes.byref(h.logits(dtype=9)), g.ctypes.data, 1, None) == _abi.CE_EDTYPE
+    assert lib.ce_scale_grad_inplace(None, g.ctypes.data, 1, None) == _abi.CE_EINVAL
+    assert h.untouched()

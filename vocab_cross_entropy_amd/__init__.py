@@ -24,7 +24,8 @@ from . import _abi
 from ._abi import CE_BF16, CE_F32, CeArgumentError, CeError
 
 __all__ = [
-    "ce_forward", "ce_backward_inplace", "ce_fwd_bwd_fused", "ce_shard_partial_stats", "ce_shard_combine",
+    "ce_forward", "ce_backward_inplace", "ce_fwd_bwd_fused", "ce_scale_grad_inplace", "ce_shard_partial_stats",
+    "ce_shard_combine",
     "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_init", "ce_workspace_check",
     "parallel_cross_entropy",
     "Profiler", "CeError", "CeArgumentError", "lib",
@@ -172,6 +173,14 @@ def ce_fwd_bwd_fused(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-1
     return loss, n_valid
 
 
+def ce_scale_grad_inplace(x, grad_out: torch.Tensor, per_row: bool):
+    """Multiply the gradient staged in ``x`` by ``grad_out`` ([N] per row, or
+    [1]) in place; rows whose factor is exactly 1 are not touched."""
+    g = grad_out.to(device=x.device, dtype=torch.float32).reshape(-1).contiguous()
+    _check(lib.ce_scale_grad_inplace(ctypes.byref(logits_desc(x)), _ptr(g), int(bool(per_row)), _stream(x.device)))
+    return x
+
+
 def ce_shard_partial_stats(shard, t, vocab_start, vocab_total, ignore_idx=-100, *, stats=None):
     """(m, d, y, r) per row of one vocabulary shard, as a [N, 4] FP32 tensor."""
     N = shard.shape[0] * shard.shape[1]
@@ -211,10 +220,39 @@ def ce_workspace_check(ws: torch.Tensor):
     _check(lib.ce_workspace_check(_ptr(ws), _stream(ws.device)))
 
 
+class ParallelCrossEntropy(torch.autograd.Function):
+    """Autograd form of the fused call (TENPU #29 sections 1 and 6).
+
+    Forward: one ce_fwd_bwd_fused call computes the FP32 loss and writes the
+    gradient for an upstream gradient of 1 over ``inp`` (in its dtype, in
+    place: no N x V gradient buffer is allocated).  Backward: the staged
+    gradient times the upstream gradient, in place, through
+    ce_scale_grad_inplace, which leaves rows whose factor is exactly 1
+    untouched (no host synchronisation to find them); ``inp``'s storage is
+    returned as the gradient.  After the forward, ``inp`` holds the gradient,
+    not the logits.
+    """
+
+    @staticmethod
+    def forward(ctx, inp, target, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100):
+        buf = inp.detach()
+        loss, _ = ce_fwd_bwd_fused(buf, target, label_smoothing, reduce_loss, ignore_idx)
+        ctx.reduce_loss = bool(reduce_loss)
+        ctx.save_for_backward(buf)
+        return loss[0] if reduce_loss else loss.view(target.shape)
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        (buf,) = ctx.saved_tensors
+        ce_scale_grad_inplace(buf, grad_loss, per_row=not ctx.reduce_loss)
+        return buf, None, None, None, None
+
+
 def parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False, dist_process_group=None,
                            ignore_idx=-100):
-    """The issue #29 interface: FP32 loss; the gradient for an upstream
-    gradient of 1 is staged in place in ``inp`` (in its dtype).
+    """The issue #29 interface: FP32 loss (per row in ``target``'s shape, or
+    their mean over non-ignored rows); the gradient is staged in place in
+    ``inp`` (in its dtype) and reaches autograd through ParallelCrossEntropy.
 
     ``inp`` is (B, SQ, V) or (SQ, B, V) (any row strides, contiguous
     columns); ``target`` the matching (B, SQ) / (SQ, B) int64 global indices.
@@ -222,8 +260,7 @@ def parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False, 
     if dist_process_group is not None:
         raise NotImplementedError("vocabulary-parallel process groups need more than one GPU; use "
                                   "ce_shard_partial_stats / ce_shard_combine / ce_backward_inplace per shard")
-    loss, _ = ce_fwd_bwd_fused(inp, target, label_smoothing, reduce_loss, ignore_idx)
-    return loss[0] if reduce_loss else loss.view(target.shape)
+    return ParallelCrossEntropy.apply(inp, target, label_smoothing, reduce_loss, ignore_idx)
 
 
 class Profiler:

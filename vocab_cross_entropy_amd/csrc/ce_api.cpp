@@ -328,6 +328,35 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
   return CE_OK;
 }
 
+ce_status ce_scale_grad_inplace(const ce_logits* x, const float* grad_out, int32_t per_row, hipStream_t stream) {
+  ce_status st;
+  if ((st = check_logits(x, false))) return st;
+  const int64_t N = x->d0 * x->d1;
+  if (N > 0 && !grad_out) return fail(CE_EINVAL, "grad_out is NULL");
+  if (per_row != 0 && per_row != 1) return fail(CE_EINVAL, "per_row must be 0 or 1");
+  vce::ScaleArgs a;
+  a.L.x = static_cast<char*>(x->data);
+  a.L.dtype = x->dtype;
+  a.L.d1 = x->d1;
+  a.L.s0 = x->s0;
+  a.L.s1 = x->s1;
+  a.L.N = N;
+  a.L.V = x->v_local;
+  a.L.vocab_start = x->vocab_start;
+  a.L.vocab_total = x->vocab_total;
+  a.L.tgt = nullptr;
+  a.L.ts0 = a.L.ts1 = 0;
+  a.L.ignore_idx = 0;
+  a.L.alpha = 0.f;
+  a.g = grad_out;
+  a.per_row = per_row;
+  hipEvent_t e0, e1;
+  prof_next(&e0, &e1);
+  hipError_t e;
+  if ((e = vce::launch_scale(a, stream, e0, e1))) return hip_fail(e, "scale launch");
+  return CE_OK;
+}
+
 ce_status ce_shard_partial_stats(const ce_logits* shard, const ce_targets* t, const ce_params* p, float* stats,
                                  hipStream_t stream) {
   ce_status st;

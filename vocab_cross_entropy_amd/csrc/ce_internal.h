@@ -82,6 +82,12 @@ struct BackwardArgs {
   const int32_t* n_valid;
 };
 
+struct ScaleArgs {
+  RowLayout L;             // logits holding a staged gradient (targets unused)
+  const float* g;          // [N] (per_row) or [1]
+  int32_t per_row;
+};
+
 struct CombineArgs {
   const float* stats;
   int32_t S;
@@ -108,5 +114,6 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, hipEvent_t
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out, hipStream_t stream);
 hipError_t launch_ws_init(void* ws, size_t bytes, hipStream_t stream);
+hipError_t launch_scale(const ScaleArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace vce

@@ -335,6 +335,23 @@ __device__ __forceinline__ Row<DT> row_geometry(const RowLayout& L, int64_t r) {
   return g;
 }
 
+// Row r's span without its target (for scaling a staged gradient).
+template <int DT>
+__device__ __forceinline__ Row<DT> row_span(const RowLayout& L, int64_t r) {
+  constexpr int E = ElemT<DT>::E, EB = ElemT<DT>::EB;
+  Row<DT> g;
+  const int64_t i0 = r / L.d1, i1 = r - i0 * L.d1;
+  g.t = 0;
+  g.base = L.x + (i0 * L.s0 + i1 * L.s1) * EB;
+  const int64_t h = (int64_t)(((16u - ((uint32_t)(uintptr_t)g.base & 15u)) & 15u) / EB);
+  g.h = h > L.V ? L.V : h;
+  g.nv = (L.V - g.h) / E;
+  g.tn = (int)(L.V - g.h - g.nv * E);
+  g.body = reinterpret_cast<uint4*>(g.base + g.h * EB);
+  g.tail = g.base + (g.h + g.nv * E) * EB;
+  return g;
+}
+
 // Upstream gradient scale s of row r.
 __device__ __forceinline__ float grad_scale(int32_t reduce, const float* g, const int32_t* n_valid, int64_t r) {
   if (reduce) return (g ? g[0] : 1.f) / (float)(*n_valid);
@@ -1208,6 +1225,44 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// --------------------------------------------------------------------------
+// A staged gradient (written for an upstream gradient of 1) scaled in place
+// by the upstream gradient once it is known: row r by g[r] (per_row) or all
+// rows by g[0].  A row whose factor is exactly 1 is neither read nor written;
+// zeros stay +0.0 (ignored rows keep their bit pattern for any factor).
+template <int DT, int T, int PB>
+__global__ __launch_bounds__(T) void k_scale(ScaleArgs a) {
+  constexpr int E = ElemT<DT>::E, EB = ElemT<DT>::EB;
+  const int tid = threadIdx.x;
+  const RowLayout& L = a.L;
+  for (int64_t r = blockIdx.x; r < L.N; r += gridDim.x) {
+    const float s = a.per_row ? a.g[r] : a.g[0];
+    if (s == 1.f) continue;
+    const Row<DT> g = row_span<DT>(L, r);
+    const Rsrc rb = make_rsrc(g.body, g.nv * 16);
+    const Rsrc rh = make_rsrc(g.base, g.h * EB);
+    const Rsrc rt = make_rsrc(g.tail, (int64_t)g.tn * EB);
+    {
+      const float hx = bload_elem<DT>(rh, tid), tx = bload_elem<DT>(rt, tid);
+      bstore_elem<DT>(hx == 0.f ? 0.f : hx * s, rh, tid);  // lanes past the head or tail: dropped
+      bstore_elem<DT>(tx == 0.f ? 0.f : tx * s, rt, tid);
+    }
+    for (int64_t base = 0; base < g.nv; base += (int64_t)T * PB) {
+      uint4 v[PB];
+#pragma unroll
+      for (int j = 0; j < PB; ++j) v[j] = bload16(rb, (uint32_t)(base + j * T + tid) * 16u);
+#pragma unroll
+      for (int j = 0; j < PB; ++j) {
+        float f[E];
+        unpack<DT>(v[j], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[e] = f[e] == 0.f ? 0.f : f[e] * s;
+        bstore16(pack<DT>(f), rb, (uint32_t)(base + j * T + tid) * 16u);  // dropped past the row
+      }
+    }
+  }
+}
+
 // Workspace initialisation: every word zero except the header's magic,
 // initialised size and epoch (1) (each word written once with its final value, so no two
 // threads race on one word).  A fill kernel, not hipMemsetAsync, so that it
@@ -1225,6 +1280,20 @@ hipError_t launch_ws_init(void* ws, size_t bytes, hipStream_t stream) {
   hipLaunchKernelGGL(k_ws_init, dim3((uint32_t)blocks), dim3(1024), 0, stream, static_cast<unsigned long long*>(ws),
                      nwords, (unsigned long long)bytes);
   return hipGetLastError();
+}
+
+hipError_t launch_scale(const ScaleArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.L.N == 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  const dim3 grid((uint32_t)stream_grid(a.L.N));
+  if (a.L.dtype == CE_BF16)
+    hipLaunchKernelGGL((k_scale<CE_BF16, kStreamT, kStreamPB>), grid, dim3(kStreamT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_scale<CE_F32, kStreamT, kStreamPB>), grid, dim3(kStreamT), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev1) e = hipEventRecord(ev1, stream);
+  return e;
 }
 
 hipError_t launch_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out, hipStream_t stream) {
