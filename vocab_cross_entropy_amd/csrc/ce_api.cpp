@@ -234,14 +234,19 @@ ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p
   auto* hdr = reinterpret_cast<vce::WsHeader*>(wsb);
   int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
   hipError_t e;
-  if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
-    return hip_fail(e, "prologue launch");
+  if (N == 0) {  // nothing to read: n = 0, and the mean of no rows is 0/0
+    if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
+      return hip_fail(e, "prologue launch");
+    if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, n_out, loss, stream))) return hip_fail(e, "mean launch");
+    return CE_OK;
+  }
   vce::StatsArgs a;
   a.L = row_layout(x, t, p);
   a.mode = vce::kStatsForward;
   a.row_loss = p->reduce_loss ? reinterpret_cast<float*>(wsb + w.row_loss) : loss;
   a.lse = lse;
   a.stats = nullptr;
+  a.n_out = n_out;  // counted by the stats kernel's workgroup 0
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
   if ((e = vce::launch_stats(a, stream, e0, e1))) return hip_fail(e, "forward launch");
@@ -371,6 +376,7 @@ ce_status ce_shard_partial_stats(const ce_logits* shard, const ce_targets* t, co
   a.row_loss = nullptr;
   a.lse = nullptr;
   a.stats = stats;
+  a.n_out = nullptr;
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
   hipError_t e;
@@ -401,8 +407,12 @@ ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1
   auto* hdr = reinterpret_cast<vce::WsHeader*>(wsb);
   int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
   hipError_t e;
-  if ((e = vce::launch_prologue(t->data, t->s0, t->s1, d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
-    return hip_fail(e, "prologue launch");
+  if (N == 0) {  // nothing to combine: n = 0, and the mean of no rows is 0/0
+    if ((e = vce::launch_prologue(t->data, t->s0, t->s1, d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
+      return hip_fail(e, "prologue launch");
+    if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, n_out, loss, stream))) return hip_fail(e, "mean launch");
+    return CE_OK;
+  }
   vce::CombineArgs a;
   a.stats = stats;
   a.S = S;
@@ -416,6 +426,7 @@ ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1
   a.alpha = p->label_smoothing;
   a.row_loss = p->reduce_loss ? reinterpret_cast<float*>(wsb + w.row_loss) : loss;
   a.lse = lse;
+  a.n_out = n_out;  // counted by the combine kernel's workgroup 0
   if ((e = vce::launch_combine(a, stream))) return hip_fail(e, "combine launch");
   if (p->reduce_loss && (e = vce::launch_mean(a.row_loss, N, n_out, loss, stream)))
     return hip_fail(e, "mean launch");

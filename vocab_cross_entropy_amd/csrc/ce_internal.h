@@ -72,6 +72,7 @@ struct StatsArgs {
   float* row_loss;  // forward: loss [N] or per-row scratch
   float* lse;       // forward: may be NULL
   float* stats;     // shard: [N][4]
+  int32_t* n_out;   // forward: [1] count of non-ignored rows, written by workgroup 0 (may be NULL)
 };
 
 struct BackwardArgs {
@@ -97,6 +98,7 @@ struct CombineArgs {
   float alpha;
   float* row_loss;
   float* lse;
+  int32_t* n_out;   // [1] count of non-ignored rows, written by workgroup 0 (may be NULL)
 };
 
 // Shape choice for the fused kernel (host side, no HIP calls).

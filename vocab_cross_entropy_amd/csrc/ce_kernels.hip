@@ -358,6 +358,30 @@ __device__ __forceinline__ float grad_scale(int32_t reduce, const float* g, cons
   return g ? g[r] : 1.f;
 }
 
+// n = #{rows whose target is not ignore_idx}, counted by one workgroup of T
+// threads (the caller's workgroup 0; nothing else in its kernel needs n, so
+// no other workgroup waits for it).  Returned in every thread.
+template <int T>
+__device__ int32_t block_count_targets(const int64_t* tgt, int64_t ts0, int64_t ts1, int64_t d1, int64_t N,
+                                       int64_t ignore_idx) {
+  __shared__ int csh[T / 64];
+  int cnt = 0;
+#pragma unroll 4
+  for (int64_t r = threadIdx.x; r < N; r += T) {
+    const int64_t i0 = r / d1, i1 = r - i0 * d1;
+    cnt += tgt[i0 * ts0 + i1 * ts1] != ignore_idx;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  if ((threadIdx.x & 63) == 0) csh[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < T / 64; ++i) n += csh[i];
+  __syncthreads();
+  return n;
+}
+
 // --------------------------------------------------------------------------
 // Prologue: n = #{rows with target != ignore_idx} (block 0), and clearing of
 // the split-row exchange words and the tagged row losses (other blocks).
@@ -906,6 +930,10 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
   __shared__ float sh[T / 64][4];
   const int tid = threadIdx.x;
   const RowLayout& L = a.L;
+  if (blockIdx.x == 0 && a.n_out) {
+    const int32_t n = block_count_targets<T>(L.tgt, L.ts0, L.ts1, L.d1, L.N, L.ignore_idx);
+    if (tid == 0) a.n_out[0] = n;
+  }
   for (int64_t r = blockIdx.x; r < L.N; r += gridDim.x) {
     const Row<DT> g = row_geometry<DT>(L, r);
     if (g.t == L.ignore_idx) {
@@ -1054,6 +1082,10 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
 // --------------------------------------------------------------------------
 // Combine of S shards' (m, d, y, r): one thread per row, shards in order.
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  if (blockIdx.x == 0 && a.n_out) {
+    const int32_t n = block_count_targets<256>(a.tgt, a.ts0, a.ts1, a.d1, a.N, a.ignore_idx);
+    if (threadIdx.x == 0) a.n_out[0] = n;
+  }
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (r >= a.N) return;
   const int64_t i0 = r / a.d1, i1 = r - i0 * a.d1;
