@@ -1158,15 +1158,14 @@ hipError_t launch_fused_dt(const FusedArgs& a, FusedShape shape, int64_t grid, h
 
 constexpr int kStreamT = 256;   // k_scale: threads per row
 constexpr int kStreamPB = 4;    //          16-byte vectors per thread per batch
-// k_stats reads 512 threads x 8 vectors per batch, k_backward 1024 x 4: on
-// 8192 rows of 128000 BF16 columns these measured 365-370 us (5.7 TB/s read)
-// and 718-723 us (5.8 TB/s read + write), against 396 and 773 us at 256 x 4.
-// (k_stats keeps the max pass's unpacked floats for the sum pass, 126 VGPRs;
-// a register barrier that re-unpacks instead, 85 VGPRs, measured slower.)
-constexpr int kStatsT = 512;
-constexpr int kStatsPB = 8;
-constexpr int kBackT = 1024;
-constexpr int kBackPB = 4;
+// Long rows: k_stats reads 512 threads x 8 vectors per batch, k_backward
+// 1024 x 4; on 8192 rows of 128000 BF16 columns these measured 365-370 us
+// (5.7 TB/s read) and 718-723 us (5.8 TB/s read + write), against 396 and
+// 773 us at 256 x 4.  (k_stats keeps the max pass's unpacked floats for the
+// sum pass, 126 VGPRs; a register barrier that re-unpacks instead, 85 VGPRs,
+// measured slower.)  Rows of at most 1024 or 2048 vectors take a workgroup
+// whose batch they fill.
+int row_vectors(const RowLayout& L) { return (int)((L.V * (L.dtype == CE_BF16 ? 2 : 4) + 15) / 16); }
 
 int64_t stream_grid(int64_t N) { return N < (1 << 20) ? N : (1 << 20); }
 
@@ -1237,10 +1236,22 @@ hipError_t launch_stats(const StatsArgs& a, hipStream_t stream, hipEvent_t ev0, 
   hipError_t e = hipSuccess;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   const dim3 grid((uint32_t)stream_grid(a.L.N));
-  if (a.L.dtype == CE_BF16)
-    hipLaunchKernelGGL((k_stats<CE_BF16, kStatsT, kStatsPB>), grid, dim3(kStatsT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_stats<CE_F32, kStatsT, kStatsPB>), grid, dim3(kStatsT), 0, stream, a);
+  const int nv = row_vectors(a.L);
+  if (a.L.dtype == CE_BF16) {
+    if (nv <= 1024)
+      hipLaunchKernelGGL((k_stats<CE_BF16, 256, 4>), grid, dim3(256), 0, stream, a);
+    else if (nv <= 2048)
+      hipLaunchKernelGGL((k_stats<CE_BF16, 256, 8>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_stats<CE_BF16, 512, 8>), grid, dim3(512), 0, stream, a);
+  } else {
+    if (nv <= 1024)
+      hipLaunchKernelGGL((k_stats<CE_F32, 256, 4>), grid, dim3(256), 0, stream, a);
+    else if (nv <= 2048)
+      hipLaunchKernelGGL((k_stats<CE_F32, 256, 8>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_stats<CE_F32, 512, 8>), grid, dim3(512), 0, stream, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1) e = hipEventRecord(ev1, stream);
   return e;
@@ -1251,10 +1262,22 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, hipEvent_t
   hipError_t e = hipSuccess;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   const dim3 grid((uint32_t)stream_grid(a.L.N));
-  if (a.L.dtype == CE_BF16)
-    hipLaunchKernelGGL((k_backward<CE_BF16, kBackT, kBackPB>), grid, dim3(kBackT), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_backward<CE_F32, kBackT, kBackPB>), grid, dim3(kBackT), 0, stream, a);
+  const int nv = row_vectors(a.L);
+  if (a.L.dtype == CE_BF16) {
+    if (nv <= 1024)
+      hipLaunchKernelGGL((k_backward<CE_BF16, 256, 4>), grid, dim3(256), 0, stream, a);
+    else if (nv <= 2048)
+      hipLaunchKernelGGL((k_backward<CE_BF16, 512, 4>), grid, dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_backward<CE_BF16, 1024, 4>), grid, dim3(1024), 0, stream, a);
+  } else {
+    if (nv <= 1024)
+      hipLaunchKernelGGL((k_backward<CE_F32, 256, 4>), grid, dim3(256), 0, stream, a);
+    else if (nv <= 2048)
+      hipLaunchKernelGGL((k_backward<CE_F32, 512, 4>), grid, dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_backward<CE_F32, 1024, 4>), grid, dim3(1024), 0, stream, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1) e = hipEventRecord(ev1, stream);
   return e;
