@@ -16,11 +16,12 @@ step's gradient (on this chip the kernel's duration depends on the values it
 reads, since it runs near the power limit).  Warmup steps reuse the pool.
 
 Printed: one JSON line with the whole-step throughput (formula bytes
-N*V*b read + N*V*b written, per step), the roofline of the fused kernel
-(its own average duration from HIP events recorded by the library on the
-same stream), HBM traffic from committed rocprofv3 counter runs when they
-match the current kernel source, and the FP64 oracle timed on a bounded
-sample of rows on the host cores.
+N*V*b read + N*V*b written, per step), the roofline of the step's dominant
+kernel (its own average duration from HIP events recorded by the library on
+the same stream) and every main kernel's duration and rate, HBM traffic from
+committed rocprofv3 counter runs when they match the current kernel source,
+each step timed alone with cold caches (median and min), and the FP64 oracle
+timed on a bounded sample of rows on the host cores.
 """
 from __future__ import annotations
 
@@ -181,14 +182,18 @@ def main():
                 vce.ce_backward_inplace(shards[s], t_view, lse, w.alpha, w.reduce_loss, grad_out=g, n_valid=n_valid,
                                         vocab_start=a, vocab_total=V)
 
+    def restore(p):
+        """One pool copy back to the generated logits."""
+        if isinstance(p, list):
+            for (a, c), sh in zip(bounds, p):
+                sh.copy_(phys_dev[..., a:c])
+        else:
+            p.copy_(phys_dev)
+
     def refresh():
         """Every pool copy back to the generated logits (outside any timed region)."""
         for p in pool:
-            if isinstance(p, list):
-                for (a, c), sh in zip(bounds, p):
-                    sh.copy_(phys_dev[..., a:c])
-            else:
-                p.copy_(phys_dev)
+            restore(p)
         torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -219,7 +224,23 @@ def main():
         for i in range(args.steps):
             step(pool[i % P])
         torch.cuda.synchronize()
-    del pool
+
+    # each step timed alone with the caches cold: before it (outside its
+    # events) its logits are restored and a 512 MiB scratch buffer is written,
+    # more than the L2s and the 256 MB Infinity Cache hold
+    evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(args.steps):
+        restore(pool[i % P])
+        evict.fill_(i & 0xFF)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        step(pool[i % P])
+        c1.record()
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1))
+    cold.sort()
+    del pool, evict
     torch.cuda.empty_cache()
 
     # plain device copy of the same byte count, for context (achievable read+write rate)
@@ -236,16 +257,44 @@ def main():
     copy_gbps = 2 * flat.numel() * flat.element_size() / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
     del dst
 
+    # each call's main kernel: its average duration over the event pass and
+    # the algorithmic bytes one launch moves (read + written, formula N*V*b
+    # per pass over the logits or a shard)
     main_ms = prof.ms
+    if w.calls == "fused":
+        layout = [("k_fused", formula_bytes)]
+    elif w.calls == "split":
+        layout = [("k_stats (ce_forward)", N * V * b), ("k_backward (ce_backward_inplace)", 2 * N * V * b)]
+    else:
+        layout = ([("k_stats (ce_shard_partial_stats)", N * (c - a) * b) for a, c in bounds]
+                  + [("k_backward (shard)", 2 * N * (c - a) * b) for a, c in bounds])
+    kernels = {}
+    for k, (name, nbytes) in enumerate(layout):
+        ms = main_ms[k::len(layout)]
+        if not ms:
+            continue
+        ent = kernels.setdefault(name, {"launches": 0, "total_ms": 0.0, "bytes": 0})
+        ent["launches"] += len(ms)
+        ent["total_ms"] += sum(ms)
+        ent["bytes"] += nbytes * len(ms)
+    kernel_summary = {name: {"avg_us": round(1e3 * e["total_ms"] / e["launches"], 2),
+                             "algorithmic_bytes_per_launch": e["bytes"] // e["launches"],
+                             "GBps": round(e["bytes"] / (e["total_ms"] * 1e-3) / 1e9, 1)}
+                      for name, e in kernels.items()}
     roofline = None
-    if w.calls == "fused" and main_ms:
-        k_ms = sum(main_ms) / len(main_ms)
-        achieved = formula_bytes / (k_ms * 1e-3) / 1e9
-        traffic, traffic_note = traffic_from_profiles(w.name)
+    if kernels:
+        # the dominant kernel: the largest share of the step's kernel time
+        dom = max(kernels, key=lambda n: kernels[n]["total_ms"])
+        e = kernels[dom]
+        k_ms = e["total_ms"] / e["launches"]
+        per_launch = e["bytes"] // e["launches"]
+        achieved = per_launch / (k_ms * 1e-3) / 1e9
+        traffic, traffic_note = (traffic_from_profiles(w.name) if dom == "k_fused"
+                                 else (None, "counters are collected for the fused kernel only"))
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-                    "kernel": "k_fused", "kernel_avg_us": round(k_ms * 1e3, 2),
-                    "algorithmic_bytes": formula_bytes, "traffic_note": traffic_note}
+                    "kernel": dom, "kernel_avg_us": round(k_ms * 1e3, 2),
+                    "algorithmic_bytes": per_launch, "traffic_note": traffic_note}
 
     value = formula_bytes / (step_ms * 1e-3) / 1e9
     out = {
@@ -268,6 +317,10 @@ def main():
         "formula_bytes_per_step": formula_bytes,
         "copy_ref_GBps": round(copy_gbps, 1),
         "roofline": roofline,
+        "kernels": kernel_summary,
+        "cold_steps": {"median_us": round(1e3 * cold[len(cold) // 2], 2), "min_us": round(1e3 * cold[0], 2),
+                       "n": len(cold), "evict_bytes": 512 << 20,
+                       "note": "each step timed alone after restoring its logits and writing 512 MiB of scratch"},
         "cpu_baseline": None,
     }
     if w.calls != "fused":

@@ -16,6 +16,7 @@ and the interface of the TransformerEngineNPU issue #29 page (section 1):
 from __future__ import annotations
 
 import ctypes
+import functools
 import weakref
 
 import torch
@@ -47,7 +48,15 @@ def _ptr(t: torch.Tensor | None):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# torch's current HIP stream of a device as a raw handle: the raw accessor
+# costs ~0.1 us a call against ~2 us for building a torch Stream object
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device: torch.device):
+    if _raw_stream is not None:
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        return ctypes.c_void_p(_raw_stream(idx))
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
@@ -77,7 +86,13 @@ def targets_desc(t: torch.Tensor) -> _abi.CeTargets:
 
 
 def params(label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, split_chunks=0) -> _abi.CeParams:
-    return _abi.CeParams(float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx), int(split_chunks), 0)
+    """A parameter block (shared per distinct value; the library only reads it)."""
+    return _params(float(label_smoothing), bool(reduce_loss), int(ignore_idx), int(split_chunks))
+
+
+@functools.lru_cache(maxsize=256)
+def _params(label_smoothing: float, reduce_loss: bool, ignore_idx: int, split_chunks: int) -> _abi.CeParams:
+    return _abi.CeParams(label_smoothing, int(reduce_loss), ignore_idx, split_chunks, 0)
 
 
 def _f32(n, device):
