@@ -26,6 +26,21 @@ _LIB_PATH = os.path.join(_HERE, "libce_oracle.so")
 OR_F32 = 0
 OR_BF16 = 1
 
+# smoothing conventions and reductions (ce_oracle.c)
+SMOOTHING = {"all": 0, "others": 1}
+REDUCTION = {"none": 0, "mean": 1, "sum": 2}
+
+
+def reduction_code(reduce_loss) -> int:
+    """False / True / "none" / "mean" / "sum" -> 0 / 1 / 0 / 1 / 2."""
+    if isinstance(reduce_loss, str):
+        return REDUCTION[reduce_loss]
+    return int(bool(reduce_loss))
+
+
+def smoothing_code(smoothing: str) -> int:
+    return SMOOTHING[smoothing]
+
 
 class OracleError(ValueError):
     """A non-ignored target is outside [0, V), or an argument is malformed."""
@@ -72,13 +87,15 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.or_count_valid.argtypes = [P(_Targets), i64, i64, i64]
     lib.or_count_valid.restype = i64
-    lib.or_loss_rows.argtypes = [P(_Logits), P(_Targets), dbl, i64, vp, i64, vp, vp]
-    lib.or_grad_rows.argtypes = [P(_Logits), P(_Targets), dbl, i64, i32, vp, dbl, i64, vp, i64, vp]
+    lib.or_loss_rows.argtypes = [P(_Logits), P(_Targets), dbl, i32, i64, vp, i64, vp, vp]
+    lib.or_grad_rows.argtypes = [P(_Logits), P(_Targets), dbl, i32, i64, i32, vp, dbl, i64, vp, i64, vp]
     lib.or_mean_loss.argtypes = [vp, i64, i64]
     lib.or_mean_loss.restype = dbl
+    lib.or_sum_loss.argtypes = [vp, i64]
+    lib.or_sum_loss.restype = dbl
     lib.or_shard_stats.argtypes = [P(_Logits), P(_Targets), i64, vp, i64, vp]
-    lib.or_shard_combine.argtypes = [vp, i32, i64, i64, P(_Targets), i64, dbl, i64, vp, vp, vp]
-    lib.or_shard_grad.argtypes = [P(_Logits), P(_Targets), dbl, i64, i32, vp, dbl, i64, vp, i64, vp, vp]
+    lib.or_shard_combine.argtypes = [vp, i32, i64, i64, P(_Targets), i64, dbl, i32, i64, vp, vp, vp]
+    lib.or_shard_grad.argtypes = [P(_Logits), P(_Targets), dbl, i32, i64, i32, vp, dbl, i64, vp, i64, vp, vp]
     for f in ("or_loss_rows", "or_grad_rows", "or_shard_stats", "or_shard_combine", "or_shard_grad"):
         getattr(lib, f).restype = ctypes.c_int
     lib.or_max_threads.restype = ctypes.c_int
@@ -143,21 +160,25 @@ class Oracle:
         d0, d1 = t.shape
         return int(self.lib.or_count_valid(ctypes.byref(self._targets(t)), d0, d1, ignore_idx))
 
-    def loss_rows(self, x, t, alpha=0.0, ignore_idx=-100, rows=None):
-        """Per-row loss and lse (float64) of the listed logical rows (all if None)."""
+    def loss_rows(self, x, t, alpha=0.0, ignore_idx=-100, rows=None, smoothing="all"):
+        """Per-row loss and lse (float64) of the listed logical rows (all if None).
+        ``smoothing``: "all" (a / V on every class) or "others" (a / (V - 1)
+        on every class but the target)."""
         lx, lt = self._logits(x), self._targets(t)
         r = self._rows(rows, lx.d0 * lx.d1)
         loss = np.empty(r.size, np.float64)
         lse = np.empty(r.size, np.float64)
-        self._check(self.lib.or_loss_rows(ctypes.byref(lx), ctypes.byref(lt), float(alpha), int(ignore_idx),
-                                          r.ctypes.data, r.size, loss.ctypes.data, lse.ctypes.data))
+        self._check(self.lib.or_loss_rows(ctypes.byref(lx), ctypes.byref(lt), float(alpha), smoothing_code(smoothing),
+                                          int(ignore_idx), r.ctypes.data, r.size, loss.ctypes.data,
+                                          lse.ctypes.data))
         return loss, lse
 
     def grad_rows(self, x, t, alpha=0.0, ignore_idx=-100, reduce_loss=False, g=None, rows=None,
-                  n_valid=None):
+                  n_valid=None, smoothing="all"):
         """Unrounded float64 gradient rows [len(rows), V].
 
-        ``g``: per-row upstream gradient [d0*d1] (not reducing) or a scalar
+        ``reduce_loss``: False / "none", True / "mean", or "sum".  ``g``:
+        per-row upstream gradient [d0*d1] (not reducing) or a scalar
         (reducing); None means 1.  ``n_valid`` defaults to the count of
         non-ignored targets.
         """
@@ -169,7 +190,7 @@ class Oracle:
         g_row_ptr, g_scalar = None, 1.0
         g_keep = None
         if g is not None:
-            if reduce_loss:
+            if reduction_code(reduce_loss):
                 g_scalar = float(g)
             else:
                 g_keep = np.ascontiguousarray(np.asarray(g, dtype=np.float64).reshape(-1))
@@ -177,14 +198,27 @@ class Oracle:
                     raise OracleError("per-row g must have d0*d1 entries")
                 g_row_ptr = g_keep.ctypes.data
         out = np.empty((r.size, lx.v_local), np.float64)
-        self._check(self.lib.or_grad_rows(ctypes.byref(lx), ctypes.byref(lt), float(alpha), int(ignore_idx),
-                                          int(bool(reduce_loss)), g_row_ptr, g_scalar, int(n_valid),
-                                          r.ctypes.data, r.size, out.ctypes.data))
+        self._check(self.lib.or_grad_rows(ctypes.byref(lx), ctypes.byref(lt), float(alpha), smoothing_code(smoothing),
+                                          int(ignore_idx), reduction_code(reduce_loss), g_row_ptr, g_scalar,
+                                          int(n_valid), r.ctypes.data, r.size, out.ctypes.data))
         return out
 
     def mean_loss(self, loss: np.ndarray, n_valid: int) -> float:
         loss = np.ascontiguousarray(loss, dtype=np.float64)
         return float(self.lib.or_mean_loss(loss.ctypes.data, loss.size, int(n_valid)))
+
+    def sum_loss(self, loss: np.ndarray) -> float:
+        loss = np.ascontiguousarray(loss, dtype=np.float64)
+        return float(self.lib.or_sum_loss(loss.ctypes.data, loss.size))
+
+    def reduce(self, loss: np.ndarray, reduce_loss, n_valid: int):
+        """The per-row losses as the given reduction returns them."""
+        code = reduction_code(reduce_loss)
+        if code == 1:
+            return self.mean_loss(loss, n_valid)
+        if code == 2:
+            return self.sum_loss(loss)
+        return loss
 
     def shard_stats(self, shard, t, vocab_start, vocab_total, ignore_idx=-100, rows=None):
         """(m, d, y, r) float64 [len(rows), 4] of one vocabulary shard."""
@@ -195,7 +229,7 @@ class Oracle:
                                             r.ctypes.data, r.size, out.ctypes.data))
         return out
 
-    def shard_combine(self, stats, t, vocab_total, alpha=0.0, ignore_idx=-100, rows=None):
+    def shard_combine(self, stats, t, vocab_total, alpha=0.0, ignore_idx=-100, rows=None, smoothing="all"):
         """Combine stats [S, len(rows), 4] into (loss, lse) for the listed rows."""
         st = np.ascontiguousarray(stats, dtype=np.float64)
         S, nr, four = st.shape
@@ -209,12 +243,12 @@ class Oracle:
         loss = np.empty(nr, np.float64)
         lse = np.empty(nr, np.float64)
         self._check(self.lib.or_shard_combine(st.ctypes.data, S, nr, int(vocab_total), ctypes.byref(lt), d1,
-                                              float(alpha), int(ignore_idx), r.ctypes.data,
-                                              loss.ctypes.data, lse.ctypes.data))
+                                              float(alpha), smoothing_code(smoothing), int(ignore_idx),
+                                              r.ctypes.data, loss.ctypes.data, lse.ctypes.data))
         return loss, lse
 
     def shard_grad(self, shard, t, vocab_start, vocab_total, lse, alpha=0.0, ignore_idx=-100,
-                   reduce_loss=False, g=None, rows=None, n_valid=None):
+                   reduce_loss=False, g=None, rows=None, n_valid=None, smoothing="all"):
         """Unrounded float64 gradient of one shard's listed rows, given combined lse."""
         lx, lt = self._logits(shard, vocab_start, vocab_total), self._targets(t)
         N = lx.d0 * lx.d1
@@ -226,15 +260,16 @@ class Oracle:
             n_valid = self.count_valid(t, ignore_idx)
         g_row_ptr, g_scalar, g_keep = None, 1.0, None
         if g is not None:
-            if reduce_loss:
+            if reduction_code(reduce_loss):
                 g_scalar = float(g)
             else:
                 g_keep = np.ascontiguousarray(np.asarray(g, dtype=np.float64).reshape(-1))
                 g_row_ptr = g_keep.ctypes.data
         out = np.empty((r.size, lx.v_local), np.float64)
-        self._check(self.lib.or_shard_grad(ctypes.byref(lx), ctypes.byref(lt), float(alpha), int(ignore_idx),
-                                           int(bool(reduce_loss)), g_row_ptr, g_scalar, int(n_valid),
-                                           r.ctypes.data, r.size, lse.ctypes.data, out.ctypes.data))
+        self._check(self.lib.or_shard_grad(ctypes.byref(lx), ctypes.byref(lt), float(alpha),
+                                           smoothing_code(smoothing), int(ignore_idx), reduction_code(reduce_loss),
+                                           g_row_ptr, g_scalar, int(n_valid), r.ctypes.data, r.size,
+                                           lse.ctypes.data, out.ctypes.data))
         return out
 
     def max_threads(self) -> int:

@@ -5,7 +5,10 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 This is the three-step computation that the CANN ops-nn fusion page sets out
 as the unfused baseline (section "standard approach: three kernels"):
 softmax, then log, then the negative log-likelihood of the target --
-generalised to the smoothed target distribution q_j = a/V + (1-a)[j == t].
+generalised to a smoothed target distribution q: either q_j = a/V +
+(1-a)[j == t] (smoothing over all classes, torch's convention) or q_t = 1 - a,
+q_j = a/(V-1) for j != t (over the other classes, the ops-nn page's kernel,
+"pitfall 3").
 It deliberately does not use the logsumexp identity the fused method relies
 on, and it works in 50-digit decimal arithmetic without any max shift, so it
 pins the FP64 oracle independently of how that oracle is written.
@@ -24,7 +27,13 @@ def _softmax(row, ctx):
     return [ei / z for ei in e]
 
 
-def loss_rows(rows, targets, alpha=0.0, ignore_idx=-100, digits=50):
+def _target_distribution(V, t, a, smoothing):
+    if smoothing == "others":
+        return [(1 - a) if j == t else a / (V - 1) for j in range(V)]
+    return [a / V + ((1 - a) if j == t else 0) for j in range(V)]
+
+
+def loss_rows(rows, targets, alpha=0.0, ignore_idx=-100, digits=50, smoothing="all"):
     """Per-row cross-entropy loss as Decimal, via softmax -> log -> NLL."""
     out = []
     with localcontext() as ctx:
@@ -39,7 +48,7 @@ def loss_rows(rows, targets, alpha=0.0, ignore_idx=-100, digits=50):
                 raise ValueError("target out of range")
             probs = _softmax(row, ctx)                      # step 1: softmax
             logp = [ctx.ln(p) for p in probs]               # step 2: log
-            q = [a / V + ((1 - a) if j == t else 0) for j in range(V)]
+            q = _target_distribution(V, t, a, smoothing)
             out.append(-sum((qj * lj for qj, lj in zip(q, logp)), Decimal(0)))  # step 3: NLL
     return out
 

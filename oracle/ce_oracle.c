@@ -18,22 +18,31 @@
  *   ("CANN ops-nn CE fusion" page, section "fusion scheme: log_softmax + NLL").
  *   lse is evaluated with the row maximum taken out first, the standard guard
  *   against exp overflow (same page, "pitfall 1: exp overflow").
- *   The smoothing convention is the uniform a/V one of torch's
- *   F.cross_entropy, which the TransformerEngineNPU issue #29 page names as the
- *   precision baseline (section 4); the page's ops-nn listing spreads a over
- *   the V-1 non-target classes instead -- that variant is not computed here.
+ *   The default smoothing convention (OR_SMOOTH_ALL) is the uniform a/V one
+ *   of torch's F.cross_entropy, which the TransformerEngineNPU issue #29 page
+ *   names as the precision baseline (section 4).  The ops-nn page's kernel
+ *   (step 4 of its forward, and "pitfall 3" for the backward) spreads a over
+ *   the V-1 classes other than the target instead (OR_SMOOTH_OTHERS):
+ *     q_ij = 1 - a if j == t_i, a / (V - 1) otherwise
+ *     loss_i = (1 - a) (lse_i - x_it) + a sum_{j != t} (lse_i - x_ij) / (V - 1)
+ *   computed in that form (the NLL term plus the mean of the other classes'
+ *   negative log-probabilities).  With V = 1 there is no other class: a > 0
+ *   is rejected, a = 0 is plain NLL.
  *
  *   Rows whose target equals ignore_idx have loss 0 and gradient 0
  *   (ops-nn page, both kernels; default ignore_idx -100 per issue #29 section 1
  *   and the hyper-parallel issue #269 section 3.1).
  *
  *   Gradient (ops-nn page, section "backward"; smoothing correction from its
- *   "pitfall 3", read with the uniform a/V convention):
+ *   "pitfall 3", with q of either convention):
  *     grad_ij = s_i (softmax_ij - q_ij)
- *   with s_i = g_i (per-row upstream gradient) when the loss is not reduced,
- *   and s_i = g / n when reduce_loss asks for the mean over the n rows whose
- *   target is not ignored (issue #29 section 1 "reduce_loss"; section 7 counts
- *   n_non_ignore).
+ *   with s_i = g_i (per-row upstream gradient) when the loss is not reduced
+ *   (OR_REDUCE_NONE), s_i = g / n for the mean over the n rows whose target
+ *   is not ignored (OR_REDUCE_MEAN; issue #29 section 1 "reduce_loss",
+ *   section 7 counts n_non_ignore), and s_i = g for the sum over rows
+ *   (OR_REDUCE_SUM; the hyper-parallel issue #269 comparison table, row
+ *   "reduction semantics": Titan trains on the sum divided by the global
+ *   count of valid tokens, which here is g = 1 / that count).
  *
  *   Vocabulary shards (hyper-parallel issue #269, section 3.1: forward is a
  *   MAX all-reduce, a SUM all-reduce and a gather of the target logit;
@@ -43,9 +52,12 @@
  *     y_k = x[t - o_k] if o_k <= t < o_k + V_k else 0,  r_k = sum_j x_j
  *     M = max_k m_k,  D = sum_k d_k exp(m_k - M),  lse = M + log D,
  *     x_t = sum_k y_k,  R = sum_k r_k,
- *     loss = lse - (1 - a) x_t - (a / V) R
- *   The last line is the expanded form of -sum_j q_j (x_j - lse); the row sum
- *   r_k is the extra statistic that a > 0 needs.
+ *     loss = lse - (1 - a) x_t - (a / V) R                        (OR_SMOOTH_ALL)
+ *     loss = (1 - a)(lse - x_t) + a ((V - 1) lse - (R - x_t)) / (V - 1)
+ *                                                                 (OR_SMOOTH_OTHERS)
+ *   The first line is the expanded form of -sum_j q_j (x_j - lse), the second
+ *   the ops-nn form with sum_{j != t} (lse - x_j) written through R; the row
+ *   sum r_k is the extra statistic that a > 0 needs.
  *
  * Inputs are read as the exact stored bits: BF16 is widened to FP32 by a
  * 16-bit shift and then to double, FP32 is widened to double.  Logical row
@@ -57,10 +69,13 @@
  *   -2  bad argument (sizes, dtype, NULL)
  *
  * Pins (tests/test_oracle_pins.py): decimal brute force of the unfused
- * softmax -> log -> NLL chain, the closed form loss = ln V for uniform logits
- * and the ops-nn page's worked lse value, torch's float64 F.cross_entropy and
- * its autograd gradient, central finite differences, shift invariance,
- * gradient rows summing to zero, and sharded == unsharded.
+ * softmax -> log -> NLL chain (both smoothing conventions), the closed form
+ * loss = ln V for uniform logits and the ops-nn page's worked lse value,
+ * torch's float64 F.cross_entropy and its autograd gradient (mean, sum and
+ * per-row reductions; the a/(V-1) convention is torch's a/V smoothing with
+ * a' = a V / (V - 1), which puts the same mass on every class), central
+ * finite differences, shift invariance, gradient rows summing to zero, and
+ * sharded == unsharded.
  */
 #include <math.h>
 #include <stdint.h>
@@ -72,6 +87,13 @@
 
 #define OR_EBADTARGET (-1)
 #define OR_EINVAL (-2)
+
+#define OR_SMOOTH_ALL 0    /* a / V on every class (torch's F.cross_entropy) */
+#define OR_SMOOTH_OTHERS 1 /* a / (V - 1) on every class but the target (ops-nn kernel) */
+
+#define OR_REDUCE_NONE 0
+#define OR_REDUCE_MEAN 1
+#define OR_REDUCE_SUM 2
 
 typedef struct or_logits {
   const void* data;
@@ -116,6 +138,25 @@ static int or_check(const or_logits* x) {
   return 0;
 }
 
+/* The smoothing convention is known and usable with V classes. */
+static int or_smooth_ok(int32_t smooth, double alpha, int64_t V) {
+  if (smooth != OR_SMOOTH_ALL && smooth != OR_SMOOTH_OTHERS) return 0;
+  return !(smooth == OR_SMOOTH_OTHERS && alpha > 0.0 && V < 2);
+}
+
+/* Smoothed target probability q_j of class j of a V-class row with target t. */
+static double or_q(int32_t smooth, double alpha, int64_t V, int is_target) {
+  if (smooth == OR_SMOOTH_OTHERS) return is_target ? 1.0 - alpha : (alpha > 0.0 ? alpha / (double)(V - 1) : 0.0);
+  return alpha / (double)V + (is_target ? 1.0 - alpha : 0.0);
+}
+
+/* Upstream scale s of row r (OR_REDUCE_* as in the header comment). */
+static double or_scale(int32_t reduce, const double* g_row, double g_scalar, int64_t n_valid, int64_t r) {
+  if (reduce == OR_REDUCE_MEAN) return g_scalar / (double)n_valid;
+  if (reduce == OR_REDUCE_SUM) return g_scalar;
+  return g_row ? g_row[r] : 1.0;
+}
+
 /* n = number of rows whose target is not ignore_idx. */
 int64_t or_count_valid(const or_targets* t, int64_t d0, int64_t d1, int64_t ignore_idx) {
   int64_t n = 0;
@@ -142,10 +183,11 @@ static double or_row_lse(const or_logits* x, int64_t off) {
  * (v_local == vocab_total).  loss_i = -sum_j q_ij (x_ij - lse_i).
  * lse_out may be NULL; for ignored rows it receives NAN (not defined).
  */
-int or_loss_rows(const or_logits* x, const or_targets* t, double alpha, int64_t ignore_idx,
+int or_loss_rows(const or_logits* x, const or_targets* t, double alpha, int32_t smooth, int64_t ignore_idx,
                  const int64_t* rows, int64_t nrows, double* loss_out, double* lse_out) {
   if (or_check(x) || x->v_local != x->vocab_total || !t || !rows || !loss_out) return OR_EINVAL;
   const int64_t V = x->v_local;
+  if (!or_smooth_ok(smooth, alpha, V)) return OR_EINVAL;
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
   for (int64_t k = 0; k < nrows; ++k) {
@@ -163,9 +205,20 @@ int or_loss_rows(const or_logits* x, const or_targets* t, double alpha, int64_t 
     int64_t off = or_row_offset(x, r);
     double lse = or_row_lse(x, off);
     double loss = 0.0;
-    for (int64_t j = 0; j < V; ++j) {
-      double q = alpha / (double)V + (j == tgt ? 1.0 - alpha : 0.0);
-      loss -= q * (or_elem(x, off + j) - lse);
+    if (smooth == OR_SMOOTH_OTHERS) {
+      /* ops-nn: (1 - a) * NLL + a * (mean over the other classes of -log softmax) */
+      loss = (1.0 - alpha) * (lse - or_elem(x, off + tgt));
+      if (alpha > 0.0) {
+        double other = 0.0;
+        for (int64_t j = 0; j < V; ++j)
+          if (j != tgt) other += lse - or_elem(x, off + j);
+        loss += alpha * other / (double)(V - 1);
+      }
+    } else {
+      for (int64_t j = 0; j < V; ++j) {
+        double q = or_q(smooth, alpha, V, j == tgt);
+        loss -= q * (or_elem(x, off + j) - lse);
+      }
     }
     loss_out[k] = loss;
     if (lse_out) lse_out[k] = lse;
@@ -175,14 +228,16 @@ int or_loss_rows(const or_logits* x, const or_targets* t, double alpha, int64_t 
 
 /*
  * Gradient of the listed rows, unrounded FP64, written as grad_out[k * V + j].
- * s_i = g_row[r] (or 1 when g_row is NULL) if !reduce_loss,
- * s_i = g_scalar / n_valid if reduce_loss.  Ignored rows get 0.
+ * s_i = g_row[r] (or 1 when g_row is NULL) for OR_REDUCE_NONE,
+ * g_scalar / n_valid for OR_REDUCE_MEAN, g_scalar for OR_REDUCE_SUM.
+ * Ignored rows get 0.
  */
-int or_grad_rows(const or_logits* x, const or_targets* t, double alpha, int64_t ignore_idx,
-                 int32_t reduce_loss, const double* g_row, double g_scalar, int64_t n_valid,
+int or_grad_rows(const or_logits* x, const or_targets* t, double alpha, int32_t smooth, int64_t ignore_idx,
+                 int32_t reduce, const double* g_row, double g_scalar, int64_t n_valid,
                  const int64_t* rows, int64_t nrows, double* grad_out) {
   if (or_check(x) || x->v_local != x->vocab_total || !t || !rows || !grad_out) return OR_EINVAL;
   const int64_t V = x->v_local;
+  if (!or_smooth_ok(smooth, alpha, V) || reduce < OR_REDUCE_NONE || reduce > OR_REDUCE_SUM) return OR_EINVAL;
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
   for (int64_t k = 0; k < nrows; ++k) {
@@ -197,13 +252,12 @@ int or_grad_rows(const or_logits* x, const or_targets* t, double alpha, int64_t 
       bad = 1;
       continue;
     }
-    double s = reduce_loss ? g_scalar / (double)n_valid : (g_row ? g_row[r] : 1.0);
+    double s = or_scale(reduce, g_row, g_scalar, n_valid, r);
     int64_t off = or_row_offset(x, r);
     double lse = or_row_lse(x, off);
     for (int64_t j = 0; j < V; ++j) {
       double p = exp(or_elem(x, off + j) - lse);
-      double q = alpha / (double)V + (j == tgt ? 1.0 - alpha : 0.0);
-      gout[j] = s * (p - q);
+      gout[j] = s * (p - or_q(smooth, alpha, V, j == tgt));
     }
   }
   return bad ? OR_EBADTARGET : 0;
@@ -214,6 +268,13 @@ double or_mean_loss(const double* loss, int64_t nrows, int64_t n_valid) {
   double s = 0.0;
   for (int64_t i = 0; i < nrows; ++i) s += loss[i];
   return s / (double)n_valid;
+}
+
+/* Sum of per-row losses (ignored rows contribute their loss of 0). */
+double or_sum_loss(const double* loss, int64_t nrows) {
+  double s = 0.0;
+  for (int64_t i = 0; i < nrows; ++i) s += loss[i];
+  return s;
 }
 
 /*
@@ -259,9 +320,10 @@ int or_shard_stats(const or_logits* x, const or_targets* t, int64_t ignore_idx,
  * loss and lse for those rows.  V in a/V is vocab_total.
  */
 int or_shard_combine(const double* stats, int32_t S, int64_t nrows, int64_t vocab_total,
-                     const or_targets* t, int64_t d1, double alpha, int64_t ignore_idx,
+                     const or_targets* t, int64_t d1, double alpha, int32_t smooth, int64_t ignore_idx,
                      const int64_t* rows, double* loss_out, double* lse_out) {
   if (!stats || S <= 0 || vocab_total <= 0 || !t || !rows || !loss_out) return OR_EINVAL;
+  if (!or_smooth_ok(smooth, alpha, vocab_total)) return OR_EINVAL;
   int bad = 0;
   for (int64_t k = 0; k < nrows; ++k) {
     int64_t tgt = or_target(t, d1, rows[k]);
@@ -287,7 +349,13 @@ int or_shard_combine(const double* stats, int32_t S, int64_t nrows, int64_t voca
       R += st[3];
     }
     double lse = M + log(D);
-    loss_out[k] = lse - (1.0 - alpha) * xt - (alpha / (double)vocab_total) * R;
+    if (smooth == OR_SMOOTH_OTHERS) {
+      double loss = (1.0 - alpha) * (lse - xt);
+      if (alpha > 0.0) loss += alpha * ((double)(vocab_total - 1) * lse - (R - xt)) / (double)(vocab_total - 1);
+      loss_out[k] = loss;
+    } else {
+      loss_out[k] = lse - (1.0 - alpha) * xt - (alpha / (double)vocab_total) * R;
+    }
     if (lse_out) lse_out[k] = lse;
   }
   return bad ? OR_EBADTARGET : 0;
@@ -298,11 +366,12 @@ int or_shard_combine(const double* stats, int32_t S, int64_t nrows, int64_t voca
  * listed row (lse[k]).  Column j of the shard is global column o + j.
  * grad_out[k * V_local + j]; scale s_i as in or_grad_rows.
  */
-int or_shard_grad(const or_logits* x, const or_targets* t, double alpha, int64_t ignore_idx,
-                  int32_t reduce_loss, const double* g_row, double g_scalar, int64_t n_valid,
+int or_shard_grad(const or_logits* x, const or_targets* t, double alpha, int32_t smooth, int64_t ignore_idx,
+                  int32_t reduce, const double* g_row, double g_scalar, int64_t n_valid,
                   const int64_t* rows, int64_t nrows, const double* lse, double* grad_out) {
   if (or_check(x) || !t || !rows || !lse || !grad_out) return OR_EINVAL;
   const int64_t V = x->v_local, o = x->vocab_start, Vt = x->vocab_total;
+  if (!or_smooth_ok(smooth, alpha, Vt) || reduce < OR_REDUCE_NONE || reduce > OR_REDUCE_SUM) return OR_EINVAL;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t k = 0; k < nrows; ++k) {
     int64_t r = rows[k];
@@ -312,12 +381,11 @@ int or_shard_grad(const or_logits* x, const or_targets* t, double alpha, int64_t
       for (int64_t j = 0; j < V; ++j) gout[j] = 0.0;
       continue;
     }
-    double s = reduce_loss ? g_scalar / (double)n_valid : (g_row ? g_row[r] : 1.0);
+    double s = or_scale(reduce, g_row, g_scalar, n_valid, r);
     int64_t off = or_row_offset(x, r);
     for (int64_t j = 0; j < V; ++j) {
       double p = exp(or_elem(x, off + j) - lse[k]);
-      double q = alpha / (double)Vt + (o + j == tgt ? 1.0 - alpha : 0.0);
-      gout[j] = s * (p - q);
+      gout[j] = s * (p - or_q(smooth, alpha, Vt, o + j == tgt));
     }
   }
   return 0;

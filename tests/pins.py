@@ -8,14 +8,19 @@ pin must fail for every mistake.
 
 What each pin rests on:
   * brute force -- the unfused softmax -> log -> NLL chain of the CANN ops-nn
-    fusion page ("standard approach: three kernels"), run in 50-digit decimal;
+    fusion page ("standard approach: three kernels"), run in 50-digit decimal,
+    with either smoothed target distribution;
   * closed form -- uniform logits give softmax 1/V, so the loss is ln V for
-    any smoothing and any target, and the gradient is s (1 - a)(1/V - [j = t]);
+    any smoothing and any target, and the gradient is s (1/V - q_j);
   * the ops-nn page's worked number ("pitfall 1"): logits all 100, V = 32000,
     lse = 100 + ln 32000, printed as 110.4 (tests/golden/p4_uniform_lse.json);
   * library special case -- torch's float64 F.cross_entropy with
     ignore_index and label_smoothing (the precision baseline named on the
-    TransformerEngineNPU issue #29 page, section 4) and its autograd gradient;
+    TransformerEngineNPU issue #29 page, section 4) and its autograd gradient,
+    for the none, mean and sum reductions.  Smoothing a over the V - 1 other
+    classes (the ops-nn page's kernel) gives the target 1 - a and every other
+    class a / (V - 1); torch's smoothing a' over all V classes gives the same
+    distribution when a' = a V / (V - 1), so torch pins that convention too;
   * finite differences -- the gradient is the derivative of the loss;
   * invariants -- a row shift leaves loss and gradient unchanged, and
     non-ignored gradient rows sum to zero;
@@ -32,6 +37,7 @@ import numpy as np
 import torch
 import torch.nn.functional as F
 
+import oracle
 import workloads
 from oracle import brute
 
@@ -75,39 +81,58 @@ def _targets_of(t):
 
 # ----------------------------------------------------------------------------
 def pin_brute_force(orc):
-    """Oracle loss == 50-digit softmax -> log -> NLL, tiny inputs, all layouts."""
+    """Oracle loss == 50-digit softmax -> log -> NLL, tiny inputs, all layouts,
+    both smoothing conventions (over the other classes needs V >= 2 once a > 0)."""
     cases = 0
     for seed, (N, V) in enumerate([(4, 1), (4, 2), (4, 5), (6, 8), (3, 7), (8, 16)]):
         for dtype in (torch.float32, torch.bfloat16):
             for alpha in (0.0, 0.1, 0.7):
                 for swapped in (False, True):
-                    x, t = _tiny_case(100 + seed, N, V, dtype, alpha, swapped=swapped)
-                    loss, _ = orc.loss_rows(x, t, alpha=alpha)
-                    ref = brute.loss_rows(_rows_of(x), _targets_of(t), alpha=alpha)
-                    _close(loss, [float(r) for r in ref], 1e-12, 1e-15, f"brute N={N} V={V} {dtype} a={alpha}")
-                    cases += 1
-    assert cases == 72
+                    for smoothing in ("all", "others"):
+                        x, t = _tiny_case(100 + seed, N, V, dtype, alpha, swapped=swapped)
+                        if smoothing == "others" and V == 1 and alpha > 0:
+                            try:
+                                orc.loss_rows(x, t, alpha=alpha, smoothing=smoothing)
+                            except oracle.OracleError:
+                                continue
+                            raise AssertionError("a > 0 over the other classes of a 1-class row must be rejected")
+                        loss, _ = orc.loss_rows(x, t, alpha=alpha, smoothing=smoothing)
+                        ref = brute.loss_rows(_rows_of(x), _targets_of(t), alpha=alpha, smoothing=smoothing)
+                        _close(loss, [float(r) for r in ref], 1e-12, 1e-15,
+                               f"brute N={N} V={V} {dtype} a={alpha} {smoothing}")
+                        cases += 1
+    assert cases == 136
 
 
 def pin_closed_form_uniform(orc):
-    """Uniform logits: loss = ln V for every smoothing; grad = s(1-a)(1/V - onehot).
+    """Uniform logits: loss = ln V for every smoothing; grad = s (1/V - q_j),
+    which is s (1-a)(1/V - onehot) over all classes and s (1/V - (1-a)) at the
+    target, s (1/V - a/(V-1)) elsewhere over the other classes.
 
     c = 1000 overflows exp() in FP64 unless the row maximum is taken out first."""
     for V in (1, 7, 4096, 32000):
         for c in (0.0, -37.5, 100.0, 1000.0):
             for alpha in (0.0, 0.1, 0.5):
-                x = torch.full((1, 3, V), c, dtype=torch.float32)
-                t = torch.tensor([[0, V - 1, V // 2]])
-                loss, lse = orc.loss_rows(x, t, alpha=alpha)
-                _close(loss, [math.log(V)] * 3, 1e-12, 1e-12, f"ln V, V={V} c={c} a={alpha}")
-                _close(lse, [c + math.log(V)] * 3, 1e-13, 1e-12, f"lse V={V} c={c}")
-                if V <= 4096:
-                    g = np.array([0.5, 2.0, -1.0])
-                    grad = orc.grad_rows(x, t, alpha=alpha, g=g)
-                    ref = np.empty_like(grad)
-                    for k in range(3):
-                        ref[k] = g[k] * (1 - alpha) * (1.0 / V - (np.arange(V) == int(t[0, k])))
-                    _close(grad, ref, 1e-12, 1e-15, f"uniform grad V={V} c={c} a={alpha}")
+                for smoothing in ("all", "others"):
+                    if smoothing == "others" and V == 1 and alpha > 0:
+                        continue
+                    x = torch.full((1, 3, V), c, dtype=torch.float32)
+                    t = torch.tensor([[0, V - 1, V // 2]])
+                    loss, lse = orc.loss_rows(x, t, alpha=alpha, smoothing=smoothing)
+                    _close(loss, [math.log(V)] * 3, 1e-12, 1e-12, f"ln V, V={V} c={c} a={alpha} {smoothing}")
+                    _close(lse, [c + math.log(V)] * 3, 1e-13, 1e-12, f"lse V={V} c={c}")
+                    if V <= 4096:
+                        g = np.array([0.5, 2.0, -1.0])
+                        grad = orc.grad_rows(x, t, alpha=alpha, g=g, smoothing=smoothing)
+                        ref = np.empty_like(grad)
+                        for k in range(3):
+                            onehot = np.arange(V) == int(t[0, k])
+                            if smoothing == "all":
+                                ref[k] = g[k] * (1 - alpha) * (1.0 / V - onehot)
+                            else:
+                                other = alpha / (V - 1) if V > 1 else 0.0
+                                ref[k] = g[k] * (1.0 / V - np.where(onehot, 1 - alpha, other))
+                        _close(grad, ref, 1e-12, 1e-15, f"uniform grad V={V} c={c} a={alpha} {smoothing}")
 
 
 def pin_golden_p4_worked_lse(orc):
@@ -123,31 +148,60 @@ def pin_golden_p4_worked_lse(orc):
     assert abs((lse[0] - c) - gold["log_v_printed"]) <= gold["printed_half_unit"]
 
 
+def pin_golden_p4_other_class_share(orc):
+    """The ops-nn page's per-class smoothing share a / (V - 1) at a = 0.1,
+    V = 32000, printed as about 3.1e-6: with the target holding nearly all the
+    probability (other classes' p ~ e^-60), every other class's gradient is
+    minus that share."""
+    with open(os.path.join(GOLDEN, "p4_smoothing_other_class.json")) as f:
+        gold = json.load(f)
+    V, alpha = gold["V"], gold["alpha"]
+    x = torch.zeros((1, 1, V), dtype=torch.float32)
+    x[0, 0, 7] = 60.0
+    t = torch.tensor([[7]])
+    grad = orc.grad_rows(x, t, alpha=alpha, smoothing="others")[0]
+    others = np.delete(grad, 7)
+    assert np.all(np.abs(-others - gold["share_printed"]) <= gold["printed_half_unit"]), others[:3]
+    _close(-others, np.full(V - 1, alpha / (V - 1)), 1e-12, 0.0, "other-class share")
+
+
+def _torch_smoothing(alpha, V, smoothing):
+    """torch's all-class smoothing that puts the same mass on every class."""
+    return alpha if smoothing == "all" else alpha * V / (V - 1)
+
+
 def pin_torch_cross_entropy(orc):
-    """Oracle loss, mean and gradient == torch float64 F.cross_entropy + autograd."""
+    """Oracle loss, mean, sum and gradient == torch float64 F.cross_entropy + autograd."""
     for seed, (N, V) in enumerate([(8, 3), (12, 50), (6, 257), (16, 1000)]):
         for dtype in (torch.float32, torch.bfloat16):
             for alpha in (0.0, 0.1, 0.3):
                 for swapped in (False, True):
-                    x, t = _tiny_case(200 + seed, N, V, dtype, alpha, ignore_frac=0.2, swapped=swapped)
-                    d0, d1, _ = x.shape
-                    xd = x.to(torch.float64).reshape(d0 * d1, V).clone().requires_grad_(True)
-                    tf = t.reshape(d0 * d1)
-                    ref = F.cross_entropy(xd, tf, ignore_index=-100, label_smoothing=alpha, reduction="none")
-                    loss, _ = orc.loss_rows(x, t, alpha=alpha)
-                    _close(loss, ref.detach().numpy(), 1e-12, 1e-14, f"torch loss {N}x{V} a={alpha}")
-                    g = torch.linspace(-1.5, 2.0, d0 * d1, dtype=torch.float64)
-                    (gx,) = torch.autograd.grad(ref, xd, g)
-                    grad = orc.grad_rows(x, t, alpha=alpha, g=g.numpy())
-                    _close(grad, gx.numpy(), 1e-11, 1e-15, f"torch grad (none) {N}x{V} a={alpha}")
-                    # mean over non-ignored rows, upstream scalar g = 0.75
-                    xm = x.to(torch.float64).reshape(d0 * d1, V).clone().requires_grad_(True)
-                    refm = F.cross_entropy(xm, tf, ignore_index=-100, label_smoothing=alpha, reduction="mean")
-                    n = orc.count_valid(t)
-                    _close([orc.mean_loss(loss, n)], [float(refm.detach())], 1e-12, 1e-14, "torch mean")
-                    (gm,) = torch.autograd.grad(refm, xm, torch.tensor(0.75, dtype=torch.float64))
-                    gradm = orc.grad_rows(x, t, alpha=alpha, reduce_loss=True, g=0.75)
-                    _close(gradm, gm.numpy(), 1e-11, 1e-15, f"torch grad (mean) {N}x{V} a={alpha}")
+                    for smoothing in ("all", "others"):
+                        x, t = _tiny_case(200 + seed, N, V, dtype, alpha, ignore_frac=0.2, swapped=swapped)
+                        d0, d1, _ = x.shape
+                        a_t = _torch_smoothing(alpha, V, smoothing)
+                        what = f"{N}x{V} a={alpha} {smoothing}"
+                        xd = x.to(torch.float64).reshape(d0 * d1, V).clone().requires_grad_(True)
+                        tf = t.reshape(d0 * d1)
+                        ref = F.cross_entropy(xd, tf, ignore_index=-100, label_smoothing=a_t, reduction="none")
+                        loss, _ = orc.loss_rows(x, t, alpha=alpha, smoothing=smoothing)
+                        _close(loss, ref.detach().numpy(), 1e-12, 1e-14, f"torch loss {what}")
+                        g = torch.linspace(-1.5, 2.0, d0 * d1, dtype=torch.float64)
+                        (gx,) = torch.autograd.grad(ref, xd, g)
+                        grad = orc.grad_rows(x, t, alpha=alpha, g=g.numpy(), smoothing=smoothing)
+                        _close(grad, gx.numpy(), 1e-11, 1e-15, f"torch grad (none) {what}")
+                        n = orc.count_valid(t)
+                        # mean over non-ignored rows and sum over rows, upstream scalar g = 0.75
+                        for red in ("mean", "sum"):
+                            xm = x.to(torch.float64).reshape(d0 * d1, V).clone().requires_grad_(True)
+                            refm = F.cross_entropy(xm, tf, ignore_index=-100, label_smoothing=a_t, reduction=red)
+                            _close([orc.reduce(loss, red, n)], [float(refm.detach())], 1e-12, 1e-14, f"torch {red}")
+                            (gm,) = torch.autograd.grad(refm, xm, torch.tensor(0.75, dtype=torch.float64))
+                            gradm = orc.grad_rows(x, t, alpha=alpha, reduce_loss=red, g=0.75, smoothing=smoothing)
+                            _close(gradm, gm.numpy(), 1e-11, 1e-15, f"torch grad ({red}) {what}")
+                        gradb = orc.grad_rows(x, t, alpha=alpha, reduce_loss=True, g=0.75, smoothing=smoothing)
+                        _close(gradb, orc.grad_rows(x, t, alpha=alpha, reduce_loss="mean", g=0.75,
+                                                    smoothing=smoothing), 0, 0, "reduce_loss=True is the mean")
 
 
 def pin_mean_all_ignored_is_nan(orc):
@@ -162,34 +216,37 @@ def pin_mean_all_ignored_is_nan(orc):
 
 
 def pin_finite_differences(orc):
-    """grad == central differences of sum_i g_i loss_i (and of g * mean).
+    """grad == central differences of sum_i g_i loss_i (and of g * mean, g * sum),
+    for both smoothing conventions.
 
     Logits sit on the 2^-10 grid and the step is 2^-10, so x +- h is exact in
     FP32 and the only error is the O(h^2) truncation."""
     h = 2.0 ** -10
     for alpha in (0.0, 0.2):
-        for reduce_loss in (False, True):
-            g = torch.Generator().manual_seed(31 + int(reduce_loss))
-            x = (torch.randint(-2048, 2048, (2, 2, 6), generator=g).double() * h).float()
-            t = torch.tensor([[1, -100], [5, 0]])
-            gr = np.array([0.7, -1.3, 2.0, 0.4])
-            gs = 1.7
-            n = orc.count_valid(t)
+        for smoothing in ("all", "others"):
+            for red in ("none", "mean", "sum"):
+                g = torch.Generator().manual_seed(31 + len(red))
+                x = (torch.randint(-2048, 2048, (2, 2, 6), generator=g).double() * h).float()
+                t = torch.tensor([[1, -100], [5, 0]])
+                gr = np.array([0.7, -1.3, 2.0, 0.4])
+                gs = 1.7
+                n = orc.count_valid(t)
 
-            def objective(xx):
-                loss, _ = orc.loss_rows(xx, t, alpha=alpha)
-                return gs * orc.mean_loss(loss, n) if reduce_loss else float(np.dot(gr, loss))
+                def objective(xx):
+                    loss, _ = orc.loss_rows(xx, t, alpha=alpha, smoothing=smoothing)
+                    return float(np.dot(gr, loss)) if red == "none" else gs * orc.reduce(loss, red, n)
 
-            grad = orc.grad_rows(x, t, alpha=alpha, reduce_loss=reduce_loss, g=gs if reduce_loss else gr)
-            fd = np.zeros_like(grad)
-            for r in range(4):
-                i0, i1 = divmod(r, 2)
-                for j in range(6):
-                    xp, xm = x.clone(), x.clone()
-                    xp[i0, i1, j] += h
-                    xm[i0, i1, j] -= h
-                    fd[r, j] = (objective(xp) - objective(xm)) / (2 * h)
-            _close(grad, fd, 1e-4, 1e-7, f"finite differences a={alpha} reduce={reduce_loss}")
+                grad = orc.grad_rows(x, t, alpha=alpha, reduce_loss=red, g=gr if red == "none" else gs,
+                                     smoothing=smoothing)
+                fd = np.zeros_like(grad)
+                for r in range(4):
+                    i0, i1 = divmod(r, 2)
+                    for j in range(6):
+                        xp, xm = x.clone(), x.clone()
+                        xp[i0, i1, j] += h
+                        xm[i0, i1, j] -= h
+                        fd[r, j] = (objective(xp) - objective(xm)) / (2 * h)
+                _close(grad, fd, 1e-4, 1e-7, f"finite differences a={alpha} {smoothing} {red}")
 
 
 def pin_shift_invariance(orc):
@@ -200,27 +257,29 @@ def pin_shift_invariance(orc):
         xs = (x.double() + 4.0).to(dtype)
         assert torch.equal(xs.double() - 4.0, x.double())
         for alpha in (0.0, 0.3):
-            l0, _ = orc.loss_rows(x, t, alpha=alpha)
-            l1, _ = orc.loss_rows(xs, t, alpha=alpha)
-            _close(l1, l0, 1e-12, 1e-13, "shift loss")
-            g0 = orc.grad_rows(x, t, alpha=alpha)
-            g1 = orc.grad_rows(xs, t, alpha=alpha)
-            _close(g1, g0, 1e-11, 1e-15, "shift grad")
+            for smoothing in ("all", "others"):
+                l0, _ = orc.loss_rows(x, t, alpha=alpha, smoothing=smoothing)
+                l1, _ = orc.loss_rows(xs, t, alpha=alpha, smoothing=smoothing)
+                _close(l1, l0, 1e-12, 1e-13, f"shift loss {smoothing}")
+                g0 = orc.grad_rows(x, t, alpha=alpha, smoothing=smoothing)
+                g1 = orc.grad_rows(xs, t, alpha=alpha, smoothing=smoothing)
+                _close(g1, g0, 1e-11, 1e-15, f"shift grad {smoothing}")
 
 
 def pin_grad_rows_sum_to_zero(orc):
     """sum_j grad_ij = s (1 - (1-a) - a) = 0 for kept rows; ignored rows are exactly 0."""
     inp = workloads.generate(workloads.WORKLOADS[2].scaled(phys=(4, 8), V=300))
     for alpha in (0.0, 0.1):
-        for reduce_loss in (False, True):
-            grad = orc.grad_rows(inp.logits, inp.targets, alpha=alpha, reduce_loss=reduce_loss,
-                                 g=0.9 if reduce_loss else None)
-            t = inp.targets.reshape(-1).numpy()
-            kept = t != -100
-            assert np.all(grad[~kept] == 0.0)
-            sums = grad[kept].sum(axis=1)
-            scale = np.abs(grad[kept]).sum(axis=1)
-            assert np.all(np.abs(sums) <= 1e-13 * np.maximum(scale, 1e-300)), np.abs(sums).max()
+        for red in ("none", "mean", "sum"):
+            for smoothing in ("all", "others"):
+                grad = orc.grad_rows(inp.logits, inp.targets, alpha=alpha, reduce_loss=red,
+                                     g=None if red == "none" else 0.9, smoothing=smoothing)
+                t = inp.targets.reshape(-1).numpy()
+                kept = t != -100
+                assert np.all(grad[~kept] == 0.0)
+                sums = grad[kept].sum(axis=1)
+                scale = np.abs(grad[kept]).sum(axis=1)
+                assert np.all(np.abs(sums) <= 1e-13 * np.maximum(scale, 1e-300)), np.abs(sums).max()
 
 
 def pin_sharded_equals_unsharded(orc):
@@ -232,16 +291,20 @@ def pin_sharded_equals_unsharded(orc):
         bounds = workloads.shard_bounds(V, shards)
         assert bounds[-1][1] == V
         for alpha in (0.0, 0.1):
-            full_loss, full_lse = orc.loss_rows(x, t, alpha=alpha)
-            stats = np.stack([orc.shard_stats(x[..., a:b].contiguous(), t, a, V) for a, b in bounds])
-            loss, lse = orc.shard_combine(stats, t, V, alpha=alpha)
-            kept = t.reshape(-1).numpy() != -100
-            _close(loss, full_loss, 1e-12, 1e-13, f"shard loss V={V} S={shards}")
-            _close(lse[kept], full_lse[kept], 1e-13, 1e-13, "shard lse")
-            full_grad = orc.grad_rows(x, t, alpha=alpha, g=np.linspace(0.5, 1.5, 10))
-            parts = [orc.shard_grad(x[..., a:b].contiguous(), t, a, V, np.where(kept, lse, 0.0), alpha=alpha,
-                                    g=np.linspace(0.5, 1.5, 10)) for a, b in bounds]
-            _close(np.concatenate(parts, axis=1), full_grad, 1e-12, 1e-16, f"shard grad V={V} S={shards}")
+            for smoothing in ("all", "others"):
+                full_loss, full_lse = orc.loss_rows(x, t, alpha=alpha, smoothing=smoothing)
+                stats = np.stack([orc.shard_stats(x[..., a:b].contiguous(), t, a, V) for a, b in bounds])
+                loss, lse = orc.shard_combine(stats, t, V, alpha=alpha, smoothing=smoothing)
+                kept = t.reshape(-1).numpy() != -100
+                _close(loss, full_loss, 1e-12, 1e-13, f"shard loss V={V} S={shards} {smoothing}")
+                _close(lse[kept], full_lse[kept], 1e-13, 1e-13, "shard lse")
+                for red, g in (("none", np.linspace(0.5, 1.5, 10)), ("sum", 0.6)):
+                    full_grad = orc.grad_rows(x, t, alpha=alpha, g=g, reduce_loss=red, smoothing=smoothing)
+                    parts = [orc.shard_grad(x[..., a:b].contiguous(), t, a, V, np.where(kept, lse, 0.0),
+                                            alpha=alpha, g=g, reduce_loss=red, smoothing=smoothing)
+                             for a, b in bounds]
+                    _close(np.concatenate(parts, axis=1), full_grad, 1e-12, 1e-16,
+                           f"shard grad V={V} S={shards} {smoothing} {red}")
 
 
 def pin_count_and_rows(orc):
@@ -260,6 +323,7 @@ ALL_PINS = [
     pin_brute_force,
     pin_closed_form_uniform,
     pin_golden_p4_worked_lse,
+    pin_golden_p4_other_class_share,
     pin_torch_cross_entropy,
     pin_mean_all_ignored_is_nan,
     pin_finite_differences,

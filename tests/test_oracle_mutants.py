@@ -17,27 +17,40 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ce_oracle.c")
 # (name, text in ce_oracle.c, replacement, expected number of occurrences)
 MUTANTS = [
     ("loss_drops_smoothing_mass",
-     "double q = alpha / (double)V + (j == tgt ? 1.0 - alpha : 0.0);\n      loss -= q",
-     "double q = (j == tgt ? 1.0 - alpha : 0.0);\n      loss -= q", 1),
-    ("grad_sign_flipped", "gout[j] = s * (p - q);\n    }\n  }\n  return bad", "gout[j] = s * (q - p);\n    }\n  }\n  return bad", 1),
-    ("grad_target_off_by_one",
-     "double q = alpha / (double)V + (j == tgt ? 1.0 - alpha : 0.0);\n      gout",
-     "double q = alpha / (double)V + (j == tgt + 1 ? 1.0 - alpha : 0.0);\n      gout", 1),
-    ("grad_smoothing_over_v_minus_1",
-     "double q = alpha / (double)V + (j == tgt ? 1.0 - alpha : 0.0);\n      gout",
-     "double q = (j == tgt ? 1.0 - alpha : alpha / (double)(V - 1));\n      gout", 1),
+     "double q = or_q(smooth, alpha, V, j == tgt);\n        loss -= q",
+     "double q = (j == tgt ? 1.0 - alpha : 0.0);\n        loss -= q", 1),
+    ("grad_sign_flipped", "gout[j] = s * (p - or_q(smooth, alpha, V, j == tgt));",
+     "gout[j] = s * (or_q(smooth, alpha, V, j == tgt) - p);", 1),
+    ("grad_target_off_by_one", "gout[j] = s * (p - or_q(smooth, alpha, V, j == tgt));",
+     "gout[j] = s * (p - or_q(smooth, alpha, V, j == tgt + 1));", 1),
+    ("grad_smoothing_conventions_confused", "gout[j] = s * (p - or_q(smooth, alpha, V, j == tgt));",
+     "gout[j] = s * (p - or_q(OR_SMOOTH_OTHERS, alpha, V, j == tgt));", 1),
+    ("smoothing_conventions_swapped", "if (smooth == OR_SMOOTH_OTHERS) return is_target",
+     "if (smooth == OR_SMOOTH_ALL) return is_target", 1),
+    ("uniform_share_over_v_minus_1", "return alpha / (double)V + (is_target",
+     "return alpha / (double)(V - 1) + (is_target", 1),
+    ("others_share_over_v", "alpha / (double)(V - 1) : 0.0);", "alpha / (double)V : 0.0);", 1),
+    ("others_target_keeps_uniform_share", "return is_target ? 1.0 - alpha :",
+     "return is_target ? 1.0 - alpha + alpha / (double)V :", 1),
+    ("others_loss_over_v", "loss += alpha * other / (double)(V - 1);", "loss += alpha * other / (double)V;", 1),
+    ("others_loss_counts_target", "if (j != tgt) other +=", "other +=", 1),
     ("row_strides_swapped", "return i0 * x->s0 + i1 * x->s1;", "return i0 * x->s1 + i1 * x->s0;", 1),
     ("target_strides_swapped", "return t->data[i0 * t->s0 + i1 * t->s1];", "return t->data[i0 * t->s1 + i1 * t->s0];", 1),
     ("no_max_shift", "s += exp(or_elem(x, off + j) - m);\n  return m + log(s);",
      "s += exp(or_elem(x, off + j));\n  return log(s);", 1),
     ("mean_divides_by_rows", "return s / (double)n_valid;", "return s / (double)nrows;", 1),
-    ("mean_grad_ignores_n",
-     "double s = reduce_loss ? g_scalar / (double)n_valid : (g_row ? g_row[r] : 1.0);\n    int64_t off = or_row_offset(x, r);\n    double lse",
-     "double s = reduce_loss ? g_scalar : (g_row ? g_row[r] : 1.0);\n    int64_t off = or_row_offset(x, r);\n    double lse", 1),
+    ("mean_grad_ignores_n", "if (reduce == OR_REDUCE_MEAN) return g_scalar / (double)n_valid;",
+     "if (reduce == OR_REDUCE_MEAN) return g_scalar;", 1),
+    ("sum_grad_divides_by_n", "if (reduce == OR_REDUCE_SUM) return g_scalar;",
+     "if (reduce == OR_REDUCE_SUM) return g_scalar / (double)n_valid;", 1),
+    ("sum_loss_is_mean_over_rows", "  return s;\n}", "  return s / (double)nrows;\n}", 1),
     ("bf16_widened_wrong", "<< 16;", "<< 15;", 1),
     ("combine_no_rescale", "D += st[1] * exp(st[0] - M);", "D += st[1];", 1),
     ("combine_drops_target_gather", "xt += st[2];", "xt = st[2];", 1),
-    ("shard_grad_uses_local_v", "alpha / (double)Vt", "alpha / (double)V", 1),
+    ("combine_others_sign", "(R - xt)) / (double)(vocab_total - 1)", "(R + xt)) / (double)(vocab_total - 1)", 1),
+    ("combine_ignores_convention", "if (smooth == OR_SMOOTH_OTHERS) {\n      double loss",
+     "if (0) {\n      double loss", 1),
+    ("shard_grad_uses_local_v", "or_q(smooth, alpha, Vt, o + j == tgt)", "or_q(smooth, alpha, V, o + j == tgt)", 1),
     ("shard_target_column_unshifted", "or_elem(x, off + (tgt - o))", "or_elem(x, off + tgt % V)", 1),
     ("ignored_row_not_zeroed", "loss_out[k] = 0.0;\n      if (lse_out) lse_out[k] = NAN;\n      continue;\n    }\n    if (tgt < 0 || tgt >= V)",
      "if (lse_out) lse_out[k] = NAN;\n    }\n    if (tgt < 0 || tgt >= V)", 1),
