@@ -5,13 +5,16 @@
  * (FP32 or BF16, accumulated in FP32):
  *
  *   lse_i  = log sum_j exp(x_ij)
- *   loss_i = lse_i - (1 - a) x_i,t_i - (a / V) sum_j x_ij
- *   grad_ij = s_i (exp(x_ij - lse_i) - a / V - (1 - a) [j == t_i])
+ *   loss_i = -sum_j q_ij (x_ij - lse_i)
+ *   grad_ij = s_i (exp(x_ij - lse_i) - q_ij)
  *
- * with label smoothing a, target t_i (a global vocabulary index), rows whose
- * target equals ignore_idx contributing loss 0 and gradient 0, and
- * s_i = g_i (per-row upstream gradient) or g / n when the loss is reduced to
- * the mean over the n non-ignored rows.
+ * with target t_i (a global vocabulary index), label smoothing a spread by
+ * the smoothed target distribution q_i of one of two conventions:
+ *   CE_SMOOTH_ALL:    q_ij = a / V + (1 - a) [j == t_i]
+ *   CE_SMOOTH_OTHERS: q_ij = 1 - a if j == t_i, a / (V - 1) otherwise
+ * rows whose target equals ignore_idx contributing loss 0 and gradient 0, and
+ * s_i = g_i (per-row upstream gradient, no reduction), g / n (the mean over
+ * the n non-ignored rows) or g (the sum over rows).
  *
  * Sources, by the pages' titles and sections:
  *  - interface and semantics: TransformerEngineNPU issue #29 "Parallel Cross
@@ -27,8 +30,16 @@
  *  - vocabulary shards: hyper-parallel issue #269, section 3.1 (forward is a
  *    MAX all-reduce, a SUM all-reduce and a target-logit gather; backward
  *    needs no collective; shards of ceil(V / tp) columns; ignore_index -100).
- *  Label smoothing follows the uniform a/V convention of torch's
- *  F.cross_entropy, the precision baseline named in issue #29 section 4.
+ *  Label smoothing: CE_SMOOTH_ALL is the uniform a/V of torch's
+ *  F.cross_entropy, the precision baseline named in issue #29 section 4;
+ *  CE_SMOOTH_OTHERS is the ops-nn page's kernel (forward step 4: (1 - a) NLL
+ *  plus a times the mean over the other classes of -log softmax; backward
+ *  "pitfall 3": 1 - a at the target, a / (V - 1) elsewhere).
+ *  Reductions: issue #29's reduce_loss (mean over non-ignored rows), and the
+ *  sum that the hyper-parallel #269 comparison table (row "reduction
+ *  semantics") names as Titan's training default, there divided by the
+ *  global count of valid tokens: CE_REDUCE_SUM with grad_out[0] = 1 / count
+ *  gives that gradient with a single rounding, and loss[0] / count the loss.
  *
  * Conventions for every call:
  *  - All pointers named "device" are HIP device (or managed) memory owned by
@@ -61,7 +72,7 @@
 extern "C" {
 #endif
 
-#define CE_ABI_VERSION 1
+#define CE_ABI_VERSION 2
 
 typedef enum ce_status {
   CE_OK = 0,
@@ -74,6 +85,11 @@ typedef enum ce_status {
 } ce_status;
 
 enum { CE_F32 = 0, CE_BF16 = 1 };
+
+/* ce_params.reduce_loss */
+enum { CE_REDUCE_NONE = 0, CE_REDUCE_MEAN = 1, CE_REDUCE_SUM = 2 };
+/* ce_params.smoothing */
+enum { CE_SMOOTH_ALL = 0, CE_SMOOTH_OTHERS = 1 };
 
 /* Logits (or one vocabulary shard of them). */
 typedef struct ce_logits {
@@ -95,11 +111,14 @@ typedef struct ce_targets {
 
 typedef struct ce_params {
   float label_smoothing; /* a in [0, 1] */
-  int32_t reduce_loss;   /* 0: per-row loss[N]; 1: mean over non-ignored rows, loss[1] */
+  int32_t reduce_loss;   /* CE_REDUCE_NONE: per-row loss[N], s_i = g_i;
+                            CE_REDUCE_MEAN: mean over non-ignored rows, loss[1], s = g / n;
+                            CE_REDUCE_SUM:  sum over rows, loss[1], s = g */
   int64_t ignore_idx;    /* rows whose target equals this are skipped (conventionally -100) */
   int32_t split_chunks;  /* 0: automatic.  > 0: ce_fwd_bwd_fused splits each row over this many
                             cooperating workgroups (tuning and testing; at most 64) */
-  int32_t reserved;      /* must be 0 */
+  int32_t smoothing;     /* CE_SMOOTH_ALL or CE_SMOOTH_OTHERS; with CE_SMOOTH_OTHERS and a > 0 the
+                            calls that use the smoothing need vocab_total >= 2 (CE_EINVAL otherwise) */
 } ce_params;
 
 /*
@@ -128,7 +147,7 @@ size_t ce_combine_workspace_bytes(int64_t rows, const ce_params* p);
 /*
  * Forward only (issue #29 section 1 forward; ops-nn "fusion scheme").
  * Unsharded logits (vocab_start == 0, v_local == vocab_total); read once.
- *   loss    [N] (reduce_loss 0) or [1] (reduce_loss 1), device FP32, written
+ *   loss    [N] (CE_REDUCE_NONE) or [1] (mean, sum), device FP32, written
  *   lse     [N] device FP32 or NULL; ignored rows get 0
  *   n_valid [1] device int32 or NULL: number of non-ignored rows
  *   ws      device workspace of at least ce_workspace_bytes(x, p) bytes
@@ -138,14 +157,14 @@ ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p
 
 /*
  * Backward, gradient written in place over the logits in their own dtype
- * (issue #29 section 6; ops-nn "backward", smoothing per "pitfall 3" read
- * with a/V).  `x` may be a vocabulary shard: column j is global column
- * vocab_start + j and a/V uses vocab_total (hyper-parallel #269 section 3.1:
- * the backward needs no collective).
+ * (issue #29 section 6; ops-nn "backward", smoothing per "pitfall 3").  `x`
+ * may be a vocabulary shard: column j is global column vocab_start + j and
+ * the smoothing's V is vocab_total (hyper-parallel #269 section 3.1: the
+ * backward needs no collective).
  *   lse       [N] device FP32 from ce_forward or ce_shard_combine
- *   grad_out  device FP32: [N] per-row upstream gradient (reduce_loss 0) or
- *             [1] (reduce_loss 1); NULL means 1
- *   n_valid   [1] device int32, required when reduce_loss is 1
+ *   grad_out  device FP32: [N] per-row upstream gradient (CE_REDUCE_NONE) or
+ *             [1] (mean, sum); NULL means 1
+ *   n_valid   [1] device int32, required with CE_REDUCE_MEAN (unused otherwise)
  * Ignored rows are set to +0.0 without being read.
  */
 ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* lse,
@@ -165,7 +184,8 @@ ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_
  *             prepared (or prepared smaller) the loss and the gradient come
  *             out NaN and the workspace status records it (ce_workspace_check).
  * One kernel launch: the first workgroups also count the non-ignored rows,
- * and the workgroup of the last (row, chunk) item writes n_valid and the mean.
+ * and the workgroup of the last (row, chunk) item writes n_valid and the
+ * mean or the sum.
  */
 ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* grad_out,
                            float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -201,7 +221,9 @@ ce_status ce_shard_partial_stats(const ce_logits* shard, const ce_targets* t, co
  * Combine S shards' statistics stats[S][N][4] (device FP32, shard-major) into
  * per-row loss and lse over the full vocabulary of vocab_total columns:
  *   M = max_s m_s, D = sum_s d_s exp(m_s - M) (s ascending), lse = M + log D,
- *   loss = lse - (1 - a) sum_s y_s - (a / V) sum_s r_s.
+ *   loss = lse - (q_t - q_o) sum_s y_s - q_o sum_s r_s,
+ * q_t and q_o being the smoothed target probability of the target and of
+ * any other class (a / V + 1 - a and a / V, or 1 - a and a / (V - 1)).
  * This is the point where a multi-GPU run would exchange the statistics.
  *   loss [N] or [1], lse [N] (may be NULL), n_valid [1] (may be NULL),
  *   ws of at least ce_combine_workspace_bytes(d0 * d1, p) bytes.

@@ -73,7 +73,7 @@ class Host:
 
     @staticmethod
     def params(**kw):
-        d = dict(label_smoothing=0.0, reduce_loss=0, ignore_idx=-100, split_chunks=0, reserved=0)
+        d = dict(label_smoothing=0.0, reduce_loss=0, ignore_idx=-100, split_chunks=0, smoothing=0)
         d.update(kw)
         return _abi.CeParams(**d)
 
@@ -107,9 +107,13 @@ BAD_FUSED = [
     ("smoothing_negative", dict(p=dict(label_smoothing=-0.1)), _abi.CE_EINVAL),
     ("smoothing_above_one", dict(p=dict(label_smoothing=1.5)), _abi.CE_EINVAL),
     ("smoothing_nan", dict(p=dict(label_smoothing=float("nan"))), _abi.CE_EINVAL),
-    ("reduce_not_bool", dict(p=dict(reduce_loss=2)), _abi.CE_EINVAL),
+    ("reduce_unknown", dict(p=dict(reduce_loss=3)), _abi.CE_EINVAL),
+    ("reduce_negative", dict(p=dict(reduce_loss=-1)), _abi.CE_EINVAL),
     ("split_chunks_too_many", dict(p=dict(split_chunks=65)), _abi.CE_EINVAL),
-    ("params_reserved", dict(p=dict(reserved=3)), _abi.CE_EINVAL),
+    ("smoothing_unknown", dict(p=dict(smoothing=2)), _abi.CE_EINVAL),
+    # a over the other classes of a one-class vocabulary: nowhere to put it
+    ("smoothing_others_one_class", dict(x=dict(d0=1, d1=1, s0=1, s1=1, v_local=1, vocab_total=1),
+                                        p=dict(smoothing=1, label_smoothing=0.1)), _abi.CE_EINVAL),
     ("null_targets", dict(t=dict(data=None)), _abi.CE_EINVAL),
     ("target_negative_stride", dict(t=dict(s1=-1)), _abi.CE_ELAYOUT),
     ("no_workspace", dict(ws=False), _abi.CE_EWORKSPACE),
@@ -150,6 +154,13 @@ def test_other_calls_reject(lib):
     pr = h.params(reduce_loss=1)
     assert lib.ce_backward_inplace(ctypes.byref(x), ctypes.byref(t), ctypes.byref(pr), h.lse.ctypes.data, None,
                                    None, None) == _abi.CE_EINVAL
+    # smoothing over the other classes of one class: backward and combine reject it too
+    po = h.params(smoothing=1, label_smoothing=0.2)
+    x1 = h.logits(d0=1, d1=1, s0=1, s1=1, v_local=1, vocab_total=1)
+    assert lib.ce_backward_inplace(ctypes.byref(x1), ctypes.byref(t), ctypes.byref(po), h.lse.ctypes.data, None,
+                                   None, None) == _abi.CE_EINVAL
+    assert lib.ce_shard_combine(h.stats.ctypes.data, 1, 2, 3, 1, ctypes.byref(t), ctypes.byref(po),
+                                h.loss.ctypes.data, None, None, h.ws.ctypes.data, h.ws.nbytes, None) == _abi.CE_EINVAL
     # shard stats: misaligned stats, shard past the vocabulary
     assert lib.ce_shard_partial_stats(ctypes.byref(x), ctypes.byref(t), ctypes.byref(p), h.stats.ctypes.data + 4,
                                       None) == _abi.CE_ELAYOUT
@@ -174,6 +185,8 @@ def test_workspace_sizes(lib):
     # header + FP32 losses of the split calls + the fused call's tagged losses
     # + 4 chunks (of at most 4096 vectors) x 4 tagged words per row
     assert n == 256 + 8192 * 4 + 8192 * 8 + 8192 * 4 * 4 * 8
+    # the sum keeps the same per-row losses as the mean
+    assert lib.ce_workspace_bytes(ctypes.byref(x), ctypes.byref(h.params(reduce_loss=2, smoothing=1))) == n
     p0 = h.params()
     x1 = h.logits(d0=2, d1=512, s0=512 * 32000, s1=32000, v_local=32000, vocab_total=32000)
     # without the mean: header + the fused call's tagged losses (every call collects them)

@@ -1,0 +1,32 @@
+"""The Python binding's argument marshalling, on the CPU (the library loads;
+no call here reaches the GPU)."""
+import pytest
+
+import vocab_cross_entropy_amd as vce
+from vocab_cross_entropy_amd import _abi
+
+
+def test_reduction_and_smoothing_codes():
+    assert vce.params(reduce_loss=False).reduce_loss == _abi.CE_REDUCE_NONE
+    assert vce.params(reduce_loss=True).reduce_loss == _abi.CE_REDUCE_MEAN
+    assert vce.params(reduce_loss="none").reduce_loss == _abi.CE_REDUCE_NONE
+    assert vce.params(reduce_loss="mean").reduce_loss == _abi.CE_REDUCE_MEAN
+    assert vce.params(reduce_loss="sum").reduce_loss == _abi.CE_REDUCE_SUM
+    assert vce.params().smoothing == _abi.CE_SMOOTH_ALL
+    assert vce.params(smoothing="others").smoothing == _abi.CE_SMOOTH_OTHERS
+    p = vce.params(0.1, "sum", -1, 3, "others")
+    assert (p.reduce_loss, p.ignore_idx, p.split_chunks, p.smoothing) == (2, -1, 3, 1)
+    assert abs(p.label_smoothing - 0.1) < 1e-7
+    # one shared block per distinct value
+    assert vce.params(0.1, True) is vce.params(0.1, "mean")
+
+
+@pytest.mark.parametrize("kw", [dict(reduce_loss="avg"), dict(smoothing="uniform"), dict(reduce_loss="Sum")])
+def test_unknown_names_rejected(kw):
+    with pytest.raises(vce.CeArgumentError):
+        vce.params(**kw)
+
+
+def test_process_group_needs_more_than_one_gpu():
+    with pytest.raises(NotImplementedError):
+        vce.parallel_cross_entropy(None, None, dist_process_group=object())

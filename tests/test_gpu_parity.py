@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import vocab_cross_entropy_amd as vce
 import workloads
 from gpu_util import (assert_grad, assert_grad_from_lse, assert_loss, ignored_rows, orc, raw_bits, rows_f64, say,
@@ -21,57 +22,66 @@ pytestmark = pytest.mark.gpu
 W = workloads.WORKLOADS
 
 
+def _reduced(reduce) -> bool:
+    """True for the mean (True / "mean") and the sum ("sum")."""
+    return oracle.reduction_code(reduce) != 0
+
+
 def _g_tensor(g, reduce):
     if g is None:
         return None
-    if reduce:
+    if _reduced(reduce):
         return torch.tensor([float(g)], dtype=torch.float32, device="cuda")
     return torch.as_tensor(np.asarray(g, dtype=np.float32), device="cuda")
 
 
 def _s_of(g, reduce, n, N):
     """Per-row gradient scale s_i (for the diagnostic floor)."""
-    if reduce:
+    code = oracle.reduction_code(reduce)
+    if code == 1:
         return (1.0 if g is None else float(g)) / max(n, 1)
+    if code == 2:
+        return 1.0 if g is None else float(g)
     return 1.0
 
 
-def check_fused(x, t, alpha, reduce, g=None, split_chunks=0, sample=None, what="", diag=True, ws=None):
+def check_fused(x, t, alpha, reduce, g=None, split_chunks=0, sample=None, what="", diag=True, ws=None,
+                smoothing="all"):
     """Run ce_fwd_bwd_fused on a device copy of (x, t) and compare with the oracle.
     Returns the device logits (holding the gradient) and the loss tensor."""
     d0, d1, V = x.shape
     N = d0 * d1
     say(f"[fused] {what} shape={tuple(x.shape)} strides={x.stride()} off={x.storage_offset()} {x.dtype} "
-        f"a={alpha} reduce={reduce} K={split_chunks}")
+        f"a={alpha} reduce={reduce} smoothing={smoothing} K={split_chunks}")
     xd, td = to_device_view(x), to_device_view(t)
     loss, n = vce.ce_fwd_bwd_fused(xd, td, alpha, reduce, grad_out=_g_tensor(g, reduce), split_chunks=split_chunks,
-                                   ws=ws)
+                                   ws=ws, smoothing=smoothing)
     torch.cuda.synchronize()
     o = orc()
     n_ref = o.count_valid(t)
     assert int(n.item()) == n_ref, (int(n.item()), n_ref)
     rows = np.arange(N) if sample is None else np.asarray(sample, dtype=np.int64)
     ign = set(ignored_rows(t).tolist())
-    loss_ref, _ = o.loss_rows(x, t, alpha, rows=rows)
-    if reduce:
+    loss_ref, _ = o.loss_rows(x, t, alpha, rows=rows, smoothing=smoothing)
+    if _reduced(reduce):
         if sample is None:
-            ref = o.mean_loss(loss_ref, n_ref)
+            ref = o.reduce(loss_ref, reduce, n_ref)
             got = float(loss.item())
-            if n_ref == 0:
+            if oracle.reduction_code(reduce) == 1 and n_ref == 0:
                 assert math.isnan(got) and math.isnan(ref)
             else:
-                assert_loss([got], [ref], f"{what} mean")
+                assert_loss([got], [ref], f"{what} {reduce}")
     else:
         got = loss.cpu().numpy().astype(np.float64)[rows]
         assert_loss(got, loss_ref, what)
         for k, r in enumerate(rows):
             if r in ign:
                 assert np.float32(got[k]).view(np.int32) == 0, f"ignored row {r} loss not +0.0"
-    g_or = None if g is None else (float(g) if reduce else np.asarray(g, dtype=np.float64))
-    grad_ref = o.grad_rows(x, t, alpha, reduce_loss=reduce, g=g_or, rows=rows, n_valid=n_ref)
+    g_or = None if g is None else (float(g) if _reduced(reduce) else np.asarray(g, dtype=np.float64))
+    grad_ref = o.grad_rows(x, t, alpha, reduce_loss=reduce, g=g_or, rows=rows, n_valid=n_ref, smoothing=smoothing)
     gpu = rows_f64(xd, rows)
     assert_grad(gpu, grad_ref, x.dtype, what)
-    if diag and reduce and n_ref > 0:
+    if diag and _reduced(reduce) and n_ref > 0:
         # bug-catcher for small s, where the 1e-7 floor hides everything: the
         # floor scaled by s, with 2^-11 |ref| more for BF16 (the kernel may stage
         # exponentials in FP16 between its passes; the official bar above gates)

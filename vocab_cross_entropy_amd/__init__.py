@@ -12,6 +12,11 @@ Entry points with the C names:
 and the interface of the TransformerEngineNPU issue #29 page (section 1):
     parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False,
                            dist_process_group=None, ignore_idx=-100)
+
+``reduce_loss`` is False / True (the page's flag: per-row losses / their mean
+over non-ignored rows) or one of "none", "mean", "sum".  ``smoothing`` (a
+keyword) is "all" (a / V on every class, torch's convention) or "others"
+(a / (V - 1) on every class but the target, the CANN ops-nn page's kernel).
 """
 from __future__ import annotations
 
@@ -85,14 +90,35 @@ def targets_desc(t: torch.Tensor) -> _abi.CeTargets:
     return _abi.CeTargets(t.data_ptr(), t.stride(0), t.stride(1))
 
 
-def params(label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, split_chunks=0) -> _abi.CeParams:
+_REDUCTIONS = {"none": _abi.CE_REDUCE_NONE, "mean": _abi.CE_REDUCE_MEAN, "sum": _abi.CE_REDUCE_SUM}
+_SMOOTHINGS = {"all": _abi.CE_SMOOTH_ALL, "others": _abi.CE_SMOOTH_OTHERS}
+
+
+def reduction_code(reduce_loss) -> int:
+    """False / True / "none" / "mean" / "sum" -> CE_REDUCE_*."""
+    if isinstance(reduce_loss, str):
+        if reduce_loss not in _REDUCTIONS:
+            raise CeArgumentError(_abi.CE_EINVAL, f"reduce_loss {reduce_loss!r} is not one of {sorted(_REDUCTIONS)}")
+        return _REDUCTIONS[reduce_loss]
+    return _abi.CE_REDUCE_MEAN if reduce_loss else _abi.CE_REDUCE_NONE
+
+
+def _smoothing_code(smoothing: str) -> int:
+    if smoothing not in _SMOOTHINGS:
+        raise CeArgumentError(_abi.CE_EINVAL, f"smoothing {smoothing!r} is not one of {sorted(_SMOOTHINGS)}")
+    return _SMOOTHINGS[smoothing]
+
+
+def params(label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, split_chunks=0, smoothing="all") -> _abi.CeParams:
     """A parameter block (shared per distinct value; the library only reads it)."""
-    return _params(float(label_smoothing), bool(reduce_loss), int(ignore_idx), int(split_chunks))
+    return _params(float(label_smoothing), reduction_code(reduce_loss), int(ignore_idx), int(split_chunks),
+                   _smoothing_code(smoothing))
 
 
 @functools.lru_cache(maxsize=256)
-def _params(label_smoothing: float, reduce_loss: bool, ignore_idx: int, split_chunks: int) -> _abi.CeParams:
-    return _abi.CeParams(label_smoothing, int(reduce_loss), ignore_idx, split_chunks, 0)
+def _params(label_smoothing: float, reduce_code: int, ignore_idx: int, split_chunks: int,
+            smoothing_code: int) -> _abi.CeParams:
+    return _abi.CeParams(label_smoothing, reduce_code, ignore_idx, split_chunks, smoothing_code)
 
 
 def _f32(n, device):
@@ -124,9 +150,10 @@ def ce_workspace_init(ws: torch.Tensor) -> torch.Tensor:
 
 
 def ce_workspace_bytes(x: torch.Tensor, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100,
-                       split_chunks=0) -> int:
+                       split_chunks=0, smoothing="all") -> int:
     n = lib.ce_workspace_bytes(ctypes.byref(logits_desc(x)),
-                               ctypes.byref(params(label_smoothing, reduce_loss, ignore_idx, split_chunks)))
+                               ctypes.byref(params(label_smoothing, reduce_loss, ignore_idx, split_chunks,
+                                                   smoothing)))
     if n == 0:
         _check(_abi.CE_EINVAL)
     return int(n)
@@ -140,12 +167,12 @@ def ce_combine_workspace_bytes(rows: int, reduce_loss=False) -> int:
 
 
 def ce_forward(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, loss=None, lse=None,
-               n_valid=None, ws=None, want_lse=True):
+               n_valid=None, ws=None, want_lse=True, smoothing="all"):
     """Forward only.  Returns (loss [N] or [1], lse [N] or None, n_valid [1])."""
     N = x.shape[0] * x.shape[1]
     dev = x.device
-    p = params(label_smoothing, reduce_loss, ignore_idx)
-    loss = _f32(1 if reduce_loss else N, dev) if loss is None else loss
+    p = params(label_smoothing, reduce_loss, ignore_idx, smoothing=smoothing)
+    loss = _f32(1 if p.reduce_loss else N, dev) if loss is None else loss
     if lse is None and want_lse:
         lse = _f32(N, dev)
     n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
@@ -158,9 +185,9 @@ def ce_forward(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *,
 
 
 def ce_backward_inplace(x, t, lse, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, grad_out=None,
-                        n_valid=None, vocab_start=0, vocab_total=None):
+                        n_valid=None, vocab_start=0, vocab_total=None, smoothing="all"):
     """Writes the gradient over ``x`` (which may be a vocabulary shard)."""
-    p = params(label_smoothing, reduce_loss, ignore_idx)
+    p = params(label_smoothing, reduce_loss, ignore_idx, smoothing=smoothing)
     _check(lib.ce_backward_inplace(ctypes.byref(logits_desc(x, vocab_start, vocab_total)),
                                    ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(lse), _ptr(grad_out),
                                    _ptr(n_valid), _stream(x.device)))
@@ -168,12 +195,16 @@ def ce_backward_inplace(x, t, lse, label_smoothing=0.0, reduce_loss=False, ignor
 
 
 def ce_fwd_bwd_fused(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, grad_out=None, loss=None,
-                     n_valid=None, ws=None, split_chunks=0):
-    """Loss and, in place over ``x``, the gradient.  Returns (loss, n_valid)."""
+                     n_valid=None, ws=None, split_chunks=0, smoothing="all"):
+    """Loss and, in place over ``x``, the gradient.  Returns (loss, n_valid).
+
+    The sum over a global count of valid tokens (data-parallel training):
+    ``reduce_loss="sum"`` with ``grad_out`` = [1 / count] gives that gradient
+    with one rounding; ``loss / count`` is the normalised loss."""
     N = x.shape[0] * x.shape[1]
     dev = x.device
-    p = params(label_smoothing, reduce_loss, ignore_idx, split_chunks)
-    loss = _f32(1 if reduce_loss else N, dev) if loss is None else loss
+    p = params(label_smoothing, reduce_loss, ignore_idx, split_chunks, smoothing)
+    loss = _f32(1 if p.reduce_loss else N, dev) if loss is None else loss
     n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
     xd = logits_desc(x)
     if ws is None:
@@ -208,14 +239,14 @@ def ce_shard_partial_stats(shard, t, vocab_start, vocab_total, ignore_idx=-100, 
 
 
 def ce_shard_combine(stats, t, vocab_total, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, loss=None,
-                     lse=None, n_valid=None, ws=None):
+                     lse=None, n_valid=None, ws=None, smoothing="all"):
     """Combine stats [S, N, 4] into (loss, lse [N], n_valid [1])."""
     S = stats.shape[0]
     d0, d1 = t.shape
     N = d0 * d1
     dev = stats.device
-    p = params(label_smoothing, reduce_loss, ignore_idx)
-    loss = _f32(1 if reduce_loss else N, dev) if loss is None else loss
+    p = params(label_smoothing, reduce_loss, ignore_idx, smoothing=smoothing)
+    loss = _f32(1 if p.reduce_loss else N, dev) if loss is None else loss
     lse = _f32(N, dev) if lse is None else lse
     n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
     if ws is None:
@@ -249,25 +280,26 @@ class ParallelCrossEntropy(torch.autograd.Function):
     """
 
     @staticmethod
-    def forward(ctx, inp, target, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100):
+    def forward(ctx, inp, target, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, smoothing="all"):
         buf = inp.detach()
-        loss, _ = ce_fwd_bwd_fused(buf, target, label_smoothing, reduce_loss, ignore_idx)
-        ctx.reduce_loss = bool(reduce_loss)
+        loss, _ = ce_fwd_bwd_fused(buf, target, label_smoothing, reduce_loss, ignore_idx, smoothing=smoothing)
+        ctx.reduced = reduction_code(reduce_loss) != _abi.CE_REDUCE_NONE
         ctx.save_for_backward(buf)
-        return loss[0] if reduce_loss else loss.view(target.shape)
+        return loss[0] if ctx.reduced else loss.view(target.shape)
 
     @staticmethod
     def backward(ctx, grad_loss):
         (buf,) = ctx.saved_tensors
-        ce_scale_grad_inplace(buf, grad_loss, per_row=not ctx.reduce_loss)
-        return buf, None, None, None, None
+        ce_scale_grad_inplace(buf, grad_loss, per_row=not ctx.reduced)
+        return buf, None, None, None, None, None
 
 
 def parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False, dist_process_group=None,
-                           ignore_idx=-100):
+                           ignore_idx=-100, *, smoothing="all"):
     """The issue #29 interface: FP32 loss (per row in ``target``'s shape, or
-    their mean over non-ignored rows); the gradient is staged in place in
-    ``inp`` (in its dtype) and reaches autograd through ParallelCrossEntropy.
+    their mean over non-ignored rows, or with ``reduce_loss="sum"`` their
+    sum); the gradient is staged in place in ``inp`` (in its dtype) and
+    reaches autograd through ParallelCrossEntropy.
 
     ``inp`` is (B, SQ, V) or (SQ, B, V) (any row strides, contiguous
     columns); ``target`` the matching (B, SQ) / (SQ, B) int64 global indices.
@@ -275,7 +307,7 @@ def parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False, 
     if dist_process_group is not None:
         raise NotImplementedError("vocabulary-parallel process groups need more than one GPU; use "
                                   "ce_shard_partial_stats / ce_shard_combine / ce_backward_inplace per shard")
-    return ParallelCrossEntropy.apply(inp, target, label_smoothing, reduce_loss, ignore_idx)
+    return ParallelCrossEntropy.apply(inp, target, label_smoothing, reduce_loss, ignore_idx, smoothing)
 
 
 class Profiler:

@@ -13,7 +13,9 @@ LIB_PATH = os.path.join(PKG, "libce.so")
 
 CE_OK, CE_EINVAL, CE_EDTYPE, CE_ELAYOUT, CE_EWORKSPACE, CE_EHIP, CE_EDEADLOCK = range(7)
 CE_F32, CE_BF16 = 0, 1
-CE_ABI_VERSION = 1
+CE_REDUCE_NONE, CE_REDUCE_MEAN, CE_REDUCE_SUM = 0, 1, 2
+CE_SMOOTH_ALL, CE_SMOOTH_OTHERS = 0, 1
+CE_ABI_VERSION = 2
 
 
 class CeLogits(ctypes.Structure):
@@ -41,7 +43,7 @@ class CeParams(ctypes.Structure):
         ("reduce_loss", ctypes.c_int32),
         ("ignore_idx", ctypes.c_int64),
         ("split_chunks", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("smoothing", ctypes.c_int32),
     ]
 
 

@@ -70,11 +70,37 @@ ce_status check_params(const ce_params* p) {
   if (!p) return fail(CE_EINVAL, "params is NULL");
   const float a = p->label_smoothing;
   if (!(a >= 0.f && a <= 1.f)) return fail(CE_EINVAL, "label_smoothing %g is outside [0, 1]", (double)a);
-  if (p->reduce_loss != 0 && p->reduce_loss != 1) return fail(CE_EINVAL, "reduce_loss must be 0 or 1");
+  if (p->reduce_loss != CE_REDUCE_NONE && p->reduce_loss != CE_REDUCE_MEAN && p->reduce_loss != CE_REDUCE_SUM)
+    return fail(CE_EINVAL, "reduce_loss %d is not CE_REDUCE_NONE, CE_REDUCE_MEAN or CE_REDUCE_SUM", p->reduce_loss);
   if (p->split_chunks < 0 || p->split_chunks > kMaxChunks)
     return fail(CE_EINVAL, "split_chunks %d outside [0, %lld]", p->split_chunks, (long long)kMaxChunks);
-  if (p->reserved != 0) return fail(CE_EINVAL, "params.reserved must be 0");
+  if (p->smoothing != CE_SMOOTH_ALL && p->smoothing != CE_SMOOTH_OTHERS)
+    return fail(CE_EINVAL, "smoothing %d is not CE_SMOOTH_ALL or CE_SMOOTH_OTHERS", p->smoothing);
   return CE_OK;
+}
+
+// Smoothing over the other classes divides a by V - 1: a vocabulary of one
+// class has no other class to give it to.
+ce_status check_smoothing(const ce_params* p, int64_t vocab_total) {
+  if (p->smoothing == CE_SMOOTH_OTHERS && p->label_smoothing > 0.f && vocab_total < 2)
+    return fail(CE_EINVAL, "smoothing over the other classes needs vocab_total >= 2 (got %lld)",
+                (long long)vocab_total);
+  return CE_OK;
+}
+
+// The smoothed target distribution: q_t on the target, q_o on every other
+// column, in double; the kernels take q_o, q_t - q_o and 1 - q_t rounded once
+// to FP32 (and the fused kernel's FP64 path q_o and q_t themselves).
+struct Smoothing {
+  double q_o, q_t;
+  float f_o() const { return (float)q_o; }
+  float f_to() const { return (float)(q_t - q_o); }
+  float f_rest() const { return (float)(1.0 - q_t); }
+};
+Smoothing smoothing_of(const ce_params* p, int64_t vocab_total) {
+  const double a = p->label_smoothing, V = (double)vocab_total;
+  if (p->smoothing == CE_SMOOTH_OTHERS) return Smoothing{a > 0.0 ? a / (V - 1.0) : 0.0, 1.0 - a};
+  return Smoothing{a / V, a / V + (1.0 - a)};
 }
 
 ce_status check_logits(const ce_logits* x, bool unsharded) {
@@ -144,6 +170,9 @@ WsLayout ws_layout(int64_t N, int32_t K, bool reduce, bool fused) {
 }
 
 
+// The divisor of a reduced loss: n for the mean, none (NULL) for the sum.
+const int32_t* mean_n(const ce_params* p, const int32_t* n) { return p->reduce_loss == CE_REDUCE_MEAN ? n : nullptr; }
+
 int32_t chunks_for(const ce_logits* x, const ce_params* p) {
   int32_t K = p->split_chunks > 0 ? p->split_chunks : vce::fused_auto_chunks(x->dtype, x->v_local);
   return K < 1 ? 1 : K;
@@ -164,7 +193,10 @@ vce::RowLayout row_layout(const ce_logits* x, const ce_targets* t, const ce_para
   L.ts0 = t->s0;
   L.ts1 = t->s1;
   L.ignore_idx = p->ignore_idx;
-  L.alpha = p->label_smoothing;
+  const Smoothing q = smoothing_of(p, x->vocab_total);
+  L.q_o = q.f_o();
+  L.q_to = q.f_to();
+  L.q_rest = q.f_rest();
   return L;
 }
 
@@ -221,7 +253,7 @@ size_t ce_combine_workspace_bytes(int64_t rows, const ce_params* p) {
 ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p, float* loss, float* lse,
                      int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
   ce_status st;
-  if ((st = check_params(p)) || (st = check_logits(x, true))) return st;
+  if ((st = check_params(p)) || (st = check_logits(x, true)) || (st = check_smoothing(p, x->vocab_total))) return st;
   const int64_t N = x->d0 * x->d1;
   if ((st = check_targets(t, N))) return st;
   if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
@@ -237,7 +269,8 @@ ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p
   if (N == 0) {  // nothing to read: n = 0, and the mean of no rows is 0/0
     if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
       return hip_fail(e, "prologue launch");
-    if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, n_out, loss, stream))) return hip_fail(e, "mean launch");
+    if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, mean_n(p, n_out), loss, stream)))
+      return hip_fail(e, "mean launch");
     return CE_OK;
   }
   vce::StatsArgs a;
@@ -250,7 +283,7 @@ ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
   if ((e = vce::launch_stats(a, stream, e0, e1))) return hip_fail(e, "forward launch");
-  if (p->reduce_loss && (e = vce::launch_mean(a.row_loss, N, n_out, loss, stream)))
+  if (p->reduce_loss && (e = vce::launch_mean(a.row_loss, N, mean_n(p, n_out), loss, stream)))
     return hip_fail(e, "mean launch");
   return CE_OK;
 }
@@ -258,11 +291,11 @@ ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p
 ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* lse,
                               const float* grad_out, const int32_t* n_valid, hipStream_t stream) {
   ce_status st;
-  if ((st = check_params(p)) || (st = check_logits(x, false))) return st;
+  if ((st = check_params(p)) || (st = check_logits(x, false)) || (st = check_smoothing(p, x->vocab_total))) return st;
   const int64_t N = x->d0 * x->d1;
   if ((st = check_targets(t, N))) return st;
   if (N > 0 && !lse) return fail(CE_EINVAL, "lse is NULL");
-  if (p->reduce_loss && !n_valid) return fail(CE_EINVAL, "reduce_loss needs n_valid");
+  if (p->reduce_loss == CE_REDUCE_MEAN && !n_valid) return fail(CE_EINVAL, "the mean (CE_REDUCE_MEAN) needs n_valid");
   vce::BackwardArgs a;
   a.L = row_layout(x, t, p);
   a.lse = lse;
@@ -279,7 +312,7 @@ ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_
 ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* grad_out,
                            float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
   ce_status st;
-  if ((st = check_params(p)) || (st = check_logits(x, true))) return st;
+  if ((st = check_params(p)) || (st = check_logits(x, true)) || (st = check_smoothing(p, x->vocab_total))) return st;
   const int64_t N = x->d0 * x->d1;
   if ((st = check_targets(t, N))) return st;
   if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
@@ -306,7 +339,8 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
     int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
     if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
       return hip_fail(e, "prologue launch");
-    if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, n_out, loss, stream))) return hip_fail(e, "mean launch");
+    if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, mean_n(p, n_out), loss, stream)))
+      return hip_fail(e, "mean launch");
     return CE_OK;
   }
   vce::FusedArgs a;
@@ -327,6 +361,14 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
   if (a.slice_rows < 2048) a.slice_rows = 2048;
   a.nslice = (int32_t)((N + a.slice_rows - 1) / a.slice_rows);
   a.ws_bytes = w.total;
+  // short whole rows take the FP64 path of the 256 x 1 kernel (its only shape for them)
+  a.short_rows = x->v_local <= vce::kShortRow && K == 1;
+  if (a.short_rows && (shape.threads != 256 || shape.vecs != 1))
+    return fail(CE_ELAYOUT, "internal: rows of %lld columns planned on a %d x %d workgroup", (long long)x->v_local,
+                shape.threads, shape.vecs);
+  const Smoothing q = smoothing_of(p, x->vocab_total);
+  a.q_o_d = q.q_o;
+  a.q_t_d = q.q_t;
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
   if ((e = vce::launch_fused(a, shape, stream, e0, e1))) return hip_fail(e, "fused launch");
@@ -352,7 +394,7 @@ ce_status ce_scale_grad_inplace(const ce_logits* x, const float* grad_out, int32
   a.L.tgt = nullptr;
   a.L.ts0 = a.L.ts1 = 0;
   a.L.ignore_idx = 0;
-  a.L.alpha = 0.f;
+  a.L.q_o = a.L.q_to = a.L.q_rest = 0.f;
   a.g = grad_out;
   a.per_row = per_row;
   hipEvent_t e0, e1;
@@ -392,6 +434,7 @@ ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1
   if (S < 1) return fail(CE_EINVAL, "S must be >= 1");
   if (d0 < 0 || d1 < 1) return fail(CE_EINVAL, "need d0 >= 0 and d1 >= 1");
   if (vocab_total < 1) return fail(CE_EINVAL, "vocab_total must be >= 1");
+  if ((st = check_smoothing(p, vocab_total))) return st;
   if (d0 > 0 && d1 > 0x7fffffffLL / d0) return fail(CE_EINVAL, "more than 2^31-1 rows");
   const int64_t N = d0 * d1;
   if ((st = check_targets(t, N))) return st;
@@ -410,7 +453,8 @@ ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1
   if (N == 0) {  // nothing to combine: n = 0, and the mean of no rows is 0/0
     if ((e = vce::launch_prologue(t->data, t->s0, t->s1, d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
       return hip_fail(e, "prologue launch");
-    if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, n_out, loss, stream))) return hip_fail(e, "mean launch");
+    if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, mean_n(p, n_out), loss, stream)))
+      return hip_fail(e, "mean launch");
     return CE_OK;
   }
   vce::CombineArgs a;
@@ -423,12 +467,14 @@ ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1
   a.ts0 = t->s0;
   a.ts1 = t->s1;
   a.ignore_idx = p->ignore_idx;
-  a.alpha = p->label_smoothing;
+  const Smoothing q = smoothing_of(p, vocab_total);
+  a.q_o = q.f_o();
+  a.q_to = q.f_to();
   a.row_loss = p->reduce_loss ? reinterpret_cast<float*>(wsb + w.row_loss) : loss;
   a.lse = lse;
   a.n_out = n_out;  // counted by the combine kernel's workgroup 0
   if ((e = vce::launch_combine(a, stream))) return hip_fail(e, "combine launch");
-  if (p->reduce_loss && (e = vce::launch_mean(a.row_loss, N, n_out, loss, stream)))
+  if (p->reduce_loss && (e = vce::launch_mean(a.row_loss, N, mean_n(p, n_out), loss, stream)))
     return hip_fail(e, "mean launch");
   return CE_OK;
 }

@@ -43,7 +43,10 @@ struct RowLayout {
   const int64_t* tgt;
   int64_t ts0, ts1;
   int64_t ignore_idx;
-  float alpha;
+  // the smoothed target distribution: q_t at the target, q_o at every other column
+  float q_o;               // a / V, or a / (V - 1)
+  float q_to;              // q_t - q_o, the target logit's weight in the loss beyond q_o
+  float q_rest;            // 1 - q_t: the target's gradient is s (q_rest - (1 - p_t))
 };
 
 struct FusedArgs {
@@ -51,18 +54,24 @@ struct FusedArgs {
   int32_t K;               // chunks per row
   int32_t aligned;         // every row starts and ends on a 16-byte boundary (no head/tail)
   int64_t C;               // body vectors per chunk
-  int32_t reduce;          // mean over non-ignored rows
+  int32_t reduce;          // CE_REDUCE_NONE / MEAN (over non-ignored rows) / SUM
   const float* g;          // upstream gradient ([N] or [1]); NULL = 1
   int32_t* n_out;          // [1] count of non-ignored rows (nullable), written by the last item's workgroup
-  float* row_loss;         // [N] loss output (reduce 0)
-  unsigned long long* row_loss_tagged;  // [N] tagged per-row losses (workspace; both modes)
-  float* mean_out;         // [1] mean loss (reduce 1), written by the workgroup of the last item
+  float* row_loss;         // [N] loss output (no reduction)
+  unsigned long long* row_loss_tagged;  // [N] tagged per-row losses (workspace; every mode)
+  float* mean_out;         // [1] mean or sum of the losses, written by the workgroup of the last item
   WsHeader* hdr;
   unsigned long long* slots;  // [N][K][4] tagged exchange words (K > 1)
   int64_t slice_rows;      // rows per target slice; workgroup b < nslice counts slice b
   unsigned long long ws_bytes;  // workspace bytes this call uses (checked against the initialised size)
   int32_t nslice;
+  // rows of at most kShortRow columns held whole (K = 1): statistics and
+  // gradient in FP64 by one wave, with the distribution in double
+  int32_t short_rows;
+  double q_o_d, q_t_d;     // q_o and q_t
 };
+// Longest row the fused kernel's FP64 path takes (one column per lane of a wave).
+constexpr int64_t kShortRow = 64;
 
 enum StatsMode { kStatsForward = 0, kStatsShard = 1 };
 
@@ -78,9 +87,9 @@ struct StatsArgs {
 struct BackwardArgs {
   RowLayout L;
   const float* lse;
-  int32_t reduce;
+  int32_t reduce;          // CE_REDUCE_*
   const float* g;
-  const int32_t* n_valid;
+  const int32_t* n_valid;  // read with CE_REDUCE_MEAN only
 };
 
 struct ScaleArgs {
@@ -95,7 +104,7 @@ struct CombineArgs {
   int64_t N, d1, vocab_total;
   const int64_t* tgt;
   int64_t ts0, ts1, ignore_idx;
-  float alpha;
+  float q_o, q_to;         // as in RowLayout
   float* row_loss;
   float* lse;
   int32_t* n_out;   // [1] count of non-ignored rows, written by workgroup 0 (may be NULL)
@@ -114,6 +123,7 @@ hipError_t launch_fused(const FusedArgs& a, FusedShape shape, hipStream_t stream
 hipError_t launch_stats(const StatsArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+// out[0] = sum of row_loss / n_valid[0], or the plain sum when n_valid is NULL
 hipError_t launch_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out, hipStream_t stream);
 hipError_t launch_ws_init(void* ws, size_t bytes, hipStream_t stream);
 hipError_t launch_scale(const ScaleArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);

@@ -1,15 +1,19 @@
 // gfx950 kernels of the fused (vocabulary-parallel) cross-entropy library.
 //
-// Arithmetic (per row of logits x, target t, smoothing a, V = vocab_total):
+// Arithmetic (per row of logits x, target t, V = vocab_total, and a smoothed
+// target distribution that puts q_t on the target and q_o on every other
+// column: q_o = a / V, q_t = q_o + 1 - a for smoothing a over all classes,
+// q_o = a / (V - 1), q_t = 1 - a over the other classes):
 //   lse  = log sum_j exp(x_j)                       (FP32 accumulation)
-//   loss = lse - (1 - a) x_t - (a / V) sum_j x_j
-//   grad_j = s (exp(x_j - lse) - a / V - (1 - a) [j == t])
+//   loss = lse - (q_t - q_o) x_t - q_o sum_j x_j    (= -sum_j q_j (x_j - lse))
+//   grad_j = s (exp(x_j - lse) - q_j)
 // -- the log_softmax + NLL identity and the softmax-minus-onehot gradient of
 // the CANN ops-nn fusion page ("fusion scheme", "backward", smoothing per its
-// "pitfall 3" read with the uniform a/V of torch's F.cross_entropy), the
-// in-place gradient staging of TransformerEngineNPU issue #29 (section 6),
-// and the per-shard (max, sum-exp, target logit) exchange of hyper-parallel
-// issue #269 (section 3.1) extended with the row sum that a > 0 needs.
+// forward step 4 and "pitfall 3", or the uniform a/V of torch's
+// F.cross_entropy), the in-place gradient staging of TransformerEngineNPU
+// issue #29 (section 6), and the per-shard (max, sum-exp, target logit)
+// exchange of hyper-parallel issue #269 (section 3.1) extended with the row
+// sum that q_o > 0 needs.  The host passes q_o, q_t - q_o and 1 - q_t.
 //
 // Exponentials are taken in base 2 on the hardware v_exp_f32: with
 // u = x * log2(e), lse = ln2 * (m2 + log2 sum_j 2^(u_j - m2)) for any m2, and
@@ -39,8 +43,8 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 // Reuse path: the sum pass's terms (scaled by 2^kReuseShift to keep them in
 // FP16's normal range) are kept as FP16 for the BF16 gradient, relative
 // error 2^-11 next to the gradient's own 2^-9 rounding, inside the 2^-8 bar.
-// Near p = a/V the gradient s (p - a/V) cancels and that FP16 error is
-// absolute, s (a/V) 2^-11; the path is taken only while s (a/V) and a/V are
+// Near p = q_o the gradient s (p - q_o) cancels and that FP16 error is
+// absolute, s q_o 2^-11; the path is taken only while s q_o and q_o are
 // small enough that this stays well under the 1e-7 floor (scaled by s).
 constexpr int kReuseShift = 14;
 constexpr float kReuseUnscale = 1.f / 16384.f;
@@ -352,9 +356,10 @@ __device__ __forceinline__ Row<DT> row_span(const RowLayout& L, int64_t r) {
   return g;
 }
 
-// Upstream gradient scale s of row r.
+// Upstream gradient scale s of row r: g_r, g / n (mean) or g (sum).
 __device__ __forceinline__ float grad_scale(int32_t reduce, const float* g, const int32_t* n_valid, int64_t r) {
-  if (reduce) return (g ? g[0] : 1.f) / (float)(*n_valid);
+  if (reduce == CE_REDUCE_MEAN) return (g ? g[0] : 1.f) / (float)(*n_valid);
+  if (reduce == CE_REDUCE_SUM) return g ? g[0] : 1.f;
   return g ? g[r] : 1.f;
 }
 
@@ -551,11 +556,12 @@ __device__ __forceinline__ void advance_epoch(const FusedArgs& a) {
 // The last item's workgroup finishes the call once its own item is done: it
 // starts after every other workgroup of the launch (in-order dispatch, see
 // k_fused), none of which waits for it, so every tagged word arrives.  It
-// writes n and, with the mean, the N losses summed in index order in FP64
-// (deterministic).  Last, it advances the epoch: every workgroup that used
-// this call's tag has read it by then (its words fed a row loss, a count or
-// both), so the next call's tag is set only after this call is done with it.
-// (The two modes keep separate tails: sharing the mean's tail measurably
+// writes n and, with a reduction, the N losses summed in index order in FP64
+// (deterministic), divided by n for the mean.  Last, it advances the epoch:
+// every workgroup that used this call's tag has read it by then (its words
+// fed a row loss, a count or both), so the next call's tag is set only after
+// this call is done with it.
+// (Reduced and unreduced calls keep separate tails: sharing the mean's tail measurably
 // raised the whole kernel's register allocation.)
 template <int T>
 __device__ void fused_finish(const FusedArgs& a, uint32_t tag) {
@@ -584,9 +590,66 @@ __device__ void fused_finish(const FusedArgs& a, uint32_t tag) {
     double tot = 0.0;
     for (int i = 0; i < T / 64; ++i) tot += s_sum[i];
     // N >= 1 here; n = 0 gives 0/0 = NaN
-    a.mean_out[0] = cnt_ok ? (float)(tot / (double)n) : __builtin_nanf("");
+    if (a.reduce == CE_REDUCE_SUM)
+      a.mean_out[0] = (float)tot;
+    else
+      a.mean_out[0] = cnt_ok ? (float)(tot / (double)n) : __builtin_nanf("");
     advance_epoch(a);
   }
+}
+
+// --------------------------------------------------------------------------
+// A whole row of at most kShortRow columns, in FP64, by wave 0 (one column
+// per lane): max, sum of exp(x - max), lse, the row sum and the target logit
+// by wave reductions, then loss and gradient s (p_j - q_j) rounded once to
+// the output.  Rows this short cost a launch whatever the arithmetic, and
+// FP32 cannot hold the gradient where p_j sits close to a large q_j (a few
+// columns, heavy smoothing): one FP32 rounding of p already exceeds the FP32
+// gradient's absolute floor there.
+__device__ __forceinline__ double wave_max_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <int DT, int T>
+__device__ void fused_short_row(const FusedArgs& a, uint32_t tag, int64_t r, const Row<DT>& g) {
+  const int lane = threadIdx.x;
+  if (lane >= 64) return;  // wave 0 holds the row
+  const RowLayout& L = a.L;
+  const bool ws_ok = (a.hdr->magic == kWsMagic) & (a.hdr->init_bytes >= a.ws_bytes);
+  const Rsrc rx = make_rsrc(g.base, L.V * ElemT<DT>::EB);  // lanes past the row read 0, their stores drop
+  const bool in = lane < L.V;
+  const double x = (double)bload_elem<DT>(rx, lane);
+  const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
+
+  // s = g_r, g / n (the mean; n from the slice counts) or g (the sum)
+  double s = a.g ? (double)a.g[a.reduce ? 0 : r] : 1.0;
+  if (a.reduce == CE_REDUCE_MEAN) {
+    bool ok;
+    const int32_t n = wave_count(a, tag, count_word_early(a), &ok);
+    s = ok ? s / (double)n : __builtin_nan("");
+  }
+  if (!ws_ok) {
+    s = __builtin_nan("");
+    if (lane == 0) atomicOr(&a.hdr->status, 2u);
+  }
+
+  const double m = wave_max_d(in ? x : -INFINITY);
+  const double d = wave_sum_d(in ? exp(x - m) : 0.0);
+  const double R = wave_sum_d(in ? x : 0.0);
+  const double y = wave_sum_d(lane == g.t ? x : 0.0);
+  const double lse = m + log(d);
+  const double loss = lse - (a.q_t_d - a.q_o_d) * y - a.q_o_d * R;
+  const double q = lane == g.t ? a.q_t_d : a.q_o_d;
+  const double gr = tvalid ? s * (exp(x - lse) - q) : __builtin_nan("");
+  bstore_elem<DT>((float)gr, rx, lane);
+  publish_row_loss<T>(a, tag, r, tvalid && ws_ok ? (float)loss : __uint_as_float(0x7fc00000u), true);
 }
 
 // --------------------------------------------------------------------------
@@ -653,8 +716,9 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       if (last && tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
     }
     publish_row_loss<T>(a, tag, r, 0.f, first);
+  } else if (P == 1 && a.short_rows) {
+    if constexpr (P == 1) fused_short_row<DT, T>(a, tag, r, g);
   } else {
-
 
     // ---- the single read of this chunk (slots past the chunk read as zero
     // and are masked below; their stores are dropped)
@@ -667,7 +731,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     // which keeps it out of the vector loads' in-order completion count, and
     // is combined without branches, so no wait is placed before the chunk is
     // in flight.
-    const unsigned long long cw = (a.reduce && tid < 64) ? count_word_early(a) : 0ull;
+    const unsigned long long cw = (a.reduce == CE_REDUCE_MEAN && tid < 64) ? count_word_early(a) : 0ull;
     const bool ws_ok = (wsrec[0] == kWsMagic) & (wsrec[1] >= a.ws_bytes);
     uint4 v[P];
 #pragma unroll
@@ -708,7 +772,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     const int own_where = own_tid < 0 ? 0 : (tl < g.h ? 1 : (tl - g.h < g.nv * E ? 2 : 3));
 
     // ---- max, and the row sum that the smoothing term needs
-    const bool smooth = L.alpha != 0.f;
+    const bool smooth = L.q_o != 0.f;
     float m = fmaxf(hx, tx);
     float rs = (hv ? hx : 0.f) + (tv ? tx : 0.f);
     if (smooth) {
@@ -726,16 +790,16 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       }
     }
     const float m_loc = m;  // this thread's own maximum (bounds its largest softmax term)
-    if (a.reduce && tid < 64) {  // n, handed to the other waves by block_max's barrier
+    if (a.reduce == CE_REDUCE_MEAN && tid < 64) {  // n, handed to the other waves by block_max's barrier
       bool ok;
       const int32_t n = wave_count(a, tag, cw, &ok);
       if (tid == 0) sh_n = ok ? n : -1;
     }
     m = block_max<T>(m, sh);
-    // s = g / n with the mean, g_r without; NaN (loud) when a count never
-    // arrived or the workspace was not initialised
+    // s = g / n with the mean, g with the sum, g_r without; NaN (loud) when a
+    // count never arrived or the workspace was not initialised
     float s_up = g_up;
-    if (a.reduce) s_up = sh_n >= 0 ? g_up / (float)sh_n : __builtin_nanf("");
+    if (a.reduce == CE_REDUCE_MEAN) s_up = sh_n >= 0 ? g_up / (float)sh_n : __builtin_nanf("");
     if (!ws_ok) {
       s_up = __builtin_nanf("");
       if (tid == 0) atomicOr(&a.hdr->status, 2u);
@@ -773,8 +837,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     // Per wave: every lane's largest term is below |s| p_max 2^-11 <= kReuseAbs, with
     // p_j <= e^(x_j - chunk max) because lse >= every chunk's max; a wave
     // holding a large softmax value keeps its logits and the exact path.
-    const bool reuse_row = DT == CE_BF16 && fabsf(s_up) * L.alpha * (1.f / (float)L.vocab_total) <= kReuseSA &&
-                           L.alpha * (1.f / (float)L.vocab_total) <= kReuseA;
+    const bool reuse_row = DT == CE_BF16 && fabsf(s_up) * L.q_o <= kReuseSA && L.q_o <= kReuseA;
     const bool big_lane = fabsf(s_up) * ex2((m_loc - m) * kL) * (1.f / 2048.f) > kReuseAbs;
     const bool reuse = reuse_row && !__any(big_lane);
     float d0 = ex2(__builtin_fmaf(hx, kL, -msub)) + ex2(__builtin_fmaf(tx, kL, -msub)), d1 = 0.f;
@@ -865,10 +928,8 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     const float c_hi = M2 + lgD;
     const float bb = c_hi - M2;
     const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
-    const float inv_v = 1.f / (float)L.vocab_total;
     const float lse = c_hi * kLn2 + c_lo * kLn2;
-    const float row_loss = tvalid && ws_ok ? lse - (1.f - L.alpha) * Y - (L.alpha * inv_v) * R
-                                          : __uint_as_float(0x7fc00000u);
+    const float row_loss = tvalid && ws_ok ? lse - L.q_to * Y - L.q_o * R : __uint_as_float(0x7fc00000u);
 
     // ---- gradient from the registers, written over the logits.  The store
     // offsets are recomputed from an opaque copy of the thread index, so the
@@ -876,7 +937,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     int tid_st = tid;
     asm volatile("" : "+v"(tid_st));
     const float s = tvalid ? s_up : __uint_as_float(0x7fc00000u);
-    const float b = -s * (L.alpha * inv_v);
+    const float b = -s * L.q_o;
     if (reuse) {
       // p = 2^(x log2e - msub) / D * 2^(msub - M2); the registers hold that first factor times 2^14
       const float kr = s * ex2(msub - M2 - (float)kReuseShift) / Dt;
@@ -903,10 +964,10 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(hx, c_hi, c_lo), s, b), rh, tid);
       bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(tx, c_hi, c_lo), s, b), rt, tid);
     }
-    // target element: s (p_t - a/V - (1 - a)) = s ((a - a/V) - (1 - p_t)) with 1 - p_t = D_excl / D,
+    // target element: s (p_t - q_t) = s ((1 - q_t) - (1 - p_t)) with 1 - p_t = D_excl / D,
     // stored by the lane that just wrote its vector (same-thread order keeps this store last)
     if (tid == own_tid) {
-      const float g_t = s * ((L.alpha - L.alpha * inv_v) - D / Dt);
+      const float g_t = s * (L.q_rest - D / Dt);
       if (own_where == 1)
         bstore_elem<DT>(g_t, rh, tid);
       else if (own_where == 3)
@@ -1003,7 +1064,7 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
         const float bb = c_hi - M2;
         const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
         const float lse = c_hi * kLn2 + c_lo * kLn2;
-        const float loss = lse - (1.f - L.alpha) * y - (L.alpha / (float)L.vocab_total) * rs;
+        const float loss = lse - L.q_to * y - L.q_o * rs;
         a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
         if (a.lse) a.lse[r] = tvalid ? lse : __uint_as_float(0x7fc00000u);
       } else {
@@ -1022,7 +1083,6 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
   constexpr int E = ElemT<DT>::E, EB = ElemT<DT>::EB;
   const int tid = threadIdx.x;
   const RowLayout& L = a.L;
-  const float inv_v = 1.f / (float)L.vocab_total;
   for (int64_t r = blockIdx.x; r < L.N; r += gridDim.x) {
     const Row<DT> g = row_geometry<DT>(L, r);
     if (g.t == L.ignore_idx) {
@@ -1039,8 +1099,8 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
     const float c_lo = __builtin_fmaf(lse, kL, -c_hi);
     float s = grad_scale(a.reduce, a.g, a.n_valid, r);
     if (!tvalid) s = __uint_as_float(0x7fc00000u);
-    const float b = -s * (L.alpha * inv_v);
-    const float a_rest = L.alpha - L.alpha * inv_v;
+    const float b = -s * L.q_o;
+    const float a_rest = L.q_rest;
     const Rsrc rb = make_rsrc(g.body, g.nv * 16);
     const Rsrc rh = make_rsrc(g.base, g.h * EB);
     const Rsrc rt = make_rsrc(g.tail, (int64_t)g.tn * EB);
@@ -1050,7 +1110,7 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
       const float tx = bload_elem<DT>(rt, tid);
       float gh = __builtin_fmaf(ex2(__builtin_fmaf(hx, kL, -c_hi) - c_lo), s, b);
       float gt = __builtin_fmaf(ex2(__builtin_fmaf(tx, kL, -c_hi) - c_lo), s, b);
-      // target: s (p_t - 1 + a - a/V) with p_t - 1 = expm1(x_t - lse), p_t never rounded first
+      // target: s (p_t - 1 + 1 - q_t) with p_t - 1 = expm1(x_t - lse), p_t never rounded first
       if (tl == tid) gh = s * (expm1f(hx - lse) + a_rest);
       if (tl == g.h + g.nv * E + tid) gt = s * (expm1f(tx - lse) + a_rest);
       bstore_elem<DT>(gh, rh, tid);
@@ -1106,14 +1166,15 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     R += q.w;
   }
   const float lse = M + lg2(D) * kLn2;
-  const float loss = lse - (1.f - a.alpha) * Y - (a.alpha / (float)a.vocab_total) * R;
+  const float loss = lse - a.q_to * Y - a.q_o * R;
   const bool tvalid = t >= 0 && t < a.vocab_total;
   a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
   if (a.lse) a.lse[r] = tvalid ? lse : __uint_as_float(0x7fc00000u);
 }
 
 // --------------------------------------------------------------------------
-// Mean over non-ignored rows: sum of per-row losses in FP64, fixed order.
+// Mean over non-ignored rows (or the plain sum when n_valid is NULL): sum of
+// per-row losses in FP64, fixed order.
 __global__ __launch_bounds__(1024) void k_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out) {
   __shared__ double sh[16];
   double s = 0.0;
@@ -1126,7 +1187,7 @@ __global__ __launch_bounds__(1024) void k_mean(const float* row_loss, int64_t N,
   if (threadIdx.x == 0) {
     double tot = 0.0;
     for (int i = 0; i < 16; ++i) tot += sh[i];
-    out[0] = (float)(tot / (double)(*n_valid));  // n = 0 gives 0/0 = NaN
+    out[0] = n_valid ? (float)(tot / (double)(*n_valid)) : (float)tot;  // n = 0 gives 0/0 = NaN
   }
 }
 
