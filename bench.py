@@ -2,13 +2,16 @@
 """Benchmark of the fused cross-entropy hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload 5] [--gpus 1]
+                    [--smoothing all|others] [--reduction none|mean|sum]
 
 A step is one pass of the whole path over one batch of synthetic input
 already resident in HBM: for the default workload (4 x 2048 rows of 128000
 BF16 logits, label smoothing 0.1, mean over the 7782 non-ignored rows) that is
-ce_fwd_bwd_fused = prologue kernel (count of non-ignored rows, workspace
-clear) + fused kernel (one read of the logits, the gradient written over them,
-the mean summed by the workgroup that finishes last).  The call overwrites its
+one ce_fwd_bwd_fused call, one kernel launch (the first workgroups count the
+non-ignored rows; every workgroup reads its part of the logits once and writes
+the gradient over it; the workgroup that starts last sums the mean).
+--smoothing and --reduction run the same step with smoothing over the other
+V-1 classes or another reduction.  The call overwrites its
 input with the gradient, so each timed step works on its own copy of the
 logits from a pool in HBM, refreshed from the generated batch just before the
 timed region: every timed step sees the logits as generated, never a previous
@@ -66,7 +69,7 @@ def traffic_from_profiles(workload_name: str):
     return t, f"fetch x{fetch_scale:.3f}, write x{write_scale:.3f} (copy calibration)"
 
 
-def cpu_baseline(w, inputs, sample_rows: int):
+def cpu_baseline(w, inputs, sample_rows: int, reduction: str, smoothing: str):
     """The FP64 oracle (as it is) on the first `sample_rows` rows: loss and
     gradient, the same work per row as the GPU step."""
     import numpy as np
@@ -80,9 +83,9 @@ def cpu_baseline(w, inputs, sample_rows: int):
     t0 = time.perf_counter()
     for b in range(0, rows.size, 256):
         blk = rows[b:b + 256]
-        orc.loss_rows(inputs.logits, inputs.targets, w.alpha, rows=blk)
-        orc.grad_rows(inputs.logits, inputs.targets, w.alpha, reduce_loss=w.reduce_loss,
-                      g=1.0 if w.reduce_loss else None, rows=blk, n_valid=n_valid)
+        orc.loss_rows(inputs.logits, inputs.targets, w.alpha, rows=blk, smoothing=smoothing)
+        orc.grad_rows(inputs.logits, inputs.targets, w.alpha, reduce_loss=reduction,
+                      g=None if reduction == "none" else 1.0, rows=blk, n_valid=n_valid, smoothing=smoothing)
     dt = time.perf_counter() - t0
     nbytes = 2 * rows.size * w.V * w.elem_bytes
     return {
@@ -106,6 +109,10 @@ def main():
     ap.add_argument("--cpu-sample-rows", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-chunks", type=int, default=0, help="tuning: force the fused kernel's split")
+    ap.add_argument("--smoothing", choices=["all", "others"], default="all",
+                    help="label smoothing a/V over all classes (default) or a/(V-1) over the other classes")
+    ap.add_argument("--reduction", choices=["none", "mean", "sum"], default=None,
+                    help="loss reduction (default: the workload's own)")
     ap.add_argument("--json-out", default=None)
     args = ap.parse_args()
 
@@ -129,6 +136,8 @@ def main():
     print(f"[bench] generated {w.name} in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
     N, V, b = w.rows, w.V, w.elem_bytes
+    red = args.reduction or ("mean" if w.reduce_loss else "none")
+    sm = args.smoothing
     formula_bytes = 2 * N * V * b  # N*V*b read + N*V*b gradient written
 
     phys_dev = inputs.logits_phys.to(dev)
@@ -145,42 +154,43 @@ def main():
     pool = [phys_dev.clone() for _ in range(P)] if w.calls != "shard" else None
     torch.cuda.synchronize()
 
-    loss = torch.empty(1 if w.reduce_loss else N, dtype=torch.float32, device=dev)
+    loss = torch.empty(1 if red != "none" else N, dtype=torch.float32, device=dev)
     n_valid = torch.empty(1, dtype=torch.int32, device=dev)
     calls_per_step = 1
     if w.calls == "fused":
-        ws = torch.empty(vce.ce_workspace_bytes(view(pool[0]), w.alpha, w.reduce_loss, split_chunks=args.split_chunks),
+        ws = torch.empty(vce.ce_workspace_bytes(view(pool[0]), w.alpha, red, split_chunks=args.split_chunks),
                          dtype=torch.uint8, device=dev)
 
         def step(p):
-            vce.ce_fwd_bwd_fused(view(p), t_view, w.alpha, w.reduce_loss, loss=loss, n_valid=n_valid, ws=ws,
-                                 split_chunks=args.split_chunks)
+            vce.ce_fwd_bwd_fused(view(p), t_view, w.alpha, red, loss=loss, n_valid=n_valid, ws=ws,
+                                 split_chunks=args.split_chunks, smoothing=sm)
     elif w.calls == "split":
-        ws = torch.empty(vce.ce_workspace_bytes(view(pool[0]), w.alpha, w.reduce_loss), dtype=torch.uint8, device=dev)
+        ws = torch.empty(vce.ce_workspace_bytes(view(pool[0]), w.alpha, red), dtype=torch.uint8, device=dev)
         lse = torch.empty(N, dtype=torch.float32, device=dev)
         g = torch.ones(N, dtype=torch.float32, device=dev)
         calls_per_step = 2
 
         def step(p):
             x = view(p)
-            vce.ce_forward(x, t_view, w.alpha, w.reduce_loss, loss=loss, lse=lse, n_valid=n_valid, ws=ws)
-            vce.ce_backward_inplace(x, t_view, lse, w.alpha, w.reduce_loss, grad_out=g, n_valid=n_valid)
+            vce.ce_forward(x, t_view, w.alpha, red, loss=loss, lse=lse, n_valid=n_valid, ws=ws, smoothing=sm)
+            vce.ce_backward_inplace(x, t_view, lse, w.alpha, red, grad_out=g, n_valid=n_valid, smoothing=sm)
     else:  # vocabulary shards: S partial-stat calls, one combine, S backward calls
         bounds = workloads.shard_bounds(V, w.shards)
         pool = [[phys_dev[..., a:c].contiguous() for a, c in bounds] for _ in range(P)]
         stats = torch.empty((len(bounds), N, 4), dtype=torch.float32, device=dev)
         lse = torch.empty(N, dtype=torch.float32, device=dev)
-        ws = torch.empty(vce.ce_combine_workspace_bytes(N, w.reduce_loss), dtype=torch.uint8, device=dev)
+        ws = torch.empty(vce.ce_combine_workspace_bytes(N, red), dtype=torch.uint8, device=dev)
         g = torch.ones(N, dtype=torch.float32, device=dev)
         calls_per_step = 2 * len(bounds)
 
         def step(shards):
             for s, (a, c) in enumerate(bounds):
                 vce.ce_shard_partial_stats(shards[s], t_view, a, V, stats=stats[s])
-            vce.ce_shard_combine(stats, t_view, V, w.alpha, w.reduce_loss, loss=loss, lse=lse, n_valid=n_valid, ws=ws)
+            vce.ce_shard_combine(stats, t_view, V, w.alpha, red, loss=loss, lse=lse, n_valid=n_valid, ws=ws,
+                                 smoothing=sm)
             for s, (a, c) in enumerate(bounds):
-                vce.ce_backward_inplace(shards[s], t_view, lse, w.alpha, w.reduce_loss, grad_out=g, n_valid=n_valid,
-                                        vocab_start=a, vocab_total=V)
+                vce.ce_backward_inplace(shards[s], t_view, lse, w.alpha, red, grad_out=g, n_valid=n_valid,
+                                        vocab_start=a, vocab_total=V, smoothing=sm)
 
     def restore(p):
         """One pool copy back to the generated logits."""
@@ -311,6 +321,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {**w.describe(), "io_dtype": "bf16" if w.elem_bytes == 2 else "f32", "calls": w.calls,
+                   "reduction": red, "smoothing": sm,
                    "split_chunks": args.split_chunks, "pool": P, "fresh_inputs": P >= args.steps},
         "rows_per_s": round(N / (step_ms * 1e-3), 1),
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
@@ -328,7 +339,7 @@ def main():
         out["moved_bytes_per_step"] = moved
         out["moved_GBps"] = round(moved / (step_ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_sample_rows)
+        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_sample_rows, red, sm)
     line = json.dumps(out)
     if args.json_out:
         with open(args.json_out, "a") as f:
