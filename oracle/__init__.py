@@ -96,7 +96,9 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.or_shard_stats.argtypes = [P(_Logits), P(_Targets), i64, vp, i64, vp]
     lib.or_shard_combine.argtypes = [vp, i32, i64, i64, P(_Targets), i64, dbl, i32, i64, vp, vp, vp]
     lib.or_shard_grad.argtypes = [P(_Logits), P(_Targets), dbl, i32, i64, i32, vp, dbl, i64, vp, i64, vp, vp]
-    for f in ("or_loss_rows", "or_grad_rows", "or_shard_stats", "or_shard_combine", "or_shard_grad"):
+    lib.or_linear_ce.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, vp, i64, dbl, i32, i64, i32, vp, dbl, i64,
+                                 i32, vp, vp, vp, vp]
+    for f in ("or_loss_rows", "or_grad_rows", "or_shard_stats", "or_shard_combine", "or_shard_grad", "or_linear_ce"):
         getattr(lib, f).restype = ctypes.c_int
     lib.or_max_threads.restype = ctypes.c_int
     return lib
@@ -271,6 +273,50 @@ class Oracle:
                                            g_row_ptr, g_scalar, int(n_valid), r.ctypes.data, r.size,
                                            lse.ctypes.data, out.ctypes.data))
         return out
+
+    def linear_ce(self, h, w, t, alpha=0.0, ignore_idx=-100, reduce_loss=False, g=None, n_valid=None,
+                  smoothing="all", round_logits=True, want_dh=True, want_dw=True, want_g=False):
+        """Head + loss of h [N, D] and w [V, D] (CPU, FP32 or BF16, contiguous
+        columns), targets t [N] int64.  Returns (loss rows [N], dh [N, D],
+        dw [V, D]) in float64, and G [N, V] after them with ``want_g``; the
+        reduction of the loss is left to ``reduce``."""
+        if h.dtype != w.dtype or h.dim() != 2 or w.dim() != 2 or h.shape[1] != w.shape[1]:
+            raise OracleError("h [N, D] and w [V, D] of one dtype")
+        if h.device.type != "cpu" or w.device.type != "cpu" or t.device.type != "cpu":
+            raise OracleError("CPU tensors only")
+        if (h.shape[0] > 1 and h.stride(1) != 1) or w.stride(1) != 1:
+            raise OracleError("contiguous columns only")
+        code = OR_F32 if h.dtype == torch.float32 else OR_BF16 if h.dtype == torch.bfloat16 else None
+        if code is None:
+            raise OracleError(f"unsupported dtype {h.dtype}")
+        N, D = h.shape
+        V = w.shape[0]
+        if t.dtype != torch.int64 or t.dim() != 1 or t.numel() != N:
+            raise OracleError("targets must be int64 [N]")
+        if n_valid is None:
+            n_valid = int((t != ignore_idx).sum())
+        red = reduction_code(reduce_loss)
+        g_row_ptr, g_scalar, g_keep = None, 1.0, None
+        if g is not None:
+            if red:
+                g_scalar = float(g)
+            else:
+                g_keep = np.ascontiguousarray(np.asarray(g, dtype=np.float64).reshape(-1))
+                if g_keep.size != N:
+                    raise OracleError("per-row g must have N entries")
+                g_row_ptr = g_keep.ctypes.data
+        loss = np.empty(N, np.float64)
+        dh = np.empty((N, D), np.float64) if want_dh else None
+        dw = np.empty((V, D), np.float64) if want_dw else None
+        G = np.empty((N, V), np.float64) if want_g else None
+        self._check(self.lib.or_linear_ce(h.data_ptr(), w.data_ptr(), code, N, D, V, max(h.stride(0), D),
+                                          max(w.stride(0), D), t.data_ptr(), t.stride(0) if N > 1 else 1,
+                                          float(alpha), smoothing_code(smoothing), int(ignore_idx), red,
+                                          g_row_ptr, g_scalar, int(n_valid), 1 if round_logits else 0,
+                                          loss.ctypes.data, None if dh is None else dh.ctypes.data,
+                                          None if dw is None else dw.ctypes.data,
+                                          None if G is None else G.ctypes.data))
+        return (loss, dh, dw, G) if want_g else (loss, dh, dw)
 
     def max_threads(self) -> int:
         return int(self.lib.or_max_threads())

@@ -391,6 +391,108 @@ int or_shard_grad(const or_logits* x, const or_targets* t, double alpha, int32_t
   return 0;
 }
 
+/*
+ * Linear head + cross-entropy (hyper-parallel #269, Titan's chunked loss:
+ * the lm_head product and its loss; chunking changes where the logits live,
+ * not what is computed, so the oracle works on all rows at once).
+ *   logits_ij = sum_d h_id W_jd, in FP64 from the exact stored values, then
+ *               materialised as the library does: rounded to FP32 (the GEMM
+ *               accumulator), then for BF16 inputs to BF16, both
+ *               round-to-nearest-even (round_mode 1); round_mode 0 keeps the
+ *               FP64 value (for finite differences);
+ *   loss_i, G_ij = s_i (softmax_ij - q_ij) of those logits, as above;
+ *   dh_id = sum_j G_ij W_jd,  dW_jd = sum_i G_ij h_id   (FP64, G unrounded).
+ * The gradient treats the rounding of the logits as the identity, as
+ * autograd does for a low-precision matmul.  h: [N, D] row stride h_ld;
+ * W: [V, D] row stride w_ld; dtype OR_F32 or OR_BF16 for both; targets
+ * t[r * t_stride].  Outputs: loss_out[N], dh_out[N * D], dw_out[V * D]
+ * (either gradient may be NULL) and, when g_out is not NULL, G itself [N * V].
+ */
+static double or_load(const void* p, int32_t dtype, int64_t off) {
+  if (dtype == OR_F32) return (double)((const float*)p)[off];
+  uint32_t bits = (uint32_t)((const uint16_t*)p)[off] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* FP32 value rounded to BF16, nearest even (finite inputs). */
+static float or_round_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+int or_linear_ce(const void* h, const void* w, int32_t dtype, int64_t N, int64_t D, int64_t V, int64_t h_ld,
+                 int64_t w_ld, const int64_t* t, int64_t t_stride, double alpha, int32_t smooth, int64_t ignore_idx,
+                 int32_t reduce, const double* g_row, double g_scalar, int64_t n_valid, int32_t round_mode,
+                 double* loss_out, double* dh_out, double* dw_out, double* g_out) {
+  if ((N > 0 && (!h || !t)) || !w || !loss_out || D < 1 || V < 1 || N < 0 || h_ld < D || w_ld < D) return OR_EINVAL;
+  if (dtype != OR_F32 && dtype != OR_BF16) return OR_EINVAL;
+  if (!or_smooth_ok(smooth, alpha, V) || reduce < OR_REDUCE_NONE || reduce > OR_REDUCE_SUM) return OR_EINVAL;
+  double* G = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * (size_t)V);
+  if (!G) return OR_EINVAL;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t r = 0; r < N; ++r) {
+    double* x = G + r * V;
+    const int64_t tgt = t[r * t_stride];
+    if (tgt == ignore_idx) {
+      loss_out[r] = 0.0;
+      for (int64_t j = 0; j < V; ++j) x[j] = 0.0;
+      continue;
+    }
+    if (tgt < 0 || tgt >= V) {
+      bad = 1;
+      for (int64_t j = 0; j < V; ++j) x[j] = 0.0;
+      continue;
+    }
+    for (int64_t j = 0; j < V; ++j) {
+      double acc = 0.0;
+      for (int64_t d = 0; d < D; ++d) acc += or_load(h, dtype, r * h_ld + d) * or_load(w, dtype, j * w_ld + d);
+      if (round_mode == 1) {
+        float f = (float)acc;
+        acc = dtype == OR_BF16 ? (double)or_round_bf16(f) : (double)f;
+      }
+      x[j] = acc;
+    }
+    double m = -INFINITY;
+    for (int64_t j = 0; j < V; ++j)
+      if (x[j] > m) m = x[j];
+    double ssum = 0.0;
+    for (int64_t j = 0; j < V; ++j) ssum += exp(x[j] - m);
+    const double lse = m + log(ssum);
+    double loss = 0.0;
+    for (int64_t j = 0; j < V; ++j) loss -= or_q(smooth, alpha, V, j == tgt) * (x[j] - lse);
+    loss_out[r] = loss;
+    const double s = or_scale(reduce, g_row, g_scalar, n_valid, r);
+    for (int64_t j = 0; j < V; ++j) x[j] = s * (exp(x[j] - lse) - or_q(smooth, alpha, V, j == tgt));
+  }
+  if (dh_out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < N; ++r)
+      for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < V; ++j) acc += G[r * V + j] * or_load(w, dtype, j * w_ld + d);
+        dh_out[r * D + d] = acc;
+      }
+  }
+  if (dw_out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < V; ++j)
+      for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < N; ++r) acc += G[r * V + j] * or_load(h, dtype, r * h_ld + d);
+        dw_out[j * D + d] = acc;
+      }
+  }
+  if (g_out) memcpy(g_out, G, sizeof(double) * (size_t)N * (size_t)V);
+  free(G);
+  return bad ? OR_EBADTARGET : 0;
+}
+
 /* Threads the OpenMP runtime would use for the parallel loops above. */
 int or_max_threads(void) {
 #ifdef _OPENMP

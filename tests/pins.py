@@ -319,6 +319,103 @@ def pin_count_and_rows(orc):
         assert np.array_equal(part, full[rows])
 
 
+def _linear_case(seed, N, D, V, dtype, ignore=2):
+    g = torch.Generator().manual_seed(seed)
+    h = (torch.randn((N, D), generator=g)).to(dtype)
+    w = (torch.randn((V, D), generator=g) * (2.0 / math.sqrt(D))).to(dtype)
+    t = torch.randint(0, V, (N,), generator=g)
+    t[torch.randperm(N, generator=g)[:ignore]] = -100
+    return h, w, t
+
+
+def pin_linear_identity_head(orc):
+    """Head = identity (D = V): the logits are h itself, so the loss and dh are
+    the cross-entropy oracle's loss and gradient (pinned above), and dW = G^T h."""
+    for dtype in (torch.float32, torch.bfloat16):
+        for smoothing in ("all", "others"):
+            for red in ("none", "mean", "sum"):
+                g = torch.Generator().manual_seed(61)
+                V = 9
+                h = (torch.randn((6, V), generator=g) * 2).to(dtype)
+                w = torch.eye(V, dtype=dtype)
+                t = torch.tensor([0, 8, -100, 3, 3, 5])
+                gg = np.linspace(0.5, 1.5, 6) if red == "none" else 0.7
+                loss, dh, dw = orc.linear_ce(h, w, t, 0.2, reduce_loss=red, g=gg, smoothing=smoothing)
+                x3, t2 = h.view(1, 6, V), t.view(1, 6)
+                ref_loss, _ = orc.loss_rows(x3, t2, 0.2, smoothing=smoothing)
+                ref_g = orc.grad_rows(x3, t2, 0.2, reduce_loss=red, g=gg, smoothing=smoothing)
+                _close(loss, ref_loss, 1e-13, 1e-15, f"identity head loss {dtype} {smoothing} {red}")
+                _close(dh, ref_g, 1e-13, 1e-16, "identity head dh")
+                _close(dw, ref_g.T @ h.double().numpy(), 1e-12, 1e-16, "identity head dW = G^T h")
+
+
+def pin_linear_torch(orc):
+    """Loss, dh and dW == torch float64: logits h W^T rounded as the library
+    materialises them (FP32, then BF16 for BF16 inputs, nearest even), then
+    F.cross_entropy with autograd on the rounded logits, dh = G W, dW = G^T h."""
+    for dtype in (torch.float32, torch.bfloat16):
+        for N, D, V in ((5, 7, 11), (8, 16, 33)):
+            for smoothing in ("all", "others"):
+                for red in ("none", "mean", "sum"):
+                    h, w, t = _linear_case(70 + N + V, N, D, V, dtype)
+                    x = (h.double() @ w.double().T).float()
+                    if dtype == torch.bfloat16:
+                        x = x.to(torch.bfloat16)
+                    x = x.double().requires_grad_(True)
+                    a_t = _torch_smoothing(0.1, V, smoothing)
+                    ref = F.cross_entropy(x, t, ignore_index=-100, label_smoothing=a_t, reduction=red)
+                    if red == "none":
+                        gg = torch.linspace(0.5, 1.5, N, dtype=torch.float64)
+                        (G,) = torch.autograd.grad(ref, x, gg)
+                        gg = gg.numpy()
+                    else:
+                        gg = 0.6
+                        (G,) = torch.autograd.grad(ref, x, torch.tensor(gg, dtype=torch.float64))
+                    loss, dh, dw = orc.linear_ce(h, w, t, 0.1, reduce_loss=red, g=gg, smoothing=smoothing)
+                    what = f"linear {dtype} {N}x{D}x{V} {smoothing} {red}"
+                    got = loss if red == "none" else orc.reduce(loss, red, int((t != -100).sum()))
+                    _close(got, ref.detach().numpy(), 1e-12, 1e-14, what + " loss")
+                    _close(dh, (G @ w.double()).numpy(), 1e-11, 1e-15, what + " dh")
+                    _close(dw, (G.T @ h.double()).numpy(), 1e-11, 1e-15, what + " dW")
+
+
+def pin_linear_finite_differences(orc):
+    """dh and dW are the derivatives of the loss (logits kept in FP64 here, so
+    the loss is differentiable); 2^-10 steps on a 2^-10 grid are exact."""
+    hstep = 2.0 ** -10
+    for red in ("none", "mean", "sum"):
+        g = torch.Generator().manual_seed(81)
+        h = (torch.randint(-1024, 1024, (3, 4), generator=g).double() * hstep).float()
+        w = (torch.randint(-1024, 1024, (5, 4), generator=g).double() * hstep).float()
+        t = torch.tensor([1, -100, 4])
+        gr = np.array([0.7, -1.3, 2.0])
+        gs = 1.7
+
+        def objective(hh, ww):
+            loss, _, _ = orc.linear_ce(hh, ww, t, 0.2, smoothing="others", round_logits=False,
+                                       want_dh=False, want_dw=False)
+            return float(np.dot(gr, loss)) if red == "none" else gs * orc.reduce(loss, red, 2)
+
+        _, dh, dw = orc.linear_ce(h, w, t, 0.2, reduce_loss=red, g=gr if red == "none" else gs,
+                                  smoothing="others", round_logits=False)
+        fd_h = np.zeros_like(dh)
+        for i in range(3):
+            for d in range(4):
+                hp, hm = h.clone(), h.clone()
+                hp[i, d] += hstep
+                hm[i, d] -= hstep
+                fd_h[i, d] = (objective(hp, w) - objective(hm, w)) / (2 * hstep)
+        fd_w = np.zeros_like(dw)
+        for j in range(5):
+            for d in range(4):
+                wp, wm = w.clone(), w.clone()
+                wp[j, d] += hstep
+                wm[j, d] -= hstep
+                fd_w[j, d] = (objective(h, wp) - objective(h, wm)) / (2 * hstep)
+        _close(dh, fd_h, 1e-4, 1e-7, f"linear finite differences dh {red}")
+        _close(dw, fd_w, 1e-4, 1e-7, f"linear finite differences dW {red}")
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_closed_form_uniform,
@@ -331,4 +428,7 @@ ALL_PINS = [
     pin_grad_rows_sum_to_zero,
     pin_sharded_equals_unsharded,
     pin_count_and_rows,
+    pin_linear_identity_head,
+    pin_linear_torch,
+    pin_linear_finite_differences,
 ]

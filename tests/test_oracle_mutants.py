@@ -44,7 +44,8 @@ MUTANTS = [
     ("sum_grad_divides_by_n", "if (reduce == OR_REDUCE_SUM) return g_scalar;",
      "if (reduce == OR_REDUCE_SUM) return g_scalar / (double)n_valid;", 1),
     ("sum_loss_is_mean_over_rows", "  return s;\n}", "  return s / (double)nrows;\n}", 1),
-    ("bf16_widened_wrong", "<< 16;", "<< 15;", 1),
+    ("bf16_widened_wrong", "((const uint16_t*)x->data)[off] << 16;", "((const uint16_t*)x->data)[off] << 15;", 1),
+    ("linear_bf16_widened_wrong", "((const uint16_t*)p)[off] << 16;", "((const uint16_t*)p)[off] << 15;", 1),
     ("combine_no_rescale", "D += st[1] * exp(st[0] - M);", "D += st[1];", 1),
     ("combine_drops_target_gather", "xt += st[2];", "xt = st[2];", 1),
     ("combine_others_sign", "(R - xt)) / (double)(vocab_total - 1)", "(R + xt)) / (double)(vocab_total - 1)", 1),
@@ -55,6 +56,15 @@ MUTANTS = [
     ("ignored_row_not_zeroed", "loss_out[k] = 0.0;\n      if (lse_out) lse_out[k] = NAN;\n      continue;\n    }\n    if (tgt < 0 || tgt >= V)",
      "if (lse_out) lse_out[k] = NAN;\n    }\n    if (tgt < 0 || tgt >= V)", 1),
     ("count_counts_ignored", "if (or_target(t, d1, r) != ignore_idx) ++n;", "++n;", 1),
+    ("linear_logits_unrounded", "if (round_mode == 1) {", "if (0) {", 1),
+    ("linear_f32_rounded_to_bf16", "acc = dtype == OR_BF16 ? (double)or_round_bf16(f) : (double)f;",
+     "acc = (double)or_round_bf16(f);", 1),
+    ("linear_bf16_truncated", "u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;", "u = u & 0xffff0000u;", 1),
+    ("linear_grad_unscaled", "x[j] = s * (exp(x[j] - lse) - or_q(smooth, alpha, V, j == tgt));",
+     "x[j] = (exp(x[j] - lse) - or_q(smooth, alpha, V, j == tgt));", 1),
+    ("linear_dh_sign", "dh_out[r * D + d] = acc;", "dh_out[r * D + d] = -acc;", 1),
+    ("linear_dw_keeps_last_row", "acc += G[r * V + j] * or_load(h, dtype, r * h_ld + d);",
+     "acc = G[r * V + j] * or_load(h, dtype, r * h_ld + d);", 1),
 ]
 
 
