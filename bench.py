@@ -114,6 +114,12 @@ def main():
     ap.add_argument("--reduction", choices=["none", "mean", "sum"], default=None,
                     help="loss reduction (default: the workload's own)")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--linear", action="store_true",
+                    help="time the chunked linear head + cross-entropy (ce_linear_cross_entropy) instead")
+    ap.add_argument("--hidden", type=int, default=4096, help="--linear: hidden size D")
+    ap.add_argument("--chunk-rows", type=int, default=0, help="--linear: rows per chunk (0: automatic)")
+    ap.add_argument("--torch-ref", action="store_true",
+                    help="--linear: also time torch's matmul + F.cross_entropy + autograd on the same inputs")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -129,6 +135,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.linear:
+        return bench_linear(args, torch, vce, workloads, dev)
     w = workloads.WORKLOADS[args.workload]
     t_gen = time.perf_counter()
     inputs = workloads.generate(w)
@@ -340,6 +348,111 @@ def main():
         out["moved_GBps"] = round(moved / (step_ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_sample_rows, red, sm)
+    line = json.dumps(out)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
+
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak, AMD public specification
+PEAK_F32_TFLOPS = 157.3    # MI355X FP32 matrix peak
+
+
+def bench_linear(args, torch, vce, workloads, dev):
+    """The language-model head and its loss over row chunks: one step is one
+    ce_linear_cross_entropy call (logits GEMM, fused cross-entropy, dh and dW
+    GEMMs for every chunk) on 4 x 2048 rows, D = --hidden, V = 128000, BF16,
+    label smoothing 0.1, mean over the non-ignored rows.  Synthetic inputs:
+    h ~ N(0, 1), W ~ N(0, (2 / sqrt(D))^2), so the logits have a standard
+    deviation near 2 as in the 128000-column cross-entropy workload."""
+    w5 = workloads.WORKLOADS[5]
+    N, D, V = w5.rows, args.hidden, w5.V
+    g = torch.Generator(device="cpu").manual_seed(4321)
+    h = torch.randn((N, D), generator=g).to(torch.bfloat16).to(dev)
+    W = (torch.randn((V, D), generator=g) * (2.0 / D ** 0.5)).to(torch.bfloat16).to(dev)
+    t = torch.randint(0, V, (N,), generator=g)
+    t[torch.randperm(N, generator=g)[:w5.n_ignored]] = -100
+    t = t.to(dev)
+    red = args.reduction or "mean"
+    nb, chunk = vce.ce_linear_workspace_bytes(h, W, red, args.chunk_rows, w5.alpha, smoothing=args.smoothing)
+    ws = vce.ce_workspace_init(torch.empty(nb, dtype=torch.uint8, device=dev))
+    loss = torch.empty(1 if red != "none" else N, dtype=torch.float32, device=dev)
+    dh = torch.empty_like(h)
+    dw = torch.empty((V, D), dtype=torch.float32, device=dev)
+    n = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def step():
+        vce.ce_linear_cross_entropy(h, W, t, w5.alpha, red, loss=loss, n_valid=n, dh=dh, dw=dw, ws=ws,
+                                    chunk_rows=args.chunk_rows, smoothing=args.smoothing)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / args.steps
+    nchunks = (N + chunk - 1) // chunk
+    with vce.Profiler(args.steps * nchunks) as prof:
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+    ce_ms = sum(prof.ms) / args.steps          # the fused cross-entropy kernels of one step
+    flops = 6.0 * N * D * V                     # logits, dh and dW products
+    gemm_ms = step_ms - ce_ms                   # the GEMMs and the two small count/finish kernels
+    ws_bytes = ws.numel()
+    out = {
+        "metric": "chunked linear head + cross-entropy fwd+bwd: TFLOP/s of its three GEMMs, step time",
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"linear_ce_n{N}_d{D}_v{V}_bf16", "rows": N, "hidden": D, "vocab": V,
+                   "chunk_rows": chunk, "chunks": nchunks, "reduction": red, "smoothing": args.smoothing,
+                   "label_smoothing": w5.alpha},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "GEMMs (hipBLASLt): step time minus the fused cross-entropy kernels"},
+        "cross_entropy": {"us_per_step": round(ce_ms * 1e3, 1), "share": round(ce_ms / step_ms, 4),
+                          "GBps": round(2 * N * V * 2 / (ce_ms * 1e-3) / 1e9, 1)},
+        "memory": {"workspace_bytes": ws_bytes, "full_logits_bytes": N * V * 2},
+        "loss": float(loss[0].item()) if red != "none" else None,
+    }
+    if args.torch_ref:
+        del ws
+        torch.cuda.empty_cache()
+        hr = h.clone().requires_grad_(True)
+        Wr = W.clone().requires_grad_(True)
+        ls = w5.alpha * V / (V - 1) if args.smoothing == "others" else w5.alpha
+
+        def tstep():
+            hr.grad = None
+            Wr.grad = None
+            logits = hr @ Wr.T
+            lo = torch.nn.functional.cross_entropy(logits.float(), t, ignore_index=-100, label_smoothing=ls,
+                                                   reduction=red)
+            (lo if red != "none" else lo.sum()).backward()
+
+        for _ in range(3):
+            tstep()
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record()
+        for _ in range(args.steps):
+            tstep()
+        r1.record()
+        torch.cuda.synchronize()
+        out["torch_reference"] = {"ms_per_step": round(r0.elapsed_time(r1) / args.steps, 3),
+                                  "peak_bytes_over_inputs": torch.cuda.max_memory_allocated() - base,
+                                  "what": "h @ W.T, F.cross_entropy on FP32 logits, autograd (torch ops)"}
     line = json.dumps(out)
     if args.json_out:
         with open(args.json_out, "a") as f:

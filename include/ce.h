@@ -232,6 +232,60 @@ ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1
                            const ce_targets* t, const ce_params* p, float* loss, float* lse, int32_t* n_valid,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Chunked linear + cross-entropy: the language-model head's matrix product
+ * and the loss, forward and backward, over row chunks, so that only one
+ * chunk of logits exists at a time (hyper-parallel #269: Titan's
+ * ChunkedLossWrapper, the sequence-chunked lm_head of its comparison table
+ * row 9 and task P2 #9, against the O(B x L x V) peak of whole logits).
+ * For each chunk of `chunk_rows` consecutive rows c:
+ *   logits_c = h_c W^T                in the input dtype (FP32 accumulation;
+ *                                      a library GEMM on the matrix cores)
+ *   loss, G_c in place of logits_c    ce_fwd_bwd_fused (smoothing and ignore
+ *                                      rules as above)
+ *   dh_c  = G_c W                      in the input dtype (FP32 accumulation)
+ *   dW   += G_c^T h_c                  FP32
+ * The mean divides by the count over all N rows (counted before the first
+ * chunk) and every chunk's gradient uses s = g / n; the sum and the per-row
+ * loss need no count.  G_c is rounded to the input dtype before the two
+ * backward products, as the fused call writes it.
+ */
+typedef struct ce_linear {
+  const void* h;      /* device [N, D] hidden states, row stride h_ld elements, columns contiguous */
+  const void* w;      /* device [V, D] head weight (torch Linear layout: logits = h W^T), row stride w_ld */
+  int32_t dtype;      /* CE_BF16 or CE_F32, for h, w and dh */
+  int32_t reserved;   /* must be 0 */
+  int64_t N, D, V;    /* rows, hidden size, vocabulary (N >= 0, D >= 1, V >= 1) */
+  int64_t h_ld, w_ld; /* >= D */
+} ce_linear;
+
+/* Workspace bytes of ce_linear_cross_entropy for `lin`, `p` and chunk_rows
+ * (0: automatic, about 256 MiB of logits per chunk); 0 if the arguments are
+ * invalid.  `*chunk_rows_out` (may be NULL) receives the chunk size used. */
+size_t ce_linear_workspace_bytes(const ce_linear* lin, const ce_params* p, int64_t chunk_rows,
+                                 int64_t* chunk_rows_out);
+
+/*
+ *   targets   device int64, row r's target at targets[r * t_stride]
+ *   grad_out  as for ce_fwd_bwd_fused over N rows ([N] or [1]; NULL = 1)
+ *   loss      [N] or [1] device FP32, written
+ *   n_valid   [1] device int32 or NULL: the number of non-ignored rows
+ *   dh        device [N, D] in the input dtype (row stride dh_ld), written; NULL: not computed
+ *   dw        device FP32 [V, D] (row stride dw_ld); accumulate_dw = 0 overwrites it, 1 adds to it;
+ *             NULL: not computed
+ *   ws        device workspace of ce_linear_workspace_bytes bytes (256-byte aligned), prepared by
+ *             ce_workspace_init; it holds the chunk's logits, the fused call's exchange words and
+ *             the GEMM library's scratch
+ * The first call on a device creates that device's GEMM library handle (host
+ * state kept until the process ends) and each new shape queries the
+ * library's heuristics once; after that the call allocates nothing.  The
+ * calls are asynchronous on `stream`, with no host synchronisation.
+ */
+ce_status ce_linear_cross_entropy(const ce_linear* lin, const int64_t* targets, int64_t t_stride,
+                                  const ce_params* p, const float* grad_out, float* loss, int32_t* n_valid,
+                                  void* dh, int64_t dh_ld, float* dw, int64_t dw_ld, int32_t accumulate_dw,
+                                  int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Waits for `stream` and reports whether any call that used `ws` since it was
  * prepared or last checked gave up waiting in a split-row exchange or count
  * (CE_EDEADLOCK; its results were NaN) or found the workspace unprepared

@@ -232,3 +232,61 @@ def test_scale_grad_validates(lib):
     assert lib.ce_scale_grad_inplace(ctypes.byref(h.logits(dtype=9)), g.ctypes.data, 1, None) == _abi.CE_EDTYPE
     assert lib.ce_scale_grad_inplace(None, g.ctypes.data, 1, None) == _abi.CE_EINVAL
     assert h.untouched()
+
+
+def _linear_host(N=16, D=8, V=32):
+    h = np.zeros((N, D), np.uint16)
+    w = np.zeros((V, D), np.uint16)
+    t = np.zeros(N, np.int64)
+    return h, w, t
+
+
+def test_linear_rejects_before_any_hip_call(lib):
+    """ce_linear_cross_entropy checks everything on the host first."""
+    h, w, t = _linear_host()
+    loss = np.full(16, 7.0, np.float32)
+    ws = np.zeros(1 << 12, np.uint8)
+
+    def call(lin=None, p=None, t_ptr=t.ctypes.data, ts=1, dh=None, dh_ld=8, dw=None, dw_ld=8, acc=0, chunk=0,
+             wsp=ws.ctypes.data, wsb=ws.nbytes):
+        d = dict(h=h.ctypes.data, w=w.ctypes.data, dtype=_abi.CE_BF16, reserved=0, N=16, D=8, V=32, h_ld=8, w_ld=8)
+        d.update(lin or {})
+        q = dict(label_smoothing=0.0, reduce_loss=1, ignore_idx=-100, split_chunks=0, smoothing=0)
+        q.update(p or {})
+        return lib.ce_linear_cross_entropy(ctypes.byref(_abi.CeLinear(**d)), t_ptr, ts,
+                                           ctypes.byref(_abi.CeParams(**q)), None, loss.ctypes.data, None, dh,
+                                           dh_ld, dw, dw_ld, acc, chunk, wsp, wsb, None)
+
+    assert call(lin=dict(dtype=3)) == _abi.CE_EDTYPE
+    assert call(lin=dict(reserved=1)) == _abi.CE_EINVAL
+    assert call(lin=dict(D=0)) == _abi.CE_EINVAL
+    assert call(lin=dict(h_ld=4)) == _abi.CE_ELAYOUT
+    assert call(lin=dict(w=None)) == _abi.CE_EINVAL
+    assert call(lin=dict(h=h.ctypes.data + 1)) == _abi.CE_ELAYOUT
+    assert call(p=dict(split_chunks=2)) == _abi.CE_EINVAL
+    assert call(p=dict(reduce_loss=7)) == _abi.CE_EINVAL
+    assert call(p=dict(label_smoothing=2.0)) == _abi.CE_EINVAL
+    assert call(lin=dict(V=1), p=dict(smoothing=1, label_smoothing=0.1)) == _abi.CE_EINVAL
+    assert call(t_ptr=None) == _abi.CE_EINVAL
+    assert call(dh=h.ctypes.data, dh_ld=4) == _abi.CE_ELAYOUT
+    assert call(dw=w.ctypes.data, dw_ld=2) == _abi.CE_ELAYOUT
+    assert call(acc=2) == _abi.CE_EINVAL
+    assert call(wsb=64) == _abi.CE_EWORKSPACE
+    assert call(wsp=None) == _abi.CE_EWORKSPACE
+    assert lib.ce_last_error()
+    assert np.all(loss == 7.0)
+
+
+def test_linear_workspace_sizes(lib):
+    h, w, t = _linear_host()
+    lin = _abi.CeLinear(h.ctypes.data, w.ctypes.data, _abi.CE_BF16, 0, 8192, 4096, 128000, 4096, 4096)
+    p = _abi.CeParams(0.1, 1, -100, 0, 0)
+    rows = ctypes.c_int64(0)
+    n = lib.ce_linear_workspace_bytes(ctypes.byref(lin), ctypes.byref(p), 0, ctypes.byref(rows))
+    # automatic chunks of 1024 rows (about 256 MiB of BF16 logits), plus the fused call's words and GEMM scratch
+    assert rows.value == 1024
+    assert 1024 * 128000 * 2 < n < 1024 * 128000 * 2 + (128 << 20)
+    n2 = lib.ce_linear_workspace_bytes(ctypes.byref(lin), ctypes.byref(p), 100, ctypes.byref(rows))
+    assert rows.value == 100 and n2 < n
+    lin.dtype = 9
+    assert lib.ce_linear_workspace_bytes(ctypes.byref(lin), ctypes.byref(p), 0, None) == 0

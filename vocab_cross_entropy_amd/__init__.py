@@ -33,6 +33,7 @@ __all__ = [
     "ce_forward", "ce_backward_inplace", "ce_fwd_bwd_fused", "ce_scale_grad_inplace", "ce_shard_partial_stats",
     "ce_shard_combine",
     "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_init", "ce_workspace_check",
+    "ce_linear_workspace_bytes", "ce_linear_cross_entropy",
     "parallel_cross_entropy",
     "Profiler", "CeError", "CeArgumentError", "lib",
 ]
@@ -257,6 +258,69 @@ def ce_shard_combine(stats, t, vocab_total, label_smoothing=0.0, reduce_loss=Fal
                                 ctypes.byref(p), _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(ws), ws.numel(),
                                 _stream(dev)))
     return loss, lse, n_valid
+
+
+def linear_desc(h: torch.Tensor, w: torch.Tensor) -> _abi.CeLinear:
+    """[N, D] hidden states and the [V, D] head weight (rows may be strided, columns contiguous)."""
+    if h.dim() != 2 or w.dim() != 2 or h.shape[1] != w.shape[1]:
+        raise CeArgumentError(_abi.CE_EINVAL, f"need h [N, D] and w [V, D], got {tuple(h.shape)} and {tuple(w.shape)}")
+    if h.dtype != w.dtype:
+        raise CeArgumentError(_abi.CE_EDTYPE, f"h is {h.dtype}, w is {w.dtype}")
+    if (h.shape[0] > 1 and h.stride(1) != 1) or w.stride(1) != 1:
+        raise CeArgumentError(_abi.CE_ELAYOUT, "h and w need contiguous columns")
+    N, D = h.shape
+    return _abi.CeLinear(_ptr(h), _ptr(w), _dtype_code(h), 0, N, D, w.shape[0], max(h.stride(0), D),
+                         max(w.stride(0), D))
+
+
+def ce_linear_workspace_bytes(h, w, reduce_loss=False, chunk_rows=0, label_smoothing=0.0, ignore_idx=-100,
+                              smoothing="all"):
+    """(bytes, chunk rows) of ce_linear_cross_entropy's workspace."""
+    got = ctypes.c_int64(0)
+    n = lib.ce_linear_workspace_bytes(ctypes.byref(linear_desc(h, w)),
+                                      ctypes.byref(params(label_smoothing, reduce_loss, ignore_idx, 0, smoothing)),
+                                      int(chunk_rows), ctypes.byref(got))
+    if n == 0:
+        _check(_abi.CE_EINVAL)
+    return int(n), int(got.value)
+
+
+def ce_linear_cross_entropy(h, w, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, grad_out=None,
+                            loss=None, n_valid=None, dh=None, dw=None, want_dh=True, want_dw=True,
+                            accumulate_dw=False, chunk_rows=0, ws=None, smoothing="all"):
+    """Loss of the head h W^T over row chunks, with dh = dL/dh (input dtype) and
+    dw = dL/dW (FP32, or added to ``dw`` with ``accumulate_dw``).  ``t`` is
+    the [N] int64 targets (any stride).  Returns (loss, dh, dw, n_valid)."""
+    N, D = h.shape
+    V = w.shape[0]
+    dev = h.device
+    p = params(label_smoothing, reduce_loss, ignore_idx, 0, smoothing)
+    loss = _f32(1 if p.reduce_loss else N, dev) if loss is None else loss
+    n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
+    if dh is None and want_dh:
+        dh = torch.empty((N, D), dtype=h.dtype, device=dev)
+    if dw is None and want_dw:
+        dw = torch.empty((V, D), dtype=torch.float32, device=dev)
+    if dh is not None and (dh.dtype != h.dtype or dh.shape != h.shape or dh.stride(1) != 1):
+        raise CeArgumentError(_abi.CE_ELAYOUT, "dh must be [N, D] in h's dtype with contiguous columns")
+    if dw is not None and (dw.dtype != torch.float32 or tuple(dw.shape) != (V, D) or dw.stride(1) != 1):
+        raise CeArgumentError(_abi.CE_ELAYOUT, "dw must be an FP32 [V, D] tensor with contiguous columns")
+    if t.dim() != 1 or t.numel() != N or t.dtype != torch.int64:
+        raise CeArgumentError(_abi.CE_EINVAL, "targets must be an int64 [N] tensor")
+    desc = linear_desc(h, w)
+    if ws is None:
+        nb = lib.ce_linear_workspace_bytes(ctypes.byref(desc), ctypes.byref(p), int(chunk_rows), None)
+        if nb == 0:
+            _check(_abi.CE_EINVAL)
+        ws = _workspace(nb, dev)
+    if not _is_prepared(ws):
+        ce_workspace_init(ws)
+    _check(lib.ce_linear_cross_entropy(ctypes.byref(desc), _ptr(t), t.stride(0) if N > 1 else 1, ctypes.byref(p),
+                                       _ptr(grad_out), _ptr(loss), _ptr(n_valid), _ptr(dh),
+                                       dh.stride(0) if dh is not None else 0, _ptr(dw),
+                                       dw.stride(0) if dw is not None else 0, int(bool(accumulate_dw)),
+                                       int(chunk_rows), _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, dh, dw, n_valid
 
 
 def ce_workspace_check(ws: torch.Tensor):

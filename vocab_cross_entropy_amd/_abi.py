@@ -47,6 +47,20 @@ class CeParams(ctypes.Structure):
     ]
 
 
+class CeLinear(ctypes.Structure):
+    _fields_ = [
+        ("h", ctypes.c_void_p),
+        ("w", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("N", ctypes.c_int64),
+        ("D", ctypes.c_int64),
+        ("V", ctypes.c_int64),
+        ("h_ld", ctypes.c_int64),
+        ("w_ld", ctypes.c_int64),
+    ]
+
+
 # Every symbol include/ce.h declares, with its ctypes signature.
 _P = ctypes.POINTER
 _vp = ctypes.c_void_p
@@ -63,6 +77,11 @@ SIGNATURES = {
     "ce_shard_combine": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                         _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "ce_workspace_init": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp]),
+    "ce_linear_workspace_bytes": (ctypes.c_size_t, [_P(CeLinear), _P(CeParams), ctypes.c_int64,
+                                                    _P(ctypes.c_int64)]),
+    "ce_linear_cross_entropy": (ctypes.c_int, [_P(CeLinear), _vp, ctypes.c_int64, _P(CeParams), _vp, _vp, _vp, _vp,
+                                               ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                               _vp, ctypes.c_size_t, _vp]),
     "ce_workspace_check": (ctypes.c_int, [_vp, _vp]),
     "ce_profile_start": (ctypes.c_int, [ctypes.c_int32]),
     "ce_profile_stop": (ctypes.c_int, [_vp, ctypes.c_int32, _P(ctypes.c_int32)]),

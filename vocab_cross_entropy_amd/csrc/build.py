@@ -37,16 +37,20 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     kobj = os.path.join(BUILD, "ce_kernels.o")
     aobj = os.path.join(BUILD, "ce_api.o")
+    lobj = os.path.join(BUILD, "ce_linear.o")
     steps = [
         [HIPCC, *DEVICE, *COMMON, "-c", os.path.join(CSRC, "ce_kernels.hip"), "-o", kobj],
         [HIPCC, *COMMON, "-c", os.path.join(CSRC, "ce_api.cpp"), "-o", aobj],
+        [HIPCC, *COMMON, "-c", os.path.join(CSRC, "ce_linear.cpp"), "-o", lobj],
     ]
     for cmd in steps:
         out = _run(cmd)
         if verbose and out.strip():
             print(out)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, aobj, "-o", tmp])
+    # the chunked linear call's GEMMs come from hipBLASLt (ROCm's matrix-core GEMM library)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, aobj, lobj, "-L/opt/rocm/lib", "-lhipblaslt",
+          "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

@@ -217,6 +217,13 @@ void prof_next(hipEvent_t* e0, hipEvent_t* e1) {
 
 }  // namespace
 
+namespace vce {
+void set_last_error(const char* msg) { snprintf(g_err, sizeof g_err, "%s", msg); }
+size_t fused_workspace_bytes(int64_t N, int32_t dtype, int64_t V, bool reduce) {
+  return ws_layout(N, fused_auto_chunks(dtype, V), reduce, true).total;
+}
+}  // namespace vce
+
 extern "C" {
 
 int32_t ce_abi_version(void) { return CE_ABI_VERSION; }
@@ -309,13 +316,15 @@ ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_
   return CE_OK;
 }
 
-ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* grad_out,
-                           float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace vce {
+// Every check of ce_fwd_bwd_fused that depends on the logits' shape and the
+// parameters (not on the buffers), and the plan it leads to.
+ce_status fused_plan(const ce_logits* x, const ce_params* p, int32_t* K_out, int64_t* C_out, FusedShape* shape_out) {
   ce_status st;
   if ((st = check_params(p)) || (st = check_logits(x, true)) || (st = check_smoothing(p, x->vocab_total))) return st;
   const int64_t N = x->d0 * x->d1;
-  if ((st = check_targets(t, N))) return st;
-  if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
   const int32_t K = chunks_for(x, p);
   if (K > kMaxChunks)
     return fail(CE_ELAYOUT, "rows of %lld columns need %d chunks (at most %lld)", (long long)x->v_local, K,
@@ -327,6 +336,25 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
     return fail(CE_ELAYOUT, "split_chunks %d leaves %lld vectors per chunk, above one workgroup's %d",
                 p->split_chunks, (long long)C, 1024 * 16);
   if (N * K > kMaxGrid) return fail(CE_EINVAL, "rows x chunks exceeds the launch grid");
+  if (K_out) *K_out = K;
+  if (C_out) *C_out = C;
+  if (shape_out) *shape_out = shape;
+  return CE_OK;
+}
+}  // namespace vce
+
+namespace {
+
+ce_status fused_call(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* grad_out,
+                     float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ce_status st;
+  int32_t K = 0;
+  int64_t C = 0;
+  vce::FusedShape shape{0, 0};
+  if ((st = vce::fused_plan(x, p, &K, &C, &shape))) return st;
+  const int64_t N = x->d0 * x->d1;
+  if ((st = check_targets(t, N))) return st;
+  if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
   const WsLayout w = ws_layout(N, K, p->reduce_loss != 0, true);
   if (!ws || ws_bytes < w.total)
     return fail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
@@ -373,6 +401,15 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
   prof_next(&e0, &e1);
   if ((e = vce::launch_fused(a, shape, stream, e0, e1))) return hip_fail(e, "fused launch");
   return CE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* grad_out,
+                           float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fused_call(x, t, p, grad_out, loss, n_valid, ws, ws_bytes, stream);
 }
 
 ce_status ce_scale_grad_inplace(const ce_logits* x, const float* grad_out, int32_t per_row, hipStream_t stream) {

@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "ce.h"
+
 namespace vce {
 
 // Workspace header (first 256 bytes of every workspace).
@@ -127,5 +129,22 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out, hipStream_t stream);
 hipError_t launch_ws_init(void* ws, size_t bytes, hipStream_t stream);
 hipError_t launch_scale(const ScaleArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+// chunked linear + cross-entropy: n over all N rows (row r's target at tgt[r * ts]) into n_out, and
+// with the mean scale[0] = g / n; then loss[0] = sum of parts (index order, FP64), / n for the mean
+hipError_t launch_linear_prep(const int64_t* tgt, int64_t ts, int64_t N, int64_t ignore_idx, int32_t reduce,
+                              const float* g, int32_t* n_out, float* scale, hipStream_t stream);
+hipError_t launch_linear_finish(const float* parts, int64_t nparts, int32_t reduce, const int32_t* n, float* out,
+                                hipStream_t stream);
+// zeros in rows x cols of an FP32 matrix with row stride ld
+hipError_t launch_fill_f32(float* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream);
+
+// Shared by the entry points (ce_api.cpp): the calling thread's error detail,
+// and the fused call's workspace need for N whole rows of V columns.
+void set_last_error(const char* msg);
+size_t fused_workspace_bytes(int64_t N, int32_t dtype, int64_t V, bool reduce);
+// every check of ce_fwd_bwd_fused that depends on the logits' shape and the
+// parameters (none on buffers), and the plan: chunks per row K, body vectors
+// per chunk C, workgroup shape
+ce_status fused_plan(const ce_logits* x, const ce_params* p, int32_t* K, int64_t* C, FusedShape* shape);
 
 }  // namespace vce

@@ -1421,6 +1421,51 @@ hipError_t launch_scale(const ScaleArgs& a, hipStream_t stream, hipEvent_t ev0, 
   return e;
 }
 
+// --------------------------------------------------------------------------
+// Chunked linear + cross-entropy: the count over all rows (and the mean's
+// scale g / n, the upstream gradient every chunk's fused call then takes),
+// and the loss from the chunks' sums.
+__global__ __launch_bounds__(1024) void k_linear_prep(const int64_t* tgt, int64_t ts, int64_t N, int64_t ignore_idx,
+                                                      int32_t reduce, const float* g, int32_t* n_out, float* scale) {
+  const int32_t n = block_count_targets<1024>(tgt, 0, ts, N > 0 ? N : 1, N, ignore_idx);
+  if (threadIdx.x == 0) {
+    n_out[0] = n;
+    if (reduce == CE_REDUCE_MEAN) scale[0] = (g ? g[0] : 1.f) / (float)n;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_linear_finish(const float* parts, int64_t nparts, int32_t reduce,
+                                                      const int32_t* n, float* out) {
+  if (threadIdx.x != 0) return;
+  double tot = 0.0;
+  for (int64_t i = 0; i < nparts; ++i) tot += (double)parts[i];
+  out[0] = reduce == CE_REDUCE_MEAN ? (float)(tot / (double)n[0]) : (float)tot;  // n = 0: 0/0 = NaN
+}
+
+__global__ __launch_bounds__(256) void k_fill_f32(float* p, int64_t rows, int64_t cols, int64_t ld) {
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
+    for (int64_t j = threadIdx.x; j < cols; j += 256) p[r * ld + j] = 0.f;
+}
+
+hipError_t launch_linear_prep(const int64_t* tgt, int64_t ts, int64_t N, int64_t ignore_idx, int32_t reduce,
+                              const float* g, int32_t* n_out, float* scale, hipStream_t stream) {
+  hipLaunchKernelGGL(k_linear_prep, dim3(1), dim3(1024), 0, stream, tgt, ts, N, ignore_idx, reduce, g, n_out, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_finish(const float* parts, int64_t nparts, int32_t reduce, const int32_t* n, float* out,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(k_linear_finish, dim3(1), dim3(64), 0, stream, parts, nparts, reduce, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int64_t grid = rows < 65536 ? rows : 65536;
+  hipLaunchKernelGGL(k_fill_f32, dim3((uint32_t)grid), dim3(256), 0, stream, p, rows, cols, ld);
+  return hipGetLastError();
+}
+
 hipError_t launch_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out, hipStream_t stream) {
   hipLaunchKernelGGL(k_mean, dim3(1), dim3(1024), 0, stream, row_loss, N, n_valid, out);
   return hipGetLastError();

@@ -1,0 +1,324 @@
+// Chunked linear + cross-entropy (the language-model head and its loss over
+// row chunks): argument checks, workspace layout, the GEMM plans, and the
+// per-chunk sequence GEMM -> fused cross-entropy -> two backward GEMMs.
+//
+// Layout in the column-major terms of the GEMM library (row-major [R, C]
+// with row stride ld is column-major [C, R] with the same ld):
+//   logits_c^T [V, n] = W [V, D] . h_c^T [D, n]   A = W   (col [D, V], op T), B = h_c (col [D, n], op N)
+//   dh_c^T     [D, n] = W^T [D, V] . G_c^T [V, n] A = W   (col [D, V], op N), B = G_c (col [V, n], op N)
+//   dW^T       [D, V] = h_c^T [D, n] . G_c [n, V] A = h_c (col [D, n], op N), B = G_c (col [V, n], op T)
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include <hip/hip_runtime_api.h>
+#include <hipblaslt/hipblaslt.h>
+
+#include "ce.h"
+#include "ce_internal.h"
+
+namespace {
+
+ce_status lfail(ce_status s, const char* fmt, ...) {
+  char msg[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(msg, sizeof msg, fmt, ap);
+  va_end(ap);
+  vce::set_last_error(msg);
+  return s;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+constexpr size_t kBlasWorkspace = 64ull << 20;   // the GEMM library's scratch, inside the caller's workspace
+constexpr size_t kChunkTarget = 256ull << 20;    // automatic chunk: about this many bytes of logits
+
+// ---- GEMM plans: one per (device, types, shape, ops, leading dims, beta != 0),
+// built on first use (heuristic query) and kept until the process ends.
+struct Plan {
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
+  hipblasLtMatmulAlgo_t algo;
+};
+typedef std::tuple<int, int, int, int64_t, int64_t, int64_t, int, int, int64_t, int64_t, int64_t> PlanKey;
+
+std::mutex g_blas_mu;
+std::map<int, hipblasLtHandle_t> g_handles;
+std::map<PlanKey, Plan> g_plans;
+
+const char* blas_status(hipblasStatus_t s) {
+  switch (s) {
+    case HIPBLAS_STATUS_SUCCESS: return "success";
+    case HIPBLAS_STATUS_NOT_INITIALIZED: return "not initialized";
+    case HIPBLAS_STATUS_ALLOC_FAILED: return "allocation failed";
+    case HIPBLAS_STATUS_INVALID_VALUE: return "invalid value";
+    case HIPBLAS_STATUS_ARCH_MISMATCH: return "architecture mismatch";
+    case HIPBLAS_STATUS_EXECUTION_FAILED: return "execution failed";
+    case HIPBLAS_STATUS_NOT_SUPPORTED: return "not supported";
+    default: return "error";
+  }
+}
+
+// One GEMM: D = alpha op(A) op(B) + beta D, column-major, m x n x k.
+struct Gemm {
+  hipDataType ab, cd;
+  int64_t m, n, k;
+  hipblasOperation_t opa, opb;
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  void* D;
+  int64_t ldd;
+  float beta;
+};
+
+ce_status get_plan(int dev, const Gemm& g, Plan** out) {
+  std::lock_guard<std::mutex> lk(g_blas_mu);
+  hipblasLtHandle_t h;
+  auto hi = g_handles.find(dev);
+  if (hi == g_handles.end()) {
+    hipblasStatus_t s = hipblasLtCreate(&h);
+    if (s != HIPBLAS_STATUS_SUCCESS) return lfail(CE_EHIP, "hipblasLtCreate: %s", blas_status(s));
+    g_handles[dev] = h;
+  } else {
+    h = hi->second;
+  }
+  const PlanKey key{dev, (int)g.ab, (int)g.cd, g.m, g.n, g.k, (int)g.opa, (int)g.opb, g.lda, g.ldb,
+                    g.ldd * 2 + (g.beta != 0.f)};
+  auto it = g_plans.find(key);
+  if (it != g_plans.end()) {
+    *out = &it->second;
+    return CE_OK;
+  }
+  Plan p;
+  hipblasStatus_t s;
+  const int32_t opa = g.opa, opb = g.opb;
+  const uint64_t ar = g.opa == HIPBLAS_OP_N ? g.m : g.k, ac = g.opa == HIPBLAS_OP_N ? g.k : g.m;
+  const uint64_t br = g.opb == HIPBLAS_OP_N ? g.k : g.n, bc = g.opb == HIPBLAS_OP_N ? g.n : g.k;
+  hipblasLtMatmulPreference_t pref = nullptr;
+  hipblasLtMatmulHeuristicResult_t res[8];
+  int nres = 0;
+  const uint64_t wsmax = kBlasWorkspace;
+  if ((s = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F)) ||
+      (s = hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opa, sizeof opa)) ||
+      (s = hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opb, sizeof opb)) ||
+      (s = hipblasLtMatrixLayoutCreate(&p.a, g.ab, ar, ac, g.lda)) ||
+      (s = hipblasLtMatrixLayoutCreate(&p.b, g.ab, br, bc, g.ldb)) ||
+      (s = hipblasLtMatrixLayoutCreate(&p.c, g.cd, g.m, g.n, g.ldd)) ||
+      (s = hipblasLtMatmulPreferenceCreate(&pref)) ||
+      (s = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsmax,
+                                                 sizeof wsmax)) ||
+      (s = hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.a, p.b, p.c, p.c, pref, 8, res, &nres))) {
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    return lfail(CE_EHIP, "GEMM plan %lld x %lld x %lld: %s", (long long)g.m, (long long)g.n, (long long)g.k,
+                 blas_status(s));
+  }
+  hipblasLtMatmulPreferenceDestroy(pref);
+  int pick = -1;
+  for (int i = 0; i < nres && pick < 0; ++i)
+    if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= kBlasWorkspace) pick = i;
+  if (pick < 0)
+    return lfail(CE_ELAYOUT, "no GEMM algorithm for %lld x %lld x %lld (leading dims %lld, %lld, %lld)",
+                 (long long)g.m, (long long)g.n, (long long)g.k, (long long)g.lda, (long long)g.ldb,
+                 (long long)g.ldd);
+  p.algo = res[pick].algo;
+  *out = &g_plans.emplace(key, p).first->second;
+  return CE_OK;
+}
+
+ce_status run_gemm(int dev, const Gemm& g, void* blas_ws, hipStream_t stream) {
+  Plan* p = nullptr;
+  ce_status st = get_plan(dev, g, &p);
+  if (st) return st;
+  hipblasLtHandle_t h;
+  {
+    std::lock_guard<std::mutex> lk(g_blas_mu);
+    h = g_handles[dev];
+  }
+  const float alpha = 1.f;
+  hipblasStatus_t s = hipblasLtMatmul(h, p->desc, &alpha, g.A, p->a, g.B, p->b, &g.beta, g.D, p->c, g.D, p->c,
+                                      &p->algo, blas_ws, kBlasWorkspace, stream);
+  if (s != HIPBLAS_STATUS_SUCCESS)
+    return lfail(CE_EHIP, "GEMM %lld x %lld x %lld: %s", (long long)g.m, (long long)g.n, (long long)g.k,
+                 blas_status(s));
+  return CE_OK;
+}
+
+int elem_bytes(int32_t dtype) { return dtype == CE_BF16 ? 2 : 4; }
+
+ce_status check_linear(const ce_linear* lin, const ce_params* p) {
+  if (!lin) return lfail(CE_EINVAL, "linear descriptor is NULL");
+  if (!p) return lfail(CE_EINVAL, "params is NULL");
+  if (lin->dtype != CE_F32 && lin->dtype != CE_BF16) return lfail(CE_EDTYPE, "unsupported dtype %d", lin->dtype);
+  if (lin->reserved != 0) return lfail(CE_EINVAL, "linear.reserved must be 0");
+  if (lin->N < 0 || lin->D < 1 || lin->V < 1)
+    return lfail(CE_EINVAL, "need N >= 0, D >= 1, V >= 1 (got %lld, %lld, %lld)", (long long)lin->N,
+                 (long long)lin->D, (long long)lin->V);
+  if (lin->N > 0x7fffffffLL || lin->V > 0x7fffffffLL || lin->D > 0x7fffffffLL)
+    return lfail(CE_EINVAL, "sizes above 2^31-1");
+  if (lin->h_ld < lin->D || lin->w_ld < lin->D) return lfail(CE_ELAYOUT, "row strides must be >= D");
+  const uintptr_t eb = (uintptr_t)elem_bytes(lin->dtype);
+  if ((lin->N > 0 && !lin->h) || !lin->w) return lfail(CE_EINVAL, "h or w is NULL");
+  if ((uintptr_t)lin->h % eb || (uintptr_t)lin->w % eb) return lfail(CE_ELAYOUT, "h or w not aligned to its dtype");
+  if (p->split_chunks != 0) return lfail(CE_EINVAL, "split_chunks must be 0 for the chunked linear call");
+  return CE_OK;
+}
+
+int64_t auto_chunk(const ce_linear* lin, int64_t chunk_rows) {
+  if (lin->N == 0) return 1;
+  int64_t c = chunk_rows;
+  if (c <= 0) {
+    c = (int64_t)(kChunkTarget / ((size_t)lin->V * (size_t)elem_bytes(lin->dtype)));
+    if (c >= 256) c -= c % 256;
+    if (c < 1) c = 1;
+  }
+  return c < lin->N ? c : lin->N;
+}
+
+// header and fused-call regions | chunk logits | per-chunk loss sums | scale | GEMM scratch
+struct LinLayout {
+  size_t fused = 0;   // bytes the per-chunk fused call needs (its regions start at 0)
+  size_t logits = 0, parts = 0, scale = 0, blas = 0, total = 0;
+  int64_t chunk = 0, nchunks = 0;
+};
+
+ce_status lin_layout(const ce_linear* lin, const ce_params* p, int64_t chunk_rows, LinLayout* out) {
+  LinLayout w;
+  w.chunk = auto_chunk(lin, chunk_rows);
+  w.nchunks = lin->N == 0 ? 0 : (lin->N + w.chunk - 1) / w.chunk;
+  w.fused = vce::fused_workspace_bytes(w.chunk, lin->dtype, lin->V, p->reduce_loss != CE_REDUCE_NONE);
+  size_t off = align256(w.fused);
+  w.logits = off;
+  off = align256(off + (size_t)w.chunk * (size_t)lin->V * (size_t)elem_bytes(lin->dtype));
+  w.parts = off;
+  off = align256(off + (size_t)(w.nchunks > 0 ? w.nchunks : 1) * 4u);
+  w.scale = off;  // float s, int32 n
+  off = align256(off + 8u);
+  w.blas = off;
+  off = align256(off + kBlasWorkspace);
+  w.total = off;
+  *out = w;
+  return CE_OK;
+}
+
+// The fused call's checks for a chunk of `rows` rows (shape and parameters
+// only: the descriptor's address is a placeholder with the buffer's alignment).
+ce_status chunk_plan_ok(const ce_linear* lin, const ce_params* p, int64_t rows) {
+  ce_logits x{};
+  x.data = reinterpret_cast<void*>((uintptr_t)256);
+  x.dtype = lin->dtype;
+  x.d0 = 1;
+  x.d1 = rows;
+  x.s1 = lin->V;
+  x.v_local = lin->V;
+  x.vocab_total = lin->V;
+  return vce::fused_plan(&x, p, nullptr, nullptr, nullptr);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ce_linear_workspace_bytes(const ce_linear* lin, const ce_params* p, int64_t chunk_rows,
+                                 int64_t* chunk_rows_out) {
+  if (check_linear(lin, p)) return 0;
+  LinLayout w;
+  if (lin_layout(lin, p, chunk_rows, &w) || chunk_plan_ok(lin, p, w.chunk)) return 0;
+  if (chunk_rows_out) *chunk_rows_out = w.chunk;
+  return w.total;
+}
+
+ce_status ce_linear_cross_entropy(const ce_linear* lin, const int64_t* targets, int64_t t_stride,
+                                  const ce_params* p, const float* grad_out, float* loss, int32_t* n_valid,
+                                  void* dh, int64_t dh_ld, float* dw, int64_t dw_ld, int32_t accumulate_dw,
+                                  int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ce_status st;
+  if ((st = check_linear(lin, p))) return st;
+  const int64_t N = lin->N, D = lin->D, V = lin->V;
+  if (N > 0 && !targets) return lfail(CE_EINVAL, "targets is NULL");
+  if ((uintptr_t)targets % 8u || t_stride < 0) return lfail(CE_ELAYOUT, "targets misaligned or negative stride");
+  if (!loss) return lfail(CE_EINVAL, "loss is NULL");
+  if (dh && (dh_ld < D || (uintptr_t)dh % (uintptr_t)elem_bytes(lin->dtype)))
+    return lfail(CE_ELAYOUT, "dh row stride must be >= D and dh aligned to its dtype");
+  if (dw && (dw_ld < D || (uintptr_t)dw % 4u)) return lfail(CE_ELAYOUT, "dw row stride must be >= D, dw 4-byte aligned");
+  if (accumulate_dw != 0 && accumulate_dw != 1) return lfail(CE_EINVAL, "accumulate_dw must be 0 or 1");
+  if (p->smoothing == CE_SMOOTH_OTHERS && p->label_smoothing > 0.f && V < 2)
+    return lfail(CE_EINVAL, "smoothing over the other classes needs V >= 2");
+  LinLayout w;
+  if ((st = lin_layout(lin, p, chunk_rows, &w))) return st;
+  // the per-chunk fused call's own checks (parameters, chunking of V), before anything is enqueued
+  if ((st = chunk_plan_ok(lin, p, w.chunk))) return st;
+  if (!ws || ws_bytes < w.total)
+    return lfail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
+  if ((uintptr_t)ws % 256u) return lfail(CE_EWORKSPACE, "workspace must be 256-byte aligned");
+  ce_params q = *p;
+  q.reduce_loss = p->reduce_loss == CE_REDUCE_NONE ? CE_REDUCE_NONE : CE_REDUCE_SUM;
+  int dev = 0;
+  hipError_t e;
+  if ((e = hipGetDevice(&dev))) return lfail(CE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+
+  char* wsb = static_cast<char*>(ws);
+  char* logits = wsb + w.logits;
+  float* parts = reinterpret_cast<float*>(wsb + w.parts);
+  float* scale = reinterpret_cast<float*>(wsb + w.scale);
+  int32_t* n_out = n_valid ? n_valid : reinterpret_cast<int32_t*>(wsb + w.scale + 4);
+  const int red = p->reduce_loss;
+
+  // the count over all rows, and for the mean the scale g / n every chunk uses
+  if ((e = vce::launch_linear_prep(targets, t_stride, N, p->ignore_idx, red, grad_out, n_out, scale, stream)))
+    return lfail(CE_EHIP, "count launch: %s", hipGetErrorString(e));
+  if (dw && !accumulate_dw && N == 0 && (e = vce::launch_fill_f32(dw, V, D, dw_ld, stream)))
+    return lfail(CE_EHIP, "fill launch: %s", hipGetErrorString(e));
+
+  const hipDataType ab = lin->dtype == CE_BF16 ? HIP_R_16BF : HIP_R_32F;
+  const size_t eb = (size_t)elem_bytes(lin->dtype);
+  for (int64_t c = 0; c < w.nchunks; ++c) {
+    const int64_t r0 = c * w.chunk;
+    const int64_t n = N - r0 < w.chunk ? N - r0 : w.chunk;
+    const char* hc = static_cast<const char*>(lin->h) + (size_t)r0 * (size_t)lin->h_ld * eb;
+    // logits_c = h_c W^T
+    Gemm g1{ab, ab, V, n, D, HIPBLAS_OP_T, HIPBLAS_OP_N, lin->w, lin->w_ld, hc, lin->h_ld, logits, V, 0.f};
+    if ((st = run_gemm(dev, g1, wsb + w.blas, stream))) return st;
+    // loss and gradient in place
+    ce_logits x{};
+    x.data = logits;
+    x.dtype = lin->dtype;
+    x.d0 = 1;
+    x.d1 = n;
+    x.s0 = 0;
+    x.s1 = V;
+    x.v_local = V;
+    x.vocab_start = 0;
+    x.vocab_total = V;
+    ce_targets t{targets + r0 * t_stride, 0, t_stride};
+    const float* gc = red == CE_REDUCE_NONE ? (grad_out ? grad_out + r0 : nullptr)
+                                            : (red == CE_REDUCE_MEAN ? scale : grad_out);
+    float* lc = red == CE_REDUCE_NONE ? loss + r0 : parts + c;
+    if ((st = ce_fwd_bwd_fused(&x, &t, &q, gc, lc, nullptr, ws, w.fused, stream)))
+      return lfail(st, "chunk %lld: %s", (long long)c, ce_last_error());
+    // dh_c = G_c W
+    if (dh) {
+      char* dhc = static_cast<char*>(dh) + (size_t)r0 * (size_t)dh_ld * eb;
+      Gemm g2{ab, ab, D, n, V, HIPBLAS_OP_N, HIPBLAS_OP_N, lin->w, lin->w_ld, logits, V, dhc, dh_ld, 0.f};
+      if ((st = run_gemm(dev, g2, wsb + w.blas, stream))) return st;
+    }
+    // dW (+)= G_c^T h_c
+    if (dw) {
+      Gemm g3{ab, HIP_R_32F, D, V, n, HIPBLAS_OP_N, HIPBLAS_OP_T, hc, lin->h_ld, logits, V, dw, dw_ld,
+              (c > 0 || accumulate_dw) ? 1.f : 0.f};
+      if ((st = run_gemm(dev, g3, wsb + w.blas, stream))) return st;
+    }
+  }
+  if (red != CE_REDUCE_NONE &&
+      (e = vce::launch_linear_finish(parts, w.nchunks, red, n_out, loss, stream)))
+    return lfail(CE_EHIP, "finish launch: %s", hipGetErrorString(e));
+  return CE_OK;
+}
+
+}  // extern "C"
