@@ -355,6 +355,24 @@ def main():
     print(line, flush=True)
 
 
+def cpu_baseline_linear(h, W, t, alpha, reduction, smoothing, n_rows):
+    """The FP64 oracle (as it is) for the head + loss of the first `n_rows`
+    rows: logits, loss, dh and those rows' share of dW (6 n D V flops)."""
+    import oracle
+
+    orc = oracle.default()
+    hs = h[:n_rows].cpu()
+    ts = t[:n_rows].cpu()
+    Wc = W.cpu()
+    t0 = time.perf_counter()
+    orc.linear_ce(hs, Wc, ts, alpha, reduce_loss=reduction, smoothing=smoothing,
+                  n_valid=int((t != -100).sum().item()))
+    dt = time.perf_counter() - t0
+    flops = 6.0 * n_rows * W.shape[1] * W.shape[0]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.max_threads(), "kind": "oracle",
+            "sample": f"first {n_rows} of {h.shape[0]} rows (logits, loss, dh, their dW share; FP64), {dt:.2f} s wall"}
+
+
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak, AMD public specification
 PEAK_F32_TFLOPS = 157.3    # MI355X FP32 matrix peak
 
@@ -424,6 +442,8 @@ def bench_linear(args, torch, vce, workloads, dev):
         "memory": {"workspace_bytes": ws_bytes, "full_logits_bytes": N * V * 2},
         "loss": float(loss[0].item()) if red != "none" else None,
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_linear(h, W, t, w5.alpha, red, args.smoothing, n_rows=4)
     if args.torch_ref:
         del ws
         torch.cuda.empty_cache()

@@ -57,13 +57,15 @@ def check_dh(got, ref, G, w, dtype, what):
     assert not bad.any(), f"{what}: dh off at {bad.sum()} elements, max err {err.max():.3e}, max tol {tol.max():.3e}"
 
 
-def check_dw(got, ref, G, h, dtype, what, rows_sampled=None):
+def check_dw(got, ref, G, h, dtype, what, out_rho=2.0 ** -23):
+    """``out_rho``: the output's own rounding (FP32 accumulator; 2^-8 once cast to BF16)."""
     r_g, a_g, _ = _bars(dtype)
     N = h.shape[0]
     H = np.abs(h.double().numpy())
     A = np.abs(G).T @ H
     B = np.broadcast_to(H.sum(axis=0), ref.shape)
-    tol = (r_g + N * 2.0 ** -24) * A + a_g * B + 2.0 ** -23 * np.abs(ref)
+    tol = (r_g + N * 2.0 ** -24) * A + a_g * B
+    tol = tol + out_rho * (np.abs(ref) + tol)
     err = np.abs(got - ref)
     bad = ~(err <= tol)
     assert not bad.any(), f"{what}: dW off at {bad.sum()} elements, max err {err.max():.3e}"
@@ -213,3 +215,40 @@ def test_linear_full_size_sampled():
     col = dw.sum(axis=0)
     bound = ((2.0 ** -8 + gamma_n) * 2 * s * (1 + 2.0 ** -8) + V * 1e-7) * habs
     assert np.all(np.abs(col) <= bound), f"dW column sums: max {np.abs(col).max():.3e}"
+
+
+@pytest.mark.parametrize("reduce", ["mean", "sum"])
+def test_linear_autograd(reduce):
+    """linear_cross_entropy: the loss and, after (0.5 * loss).backward(), h.grad
+    and W.grad (FP32 dW cast to BF16 by autograd) against the oracle with g = 0.5."""
+    h, w, t = grid_inputs(48, 64, 3001, torch.bfloat16, seed=31)
+    say(f"[linear autograd] {reduce}")
+    hd = h.cuda().requires_grad_(True)
+    wd = w.cuda().requires_grad_(True)
+    loss = vce.linear_cross_entropy(hd, wd, t.cuda(), 0.1, reduce, chunk_rows=16)
+    (0.5 * loss).backward()
+    torch.cuda.synchronize()
+    o = orc()
+    ref_rows, ref_dh, ref_dw, G = o.linear_ce(h, w, t, 0.1, reduce_loss=reduce, g=0.5, want_g=True)
+    assert_loss([loss.item()], [o.reduce(ref_rows, reduce, int((t != -100).sum()))], f"autograd {reduce}")
+    assert hd.grad.dtype == torch.bfloat16 and wd.grad.dtype == torch.bfloat16
+    check_dh(hd.grad.double().cpu().numpy(), ref_dh, G, w, torch.bfloat16, "autograd h.grad")
+    check_dw(wd.grad.double().cpu().numpy(), ref_dw, G, h, torch.bfloat16, "autograd W.grad", out_rho=2.0 ** -8)
+
+
+def test_linear_autograd_trains_a_head():
+    """A few SGD steps on a head through linear_cross_entropy lower the loss
+    (hidden states fixed, the weight learns; FP32)."""
+    g = torch.Generator().manual_seed(37)
+    h = torch.randn((256, 32), generator=g).cuda()
+    t = torch.randint(0, 500, (256,), generator=g).cuda()
+    w = (torch.randn((500, 32), generator=g) * 0.05).cuda().requires_grad_(True)
+    losses = []
+    for _ in range(20):
+        loss = vce.linear_cross_entropy(h, w, t, 0.0, "mean", chunk_rows=64)
+        w.grad = None
+        loss.backward()
+        with torch.no_grad():
+            w -= 2.0 * w.grad
+        losses.append(loss.item())
+    assert losses[-1] < 0.8 * losses[0], losses

@@ -34,7 +34,7 @@ __all__ = [
     "ce_shard_combine",
     "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_init", "ce_workspace_check",
     "ce_linear_workspace_bytes", "ce_linear_cross_entropy",
-    "parallel_cross_entropy",
+    "parallel_cross_entropy", "linear_cross_entropy",
     "Profiler", "CeError", "CeArgumentError", "lib",
 ]
 
@@ -372,6 +372,51 @@ def parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False, 
         raise NotImplementedError("vocabulary-parallel process groups need more than one GPU; use "
                                   "ce_shard_partial_stats / ce_shard_combine / ce_backward_inplace per shard")
     return ParallelCrossEntropy.apply(inp, target, label_smoothing, reduce_loss, ignore_idx, smoothing)
+
+
+class LinearCrossEntropy(torch.autograd.Function):
+    """Autograd form of the chunked head + loss (ce_linear_cross_entropy) for
+    a reduced loss (mean or sum).  The forward computes the loss and both
+    gradients for an upstream gradient of 1 (dh in h's dtype, dW in FP32; no
+    logits are kept); the backward scales them by the upstream gradient in
+    place (ce_scale_grad_inplace: nothing is read or written when it is 1,
+    and no host synchronisation finds out).  dW is returned in FP32; autograd
+    casts it to the weight's dtype."""
+
+    @staticmethod
+    def forward(ctx, h, weight, target, label_smoothing=0.0, reduce_loss="mean", ignore_idx=-100,
+                smoothing="all", chunk_rows=0):
+        if reduction_code(reduce_loss) == _abi.CE_REDUCE_NONE:
+            raise CeArgumentError(_abi.CE_EINVAL, "linear_cross_entropy needs a reduced loss (mean or sum); for "
+                                                  "per-row losses call ce_linear_cross_entropy with grad_out")
+        loss, dh, dw, _ = ce_linear_cross_entropy(h.detach(), weight.detach(), target, label_smoothing,
+                                                  reduce_loss, ignore_idx, want_dh=ctx.needs_input_grad[0],
+                                                  want_dw=ctx.needs_input_grad[1], chunk_rows=chunk_rows,
+                                                  smoothing=smoothing)
+        ctx.save_for_backward(dh if dh is not None else torch.empty(0),
+                              dw if dw is not None else torch.empty(0))
+        ctx.has = (dh is not None, dw is not None)
+        return loss[0]
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        dh, dw = ctx.saved_tensors
+        g = grad_loss.reshape(1)
+        if ctx.has[0]:
+            ce_scale_grad_inplace(dh.view(1, *dh.shape), g, per_row=False)
+        if ctx.has[1]:
+            ce_scale_grad_inplace(dw.view(1, *dw.shape), g, per_row=False)
+        return (dh if ctx.has[0] else None, dw if ctx.has[1] else None, None, None, None, None, None, None)
+
+
+def linear_cross_entropy(h, weight, target, label_smoothing=0.0, reduce_loss="mean", ignore_idx=-100, *,
+                         smoothing="all", chunk_rows=0):
+    """Cross-entropy of the head ``h @ weight.T`` without whole logits: the
+    rows go through ce_linear_cross_entropy in chunks.  ``h`` [N, D],
+    ``weight`` [V, D] (torch Linear layout), ``target`` [N] int64.  Returns
+    the FP32 mean (or sum) and reaches autograd through LinearCrossEntropy."""
+    return LinearCrossEntropy.apply(h, weight, target, label_smoothing, reduce_loss, ignore_idx, smoothing,
+                                    chunk_rows)
 
 
 class Profiler:
