@@ -252,3 +252,51 @@ def test_linear_autograd_trains_a_head():
             w -= 2.0 * w.grad
         losses.append(loss.item())
     assert losses[-1] < 0.8 * losses[0], losses
+
+
+def test_linear_graph_replays():
+    """A captured ce_linear_cross_entropy (GEMMs, one fused call per chunk,
+    count and finish kernels) replays bit-identically to the eager call: each
+    chunk's fused call takes its tag from the workspace's epoch, which every
+    call advances, so replays never see an earlier call's words."""
+    h, w, t = grid_inputs(64, 64, 3001, torch.bfloat16, seed=41)
+    hd, wd, td = h.cuda(), w.cuda(), t.cuda()
+    nb, _ = vce.ce_linear_workspace_bytes(hd, wd, "mean", 16, 0.1)
+    ws = vce.ce_workspace_init(torch.empty(nb, dtype=torch.uint8, device="cuda"))
+    loss = torch.empty(1, device="cuda")
+    dh = torch.empty_like(hd)
+    dw = torch.empty((3001, 64), device="cuda")
+    n = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def call():
+        vce.ce_linear_cross_entropy(hd, wd, td, 0.1, "mean", loss=loss, n_valid=n, dh=dh, dw=dw, ws=ws,
+                                    chunk_rows=16)
+
+    say("[linear graph] eager reference")
+    call()
+    torch.cuda.synchronize()
+    ref = (loss.clone(), dh.clone(), dw.clone())
+    say("[linear graph] capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"[linear graph] replay {rep}")
+        loss.fill_(float("nan"))
+        dh.zero_()
+        dw.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loss.view(torch.int32), ref[0].view(torch.int32)), f"replay {rep}: loss"
+        assert torch.equal(dh.view(torch.int16), ref[1].view(torch.int16)), f"replay {rep}: dh"
+        assert torch.equal(dw.view(torch.int32), ref[2].view(torch.int32)), f"replay {rep}: dW"
+        if rep == 0:
+            call()  # an eager call on the same workspace between replays
+            torch.cuda.synchronize()
+    vce.ce_workspace_check(ws)
