@@ -67,10 +67,11 @@ class _Targets(ctypes.Structure):
 
 def build(force: bool = False) -> str:
     """Compile ce_oracle.c with gcc (-O2, no fast-math, OpenMP over rows)."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "ce_oracle.h")))
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
         tmp = _LIB_PATH + ".tmp"
         subprocess.run(
-            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", "-I", _HERE,
              "-o", tmp, _SRC, "-lm"],
             check=True,
         )

@@ -82,34 +82,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define OR_F32 0
-#define OR_BF16 1
-
-#define OR_EBADTARGET (-1)
-#define OR_EINVAL (-2)
-
-#define OR_SMOOTH_ALL 0    /* a / V on every class (torch's F.cross_entropy) */
-#define OR_SMOOTH_OTHERS 1 /* a / (V - 1) on every class but the target (ops-nn kernel) */
-
-#define OR_REDUCE_NONE 0
-#define OR_REDUCE_MEAN 1
-#define OR_REDUCE_SUM 2
-
-typedef struct or_logits {
-  const void* data;
-  int32_t dtype;       /* OR_F32 or OR_BF16 */
-  int32_t pad_;
-  int64_t d0, d1;      /* logical leading dims; rows = d0 * d1 */
-  int64_t s0, s1;      /* element strides of the two leading dims */
-  int64_t v_local;     /* columns present in this buffer */
-  int64_t vocab_start; /* global index of local column 0 */
-  int64_t vocab_total; /* global vocabulary size V */
-} or_logits;
-
-typedef struct or_targets {
-  const int64_t* data;
-  int64_t s0, s1;
-} or_targets;
+#include "ce_oracle.h"
 
 /* Exact widening of one stored logit to double. */
 static double or_elem(const or_logits* x, int64_t off) {

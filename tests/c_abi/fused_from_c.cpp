@@ -1,0 +1,165 @@
+// A consumer of the C ABI with no Python and no torch: HIP device memory from
+// hipMalloc, libce.so's ce_workspace_init and ce_fwd_bwd_fused on the null
+// stream, checked against the FP64 oracle's C library (test infrastructure,
+// linked only here).  Written in plain C style; compiled with hipcc.
+//
+// Inputs: 2 x 37 rows of 5003 BF16 logits (a misaligned row length), label
+// smoothing 0.1, mean over the non-ignored rows, every ninth target ignored;
+// values from a fixed linear congruential generator.  Bar: n exact, loss
+// within 1e-4 max(1, |ref|), gradient within 2^-8 |ref| + 1e-7, ignored rows
+// +0.0.  Prints "c abi ok" and exits 0, or prints the first mismatch and
+// exits 1.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "ce.h"
+#include "ce_oracle.h"
+
+#define HIP_OK(x)                                                  \
+  do {                                                             \
+    hipError_t e_ = (x);                                           \
+    if (e_ != hipSuccess) {                                        \
+      printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+      return 1;                                                    \
+    }                                                              \
+  } while (0)
+
+static uint64_t lcg_state = 0x9e3779b97f4a7c15ull;
+static double lcg_uniform(void) {  // [0, 1)
+  lcg_state = lcg_state * 6364136223846793005ull + 1442695040888963407ull;
+  return (double)(lcg_state >> 11) * (1.0 / 9007199254740992.0);
+}
+
+static uint16_t bf16_of(float f) {  // nearest even
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  u = u + 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+static float float_of_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+int main(void) {
+  const int64_t d0 = 2, d1 = 37, V = 5003, N = d0 * d1;
+  const float alpha = 0.1f;
+  uint16_t* x = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(N * V));
+  uint16_t* grad = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(N * V));
+  int64_t* t = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+  double* ref_loss = (double*)malloc(sizeof(double) * (size_t)N);
+  double* ref_grad = (double*)malloc(sizeof(double) * (size_t)(N * V));
+  int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+  for (int64_t i = 0; i < N * V; ++i) {
+    // sum of four uniforms: mean 0, standard deviation about 2
+    double u = lcg_uniform() + lcg_uniform() + lcg_uniform() + lcg_uniform() - 2.0;
+    x[i] = bf16_of((float)(u * 3.46));
+  }
+  for (int64_t r = 0; r < N; ++r) {
+    t[r] = r % 9 == 4 ? -100 : (int64_t)(lcg_uniform() * (double)V);
+    rows[r] = r;
+  }
+
+  void *dx, *dt, *dloss, *dn, *dws;
+  HIP_OK(hipMalloc(&dx, sizeof(uint16_t) * (size_t)(N * V)));
+  HIP_OK(hipMalloc(&dt, sizeof(int64_t) * (size_t)N));
+  HIP_OK(hipMalloc(&dloss, sizeof(float)));
+  HIP_OK(hipMalloc(&dn, sizeof(int32_t)));
+  HIP_OK(hipMemcpy(dx, x, sizeof(uint16_t) * (size_t)(N * V), hipMemcpyHostToDevice));
+  HIP_OK(hipMemcpy(dt, t, sizeof(int64_t) * (size_t)N, hipMemcpyHostToDevice));
+
+  ce_logits xl;
+  memset(&xl, 0, sizeof xl);
+  xl.data = dx;
+  xl.dtype = CE_BF16;
+  xl.d0 = d0;
+  xl.d1 = d1;
+  xl.s0 = d1 * V;
+  xl.s1 = V;
+  xl.v_local = V;
+  xl.vocab_total = V;
+  ce_targets tl = {(const int64_t*)dt, d1, 1};
+  ce_params p;
+  memset(&p, 0, sizeof p);
+  p.label_smoothing = alpha;
+  p.reduce_loss = CE_REDUCE_MEAN;
+  p.ignore_idx = -100;
+  p.smoothing = CE_SMOOTH_ALL;
+  const size_t ws_bytes = ce_workspace_bytes(&xl, &p);
+  if (ws_bytes == 0) {
+    printf("ce_workspace_bytes: %s\n", ce_last_error());
+    return 1;
+  }
+  HIP_OK(hipMalloc(&dws, ws_bytes));
+  ce_status st = ce_workspace_init(dws, ws_bytes, NULL);
+  if (st == CE_OK) st = ce_fwd_bwd_fused(&xl, &tl, &p, NULL, (float*)dloss, (int32_t*)dn, dws, ws_bytes, NULL);
+  if (st != CE_OK) {
+    printf("%s: %s\n", ce_status_string(st), ce_last_error());
+    return 1;
+  }
+  HIP_OK(hipDeviceSynchronize());
+  if ((st = ce_workspace_check(dws, NULL)) != CE_OK) {
+    printf("%s: %s\n", ce_status_string(st), ce_last_error());
+    return 1;
+  }
+  float loss;
+  int32_t n;
+  HIP_OK(hipMemcpy(&loss, dloss, sizeof loss, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(&n, dn, sizeof n, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(grad, dx, sizeof(uint16_t) * (size_t)(N * V), hipMemcpyDeviceToHost));
+
+  or_logits ol = {x, OR_BF16, 0, d0, d1, d1 * V, V, V, 0, V};
+  or_targets ot = {t, d1, 1};
+  const int64_t n_ref = or_count_valid(&ot, d0, d1, -100);
+  if (or_loss_rows(&ol, &ot, alpha, OR_SMOOTH_ALL, -100, rows, N, ref_loss, NULL) ||
+      or_grad_rows(&ol, &ot, alpha, OR_SMOOTH_ALL, -100, OR_REDUCE_MEAN, NULL, 1.0, n_ref, rows, N, ref_grad)) {
+    printf("oracle rejected the inputs\n");
+    return 1;
+  }
+  const double mean_ref = or_mean_loss(ref_loss, N, n_ref);
+  if ((int64_t)n != n_ref) {
+    printf("n %d, oracle %lld\n", n, (long long)n_ref);
+    return 1;
+  }
+  if (!(fabs((double)loss - mean_ref) <= 1e-4 * fmax(1.0, fabs(mean_ref)))) {
+    printf("mean loss %.9g, oracle %.9g\n", (double)loss, mean_ref);
+    return 1;
+  }
+  double max_err = 0.0;
+  for (int64_t i = 0; i < N * V; ++i) {
+    const int64_t r = i / V;
+    if (t[r] == -100 && grad[i] != 0) {
+      printf("ignored row %lld element %lld is not +0.0\n", (long long)r, (long long)(i % V));
+      return 1;
+    }
+    const double g = (double)float_of_bf16(grad[i]), err = fabs(g - ref_grad[i]);
+    if (!(err <= ldexp(1.0, -8) * fabs(ref_grad[i]) + 1e-7)) {
+      printf("gradient row %lld column %lld: %.9g, oracle %.9g\n", (long long)r, (long long)(i % V), g,
+             ref_grad[i]);
+      return 1;
+    }
+    if (err > max_err) max_err = err;
+  }
+  printf("c abi ok: n %d, mean loss %.6f (oracle %.6f), max gradient error %.2e\n", n, (double)loss, mean_ref,
+         max_err);
+  hipFree(dx);
+  hipFree(dt);
+  hipFree(dloss);
+  hipFree(dn);
+  hipFree(dws);
+  free(x);
+  free(grad);
+  free(t);
+  free(ref_loss);
+  free(ref_grad);
+  free(rows);
+  return 0;
+}

@@ -176,7 +176,9 @@ def test_linear_no_rows():
     dw = torch.full((100, 32), 5.0, device="cuda")
     loss, dh, dwo, n = vce.ce_linear_cross_entropy(h, w, t, 0.1, "mean", dw=dw)
     ls, _, _, _ = vce.ce_linear_cross_entropy(h, w, t, 0.1, "sum", want_dw=False)
+    lr, _, _, _ = vce.ce_linear_cross_entropy(h, w, t, 0.1, "none", want_dw=False)  # an empty loss[0]
     torch.cuda.synchronize()
+    assert lr.numel() == 0
     assert int(n.item()) == 0 and math.isnan(loss.item()) and ls.item() == 0.0
     assert torch.count_nonzero(dwo).item() == 0, "no rows: dW is zero"
 

@@ -76,7 +76,8 @@ def test_some_pin_catches(tmp_path, name, old, new, count):
     c_path = tmp_path / "mutant.c"
     so_path = tmp_path / "libmutant.so"
     c_path.write_text(mutated)
-    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-w", "-o", str(so_path),
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-w", "-I", os.path.dirname(SRC),
+                    "-o", str(so_path),
                     str(c_path), "-lm"], check=True)
     orc = oracle.Oracle(oracle.load(str(so_path)))
     caught = []

@@ -46,6 +46,7 @@ constexpr size_t kChunkTarget = 512ull << 20;
 // ---- GEMM plans: one per (device, types, shape, ops, leading dims, beta != 0),
 // built on first use (heuristic query) and kept until the process ends.
 struct Plan {
+  hipblasLtHandle_t handle = nullptr;
   hipblasLtMatmulDesc_t desc = nullptr;
   hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
   hipblasLtMatmulAlgo_t algo;
@@ -133,6 +134,7 @@ ce_status get_plan(int dev, const Gemm& g, Plan** out) {
                  (long long)g.m, (long long)g.n, (long long)g.k, (long long)g.lda, (long long)g.ldb,
                  (long long)g.ldd);
   p.algo = res[pick].algo;
+  p.handle = h;
   *out = &g_plans.emplace(key, p).first->second;
   return CE_OK;
 }
@@ -141,13 +143,8 @@ ce_status run_gemm(int dev, const Gemm& g, void* blas_ws, hipStream_t stream) {
   Plan* p = nullptr;
   ce_status st = get_plan(dev, g, &p);
   if (st) return st;
-  hipblasLtHandle_t h;
-  {
-    std::lock_guard<std::mutex> lk(g_blas_mu);
-    h = g_handles[dev];
-  }
   const float alpha = 1.f;
-  hipblasStatus_t s = hipblasLtMatmul(h, p->desc, &alpha, g.A, p->a, g.B, p->b, &g.beta, g.D, p->c, g.D, p->c,
+  hipblasStatus_t s = hipblasLtMatmul(p->handle, p->desc, &alpha, g.A, p->a, g.B, p->b, &g.beta, g.D, p->c, g.D, p->c,
                                       &p->algo, blas_ws, kBlasWorkspace, stream);
   if (s != HIPBLAS_STATUS_SUCCESS)
     return lfail(CE_EHIP, "GEMM %lld x %lld x %lld: %s", (long long)g.m, (long long)g.n, (long long)g.k,
@@ -248,7 +245,7 @@ ce_status ce_linear_cross_entropy(const ce_linear* lin, const int64_t* targets, 
   const int64_t N = lin->N, D = lin->D, V = lin->V;
   if (N > 0 && !targets) return lfail(CE_EINVAL, "targets is NULL");
   if ((uintptr_t)targets % 8u || t_stride < 0) return lfail(CE_ELAYOUT, "targets misaligned or negative stride");
-  if (!loss) return lfail(CE_EINVAL, "loss is NULL");
+  if (!loss && (N > 0 || p->reduce_loss != CE_REDUCE_NONE)) return lfail(CE_EINVAL, "loss is NULL");
   if (dh && (dh_ld < D || (uintptr_t)dh % (uintptr_t)elem_bytes(lin->dtype)))
     return lfail(CE_ELAYOUT, "dh row stride must be >= D and dh aligned to its dtype");
   if (dw && (dw_ld < D || (uintptr_t)dw % 4u)) return lfail(CE_ELAYOUT, "dw row stride must be >= D, dw 4-byte aligned");
