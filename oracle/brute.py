@@ -49,7 +49,8 @@ def loss_rows(rows, targets, alpha=0.0, ignore_idx=-100, digits=50, smoothing="a
             probs = _softmax(row, ctx)                      # step 1: softmax
             logp = [ctx.ln(p) for p in probs]               # step 2: log
             q = _target_distribution(V, t, a, smoothing)
-            out.append(-sum((qj * lj for qj, lj in zip(q, logp)), Decimal(0)))  # step 3: NLL
+            # step 3: NLL; a zero weight contributes nothing (0 log 0 = 0)
+            out.append(-sum((qj * lj for qj, lj in zip(q, logp) if qj != 0), Decimal(0)))
     return out
 
 

@@ -29,6 +29,10 @@
  *   negative log-probabilities).  With V = 1 there is no other class: a > 0
  *   is rejected, a = 0 is plain NLL.
  *
+ *   A term whose weight q_ij is 0 contributes nothing to the loss (0 log 0 =
+ *   0), so a logit of -inf (a masked class) leaves the loss finite unless the
+ *   smoothing gives it weight, as in torch's F.cross_entropy.
+ *
  *   Rows whose target equals ignore_idx have loss 0 and gradient 0
  *   (ops-nn page, both kernels; default ignore_idx -100 per issue #29 section 1
  *   and the hyper-parallel issue #269 section 3.1).
@@ -180,7 +184,7 @@ int or_loss_rows(const or_logits* x, const or_targets* t, double alpha, int32_t 
     double loss = 0.0;
     if (smooth == OR_SMOOTH_OTHERS) {
       /* ops-nn: (1 - a) * NLL + a * (mean over the other classes of -log softmax) */
-      loss = (1.0 - alpha) * (lse - or_elem(x, off + tgt));
+      if (alpha < 1.0) loss = (1.0 - alpha) * (lse - or_elem(x, off + tgt));
       if (alpha > 0.0) {
         double other = 0.0;
         for (int64_t j = 0; j < V; ++j)
@@ -190,7 +194,7 @@ int or_loss_rows(const or_logits* x, const or_targets* t, double alpha, int32_t 
     } else {
       for (int64_t j = 0; j < V; ++j) {
         double q = or_q(smooth, alpha, V, j == tgt);
-        loss -= q * (or_elem(x, off + j) - lse);
+        if (q != 0.0) loss -= q * (or_elem(x, off + j) - lse); /* 0 log 0 = 0: a masked (-inf) class with q = 0 adds nothing */
       }
     }
     loss_out[k] = loss;
@@ -322,12 +326,20 @@ int or_shard_combine(const double* stats, int32_t S, int64_t nrows, int64_t voca
       R += st[3];
     }
     double lse = M + log(D);
+    /* terms with a zero weight are left out (0 log 0 = 0), so masked (-inf) logits only matter where q > 0 */
     if (smooth == OR_SMOOTH_OTHERS) {
-      double loss = (1.0 - alpha) * (lse - xt);
-      if (alpha > 0.0) loss += alpha * ((double)(vocab_total - 1) * lse - (R - xt)) / (double)(vocab_total - 1);
+      double loss = alpha < 1.0 ? (1.0 - alpha) * (lse - xt) : 0.0;
+      /* R - x_t is undefined for a masked (-inf) target; the loss is then +inf through the NLL term (a < 1),
+         since the other classes' term is never negative */
+      const int masked_target = isinf(xt) && xt < 0.0 && alpha < 1.0;
+      if (alpha > 0.0 && !masked_target)
+        loss += alpha * ((double)(vocab_total - 1) * lse - (R - xt)) / (double)(vocab_total - 1);
       loss_out[k] = loss;
     } else {
-      loss_out[k] = lse - (1.0 - alpha) * xt - (alpha / (double)vocab_total) * R;
+      double loss = lse;
+      if (alpha < 1.0) loss -= (1.0 - alpha) * xt;
+      if (alpha > 0.0) loss -= (alpha / (double)vocab_total) * R;
+      loss_out[k] = loss;
     }
     if (lse_out) lse_out[k] = lse;
   }
@@ -438,7 +450,10 @@ int or_linear_ce(const void* h, const void* w, int32_t dtype, int64_t N, int64_t
     for (int64_t j = 0; j < V; ++j) ssum += exp(x[j] - m);
     const double lse = m + log(ssum);
     double loss = 0.0;
-    for (int64_t j = 0; j < V; ++j) loss -= or_q(smooth, alpha, V, j == tgt) * (x[j] - lse);
+    for (int64_t j = 0; j < V; ++j) {
+      const double q = or_q(smooth, alpha, V, j == tgt);
+      if (q != 0.0) loss -= q * (x[j] - lse);
+    }
     loss_out[r] = loss;
     const double s = or_scale(reduce, g_row, g_scalar, n_valid, r);
     for (int64_t j = 0; j < V; ++j) x[j] = s * (exp(x[j] - lse) - or_q(smooth, alpha, V, j == tgt));

@@ -319,6 +319,39 @@ def pin_count_and_rows(orc):
         assert np.array_equal(part, full[rows])
 
 
+def pin_masked_logits(orc):
+    """Logits of -inf (masked classes) against torch float64: the loss is finite
+    where the smoothing gives those classes no weight (0 log 0 = 0) and +inf
+    where it does, or where the target itself is masked; gradients are finite.
+    Loss and lse also through the shard form."""
+    for dtype in (torch.float32, torch.bfloat16):
+        g = torch.Generator().manual_seed(91)
+        x = (torch.randn((1, 6, 13), generator=g) * 2).to(dtype)
+        x[0, :, 3] = -float("inf")
+        x[0, 1, 7:11] = -float("inf")
+        t = torch.tensor([[0, 2, 5, -100, 3, 12]])  # row 4's target is masked
+        for smoothing in ("all", "others"):
+            for alpha in (0.0, 0.2):
+                a_t = _torch_smoothing(alpha, 13, smoothing)
+                xd = x.to(torch.float64).reshape(6, 13).clone().requires_grad_(True)
+                ref = F.cross_entropy(xd, t.reshape(6), ignore_index=-100, label_smoothing=a_t, reduction="none")
+                (gx,) = torch.autograd.grad(ref.masked_fill(~torch.isfinite(ref), 0.0).sum(), xd)
+                loss, _ = orc.loss_rows(x, t, alpha, smoothing=smoothing)
+                r = ref.detach().numpy()
+                what = f"masked {dtype} {smoothing} a={alpha}"
+                assert np.array_equal(np.isinf(loss), np.isinf(r)), (what, loss, r)
+                fin = np.isfinite(r)
+                _close(loss[fin], r[fin], 1e-12, 1e-14, what + " loss")
+                # the gradient of rows whose loss is finite (torch's own grad of an inf row is its finite limit too)
+                grad = orc.grad_rows(x, t, alpha, smoothing=smoothing, g=np.ones(6))
+                _close(grad[fin], gx.numpy()[fin], 1e-11, 1e-15, what + " grad")
+                assert np.all(np.isfinite(grad))
+                stats = orc.shard_stats(x, t, 0, 13)[None]
+                sl, _ = orc.shard_combine(stats, t, 13, alpha, smoothing=smoothing)
+                assert np.array_equal(np.isinf(sl), np.isinf(r)), (what, sl, r)
+                _close(sl[fin], r[fin], 1e-12, 1e-14, what + " shard loss")
+
+
 def _linear_case(seed, N, D, V, dtype, ignore=2):
     g = torch.Generator().manual_seed(seed)
     h = (torch.randn((N, D), generator=g)).to(dtype)
@@ -428,6 +461,7 @@ ALL_PINS = [
     pin_grad_rows_sum_to_zero,
     pin_sharded_equals_unsharded,
     pin_count_and_rows,
+    pin_masked_logits,
     pin_linear_identity_head,
     pin_linear_torch,
     pin_linear_finite_differences,

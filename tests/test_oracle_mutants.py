@@ -17,8 +17,10 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ce_oracle.c")
 # (name, text in ce_oracle.c, replacement, expected number of occurrences)
 MUTANTS = [
     ("loss_drops_smoothing_mass",
-     "double q = or_q(smooth, alpha, V, j == tgt);\n        loss -= q",
-     "double q = (j == tgt ? 1.0 - alpha : 0.0);\n        loss -= q", 1),
+     "double q = or_q(smooth, alpha, V, j == tgt);\n        if (q != 0.0) loss -= q",
+     "double q = (j == tgt ? 1.0 - alpha : 0.0);\n        if (q != 0.0) loss -= q", 1),
+    ("loss_zero_weights_not_skipped", "if (q != 0.0) loss -= q * (or_elem(x, off + j) - lse);",
+     "loss -= q * (or_elem(x, off + j) - lse);", 1),
     ("grad_sign_flipped", "gout[j] = s * (p - or_q(smooth, alpha, V, j == tgt));",
      "gout[j] = s * (or_q(smooth, alpha, V, j == tgt) - p);", 1),
     ("grad_target_off_by_one", "gout[j] = s * (p - or_q(smooth, alpha, V, j == tgt));",
