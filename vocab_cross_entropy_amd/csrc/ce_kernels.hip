@@ -356,6 +356,16 @@ __device__ __forceinline__ Row<DT> row_span(const RowLayout& L, int64_t r) {
   return g;
 }
 
+// lse - (q_t - q_o) x_t - q_o sum_j x_j, leaving out a term whose weight is 0
+// (0 log 0 = 0): a masked class (a logit of -inf) with no smoothing weight
+// keeps the loss finite, as in torch's F.cross_entropy.
+__device__ __forceinline__ float row_loss_of(float lse, float q_to, float y, float q_o, float r) {
+  float l = lse;
+  if (q_to != 0.f) l -= q_to * y;
+  if (q_o != 0.f) l -= q_o * r;
+  return l;
+}
+
 // Upstream gradient scale s of row r: g_r, g / n (mean) or g (sum).
 __device__ __forceinline__ float grad_scale(int32_t reduce, const float* g, const int32_t* n_valid, int64_t r) {
   if (reduce == CE_REDUCE_MEAN) return (g ? g[0] : 1.f) / (float)(*n_valid);
@@ -645,7 +655,9 @@ __device__ void fused_short_row(const FusedArgs& a, uint32_t tag, int64_t r, con
   const double R = wave_sum_d(in ? x : 0.0);
   const double y = wave_sum_d(lane == g.t ? x : 0.0);
   const double lse = m + log(d);
-  const double loss = lse - (a.q_t_d - a.q_o_d) * y - a.q_o_d * R;
+  double loss = lse;  // zero-weight terms left out, as in row_loss_of
+  if (a.q_t_d != a.q_o_d) loss -= (a.q_t_d - a.q_o_d) * y;
+  if (a.q_o_d != 0.0) loss -= a.q_o_d * R;
   const double q = lane == g.t ? a.q_t_d : a.q_o_d;
   const double gr = tvalid ? s * (exp(x - lse) - q) : __builtin_nan("");
   bstore_elem<DT>((float)gr, rx, lane);
@@ -929,7 +941,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     const float bb = c_hi - M2;
     const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
     const float lse = c_hi * kLn2 + c_lo * kLn2;
-    const float row_loss = tvalid && ws_ok ? lse - L.q_to * Y - L.q_o * R : __uint_as_float(0x7fc00000u);
+    const float row_loss = tvalid && ws_ok ? row_loss_of(lse, L.q_to, Y, L.q_o, R) : __uint_as_float(0x7fc00000u);
 
     // ---- gradient from the registers, written over the logits.  The store
     // offsets are recomputed from an opaque copy of the thread index, so the
@@ -1064,7 +1076,7 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
         const float bb = c_hi - M2;
         const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
         const float lse = c_hi * kLn2 + c_lo * kLn2;
-        const float loss = lse - L.q_to * y - L.q_o * rs;
+        const float loss = row_loss_of(lse, L.q_to, y, L.q_o, rs);
         a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
         if (a.lse) a.lse[r] = tvalid ? lse : __uint_as_float(0x7fc00000u);
       } else {
@@ -1166,7 +1178,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     R += q.w;
   }
   const float lse = M + lg2(D) * kLn2;
-  const float loss = lse - a.q_to * Y - a.q_o * R;
+  const float loss = row_loss_of(lse, a.q_to, Y, a.q_o, R);
   const bool tvalid = t >= 0 && t < a.vocab_total;
   a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
   if (a.lse) a.lse[r] = tvalid ? lse : __uint_as_float(0x7fc00000u);
