@@ -118,6 +118,7 @@ def main():
                     help="time the chunked linear head + cross-entropy (ce_linear_cross_entropy) instead")
     ap.add_argument("--hidden", type=int, default=4096, help="--linear: hidden size D")
     ap.add_argument("--chunk-rows", type=int, default=0, help="--linear: rows per chunk (0: automatic)")
+    ap.add_argument("--tune", action="store_true", help="--linear: ce_linear_tune before the timed steps")
     ap.add_argument("--torch-ref", action="store_true",
                     help="--linear: also time torch's matmul + F.cross_entropy + autograd on the same inputs")
     args = ap.parse_args()
@@ -399,6 +400,11 @@ def bench_linear(args, torch, vce, workloads, dev):
     dh = torch.empty_like(h)
     dw = torch.empty((V, D), dtype=torch.float32, device=dev)
     n = torch.empty(1, dtype=torch.int32, device=dev)
+    if args.tune:
+        t_tune = time.perf_counter()
+        vce.ce_linear_tune(h, W, red, dh=dh, dw=dw, chunk_rows=args.chunk_rows, ws=ws, label_smoothing=w5.alpha,
+                           smoothing=args.smoothing)
+        print(f"[bench] tuned the GEMMs in {time.perf_counter() - t_tune:.1f} s", file=sys.stderr, flush=True)
 
     def step():
         vce.ce_linear_cross_entropy(h, W, t, w5.alpha, red, loss=loss, n_valid=n, dh=dh, dw=dw, ws=ws,
@@ -432,6 +438,7 @@ def bench_linear(args, torch, vce, workloads, dev):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"linear_ce_n{N}_d{D}_v{V}_bf16", "rows": N, "hidden": D, "vocab": V,
                    "chunk_rows": chunk, "chunks": nchunks, "reduction": red, "smoothing": args.smoothing,
+                   "tuned": bool(args.tune),
                    "label_smoothing": w5.alpha},
         "roofline": {"bound": "mfma", "achieved": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

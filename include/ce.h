@@ -286,6 +286,18 @@ ce_status ce_linear_cross_entropy(const ce_linear* lin, const int64_t* targets, 
                                   void* dh, int64_t dh_ld, float* dw, int64_t dw_ld, int32_t accumulate_dw,
                                   int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Optional, once per shape before a training loop: for the GEMMs that
+ * ce_linear_cross_entropy runs with these arguments (a whole chunk, the last
+ * chunk, dh and dW as requested), times the GEMM library's first candidate
+ * algorithms on the given buffers and keeps the fastest for this process.
+ * Synchronises `stream`; writes scratch values into dh, dw and the
+ * workspace's chunk buffer (run the real call afterwards).  Without it the
+ * call uses the library heuristic's first choice.
+ */
+ce_status ce_linear_tune(const ce_linear* lin, const ce_params* p, void* dh, int64_t dh_ld, float* dw,
+                         int64_t dw_ld, int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Waits for `stream` and reports whether any call that used `ws` since it was
  * prepared or last checked gave up waiting in a split-row exchange or count
  * (CE_EDEADLOCK; its results were NaN) or found the workspace unprepared

@@ -290,3 +290,17 @@ def test_linear_workspace_sizes(lib):
     assert rows.value == 100 and n2 < n
     lin.dtype = 9
     assert lib.ce_linear_workspace_bytes(ctypes.byref(lin), ctypes.byref(p), 0, None) == 0
+
+
+def test_linear_tune_rejects_before_any_hip_call(lib):
+    h, w, t = _linear_host()
+    ws = np.zeros(1 << 12, np.uint8)
+    lin = _abi.CeLinear(h.ctypes.data, w.ctypes.data, _abi.CE_BF16, 0, 16, 8, 32, 8, 8)
+    p = _abi.CeParams(0.0, 1, -100, 0, 0)
+    assert lib.ce_linear_tune(ctypes.byref(lin), ctypes.byref(p), None, 0, None, 0, 0, ws.ctypes.data, 64,
+                              None) == _abi.CE_EWORKSPACE
+    assert lib.ce_linear_tune(ctypes.byref(lin), ctypes.byref(p), h.ctypes.data, 4, None, 0, 0, ws.ctypes.data,
+                              ws.nbytes, None) == _abi.CE_ELAYOUT
+    bad = _abi.CeLinear(h.ctypes.data, w.ctypes.data, 5, 0, 16, 8, 32, 8, 8)
+    assert lib.ce_linear_tune(ctypes.byref(bad), ctypes.byref(p), None, 0, None, 0, 0, ws.ctypes.data, ws.nbytes,
+                              None) == _abi.CE_EDTYPE

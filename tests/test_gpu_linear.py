@@ -302,3 +302,13 @@ def test_linear_graph_replays():
             call()  # an eager call on the same workspace between replays
             torch.cuda.synchronize()
     vce.ce_workspace_check(ws)
+
+
+def test_linear_after_tuning():
+    """ce_linear_tune picks each GEMM's algorithm by timing; the call then
+    still meets the bar (ragged last chunk, dh and dW)."""
+    h, w, t = grid_inputs(72, 64, 3001, torch.bfloat16, seed=43)
+    hd, wd = h.cuda(), w.cuda()
+    say("[linear tune] timing candidates")
+    vce.ce_linear_tune(hd, wd, "mean", chunk_rows=32)
+    check_linear(h, w, t, 0.1, "mean", chunk_rows=32, what="after tuning")

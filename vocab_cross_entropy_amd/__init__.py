@@ -33,7 +33,7 @@ __all__ = [
     "ce_forward", "ce_backward_inplace", "ce_fwd_bwd_fused", "ce_scale_grad_inplace", "ce_shard_partial_stats",
     "ce_shard_combine",
     "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_init", "ce_workspace_check",
-    "ce_linear_workspace_bytes", "ce_linear_cross_entropy",
+    "ce_linear_workspace_bytes", "ce_linear_cross_entropy", "ce_linear_tune",
     "parallel_cross_entropy", "linear_cross_entropy",
     "Profiler", "CeError", "CeArgumentError", "lib",
 ]
@@ -321,6 +321,33 @@ def ce_linear_cross_entropy(h, w, t, label_smoothing=0.0, reduce_loss=False, ign
                                        dw.stride(0) if dw is not None else 0, int(bool(accumulate_dw)),
                                        int(chunk_rows), _ptr(ws), ws.numel(), _stream(dev)))
     return loss, dh, dw, n_valid
+
+
+def ce_linear_tune(h, w, reduce_loss="mean", *, dh=None, dw=None, want_dh=True, want_dw=True, chunk_rows=0,
+                   ws=None, label_smoothing=0.0, smoothing="all"):
+    """Time the GEMM library's candidates for the chunked call's shapes on
+    these buffers and keep the fastest (synchronises; dh and dw receive
+    scratch values).  Returns the workspace it used, which the calls can share."""
+    N, D = h.shape
+    V = w.shape[0]
+    dev = h.device
+    p = params(label_smoothing, reduce_loss, -100, 0, smoothing)
+    if dh is None and want_dh:
+        dh = torch.empty((N, D), dtype=h.dtype, device=dev)
+    if dw is None and want_dw:
+        dw = torch.empty((V, D), dtype=torch.float32, device=dev)
+    desc = linear_desc(h, w)
+    if ws is None:
+        nb = lib.ce_linear_workspace_bytes(ctypes.byref(desc), ctypes.byref(p), int(chunk_rows), None)
+        if nb == 0:
+            _check(_abi.CE_EINVAL)
+        ws = _workspace(nb, dev)
+    if not _is_prepared(ws):
+        ce_workspace_init(ws)
+    _check(lib.ce_linear_tune(ctypes.byref(desc), ctypes.byref(p), _ptr(dh), dh.stride(0) if dh is not None else 0,
+                              _ptr(dw), dw.stride(0) if dw is not None else 0, int(chunk_rows), _ptr(ws), ws.numel(),
+                              _stream(dev)))
+    return ws
 
 
 def ce_workspace_check(ws: torch.Tensor):

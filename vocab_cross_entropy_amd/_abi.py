@@ -79,6 +79,8 @@ SIGNATURES = {
     "ce_workspace_init": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp]),
     "ce_linear_workspace_bytes": (ctypes.c_size_t, [_P(CeLinear), _P(CeParams), ctypes.c_int64,
                                                     _P(ctypes.c_int64)]),
+    "ce_linear_tune": (ctypes.c_int, [_P(CeLinear), _P(CeParams), _vp, ctypes.c_int64, _vp, ctypes.c_int64,
+                                      ctypes.c_int64, _vp, ctypes.c_size_t, _vp]),
     "ce_linear_cross_entropy": (ctypes.c_int, [_P(CeLinear), _vp, ctypes.c_int64, _P(CeParams), _vp, _vp, _vp, _vp,
                                                ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
                                                _vp, ctypes.c_size_t, _vp]),

@@ -50,7 +50,9 @@ struct Plan {
   hipblasLtMatmulDesc_t desc = nullptr;
   hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
   hipblasLtMatmulAlgo_t algo;
+  bool tuned = false;  // algo chosen by timing the heuristic's candidates (ce_linear_tune)
 };
+constexpr int kTuneCandidates = 8;
 typedef std::tuple<int, int, int, int64_t, int64_t, int64_t, int, int, int64_t, int64_t, int64_t> PlanKey;
 
 std::mutex g_blas_mu;
@@ -152,6 +154,69 @@ ce_status run_gemm(int dev, const Gemm& g, void* blas_ws, hipStream_t stream) {
   return CE_OK;
 }
 
+// Times the heuristic's first kTuneCandidates algorithms for g on the given
+// buffers (stream synchronised): kTuneRounds interleaved rounds of one
+// warm-up and three timed runs each, a candidate's time its best round.  The
+// plan switches from the heuristic's first choice only to a candidate at
+// least kTuneMargin faster (timings on this chip vary by a few percent with
+// power and clocks).
+constexpr int kTuneRounds = 3;
+constexpr float kTuneMargin = 0.97f;
+ce_status tune_gemm(int dev, const Gemm& g, void* blas_ws, hipStream_t stream) {
+  Plan* p = nullptr;
+  ce_status st = get_plan(dev, g, &p);
+  if (st) return st;
+  if (p->tuned) return CE_OK;
+  hipblasLtMatmulHeuristicResult_t res[kTuneCandidates];
+  int nres = 0;
+  {
+    hipblasLtMatmulPreference_t pref = nullptr;
+    const uint64_t wsmax = kBlasWorkspace;
+    hipblasStatus_t s;
+    if ((s = hipblasLtMatmulPreferenceCreate(&pref)) ||
+        (s = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsmax,
+                                                   sizeof wsmax)) ||
+        (s = hipblasLtMatmulAlgoGetHeuristic(p->handle, p->desc, p->a, p->b, p->c, p->c, pref, kTuneCandidates, res,
+                                             &nres))) {
+      if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+      return lfail(CE_EHIP, "GEMM candidates: %s", blas_status(s));
+    }
+    hipblasLtMatmulPreferenceDestroy(pref);
+  }
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e;
+  if ((e = hipEventCreate(&e0)) || (e = hipEventCreate(&e1))) {
+    if (e0) (void)hipEventDestroy(e0);
+    return lfail(CE_EHIP, "event create: %s", hipGetErrorString(e));
+  }
+  const float alpha = 1.f;
+  float best[kTuneCandidates];
+  for (int i = 0; i < kTuneCandidates; ++i) best[i] = 1e30f;
+  for (int round = 0; round < kTuneRounds; ++round) {
+    for (int i = 0; i < nres; ++i) {
+      if (res[i].state != HIPBLAS_STATUS_SUCCESS || res[i].workspaceSize > kBlasWorkspace) continue;
+      bool ok = true;
+      for (int rep = 0; rep < 4 && ok; ++rep) {
+        if (rep == 1 && hipEventRecord(e0, stream)) ok = false;
+        ok = ok && hipblasLtMatmul(p->handle, p->desc, &alpha, g.A, p->a, g.B, p->b, &g.beta, g.D, p->c, g.D,
+                                   p->c, &res[i].algo, blas_ws, kBlasWorkspace, stream) == HIPBLAS_STATUS_SUCCESS;
+      }
+      float ms = 0.f;
+      if (!ok || hipEventRecord(e1, stream) || hipEventSynchronize(e1) || hipEventElapsedTime(&ms, e0, e1)) continue;
+      if (ms < best[i]) best[i] = ms;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  int pick = 0;
+  for (int i = 1; i < nres; ++i)
+    if (best[i] < best[pick]) pick = i;
+  std::lock_guard<std::mutex> lk(g_blas_mu);
+  if (nres > 0 && best[0] < 1e30f && best[pick] < kTuneMargin * best[0]) p->algo = res[pick].algo;
+  p->tuned = true;
+  return CE_OK;
+}
+
 int elem_bytes(int32_t dtype) { return dtype == CE_BF16 ? 2 : 4; }
 
 ce_status check_linear(const ce_linear* lin, const ce_params* p) {
@@ -234,6 +299,45 @@ size_t ce_linear_workspace_bytes(const ce_linear* lin, const ce_params* p, int64
   if (lin_layout(lin, p, chunk_rows, &w) || chunk_plan_ok(lin, p, w.chunk)) return 0;
   if (chunk_rows_out) *chunk_rows_out = w.chunk;
   return w.total;
+}
+
+ce_status ce_linear_tune(const ce_linear* lin, const ce_params* p, void* dh, int64_t dh_ld, float* dw,
+                         int64_t dw_ld, int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ce_status st;
+  if ((st = check_linear(lin, p))) return st;
+  const int64_t N = lin->N, D = lin->D, V = lin->V;
+  if (dh && (dh_ld < D || (uintptr_t)dh % (uintptr_t)elem_bytes(lin->dtype)))
+    return lfail(CE_ELAYOUT, "dh row stride must be >= D and dh aligned to its dtype");
+  if (dw && (dw_ld < D || (uintptr_t)dw % 4u)) return lfail(CE_ELAYOUT, "dw row stride must be >= D, dw 4-byte aligned");
+  LinLayout w;
+  if ((st = lin_layout(lin, p, chunk_rows, &w)) || (st = chunk_plan_ok(lin, p, w.chunk))) return st;
+  if (!ws || ws_bytes < w.total)
+    return lfail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
+  if ((uintptr_t)ws % 256u) return lfail(CE_EWORKSPACE, "workspace must be 256-byte aligned");
+  int dev = 0;
+  hipError_t e;
+  if ((e = hipGetDevice(&dev))) return lfail(CE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  char* wsb = static_cast<char*>(ws);
+  char* logits = wsb + w.logits;
+  const hipDataType ab = lin->dtype == CE_BF16 ? HIP_R_16BF : HIP_R_32F;
+  // the shapes the call uses: a whole chunk and, when N is not a multiple of it, the last one
+  int64_t shapes[2] = {w.chunk, N % w.chunk};
+  for (int64_t n : shapes) {
+    if (n == 0 || N == 0) continue;
+    Gemm g1{ab, ab, V, n, D, HIPBLAS_OP_T, HIPBLAS_OP_N, lin->w, lin->w_ld, lin->h, lin->h_ld, logits, V, 0.f};
+    if ((st = tune_gemm(dev, g1, wsb + w.blas, stream))) return st;
+    if (dh) {
+      Gemm g2{ab, ab, D, n, V, HIPBLAS_OP_N, HIPBLAS_OP_N, lin->w, lin->w_ld, logits, V, dh, dh_ld, 0.f};
+      if ((st = tune_gemm(dev, g2, wsb + w.blas, stream))) return st;
+    }
+    if (dw) {
+      for (float beta : {0.f, 1.f}) {
+        Gemm g3{ab, HIP_R_32F, D, V, n, HIPBLAS_OP_N, HIPBLAS_OP_T, lin->h, lin->h_ld, logits, V, dw, dw_ld, beta};
+        if ((st = tune_gemm(dev, g3, wsb + w.blas, stream))) return st;
+      }
+    }
+  }
+  return CE_OK;
 }
 
 ce_status ce_linear_cross_entropy(const ce_linear* lin, const int64_t* targets, int64_t t_stride,
