@@ -1,0 +1,105 @@
+"""The fused call at its limits, on the GPU, against the FP64 oracle:
+
+  * the largest vocabulary automatic chunking takes: 64 chunks of 4096
+    16-byte vectors, V = 2^21 BF16 or 2^20 FP32 columns; one vector more is
+    refused (CE_ELAYOUT), and the forward + backward calls, which stream any
+    row length, take it;
+  * a million rows (2^20, the in-kernel count over its 16 target slices of
+    65536 rows), for short rows (the FP64 path) and whole 96-column rows;
+  * two calls in flight at once on two streams, each with its own workspace.
+"""
+import numpy as np
+import pytest
+import torch
+
+import vocab_cross_entropy_amd as vce
+import workloads
+from gpu_util import assert_grad, assert_loss, orc, rows_f64, say, to_device_view
+from test_gpu_parity import check_fused
+
+pytestmark = pytest.mark.gpu
+
+
+def _logits(shape, dtype, seed, sigma=2.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * sigma).to(dtype)
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 1 << 21), (torch.float32, 1 << 20)])
+def test_largest_vocabulary(dtype, V):
+    x = _logits((1, 3, V), dtype, seed=5)
+    t = torch.tensor([[7, V - 1, -100]])
+    check_fused(x, t, 0.1, True, what=f"largest V={V}")
+    check_fused(x, t, 0.1, False, g=np.array([1.0, -0.5, 2.0]), what=f"largest V={V} rows")
+
+
+def test_vocabulary_beyond_the_fused_limit():
+    V = (1 << 21) + 8  # 64 chunks cannot hold it
+    x = _logits((1, 2, V), torch.bfloat16, seed=6)
+    t = torch.tensor([[3, V - 2]])
+    xd, td = to_device_view(x), to_device_view(t)
+    with pytest.raises(vce.CeArgumentError):
+        vce.ce_fwd_bwd_fused(xd, td, 0.1, True)
+    say(f"[limits] streaming forward + backward at V={V}")
+    loss, lse, n = vce.ce_forward(xd, td, 0.1, False)
+    vce.ce_backward_inplace(xd, td, lse, 0.1, False, grad_out=torch.ones(2, device="cuda"))
+    torch.cuda.synchronize()
+    o = orc()
+    ref_rows, _ = o.loss_rows(x, t, 0.1)
+    assert_loss(loss.cpu().numpy(), ref_rows, "beyond the fused limit: loss")
+    ref = o.grad_rows(x, t, 0.1, g=np.ones(2))
+    got = rows_f64(xd)
+    # the target element carries the FP32 lse's resolution; elsewhere the stated bar
+    mask = np.ones_like(ref, bool)
+    mask[0, 3] = mask[1, V - 2] = False
+    err = np.abs(got - ref)
+    assert np.all(err[mask] <= 2.0 ** -8 * np.abs(ref[mask]) + 1e-7)
+
+
+@pytest.mark.parametrize("V", [32, 96])
+def test_a_million_rows(V):
+    N = 1 << 20
+    x = _logits((16, N // 16, V), torch.bfloat16, seed=V)
+    t = workloads.random_targets((16, N // 16), V, seed=V, ignore_frac=0.1)
+    rng = np.random.default_rng(V)
+    sample = np.unique(np.concatenate([[0, N - 1, 65535, 65536], rng.choice(N, 60, replace=False)]))
+    say(f"[limits] {N} rows of {V} columns")
+    xd, td = to_device_view(x), to_device_view(t)
+    loss, n = vce.ce_fwd_bwd_fused(xd, td, 0.1, True)
+    torch.cuda.synchronize()
+    o = orc()
+    n_ref = o.count_valid(t)
+    assert int(n.item()) == n_ref
+    ref_rows, _ = o.loss_rows(x, t, 0.1)
+    assert_loss([loss.item()], [o.mean_loss(ref_rows, n_ref)], "million rows mean")
+    ref = o.grad_rows(x, t, 0.1, reduce_loss=True, rows=sample, n_valid=n_ref)
+    assert_grad(rows_f64(xd, sample), ref, torch.bfloat16, "million rows sampled grad")
+
+
+def test_two_streams_at_once():
+    """Each stream's calls use their own workspace; results equal the calls made one at a time."""
+    xs = [_logits((2, 64, 32003), torch.bfloat16, seed=s) for s in (8, 9)]
+    ts = [workloads.random_targets((2, 64), 32003, seed=s, ignore_frac=0.1) for s in (8, 9)]
+    refs = []
+    for x, t in zip(xs, ts):
+        xd, td = to_device_view(x), to_device_view(t)
+        loss, _ = vce.ce_fwd_bwd_fused(xd, td, 0.1, True)
+        torch.cuda.synchronize()
+        refs.append((loss.clone(), xd.clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    dev = [(to_device_view(x), to_device_view(t)) for x, t in zip(xs, ts)]
+    wss = [vce.ce_workspace_init(torch.empty(vce.ce_workspace_bytes(d[0], 0.1, True), dtype=torch.uint8,
+                                             device="cuda")) for d in dev]
+    torch.cuda.synchronize()
+    say("[limits] two streams")
+    outs = []
+    for i in range(2):
+        streams[i].wait_stream(torch.cuda.current_stream())
+    for i in range(2):
+        with torch.cuda.stream(streams[i]):
+            outs.append(vce.ce_fwd_bwd_fused(dev[i][0], dev[i][1], 0.1, True, ws=wss[i])[0])
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert torch.equal(outs[i], refs[i][0]), f"stream {i}: loss"
+        assert torch.equal(dev[i][0].view(torch.int16), refs[i][1].view(torch.int16)), f"stream {i}: gradient"
+        vce.ce_workspace_check(wss[i])
