@@ -219,20 +219,28 @@ def test_linear_full_size_sampled():
     assert np.all(np.abs(col) <= bound), f"dW column sums: max {np.abs(col).max():.3e}"
 
 
-@pytest.mark.parametrize("reduce", ["mean", "sum"])
+@pytest.mark.parametrize("reduce", ["mean", "sum", "none"])
 def test_linear_autograd(reduce):
-    """linear_cross_entropy: the loss and, after (0.5 * loss).backward(), h.grad
-    and W.grad (FP32 dW cast to BF16 by autograd) against the oracle with g = 0.5."""
+    """linear_cross_entropy: the loss and, after backward with upstream 0.5
+    (per-row weights for per-row losses), h.grad and W.grad (FP32 dW cast to
+    BF16 by autograd) against the oracle."""
     h, w, t = grid_inputs(48, 64, 3001, torch.bfloat16, seed=31)
     say(f"[linear autograd] {reduce}")
     hd = h.cuda().requires_grad_(True)
     wd = w.cuda().requires_grad_(True)
     loss = vce.linear_cross_entropy(hd, wd, t.cuda(), 0.1, reduce, chunk_rows=16)
-    (0.5 * loss).backward()
+    gw = np.linspace(-1.0, 2.0, 48) if reduce == "none" else 0.5
+    if reduce == "none":
+        loss.backward(torch.as_tensor(gw, dtype=torch.float32, device="cuda"))
+    else:
+        (0.5 * loss).backward()
     torch.cuda.synchronize()
     o = orc()
-    ref_rows, ref_dh, ref_dw, G = o.linear_ce(h, w, t, 0.1, reduce_loss=reduce, g=0.5, want_g=True)
-    assert_loss([loss.item()], [o.reduce(ref_rows, reduce, int((t != -100).sum()))], f"autograd {reduce}")
+    ref_rows, ref_dh, ref_dw, G = o.linear_ce(h, w, t, 0.1, reduce_loss=reduce, g=gw, want_g=True)
+    if reduce == "none":
+        assert_loss(loss.detach().cpu().numpy(), ref_rows, "autograd rows")
+    else:
+        assert_loss([loss.item()], [o.reduce(ref_rows, reduce, int((t != -100).sum()))], f"autograd {reduce}")
     assert hd.grad.dtype == torch.bfloat16 and wd.grad.dtype == torch.bfloat16
     check_dh(hd.grad.double().cpu().numpy(), ref_dh, G, w, torch.bfloat16, "autograd h.grad")
     check_dw(wd.grad.double().cpu().numpy(), ref_dw, G, h, torch.bfloat16, "autograd W.grad", out_rho=2.0 ** -8)

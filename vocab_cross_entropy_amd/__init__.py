@@ -402,20 +402,29 @@ def parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False, 
 
 
 class LinearCrossEntropy(torch.autograd.Function):
-    """Autograd form of the chunked head + loss (ce_linear_cross_entropy) for
-    a reduced loss (mean or sum).  The forward computes the loss and both
-    gradients for an upstream gradient of 1 (dh in h's dtype, dW in FP32; no
-    logits are kept); the backward scales them by the upstream gradient in
-    place (ce_scale_grad_inplace: nothing is read or written when it is 1,
-    and no host synchronisation finds out).  dW is returned in FP32; autograd
-    casts it to the weight's dtype."""
+    """Autograd form of the chunked head + loss (ce_linear_cross_entropy).
+
+    Mean or sum: the forward computes the loss and both gradients for an
+    upstream gradient of 1 (dh in h's dtype, dW in FP32; no logits are kept);
+    the backward scales them in place by the upstream gradient
+    (ce_scale_grad_inplace: nothing is read or written when it is 1, and no
+    host synchronisation finds out).  Per-row losses: dW needs every row's
+    upstream gradient, so the forward computes only the losses and the
+    backward runs the chunked call again with the upstream gradients (one
+    logits product more).  dW is returned in FP32; autograd casts it to the
+    weight's dtype."""
 
     @staticmethod
     def forward(ctx, h, weight, target, label_smoothing=0.0, reduce_loss="mean", ignore_idx=-100,
                 smoothing="all", chunk_rows=0):
-        if reduction_code(reduce_loss) == _abi.CE_REDUCE_NONE:
-            raise CeArgumentError(_abi.CE_EINVAL, "linear_cross_entropy needs a reduced loss (mean or sum); for "
-                                                  "per-row losses call ce_linear_cross_entropy with grad_out")
+        ctx.per_row = reduction_code(reduce_loss) == _abi.CE_REDUCE_NONE
+        ctx.args = (label_smoothing, reduce_loss, ignore_idx, smoothing, chunk_rows)
+        if ctx.per_row:
+            loss, _, _, _ = ce_linear_cross_entropy(h.detach(), weight.detach(), target, label_smoothing,
+                                                    reduce_loss, ignore_idx, want_dh=False, want_dw=False,
+                                                    chunk_rows=chunk_rows, smoothing=smoothing)
+            ctx.save_for_backward(h.detach(), weight.detach(), target)
+            return loss
         loss, dh, dw, _ = ce_linear_cross_entropy(h.detach(), weight.detach(), target, label_smoothing,
                                                   reduce_loss, ignore_idx, want_dh=ctx.needs_input_grad[0],
                                                   want_dw=ctx.needs_input_grad[1], chunk_rows=chunk_rows,
@@ -427,6 +436,15 @@ class LinearCrossEntropy(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_loss):
+        if ctx.per_row:
+            h, weight, target = ctx.saved_tensors
+            label_smoothing, reduce_loss, ignore_idx, smoothing, chunk_rows = ctx.args
+            g = grad_loss.to(dtype=torch.float32).reshape(-1).contiguous()
+            _, dh, dw, _ = ce_linear_cross_entropy(h, weight, target, label_smoothing, reduce_loss, ignore_idx,
+                                                   grad_out=g, want_dh=ctx.needs_input_grad[0],
+                                                   want_dw=ctx.needs_input_grad[1], chunk_rows=chunk_rows,
+                                                   smoothing=smoothing)
+            return dh, dw, None, None, None, None, None, None
         dh, dw = ctx.saved_tensors
         g = grad_loss.reshape(1)
         if ctx.has[0]:
@@ -441,7 +459,8 @@ def linear_cross_entropy(h, weight, target, label_smoothing=0.0, reduce_loss="me
     """Cross-entropy of the head ``h @ weight.T`` without whole logits: the
     rows go through ce_linear_cross_entropy in chunks.  ``h`` [N, D],
     ``weight`` [V, D] (torch Linear layout), ``target`` [N] int64.  Returns
-    the FP32 mean (or sum) and reaches autograd through LinearCrossEntropy."""
+    the FP32 mean or sum, or the [N] per-row losses with
+    ``reduce_loss="none"``, and reaches autograd through LinearCrossEntropy."""
     return LinearCrossEntropy.apply(h, weight, target, label_smoothing, reduce_loss, ignore_idx, smoothing,
                                     chunk_rows)
 
