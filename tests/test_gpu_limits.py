@@ -6,7 +6,8 @@
     row length, take it;
   * a million rows (2^20, the in-kernel count over its 16 target slices of
     65536 rows), for short rows (the FP64 path) and whole 96-column rows;
-  * two calls in flight at once on two streams, each with its own workspace.
+  * two calls in flight at once on two streams, each with its own workspace;
+  * logits with a large common offset (1000 + N(0, 2^2)).
 """
 import numpy as np
 import pytest
@@ -103,3 +104,15 @@ def test_two_streams_at_once():
         assert torch.equal(outs[i], refs[i][0]), f"stream {i}: loss"
         assert torch.equal(dev[i][0].view(torch.int16), refs[i][1].view(torch.int16)), f"stream {i}: gradient"
         vce.ce_workspace_check(wss[i])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_large_common_offset(dtype):
+    """Logits of 1000 + N(0, 2^2): the loss is shift-invariant, the FP32
+    arithmetic around it is not (its error grows like ulp(max |x|)); at this
+    offset it stays well inside the bar, for whole and split rows."""
+    g = torch.Generator().manual_seed(13)
+    x = (1000.0 + torch.randn((2, 8, 32003), generator=g) * 2).to(dtype)
+    t = workloads.random_targets((2, 8), 32003, seed=13, ignore_frac=0.1)
+    check_fused(x, t, 0.1, True, what=f"offset 1000 {dtype}")
+    check_fused(x, t, 0.1, False, g=np.ones(16), split_chunks=5, what=f"offset 1000 split {dtype}")
