@@ -274,8 +274,7 @@ ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p
   int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
   hipError_t e;
   if (N == 0) {  // nothing to read: n = 0, and the mean of no rows is 0/0
-    if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
-      return hip_fail(e, "prologue launch");
+    if ((e = vce::launch_zero_count(n_out, stream))) return hip_fail(e, "count launch");
     if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, mean_n(p, n_out), loss, stream)))
       return hip_fail(e, "mean launch");
     return CE_OK;
@@ -365,8 +364,7 @@ ce_status fused_call(const ce_logits* x, const ce_targets* t, const ce_params* p
   hipError_t e;
   if (N == 0) {  // nothing to read: n = 0, and the mean of no rows is 0/0
     int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
-    if ((e = vce::launch_prologue(t->data, t->s0, t->s1, x->d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
-      return hip_fail(e, "prologue launch");
+    if ((e = vce::launch_zero_count(n_out, stream))) return hip_fail(e, "count launch");
     if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, mean_n(p, n_out), loss, stream)))
       return hip_fail(e, "mean launch");
     return CE_OK;
@@ -488,8 +486,7 @@ ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1
   int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
   hipError_t e;
   if (N == 0) {  // nothing to combine: n = 0, and the mean of no rows is 0/0
-    if ((e = vce::launch_prologue(t->data, t->s0, t->s1, d1, N, p->ignore_idx, n_out, hdr, nullptr, 0, stream)))
-      return hip_fail(e, "prologue launch");
+    if ((e = vce::launch_zero_count(n_out, stream))) return hip_fail(e, "count launch");
     if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, mean_n(p, n_out), loss, stream)))
       return hip_fail(e, "mean launch");
     return CE_OK;

@@ -118,9 +118,8 @@ int64_t max_body_vecs(int32_t dtype, int64_t V);
 int32_t fused_auto_chunks(int32_t dtype, int64_t V);
 
 // Launchers: enqueue on `stream`, return the hipError_t of the launch.
-hipError_t launch_prologue(const int64_t* tgt, int64_t ts0, int64_t ts1, int64_t d1, int64_t N,
-                           int64_t ignore_idx, int32_t* n_out, WsHeader* hdr, unsigned long long* slots,
-                           int64_t nslots, hipStream_t stream);
+// n_out[0] = 0 (calls on no rows)
+hipError_t launch_zero_count(int32_t* n_out, hipStream_t stream);
 hipError_t launch_fused(const FusedArgs& a, FusedShape shape, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_stats(const StatsArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);

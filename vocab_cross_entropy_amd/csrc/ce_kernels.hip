@@ -398,33 +398,9 @@ __device__ int32_t block_count_targets(const int64_t* tgt, int64_t ts0, int64_t 
 }
 
 // --------------------------------------------------------------------------
-// Prologue: n = #{rows with target != ignore_idx} (block 0), and clearing of
-// the split-row exchange words and the tagged row losses (other blocks).
-__global__ __launch_bounds__(1024) void k_prologue(const int64_t* tgt, int64_t ts0, int64_t ts1, int64_t d1,
-                                                   int64_t N, int64_t ignore_idx, int32_t* n_out, WsHeader* hdr,
-                                                   unsigned long long* slots, int64_t nslots) {
-  if (blockIdx.x == 0) {
-    __shared__ int sh[16];
-    int cnt = 0;
-#pragma unroll 8
-    for (int64_t r = threadIdx.x; r < N; r += 1024) {
-      const int64_t i0 = r / d1, i1 = r - i0 * d1;
-      cnt += tgt[i0 * ts0 + i1 * ts1] != ignore_idx;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = cnt;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int n = 0;
-      for (int i = 0; i < 16; ++i) n += sh[i];
-      *n_out = n;
-    }
-    if (hdr && threadIdx.x == 0) hdr->status = 0u;
-  } else {
-    const int64_t stride = (int64_t)(gridDim.x - 1) * 1024;
-    for (int64_t i = (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x; i < nslots; i += stride) slots[i] = 0ull;
-  }
+// Calls on no rows: n = 0 (the mean of no rows is then 0/0).
+__global__ __launch_bounds__(64) void k_zero_count(int32_t* n_out) {
+  if (threadIdx.x == 0) n_out[0] = 0;
 }
 
 // --------------------------------------------------------------------------
@@ -1282,13 +1258,8 @@ int32_t fused_auto_chunks(int32_t dtype, int64_t V) {
   return (int32_t)best_k;
 }
 
-hipError_t launch_prologue(const int64_t* tgt, int64_t ts0, int64_t ts1, int64_t d1, int64_t N, int64_t ignore_idx,
-                           int32_t* n_out, WsHeader* hdr, unsigned long long* slots, int64_t nslots,
-                           hipStream_t stream) {
-  int64_t clear_blocks = (nslots + 8 * 1024 - 1) / (8 * 1024);
-  if (clear_blocks > 1024) clear_blocks = 1024;
-  hipLaunchKernelGGL(k_prologue, dim3((uint32_t)(1 + clear_blocks)), dim3(1024), 0, stream, tgt, ts0, ts1, d1, N,
-                     ignore_idx, n_out, hdr, slots, nslots);
+hipError_t launch_zero_count(int32_t* n_out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_zero_count, dim3(1), dim3(64), 0, stream, n_out);
   return hipGetLastError();
 }
 
