@@ -113,6 +113,8 @@ def main():
                     help="label smoothing a/V over all classes (default) or a/(V-1) over the other classes")
     ap.add_argument("--reduction", choices=["none", "mean", "sum"], default=None,
                     help="loss reduction (default: the workload's own)")
+    ap.add_argument("--fused-shards", action="store_true",
+                    help="shard workloads: one ce_shards_fwd_bwd_fused launch in place of the three-call flow")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--linear", action="store_true",
                     help="time the chunked linear head + cross-entropy (ce_linear_cross_entropy) instead")
@@ -166,14 +168,17 @@ def main():
     loss = torch.empty(1 if red != "none" else N, dtype=torch.float32, device=dev)
     n_valid = torch.empty(1, dtype=torch.int32, device=dev)
     calls_per_step = 1
-    if w.calls == "fused":
+    calls = w.calls
+    if calls == "shard" and args.fused_shards:
+        calls = "shard_fused"
+    if calls == "fused":
         ws = torch.empty(vce.ce_workspace_bytes(view(pool[0]), w.alpha, red, split_chunks=args.split_chunks),
                          dtype=torch.uint8, device=dev)
 
         def step(p):
             vce.ce_fwd_bwd_fused(view(p), t_view, w.alpha, red, loss=loss, n_valid=n_valid, ws=ws,
                                  split_chunks=args.split_chunks, smoothing=sm)
-    elif w.calls == "split":
+    elif calls == "split":
         ws = torch.empty(vce.ce_workspace_bytes(view(pool[0]), w.alpha, red), dtype=torch.uint8, device=dev)
         lse = torch.empty(N, dtype=torch.float32, device=dev)
         g = torch.ones(N, dtype=torch.float32, device=dev)
@@ -183,6 +188,15 @@ def main():
             x = view(p)
             vce.ce_forward(x, t_view, w.alpha, red, loss=loss, lse=lse, n_valid=n_valid, ws=ws, smoothing=sm)
             vce.ce_backward_inplace(x, t_view, lse, w.alpha, red, grad_out=g, n_valid=n_valid, smoothing=sm)
+    elif calls == "shard_fused":  # vocabulary shards, every shard read once in one launch
+        bounds = workloads.shard_bounds(V, w.shards)
+        pool = [[phys_dev[..., a:c].contiguous() for a, c in bounds] for _ in range(P)]
+        ws = torch.empty(vce.ce_shards_workspace_bytes(pool[0], w.alpha, red, smoothing=sm), dtype=torch.uint8,
+                         device=dev)
+
+        def step(shards):
+            vce.ce_shards_fwd_bwd_fused([view(x) for x in shards], t_view, w.alpha, red, loss=loss,
+                                        n_valid=n_valid, ws=ws, smoothing=sm)
     else:  # vocabulary shards: S partial-stat calls, one combine, S backward calls
         bounds = workloads.shard_bounds(V, w.shards)
         pool = [[phys_dev[..., a:c].contiguous() for a, c in bounds] for _ in range(P)]
@@ -280,9 +294,11 @@ def main():
     # the algorithmic bytes one launch moves (read + written, formula N*V*b
     # per pass over the logits or a shard)
     main_ms = prof.ms
-    if w.calls == "fused":
+    if calls == "fused":
         layout = [("k_fused", formula_bytes)]
-    elif w.calls == "split":
+    elif calls == "shard_fused":
+        layout = [("k_fused_shards", formula_bytes)]
+    elif calls == "split":
         layout = [("k_stats (ce_forward)", N * V * b), ("k_backward (ce_backward_inplace)", 2 * N * V * b)]
     else:
         layout = ([("k_stats (ce_shard_partial_stats)", N * (c - a) * b) for a, c in bounds]
@@ -329,7 +345,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {**w.describe(), "io_dtype": "bf16" if w.elem_bytes == 2 else "f32", "calls": w.calls,
+        "config": {**w.describe(), "io_dtype": "bf16" if w.elem_bytes == 2 else "f32", "calls": calls,
                    "reduction": red, "smoothing": sm,
                    "split_chunks": args.split_chunks, "pool": P, "fresh_inputs": P >= args.steps},
         "rows_per_s": round(N / (step_ms * 1e-3), 1),
@@ -343,7 +359,7 @@ def main():
                        "note": "each step timed alone after restoring its logits and writing 512 MiB of scratch"},
         "cpu_baseline": None,
     }
-    if w.calls != "fused":
+    if calls in ("split", "shard"):
         moved = 3 * N * V * b
         out["moved_bytes_per_step"] = moved
         out["moved_GBps"] = round(moved / (step_ms * 1e-3) / 1e9, 1)

@@ -191,6 +191,26 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
                            float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The vocabulary-shard flow in one launch, each shard read once: S shards
+ * (1 <= S <= 16) of one row set -- separate buffers, same dtype, rows and
+ * vocab_total, tiling [0, vocab_total) in order (shards[s].vocab_start is
+ * the sum of the previous shards' v_local; widths may differ, ceil(V / S)
+ * with a short last shard as on hyper-parallel #269 section 3.1).  Every
+ * shard's piece of a row stays in registers while the shards exchange
+ * (max, sum-exp, target logit, row sum) through the workspace, as the chunks
+ * of a split row do in ce_fwd_bwd_fused; then each shard's gradient is
+ * written over it.  Same loss, gradient, reduction and workspace protocol as
+ * ce_fwd_bwd_fused (ws from ce_shards_workspace_bytes, prepared by
+ * ce_workspace_init).  The exchange sits where a multi-GPU run would
+ * exchange the statistics between devices.  Shard rows of up to 4096 16-byte
+ * vectors form one chunk; longer ones are cut, with at most 64 chunks per row.
+ */
+size_t ce_shards_workspace_bytes(const ce_logits* shards, int32_t S, const ce_params* p);
+ce_status ce_shards_fwd_bwd_fused(const ce_logits* shards, int32_t S, const ce_targets* t, const ce_params* p,
+                                  const float* grad_out, float* loss, int32_t* n_valid, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/*
  * Deferred upstream gradient (TENPU #29 section 6 stages the gradient in the
  * input; the autograd backward then applies the upstream gradient).  `x`
  * holds a gradient written by ce_fwd_bwd_fused or ce_backward_inplace for an

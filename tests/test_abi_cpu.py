@@ -304,3 +304,63 @@ def test_linear_tune_rejects_before_any_hip_call(lib):
     bad = _abi.CeLinear(h.ctypes.data, w.ctypes.data, 5, 0, 16, 8, 32, 8, 8)
     assert lib.ce_linear_tune(ctypes.byref(bad), ctypes.byref(p), None, 0, None, 0, 0, ws.ctypes.data, ws.nbytes,
                               None) == _abi.CE_EDTYPE
+
+
+def _shard_set(h, widths, change=None):
+    """Shard descriptors over the host buffer: consecutive column ranges of widths."""
+    V = sum(widths)
+    arr = (_abi.CeLogits * len(widths))()
+    start = 0
+    for i, w in enumerate(widths):
+        d = dict(data=h.x.ctypes.data + 2 * start, dtype=_abi.CE_BF16, reserved=0, d0=2, d1=h.N // 2,
+                 s0=h.N // 2 * V, s1=V, v_local=w, vocab_start=start, vocab_total=V)
+        d.update((change or {}).get(i, {}))
+        arr[i] = _abi.CeLogits(**d)
+        start += w
+    return arr
+
+
+BAD_SHARDS = [
+    ("no_shards", dict(S=0), _abi.CE_EINVAL),
+    ("too_many_shards", dict(widths=[1] * 17), _abi.CE_EINVAL),
+    ("gap", dict(change={1: dict(vocab_start=9)}), _abi.CE_ELAYOUT),
+    ("overlap", dict(change={1: dict(vocab_start=7)}), _abi.CE_ELAYOUT),
+    ("short_cover", dict(change={1: dict(v_local=7)}), _abi.CE_ELAYOUT),
+    ("dtype_mismatch", dict(change={1: dict(dtype=_abi.CE_F32)}), _abi.CE_ELAYOUT),
+    ("rows_mismatch", dict(change={1: dict(d1=2)}), _abi.CE_ELAYOUT),
+    ("vocab_total_mismatch", dict(change={1: dict(vocab_total=32)}), _abi.CE_ELAYOUT),
+    ("bad_shard_stride", dict(change={1: dict(s1=4)}), _abi.CE_ELAYOUT),
+    ("split_chunks", dict(p=dict(split_chunks=2)), _abi.CE_EINVAL),
+    ("reduce_unknown", dict(p=dict(reduce_loss=5)), _abi.CE_EINVAL),
+    ("small_workspace", dict(ws_bytes=16), _abi.CE_EWORKSPACE),
+    ("no_workspace", dict(ws=False), _abi.CE_EWORKSPACE),
+    ("null_targets", dict(t=dict(data=None)), _abi.CE_EINVAL),
+]
+
+
+@pytest.mark.parametrize("name,case,status", BAD_SHARDS, ids=[b[0] for b in BAD_SHARDS])
+def test_shards_fused_rejects_before_any_hip_call(lib, name, case, status):
+    h = Host()
+    widths = case.get("widths", [8, 8])
+    arr = _shard_set(h, widths, case.get("change"))
+    S = case.get("S", len(arr))
+    p = h.params(**case.get("p", {}))
+    t = h.targets(**case.get("t", {}))
+    rc = lib.ce_shards_fwd_bwd_fused(arr, S, ctypes.byref(t), ctypes.byref(p), None, h.loss.ctypes.data,
+                                     h.n.ctypes.data, h.ws.ctypes.data if case.get("ws", True) else None,
+                                     case.get("ws_bytes", h.ws.nbytes), None)
+    assert rc == status, (rc, lib.ce_last_error())
+    assert lib.ce_last_error()
+    assert h.untouched()
+    if "ws" not in case and "ws_bytes" not in case and "t" not in case:  # the shard set itself is refused
+        assert lib.ce_shards_workspace_bytes(arr, S, ctypes.byref(p)) == 0
+
+
+def test_shards_workspace_sizes(lib):
+    h = Host()
+    p = h.params()
+    one = lib.ce_shards_workspace_bytes(_shard_set(h, [16]), 1, ctypes.byref(p))
+    two = lib.ce_shards_workspace_bytes(_shard_set(h, [8, 8]), 2, ctypes.byref(p))
+    assert 0 < one < two  # a second shard adds exchange slots per row
+    # 16 shards is the most; up to 64 chunks per row in all
+    assert lib.ce_shards_workspace_bytes(_shard_set(h, [1] * 16), 16, ctypes.byref(p)) > 0

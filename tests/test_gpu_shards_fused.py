@@ -1,0 +1,145 @@
+"""ce_shards_fwd_bwd_fused: the vocabulary-shard flow in one launch, each shard
+read once, on the GPU through the C ABI, against the FP64 oracle's full-row
+loss and gradient (each shard's gradient is that gradient's columns).
+
+Shards as column views of one tensor (in place, disjoint columns) and as
+separate buffers; even and ceil-uneven widths (hyper-parallel #269 section
+3.1), one shard, tiny shards, shards cut into several chunks; contiguous and
+transposed (SQ, B) views; every reduction, both smoothing conventions, masked
+(-inf) columns; and workload 4's shape against the three-call shard flow.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import vocab_cross_entropy_amd as vce
+import workloads
+from gpu_util import assert_grad, assert_loss, ignored_rows, orc, raw_bits, rows_f64, say, to_device_view
+
+pytestmark = pytest.mark.gpu
+
+
+def _g_dev(g, reduce, N):
+    if g is None:
+        return None
+    if reduce == "none":
+        return torch.as_tensor(np.asarray(g, np.float32)).cuda()
+    return torch.tensor([float(g)], dtype=torch.float32, device="cuda")
+
+
+def check_shards(x, t, bounds, alpha, reduce, g=None, smoothing="all", separate=False, what=""):
+    N = t.numel()
+    say(f"[shards fused] {what} {tuple(x.shape)} {x.dtype} S={len(bounds)} a={alpha} {reduce} {smoothing} "
+        f"{'buffers' if separate else 'views'}")
+    xd, td = to_device_view(x), to_device_view(t)
+    if separate:
+        shards = [xd[..., a:b].contiguous() for a, b in bounds]
+    else:
+        shards = [xd[..., a:b] for a, b in bounds]
+    loss, n = vce.ce_shards_fwd_bwd_fused(shards, td, alpha, reduce, grad_out=_g_dev(g, reduce, N),
+                                          smoothing=smoothing)
+    torch.cuda.synchronize()
+    o = orc()
+    n_ref = o.count_valid(t)
+    assert int(n.item()) == n_ref
+    ref_rows, _ = o.loss_rows(x, t, alpha, smoothing=smoothing)
+    if reduce == "none":
+        got = loss.cpu().numpy().astype(np.float64)
+        fin = np.isfinite(ref_rows)
+        assert np.array_equal(np.isposinf(got), np.isposinf(ref_rows))
+        assert_loss(got[fin], ref_rows[fin], what + " loss rows")
+    else:
+        ref = o.reduce(ref_rows, reduce, n_ref)
+        if reduce == "mean" and n_ref == 0:
+            assert math.isnan(loss.item())
+        elif math.isinf(ref):
+            assert loss.item() == ref
+        else:
+            assert_loss([loss.item()], [ref], f"{what} {reduce}")
+    ref_g = o.grad_rows(x, t, alpha, reduce_loss=reduce, g=g, smoothing=smoothing)
+    if separate:
+        got_g = np.concatenate([rows_f64(s) for s in shards], axis=1)
+    else:
+        got_g = rows_f64(xd)
+    assert_grad(got_g, ref_g, x.dtype, what + " grad")
+    ign = ignored_rows(t)
+    if len(ign) and not separate:
+        assert not raw_bits(xd, ign).any(), "ignored rows must be +0.0 in every shard"
+    return loss
+
+
+def _logits(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * 2).to(dtype)
+
+
+LAYOUTS = [(V, S) for V, S in ((5003, 4), (1001, 7), (65, 3), (128000, 16), (400000, 2), (4096, 1))]
+
+
+@pytest.mark.parametrize("V,S", LAYOUTS, ids=[f"V{v}-S{s}" for v, s in LAYOUTS])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_shard_layouts(V, S, dtype):
+    x = _logits((2, 6, V), dtype, seed=V + S)
+    t = workloads.random_targets((2, 6), V, seed=V, ignore_frac=0.2)
+    bounds = workloads.shard_bounds(V, S)
+    check_shards(x, t, bounds, 0.1, "mean", g=0.9, what=f"V={V} S={S}")
+    check_shards(x, t, bounds, 0.1, "none", g=np.linspace(-1.0, 2.0, 12), separate=True, what=f"V={V} S={S}")
+
+
+OPTS = [(red, sm, a) for red in ("none", "mean", "sum") for sm in ("all", "others") for a in (0.0, 0.2)]
+
+
+@pytest.mark.parametrize("reduce,smoothing,alpha", OPTS, ids=[f"{o[0]}-{o[1]}-a{o[2]}" for o in OPTS])
+def test_shard_options_transposed(reduce, smoothing, alpha):
+    """The (SQ, B) transposed view of (B, SQ) storage, cut into 5 uneven shards."""
+    phys = _logits((3, 8, 9001), torch.bfloat16, seed=31)
+    x = phys.transpose(0, 1)
+    tp = workloads.random_targets((3, 8), 9001, seed=31, ignore_frac=0.25)
+    t = tp.transpose(0, 1)
+    g = np.linspace(0.5, 1.5, 24) if reduce == "none" else 0.7
+    check_shards(x, t, workloads.shard_bounds(9001, 5), alpha, reduce, g=g, smoothing=smoothing, what="transposed")
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.1])
+def test_shard_masked_padding(alpha):
+    """A vocabulary padded with masked columns at its end (the last shard)."""
+    V = 32768 + 128
+    x = _logits((2, 8, V), torch.bfloat16, seed=41)
+    x[..., 32768:] = -float("inf")
+    t = workloads.random_targets((2, 8), 32768, seed=41, ignore_frac=0.1)
+    check_shards(x, t, workloads.shard_bounds(V, 4), alpha, "mean", what="masked padding")
+
+
+def test_shard_rejections():
+    x = torch.zeros((1, 4, 100), dtype=torch.bfloat16, device="cuda")
+    t = torch.zeros((1, 4), dtype=torch.int64, device="cuda")
+    a, b = x[..., :50], x[..., 50:]
+    with pytest.raises(vce.CeArgumentError):  # dtypes differ
+        vce.ce_shards_fwd_bwd_fused([a, b.float()], t)
+    with pytest.raises(vce.CeArgumentError):  # no shard
+        vce.ce_shards_fwd_bwd_fused([], t)
+    with pytest.raises(vce.CeArgumentError):  # rows differ
+        vce.ce_shards_fwd_bwd_fused([a, torch.zeros((1, 3, 50), dtype=torch.bfloat16, device="cuda")], t[:, :3])
+    with pytest.raises(vce.CeArgumentError):  # more than 16 shards
+        vce.ce_shards_fwd_bwd_fused([x[..., i * 5:(i + 1) * 5] for i in range(20)], t)
+
+
+def test_workload4_against_the_three_call_flow():
+    """Workload 4's 4 x [512, 16384] shards: the one-launch flow equals the
+    stats / combine / backward flow within the bar and matches the oracle."""
+    w = workloads.WORKLOADS[4]
+    inp = workloads.generate(w)
+    x, t = inp.logits, inp.targets
+    bounds = workloads.shard_bounds(w.V, w.shards)
+    loss = check_shards(x, t, bounds, w.alpha, "none", g=np.ones(w.rows), separate=True, what="workload 4")
+    td = to_device_view(t)
+    shards = [x[..., a:b].contiguous().cuda() for a, b in bounds]
+    stats = torch.empty((len(bounds), w.rows, 4), dtype=torch.float32, device="cuda")
+    for s, (a, b) in enumerate(bounds):
+        vce.ce_shard_partial_stats(shards[s], td, a, w.V, stats=stats[s])
+    loss3, _, _ = vce.ce_shard_combine(stats, td, w.V, w.alpha, False)
+    torch.cuda.synchronize()
+    l1, l3 = loss.cpu().numpy().astype(np.float64), loss3.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(l1 - l3) <= 1e-4 * np.maximum(1.0, np.abs(l3)))

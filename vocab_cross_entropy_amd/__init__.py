@@ -31,7 +31,7 @@ from ._abi import CE_BF16, CE_F32, CeArgumentError, CeError
 
 __all__ = [
     "ce_forward", "ce_backward_inplace", "ce_fwd_bwd_fused", "ce_scale_grad_inplace", "ce_shard_partial_stats",
-    "ce_shard_combine",
+    "ce_shard_combine", "ce_shards_fwd_bwd_fused", "ce_shards_workspace_bytes",
     "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_init", "ce_workspace_check",
     "ce_linear_workspace_bytes", "ce_linear_cross_entropy", "ce_linear_tune",
     "parallel_cross_entropy", "linear_cross_entropy",
@@ -217,6 +217,53 @@ def ce_fwd_bwd_fused(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-1
         ce_workspace_init(ws)
     _check(lib.ce_fwd_bwd_fused(ctypes.byref(xd), ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(grad_out),
                                 _ptr(loss), _ptr(n_valid), _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, n_valid
+
+
+def _shard_descs(shards):
+    """(d0, d1, V_s) shard views in vocabulary order -> a ctypes array of descriptors."""
+    if not shards:
+        raise CeArgumentError(_abi.CE_EINVAL, "at least one shard is needed")
+    total = sum(int(x.shape[2]) for x in shards)
+    arr = (_abi.CeLogits * len(shards))()
+    start = 0
+    for i, x in enumerate(shards):
+        arr[i] = logits_desc(x, start, total)
+        start += int(x.shape[2])
+    return arr
+
+
+def ce_shards_workspace_bytes(shards, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100,
+                              smoothing="all") -> int:
+    arr = _shard_descs(shards)
+    n = lib.ce_shards_workspace_bytes(arr, len(shards), ctypes.byref(params(label_smoothing, reduce_loss,
+                                                                             ignore_idx, 0, smoothing)))
+    if n == 0:
+        _check(_abi.CE_EINVAL)
+    return int(n)
+
+
+def ce_shards_fwd_bwd_fused(shards, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, grad_out=None,
+                            loss=None, n_valid=None, ws=None, smoothing="all"):
+    """The shard flow in one launch: ``shards`` are the (d0, d1, V_s) pieces of
+    the logits in vocabulary order (separate tensors); each is read once and
+    receives its gradient in place.  Returns (loss, n_valid)."""
+    arr = _shard_descs(shards)
+    d0, d1, _ = shards[0].shape
+    N = d0 * d1
+    dev = shards[0].device
+    p = params(label_smoothing, reduce_loss, ignore_idx, 0, smoothing)
+    loss = _f32(1 if p.reduce_loss else N, dev) if loss is None else loss
+    n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
+    if ws is None:
+        nb = lib.ce_shards_workspace_bytes(arr, len(shards), ctypes.byref(p))
+        if nb == 0:
+            _check(_abi.CE_EINVAL)
+        ws = _workspace(nb, dev)
+    if not _is_prepared(ws):
+        ce_workspace_init(ws)
+    _check(lib.ce_shards_fwd_bwd_fused(arr, len(shards), ctypes.byref(targets_desc(t)), ctypes.byref(p),
+                                       _ptr(grad_out), _ptr(loss), _ptr(n_valid), _ptr(ws), ws.numel(), _stream(dev)))
     return loss, n_valid
 
 

@@ -72,6 +72,9 @@ SIGNATURES = {
     "ce_backward_inplace": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp]),
     "ce_fwd_bwd_fused": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp,
                                         ctypes.c_size_t, _vp]),
+    "ce_shards_workspace_bytes": (ctypes.c_size_t, [_P(CeLogits), ctypes.c_int32, _P(CeParams)]),
+    "ce_shards_fwd_bwd_fused": (ctypes.c_int, [_P(CeLogits), ctypes.c_int32, _P(CeTargets), _P(CeParams), _vp, _vp,
+                                               _vp, _vp, ctypes.c_size_t, _vp]),
     "ce_scale_grad_inplace": (ctypes.c_int, [_P(CeLogits), _vp, ctypes.c_int32, _vp]),
     "ce_shard_partial_stats": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp]),
     "ce_shard_combine": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,

@@ -410,6 +410,119 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
   return fused_call(x, t, p, grad_out, loss, n_valid, ws, ws_bytes, stream);
 }
 
+namespace {
+
+// The shard set's checks and plan: S shards of one row set (same dtype,
+// rows and vocabulary) that tile [0, vocab_total) in order; each shard row
+// is cut into kper chunks of at most 4096 vectors.
+struct ShardPlan {
+  int32_t kper = 0, K = 0;
+  int64_t C = 0;
+  vce::FusedShape shape{0, 0};
+};
+
+ce_status shard_plan(const ce_logits* shards, int32_t S, const ce_params* p, ShardPlan* out) {
+  ce_status st;
+  if ((st = check_params(p))) return st;
+  if (!shards) return fail(CE_EINVAL, "shards is NULL");
+  if (S < 1 || S > vce::kMaxShards) return fail(CE_EINVAL, "S = %d outside [1, %d]", S, vce::kMaxShards);
+  if (p->split_chunks != 0) return fail(CE_EINVAL, "split_chunks must be 0 for sharded logits");
+  int64_t nv_max = 0, next = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    const ce_logits* x = &shards[s];
+    if ((st = check_logits(x, false))) return fail(st, "shard %d: %s", s, ce_last_error());
+    if (x->dtype != shards[0].dtype || x->d0 != shards[0].d0 || x->d1 != shards[0].d1 ||
+        x->vocab_total != shards[0].vocab_total)
+      return fail(CE_ELAYOUT, "shard %d: dtype, rows and vocab_total must match shard 0", s);
+    if (x->vocab_start != next)
+      return fail(CE_ELAYOUT, "shard %d starts at column %lld, expected %lld (shards tile the vocabulary in order)",
+                  s, (long long)x->vocab_start, (long long)next);
+    next += x->v_local;
+    const int64_t nv = vce::max_body_vecs(x->dtype, x->v_local);
+    if (nv > nv_max) nv_max = nv;
+  }
+  if (next != shards[0].vocab_total)
+    return fail(CE_ELAYOUT, "shards cover %lld of %lld columns", (long long)next, (long long)shards[0].vocab_total);
+  if ((st = check_smoothing(p, shards[0].vocab_total))) return st;
+  ShardPlan pl;
+  pl.kper = (int32_t)((nv_max + 4095) / 4096);
+  if (pl.kper < 1) pl.kper = 1;
+  pl.K = S * pl.kper;
+  if (pl.K > kMaxChunks)
+    return fail(CE_ELAYOUT, "%d shards of up to %lld vectors need %d chunks per row (at most %lld)", S,
+                (long long)nv_max, pl.K, (long long)kMaxChunks);
+  pl.C = (nv_max + pl.kper - 1) / pl.kper;
+  if (pl.C < 1) pl.C = 1;
+  pl.shape = vce::fused_shape_for(pl.C);
+  if (pl.shape.threads == 1024 || pl.shape.vecs == 16) pl.shape = vce::FusedShape{512, 8};  // C <= 4096 here
+  const int64_t N = shards[0].d0 * shards[0].d1;
+  if (N * pl.K > kMaxGrid) return fail(CE_EINVAL, "rows x chunks exceeds the launch grid");
+  *out = pl;
+  return CE_OK;
+}
+
+}  // namespace
+
+size_t ce_shards_workspace_bytes(const ce_logits* shards, int32_t S, const ce_params* p) {
+  ShardPlan pl;
+  if (shard_plan(shards, S, p, &pl)) return 0;
+  return ws_layout(shards[0].d0 * shards[0].d1, pl.K, p->reduce_loss != 0, true).total;
+}
+
+ce_status ce_shards_fwd_bwd_fused(const ce_logits* shards, int32_t S, const ce_targets* t, const ce_params* p,
+                                  const float* grad_out, float* loss, int32_t* n_valid, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  ce_status st;
+  ShardPlan pl;
+  if ((st = shard_plan(shards, S, p, &pl))) return st;
+  const int64_t N = shards[0].d0 * shards[0].d1;
+  if ((st = check_targets(t, N))) return st;
+  if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
+  const WsLayout w = ws_layout(N, pl.K, p->reduce_loss != 0, true);
+  if (!ws || ws_bytes < w.total)
+    return fail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
+  if (((uintptr_t)ws) % 256u) return fail(CE_EWORKSPACE, "workspace must be 256-byte aligned");
+
+  char* wsb = static_cast<char*>(ws);
+  auto* hdr = reinterpret_cast<vce::WsHeader*>(wsb);
+  hipError_t e;
+  if (N == 0) {  // nothing to read: n = 0, and the mean of no rows is 0/0
+    int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
+    if ((e = vce::launch_zero_count(n_out, stream))) return hip_fail(e, "count launch");
+    if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, mean_n(p, n_out), loss, stream)))
+      return hip_fail(e, "mean launch");
+    return CE_OK;
+  }
+  vce::ShardSet ss;
+  memset(&ss, 0, sizeof ss);
+  ss.S = S;
+  ss.kper = pl.kper;
+  for (int32_t s = 0; s < S; ++s) ss.L[s] = row_layout(&shards[s], t, p);
+  vce::FusedArgs a;
+  a.L = ss.L[0];
+  a.K = pl.K;
+  a.aligned = 0;
+  a.C = pl.C;
+  a.reduce = p->reduce_loss;
+  a.g = grad_out;
+  a.n_out = n_valid;
+  a.row_loss = p->reduce_loss ? nullptr : loss;
+  a.row_loss_tagged = reinterpret_cast<unsigned long long*>(wsb + w.row_loss_tagged);
+  a.mean_out = p->reduce_loss ? loss : nullptr;
+  a.hdr = hdr;
+  a.slots = pl.K > 1 ? reinterpret_cast<unsigned long long*>(wsb + w.slots) : nullptr;
+  a.slice_rows = (N + vce::kMaxSlices - 1) / vce::kMaxSlices;
+  if (a.slice_rows < 2048) a.slice_rows = 2048;
+  a.nslice = (int32_t)((N + a.slice_rows - 1) / a.slice_rows);
+  a.ws_bytes = w.total;
+  a.short_rows = 0;
+  a.q_o_d = a.q_t_d = 0.0;
+  hipEvent_t e0, e1;
+  prof_next(&e0, &e1);
+  if ((e = vce::launch_fused_shards(a, ss, pl.shape, stream, e0, e1))) return hip_fail(e, "sharded fused launch");
+  return CE_OK;
+}
+
 ce_status ce_scale_grad_inplace(const ce_logits* x, const float* grad_out, int32_t per_row, hipStream_t stream) {
   ce_status st;
   if ((st = check_logits(x, false))) return st;

@@ -75,6 +75,16 @@ struct FusedArgs {
 // Longest row the fused kernel's FP64 path takes (one column per lane of a wave).
 constexpr int64_t kShortRow = 64;
 
+// The vocabulary shards of ce_shards_fwd_bwd_fused (a kernel argument):
+// shard s's layout (buffer, strides, v_local, vocab_start); each shard row is
+// cut into kper chunks, so a row has K = S * kper chunks.
+constexpr int kMaxShards = 16;
+struct ShardSet {
+  int32_t S;
+  int32_t kper;
+  RowLayout L[kMaxShards];
+};
+
 enum StatsMode { kStatsForward = 0, kStatsShard = 1 };
 
 struct StatsArgs {
@@ -121,6 +131,9 @@ int32_t fused_auto_chunks(int32_t dtype, int64_t V);
 // n_out[0] = 0 (calls on no rows)
 hipError_t launch_zero_count(int32_t* n_out, hipStream_t stream);
 hipError_t launch_fused(const FusedArgs& a, FusedShape shape, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+// shapes 512 x 8 and 256 x {1, 2, 4, 8} only
+hipError_t launch_fused_shards(const FusedArgs& a, const ShardSet& ss, FusedShape shape, hipStream_t stream,
+                               hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_stats(const StatsArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);

@@ -124,6 +124,16 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   f2 in = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(in, h2));
 }
+// A vector's terms packed to FP16 pairs (the staging of BF16 gradients; FP32
+// rows never stage, their instance only needs to compile).
+template <int DT>
+__device__ __forceinline__ uint4 pack_terms_f16(const float (&t)[ElemT<DT>::E]) {
+  if constexpr (DT == CE_BF16)
+    return make_uint4(pack_f16(t[0], t[1]), pack_f16(t[2], t[3]), pack_f16(t[4], t[5]), pack_f16(t[6], t[7]));
+  else
+    return make_uint4(pack_f16(t[0], t[1]), pack_f16(t[2], t[3]), 0u, 0u);
+}
+
 // fma(FP16 half of w widened to FP32, k, c) in one v_fma_mix_f32
 // (op_sel_hi marks operand 0 as FP16, op_sel picks its high half).
 __device__ __forceinline__ float fma_mix_lo(uint32_t w, float k, float c) {
@@ -666,14 +676,18 @@ __device__ void fused_short_row(const FusedArgs& a, uint32_t tag, int64_t r, con
 // HT: rows may have head/tail elements (a row start or end off a 16-byte
 // boundary).  When every row is aligned the host launches HT = false, which
 // keeps the two scalar element registers out of the chunk's register budget.
-template <int DT, int T, int P, bool HT>
-__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_fused(FusedArgs a) {
+// SH: the row's K chunks are kper sub-chunks of each of ss->S vocabulary
+// shards (separate buffers, each with its own layout and vocab_start), the
+// single-read form of the shard flow; chunk k is sub-chunk k mod kper of
+// shard k / kper.  Without SH they are K consecutive pieces of one buffer.
+template <int DT, int T, int P, bool HT, bool SH>
+__device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* ss) {
   constexpr int E = ElemT<DT>::E;
   __shared__ float sh[T / 64][4];
   __shared__ float xs[64 * 4];
   __shared__ int sh_n;
   const int tid = threadIdx.x;
-  const RowLayout& L = a.L;
+  const RowLayout& L = a.L;  // targets, rows, ignore_idx, vocabulary and smoothing: common to all shards
   const int K = a.K;
 
   const int64_t item = blockIdx.x;
@@ -689,12 +703,21 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
   const int k = (int)(item - r * K);
   if (r >= L.N) return;
 
-  const Row<DT> g = row_geometry<DT, HT>(L, r);
-  const int64_t cb = (int64_t)k * a.C;
+  int kb = k, kper = K;  // this chunk's place in its buffer
+  const RowLayout* Lb = &a.L;
+  if constexpr (SH) {
+    kper = ss->kper;
+    const int sidx = k / kper;
+    kb = k - sidx * kper;
+    Lb = &ss->L[sidx];
+  }
+  const Row<DT> g = row_geometry<DT, HT>(*Lb, r);
+  const int64_t cb = (int64_t)kb * a.C;
   const int64_t cend = g.nv < cb + a.C ? g.nv : cb + a.C;
   const int nvc = cend > cb ? (int)(cend - cb) : 0;
   uint4* body = g.body + cb;
-  const bool first = (k == 0), last = (k == K - 1);
+  const bool first = (kb == 0), last = (kb == kper - 1);  // the buffer's head and tail
+  const bool row_first = (k == 0);                      // the row's loss is published once
 
   if (g.t == L.ignore_idx) {  // ignored row: +0.0 gradient, loss 0, nothing read
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
@@ -703,7 +726,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       if (first && tid < g.h) store_elem<DT>(g.base, tid, 0.f);
       if (last && tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
     }
-    publish_row_loss<T>(a, tag, r, 0.f, first);
+    publish_row_loss<T>(a, tag, r, 0.f, row_first);
   } else if (P == 1 && a.short_rows) {
     if constexpr (P == 1) fused_short_row<DT, T>(a, tag, r, g);
   } else {
@@ -737,9 +760,12 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
     // ---- where the target sits (uniform): head, body (chunk, vector, lane,
     // element) or tail; only the chunk that holds it has own_tid >= 0
     const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
-    const int64_t tl = g.t - L.vocab_start;
+    const int64_t tl = g.t - Lb->vocab_start;
+    // a shard owns the target only when it lies in the shard's own columns
+    // (one unsharded buffer holds every valid target)
+    const bool tin = SH ? (tvalid && tl >= 0 && tl < Lb->V) : tvalid;
     int own_tid = -1, own_j = 0, own_e = 0;
-    if (tvalid) {
+    if (tin) {
       if (tl < g.h) {
         if (first) own_tid = (int)tl;
       } else {
@@ -845,7 +871,7 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
           q0 += t[e];
           q1 += t[e + 1];
         }
-        v[j] = make_uint4(pack_f16(t[0], t[1]), pack_f16(t[2], t[3]), pack_f16(t[4], t[5]), pack_f16(t[6], t[7]));
+        v[j] = pack_terms_f16<DT>(t);
       }
       d0 += (q0 + q1) * kReuseUnscale;  // exact power-of-two rescale
     } else {
@@ -963,11 +989,27 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
       else
         bstore_elem<DT>(g_t, rb, (own_j * T + tid) * E + own_e);
     }
-    publish_row_loss<T>(a, tag, r, row_loss, first);
+    publish_row_loss<T>(a, tag, r, row_loss, row_first);
   }
   // one call site for both kinds of row (two inlined copies of the finish
   // measurably raised the register allocation of the whole kernel)
   if (item == last_item) fused_finish<T>(a, tag);
+}
+
+template <int DT, int T, int P, bool HT>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_fused(FusedArgs a) {
+  fused_item<DT, T, P, HT, false>(a, nullptr);
+}
+
+// The shard flow in one launch: each shard's piece of a row is read once
+// into registers, the shards exchange (max, sum-exp, target logit, row sum)
+// through the workspace's tagged words like the chunks of a split row, and
+// each writes its gradient in place.  Shards may start and end anywhere, so
+// head and tail elements are always handled.
+template <int DT, int T, int P>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_fused_shards(FusedArgs a,
+                                                                                                ShardSet ss) {
+  fused_item<DT, T, P, true, true>(a, &ss);
 }
 
 // --------------------------------------------------------------------------
@@ -1205,6 +1247,25 @@ hipError_t launch_fused_dt(const FusedArgs& a, FusedShape shape, int64_t grid, h
   return hipErrorInvalidValue;
 }
 
+template <int DT>
+hipError_t launch_fused_shards_dt(const FusedArgs& a, const ShardSet& ss, FusedShape shape, int64_t grid,
+                                  hipStream_t stream) {
+  const dim3 g((uint32_t)grid);
+  if (shape.threads == 512 && shape.vecs == 8)
+    hipLaunchKernelGGL((k_fused_shards<DT, 512, 8>), g, dim3(512), 0, stream, a, ss);
+  else if (shape.threads == 256 && shape.vecs == 8)
+    hipLaunchKernelGGL((k_fused_shards<DT, 256, 8>), g, dim3(256), 0, stream, a, ss);
+  else if (shape.threads == 256 && shape.vecs == 4)
+    hipLaunchKernelGGL((k_fused_shards<DT, 256, 4>), g, dim3(256), 0, stream, a, ss);
+  else if (shape.threads == 256 && shape.vecs == 2)
+    hipLaunchKernelGGL((k_fused_shards<DT, 256, 2>), g, dim3(256), 0, stream, a, ss);
+  else if (shape.threads == 256 && shape.vecs == 1)
+    hipLaunchKernelGGL((k_fused_shards<DT, 256, 1>), g, dim3(256), 0, stream, a, ss);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 constexpr int kStreamT = 256;   // k_scale: threads per row
 constexpr int kStreamPB = 4;    //          16-byte vectors per thread per batch
 // Long rows: k_stats reads 512 threads x 8 vectors per batch, k_backward
@@ -1270,6 +1331,19 @@ hipError_t launch_fused(const FusedArgs& a, FusedShape shape, hipStream_t stream
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   e = (a.L.dtype == CE_BF16) ? launch_fused_dt<CE_BF16>(a, shape, grid, stream)
                              : launch_fused_dt<CE_F32>(a, shape, grid, stream);
+  if (e != hipSuccess) return e;
+  if (ev1) e = hipEventRecord(ev1, stream);
+  return e;
+}
+
+hipError_t launch_fused_shards(const FusedArgs& a, const ShardSet& ss, FusedShape shape, hipStream_t stream,
+                               hipEvent_t ev0, hipEvent_t ev1) {
+  const int64_t grid = a.L.N * a.K;
+  if (grid == 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  e = (a.L.dtype == CE_BF16) ? launch_fused_shards_dt<CE_BF16>(a, ss, shape, grid, stream)
+                             : launch_fused_shards_dt<CE_F32>(a, ss, shape, grid, stream);
   if (e != hipSuccess) return e;
   if (ev1) e = hipEventRecord(ev1, stream);
   return e;
