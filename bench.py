@@ -69,6 +69,17 @@ def traffic_from_profiles(workload_name: str):
     return t, f"fetch x{fetch_scale:.3f}, write x{write_scale:.3f} (copy calibration)"
 
 
+def device_info(torch, dev) -> dict:
+    """What the runtime reports of the device the step ran on; the peak HBM
+    rate used as the roofline's denominator is the published figure."""
+    pr = torch.cuda.get_device_properties(dev)
+    info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
+            "total_memory_bytes": pr.total_memory, "l2_cache_bytes": getattr(pr, "L2_cache_size", None),
+            "lds_per_workgroup_bytes": getattr(pr, "shared_memory_per_block", None),
+            "wave_size": getattr(pr, "warp_size", None), "peak_hbm_GBps_published": PEAK_GBPS}
+    return info
+
+
 def cpu_baseline(w, inputs, sample_rows: int, reduction: str, smoothing: str):
     """The FP64 oracle (as it is) on the first `sample_rows` rows: loss and
     gradient, the same work per row as the GPU step."""
@@ -78,7 +89,7 @@ def cpu_baseline(w, inputs, sample_rows: int, reduction: str, smoothing: str):
 
     orc = oracle.default()
     N = w.rows
-    rows = np.arange(min(sample_rows, N), dtype=np.int64)
+    rows = np.arange(N if sample_rows <= 0 else min(sample_rows, N), dtype=np.int64)
     n_valid = orc.count_valid(inputs.targets)
     t0 = time.perf_counter()
     for b in range(0, rows.size, 256):
@@ -93,7 +104,8 @@ def cpu_baseline(w, inputs, sample_rows: int, reduction: str, smoothing: str):
         "unit": "GB/s",
         "cores": orc.max_threads(),
         "kind": "oracle",
-        "sample": f"first {rows.size} of {N} rows (loss + gradient, FP64), {dt:.2f} s wall",
+        "sample": (f"all {N} rows" if rows.size == N else f"first {rows.size} of {N} rows")
+                  + f" of the step's logits (loss + gradient, FP64), {dt:.2f} s wall",
         "rows_per_s": rows.size / dt,
     }
 
@@ -106,7 +118,7 @@ def main():
     ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--pool", type=int, default=0,
                     help="device copies of the input (HBM); 0 = one per timed step, as memory allows")
-    ap.add_argument("--cpu-sample-rows", type=int, default=1536)
+    ap.add_argument("--cpu-sample-rows", type=int, default=0, help="rows the CPU oracle is timed on (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-chunks", type=int, default=0, help="tuning: force the fused kernel's split")
     ap.add_argument("--smoothing", choices=["all", "others"], default="all",
@@ -358,6 +370,7 @@ def main():
                        "n": len(cold), "evict_bytes": 512 << 20,
                        "note": "each step timed alone after restoring its logits and writing 512 MiB of scratch"},
         "cpu_baseline": None,
+        "device": device_info(torch, dev),
     }
     if calls in ("split", "shard"):
         moved = 3 * N * V * b
@@ -464,6 +477,7 @@ def bench_linear(args, torch, vce, workloads, dev):
                           "GBps": round(2 * N * V * 2 / (ce_ms * 1e-3) / 1e9, 1)},
         "memory": {"workspace_bytes": ws_bytes, "full_logits_bytes": N * V * 2},
         "loss": float(loss[0].item()) if red != "none" else None,
+        "device": device_info(torch, dev),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_linear(h, W, t, w5.alpha, red, args.smoothing, n_rows=4)
