@@ -280,7 +280,7 @@ typedef struct ce_linear {
 } ce_linear;
 
 /* Workspace bytes of ce_linear_cross_entropy for `lin`, `p` and chunk_rows
- * (0: automatic, about 512 MiB of logits per chunk); 0 if the arguments are
+ * (0: automatic, about 1 GiB of logits per chunk); 0 if the arguments are
  * invalid.  `*chunk_rows_out` (may be NULL) receives the chunk size used. */
 size_t ce_linear_workspace_bytes(const ce_linear* lin, const ce_params* p, int64_t chunk_rows,
                                  int64_t* chunk_rows_out);

@@ -283,9 +283,9 @@ def test_linear_workspace_sizes(lib):
     p = _abi.CeParams(0.1, 1, -100, 0, 0)
     rows = ctypes.c_int64(0)
     n = lib.ce_linear_workspace_bytes(ctypes.byref(lin), ctypes.byref(p), 0, ctypes.byref(rows))
-    # automatic chunks of 2048 rows (about 512 MiB of BF16 logits), plus the fused call's words and GEMM scratch
-    assert rows.value == 2048
-    assert 2048 * 128000 * 2 < n < 2048 * 128000 * 2 + (128 << 20)
+    # automatic chunks of 4096 rows (about 1 GiB of BF16 logits), plus the fused call's words and GEMM scratch
+    assert rows.value == 4096
+    assert 4096 * 128000 * 2 < n < 4096 * 128000 * 2 + (128 << 20)
     n2 = lib.ce_linear_workspace_bytes(ctypes.byref(lin), ctypes.byref(p), 100, ctypes.byref(rows))
     assert rows.value == 100 and n2 < n
     lin.dtype = 9

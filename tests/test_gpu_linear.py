@@ -185,7 +185,7 @@ def test_linear_no_rows():
 
 def test_linear_full_size_sampled():
     """The 4 x 2048-row head of a 4096-wide model onto 128000 BF16 columns in
-    the automatic chunks (2048 rows): sampled rows of the loss and of dh
+    the automatic chunks (4096 rows): sampled rows of the loss and of dh
     against the oracle (a row's loss and dh depend on that row alone; the
     mean's n counts every row), and dW's column sums, which vanish because
     every gradient row sums to zero, within the bound that G's rounding leaves."""

@@ -37,11 +37,12 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 constexpr size_t kBlasWorkspace = 64ull << 20;   // the GEMM library's scratch, inside the caller's workspace
 // automatic chunk: about this many bytes of logits.  On 8192 x 4096 x 128000
-// BF16 a step took 32.0 ms in chunks of 1024 rows (256 MiB), 23.3 ms in 2048,
-// 21.5 ms in 4096 and 20.9 ms in one chunk: the dh product has few output
+// BF16 a step took 32.0 ms in chunks of 1024 rows (256 MiB), 23.2 ms in 2048,
+// 21.4 ms in 4096 and 20.8 ms in one chunk: the dh product has few output
 // tiles and the dW product re-reads and re-writes its FP32 accumulator
-// once per chunk, so small chunks cost GEMM efficiency.
-constexpr size_t kChunkTarget = 512ull << 20;
+// once per chunk, so small chunks cost GEMM efficiency.  1 GiB is a small
+// share of the device's memory and keeps most of the gain.
+constexpr size_t kChunkTarget = 1ull << 30;
 
 // ---- GEMM plans: one per (device, types, shape, ops, leading dims, beta != 0),
 // built on first use (heuristic query) and kept until the process ends.
