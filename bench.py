@@ -86,17 +86,29 @@ def cpu_baseline(w, inputs, sample_rows: int, reduction: str, smoothing: str):
     import numpy as np
 
     import oracle
+    import workloads
 
     orc = oracle.default()
     N = w.rows
     rows = np.arange(N if sample_rows <= 0 else min(sample_rows, N), dtype=np.int64)
     n_valid = orc.count_valid(inputs.targets)
+    g = None if reduction == "none" else 1.0
+    if w.shards > 1:  # the shard form: per-shard statistics, their combine, per-shard gradients
+        bounds = workloads.shard_bounds(w.V, w.shards)
+        shards = [inputs.logits[..., a:c].contiguous() for a, c in bounds]
     t0 = time.perf_counter()
     for b in range(0, rows.size, 256):
         blk = rows[b:b + 256]
-        orc.loss_rows(inputs.logits, inputs.targets, w.alpha, rows=blk, smoothing=smoothing)
-        orc.grad_rows(inputs.logits, inputs.targets, w.alpha, reduce_loss=reduction,
-                      g=None if reduction == "none" else 1.0, rows=blk, n_valid=n_valid, smoothing=smoothing)
+        if w.shards > 1:
+            st = np.stack([orc.shard_stats(sh, inputs.targets, a, w.V, rows=blk) for sh, (a, c) in zip(shards, bounds)])
+            _, lse = orc.shard_combine(st, inputs.targets, w.V, w.alpha, rows=blk, smoothing=smoothing)
+            for sh, (a, c) in zip(shards, bounds):
+                orc.shard_grad(sh, inputs.targets, a, w.V, lse, w.alpha, reduce_loss=reduction, g=g, rows=blk,
+                               n_valid=n_valid, smoothing=smoothing)
+        else:
+            orc.loss_rows(inputs.logits, inputs.targets, w.alpha, rows=blk, smoothing=smoothing)
+            orc.grad_rows(inputs.logits, inputs.targets, w.alpha, reduce_loss=reduction, g=g, rows=blk,
+                          n_valid=n_valid, smoothing=smoothing)
     dt = time.perf_counter() - t0
     nbytes = 2 * rows.size * w.V * w.elem_bytes
     return {
@@ -105,7 +117,7 @@ def cpu_baseline(w, inputs, sample_rows: int, reduction: str, smoothing: str):
         "cores": orc.max_threads(),
         "kind": "oracle",
         "sample": (f"all {N} rows" if rows.size == N else f"first {rows.size} of {N} rows")
-                  + f" of the step's logits (loss + gradient, FP64), {dt:.2f} s wall",
+                  + f" of the step's logits (loss + gradient, FP64{', shard form' if w.shards > 1 else ''}), {dt:.2f} s wall",
         "rows_per_s": rows.size / dt,
     }
 
