@@ -688,6 +688,11 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
   __shared__ int sh_n;
   const int tid = threadIdx.x;
   const RowLayout& L = a.L;  // targets, rows, ignore_idx, vocabulary and smoothing: common to all shards
+  // A new workgroup's waves take issue priority over the running ones on
+  // their SIMD until the chunk loads are out: its memory requests go in flight
+  // sooner, while the others' arithmetic loses little (on the 4 x 2048 x
+  // 128000 BF16 workload about 2% of the kernel's time, in interleaved runs).
+  __builtin_amdgcn_s_setprio(3);
   const int K = a.K;
 
   const int64_t item = blockIdx.x;
@@ -747,6 +752,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
     uint4 v[P];
 #pragma unroll
     for (int j = 0; j < P; ++j) v[j] = bload16(rb, (uint32_t)(j * T + tid) * 16u);
+    __builtin_amdgcn_s_setprio(0);
     const float g_up = a.g ? a.g[a.reduce ? 0 : r] : 1.f;
     const bool hv = HT && first && tid < g.h, tv = HT && last && tid < g.tn;
     float hx = -INFINITY, tx = -INFINITY;
