@@ -204,6 +204,14 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
  * ce_workspace_init).  The exchange sits where a multi-GPU run would
  * exchange the statistics between devices.  Shard rows of up to 4096 16-byte
  * vectors form one chunk; longer ones are cut, with at most 64 chunks per row.
+ * `shards` is a host array of S descriptors (read during the call only); the
+ * shards' data, t, grad_out, loss, n_valid and ws are device memory as for
+ * ce_fwd_bwd_fused.  Errors, found on the host before anything is enqueued:
+ * CE_EINVAL (NULL shards, S outside [1, 16], split_chunks != 0, a bad
+ * descriptor field, targets or loss), CE_ELAYOUT (shards that differ in
+ * dtype, rows or vocab_total, do not tile the vocabulary in order, or need
+ * more than 64 chunks per row), CE_EWORKSPACE.  ce_shards_workspace_bytes
+ * returns 0 for a shard set the call would refuse.
  */
 size_t ce_shards_workspace_bytes(const ce_logits* shards, int32_t S, const ce_params* p);
 ce_status ce_shards_fwd_bwd_fused(const ce_logits* shards, int32_t S, const ce_targets* t, const ce_params* p,

@@ -443,8 +443,9 @@ def parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False, 
     columns); ``target`` the matching (B, SQ) / (SQ, B) int64 global indices.
     """
     if dist_process_group is not None:
-        raise NotImplementedError("vocabulary-parallel process groups need more than one GPU; use "
-                                  "ce_shard_partial_stats / ce_shard_combine / ce_backward_inplace per shard")
+        raise NotImplementedError("vocabulary-parallel process groups need more than one GPU; on one GPU use "
+                                  "ce_shards_fwd_bwd_fused, or ce_shard_partial_stats / ce_shard_combine / "
+                                  "ce_backward_inplace per shard")
     return ParallelCrossEntropy.apply(inp, target, label_smoothing, reduce_loss, ignore_idx, smoothing)
 
 
