@@ -30,3 +30,10 @@ def test_unknown_names_rejected(kw):
 def test_process_group_needs_more_than_one_gpu():
     with pytest.raises(NotImplementedError):
         vce.parallel_cross_entropy(None, None, dist_process_group=object())
+
+
+def test_no_shards_rejected_before_any_device_work():
+    with pytest.raises(vce.CeArgumentError):
+        vce.sharded_cross_entropy([], None)
+    with pytest.raises(vce.CeArgumentError):
+        vce.ce_shards_fwd_bwd_fused([], None)

@@ -143,3 +143,47 @@ def test_workload4_against_the_three_call_flow():
     torch.cuda.synchronize()
     l1, l3 = loss.cpu().numpy().astype(np.float64), loss3.cpu().numpy().astype(np.float64)
     assert np.all(np.abs(l1 - l3) <= 1e-4 * np.maximum(1.0, np.abs(l3)))
+
+
+AUTOGRAD = [(red, gk) for red in ("none", "mean", "sum") for gk in ("one", "any")]
+
+
+@pytest.mark.parametrize("reduce,gkind", AUTOGRAD, ids=[f"{r}-{g}" for r, g in AUTOGRAD])
+def test_sharded_autograd(reduce, gkind):
+    """sharded_cross_entropy: the loss and, after backward, each shard's
+    gradient (in the shard's own storage) against the oracle's columns.  A
+    factor other than 1 rounds a BF16 gradient twice (staged, then scaled):
+    2 x 2^-8 |ref| there, as for parallel_cross_entropy."""
+    V, S = 9001, 3
+    x = _logits((2, 8, V), torch.bfloat16, seed=61)
+    t = workloads.random_targets((2, 8), V, seed=61, ignore_frac=0.2)
+    bounds = workloads.shard_bounds(V, S)
+    N = t.numel()
+    rng = np.random.default_rng(61)
+    if reduce == "none":
+        g_host = (np.ones(N) if gkind == "one" else rng.uniform(0.2, 2.5, N)).astype(np.float32)
+        grad_arg = torch.as_tensor(g_host, device="cuda").view(t.shape)
+        g_or = g_host.astype(np.float64)
+    else:
+        gval = 1.0 if gkind == "one" else 0.3
+        grad_arg = torch.tensor(gval, dtype=torch.float32, device="cuda")
+        g_or = float(np.float32(gval))
+    say(f"[sharded autograd] {reduce} g={gkind}")
+    xd, td = to_device_view(x), to_device_view(t)
+    shards = [xd[..., a:b].contiguous().requires_grad_(True) for a, b in bounds]
+    loss = vce.sharded_cross_entropy(shards, td, 0.1, reduce)
+    loss.backward(grad_arg)
+    torch.cuda.synchronize()
+    o = orc()
+    n = o.count_valid(t)
+    ref_rows, _ = o.loss_rows(x, t, 0.1)
+    if reduce == "none":
+        assert tuple(loss.shape) == tuple(t.shape)
+        assert_loss(loss.detach().reshape(-1).cpu().numpy(), ref_rows, "sharded autograd rows")
+    else:
+        assert_loss([float(loss.item())], [o.reduce(ref_rows, reduce, n)], f"sharded autograd {reduce}")
+    for sh in shards:
+        assert sh.grad is not None and sh.grad.data_ptr() == sh.data_ptr()
+    got = np.concatenate([rows_f64(sh.grad) for sh in shards], axis=1)
+    ref = o.grad_rows(x, t, 0.1, reduce_loss=reduce, g=g_or, n_valid=n)
+    assert_grad(got, ref, torch.bfloat16, "sharded autograd grad", extra_rtol=0.0 if gkind == "one" else 2.0 ** -8)

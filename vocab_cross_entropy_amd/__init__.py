@@ -35,7 +35,7 @@ __all__ = [
     "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_init", "ce_workspace_check",
     "ce_linear_workspace_bytes", "ce_linear_cross_entropy", "ce_linear_tune",
     "parallel_cross_entropy", "linear_cross_entropy",
-    "Profiler", "CeError", "CeArgumentError", "lib",
+    "Profiler", "CeError", "CeArgumentError", "lib", "ShardedCrossEntropy", "sharded_cross_entropy",
 ]
 
 lib = _abi.load()
@@ -447,6 +447,42 @@ def parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False, 
                                   "ce_shards_fwd_bwd_fused, or ce_shard_partial_stats / ce_shard_combine / "
                                   "ce_backward_inplace per shard")
     return ParallelCrossEntropy.apply(inp, target, label_smoothing, reduce_loss, ignore_idx, smoothing)
+
+
+class ShardedCrossEntropy(torch.autograd.Function):
+    """Autograd form of the one-launch shard call (ce_shards_fwd_bwd_fused):
+    the logits arrive as S vocabulary shards, separate (d0, d1, V_s) tensors
+    in vocabulary order (hyper-parallel #269 section 3.1's ceil(V / S) split,
+    as a tensor-parallel rank would hold them).  Forward: each shard is read
+    once and receives its gradient for an upstream gradient of 1 in place.
+    Backward: every shard's staged gradient times the upstream gradient
+    (ce_scale_grad_inplace, nothing touched when it is 1); the shards'
+    storage is returned as their gradients.  After the forward the shards
+    hold gradients, not logits."""
+
+    @staticmethod
+    def forward(ctx, target, label_smoothing, reduce_loss, ignore_idx, smoothing, *shards):
+        bufs = [x.detach() for x in shards]
+        loss, _ = ce_shards_fwd_bwd_fused(bufs, target, label_smoothing, reduce_loss, ignore_idx,
+                                          smoothing=smoothing)
+        ctx.reduced = reduction_code(reduce_loss) != _abi.CE_REDUCE_NONE
+        ctx.save_for_backward(*bufs)
+        return loss[0] if ctx.reduced else loss.view(target.shape)
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        bufs = ctx.saved_tensors
+        for buf in bufs:
+            ce_scale_grad_inplace(buf, grad_loss, per_row=not ctx.reduced)
+        return (None, None, None, None, None, *bufs)
+
+
+def sharded_cross_entropy(shards, target, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *,
+                          smoothing="all"):
+    """Cross-entropy over logits held as vocabulary shards (a list of (d0, d1,
+    V_s) tensors in vocabulary order, at most 16), with the same options and
+    result as parallel_cross_entropy over their concatenation; one launch."""
+    return ShardedCrossEntropy.apply(target, label_smoothing, reduce_loss, ignore_idx, smoothing, *shards)
 
 
 class LinearCrossEntropy(torch.autograd.Function):
