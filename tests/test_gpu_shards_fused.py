@@ -187,3 +187,21 @@ def test_sharded_autograd(reduce, gkind):
     got = np.concatenate([rows_f64(sh.grad) for sh in shards], axis=1)
     ref = o.grad_rows(x, t, 0.1, reduce_loss=reduce, g=g_or, n_valid=n)
     assert_grad(got, ref, torch.bfloat16, "sharded autograd grad", extra_rtol=0.0 if gkind == "one" else 2.0 ** -8)
+
+
+@pytest.mark.parametrize("reduce", ["none", "mean", "sum"])
+def test_shards_no_rows(reduce):
+    """No rows: n = 0; the mean is 0/0 = NaN, the sum 0, per-row losses empty."""
+    say(f"[shards fused] no rows {reduce}")
+    x = torch.zeros((0, 4, 300), dtype=torch.bfloat16, device="cuda")
+    t = torch.zeros((0, 4), dtype=torch.int64, device="cuda")
+    shards = [x[..., a:b] for a, b in workloads.shard_bounds(300, 3)]
+    loss, n = vce.ce_shards_fwd_bwd_fused(shards, t, 0.1, reduce)
+    torch.cuda.synchronize()
+    assert int(n.item()) == 0
+    if reduce == "none":
+        assert loss.numel() == 0
+    elif reduce == "mean":
+        assert math.isnan(loss.item())
+    else:
+        assert loss.item() == 0.0
