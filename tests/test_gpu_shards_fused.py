@@ -205,3 +205,58 @@ def test_shards_no_rows(reduce):
         assert math.isnan(loss.item())
     else:
         assert loss.item() == 0.0
+
+
+@pytest.mark.parametrize("reduce", [False, True])
+def test_shards_graph_replays(reduce):
+    """The shard call captured in a HIP graph: each replay (shards restored in
+    between, an eager call on the same workspace interleaved) takes a fresh
+    tag from the workspace and matches the eager call bit for bit."""
+    V, S = 20000, 3  # shards of 6667 columns: 834 vectors each, whole in one chunk
+    x = _logits((2, 9, V), torch.bfloat16, seed=71)
+    t = workloads.random_targets((2, 9), V, seed=71, ignore_frac=0.2)
+    xd, td = to_device_view(x), to_device_view(t)
+    bounds = workloads.shard_bounds(V, S)
+    shards = [xd[..., a:b].contiguous() for a, b in bounds]
+    pristine = [sh.clone() for sh in shards]
+    ws = vce.ce_workspace_init(torch.empty(vce.ce_shards_workspace_bytes(shards, 0.1, reduce), dtype=torch.uint8,
+                                           device="cuda"))
+    loss = torch.empty(1 if reduce else 18, dtype=torch.float32, device="cuda")
+    n = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def call():
+        vce.ce_shards_fwd_bwd_fused(shards, td, 0.1, reduce, loss=loss, n_valid=n, ws=ws)
+
+    def restore():
+        for sh, p in zip(shards, pristine):
+            sh.copy_(p)
+
+    say(f"[shards graph] eager reference reduce={reduce}")
+    call()
+    torch.cuda.synchronize()
+    ref_grads, ref_loss = [sh.clone() for sh in shards], loss.clone()
+    restore()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say(f"[shards graph] replay {rep}")
+        restore()
+        loss.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for sh, rg in zip(shards, ref_grads):
+            assert torch.equal(sh.view(torch.int16), rg.view(torch.int16)), f"replay {rep}: gradient differs"
+        assert torch.equal(loss.view(torch.int32), ref_loss.view(torch.int32)), f"replay {rep}: loss differs"
+        if rep == 1:
+            restore()
+            call()
+            torch.cuda.synchronize()
+    vce.ce_workspace_check(ws)
