@@ -1,14 +1,16 @@
 // A consumer of the C ABI with no Python and no torch: HIP device memory from
 // hipMalloc, libce.so's ce_workspace_init and ce_fwd_bwd_fused on the null
-// stream, checked against the FP64 oracle's C library (test infrastructure,
-// linked only here).  Written in plain C style; compiled with hipcc.
+// stream, then ce_shards_fwd_bwd_fused on the same logits held as three
+// separately allocated vocabulary shards, each checked against the FP64
+// oracle's C library (test infrastructure, linked only here).  Written in
+// plain C style; compiled with hipcc.
 //
 // Inputs: 2 x 37 rows of 5003 BF16 logits (a misaligned row length), label
 // smoothing 0.1, mean over the non-ignored rows, every ninth target ignored;
-// values from a fixed linear congruential generator.  Bar: n exact, loss
-// within 1e-4 max(1, |ref|), gradient within 2^-8 |ref| + 1e-7, ignored rows
-// +0.0.  Prints "c abi ok" and exits 0, or prints the first mismatch and
-// exits 1.
+// values from a fixed linear congruential generator; shards of 1668, 1668
+// and 1667 columns.  Bar: n exact, loss within 1e-4 max(1, |ref|), gradient
+// within 2^-8 |ref| + 1e-7, ignored rows +0.0.  Prints "c abi ok" and exits
+// 0, or prints the first mismatch and exits 1.
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -47,6 +49,35 @@ static float float_of_bf16(uint16_t b) {
   float f;
   memcpy(&f, &u, sizeof f);
   return f;
+}
+
+// n, the mean loss and every gradient element against the oracle's
+static int check(const char* what, int32_t n, float loss, int64_t n_ref, double mean_ref, const uint16_t* grad,
+                 const double* ref_grad, const int64_t* t, int64_t N, int64_t V, double* max_err) {
+  if ((int64_t)n != n_ref) {
+    printf("%s: n %d, oracle %lld\n", what, n, (long long)n_ref);
+    return 1;
+  }
+  if (!(fabs((double)loss - mean_ref) <= 1e-4 * fmax(1.0, fabs(mean_ref)))) {
+    printf("%s: mean loss %.9g, oracle %.9g\n", what, (double)loss, mean_ref);
+    return 1;
+  }
+  *max_err = 0.0;
+  for (int64_t i = 0; i < N * V; ++i) {
+    const int64_t r = i / V;
+    if (t[r] == -100 && grad[i] != 0) {
+      printf("%s: ignored row %lld element %lld is not +0.0\n", what, (long long)r, (long long)(i % V));
+      return 1;
+    }
+    const double g = (double)float_of_bf16(grad[i]), err = fabs(g - ref_grad[i]);
+    if (!(err <= ldexp(1.0, -8) * fabs(ref_grad[i]) + 1e-7)) {
+      printf("%s: gradient row %lld column %lld: %.9g, oracle %.9g\n", what, (long long)r, (long long)(i % V), g,
+             ref_grad[i]);
+      return 1;
+    }
+    if (err > *max_err) *max_err = err;
+  }
+  return 0;
 }
 
 int main(void) {
@@ -125,31 +156,62 @@ int main(void) {
     return 1;
   }
   const double mean_ref = or_mean_loss(ref_loss, N, n_ref);
-  if ((int64_t)n != n_ref) {
-    printf("n %d, oracle %lld\n", n, (long long)n_ref);
-    return 1;
-  }
-  if (!(fabs((double)loss - mean_ref) <= 1e-4 * fmax(1.0, fabs(mean_ref)))) {
-    printf("mean loss %.9g, oracle %.9g\n", (double)loss, mean_ref);
-    return 1;
-  }
   double max_err = 0.0;
-  for (int64_t i = 0; i < N * V; ++i) {
-    const int64_t r = i / V;
-    if (t[r] == -100 && grad[i] != 0) {
-      printf("ignored row %lld element %lld is not +0.0\n", (long long)r, (long long)(i % V));
-      return 1;
-    }
-    const double g = (double)float_of_bf16(grad[i]), err = fabs(g - ref_grad[i]);
-    if (!(err <= ldexp(1.0, -8) * fabs(ref_grad[i]) + 1e-7)) {
-      printf("gradient row %lld column %lld: %.9g, oracle %.9g\n", (long long)r, (long long)(i % V), g,
-             ref_grad[i]);
-      return 1;
-    }
-    if (err > max_err) max_err = err;
-  }
+  if (check("fused", n, loss, n_ref, mean_ref, grad, ref_grad, t, N, V, &max_err)) return 1;
   printf("c abi ok: n %d, mean loss %.6f (oracle %.6f), max gradient error %.2e\n", n, (double)loss, mean_ref,
          max_err);
+
+  // the same logits as three vocabulary shards in their own allocations
+  enum { S = 3 };
+  const int64_t width = (V + S - 1) / S;
+  void* dsh[S];
+  ce_logits sl[S];
+  for (int s = 0; s < S; ++s) {
+    const int64_t a = s * width, w = (a + width <= V ? width : V - a);
+    HIP_OK(hipMalloc(&dsh[s], sizeof(uint16_t) * (size_t)(N * w)));
+    HIP_OK(hipMemcpy2D(dsh[s], sizeof(uint16_t) * (size_t)w, x + a, sizeof(uint16_t) * (size_t)V,
+                       sizeof(uint16_t) * (size_t)w, (size_t)N, hipMemcpyHostToDevice));
+    memset(&sl[s], 0, sizeof sl[s]);
+    sl[s].data = dsh[s];
+    sl[s].dtype = CE_BF16;
+    sl[s].d0 = d0;
+    sl[s].d1 = d1;
+    sl[s].s0 = d1 * w;
+    sl[s].s1 = w;
+    sl[s].v_local = w;
+    sl[s].vocab_start = a;
+    sl[s].vocab_total = V;
+  }
+  const size_t sws_bytes = ce_shards_workspace_bytes(sl, S, &p);
+  void* dsws;
+  if (sws_bytes == 0) {
+    printf("ce_shards_workspace_bytes: %s\n", ce_last_error());
+    return 1;
+  }
+  HIP_OK(hipMalloc(&dsws, sws_bytes));
+  st = ce_workspace_init(dsws, sws_bytes, NULL);
+  if (st == CE_OK) st = ce_shards_fwd_bwd_fused(sl, S, &tl, &p, NULL, (float*)dloss, (int32_t*)dn, dsws, sws_bytes, NULL);
+  if (st != CE_OK) {
+    printf("%s: %s\n", ce_status_string(st), ce_last_error());
+    return 1;
+  }
+  HIP_OK(hipDeviceSynchronize());
+  if ((st = ce_workspace_check(dsws, NULL)) != CE_OK) {
+    printf("%s: %s\n", ce_status_string(st), ce_last_error());
+    return 1;
+  }
+  HIP_OK(hipMemcpy(&loss, dloss, sizeof loss, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(&n, dn, sizeof n, hipMemcpyDeviceToHost));
+  for (int s = 0; s < S; ++s) {
+    const int64_t a = s * width, w = sl[s].v_local;
+    HIP_OK(hipMemcpy2D(grad + a, sizeof(uint16_t) * (size_t)V, dsh[s], sizeof(uint16_t) * (size_t)w,
+                       sizeof(uint16_t) * (size_t)w, (size_t)N, hipMemcpyDeviceToHost));
+  }
+  if (check("shards", n, loss, n_ref, mean_ref, grad, ref_grad, t, N, V, &max_err)) return 1;
+  printf("c abi ok (3 shards): n %d, mean loss %.6f (oracle %.6f), max gradient error %.2e\n", n, (double)loss,
+         mean_ref, max_err);
+  for (int s = 0; s < S; ++s) hipFree(dsh[s]);
+  hipFree(dsws);
   hipFree(dx);
   hipFree(dt);
   hipFree(dloss);

@@ -1,8 +1,9 @@
 """The C ABI used from a program with no Python and no torch
 (tests/c_abi/fused_from_c.cpp, built by __graft_entry__.build()): HIP memory
 from hipMalloc, ce_workspace_init and ce_fwd_bwd_fused on the null stream,
-checked inside the program against the oracle's C library.  Run here as a
-child process."""
+then ce_shards_fwd_bwd_fused on the same logits in three separately
+allocated shards, each checked inside the program against the oracle's C
+library.  Run here as a child process."""
 import os
 import subprocess
 
@@ -20,4 +21,4 @@ def test_fused_call_from_c():
     say("[c abi] running tests/c_abi/fused_from_c")
     r = subprocess.run([BIN], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=120)
     say(r.stdout.strip())
-    assert r.returncode == 0 and "c abi ok" in r.stdout, r.stdout
+    assert r.returncode == 0 and "c abi ok:" in r.stdout and "c abi ok (3 shards)" in r.stdout, r.stdout
