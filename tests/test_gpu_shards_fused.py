@@ -260,3 +260,24 @@ def test_shards_graph_replays(reduce):
             call()
             torch.cuda.synchronize()
     vce.ce_workspace_check(ws)
+
+
+SHORT = [(V, S, a, sm) for V, S, a, sm in ((3, 3, 1.0, "others"), (17, 13, 0.45, "all"), (64, 16, 0.3, "others"),
+                                           (64, 2, 0.0, "all"), (40, 5, 0.8, "all"))]
+
+
+@pytest.mark.parametrize("V,S,alpha,smoothing", SHORT, ids=[f"V{c[0]}-S{c[1]}-a{c[2]}-{c[3]}" for c in SHORT])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_short_vocabulary_shards(V, S, alpha, smoothing, dtype):
+    """A whole vocabulary of at most 64 columns across the shards takes the
+    FP64 path (one wave per row gathers its columns from the shards): with few
+    columns and heavy smoothing p sits close to a large q, where one FP32
+    rounding of p already exceeds the FP32 gradient's absolute floor."""
+    g = torch.Generator().manual_seed(V * 31 + S)
+    x = (torch.randn((2, 42, V), generator=g) * 6).to(dtype)
+    t = workloads.random_targets((2, 42), V, seed=V + S, ignore_frac=0.1)
+    bounds = workloads.shard_bounds(V, S) if V % S else [(i * (V // S), (i + 1) * (V // S)) for i in range(S)]
+    gr = np.random.default_rng(V).uniform(-2.0, 2.0, 84).astype(np.float32).astype(np.float64)
+    for reduce, gg in (("none", gr), ("mean", 1.3), ("sum", None)):
+        check_shards(x, t, bounds, alpha, reduce, g=gg, smoothing=smoothing, separate=reduce == "none",
+                     what=f"short V={V} S={len(bounds)}")

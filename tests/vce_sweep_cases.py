@@ -1,0 +1,96 @@
+"""Seeded random configurations for the GPU sweep (tests/test_gpu_sweep.py).
+
+Inputs only: logits, targets, options and shard cut points, drawn from
+numpy/torch generators seeded by the case number; nothing of the method's
+arithmetic.  Sizes stay at most MAX_ELEMS logits per case, so the FP64 oracle
+checks every element of every case in well under a second.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import workloads
+
+N_FUSED = 40
+N_SHARDS = 24
+MAX_ELEMS = 1_500_000
+MAX_V = 200_000
+MAX_CHUNK_VECS = 4096   # one chunk of the fused call holds at most this many 16-byte vectors
+MAX_CHUNKS = 64         # chunks per row
+
+
+def elems_per_vector(dtype) -> int:
+    return 8 if dtype == torch.bfloat16 else 4
+
+
+def _draw_common(rng: np.random.Generator, v_min: int = 1):
+    dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    V = int(round(math.exp(rng.uniform(math.log(max(v_min, 1)), math.log(MAX_V)))))
+    V = max(v_min, min(MAX_V, V))
+    rows_cap = max(1, min(96, MAX_ELEMS // V))
+    rows = int(rng.integers(1, rows_cap + 1))
+    A = int(rng.integers(1, 5))
+    A = min(A, rows)
+    B = max(1, rows // A)
+    kind = str(rng.choice(["contiguous", "padded", "misaligned", "transposed"]))
+    pad = int(rng.integers(1, 40)) if kind in ("padded", "misaligned") else 0
+    off = int(rng.integers(1, 8)) if kind == "misaligned" else 0
+    sigma = float(rng.choice([0.5, 2.0, 6.0]))
+    ignore_frac = float(rng.choice([0.0, 0.1, 0.5, 1.0], p=[0.3, 0.45, 0.2, 0.05]))
+    alpha = 0.0 if rng.random() < 0.3 else float(np.float32(rng.uniform(0.01, 0.5)))
+    smoothing = "others" if rng.random() < 0.35 else "all"
+    if smoothing == "others" and V == 1 and alpha > 0:
+        smoothing = "all"
+    reduce = str(rng.choice(["none", "mean", "sum"]))
+    rows = A * B
+    if reduce == "none":
+        g = None if rng.random() < 0.3 else rng.uniform(-2.0, 2.0, rows).astype(np.float32).astype(np.float64)
+    else:
+        g = None if rng.random() < 0.3 else float(np.float32(rng.uniform(-2.0, 2.0)))
+    seed = int(rng.integers(0, 2**31 - 1))
+    gen = torch.Generator().manual_seed(seed)
+    phys = (torch.randn((A, B, V + pad + off), generator=gen) * sigma).to(dtype)
+    x = phys[..., off:off + V]
+    t = workloads.random_targets((A, B), V, seed=seed, ignore_frac=ignore_frac)
+    if kind == "transposed":
+        x, t = x.transpose(0, 1), t.transpose(0, 1)
+    what = (f"{'bf16' if dtype == torch.bfloat16 else 'f32'} V={V} rows={rows} {kind} sigma={sigma} "
+            f"ignored={ignore_frac} a={alpha} {smoothing} {reduce} g={'1' if g is None else 'drawn'}")
+    return dict(x=x, t=t, alpha=alpha, smoothing=smoothing, reduce=reduce, g=g, dtype=dtype, V=V, what=what)
+
+
+def fused_case(seed: int) -> dict:
+    rng = np.random.default_rng(1000 + seed)
+    c = _draw_common(rng)
+    nv = c["V"] // elems_per_vector(c["dtype"])
+    K = 0
+    if c["V"] > 64 and rng.random() < 0.35:  # rows of at most 64 columns take the FP64 whole-row path
+        lo = max(1, -(-nv // MAX_CHUNK_VECS))
+        hi = min(MAX_CHUNKS, nv)
+        if hi >= lo:
+            K = int(rng.integers(lo, hi + 1))
+    c["K"] = K
+    c["what"] += f" K={K}"
+    return c
+
+
+def shard_case(seed: int) -> dict:
+    rng = np.random.default_rng(5000 + seed)
+    c = _draw_common(rng, v_min=2)
+    V, E = c["V"], elems_per_vector(c["dtype"])
+    S = int(rng.integers(1, min(16, V) + 1))
+    while True:
+        cuts = np.sort(rng.choice(np.arange(1, V), size=S - 1, replace=False)) if S > 1 else np.array([], int)
+        edges = [0] + [int(v) for v in cuts] + [V]
+        widest = max(b - a for a, b in zip(edges[:-1], edges[1:]))
+        kper = max(1, -(-(widest // E) // MAX_CHUNK_VECS))
+        if S * kper <= MAX_CHUNKS:
+            break
+        S = max(1, S // 2)
+    c["bounds"] = list(zip(edges[:-1], edges[1:]))
+    c["separate"] = bool(rng.random() < 0.5)
+    c["what"] += f" S={S} widths={[b - a for a, b in c['bounds']][:6]}{'...' if S > 6 else ''}"
+    return c

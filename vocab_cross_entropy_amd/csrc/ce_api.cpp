@@ -419,6 +419,7 @@ struct ShardPlan {
   int32_t kper = 0, K = 0;
   int64_t C = 0;
   vce::FusedShape shape{0, 0};
+  bool short_rows = false;  // a vocabulary of at most kShortRow columns: one wave per row, FP64
 };
 
 ce_status shard_plan(const ce_logits* shards, int32_t S, const ce_params* p, ShardPlan* out) {
@@ -455,6 +456,15 @@ ce_status shard_plan(const ce_logits* shards, int32_t S, const ce_params* p, Sha
   if (pl.C < 1) pl.C = 1;
   pl.shape = vce::fused_shape_for(pl.C);
   if (pl.shape.threads == 1024 || pl.shape.vecs == 16) pl.shape = vce::FusedShape{512, 8};  // C <= 4096 here
+  if (shards[0].vocab_total <= vce::kShortRow) {
+    // FP32 cannot hold s (p - q) where p sits close to a large q (few columns,
+    // heavy smoothing): the whole row goes to one wave, which gathers its
+    // columns from the shards and works in FP64, as unsharded short rows do
+    pl.short_rows = true;
+    pl.kper = pl.K = 1;
+    pl.C = 1;
+    pl.shape = vce::FusedShape{256, 1};
+  }
   const int64_t N = shards[0].d0 * shards[0].d1;
   if (N * pl.K > kMaxGrid) return fail(CE_EINVAL, "rows x chunks exceeds the launch grid");
   *out = pl;
@@ -515,8 +525,10 @@ ce_status ce_shards_fwd_bwd_fused(const ce_logits* shards, int32_t S, const ce_t
   if (a.slice_rows < 2048) a.slice_rows = 2048;
   a.nslice = (int32_t)((N + a.slice_rows - 1) / a.slice_rows);
   a.ws_bytes = w.total;
-  a.short_rows = 0;
-  a.q_o_d = a.q_t_d = 0.0;
+  a.short_rows = pl.short_rows ? 1 : 0;
+  const Smoothing q = smoothing_of(p, shards[0].vocab_total);
+  a.q_o_d = q.q_o;
+  a.q_t_d = q.q_t;
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
   if ((e = vce::launch_fused_shards(a, ss, pl.shape, stream, e0, e1))) return hip_fail(e, "sharded fused launch");

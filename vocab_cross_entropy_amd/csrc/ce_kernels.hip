@@ -613,16 +613,15 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
-template <int DT, int T>
-__device__ void fused_short_row(const FusedArgs& a, uint32_t tag, int64_t r, const Row<DT>& g) {
+// The arithmetic of a short row held by wave 0, one column per lane (global
+// column index = lane; `in` marks lanes inside the row, `x` their logit):
+// publishes the row's loss and returns the lane's gradient.
+template <int T>
+__device__ double short_row_grad(const FusedArgs& a, uint32_t tag, int64_t r, int64_t t, bool in, double x) {
   const int lane = threadIdx.x;
-  if (lane >= 64) return;  // wave 0 holds the row
   const RowLayout& L = a.L;
   const bool ws_ok = (a.hdr->magic == kWsMagic) & (a.hdr->init_bytes >= a.ws_bytes);
-  const Rsrc rx = make_rsrc(g.base, L.V * ElemT<DT>::EB);  // lanes past the row read 0, their stores drop
-  const bool in = lane < L.V;
-  const double x = (double)bload_elem<DT>(rx, lane);
-  const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
+  const bool tvalid = t >= 0 && t < L.vocab_total;
 
   // s = g_r, g / n (the mean; n from the slice counts) or g (the sum)
   double s = a.g ? (double)a.g[a.reduce ? 0 : r] : 1.0;
@@ -639,15 +638,52 @@ __device__ void fused_short_row(const FusedArgs& a, uint32_t tag, int64_t r, con
   const double m = wave_max_d(in ? x : -INFINITY);
   const double d = wave_sum_d(in ? exp(x - m) : 0.0);
   const double R = wave_sum_d(in ? x : 0.0);
-  const double y = wave_sum_d(lane == g.t ? x : 0.0);
+  const double y = wave_sum_d(lane == t ? x : 0.0);
   const double lse = m + log(d);
   double loss = lse;  // zero-weight terms left out, as in row_loss_of
   if (a.q_t_d != a.q_o_d) loss -= (a.q_t_d - a.q_o_d) * y;
   if (a.q_o_d != 0.0) loss -= a.q_o_d * R;
-  const double q = lane == g.t ? a.q_t_d : a.q_o_d;
-  const double gr = tvalid ? s * (exp(x - lse) - q) : __builtin_nan("");
-  bstore_elem<DT>((float)gr, rx, lane);
+  const double q = lane == t ? a.q_t_d : a.q_o_d;
   publish_row_loss<T>(a, tag, r, tvalid && ws_ok ? (float)loss : __uint_as_float(0x7fc00000u), true);
+  return tvalid ? s * (exp(x - lse) - q) : __builtin_nan("");
+}
+
+template <int DT, int T>
+__device__ void fused_short_row(const FusedArgs& a, uint32_t tag, int64_t r, const Row<DT>& g) {
+  const int lane = threadIdx.x;
+  if (lane >= 64) return;  // wave 0 holds the row
+  const Rsrc rx = make_rsrc(g.base, a.L.V * ElemT<DT>::EB);  // lanes past the row read 0, their stores drop
+  const bool in = lane < a.L.V;
+  const double x = (double)bload_elem<DT>(rx, lane);
+  const double gr = short_row_grad<T>(a, tag, r, g.t, in, x);
+  bstore_elem<DT>((float)gr, rx, lane);
+}
+
+// The same for a short row held as vocabulary shards: lane j gathers global
+// column j from the shard that holds it (a per-lane address, so plain loads
+// and stores rather than one buffer range).  Ignored rows store +0.0 in
+// every shard's piece, loss 0.
+template <int DT, int T>
+__device__ void fused_short_row_shards(const FusedArgs& a, uint32_t tag, int64_t r, int64_t t, const ShardSet* ss) {
+  constexpr int EB = ElemT<DT>::EB;
+  const int lane = threadIdx.x;
+  if (lane >= 64) return;
+  const int64_t i0 = r / a.L.d1, i1 = r - i0 * a.L.d1;
+  char* p = nullptr;
+  for (int k = 0; k < ss->S; ++k) {
+    const RowLayout& Ls = ss->L[k];
+    if (lane >= Ls.vocab_start && lane < Ls.vocab_start + Ls.V)
+      p = Ls.x + (i0 * Ls.s0 + i1 * Ls.s1 + (lane - Ls.vocab_start)) * EB;
+  }
+  const bool in = p != nullptr;
+  if (t == a.L.ignore_idx) {
+    if (in) store_elem<DT>(p, 0, 0.f);
+    publish_row_loss<T>(a, tag, r, 0.f, true);
+    return;
+  }
+  const double x = in ? (double)load_elem<DT>(p, 0) : 0.0;
+  const double gr = short_row_grad<T>(a, tag, r, t, in, x);
+  if (in) store_elem<DT>(p, 0, (float)gr);
 }
 
 // --------------------------------------------------------------------------
@@ -724,7 +760,9 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
   const bool first = (kb == 0), last = (kb == kper - 1);  // the buffer's head and tail
   const bool row_first = (k == 0);                      // the row's loss is published once
 
-  if (g.t == L.ignore_idx) {  // ignored row: +0.0 gradient, loss 0, nothing read
+  if (SH && P == 1 && a.short_rows) {  // a vocabulary of at most 64 columns across the shards
+    if constexpr (SH && P == 1) fused_short_row_shards<DT, T>(a, tag, r, g.t, ss);
+  } else if (g.t == L.ignore_idx) {  // ignored row: +0.0 gradient, loss 0, nothing read
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     for (int i = tid; i < nvc; i += T) body[i] = z;
     if (HT) {
