@@ -357,10 +357,14 @@ def test_shards_fused_rejects_before_any_hip_call(lib, name, case, status):
 
 
 def test_shards_workspace_sizes(lib):
-    h = Host()
+    h = Host(V=200)
     p = h.params()
-    one = lib.ce_shards_workspace_bytes(_shard_set(h, [16]), 1, ctypes.byref(p))
-    two = lib.ce_shards_workspace_bytes(_shard_set(h, [8, 8]), 2, ctypes.byref(p))
+    one = lib.ce_shards_workspace_bytes(_shard_set(h, [200]), 1, ctypes.byref(p))
+    two = lib.ce_shards_workspace_bytes(_shard_set(h, [100, 100]), 2, ctypes.byref(p))
     assert 0 < one < two  # a second shard adds exchange slots per row
+    # a vocabulary of at most 64 columns is one item per row (FP64, gathered): no exchange slots
+    h = Host()
+    assert (lib.ce_shards_workspace_bytes(_shard_set(h, [8, 8]), 2, ctypes.byref(p))
+            == lib.ce_shards_workspace_bytes(_shard_set(h, [16]), 1, ctypes.byref(p)) > 0)
     # 16 shards is the most; up to 64 chunks per row in all
     assert lib.ce_shards_workspace_bytes(_shard_set(h, [1] * 16), 16, ctypes.byref(p)) > 0
