@@ -1,13 +1,15 @@
-"""A seeded random sweep of the one-launch calls against the FP64 oracle.
+"""A seeded random sweep of every entry point against the FP64 oracle.
 
 Each case draws its dtype, vocabulary size (1 to 200000, log-uniform), rows,
 memory layout (contiguous, padded rows, a misaligned first column, the
 transposed (SQ, B) view), share of ignored rows (none to all), smoothing
 convention and weight, reduction, upstream gradient and chunk split, then runs
-ce_fwd_bwd_fused, or ce_shards_fwd_bwd_fused over 1 to 16 shards cut at random
-columns, and compares loss, n and every gradient element with the oracle at
-the stated bar.  The cases are fixed by their seeds, so a failure names a
-reproducible case.
+ce_fwd_bwd_fused; ce_shards_fwd_bwd_fused over 1 to 16 shards cut at random
+columns; ce_forward + ce_backward_inplace; or the three-call shard flow, and
+compares loss, n, lse and every gradient element with the oracle at the stated
+bar (the calls that rebuild the gradient from an FP32 lse with that hand-off's
+allowance at the target element).  The cases are fixed by their seeds, so a
+failure names a reproducible case.
 """
 import math
 
@@ -15,8 +17,9 @@ import numpy as np
 import pytest
 import torch
 
+import vocab_cross_entropy_amd as vce
 import vce_sweep_cases as cases
-from gpu_util import say
+from gpu_util import assert_grad_from_lse, assert_loss, orc, rows_f64, say, to_device_view
 from test_gpu_parity import check_fused
 from test_gpu_shards_fused import check_shards
 
@@ -37,3 +40,78 @@ def test_shards_sweep(seed):
     say(f"[sweep shards] seed {seed}: {c['what']}")
     check_shards(c["x"], c["t"], c["bounds"], c["alpha"], c["reduce"], g=c["g"], smoothing=c["smoothing"],
                  separate=c["separate"], what=c["what"])
+
+
+def _g_dev(g, reduce, N):
+    if reduce == "none":
+        return torch.as_tensor(np.ones(N) if g is None else np.asarray(g), dtype=torch.float32).cuda()
+    return torch.tensor([1.0 if g is None else float(g)], dtype=torch.float32, device="cuda")
+
+
+def _scale(g, reduce, N, n):
+    if reduce == "none":
+        return np.ones(N) if g is None else np.asarray(g, np.float64)
+    gg = 1.0 if g is None else float(g)
+    return np.full(N, gg / n if reduce == "mean" else gg) if (reduce != "mean" or n) else np.full(N, np.nan)
+
+
+def _check_loss(loss, ref_rows, reduce, n, o, what):
+    if reduce == "none":
+        assert_loss(loss.cpu().numpy().astype(np.float64), ref_rows, what + " rows")
+    elif reduce == "mean" and n == 0:
+        assert math.isnan(loss.item())
+    else:
+        assert_loss([loss.item()], [o.reduce(ref_rows, reduce, n)], f"{what} {reduce}")
+
+
+@pytest.mark.parametrize("seed", range(cases.N_SPLIT))
+def test_forward_backward_sweep(seed):
+    c = cases.split_case(seed)
+    x, t, a, red, sm = c["x"], c["t"], c["alpha"], c["reduce"], c["smoothing"]
+    N = t.numel()
+    say(f"[sweep fwd+bwd] seed {seed}: {c['what']}")
+    xd, td = to_device_view(x), to_device_view(t)
+    loss, lse, n = vce.ce_forward(xd, td, a, red, smoothing=sm)
+    vce.ce_backward_inplace(xd, td, lse, a, red, grad_out=_g_dev(c["g"], red, N), n_valid=n, smoothing=sm)
+    torch.cuda.synchronize()
+    o = orc()
+    n_ref = o.count_valid(t)
+    assert int(n.item()) == n_ref
+    ref_rows, ref_lse = o.loss_rows(x, t, a, smoothing=sm)
+    _check_loss(loss, ref_rows, red, n_ref, o, c["what"])
+    kept = t.reshape(-1).numpy() != -100
+    assert_loss(lse.cpu().numpy()[kept], ref_lse[kept], c["what"] + " lse")
+    ref = o.grad_rows(x, t, a, reduce_loss=red, g=c["g"], n_valid=n_ref, smoothing=sm)
+    tl = t.reshape(-1).numpy()
+    assert_grad_from_lse(rows_f64(xd), ref, x.dtype, lse.cpu().numpy(), np.where(kept, tl, -1),
+                         _scale(c["g"], red, N, n_ref), c["what"] + " grad")
+
+
+@pytest.mark.parametrize("seed", range(cases.N_SHARD_FLOW))
+def test_shard_flow_sweep(seed):
+    c = cases.shard_flow_case(seed)
+    x, t, a, red, sm, bounds = c["x"], c["t"], c["alpha"], c["reduce"], c["smoothing"], c["bounds"]
+    N, V = t.numel(), c["V"]
+    say(f"[sweep shard flow] seed {seed}: {c['what']}")
+    td = to_device_view(t)
+    shards = [x[..., lo:hi].contiguous().cuda() for lo, hi in bounds]
+    stats = torch.empty((len(bounds), N, 4), dtype=torch.float32, device="cuda")
+    for s, (lo, hi) in enumerate(bounds):
+        vce.ce_shard_partial_stats(shards[s], td, lo, V, stats=stats[s])
+    loss, lse, n = vce.ce_shard_combine(stats, td, V, a, red, smoothing=sm)
+    for s, (lo, hi) in enumerate(bounds):
+        vce.ce_backward_inplace(shards[s], td, lse, a, red, grad_out=_g_dev(c["g"], red, N), n_valid=n,
+                                vocab_start=lo, vocab_total=V, smoothing=sm)
+    torch.cuda.synchronize()
+    o = orc()
+    n_ref = o.count_valid(t)
+    assert int(n.item()) == n_ref
+    ref_rows, _ = o.loss_rows(x, t, a, smoothing=sm)
+    _check_loss(loss, ref_rows, red, n_ref, o, c["what"])
+    ref = o.grad_rows(x, t, a, reduce_loss=red, g=c["g"], n_valid=n_ref, smoothing=sm)
+    tl = t.reshape(-1).numpy()
+    sc = _scale(c["g"], red, N, n_ref)
+    for s, (lo, hi) in enumerate(bounds):
+        local = np.where((tl >= lo) & (tl < hi), tl - lo, -1)
+        assert_grad_from_lse(rows_f64(shards[s]), ref[:, lo:hi], x.dtype, lse.cpu().numpy(), local, sc,
+                             f"{c['what']} shard {s}")

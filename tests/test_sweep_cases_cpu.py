@@ -49,3 +49,13 @@ def test_shard_cases_valid():
 def test_cases_are_reproducible():
     a, b = cases.fused_case(7), cases.fused_case(7)
     assert torch.equal(a["x"], b["x"]) and torch.equal(a["t"], b["t"]) and a["what"] == b["what"]
+
+
+def test_split_and_shard_flow_cases_valid():
+    for seed in range(cases.N_SPLIT):
+        _check_common(cases.split_case(seed))
+    for seed in range(cases.N_SHARD_FLOW):
+        c = cases.shard_flow_case(seed)
+        _check_common(c)
+        b = c["bounds"]
+        assert b[0][0] == 0 and b[-1][1] == c["V"] and all(lo < hi for lo, hi in b) and len(b) <= 16

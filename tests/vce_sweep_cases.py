@@ -16,6 +16,8 @@ import workloads
 
 N_FUSED = 40
 N_SHARDS = 24
+N_SPLIT = 24       # ce_forward + ce_backward_inplace
+N_SHARD_FLOW = 16  # ce_shard_partial_stats per shard, ce_shard_combine, ce_backward_inplace per shard
 MAX_ELEMS = 1_500_000
 MAX_V = 200_000
 MAX_CHUNK_VECS = 4096   # one chunk of the fused call holds at most this many 16-byte vectors
@@ -93,4 +95,20 @@ def shard_case(seed: int) -> dict:
     c["bounds"] = list(zip(edges[:-1], edges[1:]))
     c["separate"] = bool(rng.random() < 0.5)
     c["what"] += f" S={S} widths={[b - a for a, b in c['bounds']][:6]}{'...' if S > 6 else ''}"
+    return c
+
+
+def split_case(seed: int) -> dict:
+    return _draw_common(np.random.default_rng(9000 + seed))
+
+
+def shard_flow_case(seed: int) -> dict:
+    rng = np.random.default_rng(12000 + seed)
+    c = _draw_common(rng, v_min=2)
+    V = c["V"]
+    S = int(rng.integers(1, min(16, V) + 1))
+    cuts = np.sort(rng.choice(np.arange(1, V), size=S - 1, replace=False)) if S > 1 else np.array([], int)
+    edges = [0] + [int(v) for v in cuts] + [V]
+    c["bounds"] = list(zip(edges[:-1], edges[1:]))
+    c["what"] += f" S={S}"
     return c
