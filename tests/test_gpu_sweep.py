@@ -5,7 +5,8 @@ memory layout (contiguous, padded rows, a misaligned first column, the
 transposed (SQ, B) view), share of ignored rows (none to all), smoothing
 convention and weight, reduction, upstream gradient and chunk split, then runs
 ce_fwd_bwd_fused; ce_shards_fwd_bwd_fused over 1 to 16 shards cut at random
-columns; ce_forward + ce_backward_inplace; or the three-call shard flow, and
+columns; ce_forward + ce_backward_inplace; the three-call shard flow; or the
+chunked linear head (on the linear tests' grid-valued inputs), and
 compares loss, n, lse and every gradient element with the oracle at the stated
 bar (the calls that rebuild the gradient from an FP32 lse with that hand-off's
 allowance at the target element).  The cases are fixed by their seeds, so a
@@ -115,3 +116,13 @@ def test_shard_flow_sweep(seed):
         local = np.where((tl >= lo) & (tl < hi), tl - lo, -1)
         assert_grad_from_lse(rows_f64(shards[s]), ref[:, lo:hi], x.dtype, lse.cpu().numpy(), local, sc,
                              f"{c['what']} shard {s}")
+
+
+@pytest.mark.parametrize("seed", range(cases.N_LINEAR))
+def test_linear_sweep(seed):
+    from test_gpu_linear import check_linear, grid_inputs
+    c = cases.linear_case(seed)
+    say(f"[sweep linear] seed {seed}: {c['what']}")
+    h, w, t = grid_inputs(c["N"], c["D"], c["V"], c["dtype"], seed=c["seed"], ignore_frac=c["ignore_frac"])
+    check_linear(h, w, t, c["alpha"], c["reduce"], g=c["g"], chunk_rows=c["chunk"], smoothing=c["smoothing"],
+                 what=c["what"], want_dh=c["want_dh"], want_dw=c["want_dw"], h_pad=c["h_pad"])

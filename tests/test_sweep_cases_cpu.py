@@ -59,3 +59,11 @@ def test_split_and_shard_flow_cases_valid():
         _check_common(c)
         b = c["bounds"]
         assert b[0][0] == 0 and b[-1][1] == c["V"] and all(lo < hi for lo, hi in b) and len(b) <= 16
+
+
+def test_linear_cases_valid():
+    for seed in range(cases.N_LINEAR):
+        c = cases.linear_case(seed)
+        assert 1 <= c["N"] <= 96 and 1 <= c["D"] <= 256 and 1 <= c["V"] <= 20000 and c["chunk"] >= 0
+        assert c["want_dh"] or c["want_dw"]
+        assert not (c["smoothing"] == "others" and c["V"] == 1 and c["alpha"] > 0)

@@ -18,6 +18,7 @@ N_FUSED = 40
 N_SHARDS = 24
 N_SPLIT = 24       # ce_forward + ce_backward_inplace
 N_SHARD_FLOW = 16  # ce_shard_partial_stats per shard, ce_shard_combine, ce_backward_inplace per shard
+N_LINEAR = 12      # ce_linear_cross_entropy (grid-valued inputs: see linear_case)
 MAX_ELEMS = 1_500_000
 MAX_V = 200_000
 MAX_CHUNK_VECS = 4096   # one chunk of the fused call holds at most this many 16-byte vectors
@@ -112,3 +113,28 @@ def shard_flow_case(seed: int) -> dict:
     c["bounds"] = list(zip(edges[:-1], edges[1:]))
     c["what"] += f" S={S}"
     return c
+
+
+def linear_case(seed: int) -> dict:
+    """Sizes and options of the chunked head; the inputs themselves are the
+    linear tests' grid values (h = k/8, W = m/64), whose products are exact in
+    FP32 in any order, so the library's logits equal the oracle's."""
+    rng = np.random.default_rng(15000 + seed)
+    dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    N = int(rng.integers(1, 97))
+    D = int(rng.integers(1, 257))
+    V = int(round(math.exp(rng.uniform(0.0, math.log(20000)))))
+    chunk = int(rng.choice([0, 1, int(rng.integers(1, N + 1)), N + 5]))
+    alpha = 0.0 if rng.random() < 0.3 else float(np.float32(rng.uniform(0.01, 0.5)))
+    smoothing = "others" if (rng.random() < 0.35 and not (V == 1 and alpha > 0)) else "all"
+    reduce = str(rng.choice(["none", "mean", "sum"]))
+    g = (rng.uniform(0.2, 2.0, N).astype(np.float32).astype(np.float64) if reduce == "none"
+         else float(np.float32(rng.uniform(0.2, 2.0))))
+    ignore_frac = float(rng.choice([0.0, 0.2, 1.0], p=[0.3, 0.6, 0.1]))
+    want = str(rng.choice(["both", "dh", "dw"], p=[0.6, 0.2, 0.2]))
+    h_pad = int(rng.choice([0, 0, 5]))
+    what = (f"{'bf16' if dtype == torch.bfloat16 else 'f32'} N={N} D={D} V={V} chunk={chunk} a={alpha} "
+            f"{smoothing} {reduce} ignored={ignore_frac} want={want} pad={h_pad}")
+    return dict(dtype=dtype, N=N, D=D, V=V, chunk=chunk, alpha=alpha, smoothing=smoothing, reduce=reduce, g=g,
+                ignore_frac=ignore_frac, want_dh=want != "dw", want_dw=want != "dh", h_pad=h_pad,
+                seed=int(rng.integers(0, 2**31 - 1)), what=what)
