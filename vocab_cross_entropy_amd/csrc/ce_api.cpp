@@ -344,14 +344,17 @@ ce_status fused_plan(const ce_logits* x, const ce_params* p, int32_t* K_out, int
 
 namespace {
 
-ce_status fused_call(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* grad_out,
-                     float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
+// What both fused launches share: the targets, loss and workspace checks,
+// the workspace regions, the target slices counted by the first workgroups,
+// and the smoothing in double.  With no rows it writes n = 0 (and the mean
+// or sum of nothing) itself and sets *launch = false.  L0 is the layout of
+// the logits (the first shard for the shard call); K the chunks per row.
+ce_status fused_common(const ce_logits* L0, const ce_targets* t, const ce_params* p, int32_t K, int64_t C,
+                       const float* grad_out, float* loss, int32_t* n_valid, void* ws, size_t ws_bytes,
+                       hipStream_t stream, vce::FusedArgs* a, bool* launch) {
   ce_status st;
-  int32_t K = 0;
-  int64_t C = 0;
-  vce::FusedShape shape{0, 0};
-  if ((st = vce::fused_plan(x, p, &K, &C, &shape))) return st;
-  const int64_t N = x->d0 * x->d1;
+  *launch = false;
+  const int64_t N = L0->d0 * L0->d1;
   if ((st = check_targets(t, N))) return st;
   if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
   const WsLayout w = ws_layout(N, K, p->reduce_loss != 0, true);
@@ -369,34 +372,51 @@ ce_status fused_call(const ce_logits* x, const ce_targets* t, const ce_params* p
       return hip_fail(e, "mean launch");
     return CE_OK;
   }
-  vce::FusedArgs a;
-  a.L = row_layout(x, t, p);
-  a.K = K;
-  a.aligned = rows_aligned16(x);
-  a.C = C;
-  a.reduce = p->reduce_loss;
-  a.g = grad_out;
-  a.n_out = n_valid;
-  a.row_loss = p->reduce_loss ? nullptr : loss;
-  a.row_loss_tagged = reinterpret_cast<unsigned long long*>(wsb + w.row_loss_tagged);
-  a.mean_out = p->reduce_loss ? loss : nullptr;
-  a.hdr = hdr;
-  a.slots = K > 1 ? reinterpret_cast<unsigned long long*>(wsb + w.slots) : nullptr;
+  a->L = row_layout(L0, t, p);
+  a->K = K;
+  a->aligned = 0;
+  a->C = C;
+  a->reduce = p->reduce_loss;
+  a->g = grad_out;
+  a->n_out = n_valid;
+  a->row_loss = p->reduce_loss ? nullptr : loss;
+  a->row_loss_tagged = reinterpret_cast<unsigned long long*>(wsb + w.row_loss_tagged);
+  a->mean_out = p->reduce_loss ? loss : nullptr;
+  a->hdr = hdr;
+  a->slots = K > 1 ? reinterpret_cast<unsigned long long*>(wsb + w.slots) : nullptr;
   // at most kMaxSlices target slices of at least 2048 rows, counted by the first workgroups
-  a.slice_rows = (N + vce::kMaxSlices - 1) / vce::kMaxSlices;
-  if (a.slice_rows < 2048) a.slice_rows = 2048;
-  a.nslice = (int32_t)((N + a.slice_rows - 1) / a.slice_rows);
-  a.ws_bytes = w.total;
+  a->slice_rows = (N + vce::kMaxSlices - 1) / vce::kMaxSlices;
+  if (a->slice_rows < 2048) a->slice_rows = 2048;
+  a->nslice = (int32_t)((N + a->slice_rows - 1) / a->slice_rows);
+  a->ws_bytes = w.total;
+  a->short_rows = 0;
+  const Smoothing q = smoothing_of(p, L0->vocab_total);
+  a->q_o_d = q.q_o;
+  a->q_t_d = q.q_t;
+  *launch = true;
+  return CE_OK;
+}
+
+ce_status fused_call(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* grad_out,
+                     float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ce_status st;
+  int32_t K = 0;
+  int64_t C = 0;
+  vce::FusedShape shape{0, 0};
+  if ((st = vce::fused_plan(x, p, &K, &C, &shape))) return st;
+  vce::FusedArgs a;
+  bool launch;
+  if ((st = fused_common(x, t, p, K, C, grad_out, loss, n_valid, ws, ws_bytes, stream, &a, &launch)) || !launch)
+    return st;
+  a.aligned = rows_aligned16(x);
   // short whole rows take the FP64 path of the 256 x 1 kernel (its only shape for them)
   a.short_rows = x->v_local <= vce::kShortRow && K == 1;
   if (a.short_rows && (shape.threads != 256 || shape.vecs != 1))
     return fail(CE_ELAYOUT, "internal: rows of %lld columns planned on a %d x %d workgroup", (long long)x->v_local,
                 shape.threads, shape.vecs);
-  const Smoothing q = smoothing_of(p, x->vocab_total);
-  a.q_o_d = q.q_o;
-  a.q_t_d = q.q_t;
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
+  hipError_t e;
   if ((e = vce::launch_fused(a, shape, stream, e0, e1))) return hip_fail(e, "fused launch");
   return CE_OK;
 }
@@ -485,52 +505,20 @@ ce_status ce_shards_fwd_bwd_fused(const ce_logits* shards, int32_t S, const ce_t
   ce_status st;
   ShardPlan pl;
   if ((st = shard_plan(shards, S, p, &pl))) return st;
-  const int64_t N = shards[0].d0 * shards[0].d1;
-  if ((st = check_targets(t, N))) return st;
-  if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
-  const WsLayout w = ws_layout(N, pl.K, p->reduce_loss != 0, true);
-  if (!ws || ws_bytes < w.total)
-    return fail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
-  if (((uintptr_t)ws) % 256u) return fail(CE_EWORKSPACE, "workspace must be 256-byte aligned");
-
-  char* wsb = static_cast<char*>(ws);
-  auto* hdr = reinterpret_cast<vce::WsHeader*>(wsb);
-  hipError_t e;
-  if (N == 0) {  // nothing to read: n = 0, and the mean of no rows is 0/0
-    int32_t* n_out = n_valid ? n_valid : &hdr->n_valid;
-    if ((e = vce::launch_zero_count(n_out, stream))) return hip_fail(e, "count launch");
-    if (p->reduce_loss && (e = vce::launch_mean(nullptr, 0, mean_n(p, n_out), loss, stream)))
-      return hip_fail(e, "mean launch");
-    return CE_OK;
-  }
+  vce::FusedArgs a;
+  bool launch;
+  if ((st = fused_common(&shards[0], t, p, pl.K, pl.C, grad_out, loss, n_valid, ws, ws_bytes, stream, &a,
+                         &launch)) || !launch)
+    return st;
   vce::ShardSet ss;
   memset(&ss, 0, sizeof ss);
   ss.S = S;
   ss.kper = pl.kper;
   for (int32_t s = 0; s < S; ++s) ss.L[s] = row_layout(&shards[s], t, p);
-  vce::FusedArgs a;
-  a.L = ss.L[0];
-  a.K = pl.K;
-  a.aligned = 0;
-  a.C = pl.C;
-  a.reduce = p->reduce_loss;
-  a.g = grad_out;
-  a.n_out = n_valid;
-  a.row_loss = p->reduce_loss ? nullptr : loss;
-  a.row_loss_tagged = reinterpret_cast<unsigned long long*>(wsb + w.row_loss_tagged);
-  a.mean_out = p->reduce_loss ? loss : nullptr;
-  a.hdr = hdr;
-  a.slots = pl.K > 1 ? reinterpret_cast<unsigned long long*>(wsb + w.slots) : nullptr;
-  a.slice_rows = (N + vce::kMaxSlices - 1) / vce::kMaxSlices;
-  if (a.slice_rows < 2048) a.slice_rows = 2048;
-  a.nslice = (int32_t)((N + a.slice_rows - 1) / a.slice_rows);
-  a.ws_bytes = w.total;
   a.short_rows = pl.short_rows ? 1 : 0;
-  const Smoothing q = smoothing_of(p, shards[0].vocab_total);
-  a.q_o_d = q.q_o;
-  a.q_t_d = q.q_t;
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
+  hipError_t e;
   if ((e = vce::launch_fused_shards(a, ss, pl.shape, stream, e0, e1))) return hip_fail(e, "sharded fused launch");
   return CE_OK;
 }
