@@ -29,6 +29,7 @@ timed on a bounded sample of rows on the host cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -139,6 +140,8 @@ def main():
                     help="loss reduction (default: the workload's own)")
     ap.add_argument("--fused-shards", action="store_true",
                     help="shard workloads: one ce_shards_fwd_bwd_fused launch in place of the three-call flow")
+    ap.add_argument("--dtype", choices=["bf16", "f32"], default=None,
+                    help="the workload's logits in this dtype instead of its own (same shape and recipe)")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--linear", action="store_true",
                     help="time the chunked linear head + cross-entropy (ce_linear_cross_entropy) instead")
@@ -165,6 +168,12 @@ def main():
     if args.linear:
         return bench_linear(args, torch, vce, workloads, dev)
     w = workloads.WORKLOADS[args.workload]
+    if args.dtype:
+        dt = torch.bfloat16 if args.dtype == "bf16" else torch.float32
+        if dt != w.dtype:
+            other = "_bf16" if args.dtype == "f32" else "_f32"
+            name = w.name.replace(other, f"_{args.dtype}") if other in w.name else f"{w.name}_{args.dtype}"
+            w = dataclasses.replace(w, dtype=dt, name=name)
     t_gen = time.perf_counter()
     inputs = workloads.generate(w)
     gen_s = time.perf_counter() - t_gen
