@@ -322,6 +322,17 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 2 * flat.numel() * flat.element_size() / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
     del dst
+    # and an in-place elementwise pass over the same bytes (read, then write to the same addresses;
+    # the generated logits on the device are not used after this)
+    for _ in range(3):
+        flat.neg_()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        flat.neg_()
+    c1.record()
+    torch.cuda.synchronize()
+    inplace_gbps = 2 * flat.numel() * flat.element_size() / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
 
     # each call's main kernel: its average duration over the event pass and
     # the algorithmic bytes one launch moves (read + written, formula N*V*b
@@ -385,6 +396,7 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
         "formula_bytes_per_step": formula_bytes,
         "copy_ref_GBps": round(copy_gbps, 1),
+        "inplace_ref_GBps": round(inplace_gbps, 1),
         "roofline": roofline,
         "kernels": kernel_summary,
         "cold_steps": {"median_us": round(1e3 * cold[len(cold) // 2], 2), "min_us": round(1e3 * cold[0], 2),
