@@ -368,3 +368,34 @@ def test_shards_workspace_sizes(lib):
             == lib.ce_shards_workspace_bytes(_shard_set(h, [16]), 1, ctypes.byref(p)) > 0)
     # 16 shards is the most; up to 64 chunks per row in all
     assert lib.ce_shards_workspace_bytes(_shard_set(h, [1] * 16), 16, ctypes.byref(p)) > 0
+
+
+def test_last_error_is_per_thread(lib):
+    """ce_last_error's text belongs to the calling thread: two threads that
+    fail differently at the same time each read their own message (ctypes
+    releases the interpreter lock during the calls, so they interleave)."""
+    import threading
+
+    results = {}
+    barrier = threading.Barrier(2)
+
+    def worker(name, change, expect_status, expect_text):
+        h = Host()
+        x = h.logits(**change.get("x", {}))
+        p = h.params(**change.get("p", {}))
+        ok = True
+        barrier.wait()
+        for _ in range(2000):
+            rc = _fused(lib, h, x=x, p=p)
+            msg = lib.ce_last_error().decode()
+            ok &= rc == expect_status and expect_text in msg
+        results[name] = ok
+
+    threads = [threading.Thread(target=worker, args=("dtype", dict(x=dict(dtype=7)), _abi.CE_EDTYPE, "dtype")),
+               threading.Thread(target=worker, args=("reduce", dict(p=dict(reduce_loss=9)), _abi.CE_EINVAL,
+                                                      "reduce"))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert results == {"dtype": True, "reduce": True}
