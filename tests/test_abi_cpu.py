@@ -104,6 +104,11 @@ BAD_FUSED = [
     ("rows_overlap_outer", dict(x=dict(s0=16)), _abi.CE_ELAYOUT),
     ("sharded_for_fused", dict(x=dict(vocab_start=16, vocab_total=32)), _abi.CE_ELAYOUT),
     ("shard_past_vocab", dict(x=dict(vocab_start=8, vocab_total=20)), _abi.CE_ELAYOUT),
+    # a row of 4 GiB or more: beyond the kernels' 32-bit buffer ranges
+    ("row_of_4gib_f32", dict(x=dict(dtype=_abi.CE_F32, d0=1, d1=1, s0=1 << 30, s1=1 << 30, v_local=1 << 30,
+                                    vocab_total=1 << 30)), _abi.CE_ELAYOUT),
+    ("row_of_4gib_bf16", dict(x=dict(d0=1, d1=1, s0=1 << 31, s1=1 << 31, v_local=1 << 31,
+                                     vocab_total=1 << 31)), _abi.CE_ELAYOUT),
     ("smoothing_negative", dict(p=dict(label_smoothing=-0.1)), _abi.CE_EINVAL),
     ("smoothing_above_one", dict(p=dict(label_smoothing=1.5)), _abi.CE_EINVAL),
     ("smoothing_nan", dict(p=dict(label_smoothing=float("nan"))), _abi.CE_EINVAL),

@@ -110,6 +110,9 @@ ce_status check_logits(const ce_logits* x, bool unsharded) {
   if (x->d0 < 0 || x->d1 < 1) return fail(CE_EINVAL, "need d0 >= 0 and d1 >= 1 (got %lld, %lld)",
                                           (long long)x->d0, (long long)x->d1);
   if (x->v_local < 1) return fail(CE_EINVAL, "v_local must be >= 1");
+  // the kernels address a row through 32-bit buffer ranges and byte offsets
+  if (x->v_local > (int64_t)(0xffffffffLL / elem_bytes(x->dtype)))
+    return fail(CE_ELAYOUT, "rows of %lld columns exceed 4 GiB", (long long)x->v_local);
   if (x->vocab_start < 0 || x->vocab_total < 1 || x->vocab_start > x->vocab_total - x->v_local)
     return fail(CE_ELAYOUT, "shard [%lld, %lld) does not fit a vocabulary of %lld", (long long)x->vocab_start,
                 (long long)(x->vocab_start + x->v_local), (long long)x->vocab_total);
