@@ -98,7 +98,7 @@ typedef struct ce_logits {
   int32_t reserved;    /* must be 0 */
   int64_t d0, d1;      /* logical leading dims, d0 >= 0, d1 >= 1; N = d0 * d1 rows */
   int64_t s0, s1;      /* element strides of d0 and d1 (>= 0); the column stride is 1 */
-  int64_t v_local;     /* columns present in `data` (>= 1) */
+  int64_t v_local;     /* columns present in `data` (>= 1; a row below 4 GiB, else CE_ELAYOUT) */
   int64_t vocab_start; /* global index of local column 0 (0 when unsharded) */
   int64_t vocab_total; /* global vocabulary size V; vocab_start + v_local <= V */
 } ce_logits;
