@@ -20,7 +20,7 @@ import torch
 
 import vocab_cross_entropy_amd as vce
 import vce_sweep_cases as cases
-from gpu_util import assert_grad_from_lse, assert_loss, orc, rows_f64, say, to_device_view
+from gpu_util import assert_grad_from_lse, assert_loss, ignored_rows, orc, raw_bits, rows_f64, say, to_device_view
 from test_gpu_parity import check_fused
 from test_gpu_shards_fused import check_shards
 
@@ -56,6 +56,18 @@ def _scale(g, reduce, N, n):
     return np.full(N, gg / n if reduce == "mean" else gg) if (reduce != "mean" or n) else np.full(N, np.nan)
 
 
+def _softmax(x, t, lse_ref):
+    """p_j = exp(x_j - lse) per logical row in FP64, for the lse hand-off's allowance; 0 on ignored rows,
+    whose gradient must stay +0.0 exactly."""
+    d0, d1, V = x.shape
+    rows = x.reshape(d0 * d1, V).to(torch.float64).numpy()
+    kept = t.reshape(-1).numpy() != -100
+    with np.errstate(over="ignore", invalid="ignore"):
+        p = np.exp(rows - np.asarray(lse_ref, np.float64)[:, None])
+    p[~kept] = 0.0
+    return p
+
+
 def _check_loss(loss, ref_rows, reduce, n, o, what):
     if reduce == "none":
         assert_loss(loss.cpu().numpy().astype(np.float64), ref_rows, what + " rows")
@@ -85,7 +97,9 @@ def test_forward_backward_sweep(seed):
     ref = o.grad_rows(x, t, a, reduce_loss=red, g=c["g"], n_valid=n_ref, smoothing=sm)
     tl = t.reshape(-1).numpy()
     assert_grad_from_lse(rows_f64(xd), ref, x.dtype, lse.cpu().numpy(), np.where(kept, tl, -1),
-                         _scale(c["g"], red, N, n_ref), c["what"] + " grad")
+                         _scale(c["g"], red, N, n_ref), c["what"] + " grad", p=_softmax(x, t, ref_lse))
+    ign = ignored_rows(t)
+    assert not (len(ign) and raw_bits(xd, ign).any()), "ignored rows must be +0.0"
 
 
 @pytest.mark.parametrize("seed", range(cases.N_SHARD_FLOW))
@@ -107,15 +121,18 @@ def test_shard_flow_sweep(seed):
     o = orc()
     n_ref = o.count_valid(t)
     assert int(n.item()) == n_ref
-    ref_rows, _ = o.loss_rows(x, t, a, smoothing=sm)
+    ref_rows, ref_lse = o.loss_rows(x, t, a, smoothing=sm)
     _check_loss(loss, ref_rows, red, n_ref, o, c["what"])
     ref = o.grad_rows(x, t, a, reduce_loss=red, g=c["g"], n_valid=n_ref, smoothing=sm)
     tl = t.reshape(-1).numpy()
     sc = _scale(c["g"], red, N, n_ref)
+    p = _softmax(x, t, ref_lse)
     for s, (lo, hi) in enumerate(bounds):
         local = np.where((tl >= lo) & (tl < hi), tl - lo, -1)
         assert_grad_from_lse(rows_f64(shards[s]), ref[:, lo:hi], x.dtype, lse.cpu().numpy(), local, sc,
-                             f"{c['what']} shard {s}")
+                             f"{c['what']} shard {s}", p=p[:, lo:hi])
+        ign = ignored_rows(t)
+        assert not (len(ign) and raw_bits(shards[s], ign).any()), f"shard {s}: ignored rows must be +0.0"
 
 
 @pytest.mark.parametrize("seed", range(cases.N_LINEAR))
