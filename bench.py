@@ -142,6 +142,9 @@ def main():
                     help="shard workloads: one ce_shards_fwd_bwd_fused launch in place of the three-call flow")
     ap.add_argument("--dtype", choices=["bf16", "f32"], default=None,
                     help="the workload's logits in this dtype instead of its own (same shape and recipe)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as HIP graph replays (one captured step per input copy), without the "
+                         "host's per-call cost")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--linear", action="store_true",
                     help="time the chunked linear head + cross-entropy (ce_linear_cross_entropy) instead")
@@ -268,6 +271,26 @@ def main():
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
     refresh()
 
+    timed = step
+    if args.graph:
+        # one captured step per input copy (their pointers differ); each replay
+        # takes a fresh tag from the workspace, so replays are full calls
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for p in pool:
+                captured = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(captured, stream=cap):
+                    step(p)
+                graphs.append(captured)
+        torch.cuda.current_stream().wait_stream(cap)
+        for captured in graphs:  # a first launch of each (its upload), outside the timed region
+            captured.replay()
+        refresh()
+        by_id = {id(p): gr for p, gr in zip(pool, graphs)}
+        timed = lambda p: by_id[id(p)].replay()  # noqa: E731
+
     # the timed steps: nothing but the calls themselves between the two events
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -275,7 +298,7 @@ def main():
     h0 = time.perf_counter()
     e0.record()
     for i in range(args.steps):
-        step(pool[i % P])
+        timed(pool[i % P])
     e1.record()
     torch.cuda.synchronize()
     h1 = time.perf_counter()
@@ -391,7 +414,8 @@ def main():
         "data": "synthetic",
         "config": {**w.describe(), "io_dtype": "bf16" if w.elem_bytes == 2 else "f32", "calls": calls,
                    "reduction": red, "smoothing": sm,
-                   "split_chunks": args.split_chunks, "pool": P, "fresh_inputs": P >= args.steps},
+                   "split_chunks": args.split_chunks, "pool": P, "fresh_inputs": P >= args.steps,
+                   "graph": bool(args.graph)},
         "rows_per_s": round(N / (step_ms * 1e-3), 1),
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
         "formula_bytes_per_step": formula_bytes,
