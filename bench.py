@@ -138,6 +138,8 @@ def main():
                     help="label smoothing a/V over all classes (default) or a/(V-1) over the other classes")
     ap.add_argument("--reduction", choices=["none", "mean", "sum"], default=None,
                     help="loss reduction (default: the workload's own)")
+    ap.add_argument("--split", action="store_true",
+                    help="unsharded workloads: ce_forward then ce_backward_inplace in place of the fused call")
     ap.add_argument("--fused-shards", action="store_true",
                     help="shard workloads: one ce_shards_fwd_bwd_fused launch in place of the three-call flow")
     ap.add_argument("--dtype", choices=["bf16", "f32"], default=None,
@@ -207,6 +209,8 @@ def main():
     calls = w.calls
     if calls == "shard" and args.fused_shards:
         calls = "shard_fused"
+    if calls == "fused" and args.split:
+        calls = "split"
     if calls == "fused":
         ws = torch.empty(vce.ce_workspace_bytes(view(pool[0]), w.alpha, red, split_chunks=args.split_chunks),
                          dtype=torch.uint8, device=dev)
@@ -217,7 +221,7 @@ def main():
     elif calls == "split":
         ws = torch.empty(vce.ce_workspace_bytes(view(pool[0]), w.alpha, red), dtype=torch.uint8, device=dev)
         lse = torch.empty(N, dtype=torch.float32, device=dev)
-        g = torch.ones(N, dtype=torch.float32, device=dev)
+        g = torch.ones(N if red == "none" else 1, dtype=torch.float32, device=dev)
         calls_per_step = 2
 
         def step(p):
