@@ -52,17 +52,25 @@ def kernel_source_sha() -> str:
 
 def traffic_from_profiles(workload_name: str):
     """HBM bytes per launch of the fused kernel from committed rocprofv3 --pmc
-    runs (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter reads
-    for a plain copy kernel of known size.  None when absent or stale."""
-    try:
-        with open(PMC_FILE) as f:
-            pmc = json.load(f)
-    except (OSError, ValueError):
-        return None, "no counter file"
+    runs (FETCH_SIZE, WRITE_SIZE) of this workload, each scaled by what the
+    same counter reads for a plain copy kernel of known size.  None when no
+    counter file covers the workload or the kernel source changed since."""
+    import glob
+
+    found = []
+    for path in sorted(glob.glob(os.path.join(os.path.dirname(PMC_FILE), "*_pmc.json"))):
+        try:
+            with open(path) as f:
+                pmc = json.load(f)
+        except (OSError, ValueError):
+            continue
+        if pmc.get("workload") == workload_name:
+            found.append(pmc)
+    if not found:
+        return None, "no counter file for this workload"
+    pmc = found[0]
     if pmc.get("kernel_source_sha256") != kernel_source_sha():
         return None, "kernel changed since the counters were taken"
-    if pmc.get("workload") != workload_name:
-        return None, "counters are for another workload"
     c = pmc["copy"]
     fetch_scale = c["bytes"] / (c["fetch_kib"] * 1024.0)
     write_scale = c["bytes"] / (c["write_kib"] * 1024.0)
