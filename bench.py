@@ -167,8 +167,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the multi-GPU (vocabulary- or row-sharded) path is not implemented here; each GPU would run its own rows or shards", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the multi-GPU "
+              "(vocabulary- or row-sharded) path is not implemented here; each GPU would run its own rows or shards",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
