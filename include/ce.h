@@ -72,7 +72,8 @@
 extern "C" {
 #endif
 
-#define CE_ABI_VERSION 2
+/* 3: ce_shards_workspace_bytes and ce_shards_fwd_bwd_fused added */
+#define CE_ABI_VERSION 3
 
 typedef enum ce_status {
   CE_OK = 0,

@@ -15,7 +15,7 @@ CE_OK, CE_EINVAL, CE_EDTYPE, CE_ELAYOUT, CE_EWORKSPACE, CE_EHIP, CE_EDEADLOCK = 
 CE_F32, CE_BF16 = 0, 1
 CE_REDUCE_NONE, CE_REDUCE_MEAN, CE_REDUCE_SUM = 0, 1, 2
 CE_SMOOTH_ALL, CE_SMOOTH_OTHERS = 0, 1
-CE_ABI_VERSION = 2
+CE_ABI_VERSION = 3
 
 
 class CeLogits(ctypes.Structure):
