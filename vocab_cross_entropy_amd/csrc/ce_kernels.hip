@@ -88,8 +88,10 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit element format
 
+// A range of `bytes` (below 4 GiB: the host refuses longer rows) starting at p;
+// the hardware reads the count as unsigned, so the narrowing keeps its bits.
 __device__ __forceinline__ Rsrc make_rsrc(const void* p, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRsrcWord3);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)(uint32_t)bytes, kRsrcWord3);
 }
 __device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
@@ -167,13 +169,6 @@ __device__ __forceinline__ uint4 pack(const float (&f)[ElemT<DT>::E]) {
   } else {
     return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
   }
-}
-
-// A vector whose elements are all -inf (neutral for max and for sum-exp).
-template <int DT>
-__device__ __forceinline__ uint4 neg_inf_vec() {
-  const uint32_t w = (DT == CE_BF16) ? 0xFF80FF80u : 0xFF800000u;
-  return make_uint4(w, w, w, w);
 }
 
 template <int DT>
