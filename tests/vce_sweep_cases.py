@@ -14,11 +14,11 @@ import torch
 
 import workloads
 
-N_FUSED = 40
-N_SHARDS = 24
-N_SPLIT = 24       # ce_forward + ce_backward_inplace
-N_SHARD_FLOW = 16  # ce_shard_partial_stats per shard, ce_shard_combine, ce_backward_inplace per shard
-N_LINEAR = 12      # ce_linear_cross_entropy (grid-valued inputs: see linear_case)
+N_FUSED = 80
+N_SHARDS = 48
+N_SPLIT = 48       # ce_forward + ce_backward_inplace
+N_SHARD_FLOW = 32  # ce_shard_partial_stats per shard, ce_shard_combine, ce_backward_inplace per shard
+N_LINEAR = 24      # ce_linear_cross_entropy (grid-valued inputs: see linear_case)
 MAX_ELEMS = 1_500_000
 MAX_V = 200_000
 MAX_CHUNK_VECS = 4096   # one chunk of the fused call holds at most this many 16-byte vectors
