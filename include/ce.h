@@ -183,7 +183,8 @@ ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_
  *   ws        device workspace of at least ce_workspace_bytes(x, p) bytes,
  *             prepared by ce_workspace_init.  On a workspace that was not
  *             prepared (or prepared smaller) the loss and the gradient come
- *             out NaN and the workspace status records it (ce_workspace_check).
+ *             out NaN, n_valid is -1 and the workspace status records it
+ *             (ce_workspace_check).
  * One kernel launch: the first workgroups also count the non-ignored rows,
  * and the workgroup of the last (row, chunk) item writes n_valid and the
  * mean or the sum.

@@ -4,7 +4,7 @@ ce_fwd_bwd_fused tags every word its workgroups exchange with a fresh
 per-call value, so one workspace prepared once by ce_workspace_init serves
 any sequence of calls with no clearing in between; a workspace that was never
 prepared (or prepared smaller) makes the call fail loudly: NaN loss and
-gradient, and CE_EWORKSPACE from ce_workspace_check.  The row count n that
+gradient, n = -1, and CE_EWORKSPACE from ce_workspace_check.  The row count n that
 the mean divides by is counted inside the fused kernel, over up to 16 target
 slices of at least 2048 rows.
 """
@@ -61,7 +61,7 @@ def test_unprepared_workspace_fails_loudly():
     xd, td = to_device_view(x), to_device_view(t)
     loss, n = _raw_fused(xd, td, 0.1, True, ws, split_chunks=2)
     assert math.isnan(loss.item())
-    assert int(n.item()) == orc().count_valid(t)  # the count does not depend on the workspace
+    assert int(n.item()) == -1  # the counts travel through the workspace too: not to be trusted there
     assert np.isnan(rows_f64(xd, keep)).all()
     _expect_unprepared(ws)
 
@@ -158,4 +158,43 @@ def test_graph_replays_get_fresh_tags(reduce):
             vce.ce_fwd_bwd_fused(xd, td, 0.1, reduce, loss=loss, n_valid=n, ws=ws, split_chunks=K)
             torch.cuda.synchronize()
             assert torch.equal(xd.view(torch.int16), ref_grad.view(torch.int16))
+    vce.ce_workspace_check(ws)
+
+
+def test_shard_call_with_unprepared_workspace_fails_loudly():
+    """The one-launch shard call reads the same workspace record: never
+    prepared, its loss and every shard's gradient are NaN and
+    ce_workspace_check reports CE_EWORKSPACE; prepared, it matches the oracle."""
+    V = 9001
+    x = _logits((2, 8, V), torch.bfloat16, seed=17)
+    t = workloads.random_targets((2, 8), V, seed=17, ignore_frac=0.25)
+    keep = np.setdiff1d(np.arange(16), ignored_rows(t))
+    bounds = workloads.shard_bounds(V, 3)
+    xd, td = to_device_view(x), to_device_view(t)
+    shards = [xd[..., a:b] for a, b in bounds]
+    nb = vce.ce_shards_workspace_bytes(shards, 0.1, True)
+    say("[ws] shard call, garbage workspace, never prepared")
+    ws = torch.full((nb,), 0xAB, dtype=torch.uint8, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    n = torch.empty(1, dtype=torch.int32, device="cuda")
+    p = vce.params(0.1, True)
+    rc = vce.lib.ce_shards_fwd_bwd_fused(vce._shard_descs(shards), len(shards), ctypes.byref(vce.targets_desc(td)),
+                                         ctypes.byref(p), None, ctypes.c_void_p(loss.data_ptr()),
+                                         ctypes.c_void_p(n.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0, vce.lib.ce_last_error()
+    torch.cuda.synchronize()
+    assert math.isnan(loss.item()) and int(n.item()) == -1
+    assert np.isnan(rows_f64(xd, keep)).all()
+    _expect_unprepared(ws)
+
+    say("[ws] shard call, prepared: results match the oracle")
+    vce.ce_workspace_init(ws)
+    xd = to_device_view(x)
+    shards = [xd[..., a:b] for a, b in bounds]
+    loss, n = vce.ce_shards_fwd_bwd_fused(shards, td, 0.1, True, ws=ws)
+    torch.cuda.synchronize()
+    o = orc()
+    ref_rows, _ = o.loss_rows(x, t, 0.1)
+    assert abs(loss.item() - o.mean_loss(ref_rows, o.count_valid(t))) <= 1e-4 * max(1.0, abs(loss.item()))
     vce.ce_workspace_check(ws)

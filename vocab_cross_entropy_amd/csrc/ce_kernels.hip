@@ -555,13 +555,17 @@ __device__ __forceinline__ void advance_epoch(const FusedArgs& a) {
 // (Reduced and unreduced calls keep separate tails: sharing the mean's tail measurably
 // raised the whole kernel's register allocation.)
 template <int T>
-__device__ void fused_finish(const FusedArgs& a, uint32_t tag) {
+__device__ void fused_finish(const FusedArgs& a, uint32_t tag, bool ws_ok) {
   __shared__ double s_sum[T / 64];
+  // In a workspace ce_workspace_init never prepared (ws_ok false), stale
+  // words can carry the "tag" (both are whatever the memory held), so the
+  // counts and row losses read here mean nothing: n is then -1 and the mean
+  // or sum NaN, like every row's loss and gradient.
   bool cnt_ok = true;
   const int32_t n = wave_count(a, tag, count_word_early(a), &cnt_ok);
   if (threadIdx.x == 0) {
     if (!cnt_ok) atomicOr(&a.hdr->status, 1u);
-    if (a.n_out) a.n_out[0] = n;
+    if (a.n_out) a.n_out[0] = ws_ok ? n : -1;
   }
   bool gave_up = false;
   if (!a.reduce) {
@@ -581,7 +585,9 @@ __device__ void fused_finish(const FusedArgs& a, uint32_t tag) {
     double tot = 0.0;
     for (int i = 0; i < T / 64; ++i) tot += s_sum[i];
     // N >= 1 here; n = 0 gives 0/0 = NaN
-    if (a.reduce == CE_REDUCE_SUM)
+    if (!ws_ok)
+      a.mean_out[0] = __builtin_nanf("");
+    else if (a.reduce == CE_REDUCE_SUM)
       a.mean_out[0] = (float)tot;
     else
       a.mean_out[0] = cnt_ok ? (float)(tot / (double)n) : __builtin_nanf("");
@@ -733,6 +739,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
   typedef const __attribute__((address_space(4))) unsigned long long* ConstU64;
   const ConstU64 wsrec = (ConstU64)(&a.hdr->magic);  // magic, init_bytes, epoch
   const uint32_t tag = (uint32_t)wsrec[2];
+  const bool ws_ok = (wsrec[0] == kWsMagic) & (wsrec[1] >= a.ws_bytes);
   if (item < a.nslice) count_slice<T>(a, tag, item);
   const int64_t last_item = L.N * K - 1;
   const int64_t r = item / K;
@@ -781,7 +788,6 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
     // is combined without branches, so no wait is placed before the chunk is
     // in flight.
     const unsigned long long cw = (a.reduce == CE_REDUCE_MEAN && tid < 64) ? count_word_early(a) : 0ull;
-    const bool ws_ok = (wsrec[0] == kWsMagic) & (wsrec[1] >= a.ws_bytes);
     uint4 v[P];
 #pragma unroll
     for (int j = 0; j < P; ++j) v[j] = bload16(rb, (uint32_t)(j * T + tid) * 16u);
@@ -1032,7 +1038,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
   }
   // one call site for both kinds of row (two inlined copies of the finish
   // measurably raised the register allocation of the whole kernel)
-  if (item == last_item) fused_finish<T>(a, tag);
+  if (item == last_item) fused_finish<T>(a, tag, ws_ok);
 }
 
 template <int DT, int T, int P, bool HT>
