@@ -198,3 +198,38 @@ def test_shard_call_with_unprepared_workspace_fails_loudly():
     ref_rows, _ = o.loss_rows(x, t, 0.1)
     assert abs(loss.item() - o.mean_loss(ref_rows, o.count_valid(t))) <= 1e-4 * max(1.0, abs(loss.item()))
     vce.ce_workspace_check(ws)
+
+
+def test_fused_and_shard_calls_share_one_workspace():
+    """Fused and shard calls of different shapes and reductions interleaved on
+    one workspace prepared once: each matches the same call on a fresh
+    workspace bit for bit (the epoch tags keep their exchanged words apart)."""
+    cases = [("fused", (2, 9, 40000), 0, True), ("shards", (2, 8, 9001), 3, False), ("fused", (3, 5, 8192), 0, False),
+             ("shards", (1, 12, 130000), 5, True), ("fused", (2, 9, 40000), 0, True)]
+    need = 0
+    for kind, shape, S, red in cases:
+        x = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        if kind == "fused":
+            need = max(need, vce.ce_workspace_bytes(x, 0.1, red))
+        else:
+            need = max(need, vce.ce_shards_workspace_bytes(
+                [x[..., a:b] for a, b in workloads.shard_bounds(shape[2], S)], 0.1, red))
+    shared = vce.ce_workspace_init(torch.empty(need, dtype=torch.uint8, device="cuda"))
+    for i, (kind, shape, S, red) in enumerate(cases):
+        say(f"[ws] shared workspace, call {i}: {kind} {shape} S={S} reduce={red}")
+        x = _logits(shape, torch.bfloat16, seed=100 + i)
+        t = workloads.random_targets(shape[:2], shape[2], seed=100 + i, ignore_frac=0.2)
+        outs = []
+        for ws in (shared, None):
+            xd, td = to_device_view(x), to_device_view(t)
+            if kind == "fused":
+                loss, n = vce.ce_fwd_bwd_fused(xd, td, 0.1, red, ws=ws)
+            else:
+                loss, n = vce.ce_shards_fwd_bwd_fused([xd[..., a:b] for a, b in workloads.shard_bounds(shape[2], S)],
+                                                      td, 0.1, red, ws=ws)
+            torch.cuda.synchronize()
+            outs.append((xd.view(torch.int16).clone(), loss.view(torch.int32).clone(), int(n.item())))
+        assert torch.equal(outs[0][0], outs[1][0]), f"call {i}: gradient differs"
+        assert torch.equal(outs[0][1], outs[1][1]), f"call {i}: loss differs"
+        assert outs[0][2] == outs[1][2] == orc().count_valid(t)
+    vce.ce_workspace_check(shared)
