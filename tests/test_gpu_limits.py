@@ -6,7 +6,8 @@
     row length, take it;
   * a million rows (2^20, the in-kernel count over its 16 target slices of
     65536 rows), for short rows (the FP64 path) and whole 96-column rows;
-  * two calls in flight at once on two streams, each with its own workspace;
+  * two calls in flight at once on two streams, each with its own workspace,
+    and two host threads calling the fused and the shard call concurrently;
   * logits with a large common offset (1000 + N(0, 2^2)).
 """
 import numpy as np
@@ -116,3 +117,60 @@ def test_large_common_offset(dtype):
     t = workloads.random_targets((2, 8), 32003, seed=13, ignore_frac=0.1)
     check_fused(x, t, 0.1, True, what=f"offset 1000 {dtype}")
     check_fused(x, t, 0.1, False, g=np.ones(16), split_chunks=5, what=f"offset 1000 split {dtype}")
+
+
+def test_two_host_threads():
+    """Two host threads, each with its own stream and workspace, call the fused
+    call and the shard call in a loop at the same time (ctypes releases the
+    interpreter lock, so the library's host code runs concurrently); every
+    result equals the same call made alone."""
+    import threading
+
+    xs = [_logits((2, 32, 20011), torch.bfloat16, seed=s) for s in (21, 22)]
+    ts = [workloads.random_targets((2, 32), 20011, seed=s, ignore_frac=0.1) for s in (21, 22)]
+    refs = []
+    for i, (x, t) in enumerate(zip(xs, ts)):
+        xd, td = to_device_view(x), to_device_view(t)
+        if i == 0:
+            loss, _ = vce.ce_fwd_bwd_fused(xd, td, 0.1, True)
+        else:
+            loss, _ = vce.ce_shards_fwd_bwd_fused([xd[..., a:b] for a, b in workloads.shard_bounds(20011, 3)],
+                                                  td, 0.1, True)
+        torch.cuda.synchronize()
+        refs.append((loss.clone(), xd.view(torch.int16).clone()))
+    say("[limits] two host threads")
+    errors = []
+
+    def worker(i):
+        try:
+            stream = torch.cuda.Stream()
+            x, t = xs[i], ts[i]
+            td = to_device_view(t)
+            base = to_device_view(x)
+            xd = base.clone()
+            nb = (vce.ce_workspace_bytes(xd, 0.1, True) if i == 0 else
+                  vce.ce_shards_workspace_bytes([xd[..., a:b] for a, b in workloads.shard_bounds(20011, 3)], 0.1, True))
+            ws = vce.ce_workspace_init(torch.empty(nb, dtype=torch.uint8, device="cuda"))
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                for _ in range(30):
+                    xd.copy_(base)
+                    if i == 0:
+                        loss, _ = vce.ce_fwd_bwd_fused(xd, td, 0.1, True, ws=ws)
+                    else:
+                        loss, _ = vce.ce_shards_fwd_bwd_fused(
+                            [xd[..., a:b] for a, b in workloads.shard_bounds(20011, 3)], td, 0.1, True, ws=ws)
+                    stream.synchronize()
+                    if not (torch.equal(loss, refs[i][0]) and torch.equal(xd.view(torch.int16), refs[i][1])):
+                        errors.append(f"thread {i}: result differs")
+                        return
+            vce.ce_workspace_check(ws)
+        except Exception as e:  # reported below
+            errors.append(f"thread {i}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
