@@ -320,3 +320,39 @@ def test_linear_after_tuning():
     say("[linear tune] timing candidates")
     vce.ce_linear_tune(hd, wd, "mean", chunk_rows=32)
     check_linear(h, w, t, 0.1, "mean", chunk_rows=32, what="after tuning")
+
+
+def test_linear_from_two_host_threads():
+    """Two host threads run the chunked head at the same time, each on its own
+    stream and workspace (sharing the library's per-device GEMM handle and
+    plans); each result equals the same call made alone."""
+    import threading
+
+    cases = [grid_inputs(48, 64, 3001, torch.bfloat16, seed=s) for s in (91, 92)]
+    refs = [run_linear(h, w, t, 0.1, "mean", chunk_rows=16) for h, w, t in cases]
+    errors = []
+
+    def worker(i):
+        try:
+            h, w, t = cases[i]
+            stream = torch.cuda.Stream()
+            hd, wd, td = h.cuda(), w.cuda(), t.cuda()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                for _ in range(10):
+                    loss, dh, dw, n = vce.ce_linear_cross_entropy(hd, wd, td, 0.1, "mean", chunk_rows=16)
+                    stream.synchronize()
+                    got = (loss.cpu().double().numpy(), dh.cpu().double().numpy(), dw.cpu().double().numpy())
+                    if not all(np.array_equal(a, b) for a, b in zip(got, refs[i][:3])):
+                        errors.append(f"thread {i}: result differs")
+                        return
+        except Exception as e:  # reported below
+            errors.append(f"thread {i}: {e!r}")
+
+    say("[linear] two host threads")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
