@@ -147,8 +147,13 @@ ce_status run_gemm(int dev, const Gemm& g, void* blas_ws, hipStream_t stream) {
   ce_status st = get_plan(dev, g, &p);
   if (st) return st;
   const float alpha = 1.f;
+  hipblasLtMatmulAlgo_t algo;  // a copy: ce_linear_tune may replace the plan's choice from another thread
+  {
+    std::lock_guard<std::mutex> lk(g_blas_mu);
+    algo = p->algo;
+  }
   hipblasStatus_t s = hipblasLtMatmul(p->handle, p->desc, &alpha, g.A, p->a, g.B, p->b, &g.beta, g.D, p->c, g.D, p->c,
-                                      &p->algo, blas_ws, kBlasWorkspace, stream);
+                                      &algo, blas_ws, kBlasWorkspace, stream);
   if (s != HIPBLAS_STATUS_SUCCESS)
     return lfail(CE_EHIP, "GEMM %lld x %lld x %lld: %s", (long long)g.m, (long long)g.n, (long long)g.k,
                  blas_status(s));
