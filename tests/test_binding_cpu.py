@@ -37,3 +37,16 @@ def test_no_shards_rejected_before_any_device_work():
         vce.sharded_cross_entropy([], None)
     with pytest.raises(vce.CeArgumentError):
         vce.ce_shards_fwd_bwd_fused([], None)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says so, before any GPU work."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], stdout=subprocess.PIPE,
+                       stderr=subprocess.PIPE, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2 and "one GPU" in r.stderr, (r.returncode, r.stderr)
+    assert r.stdout == ""
