@@ -281,3 +281,34 @@ def test_short_vocabulary_shards(V, S, alpha, smoothing, dtype):
     for reduce, gg in (("none", gr), ("mean", 1.3), ("sum", None)):
         check_shards(x, t, bounds, alpha, reduce, g=gg, smoothing=smoothing, separate=reduce == "none",
                      what=f"short V={V} S={len(bounds)}")
+
+
+def test_shards_with_different_layouts():
+    """Each shard keeps its own strides: one a column range of a transposed
+    (SQ, B) view, one a contiguous buffer, one rows padded inside a wider
+    buffer starting off a 16-byte boundary; gradients match the oracle's columns."""
+    V = 7001
+    bounds = [(0, 2500), (2500, 5000), (5000, V)]
+    phys = _logits((3, 6, V), torch.bfloat16, seed=111)          # (B, SQ, V) storage
+    x = phys.transpose(0, 1)                                       # the (SQ, B, V) logical view
+    tp = workloads.random_targets((3, 6), V, seed=111, ignore_frac=0.2)
+    t = tp.transpose(0, 1)
+    say("[shards fused] mixed shard layouts")
+    xd_t = to_device_view(x)
+    s0 = xd_t[..., bounds[0][0]:bounds[0][1]]                      # strided view of the transposed tensor
+    s1 = x[..., bounds[1][0]:bounds[1][1]].contiguous().cuda()     # its own contiguous buffer
+    w2 = bounds[2][1] - bounds[2][0]
+    pad = torch.zeros((6, 3, w2 + 37), dtype=torch.bfloat16)
+    pad[..., 3:3 + w2] = x[..., bounds[2][0]:bounds[2][1]]
+    s2 = pad.cuda()[..., 3:3 + w2]                                 # padded rows, odd column offset
+    td = to_device_view(t)
+    loss, n = vce.ce_shards_fwd_bwd_fused([s0, s1, s2], td, 0.1, "none",
+                                          grad_out=torch.linspace(0.5, 1.5, 18, device="cuda"))
+    torch.cuda.synchronize()
+    o = orc()
+    assert int(n.item()) == o.count_valid(t)
+    ref_rows, _ = o.loss_rows(x, t, 0.1)
+    assert_loss(loss.cpu().numpy().astype(np.float64), ref_rows, "mixed layouts loss")
+    ref = o.grad_rows(x, t, 0.1, g=np.linspace(0.5, 1.5, 18, dtype=np.float32).astype(np.float64))
+    got = np.concatenate([rows_f64(s0), rows_f64(s1), rows_f64(s2)], axis=1)
+    assert_grad(got, ref, torch.bfloat16, "mixed layouts grad")
