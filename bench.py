@@ -78,6 +78,45 @@ def traffic_from_profiles(workload_name: str):
     return t, f"fetch x{fetch_scale:.3f}, write x{write_scale:.3f} (copy calibration)"
 
 
+def torch_ce_reference(torch, w, inputs, dev, reduction: str, smoothing: str, steps: int):
+    """torch's own F.cross_entropy, forward + autograd backward, on the same
+    logits in their own dtype: the unfused op this library stands in for.
+    Time per step (events, after warmup) and peak memory over the inputs."""
+    import torch.nn.functional as F
+
+    if smoothing != "all":  # torch spreads the smoothing over all classes only
+        return None
+    x = inputs.logits.to(dev).requires_grad_(True)
+    t = inputs.targets.to(dev).reshape(-1)
+
+    def step():
+        x.grad = None
+        loss = F.cross_entropy(x.reshape(-1, w.V), t, label_smoothing=w.alpha, ignore_index=-100,
+                               reduction=reduction)
+        (loss.sum() if reduction == "none" else loss).backward()
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    step()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del x
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "peak_bytes_over_inputs": int(peak),
+            "what": "F.cross_entropy(logits, targets, label_smoothing, ignore_index=-100) + autograd backward, "
+                    "torch ops on the same logits in their dtype"}
+
+
 def device_info(torch, dev) -> dict:
     """What the runtime reports of the device the step ran on; the peak HBM
     rate used as the roofline's denominator is the published figure."""
@@ -162,7 +201,8 @@ def main():
     ap.add_argument("--chunk-rows", type=int, default=0, help="--linear: rows per chunk (0: automatic)")
     ap.add_argument("--tune", action="store_true", help="--linear: ce_linear_tune before the timed steps")
     ap.add_argument("--torch-ref", action="store_true",
-                    help="--linear: also time torch's matmul + F.cross_entropy + autograd on the same inputs")
+                    help="also time torch's own path on the same inputs (F.cross_entropy + autograd; with --linear "
+                         "the matmul too)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -446,6 +486,11 @@ def main():
         moved = 3 * N * V * b
         out["moved_bytes_per_step"] = moved
         out["moved_GBps"] = round(moved / (step_ms * 1e-3) / 1e9, 1)
+    if args.torch_ref and calls == "fused":
+        ref = torch_ce_reference(torch, w, inputs, dev, red, sm, args.steps)
+        if ref is not None:
+            ref["time_ratio_ours_over_torch"] = round(step_ms / ref["ms_per_step"], 4)
+        out["torch_reference"] = ref
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_sample_rows, red, sm)
     line = json.dumps(out)
