@@ -1233,14 +1233,18 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const float4* st = reinterpret_cast<const float4*>(a.stats);
   float M = -INFINITY;
   for (int s = 0; s < a.S; ++s) M = fmaxf(M, st[(int64_t)s * a.N + r].x);
-  float D = 0.f, Y = 0.f, R = 0.f;
+  // lse = M + log(sum_s d_s e^(m_s - M)) in FP64, rounded once: the backward
+  // rebuilds every p_j from it, and with few columns (p_j large) each FP32
+  // rounding along the way would show in the gradient.  S <= a few per row.
+  double D = 0.0;
+  float Y = 0.f, R = 0.f;
   for (int s = 0; s < a.S; ++s) {
     const float4 q = st[(int64_t)s * a.N + r];
-    D += (q.x == -INFINITY) ? 0.f : q.y * ex2((q.x - M) * kL);
+    D += (q.x == -INFINITY) ? 0.0 : (double)q.y * exp((double)q.x - (double)M);
     Y += q.z;
     R += q.w;
   }
-  const float lse = M + lg2(D) * kLn2;
+  const float lse = (float)((double)M + log(D));
   const float loss = row_loss_of(lse, a.q_to, Y, a.q_o, R);
   const bool tvalid = t >= 0 && t < a.vocab_total;
   a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
