@@ -306,7 +306,7 @@ def test_ragged_and_misaligned(dtype, V, offset):
     loss_ref, _ = o.loss_rows(x, t, 0.1)
     assert_loss(loss.cpu().numpy(), loss_ref, "ragged forward")
     assert_grad_from_lse(rows_f64(xd), o.grad_rows(x, t, 0.1), dtype, lse.cpu().numpy(), t.reshape(-1).numpy(),
-                         np.ones(A * B), "ragged backward")
+                         np.ones(A * B), V, "ragged backward")
 
 
 # ---------------------------------------------------------------------------

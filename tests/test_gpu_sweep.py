@@ -20,7 +20,8 @@ import torch
 
 import vocab_cross_entropy_amd as vce
 import vce_sweep_cases as cases
-from gpu_util import assert_grad_from_lse, assert_loss, ignored_rows, orc, raw_bits, rows_f64, say, to_device_view
+from gpu_util import (assert_grad_from_lse, assert_loss, assert_lse, ignored_rows, orc, raw_bits, rows_f64, say,
+                      to_device_view)
 from test_gpu_parity import check_fused
 from test_gpu_shards_fused import check_shards
 
@@ -93,11 +94,11 @@ def test_forward_backward_sweep(seed):
     ref_rows, ref_lse = o.loss_rows(x, t, a, smoothing=sm)
     _check_loss(loss, ref_rows, red, n_ref, o, c["what"])
     kept = t.reshape(-1).numpy() != -100
-    assert_loss(lse.cpu().numpy()[kept], ref_lse[kept], c["what"] + " lse")
+    assert_lse(lse.cpu().numpy()[kept], ref_lse[kept], x.shape[-1], c["what"] + " lse")
     ref = o.grad_rows(x, t, a, reduce_loss=red, g=c["g"], n_valid=n_ref, smoothing=sm)
     tl = t.reshape(-1).numpy()
     assert_grad_from_lse(rows_f64(xd), ref, x.dtype, lse.cpu().numpy(), np.where(kept, tl, -1),
-                         _scale(c["g"], red, N, n_ref), c["what"] + " grad", p=_softmax(x, t, ref_lse))
+                         _scale(c["g"], red, N, n_ref), x.shape[-1], c["what"] + " grad", p=_softmax(x, t, ref_lse))
     ign = ignored_rows(t)
     assert not (len(ign) and raw_bits(xd, ign).any()), "ignored rows must be +0.0"
 
@@ -123,13 +124,15 @@ def test_shard_flow_sweep(seed):
     assert int(n.item()) == n_ref
     ref_rows, ref_lse = o.loss_rows(x, t, a, smoothing=sm)
     _check_loss(loss, ref_rows, red, n_ref, o, c["what"])
+    kept = t.reshape(-1).numpy() != -100
+    assert_lse(lse.cpu().numpy()[kept], ref_lse[kept], V, c["what"] + " lse")
     ref = o.grad_rows(x, t, a, reduce_loss=red, g=c["g"], n_valid=n_ref, smoothing=sm)
     tl = t.reshape(-1).numpy()
     sc = _scale(c["g"], red, N, n_ref)
     p = _softmax(x, t, ref_lse)
     for s, (lo, hi) in enumerate(bounds):
         local = np.where((tl >= lo) & (tl < hi), tl - lo, -1)
-        assert_grad_from_lse(rows_f64(shards[s]), ref[:, lo:hi], x.dtype, lse.cpu().numpy(), local, sc,
+        assert_grad_from_lse(rows_f64(shards[s]), ref[:, lo:hi], x.dtype, lse.cpu().numpy(), local, sc, V,
                              f"{c['what']} shard {s}", p=p[:, lo:hi])
         ign = ignored_rows(t)
         assert not (len(ign) and raw_bits(shards[s], ign).any()), f"shard {s}: ignored rows must be +0.0"
