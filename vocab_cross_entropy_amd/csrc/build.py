@@ -21,8 +21,15 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 ARCH = "gfx950"
 COMMON = ["-std=c++17", "-fPIC", "-O3", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall"]
-# Packed FP32 VALU forms are kept out of the device code.
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed FP32 VALU forms are kept out of the device code.  Multiplies and
+# adds are fused only within one expression (-ffp-contract=on; hipcc's default
+# fuses across statements): the kernels round m log2(e) once and rely on that
+# rounded value wherever it is reused, so that the rounding cancels between the
+# sum's terms and its rescaling; a product fused into a later subtraction
+# unrounded breaks that.  The fused multiply-adds the kernels want are written
+# out as __builtin_fmaf.
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-ffp-contract=on"]
 
 
 def _run(cmd):

@@ -36,6 +36,16 @@ namespace {
 
 constexpr float kL = 1.44269504088896340736f;     // log2(e)
 constexpr float kLn2 = 0.69314718055994530942f;  // ln(2)
+// 1 / kL = kLn2 + kInvLlo exactly enough: kL is log2(e) rounded to FP32, and
+// a base-2 log-sum-exp formed with it converts back to natural units by its
+// own reciprocal.  Taking ln(2) alone leaves kL's rounding (1.3e-8 relative)
+// on the whole lse, 0.13 ulp at lse = 48.
+constexpr float kInvLlo = 7.348693209507928e-09f;
+
+// natural lse from the base-2 split c_hi + c_lo, rounded once
+__device__ __forceinline__ float lse_natural(float c_hi, float c_lo) {
+  return __builtin_fmaf(c_hi, kLn2, __builtin_fmaf(c_hi, kInvLlo, c_lo * kLn2));
+}
 // Bound on polling iterations of one lane waiting for a partner chunk
 // (each iteration sleeps ~128 cycles: ~0.2 s in total), after which the
 // row is finished with NaN and the workspace status word is set.
@@ -987,7 +997,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
     const float c_hi = M2 + lgD;
     const float bb = c_hi - M2;
     const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
-    const float lse = c_hi * kLn2 + c_lo * kLn2;
+    const float lse = lse_natural(c_hi, c_lo);
     const float row_loss = tvalid && ws_ok ? row_loss_of(lse, L.q_to, Y, L.q_o, R) : __uint_as_float(0x7fc00000u);
 
     // ---- gradient from the registers, written over the logits.  The store
@@ -1023,10 +1033,14 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
       bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(hx, c_hi, c_lo), s, b), rh, tid);
       bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(tx, c_hi, c_lo), s, b), rt, tid);
     }
-    // target element: s (p_t - q_t) = s ((1 - q_t) - (1 - p_t)) with 1 - p_t = D_excl / D,
-    // stored by the lane that just wrote its vector (same-thread order keeps this store last)
+    // target element: s (p_t - q_t), stored by the lane that just wrote its
+    // vector (same-thread order keeps this store last).  Where p_t > 1/2 it is
+    // s ((1 - q_t) - (1 - p_t)) with 1 - p_t = D_excl / D, so p_t near 1 does not
+    // cancel; below, s ((p_t - q_o) - (q_t - q_o)) with p_t = e_t / D, so that
+    // q_t and p_t both far below 1 (smoothing near 1) do not cancel either.
     if (tid == own_tid) {
-      const float g_t = s * (L.q_rest - D / Dt);
+      const float ex = D / Dt;
+      const float g_t = s * (ex < 0.5f ? L.q_rest - ex : (e_t / Dt - L.q_o) - L.q_to);
       if (own_where == 1)
         bstore_elem<DT>(g_t, rh, tid);
       else if (own_where == 3)
@@ -1138,7 +1152,7 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
         const float c_hi = M2 + lgD;
         const float bb = c_hi - M2;
         const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
-        const float lse = c_hi * kLn2 + c_lo * kLn2;
+        const float lse = lse_natural(c_hi, c_lo);
         const float loss = row_loss_of(lse, L.q_to, y, L.q_o, rs);
         a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
         if (a.lse) a.lse[r] = tvalid ? lse : __uint_as_float(0x7fc00000u);
