@@ -15,7 +15,7 @@ def _check_common(c):
     assert x.stride(2) == 1
     tv = t.reshape(-1).numpy()
     assert np.all((tv == -100) | ((tv >= 0) & (tv < V)))
-    assert 0.0 <= c["alpha"] <= 0.5
+    assert 0.0 <= c["alpha"] <= (1.0 if c["wide"] else 0.5)
     assert not (c["smoothing"] == "others" and V == 1 and c["alpha"] > 0)
     if c["g"] is not None and c["reduce"] == "none":
         assert len(c["g"]) == d0 * d1
@@ -23,7 +23,7 @@ def _check_common(c):
 
 def test_fused_cases_valid():
     kinds = set()
-    for seed in range(cases.N_FUSED):
+    for seed in cases.seeds(cases.N_FUSED):
         c = cases.fused_case(seed)
         _check_common(c)
         kinds.add(c["what"].split()[3])
@@ -35,7 +35,7 @@ def test_fused_cases_valid():
 
 
 def test_shard_cases_valid():
-    for seed in range(cases.N_SHARDS):
+    for seed in cases.seeds(cases.N_SHARDS):
         c = cases.shard_case(seed)
         _check_common(c)
         b = c["bounds"]
@@ -52,9 +52,9 @@ def test_cases_are_reproducible():
 
 
 def test_split_and_shard_flow_cases_valid():
-    for seed in range(cases.N_SPLIT):
+    for seed in cases.seeds(cases.N_SPLIT):
         _check_common(cases.split_case(seed))
-    for seed in range(cases.N_SHARD_FLOW):
+    for seed in cases.seeds(cases.N_SHARD_FLOW):
         c = cases.shard_flow_case(seed)
         _check_common(c)
         b = c["bounds"]

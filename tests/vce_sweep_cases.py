@@ -23,13 +23,22 @@ MAX_ELEMS = 1_500_000
 MAX_V = 200_000
 MAX_CHUNK_VECS = 4096   # one chunk of the fused call holds at most this many 16-byte vectors
 MAX_CHUNKS = 64         # chunks per row
+# Seeds from WIDE_FROM on draw logits of sigma up to 20 (lse near 50) and
+# smoothing weights up to 1; each sweep also runs N_WIDE of them.
+WIDE_FROM = 20000
+N_WIDE = 24
+
+
+def seeds(n: int) -> list[int]:
+    """The sweep's seeds for one kind of call: n ordinary ones, then N_WIDE wide ones."""
+    return list(range(n)) + list(range(WIDE_FROM, WIDE_FROM + N_WIDE))
 
 
 def elems_per_vector(dtype) -> int:
     return 8 if dtype == torch.bfloat16 else 4
 
 
-def _draw_common(rng: np.random.Generator, v_min: int = 1):
+def _draw_common(rng: np.random.Generator, v_min: int = 1, wide: bool = False):
     dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float32
     V = int(round(math.exp(rng.uniform(math.log(max(v_min, 1)), math.log(MAX_V)))))
     V = max(v_min, min(MAX_V, V))
@@ -41,9 +50,12 @@ def _draw_common(rng: np.random.Generator, v_min: int = 1):
     kind = str(rng.choice(["contiguous", "padded", "misaligned", "transposed"]))
     pad = int(rng.integers(1, 40)) if kind in ("padded", "misaligned") else 0
     off = int(rng.integers(1, 8)) if kind == "misaligned" else 0
-    sigma = float(rng.choice([0.5, 2.0, 6.0]))
+    sigma = float(rng.choice([0.5, 2.0, 6.0, 20.0] if wide else [0.5, 2.0, 6.0]))
     ignore_frac = float(rng.choice([0.0, 0.1, 0.5, 1.0], p=[0.3, 0.45, 0.2, 0.05]))
-    alpha = 0.0 if rng.random() < 0.3 else float(np.float32(rng.uniform(0.01, 0.5)))
+    if wide:
+        alpha = 0.0 if rng.random() < 0.2 else float(np.float32(rng.uniform(0.01, 1.0)))
+    else:
+        alpha = 0.0 if rng.random() < 0.3 else float(np.float32(rng.uniform(0.01, 0.5)))
     smoothing = "others" if rng.random() < 0.35 else "all"
     if smoothing == "others" and V == 1 and alpha > 0:
         smoothing = "all"
@@ -62,12 +74,13 @@ def _draw_common(rng: np.random.Generator, v_min: int = 1):
         x, t = x.transpose(0, 1), t.transpose(0, 1)
     what = (f"{'bf16' if dtype == torch.bfloat16 else 'f32'} V={V} rows={rows} {kind} sigma={sigma} "
             f"ignored={ignore_frac} a={alpha} {smoothing} {reduce} g={'1' if g is None else 'drawn'}")
-    return dict(x=x, t=t, alpha=alpha, smoothing=smoothing, reduce=reduce, g=g, dtype=dtype, V=V, what=what)
+    return dict(x=x, t=t, alpha=alpha, smoothing=smoothing, reduce=reduce, g=g, dtype=dtype, V=V, what=what,
+                wide=wide)
 
 
 def fused_case(seed: int) -> dict:
     rng = np.random.default_rng(1000 + seed)
-    c = _draw_common(rng)
+    c = _draw_common(rng, wide=seed >= WIDE_FROM)
     nv = c["V"] // elems_per_vector(c["dtype"])
     K = 0
     if c["V"] > 64 and rng.random() < 0.35:  # rows of at most 64 columns take the FP64 whole-row path
@@ -82,7 +95,7 @@ def fused_case(seed: int) -> dict:
 
 def shard_case(seed: int) -> dict:
     rng = np.random.default_rng(5000 + seed)
-    c = _draw_common(rng, v_min=2)
+    c = _draw_common(rng, v_min=2, wide=seed >= WIDE_FROM)
     V, E = c["V"], elems_per_vector(c["dtype"])
     S = int(rng.integers(1, min(16, V) + 1))
     while True:
@@ -100,12 +113,12 @@ def shard_case(seed: int) -> dict:
 
 
 def split_case(seed: int) -> dict:
-    return _draw_common(np.random.default_rng(9000 + seed))
+    return _draw_common(np.random.default_rng(9000 + seed), wide=seed >= WIDE_FROM)
 
 
 def shard_flow_case(seed: int) -> dict:
     rng = np.random.default_rng(12000 + seed)
-    c = _draw_common(rng, v_min=2)
+    c = _draw_common(rng, v_min=2, wide=seed >= WIDE_FROM)
     V = c["V"]
     S = int(rng.integers(1, min(16, V) + 1))
     cuts = np.sort(rng.choice(np.arange(1, V), size=S - 1, replace=False)) if S > 1 else np.array([], int)
