@@ -404,3 +404,18 @@ def test_last_error_is_per_thread(lib):
     for t in threads:
         t.join()
     assert results == {"dtype": True, "reduce": True}
+
+
+def test_device_build_contracts_within_expressions_only():
+    """The kernels round m log2(e) once and reuse that value so its rounding
+    cancels between the sum's terms and its rescaling; hipcc's default
+    contraction across statements would fuse the product, unrounded, into a
+    later subtraction.  The device build must keep -ffp-contract=on."""
+    import importlib.util
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "vocab_cross_entropy_amd", "csrc", "build.py")
+    spec = importlib.util.spec_from_file_location("vce_build_flags", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert "-ffp-contract=on" in mod.DEVICE
+    assert not any(f.startswith("-ffp-contract=") and f != "-ffp-contract=on" for f in mod.DEVICE + mod.COMMON)
