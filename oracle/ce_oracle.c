@@ -52,10 +52,14 @@
  *   MAX all-reduce, a SUM all-reduce and a gather of the target logit;
  *   issue #29 section 6 gathers the per-rank (m, d, X_y) triple):
  *     shard k holds global columns [o_k, o_k + V_k)
- *     m_k = max_j x_j,  d_k = sum_j exp(x_j - m_k),
+ *     m_k = max_j x_j,  d_k = sum_{j != t} exp(x_j - m_k),
  *     y_k = x[t - o_k] if o_k <= t < o_k + V_k else 0,  r_k = sum_j x_j
- *     M = max_k m_k,  D = sum_k d_k exp(m_k - M),  lse = M + log D,
- *     x_t = sum_k y_k,  R = sum_k r_k,
+ *     M = max_k m_k,  x_t = sum_k y_k,  R = sum_k r_k,
+ *     D = sum_k d_k exp(m_k - M) + exp(x_t - M),  lse = M + log D,
+ *   d_k leaves out the target's own term (only the shard holding the target
+ *   has one) and the combine restores it from the gathered target logit;
+ *   the sum is the same, and 1 - p_t = (D - exp(x_t - M)) / D is then the
+ *   combine's first term over D, with no difference of nearly equal numbers.
  *     loss = lse - (1 - a) x_t - (a / V) R                        (OR_SMOOTH_ALL)
  *     loss = (1 - a)(lse - x_t) + a ((V - 1) lse - (R - x_t)) / (V - 1)
  *                                                                 (OR_SMOOTH_OTHERS)
@@ -256,8 +260,8 @@ double or_sum_loss(const double* loss, int64_t nrows) {
 
 /*
  * Per-shard statistics of the listed rows: stats_out[k*4 + {0,1,2,3}] =
- * (m, d, y, r) as defined in the header comment.  Targets are global.
- * Ignored rows get (0, 0, 0, 0).
+ * (m, d, y, r) as defined in the header comment (d without the target's
+ * term).  Targets are global.  Ignored rows get (0, 0, 0, 0).
  */
 int or_shard_stats(const or_logits* x, const or_targets* t, int64_t ignore_idx,
                    const int64_t* rows, int64_t nrows, double* stats_out) {
@@ -281,7 +285,7 @@ int or_shard_stats(const or_logits* x, const or_targets* t, int64_t ignore_idx,
     double d = 0.0, rs = 0.0;
     for (int64_t j = 0; j < V; ++j) {
       double v = or_elem(x, off + j);
-      d += exp(v - m);
+      if (o + j != tgt) d += exp(v - m);
       rs += v;
     }
     st[0] = m;
@@ -325,6 +329,7 @@ int or_shard_combine(const double* stats, int32_t S, int64_t nrows, int64_t voca
       xt += st[2];
       R += st[3];
     }
+    D += exp(xt - M); /* the target's term, left out of every d_k */
     double lse = M + log(D);
     /* terms with a zero weight are left out (0 log 0 = 0), so masked (-inf) logits only matter where q > 0 */
     if (smooth == OR_SMOOTH_OTHERS) {

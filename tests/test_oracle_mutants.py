@@ -50,6 +50,8 @@ MUTANTS = [
     ("linear_bf16_widened_wrong", "((const uint16_t*)p)[off] << 16;", "((const uint16_t*)p)[off] << 15;", 1),
     ("combine_no_rescale", "D += st[1] * exp(st[0] - M);", "D += st[1];", 1),
     ("combine_drops_target_gather", "xt += st[2];", "xt = st[2];", 1),
+    ("combine_forgets_target_term", "D += exp(xt - M); /* the target's term", "D += 0.0; /* the target's term", 1),
+    ("shard_stats_keep_target_term", "if (o + j != tgt) d += exp(v - m);", "d += exp(v - m);", 1),
     ("combine_others_sign", "(R - xt)) / (double)(vocab_total - 1)", "(R + xt)) / (double)(vocab_total - 1)", 1),
     ("combine_ignores_convention", "if (smooth == OR_SMOOTH_OTHERS) {\n      double loss",
      "if (0) {\n      double loss", 1),
