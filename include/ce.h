@@ -72,8 +72,10 @@
 extern "C" {
 #endif
 
-/* 3: ce_shards_workspace_bytes and ce_shards_fwd_bwd_fused added */
-#define CE_ABI_VERSION 3
+/* 3: ce_shards_workspace_bytes and ce_shards_fwd_bwd_fused added
+ * 4: the backward hand-off pair lse_aux (ce_forward_ex, ce_shard_combine_ex,
+ *    ce_backward_inplace_ex); a shard's statistic d leaves out the target */
+#define CE_ABI_VERSION 4
 
 typedef enum ce_status {
   CE_OK = 0,
@@ -152,9 +154,28 @@ size_t ce_combine_workspace_bytes(int64_t rows, const ce_params* p);
  *   lse     [N] device FP32 or NULL; ignored rows get 0
  *   n_valid [1] device int32 or NULL: number of non-ignored rows
  *   ws      device workspace of at least ce_workspace_bytes(x, p) bytes
+ * The same as ce_forward_ex with lse_aux NULL.
  */
 ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p, float* loss, float* lse,
                      int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The backward hand-off.  Issue #29 section 6 hands the backward the gathered
+ * per-rank statistics (m, d, X_y), not a rounded lse; an FP32 lse alone
+ * resolves p_t - 1 only to about ulp(lse) where the target holds nearly all
+ * the probability.  The forward calls can therefore also write, per row,
+ *   lse_aux[r][0] = the residual of lse: lse[r] + lse_aux[r][0] is the row's
+ *                   log-sum-exp as the forward's FP32 sums give it, without
+ *                   the final rounding to FP32;
+ *   lse_aux[r][1] = 1 - p_t = sum_{j != t} softmax_j, from a sum that leaves
+ *                   the target's own term out, so it keeps its digits as
+ *                   p_t approaches 1;
+ * device FP32 [N][2], 8-byte aligned; ignored rows get (0, 0), rows with an
+ * invalid target NaN.  ce_backward_inplace_ex given the pair forms the fused
+ * call's gradient: s ((1 - q_t) - (1 - p_t)) at a target with p_t > 1/2.
+ */
+ce_status ce_forward_ex(const ce_logits* x, const ce_targets* t, const ce_params* p, float* loss, float* lse,
+                        float* lse_aux, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Backward, gradient written in place over the logits in their own dtype
@@ -162,14 +183,22 @@ ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p
  * may be a vocabulary shard: column j is global column vocab_start + j and
  * the smoothing's V is vocab_total (hyper-parallel #269 section 3.1: the
  * backward needs no collective).
- *   lse       [N] device FP32 from ce_forward or ce_shard_combine
+ *   lse       [N] device FP32 from ce_forward(_ex) or ce_shard_combine(_ex)
+ *   lse_aux   [N][2] device FP32 from the same call's lse_aux, or NULL
+ *             (ce_backward_inplace): then 1 - p_t comes from expm1(x_t - lse)
+ *             and carries the FP32 lse's resolution
  *   grad_out  device FP32: [N] per-row upstream gradient (CE_REDUCE_NONE) or
  *             [1] (mean, sum); NULL means 1
  *   n_valid   [1] device int32, required with CE_REDUCE_MEAN (unused otherwise)
- * Ignored rows are set to +0.0 without being read.
+ * Ignored rows are set to +0.0 without being read.  Unsharded rows of at
+ * most 128 columns are recomputed whole from the logits in FP64 (one wave per
+ * row), as the fused call computes them; lse and lse_aux are not read there.
  */
 ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* lse,
                               const float* grad_out, const int32_t* n_valid, hipStream_t stream);
+ce_status ce_backward_inplace_ex(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* lse,
+                                 const float* lse_aux, const float* grad_out, const int32_t* n_valid,
+                                 hipStream_t stream);
 
 /*
  * Fused forward + backward: one read of the logits, the gradient written
@@ -239,10 +268,15 @@ ce_status ce_scale_grad_inplace(const ce_logits* x, const float* grad_out, int32
  * hyper-parallel #269 section 3.1 reduces MAX and SUM and gathers the target
  * logit).  For every logical row of the shard:
  *   stats[r*4 + 0] = m = max_j x_rj                      (natural units)
- *   stats[r*4 + 1] = d = sum_j exp(x_rj - m)
+ *   stats[r*4 + 1] = d = sum_{j != t_r} exp(x_rj - m)   (the target's own term
+ *                    left out; only the shard that holds t_r has it)
  *   stats[r*4 + 2] = y = x_r,(t_r - vocab_start) if the shard holds t_r, else 0
  *   stats[r*4 + 3] = r = sum_j x_rj
- * Ignored rows are not read and get (0, 0, 0, 0).  `stats` is device FP32 [N][4].
+ * The combine restores the target's term from y, and keeping it out of d
+ * keeps 1 - p_t = D_excl / D exact to the sum's precision when the target
+ * holds nearly all the probability.  Rows of at most 128 columns are summed
+ * in FP64 and rounded once.  Ignored rows are not read and get (0, 0, 0, 0).
+ * `stats` is device FP32 [N][4].
  */
 ce_status ce_shard_partial_stats(const ce_logits* shard, const ce_targets* t, const ce_params* p, float* stats,
                                  hipStream_t stream);
@@ -250,17 +284,24 @@ ce_status ce_shard_partial_stats(const ce_logits* shard, const ce_targets* t, co
 /*
  * Combine S shards' statistics stats[S][N][4] (device FP32, shard-major) into
  * per-row loss and lse over the full vocabulary of vocab_total columns:
- *   M = max_s m_s, D = sum_s d_s exp(m_s - M) (s ascending), lse = M + log D,
- *   loss = lse - (q_t - q_o) sum_s y_s - q_o sum_s r_s,
- * q_t and q_o being the smoothed target probability of the target and of
- * any other class (a / V + 1 - a and a / V, or 1 - a and a / (V - 1)).
- * This is the point where a multi-GPU run would exchange the statistics.
+ *   M = max_s m_s, D_excl = sum_s d_s exp(m_s - M) (s ascending),
+ *   x_t = sum_s y_s, D = D_excl + exp(x_t - M), lse = M + log D,
+ *   loss = lse - (q_t - q_o) x_t - q_o sum_s r_s,
+ * in FP64, each output rounded once to FP32; q_t and q_o are the smoothed
+ * target probability of the target and of any other class (a / V + 1 - a
+ * and a / V, or 1 - a and a / (V - 1)).  This is the point where a multi-GPU
+ * run would exchange the statistics.
  *   loss [N] or [1], lse [N] (may be NULL), n_valid [1] (may be NULL),
  *   ws of at least ce_combine_workspace_bytes(d0 * d1, p) bytes.
+ * ce_shard_combine_ex also writes the backward hand-off pair lse_aux [N][2]
+ * (see ce_forward_ex; may be NULL) with 1 - p_t = D_excl / D.
  */
 ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1, int64_t vocab_total,
                            const ce_targets* t, const ce_params* p, float* loss, float* lse, int32_t* n_valid,
                            void* ws, size_t ws_bytes, hipStream_t stream);
+ce_status ce_shard_combine_ex(const float* stats, int32_t S, int64_t d0, int64_t d1, int64_t vocab_total,
+                              const ce_targets* t, const ce_params* p, float* loss, float* lse, float* lse_aux,
+                              int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Chunked linear + cross-entropy: the language-model head's matrix product

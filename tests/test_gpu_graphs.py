@@ -61,8 +61,9 @@ def _replay_matches_eager(run, buffers, outputs, what):
             torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("form", ["lse", "ex"])
 @pytest.mark.parametrize("reduce", ["none", "mean"])
-def test_forward_backward_graph_replays(reduce):
+def test_forward_backward_graph_replays(reduce, form):
     x = _logits((2, 9, 5003), torch.bfloat16, seed=81)
     t = workloads.random_targets((2, 9), 5003, seed=81, ignore_frac=0.2)
     xd, td = to_device_view(x), to_device_view(t)
@@ -74,15 +75,22 @@ def test_forward_backward_graph_replays(reduce):
     n = torch.empty(1, dtype=torch.int32, device="cuda")
     g = torch.full((1,) if reduce != "none" else (N,), 0.75, dtype=torch.float32, device="cuda")
 
+    aux = torch.empty((N, 2), dtype=torch.float32, device="cuda") if form == "ex" else None
+
     def run():
-        vce.ce_forward(xd, td, 0.1, reduce, loss=loss, lse=lse, n_valid=n, ws=ws)
-        vce.ce_backward_inplace(xd, td, lse, 0.1, reduce, grad_out=g, n_valid=n)
+        if form == "ex":
+            vce.ce_forward_ex(xd, td, 0.1, reduce, loss=loss, lse=lse, lse_aux=aux, n_valid=n, ws=ws)
+        else:
+            vce.ce_forward(xd, td, 0.1, reduce, loss=loss, lse=lse, n_valid=n, ws=ws)
+        vce.ce_backward_inplace_ex(xd, td, lse, aux, 0.1, reduce, grad_out=g, n_valid=n)
 
-    _replay_matches_eager(run, [xd], [xd, loss, lse, n], f"forward + backward {reduce}")
+    outs = [xd, loss, lse, n] + ([aux] if form == "ex" else [])
+    _replay_matches_eager(run, [xd], outs, f"forward + backward {reduce} {form}")
 
 
+@pytest.mark.parametrize("form", ["lse", "ex"])
 @pytest.mark.parametrize("reduce", ["none", "sum"])
-def test_three_call_shard_flow_graph_replays(reduce):
+def test_three_call_shard_flow_graph_replays(reduce, form):
     V = 9001
     x = _logits((2, 8, V), torch.bfloat16, seed=82)
     t = workloads.random_targets((2, 8), V, seed=82, ignore_frac=0.2)
@@ -97,12 +105,18 @@ def test_three_call_shard_flow_graph_replays(reduce):
     ws = torch.empty(vce.ce_combine_workspace_bytes(N, reduce), dtype=torch.uint8, device="cuda")
     g = torch.full((1,) if reduce != "none" else (N,), 1.25, dtype=torch.float32, device="cuda")
 
+    aux = torch.empty((N, 2), dtype=torch.float32, device="cuda") if form == "ex" else None
+
     def run():
         for s, (a, b) in enumerate(bounds):
             vce.ce_shard_partial_stats(shards[s], td, a, V, stats=stats[s])
-        vce.ce_shard_combine(stats, td, V, 0.1, reduce, loss=loss, lse=lse, n_valid=n, ws=ws)
+        if form == "ex":
+            vce.ce_shard_combine_ex(stats, td, V, 0.1, reduce, loss=loss, lse=lse, lse_aux=aux, n_valid=n, ws=ws)
+        else:
+            vce.ce_shard_combine(stats, td, V, 0.1, reduce, loss=loss, lse=lse, n_valid=n, ws=ws)
         for s, (a, b) in enumerate(bounds):
-            vce.ce_backward_inplace(shards[s], td, lse, 0.1, reduce, grad_out=g, n_valid=n, vocab_start=a,
-                                    vocab_total=V)
+            vce.ce_backward_inplace_ex(shards[s], td, lse, aux, 0.1, reduce, grad_out=g, n_valid=n, vocab_start=a,
+                                       vocab_total=V)
 
-    _replay_matches_eager(run, shards, shards + [stats, loss, lse, n], f"three-call shard flow {reduce}")
+    outs = shards + [stats, loss, lse, n] + ([aux] if form == "ex" else [])
+    _replay_matches_eager(run, shards, outs, f"three-call shard flow {reduce} {form}")

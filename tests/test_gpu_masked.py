@@ -88,23 +88,31 @@ def test_fused_masked(dtype, V, pattern, K, smoothing, alpha):
 def test_forward_backward_masked(dtype, alpha):
     x, t = masked_case(dtype, 4099, "scatter", seed=77)
     N = t.numel()
-    say(f"[masked fwd+bwd] {dtype} a={alpha}")
-    xd, td = to_device_view(x), to_device_view(t)
-    loss, lse, n = vce.ce_forward(xd, td, alpha, False)
-    g = torch.ones(N, dtype=torch.float32, device="cuda")
-    vce.ce_backward_inplace(xd, td, lse, alpha, False, grad_out=g, n_valid=n)
-    torch.cuda.synchronize()
     o = orc()
     ref_rows, ref_lse = o.loss_rows(x, t, alpha)
-    assert_loss_inf(loss.cpu().numpy(), ref_rows, "masked forward rows")
-    kept = t.reshape(-1).numpy() != -100
-    assert_loss(lse.cpu().numpy()[kept], ref_lse[kept], "masked lse")
-    grad = rows_f64(xd)
-    assert np.all(np.isfinite(grad))
-    # the rebuilt target gradient carries the FP32 lse's error (as for unmasked rows)
     ref_g = o.grad_rows(x, t, alpha, g=np.ones(N))
-    assert_grad_from_lse(grad, ref_g, dtype, lse.cpu().numpy(), t.reshape(-1).numpy(), np.ones(N),
-                         x.shape[-1], "masked backward")
+    kept = t.reshape(-1).numpy() != -100
+    for form in ("ex", "lse"):
+        say(f"[masked fwd+bwd {form}] {dtype} a={alpha}")
+        xd, td = to_device_view(x), to_device_view(t)
+        g = torch.ones(N, dtype=torch.float32, device="cuda")
+        if form == "ex":
+            loss, lse, aux, n = vce.ce_forward_ex(xd, td, alpha, False)
+            vce.ce_backward_inplace_ex(xd, td, lse, aux, alpha, False, grad_out=g, n_valid=n)
+        else:
+            loss, lse, n = vce.ce_forward(xd, td, alpha, False)
+            vce.ce_backward_inplace(xd, td, lse, alpha, False, grad_out=g, n_valid=n)
+        torch.cuda.synchronize()
+        assert_loss_inf(loss.cpu().numpy(), ref_rows, f"masked forward rows [{form}]")
+        assert_loss(lse.cpu().numpy()[kept], ref_lse[kept], f"masked lse [{form}]")
+        grad = rows_f64(xd)
+        assert np.all(np.isfinite(grad))
+        if form == "ex":
+            assert_grad(grad, ref_g, dtype, "masked backward [ex]")
+        else:
+            # the FP32 lse alone: the rebuilt target gradient carries its resolution (as for unmasked rows)
+            assert_grad_from_lse(grad, ref_g, dtype, lse.cpu().numpy(), t.reshape(-1).numpy(), np.ones(N),
+                                 x.shape[-1], "masked backward [lse]")
 
 
 @pytest.mark.parametrize("alpha", [0.0, 0.1])
@@ -119,9 +127,18 @@ def test_shard_flow_masked(alpha):
     stats = torch.empty((len(bounds), N, 4), dtype=torch.float32, device="cuda")
     for s, (a, b) in enumerate(bounds):
         vce.ce_shard_partial_stats(shards[s], td, a, V, stats=stats[s])
-    loss, lse, n = vce.ce_shard_combine(stats, td, V, alpha, False)
+    loss, lse, aux, n = vce.ce_shard_combine_ex(stats, td, V, alpha, False)
+    g = torch.ones(N, dtype=torch.float32, device="cuda")
+    for s, (a, b) in enumerate(bounds):
+        vce.ce_backward_inplace_ex(shards[s], td, lse, aux, alpha, False, grad_out=g, n_valid=n, vocab_start=a,
+                                   vocab_total=V)
     torch.cuda.synchronize()
     o = orc()
     ref_rows, _ = o.loss_rows(x, t, alpha)
     assert_loss_inf(loss.cpu().numpy(), ref_rows, "masked shard loss")
     assert math.isfinite(float(lse.cpu().numpy()[t.reshape(-1).numpy() != -100].max()))
+    ref_g = o.grad_rows(x, t, alpha, g=np.ones(N))
+    for s, (a, b) in enumerate(bounds):
+        grad = rows_f64(shards[s])
+        assert np.all(np.isfinite(grad)), f"shard {s}: non-finite gradient"
+        assert_grad(grad, ref_g[:, a:b], torch.bfloat16, f"masked shard {s}")

@@ -20,7 +20,8 @@ import torch
 
 import vocab_cross_entropy_amd as vce
 import workloads
-from gpu_util import assert_grad, assert_loss, ignored_rows, orc, raw_bits, rows_f64, say, to_device_view
+from gpu_util import (assert_grad, assert_loss, check_shard_flow, check_split, ignored_rows, orc, raw_bits, rows_f64,
+                      say, to_device_view)
 from test_gpu_parity import _g_tensor, _reduced, check_fused
 
 pytestmark = pytest.mark.gpu
@@ -88,27 +89,9 @@ def test_fused_128000_columns(smoothing):
 def test_forward_backward_options(dtype, smoothing, reduce):
     w = workloads.Workload(95, "fb-options", (3, 8), 2053, dtype, 2.0, 0.2, 0.3, reduce != "none", swapped=True)
     inp = workloads.generate(w)
-    x, t = inp.logits, inp.targets
-    say(f"[fwd+bwd options] {dtype} {smoothing} {reduce}")
-    xd, td = to_device_view(x), to_device_view(t)
-    loss, lse, n = vce.ce_forward(xd, td, 0.3, reduce, smoothing=smoothing)
     gv = np.linspace(0.5, -0.5, w.rows) if reduce == "none" else 1.3
-    vce.ce_backward_inplace(xd, td, lse, 0.3, reduce, grad_out=_g_tensor(gv, reduce), n_valid=n,
-                            smoothing=smoothing)
-    torch.cuda.synchronize()
-    o = orc()
-    n_ref = o.count_valid(t)
-    assert int(n.item()) == n_ref
-    loss_ref, lse_ref = o.loss_rows(x, t, 0.3, smoothing=smoothing)
-    if _reduced(reduce):
-        assert_loss([loss.item()], [o.reduce(loss_ref, reduce, n_ref)], f"forward {reduce}")
-    else:
-        assert_loss(loss.cpu().numpy(), loss_ref, "forward rows")
-    kept = t.reshape(-1).numpy() != -100
-    assert_loss(lse.cpu().numpy()[kept], lse_ref[kept], "lse")
-    grad_ref = o.grad_rows(x, t, 0.3, reduce_loss=reduce, g=gv, n_valid=n_ref, smoothing=smoothing)
-    assert_grad(rows_f64(xd), grad_ref, dtype, f"backward {smoothing} {reduce}")
-    assert not raw_bits(xd, ignored_rows(t)).any()
+    check_split(inp.logits, inp.targets, 0.3, reduce, g=gv, smoothing=smoothing,
+                what=f"fwd+bwd options {dtype} {smoothing} {reduce}")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -118,30 +101,9 @@ def test_shard_flow_options(dtype, smoothing, reduce):
     V, S = 5003, 4
     w = workloads.Workload(96, "shard-options", (2, 6), V, dtype, 2.0, 0.1, 0.2, reduce != "none", shards=S)
     inp = workloads.generate(w)
-    x, t = inp.logits, inp.targets
-    N = w.rows
-    bounds = workloads.shard_bounds(V, S)
-    say(f"[shards options] {dtype} {smoothing} {reduce}")
-    td = to_device_view(t)
-    shards = [x[..., a:b].contiguous().cuda() for a, b in bounds]
-    stats = torch.empty((len(bounds), N, 4), dtype=torch.float32, device="cuda")
-    for s, (a, b) in enumerate(bounds):
-        vce.ce_shard_partial_stats(shards[s], td, a, V, stats=stats[s])
-    loss, lse, n = vce.ce_shard_combine(stats, td, V, 0.2, reduce, smoothing=smoothing)
-    gv = np.linspace(1.0, 2.0, N) if reduce == "none" else 0.9
-    for s, (a, b) in enumerate(bounds):
-        vce.ce_backward_inplace(shards[s], td, lse, 0.2, reduce, grad_out=_g_tensor(gv, reduce), n_valid=n,
-                                vocab_start=a, vocab_total=V, smoothing=smoothing)
-    torch.cuda.synchronize()
-    o = orc()
-    loss_ref, _ = o.loss_rows(x, t, 0.2, smoothing=smoothing)
-    if reduce == "sum":
-        assert_loss([loss.item()], [o.sum_loss(loss_ref)], "shard sum")
-    else:
-        assert_loss(loss.cpu().numpy(), loss_ref, "shard rows")
-    grad_ref = o.grad_rows(x, t, 0.2, reduce_loss=reduce, g=gv, smoothing=smoothing)
-    for s, (a, b) in enumerate(bounds):
-        assert_grad(rows_f64(shards[s]), grad_ref[:, a:b], dtype, f"shard {s} {smoothing} {reduce}")
+    gv = np.linspace(1.0, 2.0, w.rows) if reduce == "none" else 0.9
+    check_shard_flow(inp.logits, inp.targets, workloads.shard_bounds(V, S), 0.2, reduce, g=gv, smoothing=smoothing,
+                     what=f"shards options {dtype} {smoothing} {reduce}")
 
 
 # ---------------------------------------------------------------------------

@@ -23,6 +23,7 @@ MAX_ELEMS = 1_500_000
 MAX_V = 200_000
 MAX_CHUNK_VECS = 4096   # one chunk of the fused call holds at most this many 16-byte vectors
 MAX_CHUNKS = 64         # chunks per row
+SHORT_ROW = 128         # whole rows of at most this many columns take the library's FP64 path
 # Seeds from WIDE_FROM on draw logits of sigma up to 20 (lse near 50) and
 # smoothing weights up to 1; each sweep also runs N_WIDE of them.
 WIDE_FROM = 20000
@@ -38,7 +39,8 @@ def elems_per_vector(dtype) -> int:
     return 8 if dtype == torch.bfloat16 else 4
 
 
-def _draw_common(rng: np.random.Generator, v_min: int = 1, wide: bool = False):
+def _draw_params(rng: np.random.Generator, v_min: int = 1, wide: bool = False) -> dict:
+    """The case's options, from the numpy generator only (no tensors)."""
     dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float32
     V = int(round(math.exp(rng.uniform(math.log(max(v_min, 1)), math.log(MAX_V)))))
     V = max(v_min, min(MAX_V, V))
@@ -66,16 +68,28 @@ def _draw_common(rng: np.random.Generator, v_min: int = 1, wide: bool = False):
     else:
         g = None if rng.random() < 0.3 else float(np.float32(rng.uniform(-2.0, 2.0)))
     seed = int(rng.integers(0, 2**31 - 1))
-    gen = torch.Generator().manual_seed(seed)
-    phys = (torch.randn((A, B, V + pad + off), generator=gen) * sigma).to(dtype)
+    return dict(dtype=dtype, V=V, A=A, B=B, kind=kind, pad=pad, off=off, sigma=sigma, ignore_frac=ignore_frac,
+                alpha=alpha, smoothing=smoothing, reduce=reduce, g=g, seed=seed, wide=wide)
+
+
+def _materialize(c: dict) -> dict:
+    """The case's logits and targets, from its torch seed."""
+    A, B, V, dtype, kind, pad, off = c["A"], c["B"], c["V"], c["dtype"], c["kind"], c["pad"], c["off"]
+    gen = torch.Generator().manual_seed(c["seed"])
+    phys = (torch.randn((A, B, V + pad + off), generator=gen) * c["sigma"]).to(dtype)
     x = phys[..., off:off + V]
-    t = workloads.random_targets((A, B), V, seed=seed, ignore_frac=ignore_frac)
+    t = workloads.random_targets((A, B), V, seed=c["seed"], ignore_frac=c["ignore_frac"])
     if kind == "transposed":
         x, t = x.transpose(0, 1), t.transpose(0, 1)
-    what = (f"{'bf16' if dtype == torch.bfloat16 else 'f32'} V={V} rows={rows} {kind} sigma={sigma} "
-            f"ignored={ignore_frac} a={alpha} {smoothing} {reduce} g={'1' if g is None else 'drawn'}")
-    return dict(x=x, t=t, alpha=alpha, smoothing=smoothing, reduce=reduce, g=g, dtype=dtype, V=V, what=what,
-                wide=wide)
+    what = (f"{'bf16' if dtype == torch.bfloat16 else 'f32'} V={V} rows={A * B} {kind} sigma={c['sigma']} "
+            f"ignored={c['ignore_frac']} a={c['alpha']} {c['smoothing']} {c['reduce']} "
+            f"g={'1' if c['g'] is None else 'drawn'}")
+    return dict(x=x, t=t, alpha=c["alpha"], smoothing=c["smoothing"], reduce=c["reduce"], g=c["g"], dtype=dtype,
+                V=V, what=what, wide=c["wide"])
+
+
+def _draw_common(rng: np.random.Generator, v_min: int = 1, wide: bool = False):
+    return _materialize(_draw_params(rng, v_min, wide))
 
 
 def fused_case(seed: int) -> dict:
@@ -83,7 +97,7 @@ def fused_case(seed: int) -> dict:
     c = _draw_common(rng, wide=seed >= WIDE_FROM)
     nv = c["V"] // elems_per_vector(c["dtype"])
     K = 0
-    if c["V"] > 64 and rng.random() < 0.35:  # rows of at most 64 columns take the FP64 whole-row path
+    if c["V"] > SHORT_ROW and rng.random() < 0.35:  # rows of at most SHORT_ROW columns take the FP64 path
         lo = max(1, -(-nv // MAX_CHUNK_VECS))
         hi = min(MAX_CHUNKS, nv)
         if hi >= lo:
@@ -110,6 +124,19 @@ def shard_case(seed: int) -> dict:
     c["separate"] = bool(rng.random() < 0.5)
     c["what"] += f" S={S} widths={[b - a for a, b in c['bounds']][:6]}{'...' if S > 6 else ''}"
     return c
+
+
+def wide_short_row_seeds(kind: str, first: int, last: int, v_lo: int, v_hi: int, min_alpha: float) -> list[int]:
+    """Seeds in [first, last) whose fused ("fused") or shard ("shards") case has
+    FP32 logits, v_lo <= V <= v_hi and smoothing above min_alpha (numpy draws
+    only, so scanning thousands of seeds costs no tensors)."""
+    base, v_min = {"fused": (1000, 1), "shards": (5000, 2)}[kind]
+    out = []
+    for seed in range(first, last):
+        c = _draw_params(np.random.default_rng(base + seed), v_min=v_min, wide=seed >= WIDE_FROM)
+        if c["dtype"] == torch.float32 and v_lo <= c["V"] <= v_hi and c["alpha"] > min_alpha:
+            out.append(seed)
+    return out
 
 
 def split_case(seed: int) -> dict:

@@ -9,6 +9,8 @@ provides device memory and streams.
 Entry points with the C names:
     ce_forward, ce_backward_inplace, ce_fwd_bwd_fused,
     ce_shard_partial_stats, ce_shard_combine
+    (and ce_forward_ex, ce_backward_inplace_ex, ce_shard_combine_ex, which
+    also hand the backward the lse residual and 1 - p_t)
 and the interface of the TransformerEngineNPU issue #29 page (section 1):
     parallel_cross_entropy(inp, target, label_smoothing=0.0, reduce_loss=False,
                            dist_process_group=None, ignore_idx=-100)
@@ -30,7 +32,8 @@ from . import _abi
 from ._abi import CE_BF16, CE_F32, CeArgumentError, CeError
 
 __all__ = [
-    "ce_forward", "ce_backward_inplace", "ce_fwd_bwd_fused", "ce_scale_grad_inplace", "ce_shard_partial_stats",
+    "ce_forward", "ce_backward_inplace", "ce_fwd_bwd_fused", "ce_forward_ex", "ce_backward_inplace_ex",
+    "ce_shard_combine_ex", "ce_scale_grad_inplace", "ce_shard_partial_stats",
     "ce_shard_combine", "ce_shards_fwd_bwd_fused", "ce_shards_workspace_bytes",
     "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_init", "ce_workspace_check",
     "ce_linear_workspace_bytes", "ce_linear_cross_entropy", "ce_linear_tune",
@@ -64,6 +67,43 @@ def _stream(device: torch.device):
         idx = device.index if device.index is not None else torch.cuda.current_device()
         return ctypes.c_void_p(_raw_stream(idx))
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _device_of(x, what="logits") -> torch.device:
+    """The GPU device of ``x``; anything else is refused before the library
+    sees a pointer (a host pointer handed to a kernel would fault the GPU)."""
+    if not isinstance(x, torch.Tensor):
+        raise CeArgumentError(_abi.CE_EINVAL, f"{what} must be a torch tensor")
+    if x.device.type != "cuda":
+        raise CeArgumentError(_abi.CE_EINVAL, f"{what} must be a GPU tensor, got one on {x.device}")
+    return x.device
+
+
+def _need(dev: torch.device, what: str, v, dtype=None, numel=0, contiguous=True):
+    """``v`` (a tensor or None) lives on ``dev``, has ``dtype`` and holds at
+    least ``numel`` elements (contiguous ones, for the flat buffers)."""
+    if v is None:
+        return
+    if not isinstance(v, torch.Tensor):
+        raise CeArgumentError(_abi.CE_EINVAL, f"{what} must be a torch tensor")
+    if v.device != dev:
+        raise CeArgumentError(_abi.CE_EINVAL, f"{what} is on {v.device}, the logits on {dev}")
+    if dtype is not None and v.dtype != dtype:
+        raise CeArgumentError(_abi.CE_EINVAL, f"{what} must be {dtype}, got {v.dtype}")
+    if v.numel() < numel:
+        raise CeArgumentError(_abi.CE_EINVAL, f"{what} holds {v.numel()} elements, {numel} needed")
+    if contiguous and not v.is_contiguous():
+        raise CeArgumentError(_abi.CE_ELAYOUT, f"{what} must be contiguous")
+
+
+def _need_targets(dev: torch.device, t, d0: int, d1: int):
+    _need(dev, "targets", t, torch.int64, contiguous=False)
+    if t is None or tuple(t.shape) != (d0, d1):
+        raise CeArgumentError(_abi.CE_EINVAL, f"targets must be a ({d0}, {d1}) int64 tensor")
+
+
+def _need_ws(dev: torch.device, ws):
+    _need(dev, "workspace", ws, torch.uint8)
 
 
 def _dtype_code(x: torch.Tensor) -> int:
@@ -143,6 +183,7 @@ def _is_prepared(ws: torch.Tensor) -> bool:
 
 def ce_workspace_init(ws: torch.Tensor) -> torch.Tensor:
     """Prepare ``ws`` (uint8 device tensor) for ce_fwd_bwd_fused; once is enough."""
+    _need_ws(_device_of(ws, "workspace"), ws)
     _check(lib.ce_workspace_init(_ptr(ws), ws.numel(), _stream(ws.device)))
     for k in [k for k, r in _prepared.items() if r() is None]:
         del _prepared[k]
@@ -167,32 +208,72 @@ def ce_combine_workspace_bytes(rows: int, reduce_loss=False) -> int:
     return int(n)
 
 
-def ce_forward(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, loss=None, lse=None,
-               n_valid=None, ws=None, want_lse=True, smoothing="all"):
-    """Forward only.  Returns (loss [N] or [1], lse [N] or None, n_valid [1])."""
+def _forward(x, t, label_smoothing, reduce_loss, ignore_idx, loss, lse, lse_aux, n_valid, ws, want_lse, want_aux,
+             smoothing):
+    dev = _device_of(x)
     N = x.shape[0] * x.shape[1]
-    dev = x.device
+    _need_targets(dev, t, x.shape[0], x.shape[1])
     p = params(label_smoothing, reduce_loss, ignore_idx, smoothing=smoothing)
     loss = _f32(1 if p.reduce_loss else N, dev) if loss is None else loss
     if lse is None and want_lse:
         lse = _f32(N, dev)
+    if lse_aux is None and want_aux:
+        lse_aux = torch.empty((N, 2), dtype=torch.float32, device=dev)
     n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
+    _need(dev, "loss", loss, torch.float32, 1 if p.reduce_loss else N)
+    _need(dev, "lse", lse, torch.float32, N)
+    _need(dev, "lse_aux", lse_aux, torch.float32, 2 * N)
+    _need(dev, "n_valid", n_valid, torch.int32, 1)
     xd = logits_desc(x)
     if ws is None:
         ws = _workspace(lib.ce_workspace_bytes(ctypes.byref(xd), ctypes.byref(p)), dev)
-    _check(lib.ce_forward(ctypes.byref(xd), ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(loss), _ptr(lse),
-                          _ptr(n_valid), _ptr(ws), ws.numel(), _stream(dev)))
+    _need_ws(dev, ws)
+    _check(lib.ce_forward_ex(ctypes.byref(xd), ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(loss),
+                             _ptr(lse), _ptr(lse_aux), _ptr(n_valid), _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, lse, lse_aux, n_valid
+
+
+def ce_forward(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, loss=None, lse=None,
+               n_valid=None, ws=None, want_lse=True, smoothing="all"):
+    """Forward only.  Returns (loss [N] or [1], lse [N] or None, n_valid [1])."""
+    loss, lse, _, n_valid = _forward(x, t, label_smoothing, reduce_loss, ignore_idx, loss, lse, None, n_valid, ws,
+                                     want_lse, False, smoothing)
     return loss, lse, n_valid
+
+
+def ce_forward_ex(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, loss=None, lse=None,
+                  lse_aux=None, n_valid=None, ws=None, smoothing="all"):
+    """Forward with the backward hand-off.  Returns (loss, lse [N], lse_aux
+    [N, 2] = (lse residual, 1 - p_t), n_valid [1]); ce_backward_inplace_ex
+    takes lse and lse_aux."""
+    return _forward(x, t, label_smoothing, reduce_loss, ignore_idx, loss, lse, lse_aux, n_valid, ws, True, True,
+                    smoothing)
+
+
+def ce_backward_inplace_ex(x, t, lse, lse_aux, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *,
+                           grad_out=None, n_valid=None, vocab_start=0, vocab_total=None, smoothing="all"):
+    """Writes the gradient over ``x`` (which may be a vocabulary shard) from
+    the forward's lse and, when not None, its lse_aux pair."""
+    dev = _device_of(x)
+    N = x.shape[0] * x.shape[1]
+    _need_targets(dev, t, x.shape[0], x.shape[1])
+    p = params(label_smoothing, reduce_loss, ignore_idx, smoothing=smoothing)
+    _need(dev, "lse", lse, torch.float32, N)
+    _need(dev, "lse_aux", lse_aux, torch.float32, 2 * N)
+    _need(dev, "grad_out", grad_out, torch.float32, N if p.reduce_loss == _abi.CE_REDUCE_NONE else 1)
+    _need(dev, "n_valid", n_valid, torch.int32, 1)
+    _check(lib.ce_backward_inplace_ex(ctypes.byref(logits_desc(x, vocab_start, vocab_total)),
+                                      ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(lse), _ptr(lse_aux),
+                                      _ptr(grad_out), _ptr(n_valid), _stream(dev)))
+    return x
 
 
 def ce_backward_inplace(x, t, lse, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, grad_out=None,
                         n_valid=None, vocab_start=0, vocab_total=None, smoothing="all"):
-    """Writes the gradient over ``x`` (which may be a vocabulary shard)."""
-    p = params(label_smoothing, reduce_loss, ignore_idx, smoothing=smoothing)
-    _check(lib.ce_backward_inplace(ctypes.byref(logits_desc(x, vocab_start, vocab_total)),
-                                   ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(lse), _ptr(grad_out),
-                                   _ptr(n_valid), _stream(x.device)))
-    return x
+    """Writes the gradient over ``x`` (which may be a vocabulary shard) from the lse alone."""
+    return ce_backward_inplace_ex(x, t, lse, None, label_smoothing, reduce_loss, ignore_idx, grad_out=grad_out,
+                                  n_valid=n_valid, vocab_start=vocab_start, vocab_total=vocab_total,
+                                  smoothing=smoothing)
 
 
 def ce_fwd_bwd_fused(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, grad_out=None, loss=None,
@@ -202,17 +283,22 @@ def ce_fwd_bwd_fused(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-1
     The sum over a global count of valid tokens (data-parallel training):
     ``reduce_loss="sum"`` with ``grad_out`` = [1 / count] gives that gradient
     with one rounding; ``loss / count`` is the normalised loss."""
+    dev = _device_of(x)
     N = x.shape[0] * x.shape[1]
-    dev = x.device
+    _need_targets(dev, t, x.shape[0], x.shape[1])
     p = params(label_smoothing, reduce_loss, ignore_idx, split_chunks, smoothing)
     loss = _f32(1 if p.reduce_loss else N, dev) if loss is None else loss
     n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
+    _need(dev, "grad_out", grad_out, torch.float32, N if p.reduce_loss == _abi.CE_REDUCE_NONE else 1)
+    _need(dev, "loss", loss, torch.float32, 1 if p.reduce_loss else N)
+    _need(dev, "n_valid", n_valid, torch.int32, 1)
     xd = logits_desc(x)
     if ws is None:
         nb = lib.ce_workspace_bytes(ctypes.byref(xd), ctypes.byref(p))
         if nb == 0:
             _check(_abi.CE_EINVAL)
         ws = _workspace(nb, dev)
+    _need_ws(dev, ws)
     if not _is_prepared(ws):
         ce_workspace_init(ws)
     _check(lib.ce_fwd_bwd_fused(ctypes.byref(xd), ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(grad_out),
@@ -251,10 +337,17 @@ def ce_shards_fwd_bwd_fused(shards, t, label_smoothing=0.0, reduce_loss=False, i
     arr = _shard_descs(shards)
     d0, d1, _ = shards[0].shape
     N = d0 * d1
-    dev = shards[0].device
+    dev = _device_of(shards[0], "shard 0")
+    for i, x in enumerate(shards):
+        _need(dev, f"shard {i}", x, contiguous=False)
+    _need_targets(dev, t, d0, d1)
     p = params(label_smoothing, reduce_loss, ignore_idx, 0, smoothing)
     loss = _f32(1 if p.reduce_loss else N, dev) if loss is None else loss
     n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
+    _need(dev, "grad_out", grad_out, torch.float32, N if p.reduce_loss == _abi.CE_REDUCE_NONE else 1)
+    _need(dev, "loss", loss, torch.float32, 1 if p.reduce_loss else N)
+    _need(dev, "n_valid", n_valid, torch.int32, 1)
+    _need_ws(dev, ws)
     if ws is None:
         nb = lib.ce_shards_workspace_bytes(arr, len(shards), ctypes.byref(p))
         if nb == 0:
@@ -270,41 +363,71 @@ def ce_shards_fwd_bwd_fused(shards, t, label_smoothing=0.0, reduce_loss=False, i
 def ce_scale_grad_inplace(x, grad_out: torch.Tensor, per_row: bool):
     """Multiply the gradient staged in ``x`` by ``grad_out`` ([N] per row, or
     [1]) in place; rows whose factor is exactly 1 are not touched."""
-    g = grad_out.to(device=x.device, dtype=torch.float32).reshape(-1).contiguous()
-    _check(lib.ce_scale_grad_inplace(ctypes.byref(logits_desc(x)), _ptr(g), int(bool(per_row)), _stream(x.device)))
+    dev = _device_of(x)
+    g = grad_out.to(device=dev, dtype=torch.float32).reshape(-1).contiguous()
+    _need(dev, "grad_out", g, torch.float32, x.shape[0] * x.shape[1] if per_row else 1)
+    _check(lib.ce_scale_grad_inplace(ctypes.byref(logits_desc(x)), _ptr(g), int(bool(per_row)), _stream(dev)))
     return x
 
 
 def ce_shard_partial_stats(shard, t, vocab_start, vocab_total, ignore_idx=-100, *, stats=None):
     """(m, d, y, r) per row of one vocabulary shard, as a [N, 4] FP32 tensor."""
+    dev = _device_of(shard, "shard")
     N = shard.shape[0] * shard.shape[1]
-    stats = torch.empty((N, 4), dtype=torch.float32, device=shard.device) if stats is None else stats
+    _need_targets(dev, t, shard.shape[0], shard.shape[1])
+    stats = torch.empty((N, 4), dtype=torch.float32, device=dev) if stats is None else stats
+    _need(dev, "stats", stats, torch.float32, 4 * N)
     p = params(ignore_idx=ignore_idx)
     _check(lib.ce_shard_partial_stats(ctypes.byref(logits_desc(shard, vocab_start, vocab_total)),
-                                      ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(stats),
-                                      _stream(shard.device)))
+                                      ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(stats), _stream(dev)))
     return stats
+
+
+def _combine(stats, t, vocab_total, label_smoothing, reduce_loss, ignore_idx, loss, lse, lse_aux, n_valid, ws,
+             want_aux, smoothing):
+    dev = _device_of(stats, "stats")
+    if stats.dim() != 3 or stats.shape[2] != 4:
+        raise CeArgumentError(_abi.CE_EINVAL, "stats must be an [S, N, 4] tensor")
+    S = stats.shape[0]
+    _need(dev, "targets", t, torch.int64, contiguous=False)
+    if t is None or t.dim() != 2:
+        raise CeArgumentError(_abi.CE_EINVAL, "targets must be a 2-d int64 tensor")
+    d0, d1 = t.shape
+    N = d0 * d1
+    p = params(label_smoothing, reduce_loss, ignore_idx, smoothing=smoothing)
+    loss = _f32(1 if p.reduce_loss else N, dev) if loss is None else loss
+    lse = _f32(N, dev) if lse is None else lse
+    if lse_aux is None and want_aux:
+        lse_aux = torch.empty((N, 2), dtype=torch.float32, device=dev)
+    n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
+    if ws is None:
+        ws = _workspace(ce_combine_workspace_bytes(N, reduce_loss), dev)
+    _need(dev, "stats", stats, torch.float32, 4 * S * N)
+    _need(dev, "loss", loss, torch.float32, 1 if p.reduce_loss else N)
+    _need(dev, "lse", lse, torch.float32, N)
+    _need(dev, "lse_aux", lse_aux, torch.float32, 2 * N)
+    _need(dev, "n_valid", n_valid, torch.int32, 1)
+    _need_ws(dev, ws)
+    _check(lib.ce_shard_combine_ex(_ptr(stats), S, d0, d1, int(vocab_total), ctypes.byref(targets_desc(t)),
+                                   ctypes.byref(p), _ptr(loss), _ptr(lse), _ptr(lse_aux), _ptr(n_valid), _ptr(ws),
+                                   ws.numel(), _stream(dev)))
+    return loss, lse, lse_aux, n_valid
 
 
 def ce_shard_combine(stats, t, vocab_total, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, loss=None,
                      lse=None, n_valid=None, ws=None, smoothing="all"):
     """Combine stats [S, N, 4] into (loss, lse [N], n_valid [1])."""
-    S = stats.shape[0]
-    d0, d1 = t.shape
-    N = d0 * d1
-    dev = stats.device
-    p = params(label_smoothing, reduce_loss, ignore_idx, smoothing=smoothing)
-    loss = _f32(1 if p.reduce_loss else N, dev) if loss is None else loss
-    lse = _f32(N, dev) if lse is None else lse
-    n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
-    if ws is None:
-        ws = _workspace(ce_combine_workspace_bytes(N, reduce_loss), dev)
-    if not stats.is_contiguous():
-        raise CeArgumentError(_abi.CE_ELAYOUT, "stats must be a contiguous [S, N, 4] tensor")
-    _check(lib.ce_shard_combine(_ptr(stats), S, d0, d1, int(vocab_total), ctypes.byref(targets_desc(t)),
-                                ctypes.byref(p), _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(ws), ws.numel(),
-                                _stream(dev)))
+    loss, lse, _, n_valid = _combine(stats, t, vocab_total, label_smoothing, reduce_loss, ignore_idx, loss, lse,
+                                     None, n_valid, ws, False, smoothing)
     return loss, lse, n_valid
+
+
+def ce_shard_combine_ex(stats, t, vocab_total, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *,
+                        loss=None, lse=None, lse_aux=None, n_valid=None, ws=None, smoothing="all"):
+    """Combine stats [S, N, 4] into (loss, lse [N], lse_aux [N, 2], n_valid
+    [1]); lse and lse_aux are the per-shard backward's hand-off."""
+    return _combine(stats, t, vocab_total, label_smoothing, reduce_loss, ignore_idx, loss, lse, lse_aux, n_valid,
+                    ws, True, smoothing)
 
 
 def linear_desc(h: torch.Tensor, w: torch.Tensor) -> _abi.CeLinear:
@@ -340,10 +463,18 @@ def ce_linear_cross_entropy(h, w, t, label_smoothing=0.0, reduce_loss=False, ign
     the [N] int64 targets (any stride).  Returns (loss, dh, dw, n_valid)."""
     N, D = h.shape
     V = w.shape[0]
-    dev = h.device
+    dev = _device_of(h, "h")
+    _need(dev, "w", w, contiguous=False)
+    _need(dev, "targets", t, torch.int64, contiguous=False)
     p = params(label_smoothing, reduce_loss, ignore_idx, 0, smoothing)
     loss = _f32(1 if p.reduce_loss else N, dev) if loss is None else loss
     n_valid = torch.empty(1, dtype=torch.int32, device=dev) if n_valid is None else n_valid
+    _need(dev, "grad_out", grad_out, torch.float32, N if p.reduce_loss == _abi.CE_REDUCE_NONE else 1)
+    _need(dev, "loss", loss, torch.float32, 1 if p.reduce_loss else N)
+    _need(dev, "n_valid", n_valid, torch.int32, 1)
+    _need(dev, "dh", dh, contiguous=False)
+    _need(dev, "dw", dw, contiguous=False)
+    _need_ws(dev, ws)
     if dh is None and want_dh:
         dh = torch.empty((N, D), dtype=h.dtype, device=dev)
     if dw is None and want_dw:
@@ -377,7 +508,11 @@ def ce_linear_tune(h, w, reduce_loss="mean", *, dh=None, dw=None, want_dh=True, 
     scratch values).  Returns the workspace it used, which the calls can share."""
     N, D = h.shape
     V = w.shape[0]
-    dev = h.device
+    dev = _device_of(h, "h")
+    _need(dev, "w", w, contiguous=False)
+    _need(dev, "dh", dh, contiguous=False)
+    _need(dev, "dw", dw, contiguous=False)
+    _need_ws(dev, ws)
     p = params(label_smoothing, reduce_loss, -100, 0, smoothing)
     if dh is None and want_dh:
         dh = torch.empty((N, D), dtype=h.dtype, device=dev)
@@ -401,6 +536,7 @@ def ce_workspace_check(ws: torch.Tensor):
     """Raises CeError(CE_EDEADLOCK) if a call since the last check gave up
     waiting, CeArgumentError(CE_EWORKSPACE) if a fused call found ``ws``
     unprepared; clears that record.  Synchronises the stream."""
+    _device_of(ws, "workspace")
     _check(lib.ce_workspace_check(_ptr(ws), _stream(ws.device)))
 
 

@@ -15,7 +15,7 @@ CE_OK, CE_EINVAL, CE_EDTYPE, CE_ELAYOUT, CE_EWORKSPACE, CE_EHIP, CE_EDEADLOCK = 
 CE_F32, CE_BF16 = 0, 1
 CE_REDUCE_NONE, CE_REDUCE_MEAN, CE_REDUCE_SUM = 0, 1, 2
 CE_SMOOTH_ALL, CE_SMOOTH_OTHERS = 0, 1
-CE_ABI_VERSION = 3
+CE_ABI_VERSION = 4
 
 
 class CeLogits(ctypes.Structure):
@@ -69,7 +69,11 @@ SIGNATURES = {
     "ce_combine_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, _P(CeParams)]),
     "ce_forward": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                   _vp]),
+    "ce_forward_ex": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp]),
     "ce_backward_inplace": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp]),
+    "ce_backward_inplace_ex": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp,
+                                              _vp]),
     "ce_fwd_bwd_fused": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp,
                                         ctypes.c_size_t, _vp]),
     "ce_shards_workspace_bytes": (ctypes.c_size_t, [_P(CeLogits), ctypes.c_int32, _P(CeParams)]),
@@ -79,6 +83,9 @@ SIGNATURES = {
     "ce_shard_partial_stats": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp]),
     "ce_shard_combine": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                         _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "ce_shard_combine_ex": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                           _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                           _vp]),
     "ce_workspace_init": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp]),
     "ce_linear_workspace_bytes": (ctypes.c_size_t, [_P(CeLinear), _P(CeParams), ctypes.c_int64,
                                                     _P(ctypes.c_int64)]),

@@ -203,6 +203,15 @@ vce::RowLayout row_layout(const ce_logits* x, const ce_targets* t, const ce_para
   return L;
 }
 
+// Whole rows of at most kShortRow columns take the streaming kernels' FP64
+// path (one wave per row), with the distribution in double.
+void set_short_rows(vce::StatsArgs* a, const ce_logits* x, const ce_params* p) {
+  a->short_rows = x->v_local <= vce::kShortRow;
+  const Smoothing q = smoothing_of(p, x->vocab_total);
+  a->q_o_d = q.q_o;
+  a->q_t_d = q.q_t;
+}
+
 // ---- profiling state (instrumentation only)
 std::mutex g_prof_mu;
 std::vector<hipEvent_t> g_prof_ev;  // pairs
@@ -260,13 +269,14 @@ size_t ce_combine_workspace_bytes(int64_t rows, const ce_params* p) {
   return ws_layout(rows, 1, p->reduce_loss != 0, false).total;
 }
 
-ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p, float* loss, float* lse,
-                     int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
+ce_status ce_forward_ex(const ce_logits* x, const ce_targets* t, const ce_params* p, float* loss, float* lse,
+                        float* lse_aux, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
   ce_status st;
   if ((st = check_params(p)) || (st = check_logits(x, true)) || (st = check_smoothing(p, x->vocab_total))) return st;
   const int64_t N = x->d0 * x->d1;
   if ((st = check_targets(t, N))) return st;
   if (!loss && (N > 0 || p->reduce_loss)) return fail(CE_EINVAL, "loss is NULL");
+  if (((uintptr_t)lse_aux) % 8u) return fail(CE_ELAYOUT, "lse_aux must be 8-byte aligned");
   const WsLayout w = ws_layout(N, 1, p->reduce_loss != 0, false);
   if (!ws || ws_bytes < w.total)
     return fail(CE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, ws ? ws_bytes : (size_t)0);
@@ -287,8 +297,10 @@ ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p
   a.mode = vce::kStatsForward;
   a.row_loss = p->reduce_loss ? reinterpret_cast<float*>(wsb + w.row_loss) : loss;
   a.lse = lse;
+  a.lse_aux = lse_aux;
   a.stats = nullptr;
   a.n_out = n_out;  // counted by the stats kernel's workgroup 0
+  set_short_rows(&a, x, p);
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
   if ((e = vce::launch_stats(a, stream, e0, e1))) return hip_fail(e, "forward launch");
@@ -297,25 +309,46 @@ ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p
   return CE_OK;
 }
 
-ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* lse,
-                              const float* grad_out, const int32_t* n_valid, hipStream_t stream) {
+ce_status ce_forward(const ce_logits* x, const ce_targets* t, const ce_params* p, float* loss, float* lse,
+                     int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return ce_forward_ex(x, t, p, loss, lse, nullptr, n_valid, ws, ws_bytes, stream);
+}
+
+ce_status ce_backward_inplace_ex(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* lse,
+                                 const float* lse_aux, const float* grad_out, const int32_t* n_valid,
+                                 hipStream_t stream) {
   ce_status st;
   if ((st = check_params(p)) || (st = check_logits(x, false)) || (st = check_smoothing(p, x->vocab_total))) return st;
   const int64_t N = x->d0 * x->d1;
   if ((st = check_targets(t, N))) return st;
   if (N > 0 && !lse) return fail(CE_EINVAL, "lse is NULL");
+  if (((uintptr_t)lse_aux) % 8u) return fail(CE_ELAYOUT, "lse_aux must be 8-byte aligned");
   if (p->reduce_loss == CE_REDUCE_MEAN && !n_valid) return fail(CE_EINVAL, "the mean (CE_REDUCE_MEAN) needs n_valid");
   vce::BackwardArgs a;
   a.L = row_layout(x, t, p);
   a.lse = lse;
+  a.lse_aux = lse_aux;
   a.reduce = p->reduce_loss;
   a.g = grad_out;
   a.n_valid = n_valid;
+  // short rows go to one wave in FP64: whole rows are recomputed from the
+  // logits, shard rows of a short vocabulary use the handed-over lse
+  a.short_rows = x->vocab_total > vce::kShortRow ? vce::kShortNone
+                 : x->v_local == x->vocab_total  ? vce::kShortRecompute
+                                                 : vce::kShortFromLse;
+  const Smoothing q = smoothing_of(p, x->vocab_total);
+  a.q_o_d = q.q_o;
+  a.q_t_d = q.q_t;
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
   hipError_t e;
   if ((e = vce::launch_backward(a, stream, e0, e1))) return hip_fail(e, "backward launch");
   return CE_OK;
+}
+
+ce_status ce_backward_inplace(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* lse,
+                              const float* grad_out, const int32_t* n_valid, hipStream_t stream) {
+  return ce_backward_inplace_ex(x, t, p, lse, nullptr, grad_out, n_valid, stream);
 }
 
 }  // extern "C"
@@ -568,8 +601,10 @@ ce_status ce_shard_partial_stats(const ce_logits* shard, const ce_targets* t, co
   a.mode = vce::kStatsShard;
   a.row_loss = nullptr;
   a.lse = nullptr;
+  a.lse_aux = nullptr;
   a.stats = stats;
   a.n_out = nullptr;
+  set_short_rows(&a, shard, p);
   hipEvent_t e0, e1;
   prof_next(&e0, &e1);
   hipError_t e;
@@ -577,10 +612,11 @@ ce_status ce_shard_partial_stats(const ce_logits* shard, const ce_targets* t, co
   return CE_OK;
 }
 
-ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1, int64_t vocab_total,
-                           const ce_targets* t, const ce_params* p, float* loss, float* lse, int32_t* n_valid,
-                           void* ws, size_t ws_bytes, hipStream_t stream) {
+ce_status ce_shard_combine_ex(const float* stats, int32_t S, int64_t d0, int64_t d1, int64_t vocab_total,
+                              const ce_targets* t, const ce_params* p, float* loss, float* lse, float* lse_aux,
+                              int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream) {
   ce_status st;
+  if (((uintptr_t)lse_aux) % 8u) return fail(CE_ELAYOUT, "lse_aux must be 8-byte aligned");
   if ((st = check_params(p))) return st;
   if (S < 1) return fail(CE_EINVAL, "S must be >= 1");
   if (d0 < 0 || d1 < 1) return fail(CE_EINVAL, "need d0 >= 0 and d1 >= 1");
@@ -618,15 +654,22 @@ ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1
   a.ts1 = t->s1;
   a.ignore_idx = p->ignore_idx;
   const Smoothing q = smoothing_of(p, vocab_total);
-  a.q_o = q.f_o();
-  a.q_to = q.f_to();
+  a.q_o_d = q.q_o;
+  a.q_t_d = q.q_t;
   a.row_loss = p->reduce_loss ? reinterpret_cast<float*>(wsb + w.row_loss) : loss;
   a.lse = lse;
+  a.lse_aux = lse_aux;
   a.n_out = n_out;  // counted by the combine kernel's workgroup 0
   if ((e = vce::launch_combine(a, stream))) return hip_fail(e, "combine launch");
   if (p->reduce_loss && (e = vce::launch_mean(a.row_loss, N, mean_n(p, n_out), loss, stream)))
     return hip_fail(e, "mean launch");
   return CE_OK;
+}
+
+ce_status ce_shard_combine(const float* stats, int32_t S, int64_t d0, int64_t d1, int64_t vocab_total,
+                           const ce_targets* t, const ce_params* p, float* loss, float* lse, int32_t* n_valid,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  return ce_shard_combine_ex(stats, S, d0, d1, vocab_total, t, p, loss, lse, nullptr, n_valid, ws, ws_bytes, stream);
 }
 
 ce_status ce_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -72,8 +72,8 @@ struct FusedArgs {
   int32_t short_rows;
   double q_o_d, q_t_d;     // q_o and q_t
 };
-// Longest row the fused kernel's FP64 path takes (one column per lane of a wave).
-constexpr int64_t kShortRow = 64;
+// Longest row the FP64 whole-row paths take (two columns per lane of a wave).
+constexpr int64_t kShortRow = 128;
 
 // The vocabulary shards of ce_shards_fwd_bwd_fused (a kernel argument):
 // shard s's layout (buffer, strides, v_local, vocab_start); each shard row is
@@ -92,17 +92,28 @@ struct StatsArgs {
   int32_t mode;
   float* row_loss;  // forward: loss [N] or per-row scratch
   float* lse;       // forward: may be NULL
+  float* lse_aux;   // forward: [N][2] (lse residual, 1 - p_t) or NULL
   float* stats;     // shard: [N][4]
   int32_t* n_out;   // forward: [1] count of non-ignored rows, written by workgroup 0 (may be NULL)
+  // rows of at most kShortRow columns: one wave in FP64, the distribution in double
+  int32_t short_rows;
+  double q_o_d, q_t_d;
 };
 
 struct BackwardArgs {
   RowLayout L;
   const float* lse;
+  const float* lse_aux;    // [N][2] (lse residual, 1 - p_t) or NULL: the lse alone
   int32_t reduce;          // CE_REDUCE_*
   const float* g;
   const int32_t* n_valid;  // read with CE_REDUCE_MEAN only
+  // rows of at most kShortRow columns, one wave in FP64 (kShortRecompute:
+  // unsharded rows recomputed whole; kShortFromLse: shard rows of a vocabulary
+  // of at most kShortRow columns, from the handed-over lse)
+  int32_t short_rows;
+  double q_o_d, q_t_d;
 };
+enum { kShortNone = 0, kShortRecompute = 1, kShortFromLse = 2 };
 
 struct ScaleArgs {
   RowLayout L;             // logits holding a staged gradient (targets unused)
@@ -116,9 +127,10 @@ struct CombineArgs {
   int64_t N, d1, vocab_total;
   const int64_t* tgt;
   int64_t ts0, ts1, ignore_idx;
-  float q_o, q_to;         // as in RowLayout
+  double q_o_d, q_t_d;     // q_o and q_t (the loss is formed in FP64 and rounded once)
   float* row_loss;
   float* lse;
+  float* lse_aux;   // [N][2] (lse residual, 1 - p_t) or NULL
   int32_t* n_out;   // [1] count of non-ignored rows, written by workgroup 0 (may be NULL)
 };
 

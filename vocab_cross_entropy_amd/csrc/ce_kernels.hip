@@ -62,6 +62,10 @@ constexpr float kReuseSA = 4e-5f;
 constexpr float kReuseA = 5e-5f;
 // and the FP16 error of a single term, |s| p 2^-11, stays below half the floor
 constexpr float kReuseAbs = 5e-8f;
+// The streaming kernels' instance for rows of at most 1024 vectors, the only
+// one that rows of at most kShortRow columns get; it alone compiles their
+// FP64 whole-row path.
+constexpr int kShortT = 256, kShortPB = 4;
 
 template <int DT>
 struct ElemT;
@@ -606,13 +610,14 @@ __device__ void fused_finish(const FusedArgs& a, uint32_t tag, bool ws_ok) {
 }
 
 // --------------------------------------------------------------------------
-// A whole row of at most kShortRow columns, in FP64, by wave 0 (one column
-// per lane): max, sum of exp(x - max), lse, the row sum and the target logit
+// A whole row of at most kShortRow = 128 columns, in FP64, by one wave (two
+// columns per lane: columns lane and lane + 64): max, the sum of exp(x - max)
+// over the columns other than the target, the target logit and the row sum
 // by wave reductions, then loss and gradient s (p_j - q_j) rounded once to
 // the output.  Rows this short cost a launch whatever the arithmetic, and
-// FP32 cannot hold the gradient where p_j sits close to a large q_j (a few
-// columns, heavy smoothing): one FP32 rounding of p already exceeds the FP32
-// gradient's absolute floor there.
+// FP32 cannot hold the gradient where p_j sits close to a large q_j (few
+// columns, heavy smoothing: q_o = a / V reaches 1/128 at 128 columns): one
+// FP32 rounding of p already exceeds the FP32 gradient's absolute floor there.
 __device__ __forceinline__ double wave_max_d(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
@@ -624,11 +629,41 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
-// The arithmetic of a short row held by wave 0, one column per lane (global
-// column index = lane; `in` marks lanes inside the row, `x` their logit):
-// publishes the row's loss and returns the lane's gradient.
+// (m, d, y, r) of a row held by one wave, two columns per lane: x0 is column
+// lane, x1 column lane + 64 (in0 / in1: inside the row); tl is the target's
+// column in this buffer (outside [0, 128): not here, y = 0).  d leaves the
+// target's term out.  Uniform over the wave.
+struct Stats64 {
+  double m, d, y, r;
+};
+__device__ __forceinline__ Stats64 wave_stats64(double x0, bool in0, double x1, bool in1, int64_t tl) {
+  const int lane = threadIdx.x & 63;
+  const bool t0 = in0 && tl == lane, t1 = in1 && tl == lane + 64;
+  Stats64 st;
+  st.m = wave_max_d(fmax(in0 ? x0 : -INFINITY, in1 ? x1 : -INFINITY));
+  st.d = wave_sum_d((in0 && !t0 ? exp(x0 - st.m) : 0.0) + (in1 && !t1 ? exp(x1 - st.m) : 0.0));
+  st.y = wave_sum_d(t0 ? x0 : (t1 ? x1 : 0.0));
+  st.r = wave_sum_d((in0 ? x0 : 0.0) + (in1 ? x1 : 0.0));
+  return st;
+}
+// lse of a whole row from its wave statistics, the target's term restored
+__device__ __forceinline__ double lse_of64(const Stats64& st) {
+  return st.m + log(st.d + (st.y == -INFINITY ? 0.0 : exp(st.y - st.m)));
+}
+// lse - (q_t - q_o) y - q_o r, leaving out a term whose weight is 0 (as row_loss_of)
+__device__ __forceinline__ double row_loss64(double lse, double q_o, double q_t, double y, double r) {
+  double loss = lse;
+  if (q_t != q_o) loss -= (q_t - q_o) * y;
+  if (q_o != 0.0) loss -= q_o * r;
+  return loss;
+}
+
+// The arithmetic of a short row held by wave 0 (columns lane and lane + 64,
+// global index = local index): publishes the row's loss and returns the
+// lane's two gradients.
 template <int T>
-__device__ double short_row_grad(const FusedArgs& a, uint32_t tag, int64_t r, int64_t t, bool in, double x) {
+__device__ void short_row_grad(const FusedArgs& a, uint32_t tag, int64_t r, int64_t t, double x0, bool in0,
+                               double x1, bool in1, double* g0, double* g1) {
   const int lane = threadIdx.x;
   const RowLayout& L = a.L;
   const bool ws_ok = (a.hdr->magic == kWsMagic) & (a.hdr->init_bytes >= a.ws_bytes);
@@ -646,17 +681,13 @@ __device__ double short_row_grad(const FusedArgs& a, uint32_t tag, int64_t r, in
     if (lane == 0) atomicOr(&a.hdr->status, 2u);
   }
 
-  const double m = wave_max_d(in ? x : -INFINITY);
-  const double d = wave_sum_d(in ? exp(x - m) : 0.0);
-  const double R = wave_sum_d(in ? x : 0.0);
-  const double y = wave_sum_d(lane == t ? x : 0.0);
-  const double lse = m + log(d);
-  double loss = lse;  // zero-weight terms left out, as in row_loss_of
-  if (a.q_t_d != a.q_o_d) loss -= (a.q_t_d - a.q_o_d) * y;
-  if (a.q_o_d != 0.0) loss -= a.q_o_d * R;
-  const double q = lane == t ? a.q_t_d : a.q_o_d;
+  const Stats64 st = wave_stats64(x0, in0, x1, in1, tvalid ? t : -1);
+  const double lse = lse_of64(st);
+  const double loss = row_loss64(lse, a.q_o_d, a.q_t_d, st.y, st.r);
   publish_row_loss<T>(a, tag, r, tvalid && ws_ok ? (float)loss : __uint_as_float(0x7fc00000u), true);
-  return tvalid ? s * (exp(x - lse) - q) : __builtin_nan("");
+  const double q0 = lane == t ? a.q_t_d : a.q_o_d, q1 = lane + 64 == t ? a.q_t_d : a.q_o_d;
+  *g0 = tvalid ? s * (exp(x0 - lse) - q0) : __builtin_nan("");
+  *g1 = tvalid ? s * (exp(x1 - lse) - q1) : __builtin_nan("");
 }
 
 template <int DT, int T>
@@ -664,37 +695,45 @@ __device__ void fused_short_row(const FusedArgs& a, uint32_t tag, int64_t r, con
   const int lane = threadIdx.x;
   if (lane >= 64) return;  // wave 0 holds the row
   const Rsrc rx = make_rsrc(g.base, a.L.V * ElemT<DT>::EB);  // lanes past the row read 0, their stores drop
-  const bool in = lane < a.L.V;
-  const double x = (double)bload_elem<DT>(rx, lane);
-  const double gr = short_row_grad<T>(a, tag, r, g.t, in, x);
-  bstore_elem<DT>((float)gr, rx, lane);
+  const bool in0 = lane < a.L.V, in1 = lane + 64 < a.L.V;
+  const double x0 = (double)bload_elem<DT>(rx, lane), x1 = (double)bload_elem<DT>(rx, lane + 64);
+  double g0, g1;
+  short_row_grad<T>(a, tag, r, g.t, x0, in0, x1, in1, &g0, &g1);
+  bstore_elem<DT>((float)g0, rx, lane);
+  bstore_elem<DT>((float)g1, rx, lane + 64);
 }
 
 // The same for a short row held as vocabulary shards: lane j gathers global
-// column j from the shard that holds it (a per-lane address, so plain loads
-// and stores rather than one buffer range).  Ignored rows store +0.0 in
-// every shard's piece, loss 0.
+// columns j and j + 64 from the shards that hold them (per-lane addresses, so
+// plain loads and stores rather than one buffer range).  Ignored rows store
+// +0.0 in every shard's piece, loss 0.
 template <int DT, int T>
 __device__ void fused_short_row_shards(const FusedArgs& a, uint32_t tag, int64_t r, int64_t t, const ShardSet* ss) {
   constexpr int EB = ElemT<DT>::EB;
   const int lane = threadIdx.x;
   if (lane >= 64) return;
   const int64_t i0 = r / a.L.d1, i1 = r - i0 * a.L.d1;
-  char* p = nullptr;
+  char* p0 = nullptr;
+  char* p1 = nullptr;
   for (int k = 0; k < ss->S; ++k) {
     const RowLayout& Ls = ss->L[k];
-    if (lane >= Ls.vocab_start && lane < Ls.vocab_start + Ls.V)
-      p = Ls.x + (i0 * Ls.s0 + i1 * Ls.s1 + (lane - Ls.vocab_start)) * EB;
+    char* rowp = Ls.x + (i0 * Ls.s0 + i1 * Ls.s1) * EB;
+    if (lane >= Ls.vocab_start && lane < Ls.vocab_start + Ls.V) p0 = rowp + (lane - Ls.vocab_start) * EB;
+    if (lane + 64 >= Ls.vocab_start && lane + 64 < Ls.vocab_start + Ls.V) p1 = rowp + (lane + 64 - Ls.vocab_start) * EB;
   }
-  const bool in = p != nullptr;
+  const bool in0 = p0 != nullptr, in1 = p1 != nullptr;
   if (t == a.L.ignore_idx) {
-    if (in) store_elem<DT>(p, 0, 0.f);
+    if (in0) store_elem<DT>(p0, 0, 0.f);
+    if (in1) store_elem<DT>(p1, 0, 0.f);
     publish_row_loss<T>(a, tag, r, 0.f, true);
     return;
   }
-  const double x = in ? (double)load_elem<DT>(p, 0) : 0.0;
-  const double gr = short_row_grad<T>(a, tag, r, t, in, x);
-  if (in) store_elem<DT>(p, 0, (float)gr);
+  const double x0 = in0 ? (double)load_elem<DT>(p0, 0) : 0.0;
+  const double x1 = in1 ? (double)load_elem<DT>(p1, 0) : 0.0;
+  double g0, g1;
+  short_row_grad<T>(a, tag, r, t, x0, in0, x1, in1, &g0, &g1);
+  if (in0) store_elem<DT>(p0, 0, (float)g0);
+  if (in1) store_elem<DT>(p1, 0, (float)g1);
 }
 
 // --------------------------------------------------------------------------
@@ -772,7 +811,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
   const bool first = (kb == 0), last = (kb == kper - 1);  // the buffer's head and tail
   const bool row_first = (k == 0);                      // the row's loss is published once
 
-  if (SH && P == 1 && a.short_rows) {  // a vocabulary of at most 64 columns across the shards
+  if (SH && P == 1 && a.short_rows) {  // a vocabulary of at most kShortRow columns across the shards
     if constexpr (SH && P == 1) fused_short_row_shards<DT, T>(a, tag, r, g.t, ss);
   } else if (g.t == L.ignore_idx) {  // ignored row: +0.0 gradient, loss 0, nothing read
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
@@ -1072,8 +1111,48 @@ __global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void 
 }
 
 // --------------------------------------------------------------------------
+// The natural lse c / kL of a base-2 log-sum-exp c = c_hi + c_lo, split into
+// its FP32 rounding and the residual: lse_hi + lse_lo carries the sum's own
+// precision, and the separate backward rebuilds c from the pair.
+__device__ __forceinline__ void lse_pair(float c_hi, float c_lo, float* lse_hi, float* lse_lo) {
+  const float hi = lse_natural(c_hi, c_lo);
+  // c - hi kL: hi kL is within an ulp of c_hi, so the fma's difference is exact
+  const float rc = __builtin_fmaf(-hi, kL, c_hi) + c_lo;
+  *lse_hi = hi;
+  *lse_lo = rc * kLn2;  // rc / kL to far below the FP32 rounding of lse
+}
+
 // Streaming statistics of whole rows (forward) or of shard rows.  Each thread
-// keeps an online (max, sum) pair, rescaled once per batch of PB vectors.
+// keeps an online (max, sum) pair, rescaled once per batch of PB vectors.  The
+// max covers every column; the sum leaves out the row's target (its lane sets
+// its register copy to -inf after the batch's max), so that 1 - p_t = d / (d +
+// e^(x_t - m)) keeps its digits when the target holds nearly all the
+// probability; the forward restores the term from the target logit, the
+// shard statistics leave it to the combine.
+template <int DT, int T>
+__device__ void stats_short_row(const StatsArgs& a, int64_t r, const Row<DT>& g, bool tvalid, bool owns, int64_t tl) {
+  const int lane = threadIdx.x;
+  const RowLayout& L = a.L;
+  const Rsrc rx = make_rsrc(g.base, L.V * ElemT<DT>::EB);
+  const bool in0 = lane < L.V, in1 = lane + 64 < L.V;
+  const double x0 = (double)bload_elem<DT>(rx, lane), x1 = (double)bload_elem<DT>(rx, lane + 64);
+  const Stats64 st = wave_stats64(x0, in0, x1, in1, owns ? tl : -1);
+  if (lane != 0) return;
+  if (a.mode == kStatsForward) {
+    const double D = st.d + (st.y == -INFINITY ? 0.0 : exp(st.y - st.m));
+    const double lse = st.m + log(D);
+    const double loss = row_loss64(lse, a.q_o_d, a.q_t_d, st.y, st.r);
+    const float lse_hi = (float)lse;
+    a.row_loss[r] = tvalid ? (float)loss : __uint_as_float(0x7fc00000u);
+    if (a.lse) a.lse[r] = tvalid ? lse_hi : __uint_as_float(0x7fc00000u);
+    if (a.lse_aux)
+      reinterpret_cast<float2*>(a.lse_aux)[r] =
+          tvalid ? make_float2((float)(lse - (double)lse_hi), (float)(st.d / D)) : make_float2(NAN, NAN);
+  } else {
+    reinterpret_cast<float4*>(a.stats)[r] = make_float4((float)st.m, (float)st.d, (float)st.y, (float)st.r);
+  }
+}
+
 template <int DT, int T, int PB>
 __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
   constexpr int E = ElemT<DT>::E, EB = ElemT<DT>::EB;
@@ -1091,6 +1170,7 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
         if (a.mode == kStatsForward) {
           a.row_loss[r] = 0.f;
           if (a.lse) a.lse[r] = 0.f;
+          if (a.lse_aux) reinterpret_cast<float2*>(a.lse_aux)[r] = make_float2(0.f, 0.f);
         } else {
           reinterpret_cast<float4*>(a.stats)[r] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
@@ -1100,6 +1180,12 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
     const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
     const int64_t tl = g.t - L.vocab_start;
     const bool owns = tvalid && tl >= 0 && tl < L.V;
+    if constexpr (T == kShortT && PB == kShortPB) {  // the instance rows of at most kShortRow columns get
+      if (a.short_rows) {  // whole rows of at most kShortRow columns: wave 0, FP64
+        if (tid < 64) stats_short_row<DT, T>(a, r, g, tvalid, owns, tl);
+        continue;
+      }
+    }
     const Rsrc rb = make_rsrc(g.body, g.nv * 16);
     const Rsrc rh = make_rsrc(g.base, g.h * EB);
     const Rsrc rt = make_rsrc(g.tail, (int64_t)g.tn * EB);
@@ -1113,8 +1199,21 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
     float m = fmaxf(hx, tx);
     float m2 = m * kL;
     float msub = (m == -INFINITY) ? 0.f : m2;
-    float d = ex2(__builtin_fmaf(hx, kL, -msub)) + ex2(__builtin_fmaf(tx, kL, -msub));
     float rs = (hv ? hx : 0.f) + (tv ? tx : 0.f);
+    // the target's place in the row: head lane, body vector (element te) or tail lane
+    int64_t tvec = -1;
+    int te = 0;
+    if (owns) {
+      if (tl < g.h) {
+        if (tid == tl) hx = -INFINITY;
+      } else if (tl - g.h < g.nv * E) {
+        tvec = (tl - g.h) / E;
+        te = (int)(tl - g.h - tvec * E);
+      } else if (tid == tl - g.h - g.nv * E) {
+        tx = -INFINITY;
+      }
+    }
+    float d = ex2(__builtin_fmaf(hx, kL, -msub)) + ex2(__builtin_fmaf(tx, kL, -msub));
     for (int64_t base = 0; base < g.nv; base += (int64_t)T * PB) {
       uint4 v[PB];
 #pragma unroll
@@ -1133,6 +1232,16 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
         m2 = bm2;
         msub = m2;
       }
+      // the batch holding the target vector (uniform test): its lane drops the target from the sum
+      const int64_t tq = tvec - base;
+      if (tq >= 0 && tq < (int64_t)T * PB) {
+        const int own_j = (int)(tq / T);
+        if (tid == (int)(tq - (int64_t)own_j * T)) {
+#pragma unroll
+          for (int j = 0; j < PB; ++j)
+            if (j == own_j) v[j] = with_neg_inf<DT>(v[j], te);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
         float f[E];
@@ -1148,14 +1257,20 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
     block_sum3<T>(dadj, y, rs, sh);
     if (tid == 0) {
       if (a.mode == kStatsForward) {
-        const float lgD = lg2(dadj);
+        // the target's term restored: D = d_excl + 2^(y log2e - M2)
+        const float e_t = (owns && y != -INFINITY) ? ex2(__builtin_fmaf(y, kL, -M2)) : 0.f;
+        const float Dt = dadj + e_t;
+        const float lgD = lg2(Dt);
         const float c_hi = M2 + lgD;
         const float bb = c_hi - M2;
         const float c_lo = (M2 - (c_hi - bb)) + (lgD - bb);
-        const float lse = lse_natural(c_hi, c_lo);
+        float lse, lse_lo;
+        lse_pair(c_hi, c_lo, &lse, &lse_lo);
         const float loss = row_loss_of(lse, L.q_to, y, L.q_o, rs);
         a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
         if (a.lse) a.lse[r] = tvalid ? lse : __uint_as_float(0x7fc00000u);
+        if (a.lse_aux)
+          reinterpret_cast<float2*>(a.lse_aux)[r] = tvalid ? make_float2(lse_lo, dadj / Dt) : make_float2(NAN, NAN);
       } else {
         // natural-units sum: sum exp(x - M) = dadj * 2^(M2 - M log2e)
         const float dn = (M == -INFINITY) ? 0.f : dadj * ex2(-__builtin_fmaf(M, kL, -M2));
@@ -1166,7 +1281,14 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// Streaming in-place backward from a given lse[N]; works on shards.
+// Streaming in-place backward from the forward's hand-off; works on shards.
+// With lse_aux the row's lse is the pair lse + lse_aux[r][0] and its target
+// gradient takes the fused kernel's form: s ((1 - q_t) - (1 - p_t)) from the
+// handed-over 1 - p_t = lse_aux[r][1] where that is below 1/2, else
+// s ((p_t - q_o) - (q_t - q_o)).  With the lse alone, 1 - p_t comes from
+// expm1(x_t - lse) instead, resolved only to the FP32 lse's own precision.
+// Unsharded rows of at most kShortRow columns are recomputed whole by one
+// wave in FP64 (the fused kernel's short-row arithmetic); lse is not read.
 template <int DT, int T, int PB>
 __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
   constexpr int E = ElemT<DT>::E, EB = ElemT<DT>::EB;
@@ -1183,13 +1305,47 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
     }
     const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
     const int64_t tl = tvalid ? g.t - L.vocab_start : -1;  // may fall outside this shard
-    const float lse = a.lse[r];
-    const float c_hi = lse * kL;
-    const float c_lo = __builtin_fmaf(lse, kL, -c_hi);
     float s = grad_scale(a.reduce, a.g, a.n_valid, r);
     if (!tvalid) s = __uint_as_float(0x7fc00000u);
+    if (T == kShortT && PB == kShortPB && a.short_rows) {  // the instance rows of at most kShortRow columns get
+      // one wave, two columns per lane, FP64: the whole row recomputed (unsharded), or the shard's
+      // columns from the handed-over lse (a vocabulary of at most kShortRow columns)
+      if (tid < 64) {
+        const Rsrc rx = make_rsrc(g.base, L.V * EB);
+        const bool in0 = tid < L.V, in1 = tid + 64 < L.V;
+        const double x0 = (double)bload_elem<DT>(rx, tid), x1 = (double)bload_elem<DT>(rx, tid + 64);
+        double lse;
+        float rest = 2.f;  // 1 - p_t from the hand-off (2: not given)
+        if (a.short_rows == kShortRecompute) {
+          lse = lse_of64(wave_stats64(x0, in0, x1, in1, tl));
+        } else {
+          const float2 aux = a.lse_aux ? reinterpret_cast<const float2*>(a.lse_aux)[r] : make_float2(0.f, 2.f);
+          lse = (double)a.lse[r] + (double)aux.x;
+          rest = aux.y;
+        }
+        const double sd = a.reduce == CE_REDUCE_MEAN ? (a.g ? (double)a.g[0] : 1.0) / (double)(*a.n_valid) : (double)s;
+        // s (p - q); at a target holding more than half the probability, s ((1 - q_t) - (1 - p_t)) from the
+        // handed-over 1 - p_t, which keeps the digits that p_t - 1 would lose
+        auto grad64 = [&](double x, int64_t col) {
+          if (col != tl) return sd * (exp(x - lse) - a.q_o_d);
+          return rest < 0.5f ? sd * ((1.0 - a.q_t_d) - (double)rest) : sd * (exp(x - lse) - a.q_t_d);
+        };
+        bstore_elem<DT>(tvalid ? (float)grad64(x0, tid) : s, rx, tid);
+        bstore_elem<DT>(tvalid ? (float)grad64(x1, tid + 64) : s, rx, tid + 64);
+      }
+      continue;
+    }
+    const float lse = a.lse[r];
+    float2 aux = make_float2(0.f, 2.f);  // no hand-off: 1 - p_t unknown (never below 1/2)
+    if (a.lse_aux) aux = reinterpret_cast<const float2*>(a.lse_aux)[r];
+    const float c_hi = lse * kL;
+    const float c_lo = __builtin_fmaf(lse, kL, -c_hi) + aux.x * kL;
     const float b = -s * L.q_o;
-    const float a_rest = L.q_rest;
+    // target: s (p_t - q_t) without subtracting numbers near 1 (see above)
+    auto target_grad = [&](float x, float p) {
+      if (a.lse_aux) return s * (aux.y < 0.5f ? L.q_rest - aux.y : (p - L.q_o) - L.q_to);
+      return s * (p > 0.5f ? expm1f(x - lse) + L.q_rest : (p - L.q_o) - L.q_to);
+    };
     const Rsrc rb = make_rsrc(g.body, g.nv * 16);
     const Rsrc rh = make_rsrc(g.base, g.h * EB);
     const Rsrc rt = make_rsrc(g.tail, (int64_t)g.tn * EB);
@@ -1197,11 +1353,11 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
       // head and tail elements (range-checked: lanes past them do nothing)
       const float hx = bload_elem<DT>(rh, tid);
       const float tx = bload_elem<DT>(rt, tid);
-      float gh = __builtin_fmaf(ex2(__builtin_fmaf(hx, kL, -c_hi) - c_lo), s, b);
-      float gt = __builtin_fmaf(ex2(__builtin_fmaf(tx, kL, -c_hi) - c_lo), s, b);
-      // target: s (p_t - 1 + 1 - q_t) with p_t - 1 = expm1(x_t - lse), p_t never rounded first
-      if (tl == tid) gh = s * (expm1f(hx - lse) + a_rest);
-      if (tl == g.h + g.nv * E + tid) gt = s * (expm1f(tx - lse) + a_rest);
+      const float ph = ex2(__builtin_fmaf(hx, kL, -c_hi) - c_lo), pt = ex2(__builtin_fmaf(tx, kL, -c_hi) - c_lo);
+      float gh = __builtin_fmaf(ph, s, b);
+      float gt = __builtin_fmaf(pt, s, b);
+      if (tl == tid) gh = target_grad(hx, ph);
+      if (tl == g.h + g.nv * E + tid) gt = target_grad(tx, pt);
       bstore_elem<DT>(gh, rh, tid);
       bstore_elem<DT>(gt, rt, tid);
     }
@@ -1214,13 +1370,16 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
         const int64_t i = base + j * T + tid;
         float f[E];
         unpack<DT>(v[j], f);
-        float gr[E];
+        float pr[E], gr[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(ex2(__builtin_fmaf(f[e], kL, -c_hi) - c_lo), s, b);
+        for (int e = 0; e < E; ++e) {
+          pr[e] = ex2(__builtin_fmaf(f[e], kL, -c_hi) - c_lo);
+          gr[e] = __builtin_fmaf(pr[e], s, b);
+        }
         const uint64_t off = (uint64_t)(tl - (g.h + i * E));
         if (off < (uint64_t)E) {
 #pragma unroll
-          for (int e = 0; e < E; ++e) gr[e] = (e == (int)off) ? s * (expm1f(f[e] - lse) + a_rest) : gr[e];
+          for (int e = 0; e < E; ++e) gr[e] = (e == (int)off) ? target_grad(f[e], pr[e]) : gr[e];
         }
         bstore16(pack<DT>(gr), rb, (uint32_t)i * 16u);  // dropped past the row
       }
@@ -1230,6 +1389,13 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
 
 // --------------------------------------------------------------------------
 // Combine of S shards' (m, d, y, r): one thread per row, shards in order.
+// Each d leaves out the row's target (only its owner holds it); the combine
+// restores that term from the gathered target logit:
+//   M = max_s m_s, D_excl = sum_s d_s e^(m_s - M), D = D_excl + e^(x_t - M),
+//   lse = M + log D, 1 - p_t = D_excl / D,
+// in FP64 and rounded once: the backward rebuilds every p_j from lse (and the
+// residual lse_aux[r][0]), and with few columns (p_j large) each FP32 rounding
+// along the way would show in the gradient.
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   if (blockIdx.x == 0 && a.n_out) {
     const int32_t n = block_count_targets<256>(a.tgt, a.ts0, a.ts1, a.d1, a.N, a.ignore_idx);
@@ -1242,27 +1408,29 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   if (t == a.ignore_idx) {
     a.row_loss[r] = 0.f;
     if (a.lse) a.lse[r] = 0.f;
+    if (a.lse_aux) reinterpret_cast<float2*>(a.lse_aux)[r] = make_float2(0.f, 0.f);
     return;
   }
   const float4* st = reinterpret_cast<const float4*>(a.stats);
-  float M = -INFINITY;
-  for (int s = 0; s < a.S; ++s) M = fmaxf(M, st[(int64_t)s * a.N + r].x);
-  // lse = M + log(sum_s d_s e^(m_s - M)) in FP64, rounded once: the backward
-  // rebuilds every p_j from it, and with few columns (p_j large) each FP32
-  // rounding along the way would show in the gradient.  S <= a few per row.
-  double D = 0.0;
-  float Y = 0.f, R = 0.f;
+  double M = -INFINITY;
+  for (int s = 0; s < a.S; ++s) M = fmax(M, (double)st[(int64_t)s * a.N + r].x);
+  double Dx = 0.0, Y = 0.0, R = 0.0;
   for (int s = 0; s < a.S; ++s) {
     const float4 q = st[(int64_t)s * a.N + r];
-    D += (q.x == -INFINITY) ? 0.0 : (double)q.y * exp((double)q.x - (double)M);
-    Y += q.z;
-    R += q.w;
+    Dx += (q.x == -INFINITY) ? 0.0 : (double)q.y * exp((double)q.x - M);
+    Y += (double)q.z;
+    R += (double)q.w;
   }
-  const float lse = (float)((double)M + log(D));
-  const float loss = row_loss_of(lse, a.q_to, Y, a.q_o, R);
+  const double D = Dx + (Y == -INFINITY ? 0.0 : exp(Y - M));
+  const double lse = M + log(D);
+  const float lse_hi = (float)lse;
   const bool tvalid = t >= 0 && t < a.vocab_total;
-  a.row_loss[r] = tvalid ? loss : __uint_as_float(0x7fc00000u);
-  if (a.lse) a.lse[r] = tvalid ? lse : __uint_as_float(0x7fc00000u);
+  const float nan = __uint_as_float(0x7fc00000u);
+  a.row_loss[r] = tvalid ? (float)row_loss64(lse, a.q_o_d, a.q_t_d, Y, R) : nan;
+  if (a.lse) a.lse[r] = tvalid ? lse_hi : nan;
+  if (a.lse_aux)
+    reinterpret_cast<float2*>(a.lse_aux)[r] =
+        tvalid ? make_float2((float)(lse - (double)lse_hi), (float)(Dx / D)) : make_float2(nan, nan);
 }
 
 // --------------------------------------------------------------------------
@@ -1420,14 +1588,14 @@ hipError_t launch_stats(const StatsArgs& a, hipStream_t stream, hipEvent_t ev0, 
   const int nv = row_vectors(a.L);
   if (a.L.dtype == CE_BF16) {
     if (nv <= 1024)
-      hipLaunchKernelGGL((k_stats<CE_BF16, 256, 4>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_stats<CE_BF16, kShortT, kShortPB>), grid, dim3(kShortT), 0, stream, a);
     else if (nv <= 2048)
       hipLaunchKernelGGL((k_stats<CE_BF16, 256, 8>), grid, dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((k_stats<CE_BF16, 512, 8>), grid, dim3(512), 0, stream, a);
   } else {
     if (nv <= 1024)
-      hipLaunchKernelGGL((k_stats<CE_F32, 256, 4>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_stats<CE_F32, kShortT, kShortPB>), grid, dim3(kShortT), 0, stream, a);
     else if (nv <= 2048)
       hipLaunchKernelGGL((k_stats<CE_F32, 256, 8>), grid, dim3(256), 0, stream, a);
     else
@@ -1446,14 +1614,14 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, hipEvent_t
   const int nv = row_vectors(a.L);
   if (a.L.dtype == CE_BF16) {
     if (nv <= 1024)
-      hipLaunchKernelGGL((k_backward<CE_BF16, 256, 4>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_backward<CE_BF16, kShortT, kShortPB>), grid, dim3(kShortT), 0, stream, a);
     else if (nv <= 2048)
       hipLaunchKernelGGL((k_backward<CE_BF16, 512, 4>), grid, dim3(512), 0, stream, a);
     else
       hipLaunchKernelGGL((k_backward<CE_BF16, 1024, 4>), grid, dim3(1024), 0, stream, a);
   } else {
     if (nv <= 1024)
-      hipLaunchKernelGGL((k_backward<CE_F32, 256, 4>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_backward<CE_F32, kShortT, kShortPB>), grid, dim3(kShortT), 0, stream, a);
     else if (nv <= 2048)
       hipLaunchKernelGGL((k_backward<CE_F32, 512, 4>), grid, dim3(512), 0, stream, a);
     else
