@@ -74,8 +74,9 @@ extern "C" {
 
 /* 3: ce_shards_workspace_bytes and ce_shards_fwd_bwd_fused added
  * 4: the backward hand-off pair lse_aux (ce_forward_ex, ce_shard_combine_ex,
- *    ce_backward_inplace_ex); a shard's statistic d leaves out the target */
-#define CE_ABI_VERSION 4
+ *    ce_backward_inplace_ex); a shard's statistic d leaves out the target
+ * 5: ce_fwd_bwd_fused_noalloc */
+#define CE_ABI_VERSION 5
 
 typedef enum ce_status {
   CE_OK = 0,
@@ -220,6 +221,29 @@ ce_status ce_backward_inplace_ex(const ce_logits* x, const ce_targets* t, const 
  */
 ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_params* p, const float* grad_out,
                            float* loss, int32_t* n_valid, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ce_fwd_bwd_fused for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, which is a static
+ * device array of 16 MiB per device inside the library (held until the
+ * process ends).  Calls no hipMalloc, hipFree or allocating routine.
+ *   - It holds a call that needs at most 16 MiB of workspace: about
+ *     256 + 12 N bytes, plus 32 N K when rows are split into K > 1 chunks
+ *     (N = 8192 rows of 128000 BF16 columns, K = 4: 1.1 MB; unsplit rows: up
+ *     to about 1.39 million rows).  A larger call returns CE_EWORKSPACE
+ *     before any HIP call.
+ *   - The array used is that of the device `stream` belongs to (NULL: the
+ *     current device).  The first call on a device prepares it on `stream`
+ *     (one fill kernel) and must not be captured in a graph (CE_EINVAL);
+ *     later calls may be.
+ *   - Every call on a device shares its array: calls that overlap on one
+ *     device (unordered streams) race, as two calls sharing one workspace do.
+ *   - Results, errors and ce_workspace_check's record are as for
+ *     ce_fwd_bwd_fused; the record is not reachable from the caller here.
+ */
+ce_status ce_fwd_bwd_fused_noalloc(const ce_logits* x, const ce_targets* t, const ce_params* p,
+                                   const float* grad_out, float* loss, int32_t* n_valid, hipStream_t stream);
 
 /*
  * The vocabulary-shard flow in one launch, each shard read once: S shards

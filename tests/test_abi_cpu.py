@@ -141,6 +141,26 @@ def test_fused_rejects_before_any_hip_call(lib, name, change, status):
     assert h.untouched()
 
 
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """The allocation-free fused call refuses bad arguments, and a call whose
+    workspace would not fit its 16 MiB static scratch, on the host."""
+    h = Host()
+    t, p = h.targets(), h.params()
+
+    def call(x, pp=p):
+        return lib.ce_fwd_bwd_fused_noalloc(ctypes.byref(x), ctypes.byref(t), ctypes.byref(pp), None,
+                                            h.loss.ctypes.data, h.n.ctypes.data, None)
+
+    assert call(h.logits(dtype=7)) == _abi.CE_EDTYPE
+    assert call(h.logits(vocab_start=16, vocab_total=32)) == _abi.CE_ELAYOUT
+    assert call(h.logits(), h.params(split_chunks=65)) == _abi.CE_EINVAL
+    # 131072 rows of 128000 BF16 columns in 4 chunks: 256 + (12 + 128) N bytes, above 16 MiB
+    big = h.logits(d0=1, d1=131072, s0=131072 * 128000, s1=128000, v_local=128000, vocab_total=128000)
+    assert call(big, h.params(reduce_loss=1)) == _abi.CE_EWORKSPACE
+    assert b"16777216" in lib.ce_last_error()
+    assert h.untouched()
+
+
 def test_other_calls_reject(lib):
     h = Host()
     p = h.params()

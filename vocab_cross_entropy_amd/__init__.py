@@ -33,7 +33,7 @@ from ._abi import CE_BF16, CE_F32, CeArgumentError, CeError
 
 __all__ = [
     "ce_forward", "ce_backward_inplace", "ce_fwd_bwd_fused", "ce_forward_ex", "ce_backward_inplace_ex",
-    "ce_shard_combine_ex", "ce_scale_grad_inplace", "ce_shard_partial_stats",
+    "ce_shard_combine_ex", "ce_fwd_bwd_fused_noalloc", "ce_scale_grad_inplace", "ce_shard_partial_stats",
     "ce_shard_combine", "ce_shards_fwd_bwd_fused", "ce_shards_workspace_bytes",
     "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_init", "ce_workspace_check",
     "ce_linear_workspace_bytes", "ce_linear_cross_entropy", "ce_linear_tune",
@@ -303,6 +303,23 @@ def ce_fwd_bwd_fused(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-1
         ce_workspace_init(ws)
     _check(lib.ce_fwd_bwd_fused(ctypes.byref(xd), ctypes.byref(targets_desc(t)), ctypes.byref(p), _ptr(grad_out),
                                 _ptr(loss), _ptr(n_valid), _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, n_valid
+
+
+def ce_fwd_bwd_fused_noalloc(x, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, grad_out=None,
+                             loss, n_valid, split_chunks=0, smoothing="all"):
+    """ce_fwd_bwd_fused with the library's static per-device scratch as its
+    workspace: nothing is allocated, so ``loss`` and ``n_valid`` must be
+    given.  Returns (loss, n_valid)."""
+    dev = _device_of(x)
+    N = x.shape[0] * x.shape[1]
+    _need_targets(dev, t, x.shape[0], x.shape[1])
+    p = params(label_smoothing, reduce_loss, ignore_idx, split_chunks, smoothing)
+    _need(dev, "grad_out", grad_out, torch.float32, N if p.reduce_loss == _abi.CE_REDUCE_NONE else 1)
+    _need(dev, "loss", loss, torch.float32, 1 if p.reduce_loss else N)
+    _need(dev, "n_valid", n_valid, torch.int32, 1)
+    _check(lib.ce_fwd_bwd_fused_noalloc(ctypes.byref(logits_desc(x)), ctypes.byref(targets_desc(t)),
+                                        ctypes.byref(p), _ptr(grad_out), _ptr(loss), _ptr(n_valid), _stream(dev)))
     return loss, n_valid
 
 

@@ -15,7 +15,7 @@ CE_OK, CE_EINVAL, CE_EDTYPE, CE_ELAYOUT, CE_EWORKSPACE, CE_EHIP, CE_EDEADLOCK = 
 CE_F32, CE_BF16 = 0, 1
 CE_REDUCE_NONE, CE_REDUCE_MEAN, CE_REDUCE_SUM = 0, 1, 2
 CE_SMOOTH_ALL, CE_SMOOTH_OTHERS = 0, 1
-CE_ABI_VERSION = 4
+CE_ABI_VERSION = 5
 
 
 class CeLogits(ctypes.Structure):
@@ -76,6 +76,7 @@ SIGNATURES = {
                                               _vp]),
     "ce_fwd_bwd_fused": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp,
                                         ctypes.c_size_t, _vp]),
+    "ce_fwd_bwd_fused_noalloc": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp]),
     "ce_shards_workspace_bytes": (ctypes.c_size_t, [_P(CeLogits), ctypes.c_int32, _P(CeParams)]),
     "ce_shards_fwd_bwd_fused": (ctypes.c_int, [_P(CeLogits), ctypes.c_int32, _P(CeTargets), _P(CeParams), _vp, _vp,
                                                _vp, _vp, ctypes.c_size_t, _vp]),

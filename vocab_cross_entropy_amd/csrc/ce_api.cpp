@@ -466,6 +466,27 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
   return fused_call(x, t, p, grad_out, loss, n_valid, ws, ws_bytes, stream);
 }
 
+ce_status ce_fwd_bwd_fused_noalloc(const ce_logits* x, const ce_targets* t, const ce_params* p,
+                                   const float* grad_out, float* loss, int32_t* n_valid, hipStream_t stream) {
+  ce_status st;
+  int32_t K = 0;
+  if ((st = vce::fused_plan(x, p, &K, nullptr, nullptr))) return st;
+  const size_t need = ws_layout(x->d0 * x->d1, K, p->reduce_loss != 0, true).total;
+  if (need > vce::kStaticScratchBytes)
+    return fail(CE_EWORKSPACE,
+                "this call needs %zu bytes of workspace; the allocation-free call holds %zu (use ce_fwd_bwd_fused "
+                "with a workspace of ce_workspace_bytes)",
+                need, vce::kStaticScratchBytes);
+  void* ws = nullptr;
+  hipError_t e;
+  if ((e = vce::static_scratch(stream, &ws)))
+    return e == hipErrorStreamCaptureUnsupported
+               ? fail(CE_EINVAL, "the first ce_fwd_bwd_fused_noalloc call on a device prepares its scratch and "
+                                 "must not be captured")
+               : hip_fail(e, "static scratch");
+  return fused_call(x, t, p, grad_out, loss, n_valid, ws, vce::kStaticScratchBytes, stream);
+}
+
 namespace {
 
 // The shard set's checks and plan: S shards of one row set (same dtype,

@@ -134,6 +134,16 @@ struct CombineArgs {
   int32_t* n_out;   // [1] count of non-ignored rows, written by workgroup 0 (may be NULL)
 };
 
+// The allocation-free fused call's workspace: a file-scope device array of
+// this many bytes in ce_kernels.hip, one per device, held until the process ends.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+// The device address of that array on the device of `stream` (NULL: the
+// current device), looked up once per device with that device current; the
+// first call on a device also enqueues the array's preparation (a fill
+// kernel) on `stream`, and refuses a stream that is being captured.
+hipError_t static_scratch(hipStream_t stream, void** out);
+
 // Shape choice for the fused kernel (host side, no HIP calls).
 FusedShape fused_shape_for(int64_t body_vecs_per_chunk);
 int64_t max_body_vecs(int32_t dtype, int64_t V);

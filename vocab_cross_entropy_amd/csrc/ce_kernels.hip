@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ce.h"
 #include "ce_internal.h"
 
@@ -1693,6 +1695,49 @@ hipError_t launch_ws_init(void* ws, size_t bytes, hipStream_t stream) {
   hipLaunchKernelGGL(k_ws_init, dim3((uint32_t)blocks), dim3(1024), 0, stream, static_cast<unsigned long long*>(ws),
                      nwords, (unsigned long long)bytes);
   return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// The allocation-free fused call's workspace.  In host code `scratch` is only
+// a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, per device, and host code passes that address, never
+// the name.  Calls that use it on one device share it (and race if they
+// overlap); each keeps the tagged-word protocol of a prepared workspace, so
+// nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t static_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // the preparation must run once, not on every replay of a captured graph
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(stream, &cs)) != hipSuccess) return e;
+    if (cs != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    if ((e = launch_ws_init(p, kStaticScratchBytes, stream)) != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_scale(const ScaleArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
