@@ -78,45 +78,6 @@ def traffic_from_profiles(workload_name: str):
     return t, f"fetch x{fetch_scale:.3f}, write x{write_scale:.3f} (copy calibration)"
 
 
-def torch_ce_reference(torch, w, inputs, dev, reduction: str, smoothing: str, steps: int):
-    """torch's own F.cross_entropy, forward + autograd backward, on the same
-    logits in their own dtype: the unfused op this library stands in for.
-    Time per step (events, after warmup) and peak memory over the inputs."""
-    import torch.nn.functional as F
-
-    if smoothing != "all":  # torch spreads the smoothing over all classes only
-        return None
-    x = inputs.logits.to(dev).requires_grad_(True)
-    t = inputs.targets.to(dev).reshape(-1)
-
-    def step():
-        x.grad = None
-        loss = F.cross_entropy(x.reshape(-1, w.V), t, label_smoothing=w.alpha, ignore_index=-100,
-                               reduction=reduction)
-        (loss.sum() if reduction == "none" else loss).backward()
-
-    for _ in range(3):
-        step()
-    torch.cuda.synchronize()
-    base = torch.cuda.memory_allocated(dev)
-    torch.cuda.reset_peak_memory_stats(dev)
-    step()
-    torch.cuda.synchronize()
-    peak = torch.cuda.max_memory_allocated(dev) - base
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    del x
-    torch.cuda.empty_cache()
-    return {"ms_per_step": round(ms, 4), "peak_bytes_over_inputs": int(peak),
-            "what": "F.cross_entropy(logits, targets, label_smoothing, ignore_index=-100) + autograd backward, "
-                    "torch ops on the same logits in their dtype"}
-
-
 def device_info(torch, dev) -> dict:
     """What the runtime reports of the device the step ran on; the peak HBM
     rate used as the roofline's denominator is the published figure."""
@@ -200,9 +161,6 @@ def main():
     ap.add_argument("--hidden", type=int, default=4096, help="--linear: hidden size D")
     ap.add_argument("--chunk-rows", type=int, default=0, help="--linear: rows per chunk (0: automatic)")
     ap.add_argument("--tune", action="store_true", help="--linear: ce_linear_tune before the timed steps")
-    ap.add_argument("--torch-ref", action="store_true",
-                    help="also time torch's own path on the same inputs (F.cross_entropy + autograd; with --linear "
-                         "the matmul too)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -267,16 +225,19 @@ def main():
         def step(p):
             vce.ce_fwd_bwd_fused(view(p), t_view, w.alpha, red, loss=loss, n_valid=n_valid, ws=ws,
                                  split_chunks=args.split_chunks, smoothing=sm)
-    elif calls == "split":
+    elif calls == "split":  # forward, then the backward from its lse and lse_aux hand-off
         ws = torch.empty(vce.ce_workspace_bytes(view(pool[0]), w.alpha, red), dtype=torch.uint8, device=dev)
         lse = torch.empty(N, dtype=torch.float32, device=dev)
+        aux = torch.empty((N, 2), dtype=torch.float32, device=dev)
         g = torch.ones(N if red == "none" else 1, dtype=torch.float32, device=dev)
         calls_per_step = 2
 
         def step(p):
             x = view(p)
-            vce.ce_forward(x, t_view, w.alpha, red, loss=loss, lse=lse, n_valid=n_valid, ws=ws, smoothing=sm)
-            vce.ce_backward_inplace(x, t_view, lse, w.alpha, red, grad_out=g, n_valid=n_valid, smoothing=sm)
+            vce.ce_forward_ex(x, t_view, w.alpha, red, loss=loss, lse=lse, lse_aux=aux, n_valid=n_valid, ws=ws,
+                              smoothing=sm)
+            vce.ce_backward_inplace_ex(x, t_view, lse, aux, w.alpha, red, grad_out=g, n_valid=n_valid,
+                                       smoothing=sm)
     elif calls == "shard_fused":  # vocabulary shards, every shard read once in one launch
         bounds = workloads.shard_bounds(V, w.shards)
         pool = [[phys_dev[..., a:c].contiguous() for a, c in bounds] for _ in range(P)]
@@ -291,18 +252,19 @@ def main():
         pool = [[phys_dev[..., a:c].contiguous() for a, c in bounds] for _ in range(P)]
         stats = torch.empty((len(bounds), N, 4), dtype=torch.float32, device=dev)
         lse = torch.empty(N, dtype=torch.float32, device=dev)
+        aux = torch.empty((N, 2), dtype=torch.float32, device=dev)
         ws = torch.empty(vce.ce_combine_workspace_bytes(N, red), dtype=torch.uint8, device=dev)
-        g = torch.ones(N, dtype=torch.float32, device=dev)
+        g = torch.ones(N if red == "none" else 1, dtype=torch.float32, device=dev)
         calls_per_step = 2 * len(bounds)
 
         def step(shards):
             for s, (a, c) in enumerate(bounds):
                 vce.ce_shard_partial_stats(shards[s], t_view, a, V, stats=stats[s])
-            vce.ce_shard_combine(stats, t_view, V, w.alpha, red, loss=loss, lse=lse, n_valid=n_valid, ws=ws,
-                                 smoothing=sm)
+            vce.ce_shard_combine_ex(stats, t_view, V, w.alpha, red, loss=loss, lse=lse, lse_aux=aux,
+                                    n_valid=n_valid, ws=ws, smoothing=sm)
             for s, (a, c) in enumerate(bounds):
-                vce.ce_backward_inplace(shards[s], t_view, lse, w.alpha, red, grad_out=g, n_valid=n_valid,
-                                        vocab_start=a, vocab_total=V, smoothing=sm)
+                vce.ce_backward_inplace_ex(shards[s], t_view, lse, aux, w.alpha, red, grad_out=g,
+                                           n_valid=n_valid, vocab_start=a, vocab_total=V, smoothing=sm)
 
     def restore(p):
         """One pool copy back to the generated logits."""
@@ -486,11 +448,6 @@ def main():
         moved = 3 * N * V * b
         out["moved_bytes_per_step"] = moved
         out["moved_GBps"] = round(moved / (step_ms * 1e-3) / 1e9, 1)
-    if args.torch_ref and calls == "fused":
-        ref = torch_ce_reference(torch, w, inputs, dev, red, sm, args.steps)
-        if ref is not None:
-            ref["time_ratio_ours_over_torch"] = round(step_ms / ref["ms_per_step"], 4)
-        out["torch_reference"] = ref
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_sample_rows, red, sm)
     line = json.dumps(out)
@@ -596,35 +553,6 @@ def bench_linear(args, torch, vce, workloads, dev):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_linear(h, W, t, w5.alpha, red, args.smoothing, n_rows=4)
-    if args.torch_ref:
-        del ws
-        torch.cuda.empty_cache()
-        hr = h.clone().requires_grad_(True)
-        Wr = W.clone().requires_grad_(True)
-        ls = w5.alpha * V / (V - 1) if args.smoothing == "others" else w5.alpha
-
-        def tstep():
-            hr.grad = None
-            Wr.grad = None
-            logits = hr @ Wr.T
-            lo = torch.nn.functional.cross_entropy(logits.float(), t, ignore_index=-100, label_smoothing=ls,
-                                                   reduction=red)
-            (lo if red != "none" else lo.sum()).backward()
-
-        for _ in range(3):
-            tstep()
-        torch.cuda.synchronize()
-        base = torch.cuda.memory_allocated()
-        torch.cuda.reset_peak_memory_stats()
-        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        r0.record()
-        for _ in range(args.steps):
-            tstep()
-        r1.record()
-        torch.cuda.synchronize()
-        out["torch_reference"] = {"ms_per_step": round(r0.elapsed_time(r1) / args.steps, 3),
-                                  "peak_bytes_over_inputs": torch.cuda.max_memory_allocated() - base,
-                                  "what": "h @ W.T, F.cross_entropy on FP32 logits, autograd (torch ops)"}
     line = json.dumps(out)
     if args.json_out:
         with open(args.json_out, "a") as f:
