@@ -17,7 +17,7 @@ import torch
 
 import vocab_cross_entropy_amd as vce
 import workloads
-from gpu_util import ignored_rows, orc, rows_f64, say, to_device_view
+from gpu_util import assert_grad, assert_loss, ignored_rows, orc, rows_f64, say, to_device_view
 from test_gpu_parity import check_fused
 
 pytestmark = pytest.mark.gpu
@@ -233,3 +233,47 @@ def test_fused_and_shard_calls_share_one_workspace():
         assert torch.equal(outs[0][1], outs[1][1]), f"call {i}: loss differs"
         assert outs[0][2] == outs[1][2] == orc().count_valid(t)
     vce.ce_workspace_check(shared)
+
+
+def test_withheld_exchange_words_give_up_with_nan_and_edeadlock():
+    """The CE_EDEADLOCK contract, forced from the host with no hang: a test
+    hook in the workspace header (word 4, which the library never sets and
+    ce_workspace_init zeroes) makes chunk 2 of split row 3 leave its exchange
+    words unpublished.  Every chunk of the row reads all of the row's words,
+    its own included, so all three chunks' bounded waits give up and every
+    workgroup exits: row 3's loss and gradient come out NaN, all other rows
+    match the oracle, and ce_workspace_check reports CE_EDEADLOCK once; the
+    next call on the same workspace, hook cleared, is exact again."""
+    V, K, row, chunk = 12288, 3, 3, 2   # aligned BF16 rows: 1536 vectors, 512 per chunk
+    x = _logits((2, 4, V), torch.bfloat16, seed=404)
+    t = workloads.random_targets((2, 4), V, seed=404)
+    o = orc()
+    ref_rows, _ = o.loss_rows(x, t, 0.1)
+    ref = o.grad_rows(x, t, 0.1)
+    xd, td = to_device_view(x), to_device_view(t)
+    ws = vce.ce_workspace_init(torch.empty(vce.ce_workspace_bytes(xd, 0.1, False, split_chunks=K),
+                                           dtype=torch.uint8, device="cuda"))
+    hook = ws[:40].view(torch.int64)[4:5]
+    hook.fill_(((row + 1) << 8) | chunk)
+    say(f"[workspace] withheld exchange: row {row}, chunk {chunk} of {K}")
+    loss, n = vce.ce_fwd_bwd_fused(xd, td, 0.1, False, split_chunks=K, ws=ws)
+    torch.cuda.synchronize()
+    with pytest.raises(vce.CeError) as err:
+        vce.ce_workspace_check(ws)
+    assert err.value.status == vce._abi.CE_EDEADLOCK
+    vce.ce_workspace_check(ws)  # the record is cleared
+    lv = loss.cpu().numpy().astype(np.float64)
+    others = [r for r in range(8) if r != row]
+    assert np.isnan(lv[row]) and not np.isnan(lv[others]).any()
+    assert_loss(lv[others], ref_rows[others], "rows that did not wait")
+    g = rows_f64(xd)
+    assert_grad(g[others], ref[others], torch.bfloat16, "rows that did not wait")
+    assert np.isnan(g[row]).all(), "the chunks that gave up must write NaN"
+    # the hook cleared, the same workspace serves an exact call (a fresh tag)
+    hook.zero_()
+    xd2 = to_device_view(x)
+    loss2, _ = vce.ce_fwd_bwd_fused(xd2, td, 0.1, False, split_chunks=K, ws=ws)
+    torch.cuda.synchronize()
+    vce.ce_workspace_check(ws)
+    assert_loss(loss2.cpu().numpy().astype(np.float64), ref_rows, "after the give-up")
+    assert_grad(rows_f64(xd2), ref, torch.bfloat16, "after the give-up")

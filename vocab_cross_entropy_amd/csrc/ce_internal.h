@@ -19,7 +19,11 @@ struct WsHeader {
   unsigned long long magic;        // kWsMagic once ce_workspace_init has run
   unsigned long long init_bytes;   // bytes ce_workspace_init cleared
   unsigned long long epoch;        // fused call: its low 32 bits tag the call's words (1 after init, never 0)
-  unsigned long long reserved[12];
+  // Test hook, never set by the library (ce_workspace_init zeroes it): when
+  // it equals (row + 1) << 8 | chunk, that chunk of that split row leaves its
+  // exchange words unpublished, so its partners' bounded waits give up.
+  unsigned long long withhold;
+  unsigned long long reserved[11];
   unsigned long long counts[kMaxSlices];  // fused call: tagged counts of non-ignored rows per target slice
 };
 constexpr size_t kWsHeaderBytes = 256;
@@ -27,6 +31,7 @@ static_assert(sizeof(WsHeader) == kWsHeaderBytes, "workspace header is 256 bytes
 // k_ws_init writes the header by word index: 1 = magic, 2 = init_bytes, 3 = epoch
 static_assert(offsetof(WsHeader, magic) == 8 && offsetof(WsHeader, init_bytes) == 16, "header word layout");
 static_assert(offsetof(WsHeader, epoch) == 24 && offsetof(WsHeader, counts) == 128, "header word layout");
+static_assert(offsetof(WsHeader, withhold) == 32, "header word layout: the fused kernel reads it after the epoch");
 constexpr unsigned long long kWsMagic = 0x43452d5753304331ull;
 
 // Which template instance of the fused kernel a plan uses.

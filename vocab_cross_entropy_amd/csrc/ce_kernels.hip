@@ -788,9 +788,10 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
   // address space: nothing writes them before this call's last workgroup
   // finishes); the epoch's low half is this call's tag
   typedef const __attribute__((address_space(4))) unsigned long long* ConstU64;
-  const ConstU64 wsrec = (ConstU64)(&a.hdr->magic);  // magic, init_bytes, epoch
+  const ConstU64 wsrec = (ConstU64)(&a.hdr->magic);  // magic, init_bytes, epoch, withhold
   const uint32_t tag = (uint32_t)wsrec[2];
   const bool ws_ok = (wsrec[0] == kWsMagic) & (wsrec[1] >= a.ws_bytes);
+  const unsigned long long withhold = wsrec[3];  // the test hook (0 in every prepared workspace)
   if (item < a.nslice) count_slice<T>(a, tag, item);
   const int64_t last_item = L.N * K - 1;
   const int64_t r = item / K;
@@ -844,6 +845,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
     for (int j = 0; j < P; ++j) v[j] = bload16(rb, (uint32_t)(j * T + tid) * 16u);
     __builtin_amdgcn_s_setprio(0);
     const float g_up = a.g ? a.g[a.reduce ? 0 : r] : 1.f;
+
     const bool hv = HT && first && tid < g.h, tv = HT && last && tid < g.tn;
     float hx = -INFINITY, tx = -INFINITY;
     if (HT) {
@@ -992,7 +994,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
     float M2 = m2, D = d, Y = y, R = rs;
     if (K > 1) {
       unsigned long long* row_slots = a.slots + (size_t)r * (size_t)K * 4u;
-      if (tid == 0) {
+      if (tid == 0 && withhold != ((((unsigned long long)r + 1u) << 8) | (unsigned)k)) {
         const float mine[4] = {m2, d, y, rs};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
