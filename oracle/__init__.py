@@ -319,6 +319,53 @@ class Oracle:
                                           None if G is None else G.ctypes.data))
         return (loss, dh, dw, G) if want_g else (loss, dh, dw)
 
+    def linear_ce_blocked(self, h, w, t, alpha=0.0, ignore_idx=-100, reduce_loss=False, g=None, n_valid=None,
+                          smoothing="all", dw_cols=(), block=512, on_block=None):
+        """The head + loss of every row, for heads whose logits are too large
+        for or_linear_ce's loops (hyper-parallel #269's chunked lm_head at full
+        size).  Per block of rows: the logits as a float64 matrix product of
+        the exact stored values (a library matmul as the step; exact whenever
+        every partial sum is, as for grid-valued inputs), materialised as the
+        library does (FP32, then BF16 by nearest even for BF16 inputs), then
+        that block's loss rows and gradient G by or_loss_rows / or_grad_rows
+        on the materialised logits, and dW's columns ``dw_cols`` accumulated as
+        G^T h[:, cols] in float64.  ``on_block(rows, G)`` sees each block's G.
+        Returns (loss rows [N], dW[:, dw_cols] [V, len(dw_cols)])."""
+        if h.dtype != w.dtype or h.dim() != 2 or w.dim() != 2 or h.shape[1] != w.shape[1]:
+            raise OracleError("h [N, D] and w [V, D] of one dtype")
+        if h.dtype not in (torch.float32, torch.bfloat16):
+            raise OracleError(f"unsupported dtype {h.dtype}")
+        N, D = h.shape
+        V = w.shape[0]
+        if t.dtype != torch.int64 or t.dim() != 1 or t.numel() != N:
+            raise OracleError("targets must be int64 [N]")
+        if n_valid is None:
+            n_valid = int((t != ignore_idx).sum())
+        cols = np.asarray(dw_cols, dtype=np.int64)
+        wt = w.to(torch.float64).T.contiguous()
+        hc = h.to(torch.float64)[:, torch.as_tensor(cols)].numpy() if cols.size else None
+        loss = np.empty(N, np.float64)
+        dwc = np.zeros((V, cols.size), np.float64)
+        red = reduction_code(reduce_loss)
+        for r0 in range(0, N, block):
+            r1 = min(N, r0 + block)
+            logits = (h[r0:r1].to(torch.float64) @ wt).to(torch.float32)
+            if h.dtype == torch.bfloat16:
+                logits = logits.to(torch.bfloat16)
+            x = logits.reshape(1, r1 - r0, V)
+            tb = t[r0:r1].reshape(1, r1 - r0).contiguous()
+            loss[r0:r1], _ = self.loss_rows(x, tb, alpha, ignore_idx, smoothing=smoothing)
+            gb = None
+            if g is not None:
+                gb = float(g) if red else np.asarray(g, np.float64).reshape(-1)[r0:r1]
+            G = self.grad_rows(x, tb, alpha, ignore_idx, reduce_loss=reduce_loss, g=gb, n_valid=n_valid,
+                               smoothing=smoothing)
+            if cols.size:
+                dwc += G.T @ hc[r0:r1]
+            if on_block is not None:
+                on_block(np.arange(r0, r1), G)
+        return loss, dwc
+
     def max_threads(self) -> int:
         return int(self.lib.or_max_threads())
 

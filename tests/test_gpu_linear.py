@@ -183,40 +183,48 @@ def test_linear_no_rows():
     assert torch.count_nonzero(dwo).item() == 0, "no rows: dW is zero"
 
 
-def test_linear_full_size_sampled():
+def test_linear_full_size():
     """The 4 x 2048-row head of a 4096-wide model onto 128000 BF16 columns in
-    the automatic chunks (4096 rows): sampled rows of the loss and of dh
-    against the oracle (a row's loss and dh depend on that row alone; the
-    mean's n counts every row), and dW's column sums, which vanish because
-    every gradient row sums to zero, within the bound that G's rounding leaves."""
+    the automatic chunks (4096 rows), against the oracle's blocked head over
+    every row: the mean against the oracle's mean over all rows, every row's
+    loss (an unreduced call), dW element by element on 16 sampled hidden
+    columns (all 128000 vocabulary rows of each) within the derived bar, and
+    dh on sampled rows (the oracle's own loops)."""
     N, D, V = 8192, 4096, 128000
     say("[linear] generating the full-size grid inputs")
     h, w, t = grid_inputs(N, D, V, torch.bfloat16, seed=29, ignore_frac=0.05)
     n_all = int((t != -100).sum())
     loss, dh, dw, n = run_linear(h, w, t, 0.1, "mean")
     assert n == n_all
-    rows = np.array([0, 1, 1023, 1024, 4097, 8191] + list(np.random.default_rng(1).choice(N, 6, replace=False)))
-    say(f"[linear] oracle on {len(rows)} sampled rows")
     o = orc()
-    hs, ts = h[rows].contiguous(), t[rows].contiguous()
-    ref_rows, ref_dh, _, G = o.linear_ce(hs, w, ts, 0.1, reduce_loss="mean", n_valid=n_all, want_dw=False,
-                                         want_g=True)
-    check_dh(dh[rows], ref_dh, G, w, torch.bfloat16, "full size sampled dh")
-    # the mean from the sampled rows cannot be formed; each sampled row's loss is pinned through dh's
-    # rows and the loss path is the same kernel; the mean is checked against the per-row losses below
+    rng = np.random.default_rng(1)
+    cols = np.unique(np.concatenate([[0, 1, D - 1], rng.choice(D, 13, replace=False)]))
+    habs = np.abs(h.double().numpy()[:, cols])
+    acc = [np.zeros((V, cols.size))]
+
+    def bar_terms(rows, G):  # sum_i |G_ij| |h_id| over the rows, for the dW bar
+        acc[0] += np.abs(G).T @ habs[rows]
+
+    say("[linear] oracle over every row (blocked head)")
+    ref_rows, ref_dw = o.linear_ce_blocked(h, w, t, 0.1, reduce_loss="mean", n_valid=n_all, dw_cols=cols,
+                                           on_block=bar_terms)
+    assert_loss([loss[0]], [o.mean_loss(ref_rows, n_all)], "full size mean")
     rl, _, _, _ = run_linear(h, w, t, 0.1, "none", want_dh=False, want_dw=False)
-    assert_loss(rl[rows], ref_rows, "full size sampled loss rows")
-    assert abs(loss[0] - rl.sum() / n_all) <= 1e-5 * max(1.0, abs(loss[0]))
-    # column sums of dW: sum_j dW_jd = sum_i (sum_j G_ij) h_id = 0 exactly; the library's G rows sum to
-    # at most sum_j |G~_ij - G_ij| <= 2^-8 sum_j |G_ij| + V 1e-7, so |sum_j dW_jd| is bounded by
-    # sum_i (2^-8 * 2 s + V 1e-7) |h_id| (sum_j |G_ij| <= 2 s) plus FP32 accumulation
-    # (and the FP32 accumulation over N rows, gamma_N times the same sums of |G~||h|)
-    s = 1.0 / n_all
-    gamma_n = N * 2.0 ** -24
-    habs = np.abs(h.double().numpy()).sum(axis=0)
-    col = dw.sum(axis=0)
-    bound = ((2.0 ** -8 + gamma_n) * 2 * s * (1 + 2.0 ** -8) + V * 1e-7) * habs
-    assert np.all(np.abs(col) <= bound), f"dW column sums: max {np.abs(col).max():.3e}"
+    assert_loss(rl, ref_rows, "full size loss rows")
+    assert np.all(rl[t.numpy() == -100] == 0.0)
+    # dW: (r_G + gamma_N) sum_i |G||h| + a_G sum_i |h| + the FP32 output's rounding
+    r_g, a_g, _ = _bars(torch.bfloat16)
+    tol = (r_g + N * 2.0 ** -24) * acc[0] + a_g * np.broadcast_to(habs.sum(axis=0), ref_dw.shape)
+    tol = tol + 2.0 ** -23 * (np.abs(ref_dw) + tol)
+    got = dw[:, cols]
+    err = np.abs(got - ref_dw)
+    bad = ~(err <= tol)
+    assert not bad.any(), f"full size dW: {bad.sum()} elements off, max err {err.max():.3e}"
+    rows = np.array([0, 1, 1023, 1024, 4097, 8191] + list(rng.choice(N, 6, replace=False)))
+    say(f"[linear] oracle dh on {len(rows)} sampled rows")
+    hs, ts = h[rows].contiguous(), t[rows].contiguous()
+    _, ref_dh, _, G = o.linear_ce(hs, w, ts, 0.1, reduce_loss="mean", n_valid=n_all, want_dw=False, want_g=True)
+    check_dh(dh[rows], ref_dh, G, w, torch.bfloat16, "full size sampled dh")
 
 
 @pytest.mark.parametrize("reduce", ["mean", "sum", "none"])
