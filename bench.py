@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as HIP graph replays (one captured step per input copy), without the "
                          "host's per-call cost")
+    ap.add_argument("--phases", action="store_true",
+                    help="time the main kernel's phases per workgroup with the phase-stamped library build "
+                         "(libce_phases.so) and print their summary instead of the benchmark line")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--linear", action="store_true",
                     help="time the chunked linear head + cross-entropy (ce_linear_cross_entropy) instead")
@@ -169,6 +172,9 @@ def main():
               "(vocabulary- or row-sharded) path is not implemented here; each GPU would run its own rows or shards",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.phases:
+        os.environ["VCE_PHASE_CLOCK"] = "1"  # the binding then loads libce_phases.so
 
     import torch
 
@@ -285,6 +291,9 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
     refresh()
+    if args.phases:
+        return phase_profile(args, torch, vce, w, calls, step, pool, restore, bounds if calls.startswith("shard")
+                             else None, t_view, red, sm, dev)
 
     timed = step
     if args.graph:
@@ -450,6 +459,101 @@ def main():
         out["moved_GBps"] = round(moved / (step_ms * 1e-3) / 1e9, 1)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_sample_rows, red, sm)
+    line = json.dumps(out)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
+
+
+PHASES_FUSED = ["start -> chunk loads issued", "loads + max pass", "sum pass", "partner exchange",
+                "gradient + stores issued", "target store + loss publish"]
+PHASES_STATS = ["start -> first batch issued", "loads + max (all batches)", "reduction + outputs"]
+
+
+def _phase_summary(st, names, tick_us):
+    """Per-phase means over the records that reached every stamp, the item
+    time, the launch's span, the spread of start times and the mean number
+    of records in flight (sum of item times / span)."""
+    import numpy as np
+
+    n = len(names) + 1
+    full = np.all(st[:, :n] != 0, axis=1)
+    t = st[full, :n].astype(np.float64) * tick_us
+    t0 = st[st[:, 0] != 0, 0].astype(np.float64) * tick_us
+    ends = [st[:, n - 1][st[:, n - 1] != 0].astype(np.float64) * tick_us]
+    if st.shape[1] > 7 and np.any(st[:, 7]):
+        ends.append(st[:, 7][st[:, 7] != 0].astype(np.float64) * tick_us)
+    end = max(e.max() for e in ends)
+    span = end - t0.min()
+    d = np.diff(t, axis=1)
+    item = t[:, -1] - t[:, 0]
+    out = {"records": int(st.shape[0]), "timed_records": int(full.sum()), "span_us": round(span, 2),
+           "start_spread_us": round(t0.max() - t0.min(), 2),
+           "tail_after_last_start_us": round(end - t0.max(), 2),
+           "item_us_mean": round(float(item.mean()), 3), "item_us_p90": round(float(np.percentile(item, 90)), 3),
+           "in_flight_mean": round(float(item.sum() / span), 1) if span > 0 else None,
+           "phases_us_mean": {nm: round(float(d[:, i].mean()), 3) for i, nm in enumerate(names)}}
+    if st.shape[1] > 7 and np.any(st[:, 7]):
+        last = st[st[:, 7] != 0]
+        out["finish_us"] = round(float((last[:, 7] - last[:, 6]).mean() * tick_us), 3)
+    return out
+
+
+def phase_profile(args, torch, vce, w, calls, step, pool, restore, bounds, t_view, red, sm, dev):
+    """Phase stamps of the main kernel: the real-time counter (100 MHz) read by
+    thread 0 of every workgroup at its phase boundaries, from the
+    phase-stamped build of the same sources, over --steps launches on fresh
+    copies of the logits; the summary is the mean over launches."""
+    import ctypes
+
+    import numpy as np
+
+    tick_us = 0.01  # the 100 MHz real-time counter
+    N = w.rows
+    buf = torch.zeros((N * 64 * 8,), dtype=torch.int64, device=dev)  # up to 64 workgroups per row, 8 stamps each
+    lib = vce.lib
+    summaries = []
+    kernel_ms = []
+    if calls in ("fused", "shard_fused"):
+        names, kernel = PHASES_FUSED, "k_fused_shards" if calls == "shard_fused" else "k_fused"
+    elif calls == "shard":
+        names, kernel = PHASES_STATS, "k_stats (ce_shard_partial_stats, shard 0)"
+    else:
+        names, kernel = PHASES_STATS, "k_stats (ce_forward_ex)"
+    for i in range(args.steps):
+        p = pool[i % len(pool)]
+        restore(p)
+        buf.zero_()
+        torch.cuda.synchronize()
+        lib.ce_phase_clock(ctypes.c_void_p(buf.data_ptr()), buf.numel() * 8)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if calls in ("fused", "shard_fused"):
+            step(p)
+        elif calls == "shard":
+            a, c = bounds[0]
+            vce.ce_shard_partial_stats(p[0], t_view, a, w.V, stats=torch.empty((N, 4), device=dev))
+        else:
+            vce.ce_forward_ex(p.transpose(0, 1) if w.swapped else p, t_view, w.alpha, red, smoothing=sm)
+        e1.record()
+        torch.cuda.synchronize()
+        lib.ce_phase_clock(None, 0)
+        kernel_ms.append(e0.elapsed_time(e1))
+        st = buf.view(-1, 8).cpu().numpy().view(np.uint64)
+        st = st[np.any(st != 0, axis=1)]
+        summaries.append(_phase_summary(st, names, tick_us))
+    keys = ["span_us", "start_spread_us", "tail_after_last_start_us", "item_us_mean", "item_us_p90", "in_flight_mean"]
+    mean = {k: round(float(np.mean([s_[k] for s_ in summaries])), 3) for k in keys}
+    mean["phases_us_mean"] = {nm: round(float(np.mean([s_["phases_us_mean"][nm] for s_ in summaries])), 3)
+                              for nm in names}
+    if "finish_us" in summaries[0]:
+        mean["finish_us"] = round(float(np.mean([s_["finish_us"] for s_ in summaries])), 3)
+    out = {"phases": True, "workload": w.name, "kernel": kernel, "calls": calls, "launches": len(summaries),
+           "records_per_launch": summaries[0]["records"], "timed_records": summaries[0]["timed_records"],
+           "event_us_mean": round(1e3 * float(np.mean(kernel_ms)), 2), "mean": mean,
+           "note": "stamps from the phase-stamped build (libce_phases.so): its kernels carry the stamps' "
+                   "extra registers and stores; event_us brackets the call on its stream"}
     line = json.dumps(out)
     if args.json_out:
         with open(args.json_out, "a") as f:

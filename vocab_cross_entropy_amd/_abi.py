@@ -10,6 +10,9 @@ import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libce.so")
+# the same library with phase stamps compiled in; loaded only when
+# VCE_PHASE_CLOCK=1 (bench.py --phases sets it)
+PHASES_LIB_PATH = os.path.join(PKG, "libce_phases.so")
 
 CE_OK, CE_EINVAL, CE_EDTYPE, CE_ELAYOUT, CE_EWORKSPACE, CE_EHIP, CE_EDEADLOCK = range(7)
 CE_F32, CE_BF16 = 0, 1
@@ -104,15 +107,22 @@ SIGNATURES = {
 }
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
+def load(path: str | None = None) -> ctypes.CDLL:
+    phases = path is None and os.environ.get("VCE_PHASE_CLOCK") == "1"
+    if path is None:
+        path = PHASES_LIB_PATH if phases else LIB_PATH
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is not built; run `python vocab_cross_entropy_amd/csrc/build.py` (hipcc, gfx950) first")
+            f"{path} is not built; run `python vocab_cross_entropy_amd/csrc/build.py"
+            f"{' --phases' if phases else ''}` (hipcc, gfx950) first")
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if phases:
+        lib.ce_phase_clock.restype = ctypes.c_int
+        lib.ce_phase_clock.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     if lib.ce_abi_version() != CE_ABI_VERSION:
         raise ImportError(f"{path} has ABI version {lib.ce_abi_version()}, expected {CE_ABI_VERSION}")
     return lib

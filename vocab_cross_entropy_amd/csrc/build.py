@@ -1,6 +1,9 @@
 """Build libce.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python vocab_cross_entropy_amd/csrc/build.py
+    python vocab_cross_entropy_amd/csrc/build.py [--phases]
+
+--phases builds libce_phases.so instead: the same library with phase stamps
+compiled into the fused and statistics kernels (bench.py --phases).
 
 Objects go to _build/ at the repository root; the shared library lands next
 to this file so that it travels with the source tree.
@@ -40,27 +43,38 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    kobj = os.path.join(BUILD, "ce_kernels.o")
-    aobj = os.path.join(BUILD, "ce_api.o")
-    lobj = os.path.join(BUILD, "ce_linear.o")
+# The instrumented variant: the same sources with the phase stamps compiled in
+# (CE_PHASE_CLOCK), for `bench.py --phases`; never loaded by default.
+PHASES_LIB = os.path.join(PKG, "libce_phases.so")
+
+
+def build(verbose: bool = False, variant: str = "") -> str:
+    """Build libce.so, or with variant="phases" the instrumented libce_phases.so."""
+    if variant not in ("", "phases"):
+        raise ValueError(f"unknown variant {variant!r}")
+    bdir = os.path.join(BUILD, variant) if variant else BUILD
+    lib = PHASES_LIB if variant else LIB
+    extra = ["-DCE_PHASE_CLOCK"] if variant else []
+    os.makedirs(bdir, exist_ok=True)
+    kobj = os.path.join(bdir, "ce_kernels.o")
+    aobj = os.path.join(bdir, "ce_api.o")
+    lobj = os.path.join(bdir, "ce_linear.o")
     steps = [
-        [HIPCC, *DEVICE, *COMMON, "-c", os.path.join(CSRC, "ce_kernels.hip"), "-o", kobj],
-        [HIPCC, *COMMON, "-c", os.path.join(CSRC, "ce_api.cpp"), "-o", aobj],
-        [HIPCC, *COMMON, "-c", os.path.join(CSRC, "ce_linear.cpp"), "-o", lobj],
+        [HIPCC, *DEVICE, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_kernels.hip"), "-o", kobj],
+        [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_api.cpp"), "-o", aobj],
+        [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_linear.cpp"), "-o", lobj],
     ]
     for cmd in steps:
         out = _run(cmd)
         if verbose and out.strip():
             print(out)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     # the chunked linear call's GEMMs come from hipBLASLt (ROCm's matrix-core GEMM library)
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, aobj, lobj, "-L/opt/rocm/lib", "-lhipblaslt",
           "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, variant="phases" if "--phases" in sys.argv else ""))

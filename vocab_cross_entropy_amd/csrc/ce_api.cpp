@@ -210,6 +210,7 @@ void set_short_rows(vce::StatsArgs* a, const ce_logits* x, const ce_params* p) {
   const Smoothing q = smoothing_of(p, x->vocab_total);
   a->q_o_d = q.q_o;
   a->q_t_d = q.q_t;
+  a->phase = vce::phase_buffer((size_t)(x->d0 * x->d1) * 64u);
 }
 
 // ---- profiling state (instrumentation only)
@@ -230,6 +231,15 @@ void prof_next(hipEvent_t* e0, hipEvent_t* e1) {
 }  // namespace
 
 namespace vce {
+#ifdef CE_PHASE_CLOCK
+namespace {
+unsigned long long* g_phase = nullptr;
+size_t g_phase_bytes = 0;
+}  // namespace
+unsigned long long* phase_buffer(size_t bytes) { return bytes <= g_phase_bytes ? g_phase : nullptr; }
+#else
+unsigned long long* phase_buffer(size_t) { return nullptr; }
+#endif
 void set_last_error(const char* msg) { snprintf(g_err, sizeof g_err, "%s", msg); }
 size_t fused_workspace_bytes(int64_t N, int32_t dtype, int64_t V, bool reduce) {
   return ws_layout(N, fused_auto_chunks(dtype, V), reduce, true).total;
@@ -237,6 +247,17 @@ size_t fused_workspace_bytes(int64_t N, int32_t dtype, int64_t V, bool reduce) {
 }  // namespace vce
 
 extern "C" {
+
+#ifdef CE_PHASE_CLOCK
+// The instrumented build's one extra export (not part of ce.h): the device
+// buffer that later fused and statistics calls stamp their phases into, 64
+// bytes per workgroup item (fused) or row (statistics); NULL stops it.
+ce_status ce_phase_clock(void* buf, size_t bytes) {
+  vce::g_phase = static_cast<unsigned long long*>(buf);
+  vce::g_phase_bytes = buf ? bytes : 0;
+  return CE_OK;
+}
+#endif
 
 int32_t ce_abi_version(void) { return CE_ABI_VERSION; }
 
@@ -429,6 +450,7 @@ ce_status fused_common(const ce_logits* L0, const ce_targets* t, const ce_params
   const Smoothing q = smoothing_of(p, L0->vocab_total);
   a->q_o_d = q.q_o;
   a->q_t_d = q.q_t;
+  a->phase = vce::phase_buffer((size_t)N * (size_t)K * 64u);
   *launch = true;
   return CE_OK;
 }

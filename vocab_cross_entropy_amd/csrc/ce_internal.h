@@ -76,6 +76,7 @@ struct FusedArgs {
   // gradient in FP64 by one wave, with the distribution in double
   int32_t short_rows;
   double q_o_d, q_t_d;     // q_o and q_t
+  unsigned long long* phase;  // [items][8] phase stamps (the instrumented build; NULL otherwise)
 };
 // Longest row the FP64 whole-row paths take (two columns per lane of a wave).
 constexpr int64_t kShortRow = 128;
@@ -103,6 +104,7 @@ struct StatsArgs {
   // rows of at most kShortRow columns: one wave in FP64, the distribution in double
   int32_t short_rows;
   double q_o_d, q_t_d;
+  unsigned long long* phase;  // [rows][8] phase stamps (the instrumented build; NULL otherwise)
 };
 
 struct BackwardArgs {
@@ -176,6 +178,10 @@ hipError_t launch_linear_finish(const float* parts, int64_t nparts, int32_t redu
                                 hipStream_t stream);
 // zeros in rows x cols of an FP32 matrix with row stride ld
 hipError_t launch_fill_f32(float* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream);
+
+// The instrumented build's phase-stamp buffer when it holds `bytes`, else NULL
+// (always NULL in the normal build).
+unsigned long long* phase_buffer(size_t bytes);
 
 // Shared by the entry points (ce_api.cpp): the calling thread's error detail,
 // and the fused call's workspace need for N whole rows of V columns.

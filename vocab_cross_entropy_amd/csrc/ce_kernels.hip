@@ -69,6 +69,20 @@ constexpr float kReuseAbs = 5e-8f;
 // FP64 whole-row path.
 constexpr int kShortT = 256, kShortPB = 4;
 
+// Phase stamps, in the instrumented build only (-DCE_PHASE_CLOCK, libce_phases.so):
+// thread 0 of a workgroup stores the real-time counter (100 MHz) into
+// slot i of its record; the normal build compiles them out.
+#ifdef CE_PHASE_CLOCK
+#define CE_STAMP(buf, rec, i)                                                   \
+  do {                                                                          \
+    if ((buf) && threadIdx.x == 0) (buf)[(size_t)(rec) * 8u + (i)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define CE_STAMP(buf, rec, i) \
+  do {                        \
+  } while (0)
+#endif
+
 template <int DT>
 struct ElemT;
 template <>
@@ -784,6 +798,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
   const int K = a.K;
 
   const int64_t item = blockIdx.x;
+  CE_STAMP(a.phase, item, 0);
   // the workspace's init record and epoch, with scalar loads (constant
   // address space: nothing writes them before this call's last workgroup
   // finishes); the epoch's low half is this call's tag
@@ -843,6 +858,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
     uint4 v[P];
 #pragma unroll
     for (int j = 0; j < P; ++j) v[j] = bload16(rb, (uint32_t)(j * T + tid) * 16u);
+    CE_STAMP(a.phase, item, 1);
     __builtin_amdgcn_s_setprio(0);
     const float g_up = a.g ? a.g[a.reduce ? 0 : r] : 1.f;
 
@@ -908,6 +924,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
       if (tid == 0) sh_n = ok ? n : -1;
     }
     m = block_max<T>(m, sh);
+    CE_STAMP(a.phase, item, 2);
     // s = g / n with the mean, g with the sum, g_r without; NaN (loud) when a
     // count never arrived or the workspace was not initialised
     float s_up = g_up;
@@ -989,6 +1006,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
 #pragma unroll
     for (int j = 0; j < P; ++j) launder(v[j]);
     block_sum3<T>(d, y, rs, sh);
+    CE_STAMP(a.phase, item, 3);
 
     // ---- exchange between the chunks of a split row
     float M2 = m2, D = d, Y = y, R = rs;
@@ -1032,6 +1050,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
       }
     }
 
+    CE_STAMP(a.phase, item, 4);
     // ---- sum with the target term restored, lse (base 2, split into hi + lo
     // by an exact two-sum), loss
     const float e_t = tvalid ? ex2(__builtin_fmaf(Y, kL, -M2)) : 0.f;
@@ -1076,6 +1095,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
       bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(hx, c_hi, c_lo), s, b), rh, tid);
       bstore_elem<DT>(__builtin_fmaf(softmax_term<DT>(tx, c_hi, c_lo), s, b), rt, tid);
     }
+    CE_STAMP(a.phase, item, 5);
     // target element: s (p_t - q_t), stored by the lane that just wrote its
     // vector (same-thread order keeps this store last).  Where p_t > 1/2 it is
     // s ((1 - q_t) - (1 - p_t)) with 1 - p_t = D_excl / D, so p_t near 1 does not
@@ -1093,9 +1113,13 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
     }
     publish_row_loss<T>(a, tag, r, row_loss, row_first);
   }
+  CE_STAMP(a.phase, item, 6);
   // one call site for both kinds of row (two inlined copies of the finish
   // measurably raised the register allocation of the whole kernel)
-  if (item == last_item) fused_finish<T>(a, tag, ws_ok);
+  if (item == last_item) {
+    fused_finish<T>(a, tag, ws_ok);
+    CE_STAMP(a.phase, item, 7);
+  }
 }
 
 template <int DT, int T, int P, bool HT>
@@ -1168,6 +1192,7 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
     if (tid == 0) a.n_out[0] = n;
   }
   for (int64_t r = blockIdx.x; r < L.N; r += gridDim.x) {
+    CE_STAMP(a.phase, r, 0);
     const Row<DT> g = row_geometry<DT>(L, r);
     if (g.t == L.ignore_idx) {
       if (tid == 0) {
@@ -1222,6 +1247,7 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
       uint4 v[PB];
 #pragma unroll
       for (int j = 0; j < PB; ++j) v[j] = bload16(rb, (uint32_t)(base + j * T + tid) * 16u);
+      if (base == 0) CE_STAMP(a.phase, r, 1);
       float bm = -INFINITY;
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
@@ -1256,6 +1282,7 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
       }
     }
     const float M = block_max<T>(m, sh);
+    CE_STAMP(a.phase, r, 2);
     const float M2 = M * kL;
     float dadj = (m == -INFINITY) ? 0.f : d * ex2(m2 - M2);
     block_sum3<T>(dadj, y, rs, sh);
@@ -1281,6 +1308,7 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
         reinterpret_cast<float4*>(a.stats)[r] = make_float4(M, dn, y, rs);
       }
     }
+    CE_STAMP(a.phase, r, 3);
   }
 }
 
