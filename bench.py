@@ -152,6 +152,9 @@ def main():
                     help="shard workloads: one ce_shards_fwd_bwd_fused launch in place of the three-call flow")
     ap.add_argument("--dtype", choices=["bf16", "f32"], default=None,
                     help="the workload's logits in this dtype instead of its own (same shape and recipe)")
+    ap.add_argument("--vocab", type=int, default=0,
+                    help="tuning: the workload's recipe with this many columns (the metric's workload is unchanged "
+                         "otherwise)")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as HIP graph replays (one captured step per input copy), without the "
                          "host's per-call cost")
@@ -192,6 +195,8 @@ def main():
             other = "_bf16" if args.dtype == "f32" else "_f32"
             name = w.name.replace(other, f"_{args.dtype}") if other in w.name else f"{w.name}_{args.dtype}"
             w = dataclasses.replace(w, dtype=dt, name=name)
+    if args.vocab:
+        w = w.scaled(V=args.vocab, name=w.name.replace(f"_v{w.V}_", f"_v{args.vocab}_"))
     t_gen = time.perf_counter()
     inputs = workloads.generate(w)
     gen_s = time.perf_counter() - t_gen
@@ -471,7 +476,7 @@ PHASES_FUSED = ["start -> chunk loads issued", "loads + max pass", "sum pass", "
 PHASES_STATS = ["start -> first batch issued", "loads + max (all batches)", "reduction + outputs"]
 
 
-def _phase_summary(st, names, tick_us):
+def _phase_summary(st, names, tick_us, chunks=1):
     """Per-phase means over the records that reached every stamp, the item
     time, the launch's span, the spread of start times and the mean number
     of records in flight (sum of item times / span)."""
@@ -497,6 +502,14 @@ def _phase_summary(st, names, tick_us):
     if st.shape[1] > 7 and np.any(st[:, 7]):
         last = st[st[:, 7] != 0]
         out["finish_us"] = round(float((last[:, 7] - last[:, 6]).mean() * tick_us), 3)
+    if chunks > 1 and st.shape[0] % chunks == 0:
+        # split rows: how far apart a row's chunks start, and finish their sums (the exchange waits for the last)
+        rows = st.reshape(-1, chunks, 8).astype(np.float64) * tick_us
+        ok = np.all(rows[:, :, :4] > 0, axis=(1, 2))
+        rows = rows[ok]
+        out["row_chunk_start_spread_us"] = round(float((rows[:, :, 0].max(1) - rows[:, :, 0].min(1)).mean()), 3)
+        out["row_chunk_sum_done_spread_us"] = round(float((rows[:, :, 3].max(1) - rows[:, :, 3].min(1)).mean()), 3)
+        out["row_chunk_loads_done_spread_us"] = round(float((rows[:, :, 2].max(1) - rows[:, :, 2].min(1)).mean()), 3)
     return out
 
 
@@ -542,13 +555,16 @@ def phase_profile(args, torch, vce, w, calls, step, pool, restore, bounds, t_vie
         kernel_ms.append(e0.elapsed_time(e1))
         st = buf.view(-1, 8).cpu().numpy().view(np.uint64)
         st = st[np.any(st != 0, axis=1)]
-        summaries.append(_phase_summary(st, names, tick_us))
+        chunks = st.shape[0] // N if calls in ("fused", "shard_fused") and st.shape[0] % N == 0 else 1
+        summaries.append(_phase_summary(st, names, tick_us, chunks))
     keys = ["span_us", "start_spread_us", "tail_after_last_start_us", "item_us_mean", "item_us_p90", "in_flight_mean"]
     mean = {k: round(float(np.mean([s_[k] for s_ in summaries])), 3) for k in keys}
     mean["phases_us_mean"] = {nm: round(float(np.mean([s_["phases_us_mean"][nm] for s_ in summaries])), 3)
                               for nm in names}
-    if "finish_us" in summaries[0]:
-        mean["finish_us"] = round(float(np.mean([s_["finish_us"] for s_ in summaries])), 3)
+    for k in ("finish_us", "row_chunk_start_spread_us", "row_chunk_loads_done_spread_us",
+              "row_chunk_sum_done_spread_us"):
+        if k in summaries[0]:
+            mean[k] = round(float(np.mean([s_[k] for s_ in summaries])), 3)
     out = {"phases": True, "workload": w.name, "kernel": kernel, "calls": calls, "launches": len(summaries),
            "records_per_launch": summaries[0]["records"], "timed_records": summaries[0]["timed_records"],
            "event_us_mean": round(1e3 * float(np.mean(kernel_ms)), 2), "mean": mean,
