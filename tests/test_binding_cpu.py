@@ -50,3 +50,28 @@ def test_bench_refuses_more_than_one_gpu():
                        stderr=subprocess.PIPE, text=True, timeout=120, cwd=root)
     assert r.returncode == 2 and "one GPU" in r.stderr, (r.returncode, r.stderr)
     assert r.stdout == ""
+
+
+def test_host_tensors_refused_before_any_launch():
+    """A host (CPU) tensor handed to a call would give a kernel a host pointer:
+    the binding refuses it, and wrongly typed or sized outputs, before the
+    library sees anything."""
+    import torch
+
+    x = torch.zeros((2, 3, 16), dtype=torch.bfloat16)
+    t = torch.zeros((2, 3), dtype=torch.int64)
+    for call in (lambda: vce.ce_fwd_bwd_fused(x, t), lambda: vce.ce_forward(x, t), lambda: vce.ce_forward_ex(x, t),
+                 lambda: vce.ce_backward_inplace(x, t, torch.zeros(6)),
+                 lambda: vce.ce_backward_inplace_ex(x, t, torch.zeros(6), torch.zeros((6, 2))),
+                 lambda: vce.ce_shard_partial_stats(x, t, 0, 16),
+                 lambda: vce.ce_shard_combine_ex(torch.zeros((1, 6, 4)), t, 16),
+                 lambda: vce.ce_fwd_bwd_fused_noalloc(x, t, loss=torch.zeros(6), n_valid=torch.zeros(1, dtype=torch.int32)),
+                 lambda: vce.ce_shards_fwd_bwd_fused([x], t),
+                 lambda: vce.ce_scale_grad_inplace(x, torch.ones(6), True),
+                 lambda: vce.parallel_cross_entropy(x, t)):
+        with pytest.raises(vce.CeArgumentError):
+            call()
+    with pytest.raises(vce.CeArgumentError):
+        vce.ce_linear_cross_entropy(torch.zeros((4, 8)), torch.zeros((16, 8)), torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(vce.CeArgumentError):
+        vce.ce_workspace_init(torch.zeros(256, dtype=torch.uint8))
