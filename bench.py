@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--hidden", type=int, default=4096, help="--linear: hidden size D")
     ap.add_argument("--chunk-rows", type=int, default=0, help="--linear: rows per chunk (0: automatic)")
     ap.add_argument("--tune", action="store_true", help="--linear: ce_linear_tune before the timed steps")
+    ap.add_argument("--gemm", choices=["auto", "native", "library"], default="auto",
+                    help="--linear: the products' engine (the library's MFMA kernel or hipBLASLt)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -624,12 +626,12 @@ def bench_linear(args, torch, vce, workloads, dev):
     if args.tune:
         t_tune = time.perf_counter()
         vce.ce_linear_tune(h, W, red, dh=dh, dw=dw, chunk_rows=args.chunk_rows, ws=ws, label_smoothing=w5.alpha,
-                           smoothing=args.smoothing)
+                           smoothing=args.smoothing, gemm=args.gemm)
         print(f"[bench] tuned the GEMMs in {time.perf_counter() - t_tune:.1f} s", file=sys.stderr, flush=True)
 
     def step():
         vce.ce_linear_cross_entropy(h, W, t, w5.alpha, red, loss=loss, n_valid=n, dh=dh, dw=dw, ws=ws,
-                                    chunk_rows=args.chunk_rows, smoothing=args.smoothing)
+                                    chunk_rows=args.chunk_rows, smoothing=args.smoothing, gemm=args.gemm)
 
     for _ in range(args.warmup):
         step()
@@ -659,12 +661,15 @@ def bench_linear(args, torch, vce, workloads, dev):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"linear_ce_n{N}_d{D}_v{V}_bf16", "rows": N, "hidden": D, "vocab": V,
                    "chunk_rows": chunk, "chunks": nchunks, "reduction": red, "smoothing": args.smoothing,
-                   "tuned": bool(args.tune),
+                   "tuned": bool(args.tune), "gemm": args.gemm,
+                   "native_products": vce.ce_linear_gemm_plan(h, W, args.gemm),
                    "label_smoothing": w5.alpha},
         "roofline": {"bound": "mfma", "achieved": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "GEMMs (hipBLASLt): step time minus the fused cross-entropy kernels"},
+                     "kernel": "the three products (native MFMA kernel for the products in native_products, bit 0 "
+                               "logits, 1 dh, 2 dW; hipBLASLt for the rest): step time minus the fused "
+                               "cross-entropy kernels"},
         "cross_entropy": {"us_per_step": round(ce_ms * 1e3, 1), "share": round(ce_ms / step_ms, 4),
                           "GBps": round(2 * N * V * 2 / (ce_ms * 1e-3) / 1e9, 1)},
         "memory": {"workspace_bytes": ws_bytes, "full_logits_bytes": N * V * 2},

@@ -75,8 +75,10 @@ extern "C" {
 /* 3: ce_shards_workspace_bytes and ce_shards_fwd_bwd_fused added
  * 4: the backward hand-off pair lse_aux (ce_forward_ex, ce_shard_combine_ex,
  *    ce_backward_inplace_ex); a shard's statistic d leaves out the target
- * 5: ce_fwd_bwd_fused_noalloc */
-#define CE_ABI_VERSION 5
+ * 5: ce_fwd_bwd_fused_noalloc
+ * 6: ce_linear.gemm (was reserved): the chunked head's GEMM engine; the head's
+ *    logits stride in the workspace rounded up to a multiple of 8 */
+#define CE_ABI_VERSION 6
 
 typedef enum ce_status {
   CE_OK = 0,
@@ -334,8 +336,8 @@ ce_status ce_shard_combine_ex(const float* stats, int32_t S, int64_t d0, int64_t
  * ChunkedLossWrapper, the sequence-chunked lm_head of its comparison table
  * row 9 and task P2 #9, against the O(B x L x V) peak of whole logits).
  * For each chunk of `chunk_rows` consecutive rows c:
- *   logits_c = h_c W^T                in the input dtype (FP32 accumulation;
- *                                      a library GEMM on the matrix cores)
+ *   logits_c = h_c W^T                in the input dtype (FP32 accumulation,
+ *                                      on the matrix cores: see `gemm`)
  *   loss, G_c in place of logits_c    ce_fwd_bwd_fused (smoothing and ignore
  *                                      rules as above)
  *   dh_c  = G_c W                      in the input dtype (FP32 accumulation)
@@ -345,11 +347,26 @@ ce_status ce_shard_combine_ex(const float* stats, int32_t S, int64_t d0, int64_t
  * loss need no count.  G_c is rounded to the input dtype before the two
  * backward products, as the fused call writes it.
  */
+/* The engine of the three products (ce_linear.gemm):
+ *   CE_GEMM_NATIVE   the library's own MFMA kernel (v_mfma_f32_32x32x16_bf16,
+ *                    256 x 256 output tiles, operands staged two k-tiles deep
+ *                    through registers into LDS) wherever it applies: BF16,
+ *                    h and w 16-byte aligned, h_ld, w_ld and D multiples of 8;
+ *                    other calls, and FP32 heads, run on the GEMM library
+ *   CE_GEMM_LIBRARY  hipBLASLt, ROCm's GEMM library, for every product
+ *   CE_GEMM_AUTO     per product, the engine measured faster on gfx950 at the
+ *                    head's shapes (currently the library for all three)
+ * Both engines accumulate in FP32 and round the output once; their results
+ * differ only in the summation order. */
+#define CE_GEMM_AUTO 0
+#define CE_GEMM_NATIVE 1
+#define CE_GEMM_LIBRARY 2
+
 typedef struct ce_linear {
   const void* h;      /* device [N, D] hidden states, row stride h_ld elements, columns contiguous */
   const void* w;      /* device [V, D] head weight (torch Linear layout: logits = h W^T), row stride w_ld */
   int32_t dtype;      /* CE_BF16 or CE_F32, for h, w and dh */
-  int32_t reserved;   /* must be 0 */
+  int32_t gemm;       /* CE_GEMM_AUTO (0), CE_GEMM_NATIVE or CE_GEMM_LIBRARY; else CE_EINVAL */
   int64_t N, D, V;    /* rows, hidden size, vocabulary (N >= 0, D >= 1, V >= 1) */
   int64_t h_ld, w_ld; /* >= D */
 } ce_linear;
@@ -369,17 +386,23 @@ size_t ce_linear_workspace_bytes(const ce_linear* lin, const ce_params* p, int64
  *   dw        device FP32 [V, D] (row stride dw_ld); accumulate_dw = 0 overwrites it, 1 adds to it;
  *             NULL: not computed
  *   ws        device workspace of ce_linear_workspace_bytes bytes (256-byte aligned), prepared by
- *             ce_workspace_init; it holds the chunk's logits, the fused call's exchange words and
- *             the GEMM library's scratch
+ *             ce_workspace_init; it holds the chunk's logits (row stride V rounded up to a multiple
+ *             of 8), the fused call's exchange words and the GEMM library's scratch
  * The first call on a device creates that device's GEMM library handle (host
- * state kept until the process ends) and each new shape queries the
- * library's heuristics once; after that the call allocates nothing.  The
+ * state kept until the process ends) and each new shape that runs on the
+ * library queries its heuristics once; after that the call allocates nothing.  The
  * calls are asynchronous on `stream`, with no host synchronisation.
  */
 ce_status ce_linear_cross_entropy(const ce_linear* lin, const int64_t* targets, int64_t t_stride,
                                   const ce_params* p, const float* grad_out, float* loss, int32_t* n_valid,
                                   void* dh, int64_t dh_ld, float* dw, int64_t dw_ld, int32_t accumulate_dw,
                                   int64_t chunk_rows, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Which of the three products ce_linear_cross_entropy would run on the
+ * library's MFMA kernel for `lin` (lin->gemm and the layout checks): bit 0
+ * the logits product, bit 1 dh, bit 2 dW; -1 if `lin` is NULL or invalid.
+ * Host only, no HIP calls. */
+int32_t ce_linear_gemm_plan(const ce_linear* lin);
 
 /*
  * Optional, once per shape before a training loop: for the GEMMs that

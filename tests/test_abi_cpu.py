@@ -274,7 +274,7 @@ def test_linear_rejects_before_any_hip_call(lib):
 
     def call(lin=None, p=None, t_ptr=t.ctypes.data, ts=1, dh=None, dh_ld=8, dw=None, dw_ld=8, acc=0, chunk=0,
              wsp=ws.ctypes.data, wsb=ws.nbytes):
-        d = dict(h=h.ctypes.data, w=w.ctypes.data, dtype=_abi.CE_BF16, reserved=0, N=16, D=8, V=32, h_ld=8, w_ld=8)
+        d = dict(h=h.ctypes.data, w=w.ctypes.data, dtype=_abi.CE_BF16, gemm=0, N=16, D=8, V=32, h_ld=8, w_ld=8)
         d.update(lin or {})
         q = dict(label_smoothing=0.0, reduce_loss=1, ignore_idx=-100, split_chunks=0, smoothing=0)
         q.update(p or {})
@@ -283,7 +283,8 @@ def test_linear_rejects_before_any_hip_call(lib):
                                            dh_ld, dw, dw_ld, acc, chunk, wsp, wsb, None)
 
     assert call(lin=dict(dtype=3)) == _abi.CE_EDTYPE
-    assert call(lin=dict(reserved=1)) == _abi.CE_EINVAL
+    assert call(lin=dict(gemm=3)) == _abi.CE_EINVAL
+    assert call(lin=dict(gemm=-1)) == _abi.CE_EINVAL
     assert call(lin=dict(D=0)) == _abi.CE_EINVAL
     assert call(lin=dict(h_ld=4)) == _abi.CE_ELAYOUT
     assert call(lin=dict(w=None)) == _abi.CE_EINVAL
@@ -439,3 +440,35 @@ def test_device_build_contracts_within_expressions_only():
     spec.loader.exec_module(mod)
     assert "-ffp-contract=on" in mod.DEVICE
     assert not any(f.startswith("-ffp-contract=") and f != "-ffp-contract=on" for f in mod.DEVICE + mod.COMMON)
+
+
+def test_linear_gemm_plan(lib):
+    """Which products run on the native MFMA kernel: every one for a BF16 head
+    with 16-byte rows under CE_GEMM_NATIVE; none under the library engine, for
+    FP32 heads, or when D or a row stride is not a multiple of 8 or a base
+    pointer not 16-byte aligned; -1 for an invalid descriptor."""
+    h = np.zeros(16 * 64 + 8, np.uint16)
+    w = np.zeros(32 * 64 + 8, np.uint16)
+    hp = h.ctypes.data + (-h.ctypes.data) % 16
+    wp = w.ctypes.data + (-w.ctypes.data) % 16
+
+    def plan(**kw):
+        d = dict(h=hp, w=wp, dtype=_abi.CE_BF16, gemm=_abi.CE_GEMM_NATIVE, N=16, D=64, V=32, h_ld=64, w_ld=64)
+        d.update(kw)
+        return lib.ce_linear_gemm_plan(ctypes.byref(_abi.CeLinear(**d)))
+
+    assert plan() == 7
+    assert plan(V=30001) == 7  # the logits stride is padded to a multiple of 8
+    assert plan(N=0) == 7
+    assert plan(gemm=_abi.CE_GEMM_LIBRARY) == 0
+    assert plan(dtype=_abi.CE_F32) == 0
+    assert plan(D=60, h_ld=64, w_ld=64) == 0
+    assert plan(h_ld=68) == 0
+    assert plan(w_ld=72) == 7
+    assert plan(h=hp + 2) == 0
+    assert plan(w=wp + 8) == 0
+    assert plan(gemm=3) == -1
+    assert plan(D=0) == -1
+    assert plan(h_ld=32) == -1
+    assert lib.ce_linear_gemm_plan(None) == -1
+    assert plan(gemm=_abi.CE_GEMM_AUTO) in range(8)

@@ -8,6 +8,11 @@ oracle's (FP32, then BF16 by nearest even) bit for bit, and the stated
 cross-entropy bar applies to the loss.  The logits have a standard deviation
 of about 0.08 sqrt(D).
 
+Every test runs under both GEMM engines: "native" (the library's MFMA
+kernel, ce_gemm.hip, for BF16 heads whose rows are 16-byte multiples; the
+plan query confirms it ran) and "library" (hipBLASLt).  Both accumulate in
+FP32, so the same bars hold for both.
+
 Gradient bars, derived from the cross-entropy bar (the library's G differs
 from the exact G by at most r_G |G| + a_G per element: 2^-8 and 1e-7 for
 BF16, 1e-5 and 1e-8 for FP32) and from FP32 accumulation over K terms
@@ -26,6 +31,16 @@ import vocab_cross_entropy_amd as vce
 from gpu_util import GRAD_TOL, assert_loss, orc, say
 
 pytestmark = pytest.mark.gpu
+
+ENGINES = ["native", "library"]
+
+
+def expected_plan(h, w, gemm):
+    """The products the native kernel takes: all three for BF16 with 16-byte rows under "native"."""
+    D = h.shape[1]
+    ok = (h.dtype == torch.bfloat16 and D % 8 == 0 and max(h.stride(0), D) % 8 == 0 and w.stride(0) % 8 == 0
+          and h.data_ptr() % 16 == 0 and w.data_ptr() % 16 == 0)
+    return 7 if (gemm == "native" and ok) else 0
 
 
 def grid_inputs(N, D, V, dtype, seed, ignore_frac=0.2):
@@ -72,7 +87,7 @@ def check_dw(got, ref, G, h, dtype, what, out_rho=2.0 ** -23):
 
 
 def run_linear(h, w, t, alpha, reduce, g=None, chunk_rows=0, smoothing="all", want_dh=True, want_dw=True,
-               dw0=None, h_pad=0):
+               dw0=None, h_pad=0, gemm="auto"):
     """Device copies (h optionally inside a wider buffer: row stride D + h_pad), the call, results on the host."""
     N, D = h.shape
     hd_full = torch.zeros((N, D + h_pad), dtype=h.dtype)
@@ -88,9 +103,11 @@ def run_linear(h, w, t, alpha, reduce, g=None, chunk_rows=0, smoothing="all", wa
     dw = None
     if dw0 is not None:
         dw = torch.as_tensor(dw0, dtype=torch.float32).cuda()
+    if gemm != "auto":
+        assert vce.ce_linear_gemm_plan(hd, wd, gemm) == expected_plan(hd, wd, gemm)
     loss, dh, dwo, n = vce.ce_linear_cross_entropy(hd, wd, td, alpha, reduce, grad_out=gd, chunk_rows=chunk_rows,
                                                    smoothing=smoothing, want_dh=want_dh, want_dw=want_dw, dw=dw,
-                                                   accumulate_dw=dw0 is not None)
+                                                   accumulate_dw=dw0 is not None, gemm=gemm)
     torch.cuda.synchronize()
     return (loss.cpu().double().numpy(), None if dh is None else dh.cpu().double().numpy(),
             None if dwo is None else dwo.cpu().double().numpy(), int(n.item()))
@@ -99,7 +116,8 @@ def run_linear(h, w, t, alpha, reduce, g=None, chunk_rows=0, smoothing="all", wa
 def check_linear(h, w, t, alpha, reduce, g=None, chunk_rows=0, smoothing="all", what="", **kw):
     N, D = h.shape
     V = w.shape[0]
-    say(f"[linear] {what} N={N} D={D} V={V} {h.dtype} a={alpha} {reduce} {smoothing} chunk={chunk_rows}")
+    say(f"[linear] {what} N={N} D={D} V={V} {h.dtype} a={alpha} {reduce} {smoothing} chunk={chunk_rows} "
+        f"gemm={kw.get('gemm', 'auto')}")
     loss, dh, dw, n = run_linear(h, w, t, alpha, reduce, g, chunk_rows, smoothing, **kw)
     o = orc()
     n_ref = int((t != -100).sum())
@@ -131,42 +149,59 @@ CASES = [(dt, red, sm) for dt in (torch.bfloat16, torch.float32) for red in ("no
          for sm in ("all", "others")]
 
 
+@pytest.mark.parametrize("gemm", ENGINES)
 @pytest.mark.parametrize("dtype,reduce,smoothing", CASES,
                          ids=[f"{'bf16' if c[0] == torch.bfloat16 else 'f32'}-{c[1]}-{c[2]}" for c in CASES])
-def test_linear_chunks_of_32(dtype, reduce, smoothing):
-    """100 rows in chunks of 32, 32, 32 and 4; V = 4099 (ragged rows), D = 96."""
+def test_linear_chunks_of_32(dtype, reduce, smoothing, gemm):
+    """100 rows in chunks of 32, 32, 32 and 4; V = 4099 (ragged rows; the
+    native dh product's K tail), D = 96 (the logits product's K tail)."""
     h, w, t = grid_inputs(100, 96, 4099, dtype, seed=5)
     g = np.linspace(-1.0, 2.0, 100) if reduce == "none" else 0.8
-    check_linear(h, w, t, 0.1, reduce, g=g, chunk_rows=32, smoothing=smoothing, what="chunks of 32")
+    check_linear(h, w, t, 0.1, reduce, g=g, chunk_rows=32, smoothing=smoothing, what="chunks of 32", gemm=gemm)
 
 
+@pytest.mark.parametrize("gemm", ENGINES)
 @pytest.mark.parametrize("chunk_rows", [0, 1, 7, 64, 100, 1000])
-def test_linear_chunk_sizes(chunk_rows):
+def test_linear_chunk_sizes(chunk_rows, gemm):
     """One chunk, one row per chunk, ragged chunks, more rows per chunk than rows."""
     h, w, t = grid_inputs(64, 64, 3001, torch.bfloat16, seed=11)
-    check_linear(h, w, t, 0.1, "mean", chunk_rows=chunk_rows, what=f"chunk {chunk_rows}")
+    check_linear(h, w, t, 0.1, "mean", chunk_rows=chunk_rows, what=f"chunk {chunk_rows}", gemm=gemm)
 
 
-def test_linear_partial_outputs_and_accumulation():
+@pytest.mark.parametrize("gemm", ENGINES)
+def test_linear_partial_outputs_and_accumulation(gemm):
     """dh only, dW only, dW added to an existing gradient, and a strided h."""
     h, w, t = grid_inputs(40, 64, 2048, torch.bfloat16, seed=13)
-    check_linear(h, w, t, 0.0, "sum", chunk_rows=16, want_dw=False, what="dh only")
-    check_linear(h, w, t, 0.0, "sum", chunk_rows=16, want_dh=False, what="dW only")
+    check_linear(h, w, t, 0.0, "sum", chunk_rows=16, want_dw=False, what="dh only", gemm=gemm)
+    check_linear(h, w, t, 0.0, "sum", chunk_rows=16, want_dh=False, what="dW only", gemm=gemm)
     rng = np.random.default_rng(3)
     dw0 = rng.standard_normal((2048, 64)).astype(np.float32)
-    check_linear(h, w, t, 0.0, "sum", chunk_rows=16, dw0=dw0, what="dW accumulated")
-    check_linear(h, w, t, 0.1, "mean", chunk_rows=16, h_pad=24, what="strided h")
+    check_linear(h, w, t, 0.0, "sum", chunk_rows=16, dw0=dw0, what="dW accumulated", gemm=gemm)
+    check_linear(h, w, t, 0.1, "mean", chunk_rows=16, h_pad=24, what="strided h", gemm=gemm)
 
 
-def test_linear_short_rows_and_small_heads():
+@pytest.mark.parametrize("gemm", ENGINES)
+def test_linear_short_rows_and_small_heads(gemm):
     """V = 7 (the fused kernel's FP64 path for short rows), D = 1, all rows of a chunk ignored."""
     h, w, t = grid_inputs(20, 8, 7, torch.float32, seed=17)
-    check_linear(h, w, t, 0.3, "mean", chunk_rows=8, smoothing="others", what="V=7")
+    check_linear(h, w, t, 0.3, "mean", chunk_rows=8, smoothing="others", what="V=7", gemm=gemm)
     h, w, t = grid_inputs(12, 1, 500, torch.bfloat16, seed=19)
-    check_linear(h, w, t, 0.1, "none", g=np.ones(12), chunk_rows=5, what="D=1")
+    check_linear(h, w, t, 0.1, "none", g=np.ones(12), chunk_rows=5, what="D=1", gemm=gemm)
     h, w, t = grid_inputs(12, 32, 500, torch.bfloat16, seed=23, ignore_frac=0.0)
     t[4:8] = -100
-    check_linear(h, w, t, 0.1, "mean", chunk_rows=4, what="an all-ignored chunk")
+    check_linear(h, w, t, 0.1, "mean", chunk_rows=4, what="an all-ignored chunk", gemm=gemm)
+    h, w, t = grid_inputs(20, 8, 13, torch.bfloat16, seed=43)
+    check_linear(h, w, t, 0.2, "sum", chunk_rows=3, what="V=13, D=8", gemm=gemm)
+
+
+@pytest.mark.parametrize("gemm", ENGINES)
+def test_linear_tile_edges(gemm):
+    """Sizes around the native kernel's 256 x 256 x 64 tiles and its even
+    k-tile count: K = D of 64, 128 and 192 (one, two and three k-tiles),
+    V one past and one short of a tile, chunks of 255, 256 and 257 rows."""
+    for N, D, V, chunk in [(300, 64, 257, 256), (257, 128, 511, 255), (520, 192, 768, 257), (64, 448, 1000, 0)]:
+        h, w, t = grid_inputs(N, D, V, torch.bfloat16, seed=N + D)
+        check_linear(h, w, t, 0.1, "mean", chunk_rows=chunk, what=f"tile edges N={N} D={D} V={V}", gemm=gemm)
 
 
 def test_linear_no_rows():
@@ -183,7 +218,8 @@ def test_linear_no_rows():
     assert torch.count_nonzero(dwo).item() == 0, "no rows: dW is zero"
 
 
-def test_linear_full_size():
+@pytest.mark.parametrize("gemm", ENGINES)
+def test_linear_full_size(gemm):
     """The 4 x 2048-row head of a 4096-wide model onto 128000 BF16 columns in
     the automatic chunks (4096 rows), against the oracle's blocked head over
     every row: the mean against the oracle's mean over all rows, every row's
@@ -194,7 +230,7 @@ def test_linear_full_size():
     say("[linear] generating the full-size grid inputs")
     h, w, t = grid_inputs(N, D, V, torch.bfloat16, seed=29, ignore_frac=0.05)
     n_all = int((t != -100).sum())
-    loss, dh, dw, n = run_linear(h, w, t, 0.1, "mean")
+    loss, dh, dw, n = run_linear(h, w, t, 0.1, "mean", gemm=gemm)
     assert n == n_all
     o = orc()
     rng = np.random.default_rng(1)
@@ -209,7 +245,7 @@ def test_linear_full_size():
     ref_rows, ref_dw = o.linear_ce_blocked(h, w, t, 0.1, reduce_loss="mean", n_valid=n_all, dw_cols=cols,
                                            on_block=bar_terms)
     assert_loss([loss[0]], [o.mean_loss(ref_rows, n_all)], "full size mean")
-    rl, _, _, _ = run_linear(h, w, t, 0.1, "none", want_dh=False, want_dw=False)
+    rl, _, _, _ = run_linear(h, w, t, 0.1, "none", want_dh=False, want_dw=False, gemm=gemm)
     assert_loss(rl, ref_rows, "full size loss rows")
     assert np.all(rl[t.numpy() == -100] == 0.0)
     # dW: (r_G + gamma_N) sum_i |G||h| + a_G sum_i |h| + the FP32 output's rounding
@@ -227,8 +263,9 @@ def test_linear_full_size():
     check_dh(dh[rows], ref_dh, G, w, torch.bfloat16, "full size sampled dh")
 
 
+@pytest.mark.parametrize("gemm", ENGINES)
 @pytest.mark.parametrize("reduce", ["mean", "sum", "none"])
-def test_linear_autograd(reduce):
+def test_linear_autograd(reduce, gemm):
     """linear_cross_entropy: the loss and, after backward with upstream 0.5
     (per-row weights for per-row losses), h.grad and W.grad (FP32 dW cast to
     BF16 by autograd) against the oracle."""
@@ -236,7 +273,7 @@ def test_linear_autograd(reduce):
     say(f"[linear autograd] {reduce}")
     hd = h.cuda().requires_grad_(True)
     wd = w.cuda().requires_grad_(True)
-    loss = vce.linear_cross_entropy(hd, wd, t.cuda(), 0.1, reduce, chunk_rows=16)
+    loss = vce.linear_cross_entropy(hd, wd, t.cuda(), 0.1, reduce, chunk_rows=16, gemm=gemm)
     gw = np.linspace(-1.0, 2.0, 48) if reduce == "none" else 0.5
     if reduce == "none":
         loss.backward(torch.as_tensor(gw, dtype=torch.float32, device="cuda"))
@@ -272,7 +309,8 @@ def test_linear_autograd_trains_a_head():
     assert losses[-1] < 0.8 * losses[0], losses
 
 
-def test_linear_graph_replays():
+@pytest.mark.parametrize("gemm", ENGINES)
+def test_linear_graph_replays(gemm):
     """A captured ce_linear_cross_entropy (GEMMs, one fused call per chunk,
     count and finish kernels) replays bit-identically to the eager call: each
     chunk's fused call takes its tag from the workspace's epoch, which every
@@ -288,7 +326,7 @@ def test_linear_graph_replays():
 
     def call():
         vce.ce_linear_cross_entropy(hd, wd, td, 0.1, "mean", loss=loss, n_valid=n, dh=dh, dw=dw, ws=ws,
-                                    chunk_rows=16)
+                                    chunk_rows=16, gemm=gemm)
 
     say("[linear graph] eager reference")
     call()

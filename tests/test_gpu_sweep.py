@@ -8,7 +8,8 @@ to 1), reduction, upstream gradient and chunk split, then runs
 ce_fwd_bwd_fused; ce_shards_fwd_bwd_fused over 1 to 16 shards cut at random
 columns; ce_forward_ex + ce_backward_inplace_ex (and the FP32-lse form
 ce_forward + ce_backward_inplace); the three-call shard flow; or the chunked
-linear head (on the linear tests' grid-valued inputs), and compares loss, n,
+linear head (on the linear tests' grid-valued inputs; even seeds on the
+native GEMM engine, odd ones on the library), and compares loss, n,
 lse and every gradient element with the oracle at the stated bar.  The
 separate backward fed the forward's lse_aux pair takes no allowance; fed the
 FP32 lse alone it takes that hand-off's (lse_allowance), and fed FP32 shard
@@ -63,4 +64,5 @@ def test_linear_sweep(seed):
     say(f"[sweep linear] seed {seed}: {c['what']}")
     h, w, t = grid_inputs(c["N"], c["D"], c["V"], c["dtype"], seed=c["seed"], ignore_frac=c["ignore_frac"])
     check_linear(h, w, t, c["alpha"], c["reduce"], g=c["g"], chunk_rows=c["chunk"], smoothing=c["smoothing"],
-                 what=c["what"], want_dh=c["want_dh"], want_dw=c["want_dw"], h_pad=c["h_pad"])
+                 what=c["what"], want_dh=c["want_dh"], want_dw=c["want_dw"], h_pad=c["h_pad"],
+                 gemm="native" if seed % 2 == 0 else "library")

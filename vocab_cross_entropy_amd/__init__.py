@@ -36,7 +36,7 @@ __all__ = [
     "ce_shard_combine_ex", "ce_fwd_bwd_fused_noalloc", "ce_scale_grad_inplace", "ce_shard_partial_stats",
     "ce_shard_combine", "ce_shards_fwd_bwd_fused", "ce_shards_workspace_bytes",
     "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_init", "ce_workspace_check",
-    "ce_linear_workspace_bytes", "ce_linear_cross_entropy", "ce_linear_tune",
+    "ce_linear_workspace_bytes", "ce_linear_cross_entropy", "ce_linear_tune", "ce_linear_gemm_plan",
     "parallel_cross_entropy", "linear_cross_entropy",
     "Profiler", "CeError", "CeArgumentError", "lib", "ShardedCrossEntropy", "sharded_cross_entropy",
 ]
@@ -447,8 +447,19 @@ def ce_shard_combine_ex(stats, t, vocab_total, label_smoothing=0.0, reduce_loss=
                     ws, True, smoothing)
 
 
-def linear_desc(h: torch.Tensor, w: torch.Tensor) -> _abi.CeLinear:
-    """[N, D] hidden states and the [V, D] head weight (rows may be strided, columns contiguous)."""
+_GEMM = {"auto": _abi.CE_GEMM_AUTO, "native": _abi.CE_GEMM_NATIVE, "library": _abi.CE_GEMM_LIBRARY}
+
+
+def _gemm_code(gemm: str) -> int:
+    if gemm not in _GEMM:
+        raise CeArgumentError(_abi.CE_EINVAL, f"gemm must be one of {sorted(_GEMM)}, got {gemm!r}")
+    return _GEMM[gemm]
+
+
+def linear_desc(h: torch.Tensor, w: torch.Tensor, gemm: str = "auto") -> _abi.CeLinear:
+    """[N, D] hidden states and the [V, D] head weight (rows may be strided, columns contiguous); ``gemm``
+    picks the products' engine: "auto", "native" (the library's MFMA kernel where it applies) or
+    "library" (hipBLASLt)."""
     if h.dim() != 2 or w.dim() != 2 or h.shape[1] != w.shape[1]:
         raise CeArgumentError(_abi.CE_EINVAL, f"need h [N, D] and w [V, D], got {tuple(h.shape)} and {tuple(w.shape)}")
     if h.dtype != w.dtype:
@@ -456,8 +467,17 @@ def linear_desc(h: torch.Tensor, w: torch.Tensor) -> _abi.CeLinear:
     if (h.shape[0] > 1 and h.stride(1) != 1) or w.stride(1) != 1:
         raise CeArgumentError(_abi.CE_ELAYOUT, "h and w need contiguous columns")
     N, D = h.shape
-    return _abi.CeLinear(_ptr(h), _ptr(w), _dtype_code(h), 0, N, D, w.shape[0], max(h.stride(0), D),
+    return _abi.CeLinear(_ptr(h), _ptr(w), _dtype_code(h), _gemm_code(gemm), N, D, w.shape[0], max(h.stride(0), D),
                          max(w.stride(0), D))
+
+
+def ce_linear_gemm_plan(h, w, gemm="auto") -> int:
+    """Bit mask of the products ce_linear_cross_entropy runs on the library's MFMA kernel for these
+    operands and engine: 1 logits, 2 dh, 4 dW."""
+    plan = lib.ce_linear_gemm_plan(ctypes.byref(linear_desc(h, w, gemm)))
+    if plan < 0:
+        _check(_abi.CE_EINVAL)
+    return int(plan)
 
 
 def ce_linear_workspace_bytes(h, w, reduce_loss=False, chunk_rows=0, label_smoothing=0.0, ignore_idx=-100,
@@ -474,10 +494,11 @@ def ce_linear_workspace_bytes(h, w, reduce_loss=False, chunk_rows=0, label_smoot
 
 def ce_linear_cross_entropy(h, w, t, label_smoothing=0.0, reduce_loss=False, ignore_idx=-100, *, grad_out=None,
                             loss=None, n_valid=None, dh=None, dw=None, want_dh=True, want_dw=True,
-                            accumulate_dw=False, chunk_rows=0, ws=None, smoothing="all"):
+                            accumulate_dw=False, chunk_rows=0, ws=None, smoothing="all", gemm="auto"):
     """Loss of the head h W^T over row chunks, with dh = dL/dh (input dtype) and
     dw = dL/dW (FP32, or added to ``dw`` with ``accumulate_dw``).  ``t`` is
-    the [N] int64 targets (any stride).  Returns (loss, dh, dw, n_valid)."""
+    the [N] int64 targets (any stride); ``gemm`` the products' engine (see
+    linear_desc).  Returns (loss, dh, dw, n_valid)."""
     N, D = h.shape
     V = w.shape[0]
     dev = _device_of(h, "h")
@@ -502,7 +523,7 @@ def ce_linear_cross_entropy(h, w, t, label_smoothing=0.0, reduce_loss=False, ign
         raise CeArgumentError(_abi.CE_ELAYOUT, "dw must be an FP32 [V, D] tensor with contiguous columns")
     if t.dim() != 1 or t.numel() != N or t.dtype != torch.int64:
         raise CeArgumentError(_abi.CE_EINVAL, "targets must be an int64 [N] tensor")
-    desc = linear_desc(h, w)
+    desc = linear_desc(h, w, gemm)
     if ws is None:
         nb = lib.ce_linear_workspace_bytes(ctypes.byref(desc), ctypes.byref(p), int(chunk_rows), None)
         if nb == 0:
@@ -519,7 +540,7 @@ def ce_linear_cross_entropy(h, w, t, label_smoothing=0.0, reduce_loss=False, ign
 
 
 def ce_linear_tune(h, w, reduce_loss="mean", *, dh=None, dw=None, want_dh=True, want_dw=True, chunk_rows=0,
-                   ws=None, label_smoothing=0.0, smoothing="all"):
+                   ws=None, label_smoothing=0.0, smoothing="all", gemm="auto"):
     """Time the GEMM library's candidates for the chunked call's shapes on
     these buffers and keep the fastest (synchronises; dh and dw receive
     scratch values).  Returns the workspace it used, which the calls can share."""
@@ -535,7 +556,7 @@ def ce_linear_tune(h, w, reduce_loss="mean", *, dh=None, dw=None, want_dh=True, 
         dh = torch.empty((N, D), dtype=h.dtype, device=dev)
     if dw is None and want_dw:
         dw = torch.empty((V, D), dtype=torch.float32, device=dev)
-    desc = linear_desc(h, w)
+    desc = linear_desc(h, w, gemm)
     if ws is None:
         nb = lib.ce_linear_workspace_bytes(ctypes.byref(desc), ctypes.byref(p), int(chunk_rows), None)
         if nb == 0:
@@ -653,19 +674,19 @@ class LinearCrossEntropy(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, h, weight, target, label_smoothing=0.0, reduce_loss="mean", ignore_idx=-100,
-                smoothing="all", chunk_rows=0):
+                smoothing="all", chunk_rows=0, gemm="auto"):
         ctx.per_row = reduction_code(reduce_loss) == _abi.CE_REDUCE_NONE
-        ctx.args = (label_smoothing, reduce_loss, ignore_idx, smoothing, chunk_rows)
+        ctx.args = (label_smoothing, reduce_loss, ignore_idx, smoothing, chunk_rows, gemm)
         if ctx.per_row:
             loss, _, _, _ = ce_linear_cross_entropy(h.detach(), weight.detach(), target, label_smoothing,
                                                     reduce_loss, ignore_idx, want_dh=False, want_dw=False,
-                                                    chunk_rows=chunk_rows, smoothing=smoothing)
+                                                    chunk_rows=chunk_rows, smoothing=smoothing, gemm=gemm)
             ctx.save_for_backward(h.detach(), weight.detach(), target)
             return loss
         loss, dh, dw, _ = ce_linear_cross_entropy(h.detach(), weight.detach(), target, label_smoothing,
                                                   reduce_loss, ignore_idx, want_dh=ctx.needs_input_grad[0],
                                                   want_dw=ctx.needs_input_grad[1], chunk_rows=chunk_rows,
-                                                  smoothing=smoothing)
+                                                  smoothing=smoothing, gemm=gemm)
         ctx.save_for_backward(dh if dh is not None else torch.empty(0),
                               dw if dw is not None else torch.empty(0))
         ctx.has = (dh is not None, dw is not None)
@@ -675,31 +696,32 @@ class LinearCrossEntropy(torch.autograd.Function):
     def backward(ctx, grad_loss):
         if ctx.per_row:
             h, weight, target = ctx.saved_tensors
-            label_smoothing, reduce_loss, ignore_idx, smoothing, chunk_rows = ctx.args
+            label_smoothing, reduce_loss, ignore_idx, smoothing, chunk_rows, gemm = ctx.args
             g = grad_loss.to(dtype=torch.float32).reshape(-1).contiguous()
             _, dh, dw, _ = ce_linear_cross_entropy(h, weight, target, label_smoothing, reduce_loss, ignore_idx,
                                                    grad_out=g, want_dh=ctx.needs_input_grad[0],
                                                    want_dw=ctx.needs_input_grad[1], chunk_rows=chunk_rows,
-                                                   smoothing=smoothing)
-            return dh, dw, None, None, None, None, None, None
+                                                   smoothing=smoothing, gemm=gemm)
+            return dh, dw, None, None, None, None, None, None, None
         dh, dw = ctx.saved_tensors
         g = grad_loss.reshape(1)
         if ctx.has[0]:
             ce_scale_grad_inplace(dh.view(1, *dh.shape), g, per_row=False)
         if ctx.has[1]:
             ce_scale_grad_inplace(dw.view(1, *dw.shape), g, per_row=False)
-        return (dh if ctx.has[0] else None, dw if ctx.has[1] else None, None, None, None, None, None, None)
+        return (dh if ctx.has[0] else None, dw if ctx.has[1] else None, None, None, None, None, None, None, None)
 
 
 def linear_cross_entropy(h, weight, target, label_smoothing=0.0, reduce_loss="mean", ignore_idx=-100, *,
-                         smoothing="all", chunk_rows=0):
+                         smoothing="all", chunk_rows=0, gemm="auto"):
     """Cross-entropy of the head ``h @ weight.T`` without whole logits: the
     rows go through ce_linear_cross_entropy in chunks.  ``h`` [N, D],
     ``weight`` [V, D] (torch Linear layout), ``target`` [N] int64.  Returns
     the FP32 mean or sum, or the [N] per-row losses with
-    ``reduce_loss="none"``, and reaches autograd through LinearCrossEntropy."""
+    ``reduce_loss="none"``, and reaches autograd through LinearCrossEntropy.
+    ``gemm`` picks the products' engine (see linear_desc)."""
     return LinearCrossEntropy.apply(h, weight, target, label_smoothing, reduce_loss, ignore_idx, smoothing,
-                                    chunk_rows)
+                                    chunk_rows, gemm)
 
 
 class Profiler:

@@ -18,7 +18,8 @@ CE_OK, CE_EINVAL, CE_EDTYPE, CE_ELAYOUT, CE_EWORKSPACE, CE_EHIP, CE_EDEADLOCK = 
 CE_F32, CE_BF16 = 0, 1
 CE_REDUCE_NONE, CE_REDUCE_MEAN, CE_REDUCE_SUM = 0, 1, 2
 CE_SMOOTH_ALL, CE_SMOOTH_OTHERS = 0, 1
-CE_ABI_VERSION = 5
+CE_GEMM_AUTO, CE_GEMM_NATIVE, CE_GEMM_LIBRARY = 0, 1, 2
+CE_ABI_VERSION = 6
 
 
 class CeLogits(ctypes.Structure):
@@ -55,7 +56,7 @@ class CeLinear(ctypes.Structure):
         ("h", ctypes.c_void_p),
         ("w", ctypes.c_void_p),
         ("dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("gemm", ctypes.c_int32),
         ("N", ctypes.c_int64),
         ("D", ctypes.c_int64),
         ("V", ctypes.c_int64),
@@ -91,6 +92,7 @@ SIGNATURES = {
                                            _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                            _vp]),
     "ce_workspace_init": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp]),
+    "ce_linear_gemm_plan": (ctypes.c_int32, [_P(CeLinear)]),
     "ce_linear_workspace_bytes": (ctypes.c_size_t, [_P(CeLinear), _P(CeParams), ctypes.c_int64,
                                                     _P(ctypes.c_int64)]),
     "ce_linear_tune": (ctypes.c_int, [_P(CeLinear), _P(CeParams), _vp, ctypes.c_int64, _vp, ctypes.c_int64,

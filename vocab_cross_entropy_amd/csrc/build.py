@@ -59,8 +59,10 @@ def build(verbose: bool = False, variant: str = "") -> str:
     kobj = os.path.join(bdir, "ce_kernels.o")
     aobj = os.path.join(bdir, "ce_api.o")
     lobj = os.path.join(bdir, "ce_linear.o")
+    gobj = os.path.join(bdir, "ce_gemm.o")
     steps = [
         [HIPCC, *DEVICE, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_kernels.hip"), "-o", kobj],
+        [HIPCC, *DEVICE, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_gemm.hip"), "-o", gobj],
         [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_api.cpp"), "-o", aobj],
         [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_linear.cpp"), "-o", lobj],
     ]
@@ -69,9 +71,10 @@ def build(verbose: bool = False, variant: str = "") -> str:
         if verbose and out.strip():
             print(out)
     tmp = lib + ".tmp"
-    # the chunked linear call's GEMMs come from hipBLASLt (ROCm's matrix-core GEMM library)
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, aobj, lobj, "-L/opt/rocm/lib", "-lhipblaslt",
-          "-o", tmp])
+    # the chunked linear call's products run on the library's MFMA kernel (ce_gemm.hip) or on hipBLASLt
+    # (ROCm's matrix-core GEMM library), per ce_linear.gemm
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, gobj, aobj, lobj, "-L/opt/rocm/lib",
+          "-lhipblaslt", "-o", tmp])
     os.replace(tmp, lib)
     return lib
 

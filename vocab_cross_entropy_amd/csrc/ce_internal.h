@@ -179,6 +179,28 @@ hipError_t launch_linear_finish(const float* parts, int64_t nparts, int32_t redu
 // zeros in rows x cols of an FP32 matrix with row stride ld
 hipError_t launch_fill_f32(float* p, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream);
 
+// One BF16 product on the library's MFMA kernel (ce_gemm.hip), FP32 accumulation:
+//   C[M][N] (+)= sum_k A(m, k) B(n, k)
+// A is [M][K] (a_kc: K contiguous) or [K][M]; B is [N][K] (b_kc) or [K][N]; leading dimensions in elements.
+// out 0: C BF16, written; 1: C FP32, written; 2: C FP32, added to.  The layouts of the chunked head's three
+// products are supported: (a_kc, b_kc, out) = (1, 1, 0) logits, (1, 0, 0) dh, (0, 0, 1 or 2) dW.
+struct GemmBf16 {
+  const void* A;
+  int64_t lda;
+  bool a_kc;
+  const void* B;
+  int64_t ldb;
+  bool b_kc;
+  void* C;
+  int64_t ldc;
+  int out;
+  int M, N, K;
+};
+// Whether launch_gemm_bf16 takes g: M, N, K >= 1; lda and ldb multiples of 8 and at least the contiguous
+// extent; A and B 16-byte aligned (so no 16-byte chunk straddles a row's end); one of the head's layouts.
+bool gemm_bf16_supported(const GemmBf16& g);
+hipError_t launch_gemm_bf16(const GemmBf16& g, hipStream_t stream);
+
 // The instrumented build's phase-stamp buffer when it holds `bytes`, else NULL
 // (always NULL in the normal build).
 unsigned long long* phase_buffer(size_t bytes);

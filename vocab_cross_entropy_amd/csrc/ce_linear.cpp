@@ -229,7 +229,8 @@ ce_status check_linear(const ce_linear* lin, const ce_params* p) {
   if (!lin) return lfail(CE_EINVAL, "linear descriptor is NULL");
   if (!p) return lfail(CE_EINVAL, "params is NULL");
   if (lin->dtype != CE_F32 && lin->dtype != CE_BF16) return lfail(CE_EDTYPE, "unsupported dtype %d", lin->dtype);
-  if (lin->reserved != 0) return lfail(CE_EINVAL, "linear.reserved must be 0");
+  if (lin->gemm != CE_GEMM_AUTO && lin->gemm != CE_GEMM_NATIVE && lin->gemm != CE_GEMM_LIBRARY)
+    return lfail(CE_EINVAL, "linear.gemm must be CE_GEMM_AUTO, CE_GEMM_NATIVE or CE_GEMM_LIBRARY (got %d)", lin->gemm);
   if (lin->N < 0 || lin->D < 1 || lin->V < 1)
     return lfail(CE_EINVAL, "need N >= 0, D >= 1, V >= 1 (got %lld, %lld, %lld)", (long long)lin->N,
                  (long long)lin->D, (long long)lin->V);
@@ -259,6 +260,7 @@ struct LinLayout {
   size_t fused = 0;   // bytes the per-chunk fused call needs (its regions start at 0)
   size_t logits = 0, parts = 0, scale = 0, blas = 0, total = 0;
   int64_t chunk = 0, nchunks = 0;
+  int64_t ldl = 0;    // the chunk logits' row stride: V rounded up to a multiple of 8 (16-byte BF16 rows)
 };
 
 ce_status lin_layout(const ce_linear* lin, const ce_params* p, int64_t chunk_rows, LinLayout* out) {
@@ -266,9 +268,10 @@ ce_status lin_layout(const ce_linear* lin, const ce_params* p, int64_t chunk_row
   w.chunk = auto_chunk(lin, chunk_rows);
   w.nchunks = lin->N == 0 ? 0 : (lin->N + w.chunk - 1) / w.chunk;
   w.fused = vce::fused_workspace_bytes(w.chunk, lin->dtype, lin->V, p->reduce_loss != CE_REDUCE_NONE);
+  w.ldl = (lin->V + 7) & ~(int64_t)7;
   size_t off = align256(w.fused);
   w.logits = off;
-  off = align256(off + (size_t)w.chunk * (size_t)lin->V * (size_t)elem_bytes(lin->dtype));
+  off = align256(off + (size_t)w.chunk * (size_t)w.ldl * (size_t)elem_bytes(lin->dtype));
   w.parts = off;
   off = align256(off + (size_t)(w.nchunks > 0 ? w.nchunks : 1) * 4u);
   w.scale = off;  // float s, int32 n
@@ -288,10 +291,40 @@ ce_status chunk_plan_ok(const ce_linear* lin, const ce_params* p, int64_t rows) 
   x.dtype = lin->dtype;
   x.d0 = 1;
   x.d1 = rows;
-  x.s1 = lin->V;
+  x.s1 = (lin->V + 7) & ~(int64_t)7;
   x.v_local = lin->V;
   x.vocab_total = lin->V;
   return vce::fused_plan(&x, p, nullptr, nullptr, nullptr);
+}
+
+// The three products of a chunk.  CE_GEMM_NATIVE runs each on the library's
+// MFMA kernel (ce_gemm.hip) where it applies (BF16; h and W 16-byte aligned;
+// h_ld, w_ld and D multiples of 8), CE_GEMM_LIBRARY on hipBLASLt; CE_GEMM_AUTO
+// takes, per product, the engine measured faster on gfx950 at the head's
+// shapes (kAutoNative).
+enum Product { kLogits = 0, kDh = 1, kDw = 2 };
+constexpr bool kAutoNative[3] = {false, false, false};
+
+bool native_layout_ok(const ce_linear* lin) {
+  return lin->dtype == CE_BF16 && lin->h_ld % 8 == 0 && lin->w_ld % 8 == 0 && lin->D % 8 == 0 &&
+         (uintptr_t)lin->h % 16 == 0 && (uintptr_t)lin->w % 16 == 0;
+}
+
+bool use_native(const ce_linear* lin, Product prod) {
+  if (!native_layout_ok(lin)) return false;
+  return lin->gemm == CE_GEMM_NATIVE || (lin->gemm == CE_GEMM_AUTO && kAutoNative[prod]);
+}
+
+// One product on the engine chosen for it: the native kernel when selected and its checks pass, else the
+// GEMM library with the column-major form `lib`.
+ce_status run_product(int dev, const ce_linear* lin, Product prod, const vce::GemmBf16& nat, const Gemm& lib,
+                      void* blas_ws, hipStream_t stream) {
+  if (use_native(lin, prod) && vce::gemm_bf16_supported(nat)) {
+    hipError_t e = vce::launch_gemm_bf16(nat, stream);
+    if (e) return lfail(CE_EHIP, "GEMM %d x %d x %d launch: %s", nat.M, nat.N, nat.K, hipGetErrorString(e));
+    return CE_OK;
+  }
+  return run_gemm(dev, lib, blas_ws, stream);
 }
 
 }  // namespace
@@ -305,6 +338,25 @@ size_t ce_linear_workspace_bytes(const ce_linear* lin, const ce_params* p, int64
   if (lin_layout(lin, p, chunk_rows, &w) || chunk_plan_ok(lin, p, w.chunk)) return 0;
   if (chunk_rows_out) *chunk_rows_out = w.chunk;
   return w.total;
+}
+
+int32_t ce_linear_gemm_plan(const ce_linear* lin) {
+  if (!lin || (lin->dtype != CE_F32 && lin->dtype != CE_BF16) || lin->N < 0 || lin->D < 1 || lin->V < 1 ||
+      lin->N > 0x7fffffffLL || lin->V > 0x7fffffffLL || lin->D > 0x7fffffffLL || lin->h_ld < lin->D ||
+      lin->w_ld < lin->D || (lin->gemm != CE_GEMM_AUTO && lin->gemm != CE_GEMM_NATIVE && lin->gemm != CE_GEMM_LIBRARY))
+    return -1;
+  // the descriptors a chunk of n rows would use (the checks depend on the layouts, not on n or the buffers)
+  const int64_t ldl = (lin->V + 7) & ~(int64_t)7, n = lin->N > 0 ? lin->N : 1;
+  void* logits = reinterpret_cast<void*>((uintptr_t)256);
+  const int N = (int)n, D = (int)lin->D, V = (int)lin->V;
+  const vce::GemmBf16 d[3] = {
+      {lin->h, lin->h_ld, true, lin->w, lin->w_ld, true, logits, ldl, 0, N, V, D},
+      {logits, ldl, true, lin->w, lin->w_ld, false, logits, lin->D, 0, N, D, V},
+      {logits, ldl, false, lin->h, lin->h_ld, false, logits, lin->D, 1, V, D, N}};
+  int32_t plan = 0;
+  for (int k = 0; k < 3; ++k)
+    if (use_native(lin, (Product)k) && vce::gemm_bf16_supported(d[k])) plan |= 1 << k;
+  return plan;
 }
 
 ce_status ce_linear_tune(const ce_linear* lin, const ce_params* p, void* dh, int64_t dh_ld, float* dw,
@@ -330,15 +382,20 @@ ce_status ce_linear_tune(const ce_linear* lin, const ce_params* p, void* dh, int
   int64_t shapes[2] = {w.chunk, N % w.chunk};
   for (int64_t n : shapes) {
     if (n == 0 || N == 0) continue;
-    Gemm g1{ab, ab, V, n, D, HIPBLAS_OP_T, HIPBLAS_OP_N, lin->w, lin->w_ld, lin->h, lin->h_ld, logits, V, 0.f};
-    if ((st = tune_gemm(dev, g1, wsb + w.blas, stream))) return st;
-    if (dh) {
-      Gemm g2{ab, ab, D, n, V, HIPBLAS_OP_N, HIPBLAS_OP_N, lin->w, lin->w_ld, logits, V, dh, dh_ld, 0.f};
+    const int64_t ldl = w.ldl;
+    // (products that run on the native kernel have nothing to tune)
+    if (!use_native(lin, kLogits)) {
+      Gemm g1{ab, ab, V, n, D, HIPBLAS_OP_T, HIPBLAS_OP_N, lin->w, lin->w_ld, lin->h, lin->h_ld, logits, ldl, 0.f};
+      if ((st = tune_gemm(dev, g1, wsb + w.blas, stream))) return st;
+    }
+    if (dh && !use_native(lin, kDh)) {
+      Gemm g2{ab, ab, D, n, V, HIPBLAS_OP_N, HIPBLAS_OP_N, lin->w, lin->w_ld, logits, ldl, dh, dh_ld, 0.f};
       if ((st = tune_gemm(dev, g2, wsb + w.blas, stream))) return st;
     }
-    if (dw) {
+    if (dw && !use_native(lin, kDw)) {
       for (float beta : {0.f, 1.f}) {
-        Gemm g3{ab, HIP_R_32F, D, V, n, HIPBLAS_OP_N, HIPBLAS_OP_T, lin->h, lin->h_ld, logits, V, dw, dw_ld, beta};
+        Gemm g3{ab, HIP_R_32F, D, V, n, HIPBLAS_OP_N, HIPBLAS_OP_T, lin->h, lin->h_ld, logits, ldl, dw, dw_ld,
+                beta};
         if ((st = tune_gemm(dev, g3, wsb + w.blas, stream))) return st;
       }
     }
@@ -395,8 +452,10 @@ ce_status ce_linear_cross_entropy(const ce_linear* lin, const int64_t* targets, 
     const int64_t n = N - r0 < w.chunk ? N - r0 : w.chunk;
     const char* hc = static_cast<const char*>(lin->h) + (size_t)r0 * (size_t)lin->h_ld * eb;
     // logits_c = h_c W^T
-    Gemm g1{ab, ab, V, n, D, HIPBLAS_OP_T, HIPBLAS_OP_N, lin->w, lin->w_ld, hc, lin->h_ld, logits, V, 0.f};
-    if ((st = run_gemm(dev, g1, wsb + w.blas, stream))) return st;
+    const int64_t ldl = w.ldl;
+    Gemm g1{ab, ab, V, n, D, HIPBLAS_OP_T, HIPBLAS_OP_N, lin->w, lin->w_ld, hc, lin->h_ld, logits, ldl, 0.f};
+    const vce::GemmBf16 n1{hc, lin->h_ld, true, lin->w, lin->w_ld, true, logits, ldl, 0, (int)n, (int)V, (int)D};
+    if ((st = run_product(dev, lin, kLogits, n1, g1, wsb + w.blas, stream))) return st;
     // loss and gradient in place
     ce_logits x{};
     x.data = logits;
@@ -404,7 +463,7 @@ ce_status ce_linear_cross_entropy(const ce_linear* lin, const int64_t* targets, 
     x.d0 = 1;
     x.d1 = n;
     x.s0 = 0;
-    x.s1 = V;
+    x.s1 = ldl;
     x.v_local = V;
     x.vocab_start = 0;
     x.vocab_total = V;
@@ -417,14 +476,17 @@ ce_status ce_linear_cross_entropy(const ce_linear* lin, const int64_t* targets, 
     // dh_c = G_c W
     if (dh) {
       char* dhc = static_cast<char*>(dh) + (size_t)r0 * (size_t)dh_ld * eb;
-      Gemm g2{ab, ab, D, n, V, HIPBLAS_OP_N, HIPBLAS_OP_N, lin->w, lin->w_ld, logits, V, dhc, dh_ld, 0.f};
-      if ((st = run_gemm(dev, g2, wsb + w.blas, stream))) return st;
+      Gemm g2{ab, ab, D, n, V, HIPBLAS_OP_N, HIPBLAS_OP_N, lin->w, lin->w_ld, logits, ldl, dhc, dh_ld, 0.f};
+      const vce::GemmBf16 n2{logits, ldl, true, lin->w, lin->w_ld, false, dhc, dh_ld, 0, (int)n, (int)D, (int)V};
+      if ((st = run_product(dev, lin, kDh, n2, g2, wsb + w.blas, stream))) return st;
     }
     // dW (+)= G_c^T h_c
     if (dw) {
-      Gemm g3{ab, HIP_R_32F, D, V, n, HIPBLAS_OP_N, HIPBLAS_OP_T, hc, lin->h_ld, logits, V, dw, dw_ld,
-              (c > 0 || accumulate_dw) ? 1.f : 0.f};
-      if ((st = run_gemm(dev, g3, wsb + w.blas, stream))) return st;
+      const bool add = c > 0 || accumulate_dw;
+      Gemm g3{ab, HIP_R_32F, D, V, n, HIPBLAS_OP_N, HIPBLAS_OP_T, hc, lin->h_ld, logits, ldl, dw, dw_ld,
+              add ? 1.f : 0.f};
+      const vce::GemmBf16 n3{logits, ldl, false, hc, lin->h_ld, false, dw, dw_ld, add ? 2 : 1, (int)V, (int)D, (int)n};
+      if ((st = run_product(dev, lin, kDw, n3, g3, wsb + w.blas, stream))) return st;
     }
   }
   if (red != CE_REDUCE_NONE &&
