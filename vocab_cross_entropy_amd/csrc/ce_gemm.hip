@@ -25,7 +25,9 @@
 //    column.  Both layouts XOR-swizzle 16-byte chunks so that the reads and
 //    writes are free of bank conflicts.
 //  * Each k-tile runs 4 groups of 16 MFMAs; the next group's fragments, the
-//    loads and the LDS writes are interleaved between them, and the one
+//    loads (group 0) and the LDS writes (spread over groups 0-2: the writes
+//    compete with the fragment reads for the LDS data path, and bunched
+//    together they stall it) are interleaved between them, and the one
 //    barrier per k-tile sits before the last group, so the next tile's first
 //    fragments are read while that group runs.
 //  * Bounds: buffer loads with byte ranges read rows past M, N or K as zero;
@@ -117,21 +119,17 @@ struct Operand {
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)vo, (int)(s0 + j * jstr), 0);
   }
-  // half 0 or 1 of the staged chunks into LDS; with MASK (K-contiguous), elements at k >= K, which hold
-  // whatever follows in memory, are zeroed on the way
+  // staged chunk j into LDS; with MASK (K-contiguous), elements at k >= K, which hold whatever follows in
+  // memory, are zeroed on the way
   template <bool MASK>
-  __device__ __forceinline__ void lwrite(unsigned char* tile, const u32x4 (&v)[8], int half, int kt, int tid) const {
+  __device__ __forceinline__ void lwrite(unsigned char* tile, const u32x4 (&v)[8], int j, int kt, int tid) const {
     u32x4 keep = {~0u, ~0u, ~0u, ~0u};
     if constexpr (MASK && KC) {
       const int nv = K - (kt * kBK + (tid & 7) * 8);  // valid elements of this thread's 8
 #pragma unroll
       for (int w = 0; w < 4; ++w) keep[w] = (nv >= 2 * w + 2) ? 0xffffffffu : (nv == 2 * w + 1 ? 0x0000ffffu : 0u);
     }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = half * 4 + jj;
-      *reinterpret_cast<u32x4*>(tile + lw + j * 4096) = (MASK && KC) ? (v[j] & keep) : v[j];
-    }
+    *reinterpret_cast<u32x4*>(tile + lw + j * 4096) = (MASK && KC) ? (v[j] & keep) : v[j];
   }
   // fragment of rows (columns) rb .. rb+31 at k = kk*16 .. +15: lane l gets row rb + l%32 and
   // k = kk*16 + 8 (l/32) + e in element e (the MFMA's operand layout)
@@ -204,7 +202,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   // k-tile kt of parity P: MODE 2 loads tile kt+2 into register set P (which held tile kt, already in LDS)
-  // and writes tile kt+1 (set P^1) into the other LDS stage; MODE 0 (the last tile) neither.  The tile count
+  // and writes tile kt+1 (set P^1, loaded one tile earlier) into the other LDS stage; MODE 0 (the last
+  // tile) neither.  The tile count
   // is rounded up to even: a tile past K holds zeros (out of range, or masked), as do loads past the end.
   auto tile = [&](int kt, auto mode, auto parity) {
     constexpr int MODE = decltype(mode)::value;
@@ -214,6 +213,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
     auto& wa = P ? ra0 : ra1;
     auto& wb = P ? rb0 : rb1;
     unsigned char* nxt = smem + (P ^ 1) * kStage;
+    // tile kt+1's loads were issued a tile ago; its 16 chunks per operand go into LDS spread over groups 0-2
+    if constexpr (MODE == 2) GEMM_WAIT_VM(0);
 #pragma unroll
     for (int kk = 0; kk < 3; ++kk) {
       const int s = kk & 1;
@@ -223,20 +224,25 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
           oa.gload(kt + 2, la);
           ob.gload(kt + 2, lb);
         }
-        if (kk == 1) GEMM_WAIT_VM(16);  // tile kt+1's loads have landed (tile kt+2's may not have)
-        if (kk >= 1) {
-          oa.template lwrite<TAIL>(nxt, wa, kk - 1, kt + 1, tid);
-          ob.template lwrite<TAIL>(nxt + kTile, wb, kk - 1, kt + 1, tid);
-        }
+        // chunks j of each operand: group 0 takes j 0..1, group 1 j 2..4, group 2 j 5..7
+        const int j0 = kk == 0 ? 0 : (kk == 1 ? 2 : 5), j1 = kk == 0 ? 2 : (kk == 1 ? 5 : 8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j >= j0 && j < j1) {
+            oa.template lwrite<TAIL>(nxt, wa, j, kt + 1, tid);
+            ob.template lwrite<TAIL>(nxt + kTile, wb, j, kt + 1, tid);
+          }
       }
       mfmas(s);
       for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // an MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, kReads / 8, 0);   // fragment reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // an MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, kReads / 8, 0);                 // fragment reads
         if (MODE == 2 && kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // global loads
-        if (MODE == 2 && kk >= 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS writes
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (MODE == 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);            // LDS writes
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (MODE == 2) {
@@ -260,11 +266,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
   ob.gload(0, rb0);
   oa.gload(1, ra1);
   ob.gload(1, rb1);
-  GEMM_WAIT_VM(16);
-  oa.template lwrite<TAIL>(smem, ra0, 0, 0, tid);
-  oa.template lwrite<TAIL>(smem, ra0, 1, 0, tid);
-  ob.template lwrite<TAIL>(smem + kTile, rb0, 0, 0, tid);
-  ob.template lwrite<TAIL>(smem + kTile, rb0, 1, 0, tid);
+  GEMM_WAIT_VM(16);  // tile 0 has landed
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    oa.template lwrite<TAIL>(smem, ra0, j, 0, tid);
+    ob.template lwrite<TAIL>(smem + kTile, rb0, j, 0, tid);
+  }
   GEMM_WAIT_LGKM(0);
   __syncthreads();
   fread(0, 0, 0);
@@ -275,45 +282,68 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
   tile(nk2 - 2, I2{}, I0{});
   tile(nk2 - 1, I0{}, I1{});
 
-  // lane l holds rows (e/4)*8 + (l/32)*4 + e%4 and column l%32 of each 32 x 32 tile
+  // lane l holds rows (e/4)*8 + (l/32)*4 + e%4 and column l%32 of each 32 x 32 tile; slice i is the wave's
+  // rows i*32 .. +31 (64 values per lane)
+  auto at = [&](int i, int j, int e, int& row, int& col) {
+    row = m0 + wm * 128 + i * 32 + (lane >> 5) * 4 + (e >> 2) * 8 + (e & 3);
+    col = n0 + wn * 128 + j * 32 + (lane & 31);
+  };
+  if constexpr (OUT == 0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rb = m0 + wm * 128 + i * 32 + (lane >> 5) * 4;
-    if constexpr (OUT == 0) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = rb + (e >> 2) * 8 + (e & 3);
+          int row, col;
+          at(i, j, e, row, col);
           if (row < M && col < N) static_cast<__bf16*>(C)[(int64_t)row * ldc + col] = (__bf16)acc[i][j][e];
         }
-      }
-    } else {
-      float* __restrict__ Cf = static_cast<float*>(C);
-      float old[4][16];
-      if constexpr (OUT == 2) {
-        // the slice's old values first (64 loads in flight), then the sums
+  } else if constexpr (OUT == 1) {
+    float* __restrict__ Cf = static_cast<float*>(C);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int row = rb + (e >> 2) * 8 + (e & 3);
-            old[j][e] = (row < M && col < N) ? Cf[(int64_t)row * ldc + col] : 0.f;
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int row = rb + (e >> 2) * 8 + (e & 3);
-          if (row < M && col < N) Cf[(int64_t)row * ldc + col] = OUT == 2 ? old[j][e] + acc[i][j][e] : acc[i][j][e];
+          int row, col;
+          at(i, j, e, row, col);
+          if (row < M && col < N) Cf[(int64_t)row * ldc + col] = acc[i][j][e];
         }
-      }
-    }
+  } else {
+    // C += acc, two slices' old values in flight: the loads of slice i+1 are issued before slice i is summed
+    // and stored (the main loop's staging and fragment registers are free by now)
+    float* __restrict__ Cf = static_cast<float*>(C);
+    float old[2][4][16];
+    auto load = [&](int i, float (&o)[4][16]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          int row, col;
+          at(i, j, e, row, col);
+          o[j][e] = (row < M && col < N) ? Cf[(int64_t)row * ldc + col] : 0.f;
+        }
+    };
+    auto store = [&](int i, const float (&o)[4][16]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          int row, col;
+          at(i, j, e, row, col);
+          if (row < M && col < N) Cf[(int64_t)row * ldc + col] = o[j][e] + acc[i][j][e];
+        }
+    };
+    load(0, old[0]);
+    load(1, old[1]);
+    store(0, old[0]);
+    load(2, old[0]);
+    store(1, old[1]);
+    load(3, old[1]);
+    store(2, old[0]);
+    store(3, old[1]);
   }
 }
 
