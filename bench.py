@@ -78,6 +78,77 @@ def traffic_from_profiles(workload_name: str):
     return t, f"fetch x{fetch_scale:.3f}, write x{write_scale:.3f} (copy calibration)"
 
 
+def _counter_rows(outdir: str, counter: str):
+    """{dispatch id: (kernel name, summed counter value)} from a rocprofv3 --pmc csv output directory."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(outdir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {outdir}")
+    out = {}
+    for path in files:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = (path, r["Dispatch_Id"])
+                name, v = out.get(k, (r["Kernel_Name"], 0.0))
+                out[k] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def write_pmc_json(args):
+    """The counter file of the fused kernel on a workload: the median FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of its launches, and of the benchmark's full-size input copies (the calibration: a copy of
+    known size), stamped with the kernel source's sha256."""
+    import statistics
+
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    dt = args.dtype or ("bf16" if "bf16" in w.name else "f32")
+    if args.dtype:
+        other = "_bf16" if args.dtype == "f32" else "_f32"
+        name = w.name.replace(other, f"_{args.dtype}") if other in w.name else w.name
+    else:
+        name = w.name
+    eb = 2 if dt == "bf16" else 4
+    copy_bytes = w.rows * w.V * eb
+    vals = {}
+    for counter, d in (("FETCH_SIZE", args.pmc_json[0]), ("WRITE_SIZE", args.pmc_json[1])):
+        rows = _counter_rows(d, counter)
+        fused = [v for n, v in rows.values() if "k_fused<" in n]
+        copies = [v for n, v in rows.values() if "copyBuffer" in n]
+        if not fused or not copies:
+            raise SystemExit(f"{d}: no k_fused or copy dispatches with {counter}")
+        kname = sorted({n for n, _ in rows.values() if "k_fused<" in n})
+        vals[counter] = (statistics.median(fused), statistics.median(sorted(copies)[len(copies) // 2:]), kname)
+    kernel = vals["FETCH_SIZE"][2][0]
+    kernel = kernel[kernel.index("k_fused<"):kernel.index(">", kernel.index("k_fused<")) + 1]
+    pmc = {
+        "workload": name,
+        "kernel": kernel,
+        "kernel_source_sha256": kernel_source_sha(),
+        "fetch_kib": vals["FETCH_SIZE"][0],
+        "write_kib": vals["WRITE_SIZE"][0],
+        "copy": {"bytes": copy_bytes, "fetch_kib": vals["FETCH_SIZE"][1], "write_kib": vals["WRITE_SIZE"][1]},
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE -d {args.pmc_json[0]} -o pmc --output-format csv -- python -u bench.py "
+            f"--workload {args.workload} --steps 3 --warmup 1 --no-cpu-baseline",
+            f"rocprofv3 --pmc WRITE_SIZE -d {args.pmc_json[1]} -o pmc --output-format csv -- python -u bench.py "
+            f"--workload {args.workload} --steps 3 --warmup 1 --no-cpu-baseline",
+            f"python bench.py --workload {args.workload} --pmc-json {args.pmc_json[0]} {args.pmc_json[1]}",
+        ],
+    }
+    out = os.path.join(os.path.dirname(PMC_FILE), f"fused_{dt}_v{w.V}_pmc.json")
+    with open(out, "w") as f:
+        json.dump(pmc, f, indent=1)
+        f.write("\n")
+    t, note = traffic_from_profiles(name)
+    print(json.dumps({"written": out, "traffic_bytes_per_launch": t, "note": note}))
+
+
 def device_info(torch, dev) -> dict:
     """What the runtime reports of the device the step ran on; the peak HBM
     rate used as the roofline's denominator is the published figure."""
@@ -169,7 +240,13 @@ def main():
     ap.add_argument("--tune", action="store_true", help="--linear: ce_linear_tune before the timed steps")
     ap.add_argument("--gemm", choices=["auto", "native", "library"], default="auto",
                     help="--linear: the products' engine (the library's MFMA kernel or hipBLASLt)")
+    ap.add_argument("--pmc-json", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="no GPU work: from the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE output directories of "
+                         "two runs of this benchmark (same workload), write the counter file "
+                         "profiles/fused_<dtype>_v<V>_pmc.json that the benchmark line's roofline.traffic reads")
     args = ap.parse_args()
+    if args.pmc_json:
+        return write_pmc_json(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
