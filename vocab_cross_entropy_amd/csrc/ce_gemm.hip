@@ -288,6 +288,71 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
     row = m0 + wm * 128 + i * 32 + (lane >> 5) * 4 + (e >> 2) * 8 + (e & 3);
     col = n0 + wn * 128 + j * 32 + (lane & 31);
   };
+  // C += acc (FP32) through 16-byte row vectors, which need C 16-byte aligned and its rows a multiple of 16
+  // bytes; the written-only outputs keep the direct element stores, which the next tile's loads overlap
+  const bool vec = OUT == 2 && ((uintptr_t)C & 15u) == 0 && (ldc % 4) == 0;
+  if (vec) {
+    // Each wave's slice goes through its own LDS region (32 rows of 136 floats: the pad puts rows r and r+4,
+    // written by one instruction, on disjoint banks) and comes back as row vectors of 4 columns a lane.  The
+    // main loop's last fragment reads must be done in every wave first.
+    constexpr int kPad = 136;
+    __syncthreads();
+    float* reg = reinterpret_cast<float*>(smem) + wave * (32 * kPad);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const int rbase = m0 + wm * 128, cbase = n0 + wn * 128;
+    auto to_lds = [&](int i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          reg[((lane >> 5) * 4 + (e >> 2) * 8 + (e & 3)) * kPad + j * 32 + (lane & 31)] = acc[i][j][e];
+    };
+    {
+      float* __restrict__ Cf = static_cast<float*>(C);
+      // lane l takes columns (l%32)*4 .. +3 of rows q*2 + l/32; the next slice's old values are loaded before
+      // this slice is summed and stored
+      f32x4 old[2][16];
+      auto ld_old = [&](int i, f32x4 (&o)[16]) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int row = rbase + i * 32 + q * 2 + (lane >> 5), col = cbase + (lane & 31) * 4;
+          const float* src = Cf + (int64_t)row * ldc + col;
+          if (row < M && col + 4 <= N) {
+            o[q] = *reinterpret_cast<const f32x4*>(src);
+          } else {
+            o[q] = (f32x4){};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (row < M && col + k < N) o[q][k] = src[k];
+          }
+        }
+      };
+      ld_old(0, old[0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i + 1 < 4) ld_old(i + 1, old[(i + 1) & 1]);
+        to_lds(i);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = q * 2 + (lane >> 5), c = (lane & 31) * 4;
+          f32x4 v = *reinterpret_cast<const f32x4*>(reg + r * kPad + c);
+          v += old[i & 1][q];
+          const int row = rbase + i * 32 + r, col = cbase + c;
+          if (row >= M) continue;
+          float* dst = Cf + (int64_t)row * ldc + col;
+          if (col + 4 <= N) {
+            *reinterpret_cast<f32x4*>(dst) = v;
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (col + k < N) dst[k] = v[k];
+          }
+        }
+      }
+    }
+    return;
+  }
+  // element stores from the accumulator layout (and C += acc where C is not 16-byte aligned)
   if constexpr (OUT == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -299,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
           at(i, j, e, row, col);
           if (row < M && col < N) static_cast<__bf16*>(C)[(int64_t)row * ldc + col] = (__bf16)acc[i][j][e];
         }
-  } else if constexpr (OUT == 1) {
+  } else {
     float* __restrict__ Cf = static_cast<float*>(C);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -309,41 +374,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
         for (int e = 0; e < 16; ++e) {
           int row, col;
           at(i, j, e, row, col);
-          if (row < M && col < N) Cf[(int64_t)row * ldc + col] = acc[i][j][e];
+          if (row < M && col < N) {
+            float* p = Cf + (int64_t)row * ldc + col;
+            *p = OUT == 2 ? *p + acc[i][j][e] : acc[i][j][e];
+          }
         }
-  } else {
-    // C += acc, two slices' old values in flight: the loads of slice i+1 are issued before slice i is summed
-    // and stored (the main loop's staging and fragment registers are free by now)
-    float* __restrict__ Cf = static_cast<float*>(C);
-    float old[2][4][16];
-    auto load = [&](int i, float (&o)[4][16]) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          int row, col;
-          at(i, j, e, row, col);
-          o[j][e] = (row < M && col < N) ? Cf[(int64_t)row * ldc + col] : 0.f;
-        }
-    };
-    auto store = [&](int i, const float (&o)[4][16]) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          int row, col;
-          at(i, j, e, row, col);
-          if (row < M && col < N) Cf[(int64_t)row * ldc + col] = o[j][e] + acc[i][j][e];
-        }
-    };
-    load(0, old[0]);
-    load(1, old[1]);
-    store(0, old[0]);
-    load(2, old[0]);
-    store(1, old[1]);
-    load(3, old[1]);
-    store(2, old[0]);
-    store(3, old[1]);
   }
 }
 
