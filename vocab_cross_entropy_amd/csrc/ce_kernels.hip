@@ -1545,8 +1545,10 @@ int64_t stream_grid(int64_t N) { return N < (1 << 20) ? N : (1 << 20); }
 }  // namespace
 
 // Shapes available to the fused kernel, smallest capacity first.
-// (512, 8) covers 2049..4096 vectors with 8 waves a workgroup (56 VGPRs for
-// BF16, 8 waves per SIMD), which measured faster than (256, 16) at 128 VGPRs.
+// (512, 8) covers 2049..4096 vectors with 8 waves a workgroup (56 VGPRs and
+// 102 SGPRs for BF16: 7 waves per SIMD), which measured faster than (256, 16)
+// (90 VGPRs, 5 waves per SIMD), also on the 1024 rows of 32000 BF16 columns
+// that (256, 16) runs in one resident round and (512, 8) in two.
 static const FusedShape kShapes[] = {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {512, 8}, {512, 16}, {1024, 16}};
 
 FusedShape fused_shape_for(int64_t vecs) {
