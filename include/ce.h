@@ -232,7 +232,7 @@ ce_status ce_fwd_bwd_fused(const ce_logits* x, const ce_targets* t, const ce_par
  * process ends).  Calls no hipMalloc, hipFree or allocating routine.
  *   - It holds a call that needs at most 16 MiB of workspace: about
  *     256 + 12 N bytes, plus 32 N K when rows are split into K > 1 chunks
- *     (N = 8192 rows of 128000 BF16 columns, K = 4: 1.1 MB; unsplit rows: up
+ *     (N = 8192 rows of 128000 BF16 columns, K = 8: 2.2 MB; unsplit rows: up
  *     to about 1.39 million rows).  A larger call returns CE_EWORKSPACE
  *     before any HIP call.
  *   - The array used is that of the device `stream` belongs to (NULL: the

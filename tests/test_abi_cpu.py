@@ -154,7 +154,7 @@ def test_noalloc_rejects_before_any_hip_call(lib):
     assert call(h.logits(dtype=7)) == _abi.CE_EDTYPE
     assert call(h.logits(vocab_start=16, vocab_total=32)) == _abi.CE_ELAYOUT
     assert call(h.logits(), h.params(split_chunks=65)) == _abi.CE_EINVAL
-    # 131072 rows of 128000 BF16 columns in 4 chunks: 256 + (12 + 128) N bytes, above 16 MiB
+    # 131072 rows of 128000 BF16 columns in 8 chunks: 256 + (12 + 256) N bytes, above 16 MiB
     big = h.logits(d0=1, d1=131072, s0=131072 * 128000, s1=128000, v_local=128000, vocab_total=128000)
     assert call(big, h.params(reduce_loss=1)) == _abi.CE_EWORKSPACE
     assert b"16777216" in lib.ce_last_error()
@@ -208,8 +208,8 @@ def test_workspace_sizes(lib):
     p = h.params(reduce_loss=1, label_smoothing=0.1)
     n = lib.ce_workspace_bytes(ctypes.byref(x), ctypes.byref(p))
     # header + FP32 losses of the split calls + the fused call's tagged losses
-    # + 4 chunks (of at most 4096 vectors) x 4 tagged words per row
-    assert n == 256 + 8192 * 4 + 8192 * 8 + 8192 * 4 * 4 * 8
+    # + 8 chunks (of 2000 of the 2048 vectors of a 256 x 8 workgroup) x 4 tagged words per row
+    assert n == 256 + 8192 * 4 + 8192 * 8 + 8192 * 8 * 4 * 8
     # the sum keeps the same per-row losses as the mean
     assert lib.ce_workspace_bytes(ctypes.byref(x), ctypes.byref(h.params(reduce_loss=2, smoothing=1))) == n
     p0 = h.params()

@@ -123,13 +123,23 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit element format
 __device__ __forceinline__ Rsrc make_rsrc(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)(uint32_t)bytes, kRsrcWord3);
 }
+// Cache policy of the 16-byte loads and stores (the buffer instructions'
+// cache-policy operand).  kStream sets the non-temporal bit: the line is
+// touched once, so the caches give it the lowest priority to stay.  The
+// fused, statistics and backward kernels take it for the logits they stream.
+// On the 4 x 2048 x 128000 BF16 fused step: 675 against 735 us with loads and
+// stores marked, 706 with the stores alone, 714 with the loads alone; the
+// forward + backward pair: 1,151 against 1,174 us.
+constexpr int kCacheDefault = 0, kCacheStream = 2;
+template <int CP = kCacheDefault>
 __device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CP);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+template <int CP = kCacheDefault>
 __device__ __forceinline__ void bstore16(const uint4& v, Rsrc r, uint32_t off) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, CP);
 }
 // one element (index j) of a range-checked buffer, widened to FP32 (0 outside)
 template <int DT>
@@ -857,7 +867,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
     const unsigned long long cw = (a.reduce == CE_REDUCE_MEAN && tid < 64) ? count_word_early(a) : 0ull;
     uint4 v[P];
 #pragma unroll
-    for (int j = 0; j < P; ++j) v[j] = bload16(rb, (uint32_t)(j * T + tid) * 16u);
+    for (int j = 0; j < P; ++j) v[j] = bload16<kCacheStream>(rb, (uint32_t)(j * T + tid) * 16u);
     CE_STAMP(a.phase, item, 1);
     __builtin_amdgcn_s_setprio(0);
     const float g_up = a.g ? a.g[a.reduce ? 0 : r] : 1.f;
@@ -1078,7 +1088,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
         uint32_t o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = pack_bf16(fma_mix_lo(w[q], kr, b), fma_mix_hi(w[q], kr, b));
-        bstore16(make_uint4(o[0], o[1], o[2], o[3]), rb, (uint32_t)(j * T + tid_st) * 16u);
+        bstore16<kCacheStream>(make_uint4(o[0], o[1], o[2], o[3]), rb, (uint32_t)(j * T + tid_st) * 16u);
       }
     } else {
 #pragma unroll
@@ -1088,7 +1098,7 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
         float gr[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) gr[e] = __builtin_fmaf(softmax_term<DT>(f[e], c_hi, c_lo), s, b);
-        bstore16(pack<DT>(gr), rb, (uint32_t)(j * T + tid_st) * 16u);
+        bstore16<kCacheStream>(pack<DT>(gr), rb, (uint32_t)(j * T + tid_st) * 16u);
       }
     }
     if (HT) {
@@ -1246,7 +1256,7 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
     for (int64_t base = 0; base < g.nv; base += (int64_t)T * PB) {
       uint4 v[PB];
 #pragma unroll
-      for (int j = 0; j < PB; ++j) v[j] = bload16(rb, (uint32_t)(base + j * T + tid) * 16u);
+      for (int j = 0; j < PB; ++j) v[j] = bload16<kCacheStream>(rb, (uint32_t)(base + j * T + tid) * 16u);
       if (base == 0) CE_STAMP(a.phase, r, 1);
       float bm = -INFINITY;
 #pragma unroll
@@ -1396,7 +1406,7 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
     for (int64_t base = 0; base < g.nv; base += (int64_t)T * PB) {
       uint4 v[PB];
 #pragma unroll
-      for (int j = 0; j < PB; ++j) v[j] = bload16(rb, (uint32_t)(base + j * T + tid) * 16u);
+      for (int j = 0; j < PB; ++j) v[j] = bload16<kCacheStream>(rb, (uint32_t)(base + j * T + tid) * 16u);
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
         const int64_t i = base + j * T + tid;
@@ -1413,7 +1423,7 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
 #pragma unroll
           for (int e = 0; e < E; ++e) gr[e] = (e == (int)off) ? target_grad(f[e], pr[e]) : gr[e];
         }
-        bstore16(pack<DT>(gr), rb, (uint32_t)i * 16u);  // dropped past the row
+        bstore16<kCacheStream>(pack<DT>(gr), rb, (uint32_t)i * 16u);  // dropped past the row
       }
     }
   }
@@ -1562,12 +1572,18 @@ int64_t max_body_vecs(int32_t dtype, int64_t V) { return V / (dtype == CE_BF16 ?
 // Rows of up to 4096 vectors stay whole.  Longer rows are split into K
 // chunks held by 256 x 8 (2048 vectors) or 512 x 8 (4096 vectors)
 // workgroups; K is the one between ceil(nv / 4096) and ceil(nv / 2048) whose
-// chunks fill their workgroup's registers best (the fewer chunks on a tie
-// within 1%).  Measured on 8192 BF16 rows: how full the registers are
-// matters most (V = 100000: 7 chunks at 87% beat 4 at 76% by 7%; V = 49152:
-// 3 at 100% beat 2 at 75% by 4%), and between equally full options the one
-// with fewer chunks was as fast or faster at 65536, 152064 and 256000
-// columns (at 128000, 4 and 8 chunks measured within 1%).
+// chunks fill their workgroup's registers best.  How full the registers are
+// matters most (8192 BF16 rows of 100000 columns: 7 chunks at 87% beat 4 at
+// 76% by 8%).  Between options within 1% of each other, BF16 takes the
+// 256-thread chunks as long as K stays at most 8, FP32 the fewer chunks: the
+// BF16 512 x 8 instance runs 7 waves per SIMD (its scalar registers), so
+// three of its 8-wave workgroups leave one wave slot per SIMD idle where
+// seven 4-wave ones fill them (128000 columns: 8 chunks 653 against 4 at 673
+// us; 65536: 4 at 357-363 against 2 at 385-387), while FP32's runs 8 waves
+// per SIMD and gains nothing from the smaller shape (128000 FP32: 8 chunks
+// 1,279 against 16 at 1,328).  Past 8 chunks the exchange, where every chunk
+// reads all of its partners' words, costs more than the slot gains (256000
+// BF16: 8 chunks 1,318 against 16 at 1,338-1,342).
 int32_t fused_auto_chunks(int32_t dtype, int64_t V) {
   const int64_t nv = max_body_vecs(dtype, V);
   if (nv <= 4096) return 1;
@@ -1576,8 +1592,9 @@ int32_t fused_auto_chunks(int32_t dtype, int64_t V) {
   for (int64_t k = (nv + 4095) / 4096; k <= (nv + 2047) / 2048; ++k) {
     const int64_t c = (nv + k - 1) / k;
     const double fill = (double)c / (c <= 2048 ? 2048.0 : 4096.0);
-    if (fill > best_fill + 0.01) {
-      best_fill = fill;
+    const bool tie_to_more = dtype == CE_BF16 && k <= 8 && c <= 2048 && fill >= best_fill - 0.01;
+    if (fill > best_fill + 0.01 || tie_to_more) {
+      best_fill = fill > best_fill ? fill : best_fill;
       best_k = k;
     }
   }
