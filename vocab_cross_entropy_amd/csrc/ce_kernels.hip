@@ -247,17 +247,27 @@ __device__ __forceinline__ void launder(uint4& v) {
   asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 }
 
+// The largest of three floats in one v_max3_f32.  fmaxf on values that come
+// from integer unpacking makes the compiler quiet each operand first (one
+// v_max_f32 x, x per element), which doubled the max pass's instructions.  A
+// NaN element still makes the row NaN: the sum pass's exponential carries it.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // max(m, elements of v)
 template <int DT>
 __device__ __forceinline__ float vec_max(const uint4& v, float m) {
   if constexpr (DT == CE_BF16) {
-    m = fmaxf(m, fmaxf(bf_lo(v.x), bf_hi(v.x)));
-    m = fmaxf(m, fmaxf(bf_lo(v.y), bf_hi(v.y)));
-    m = fmaxf(m, fmaxf(bf_lo(v.z), bf_hi(v.z)));
-    return fmaxf(m, fmaxf(bf_lo(v.w), bf_hi(v.w)));
+    m = max3(m, bf_lo(v.x), bf_hi(v.x));
+    m = max3(m, bf_lo(v.y), bf_hi(v.y));
+    m = max3(m, bf_lo(v.z), bf_hi(v.z));
+    return max3(m, bf_lo(v.w), bf_hi(v.w));
   } else {
-    m = fmaxf(m, fmaxf(__uint_as_float(v.x), __uint_as_float(v.y)));
-    return fmaxf(m, fmaxf(__uint_as_float(v.z), __uint_as_float(v.w)));
+    m = max3(m, __uint_as_float(v.x), __uint_as_float(v.y));
+    return max3(m, __uint_as_float(v.z), __uint_as_float(v.w));
   }
 }
 
