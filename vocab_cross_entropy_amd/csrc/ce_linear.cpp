@@ -147,13 +147,16 @@ ce_status run_gemm(int dev, const Gemm& g, void* blas_ws, hipStream_t stream) {
   ce_status st = get_plan(dev, g, &p);
   if (st) return st;
   const float alpha = 1.f;
-  hipblasLtMatmulAlgo_t algo;  // a copy: ce_linear_tune may replace the plan's choice from another thread
+  // hipBLASLt states no thread safety for a handle or descriptor shared by host threads, and two threads'
+  // calls on one plan at the same time have failed (execution failed), so the enqueue is serialised; the
+  // kernels still run concurrently on the callers' streams.  The lock also covers ce_linear_tune replacing
+  // the plan's algorithm from another thread.
+  hipblasStatus_t s;
   {
     std::lock_guard<std::mutex> lk(g_blas_mu);
-    algo = p->algo;
+    s = hipblasLtMatmul(p->handle, p->desc, &alpha, g.A, p->a, g.B, p->b, &g.beta, g.D, p->c, g.D, p->c, &p->algo,
+                        blas_ws, kBlasWorkspace, stream);
   }
-  hipblasStatus_t s = hipblasLtMatmul(p->handle, p->desc, &alpha, g.A, p->a, g.B, p->b, &g.beta, g.D, p->c, g.D, p->c,
-                                      &algo, blas_ws, kBlasWorkspace, stream);
   if (s != HIPBLAS_STATUS_SUCCESS)
     return lfail(CE_EHIP, "GEMM %lld x %lld x %lld: %s", (long long)g.m, (long long)g.n, (long long)g.k,
                  blas_status(s));
@@ -176,6 +179,7 @@ ce_status tune_gemm(int dev, const Gemm& g, void* blas_ws, hipStream_t stream) {
   hipblasLtMatmulHeuristicResult_t res[kTuneCandidates];
   int nres = 0;
   {
+    std::lock_guard<std::mutex> lk(g_blas_mu);  // the plan's descriptors are shared with other threads' calls
     hipblasLtMatmulPreference_t pref = nullptr;
     const uint64_t wsmax = kBlasWorkspace;
     hipblasStatus_t s;
@@ -204,6 +208,7 @@ ce_status tune_gemm(int dev, const Gemm& g, void* blas_ws, hipStream_t stream) {
       bool ok = true;
       for (int rep = 0; rep < 4 && ok; ++rep) {
         if (rep == 1 && hipEventRecord(e0, stream)) ok = false;
+        std::lock_guard<std::mutex> lk(g_blas_mu);
         ok = ok && hipblasLtMatmul(p->handle, p->desc, &alpha, g.A, p->a, g.B, p->b, &g.beta, g.D, p->c, g.D,
                                    p->c, &res[i].algo, blas_ws, kBlasWorkspace, stream) == HIPBLAS_STATUS_SUCCESS;
       }
