@@ -1142,8 +1142,17 @@ __device__ __forceinline__ void fused_item(const FusedArgs& a, const ShardSet* s
   }
 }
 
+// The BF16 512 x 8 instances are held to 8 waves per SIMD (four workgroups a
+// CU; FP32's reach 8 by themselves).  That spills about 35 scalar registers to
+// vector lanes (the kernel needs 102 for 7 waves), and still wins: 1024 rows of 32000 columns then run in
+// one resident round, 27.3-27.4 against 28.8-29.3 us, and the split rows
+// that take this shape gain 1-2% (152064 columns: 818-820 against 828-829 us;
+// 256000: 1,308-1,314 against 1,333-1,337).  The 256-thread instances lose
+// from it (8192 rows of 128000: 668 against 654 us; 1024 of 8192: 15.5
+// against 14.2) and keep the default.
 template <int DT, int T, int P, bool HT>
-__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_fused(FusedArgs a) {
+__global__ __launch_bounds__(T)
+__attribute__((amdgpu_waves_per_eu((DT == CE_BF16 && T == 512 && P == 8) ? 8 : 4, 8))) void k_fused(FusedArgs a) {
   fused_item<DT, T, P, HT, false>(a, nullptr);
 }
 
