@@ -109,6 +109,7 @@ struct StatsArgs {
 
 struct BackwardArgs {
   RowLayout L;
+  int32_t K;               // items per row: batches of T x PB vectors, one a workgroup (set by the launcher)
   const float* lse;
   const float* lse_aux;    // [N][2] (lse residual, 1 - p_t) or NULL: the lse alone
   int32_t reduce;          // CE_REDUCE_*

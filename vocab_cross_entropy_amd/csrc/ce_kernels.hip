@@ -1291,6 +1291,11 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
         m2 = bm2;
         msub = m2;
       }
+      // The sum pass unpacks again rather than keep the max pass's floats: 96 instead of 130-137
+      // VGPRs, two 512-thread workgroups a CU instead of one (8192 rows of 128000 BF16 columns:
+      // 303-305 against 366-373 us).
+#pragma unroll
+      for (int j = 0; j < PB; ++j) launder(v[j]);
       // the batch holding the target vector (uniform test): its lane drops the target from the sum
       const int64_t tq = tvec - base;
       if (tq >= 0 && tq < (int64_t)T * PB) {
@@ -1350,18 +1355,26 @@ __global__ __launch_bounds__(T) void k_stats(StatsArgs a) {
 // expm1(x_t - lse) instead, resolved only to the FP32 lse's own precision.
 // Unsharded rows of at most kShortRow columns are recomputed whole by one
 // wave in FP64 (the fused kernel's short-row arithmetic); lse is not read.
+// A workgroup takes one item: batch k (T x PB body vectors) of row r, item
+// r K + k, so that a long row's batches run in K workgroups at once rather
+// than one after another in one (8192 rows of 128000 BF16 columns, K = 4:
+// 670-678 against 734-739 us); chunk 0 also takes the row's head and tail.
 template <int DT, int T, int PB>
 __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
   constexpr int E = ElemT<DT>::E, EB = ElemT<DT>::EB;
   const int tid = threadIdx.x;
   const RowLayout& L = a.L;
-  for (int64_t r = blockIdx.x; r < L.N; r += gridDim.x) {
+  const int64_t K = a.K, items = L.N * K;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t r = it / K, k = it - r * K;
     const Row<DT> g = row_geometry<DT>(L, r);
+    const int64_t cb = k * (int64_t)(T * PB);  // this item's first body vector
+    const int64_t ce = g.nv < cb + T * PB ? g.nv : cb + T * PB;
     if (g.t == L.ignore_idx) {
       const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-      for (int64_t i = tid; i < g.nv; i += T) g.body[i] = z;
-      if (tid < g.h) store_elem<DT>(g.base, tid, 0.f);
-      if (tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
+      for (int64_t i = cb + tid; i < ce; i += T) g.body[i] = z;
+      if (k == 0 && tid < g.h) store_elem<DT>(g.base, tid, 0.f);
+      if (k == 0 && tid < g.tn) store_elem<DT>(g.tail, tid, 0.f);
       continue;
     }
     const bool tvalid = g.t >= 0 && g.t < L.vocab_total;
@@ -1408,10 +1421,10 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
       return s * (p > 0.5f ? expm1f(x - lse) + L.q_rest : (p - L.q_o) - L.q_to);
     };
     const Rsrc rb = make_rsrc(g.body, g.nv * 16);
-    const Rsrc rh = make_rsrc(g.base, g.h * EB);
-    const Rsrc rt = make_rsrc(g.tail, (int64_t)g.tn * EB);
+    const Rsrc rh = make_rsrc(g.base, k == 0 ? g.h * EB : 0);
+    const Rsrc rt = make_rsrc(g.tail, k == 0 ? (int64_t)g.tn * EB : 0);
     {
-      // head and tail elements (range-checked: lanes past them do nothing)
+      // head and tail elements, chunk 0 (range-checked: lanes past them, and other chunks, do nothing)
       const float hx = bload_elem<DT>(rh, tid);
       const float tx = bload_elem<DT>(rt, tid);
       const float ph = ex2(__builtin_fmaf(hx, kL, -c_hi) - c_lo), pt = ex2(__builtin_fmaf(tx, kL, -c_hi) - c_lo);
@@ -1422,7 +1435,7 @@ __global__ __launch_bounds__(T) void k_backward(BackwardArgs a) {
       bstore_elem<DT>(gh, rh, tid);
       bstore_elem<DT>(gt, rt, tid);
     }
-    for (int64_t base = 0; base < g.nv; base += (int64_t)T * PB) {
+    for (int64_t base = cb; base < ce; base += (int64_t)T * PB) {  // one batch
       uint4 v[PB];
 #pragma unroll
       for (int j = 0; j < PB; ++j) v[j] = bload16<kCacheStream>(rb, (uint32_t)(base + j * T + tid) * 16u);
@@ -1676,12 +1689,15 @@ hipError_t launch_stats(const StatsArgs& a, hipStream_t stream, hipEvent_t ev0, 
   return e;
 }
 
-hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  if (a.L.N == 0) return hipSuccess;
+hipError_t launch_backward(const BackwardArgs& args, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  if (args.L.N == 0) return hipSuccess;
   hipError_t e = hipSuccess;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  const dim3 grid((uint32_t)stream_grid(a.L.N));
+  BackwardArgs a = args;
   const int nv = row_vectors(a.L);
+  // rows of more than 2048 vectors: items of 1024 x 4 vectors; shorter rows fit one batch
+  a.K = nv <= 2048 ? 1 : (int32_t)((nv + 4095) / 4096);
+  const dim3 grid((uint32_t)stream_grid(a.L.N * a.K));
   if (a.L.dtype == CE_BF16) {
     if (nv <= 1024)
       hipLaunchKernelGGL((k_backward<CE_BF16, kShortT, kShortPB>), grid, dim3(kShortT), 0, stream, a);
