@@ -271,8 +271,9 @@ def test_matrix_forward_backward(dtype, reduce, swapped, alpha):
 
 # ---------------------------------------------------------------------------
 # ragged and misaligned rows
-RAGGED = [(dt, V, off) for dt in (torch.float32, torch.bfloat16) for V in (1, 2, 7, 8, 9, 15, 17, 33, 1000, 4095, 32003)
-          for off in (0, 1)]
+# 70001 columns: rows of several backward items (BF16 3, FP32 5) with a head and a tail when offset
+RAGGED = [(dt, V, off) for dt in (torch.float32, torch.bfloat16)
+          for V in (1, 2, 7, 8, 9, 15, 17, 33, 1000, 4095, 32003, 70001) for off in (0, 1)]
 
 
 @pytest.mark.parametrize("dtype,V,offset", RAGGED, ids=[f"{'bf16' if r[0] == torch.bfloat16 else 'f32'}-V{r[1]}-off{r[2]}"
