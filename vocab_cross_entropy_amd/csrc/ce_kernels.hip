@@ -1587,10 +1587,9 @@ int64_t stream_grid(int64_t N) { return N < (1 << 20) ? N : (1 << 20); }
 }  // namespace
 
 // Shapes available to the fused kernel, smallest capacity first.
-// (512, 8) covers 2049..4096 vectors with 8 waves a workgroup (56 VGPRs and
-// 102 SGPRs for BF16: 7 waves per SIMD), which measured faster than (256, 16)
-// (90 VGPRs, 5 waves per SIMD), also on the 1024 rows of 32000 BF16 columns
-// that (256, 16) runs in one resident round and (512, 8) in two.
+// (512, 8) covers 2049..4096 vectors with 8 waves a workgroup (56 VGPRs; for
+// BF16 held to 8 waves per SIMD, see k_fused), which measured faster than
+// (256, 16) (90 VGPRs, 5 waves per SIMD).
 static const FusedShape kShapes[] = {{256, 1}, {256, 2}, {256, 4}, {256, 8}, {512, 8}, {512, 16}, {1024, 16}};
 
 FusedShape fused_shape_for(int64_t vecs) {
@@ -1607,15 +1606,17 @@ int64_t max_body_vecs(int32_t dtype, int64_t V) { return V / (dtype == CE_BF16 ?
 // chunks fill their workgroup's registers best.  How full the registers are
 // matters most (8192 BF16 rows of 100000 columns: 7 chunks at 87% beat 4 at
 // 76% by 8%).  Between options within 1% of each other, BF16 takes the
-// 256-thread chunks as long as K stays at most 8, FP32 the fewer chunks: the
-// BF16 512 x 8 instance runs 7 waves per SIMD (its scalar registers), so
-// three of its 8-wave workgroups leave one wave slot per SIMD idle where
-// seven 4-wave ones fill them (128000 columns: 8 chunks 653 against 4 at 673
-// us; 65536: 4 at 357-363 against 2 at 385-387), while FP32's runs 8 waves
-// per SIMD and gains nothing from the smaller shape (128000 FP32: 8 chunks
-// 1,279 against 16 at 1,328).  Past 8 chunks the exchange, where every chunk
-// reads all of its partners' words, costs more than the slot gains (256000
-// BF16: 8 chunks 1,318 against 16 at 1,338-1,342).
+// 256-thread chunks as long as K stays at most 8, FP32 the fewer chunks.
+// BF16 needs 102 scalar registers, 7 waves per SIMD: seven 4-wave workgroups
+// a CU fill them, where 8-wave workgroups run three a CU, or four held to 8
+// waves with spilled scalars; either way the smaller chunks won (128000
+// columns: 8 chunks 653 against 4 at 673 us at three a CU and 679 at four;
+// 65536: 4 at 357-363 against 2 at 385-387 and 397).  FP32's 512 x 8
+// instance runs 8 waves per SIMD by itself and gains nothing from the smaller
+// shape (128000 FP32: 8 chunks 1,279 against 16 at 1,328).  Past 8 chunks
+// the exchange, where every chunk reads all of its partners' words, costs
+// more than the slots gain (256000 BF16: 8 chunks 1,318 against 16 at
+// 1,338-1,342).
 int32_t fused_auto_chunks(int32_t dtype, int64_t V) {
   const int64_t nv = max_body_vecs(dtype, V);
   if (nv <= 4096) return 1;
