@@ -232,6 +232,26 @@ def test_workspace_init_validates(lib):
     assert lib.ce_workspace_init(ctypes.c_void_p(0x10000), 4100, None) == _abi.CE_EWORKSPACE
 
 
+# The automatic chunk count of a split row (the workspace holds 4 tagged 8-byte words per row and chunk): the
+# count whose chunks fill their workgroup's registers best; between options within 1%, BF16 takes the
+# 256-thread chunks while K stays at most 8, FP32 the fewer chunks.
+AUTO_CHUNKS = [(_abi.CE_BF16, 49152, 3), (_abi.CE_BF16, 65536, 4), (_abi.CE_BF16, 100000, 7),
+               (_abi.CE_BF16, 128000, 8), (_abi.CE_BF16, 152064, 5), (_abi.CE_BF16, 256000, 8),
+               (_abi.CE_BF16, 32768, 1), (_abi.CE_F32, 65536, 4), (_abi.CE_F32, 128000, 8),
+               (_abi.CE_F32, 16384, 1)]
+
+
+@pytest.mark.parametrize("dtype,V,K", AUTO_CHUNKS, ids=[f"{'bf16' if d == _abi.CE_BF16 else 'f32'}-V{v}"
+                                                        for d, v, _ in AUTO_CHUNKS])
+def test_automatic_chunk_count(lib, dtype, V, K):
+    h = Host(N=64, V=V)
+    x = h.logits(dtype=dtype, d0=1, d1=64, s0=64 * V, s1=V)
+    p = h.params()  # no reduction: header + tagged losses + the exchange words
+    n = lib.ce_workspace_bytes(ctypes.byref(x), ctypes.byref(p))
+    tagged = (256 + 64 * 8 + 255) // 256 * 256
+    assert n == tagged + (64 * K * 4 * 8 if K > 1 else 0), (n, K)
+
+
 def test_split_chunks_too_few_rejected(lib):
     # V = 600000 BF16 rows need at least 5 chunks of 16384 vectors; 4 cannot hold them
     h = Host()
