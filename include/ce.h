@@ -349,13 +349,14 @@ ce_status ce_shard_combine_ex(const float* stats, int32_t S, int64_t d0, int64_t
  */
 /* The engine of the three products (ce_linear.gemm):
  *   CE_GEMM_NATIVE   the library's own MFMA kernel (v_mfma_f32_32x32x16_bf16,
- *                    256 x 256 output tiles, operands staged two k-tiles deep
- *                    through registers into LDS) wherever it applies: BF16,
- *                    h and w 16-byte aligned, h_ld, w_ld and D multiples of 8;
- *                    other calls, and FP32 heads, run on the GEMM library
+ *                    256 x 256 output tiles, operands loaded straight into
+ *                    two LDS stages) wherever it applies: BF16, h and w
+ *                    16-byte aligned, h_ld, w_ld and D multiples of 8; other
+ *                    calls, and FP32 heads, run on the GEMM library
  *   CE_GEMM_LIBRARY  hipBLASLt, ROCm's GEMM library, for every product
  *   CE_GEMM_AUTO     per product, the engine measured faster on gfx950 at the
- *                    head's shapes (currently the library for all three)
+ *                    head's shapes (currently the native kernel for dW and
+ *                    the library for logits and dh)
  * Both engines accumulate in FP32 and round the output once; their results
  * differ only in the summation order. */
 #define CE_GEMM_AUTO 0

@@ -8,10 +8,11 @@ oracle's (FP32, then BF16 by nearest even) bit for bit, and the stated
 cross-entropy bar applies to the loss.  The logits have a standard deviation
 of about 0.08 sqrt(D).
 
-Every test runs under both GEMM engines: "native" (the library's MFMA
-kernel, ce_gemm.hip, for BF16 heads whose rows are 16-byte multiples; the
-plan query confirms it ran) and "library" (hipBLASLt).  Both accumulate in
-FP32, so the same bars hold for both.
+Every test runs under each GEMM choice: "native" (the library's MFMA
+kernel, ce_gemm.hip, for BF16 heads whose rows are 16-byte multiples),
+"library" (hipBLASLt) and "auto" (the default: the native kernel for dW, the
+library for logits and dh); the plan query confirms which products ran
+natively.  Both engines accumulate in FP32, so the same bars hold for all.
 
 Gradient bars, derived from the cross-entropy bar (the library's G differs
 from the exact G by at most r_G |G| + a_G per element: 2^-8 and 1e-7 for
@@ -32,15 +33,16 @@ from gpu_util import GRAD_TOL, assert_loss, orc, say
 
 pytestmark = pytest.mark.gpu
 
-ENGINES = ["native", "library"]
+ENGINES = ["native", "library", "auto"]
 
 
 def expected_plan(h, w, gemm):
-    """The products the native kernel takes: all three for BF16 with 16-byte rows under "native"."""
+    """The products the native kernel takes: all three for BF16 with 16-byte rows under "native", dW alone
+    under "auto"."""
     D = h.shape[1]
     ok = (h.dtype == torch.bfloat16 and D % 8 == 0 and max(h.stride(0), D) % 8 == 0 and w.stride(0) % 8 == 0
           and h.data_ptr() % 16 == 0 and w.data_ptr() % 16 == 0)
-    return 7 if (gemm == "native" and ok) else 0
+    return 0 if not ok else {"native": 7, "auto": 4}.get(gemm, 0)
 
 
 def grid_inputs(N, D, V, dtype, seed, ignore_frac=0.2):
@@ -103,8 +105,7 @@ def run_linear(h, w, t, alpha, reduce, g=None, chunk_rows=0, smoothing="all", wa
     dw = None
     if dw0 is not None:
         dw = torch.as_tensor(dw0, dtype=torch.float32).cuda()
-    if gemm != "auto":
-        assert vce.ce_linear_gemm_plan(hd, wd, gemm) == expected_plan(hd, wd, gemm)
+    assert vce.ce_linear_gemm_plan(hd, wd, gemm) == expected_plan(hd, wd, gemm)
     loss, dh, dwo, n = vce.ce_linear_cross_entropy(hd, wd, td, alpha, reduce, grad_out=gd, chunk_rows=chunk_rows,
                                                    smoothing=smoothing, want_dh=want_dh, want_dw=want_dw, dw=dw,
                                                    accumulate_dw=dw0 is not None, gemm=gemm)

@@ -10,30 +10,31 @@
 //   dh_c     [n][D] = G_c W      A = G_c (K-contig.)  B = W ([V][D], N-contig.)  BF16 out
 //   dW       [V][D] (+)= G_c^T h_c   A = G_c ([n][V], M-contig.)  B = h_c ([n][D], N-contig.)  FP32 out
 //
-// Design (one 256 x 256 output tile per workgroup of 4 waves, 128 x 128 per
-// wave, the FP32 accumulators in AGPRs):
-//  * k-tiles of 64: every thread stages 8 chunks of 16 bytes of each operand
-//    per k-tile through registers, in two register sets, so the loads of tile
-//    kt+2 are in flight while tile kt+1 goes into LDS and tile kt feeds the
-//    MFMAs.  Two loads deep is what keeps the operand stream near the rate
-//    the matrix cores consume it (one deep, or loads straight into LDS, leave
-//    them waiting).
-//  * LDS holds two stages of both tiles (128 KiB).  K-contiguous tiles are
-//    [256][64] with 128-byte rows and fragments read by ds_read_b128;
-//    M/N-contiguous tiles are [64][256] with 512-byte rows and fragments read
-//    by ds_read_b64_tr_b16, which hands every lane 4 consecutive k of its own
-//    column.  Both layouts XOR-swizzle 16-byte chunks so that the reads and
-//    writes are free of bank conflicts.
-//  * Each k-tile runs 4 groups of 16 MFMAs; the next group's fragments, the
-//    loads (group 0) and the LDS writes (spread over groups 0-2: the writes
-//    compete with the fragment reads for the LDS data path, and bunched
-//    together they stall it) are interleaved between them, and the one
-//    barrier per k-tile sits before the last group, so the next tile's first
-//    fragments are read while that group runs.
-//  * Bounds: buffer loads with byte ranges read rows past M, N or K as zero;
-//    K-contiguous elements past K (the rest of a row) are zeroed on their way
-//    into LDS; stores are guarded.  Leading dimensions are multiples of 8 and
-//    the operands 16-byte aligned, so no 16-byte chunk straddles a range end.
+// One 256 x 256 output tile per workgroup of 4 waves, 128 x 128 per wave, the FP32 accumulators in AGPRs,
+// k-tiles of 64, two LDS stages (128 KiB).  Two kernels:
+//  * k_gemm_dma (the default): both operands go from memory straight into LDS (buffer_load ... lds, 1 KiB
+//    per wave instruction, whole 128-byte lines).  The one barrier per k-tile sits before its last group of
+//    MFMAs: by then every wave holds the tile's last fragments and the next tile has landed, so the stage
+//    just read takes the loads of the tile after next (issued alongside the last group) while the next
+//    tile's first fragments are read.  The loads are issued in asm: the compiler cannot tell the two stages
+//    of the LDS array apart and would otherwise wait for every load in flight before each LDS read.  BF16
+//    results leave through a per-wave LDS slice as 16-byte row chunks (the MFMA operands are swapped so
+//    that each lane holds 4 consecutive columns of one row).
+//  * k_gemm (shapes the first does not take: a K-contiguous operand whose K is not a multiple of 64, which
+//    must be masked on its way into LDS, or an M/N-contiguous operand whose k-extent exceeds a 31-bit byte
+//    range): every thread stages 8 chunks of 16 bytes of each operand per k-tile through registers, in two
+//    register sets, so the loads of tile kt+2 are in flight while tile kt+1 goes into LDS (ds_write) and
+//    tile kt feeds the MFMAs; the barrier also sits before the last group.
+// Common to both:
+//  * LDS layouts: K-contiguous tiles are [256][64] with 128-byte rows, fragments read by ds_read_b128;
+//    M/N-contiguous tiles are [64][256] with 512-byte rows, fragments read by ds_read_b64_tr_b16, which
+//    hands every lane 4 consecutive k of its own column.  Both XOR-swizzle 16-byte chunks so that reads
+//    and writes are free of bank conflicts.
+//  * Each k-tile runs 4 groups of 16 MFMAs with the next group's fragments read between them.
+//  * Bounds: buffer loads with byte ranges read rows past M, N or K as zero (an M/N-contiguous operand's
+//    columns past M or N may read what follows them, which reaches only output rows or columns that are
+//    never stored); stores are guarded.  Leading dimensions are multiples of 8 and the operands 16-byte
+//    aligned, so no 16-byte chunk straddles a range end.
 #include <stdint.h>
 
 #include <type_traits>
@@ -51,6 +52,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_t;
 
 constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
 constexpr int kTile = 256 * kBK * 2;  // one operand's tile: 32 KiB
@@ -150,6 +152,142 @@ struct Operand {
   }
 };
 
+// One wave's 1 KiB load from a buffer straight into LDS at `lds` (lane l's 16 bytes at lds + 16 l), from
+// byte offset vo + soff of the buffer `desc`.  No registers receive data, so the compiler tracks nothing;
+// the caller waits for it (vmcnt) and makes it visible to the other waves (barrier) before reading.
+__device__ __forceinline__ void lds_dma16(u32x4 desc, uint32_t lds, uint32_t vo, uint32_t soff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(vo), "s"(desc), "s"(soff), "{m0}"(lds) : "memory");
+}
+// raw buffer descriptor: base, no stride, `bytes` in range (reads past it return zero)
+__device__ __forceinline__ u32x4 desc16(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  return (u32x4){(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// One operand's loads straight into LDS: wave w fills 1 KiB blocks 8w .. 8w+7 of the operand's stage tile.
+// K-contiguous: block q holds rows 8q .. 8q+7 (lane l: row 8q + l/8, physical chunk l%8, which holds the
+// logical chunk (l%8) ^ swz_k(row)); the buffer is the block's rows, k-tile kt at byte offset 128 kt.
+// M/N-contiguous: block q holds k-rows 2q, 2q+1 (lane l: k-row 2q + l/32, physical chunk l%32, holding the
+// logical chunk (l%32) ^ swz_mn(k)); the buffer is rows 0 .. K-1 from column r0, k-tile kt at 64 kt rows.
+template <bool KC>
+struct DmaOperand {
+  u32x4 d;
+  uint32_t vo[8];
+  uint32_t kstep;  // bytes between k-tiles
+  __device__ __forceinline__ void init(const __bf16* p, int64_t ld, int R, int r0, int K, int wave, int lane) {
+    if constexpr (KC) {
+      const int rows = R - r0 < 256 ? R - r0 : 256;
+      d = desc16(p + (int64_t)r0 * ld, (uint32_t)(rows * ld * 2));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = (wave * 8 + j) * 8 + (lane >> 3);
+        vo[j] = (uint32_t)(r * ld * 2) + ((((uint32_t)lane & 7u) ^ swz_k(r)) << 4);
+      }
+      kstep = kBK * 2;
+    } else {
+      // the range ends with row K-1's last column of this block (rounded up to a 16-byte chunk)
+      const int64_t cols = ((int64_t)(R - r0) + 7) & ~(int64_t)7;
+      d = desc16(p + r0, (uint32_t)(((int64_t)(K - 1) * ld + (cols < 256 ? cols : 256)) * 2));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = (wave * 8 + j) * 2 + (lane >> 5);
+        vo[j] = (uint32_t)(k * ld * 2) + ((((uint32_t)lane & 31u) ^ swz_mn(k)) << 4);
+      }
+      kstep = (uint32_t)(kBK * ld * 2);
+    }
+  }
+};
+
+// The workgroup's output tile.  The 8 XCDs take blocks round-robin (block id mod 8); each gets a contiguous
+// run of tiles, which it walks in groups of 4 n-blocks, n fastest, so that the tiles resident on one XCD
+// share operand slabs in its L2.
+__device__ __forceinline__ void tile_origin(int mblocks, int& m0, int& n0) {
+  constexpr int kGroup = 4;
+  const int T = gridDim.x, per = (T + 7) / 8;
+  const int L = (T & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * per + (blockIdx.x >> 3));
+  const int nblocks = T / mblocks;
+  const int grp = L / (kGroup * mblocks), first = grp * kGroup;
+  const int gsz = nblocks - first < kGroup ? nblocks - first : kGroup;
+  n0 = (first + (L - grp * kGroup * mblocks) % gsz) * kBN;
+  m0 = ((L - grp * kGroup * mblocks) / gsz) * kBM;
+}
+
+// FP32 results (OUT 1: written, 2: added) from the accumulator layout: lane l holds rows
+// (e/4)*8 + (l/32)*4 + e%4 and column l%32 of each 32 x 32 block.  C += acc goes through LDS (`smem`, free
+// by now) as 16-byte row vectors where C allows them; the written-only output keeps element stores.
+template <int OUT>
+__device__ __forceinline__ void store_acc_f32(const f32x16 (&acc)[4][4], unsigned char* smem, void* C, int64_t ldc,
+                                              int M, int N, int m0, int n0, int wm, int wn, int wave, int lane) {
+  float* __restrict__ Cf = static_cast<float*>(C);
+  const bool vec = OUT == 2 && ((uintptr_t)C & 15u) == 0 && (ldc % 4) == 0;
+  if (vec) {
+    // Each wave's slice goes through its own LDS region (32 rows of 136 floats: the pad puts rows r and r+4,
+    // written by one instruction, on disjoint banks) and comes back as row vectors of 4 columns a lane.
+    constexpr int kPad = 136;
+    float* reg = reinterpret_cast<float*>(smem) + wave * (32 * kPad);
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const int rbase = m0 + wm * 128, cbase = n0 + wn * 128;
+    // lane l takes columns (l%32)*4 .. +3 of rows q*2 + l/32; the next slice's old values are loaded before
+    // this slice is summed and stored
+    f32x4 old[2][16];
+    auto ld_old = [&](int i, f32x4 (&o)[16]) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = rbase + i * 32 + q * 2 + (lane >> 5), col = cbase + (lane & 31) * 4;
+        const float* src = Cf + (int64_t)row * ldc + col;
+        if (row < M && col + 4 <= N) {
+          o[q] = *reinterpret_cast<const f32x4*>(src);
+        } else {
+          o[q] = (f32x4){};
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (row < M && col + k < N) o[q][k] = src[k];
+        }
+      }
+    };
+    ld_old(0, old[0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i + 1 < 4) ld_old(i + 1, old[(i + 1) & 1]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          reg[((lane >> 5) * 4 + (e >> 2) * 8 + (e & 3)) * kPad + j * 32 + (lane & 31)] = acc[i][j][e];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = q * 2 + (lane >> 5), c = (lane & 31) * 4;
+        f32x4 v = *reinterpret_cast<const f32x4*>(reg + r * kPad + c);
+        v += old[i & 1][q];
+        const int row = rbase + i * 32 + r, col = cbase + c;
+        if (row >= M) continue;
+        float* dst = Cf + (int64_t)row * ldc + col;
+        if (col + 4 <= N) {
+          *reinterpret_cast<f32x4*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (col + k < N) dst[k] = v[k];
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * 128 + i * 32 + (lane >> 5) * 4 + (e >> 2) * 8 + (e & 3);
+        const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+        if (row < M && col < N) {
+          float* p = Cf + (int64_t)row * ldc + col;
+          *p = OUT == 2 ? *p + acc[i][j][e] : acc[i][j][e];
+        }
+      }
+}
+
 // OUT 0: BF16 store, 1: FP32 store, 2: FP32 accumulate.  TAIL: the k-tiles (64 wide, an even number of them)
 // reach past K, and a K-contiguous operand must have those elements zeroed.
 template <bool AK, bool BKC, int OUT, bool TAIL>
@@ -158,16 +296,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
                                                    int64_t ldc, int M, int N, int K, int mblocks) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // The 8 XCDs take blocks round-robin (block id mod 8); each gets a contiguous run of tiles, which it walks
-  // in groups of 4 n-blocks, n fastest, so that the tiles resident on one XCD share operand slabs in its L2.
-  constexpr int kGroup = 4;
-  const int T = gridDim.x, per = (T + 7) / 8;
-  const int L = (T & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * per + (blockIdx.x >> 3));
-  const int nblocks = T / mblocks;
-  const int grp = L / (kGroup * mblocks), first = grp * kGroup;
-  const int gsz = nblocks - first < kGroup ? nblocks - first : kGroup;
-  const int bn = first + (L - grp * kGroup * mblocks) % gsz, bm = (L - grp * kGroup * mblocks) / gsz;
-  const int m0 = bm * kBM, n0 = bn * kBN;
+  int m0, n0;
+  tile_origin(mblocks, m0, n0);
   const int wm = wave & 1, wn = wave >> 1;
   Operand<AK> oa;
   Operand<BKC> ob;
@@ -282,103 +412,157 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
   tile(nk2 - 2, I2{}, I0{});
   tile(nk2 - 1, I0{}, I1{});
 
-  // lane l holds rows (e/4)*8 + (l/32)*4 + e%4 and column l%32 of each 32 x 32 tile; slice i is the wave's
-  // rows i*32 .. +31 (64 values per lane)
-  auto at = [&](int i, int j, int e, int& row, int& col) {
-    row = m0 + wm * 128 + i * 32 + (lane >> 5) * 4 + (e >> 2) * 8 + (e & 3);
-    col = n0 + wn * 128 + j * 32 + (lane & 31);
-  };
-  // C += acc (FP32) through 16-byte row vectors, which need C 16-byte aligned and its rows a multiple of 16
-  // bytes; the written-only outputs keep the direct element stores, which the next tile's loads overlap
-  const bool vec = OUT == 2 && ((uintptr_t)C & 15u) == 0 && (ldc % 4) == 0;
-  if (vec) {
-    // Each wave's slice goes through its own LDS region (32 rows of 136 floats: the pad puts rows r and r+4,
-    // written by one instruction, on disjoint banks) and comes back as row vectors of 4 columns a lane.  The
-    // main loop's last fragment reads must be done in every wave first.
-    constexpr int kPad = 136;
-    __syncthreads();
-    float* reg = reinterpret_cast<float*>(smem) + wave * (32 * kPad);
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    const int rbase = m0 + wm * 128, cbase = n0 + wn * 128;
-    auto to_lds = [&](int i) {
+  if constexpr (OUT == 0) {
+    // BF16 element stores from the accumulator layout (rows (e/4)*8 + (l/32)*4 + e%4, column l%32 of each
+    // 32 x 32 block): 32 consecutive columns of two rows per instruction
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          reg[((lane >> 5) * 4 + (e >> 2) * 8 + (e & 3)) * kPad + j * 32 + (lane & 31)] = acc[i][j][e];
-    };
-    {
-      float* __restrict__ Cf = static_cast<float*>(C);
-      // lane l takes columns (l%32)*4 .. +3 of rows q*2 + l/32; the next slice's old values are loaded before
-      // this slice is summed and stored
-      f32x4 old[2][16];
-      auto ld_old = [&](int i, f32x4 (&o)[16]) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int row = rbase + i * 32 + q * 2 + (lane >> 5), col = cbase + (lane & 31) * 4;
-          const float* src = Cf + (int64_t)row * ldc + col;
-          if (row < M && col + 4 <= N) {
-            o[q] = *reinterpret_cast<const f32x4*>(src);
-          } else {
-            o[q] = (f32x4){};
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              if (row < M && col + k < N) o[q][k] = src[k];
-          }
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + wm * 128 + i * 32 + (lane >> 5) * 4 + (e >> 2) * 8 + (e & 3);
+          const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+          if (row < M && col < N) static_cast<__bf16*>(C)[(int64_t)row * ldc + col] = (__bf16)acc[i][j][e];
         }
-      };
-      ld_old(0, old[0]);
+  } else {
+    // C += acc reuses LDS: the main loop's last fragment reads must be done in every wave
+    if constexpr (OUT == 2) __syncthreads();
+    store_acc_f32<OUT>(acc, smem, C, ldc, M, N, m0, n0, wm, wn, wave, lane);
+  }
+}
+
+// Both operands straight into LDS (shapes: gemm_dma_ok).  Same tile, LDS layouts and fragment reads as
+// k_gemm; k-tile kt's loads are issued with the last MFMA group of tile kt-2, right after the barrier that
+// frees that tile's stage.
+template <bool AK, bool BKC, int OUT>
+__global__ __launch_bounds__(kThreads) void k_gemm_dma(const __bf16* __restrict__ A, int64_t lda,
+                                                       const __bf16* __restrict__ B, int64_t ldb, void* __restrict__ C,
+                                                       int64_t ldc, int M, int N, int K, int mblocks) {
+  constexpr bool BF16_OUT = OUT == 0;  // through LDS slices, from transposed accumulator blocks
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  int m0, n0;
+  tile_origin(mblocks, m0, n0);
+  const int wm = wave & 1, wn = wave >> 1;
+  DmaOperand<AK> da;
+  DmaOperand<BKC> db;
+  da.init(A, lda, M, m0, K, wave, lane);
+  db.init(B, ldb, N, n0, K, wave, lane);
+  const Operand<AK> oa{};  // fragment reads
+  const Operand<BKC> ob{};
+  const u32x4 none = desc16(A, 0);  // loads past the last k-tile: out of range, no memory traffic
+  const uint32_t lwave = (uint32_t)(uintptr_t)(lds_t*)smem + (uint32_t)wave * 8192u;
+  const int nk = (K + kBK - 1) / kBK;
+  // load q of k-tile kt (0-7: A's blocks, 8-15: B's) into stage kt % 2
+  auto issue = [&](int kt, int q) {
+    const uint32_t st = lwave + (uint32_t)(kt & 1) * kStage + (q >= 8 ? kTile : 0) + (q & 7) * 1024;
+    const bool live = kt < nk;
+    if (q < 8) lds_dma16(live ? da.d : none, st, da.vo[q], (uint32_t)kt * da.kstep);
+    else lds_dma16(live ? db.d : none, st, db.vo[q - 8], (uint32_t)kt * db.kstep);
+  };
+  f32x16 acc[4][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i + 1 < 4) ld_old(i + 1, old[(i + 1) & 1]);
-        to_lds(i);
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = q * 2 + (lane >> 5), c = (lane & 31) * 4;
-          f32x4 v = *reinterpret_cast<const f32x4*>(reg + r * kPad + c);
-          v += old[i & 1][q];
-          const int row = rbase + i * 32 + r, col = cbase + c;
-          if (row >= M) continue;
-          float* dst = Cf + (int64_t)row * ldc + col;
-          if (col + 4 <= N) {
-            *reinterpret_cast<f32x4*>(dst) = v;
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+  bf16x8 fa[2][4], fb[2][4];
+  // fragment read q of tile kt at k-step kk into set s, in the order the MFMAs use them: q 0 A block 0,
+  // 1-4 B blocks 0-3, 5-7 A blocks 1-3
+  auto read = [&](int kt, int kk, int s, int q) {
+    const unsigned char* as = smem + (kt & 1) * kStage;
+    if (q == 0) fa[s][0] = oa.frag(as, wm * 128, kk, lane);
+    else if (q <= 4) fb[s][q - 1] = ob.frag(as + kTile, wn * 128 + (q - 1) * 32, kk, lane);
+    else fa[s][q - 4] = oa.frag(as, wm * 128 + (q - 4) * 32, kk, lane);
+  };
+  auto mfma = [&](int s, int n) {
+    const int i = n >> 2, j = n & 3;
+    if (BF16_OUT)  // the transposed block: lane l gets row l%32 and columns 8q + 4(l/32) .. +3 in 4q .. 4q+3
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][j], fa[s][i], acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+  };
+#pragma unroll
+  for (int q = 0; q < 16; ++q) issue(0, q);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) issue(1, q);
+  GEMM_WAIT_VM(16);  // tile 0 has landed (this wave's part)
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) read(0, 0, 0, q);
+  for (int kt = 0; kt < nk; ++kt) {
+    // groups 0-2: k-steps 0-2, the next step's fragments read between the MFMAs
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        mfma(kk & 1, 2 * q);
+        mfma(kk & 1, 2 * q + 1);
+        read(kt, kk + 1, (kk + 1) & 1, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // every wave holds tile kt's last fragments and has tile kt+1's loads done; after the barrier tile kt's
+    // stage takes tile kt+2 and tile kt+1 is readable
+    GEMM_WAIT_VM(0);
+    GEMM_WAIT_LGKM(0);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      issue(kt + 2, 2 * q);
+      issue(kt + 2, 2 * q + 1);
+      mfma(1, 2 * q);
+      mfma(1, 2 * q + 1);
+      read(kt + 1, 0, 0, q);  // after the last tile: a stage's stale contents, never used
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  GEMM_WAIT_VM(0);
+  GEMM_WAIT_LGKM(0);
+  __syncthreads();
+  if constexpr (BF16_OUT) {
+    // per wave, 32 rows x 128 columns at a time through 8 KiB of LDS (8-byte unit u of row r at u ^ r),
+    // out as 16-byte row chunks (16 lanes a row, 4 rows an instruction)
+    unsigned char* slice = smem + wave * 8192;
+    __bf16* Cb = static_cast<__bf16*>(C);
+    const bool vec = ((uintptr_t)C & 15u) == 0 && (ldc & 7) == 0;
+    const int row0 = m0 + wm * 128, col0 = n0 + wn * 128;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x4 v = {(__bf16)acc[i][j][4 * q], (__bf16)acc[i][j][4 * q + 1], (__bf16)acc[i][j][4 * q + 2],
+                            (__bf16)acc[i][j][4 * q + 3]};
+          const int u = 8 * j + 2 * q + h;
+          *reinterpret_cast<bf16x4*>(slice + r * 256 + ((u ^ r) << 3)) = v;
+        }
+      // 16-byte chunk t of row rr holds units 2t and 2t+1, at chunk t ^ (rr/2), in swapped order for odd rr
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int rr = g * 4 + (lane >> 4), t = lane & 15;
+        u32x4 v = *reinterpret_cast<const u32x4*>(slice + rr * 256 + ((t ^ (rr >> 1)) << 4));
+        if (rr & 1) v = (u32x4){v[2], v[3], v[0], v[1]};
+        const int row = row0 + i * 32 + rr, col = col0 + t * 8;
+        if (row < M) {
+          __bf16* dst = Cb + (int64_t)row * ldc + col;
+          if (vec && col + 8 <= N) {
+            *reinterpret_cast<u32x4*>(dst) = v;
           } else {
+            const bf16x8 b = __builtin_bit_cast(bf16x8, v);
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-              if (col + k < N) dst[k] = v[k];
+            for (int e = 0; e < 8; ++e)
+              if (col + e < N) dst[e] = b[e];
           }
         }
       }
     }
-    return;
-  }
-  // element stores from the accumulator layout (and C += acc where C is not 16-byte aligned)
-  if constexpr (OUT == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          int row, col;
-          at(i, j, e, row, col);
-          if (row < M && col < N) static_cast<__bf16*>(C)[(int64_t)row * ldc + col] = (__bf16)acc[i][j][e];
-        }
   } else {
-    float* __restrict__ Cf = static_cast<float*>(C);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          int row, col;
-          at(i, j, e, row, col);
-          if (row < M && col < N) {
-            float* p = Cf + (int64_t)row * ldc + col;
-            *p = OUT == 2 ? *p + acc[i][j][e] : acc[i][j][e];
-          }
-        }
+    store_acc_f32<OUT>(acc, smem, C, ldc, M, N, m0, n0, wm, wn, wave, lane);
   }
 }
 
@@ -402,13 +586,33 @@ bool gemm_bf16_supported(const GemmBf16& g) {
   return tiles < lim;
 }
 
+// Shapes k_gemm_dma takes: K-contiguous operands need K % 64 == 0 (their rows are not masked on the way
+// in), and an M/N-contiguous operand's k-extent must fit a 31-bit byte range from its first column.
+static bool gemm_dma_ok(const GemmBf16& g) {
+  const int64_t lim = (int64_t)1 << 31;
+  auto mn_ok = [&](int64_t ld) { return ((int64_t)(g.K - 1) * ld + 256) * 2 < lim; };
+  return (g.a_kc ? g.K % kBK == 0 : mn_ok(g.lda)) && (g.b_kc ? g.K % kBK == 0 : mn_ok(g.ldb));
+}
+
 hipError_t launch_gemm_bf16(const GemmBf16& g, hipStream_t stream) {
   if (!gemm_bf16_supported(g)) return hipErrorInvalidValue;
   const int mblocks = (g.M + kBM - 1) / kBM, nblocks = (g.N + kBN - 1) / kBN;
   const dim3 grid((unsigned)(mblocks * nblocks)), block(kThreads);
-  const bool tail = g.K % (2 * kBK) != 0;  // the tile count is rounded up to even
   const __bf16* A = static_cast<const __bf16*>(g.A);
   const __bf16* B = static_cast<const __bf16*>(g.B);
+  if (gemm_dma_ok(g)) {
+#define CE_GEMM_DMA(AKv, BKv, O)                                                                                 \
+  hipLaunchKernelGGL((k_gemm_dma<AKv, BKv, O>), grid, block, 0, stream, A, g.lda, B, g.ldb, g.C, g.ldc, g.M, g.N, \
+                     g.K, mblocks)
+    if (g.a_kc && g.b_kc && g.out == 0) CE_GEMM_DMA(true, true, 0);
+    else if (g.a_kc && !g.b_kc && g.out == 0) CE_GEMM_DMA(true, false, 0);
+    else if (!g.a_kc && !g.b_kc && g.out == 1) CE_GEMM_DMA(false, false, 1);
+    else if (!g.a_kc && !g.b_kc && g.out == 2) CE_GEMM_DMA(false, false, 2);
+    else return hipErrorInvalidValue;
+#undef CE_GEMM_DMA
+    return hipGetLastError();
+  }
+  const bool tail = g.K % (2 * kBK) != 0;  // the tile count is rounded up to even
 #define CE_GEMM(AKv, BKv, O, T)                                                                                   \
   hipLaunchKernelGGL((k_gemm<AKv, BKv, O, T>), grid, block, 0, stream, A, g.lda, B, g.ldb, g.C, g.ldc, g.M, g.N, \
                      g.K, mblocks)
