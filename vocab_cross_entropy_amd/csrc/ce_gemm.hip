@@ -15,8 +15,8 @@
 //  * k_gemm_dma (the default): both operands go from memory straight into LDS (buffer_load ... lds, 1 KiB
 //    per wave instruction, whole 128-byte lines).  The one barrier per k-tile sits before its last group of
 //    MFMAs: by then every wave holds the tile's last fragments and the next tile has landed, so the stage
-//    just read takes the loads of the tile after next (issued alongside the last group) while the next
-//    tile's first fragments are read.  The loads are issued in asm: the compiler cannot tell the two stages
+//    just read takes the loads of the tile after next (spread over that last group and the next tile's
+//    first two groups) while the next tile's first fragments are read.  The loads are issued in asm: the compiler cannot tell the two stages
 //    of the LDS array apart and would otherwise wait for every load in flight before each LDS read.  BF16
 //    results leave through a per-wave LDS slice as 16-byte row chunks (the MFMA operands are swapped so
 //    that each lane holds 4 consecutive columns of one row).
@@ -433,8 +433,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
 }
 
 // Both operands straight into LDS (shapes: gemm_dma_ok).  Same tile, LDS layouts and fragment reads as
-// k_gemm; k-tile kt's loads are issued with the last MFMA group of tile kt-2, right after the barrier that
-// frees that tile's stage.
+// k_gemm; k-tile kt's loads start with the last MFMA group of tile kt-2, right after the barrier that frees
+// that tile's stage, and finish in the first two groups of tile kt-1.
 template <bool AK, bool BKC, int OUT>
 __global__ __launch_bounds__(kThreads) void k_gemm_dma(const __bf16* __restrict__ A, int64_t lda,
                                                        const __bf16* __restrict__ B, int64_t ldb, void* __restrict__ C,
@@ -455,7 +455,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dma(const __bf16* __restrict_
   const u32x4 none = desc16(A, 0);  // loads past the last k-tile: out of range, no memory traffic
   const uint32_t lwave = (uint32_t)(uintptr_t)(lds_t*)smem + (uint32_t)wave * 8192u;
   const int nk = (K + kBK - 1) / kBK;
-  // load q of k-tile kt (0-7: A's blocks, 8-15: B's) into stage kt % 2
+  // load q of k-tile kt (0-7: A's blocks, 8-15: B's) into stage kt % 2.  Tile kt+2's loads go out spread
+  // over three MFMA groups: A's 8 with tile kt's last group (right after the barrier that frees the stage),
+  // B's 8 with the first two groups of tile kt+1, 4 in each; bunched into one group they back up the
+  // memory pipeline and hold up the MFMAs queued behind them.
+  constexpr int kLast = 8, kG0 = 4, kG1 = 4;
+  static_assert(kLast <= 8 && kG0 <= 8 && kG1 <= 8 && kLast + kG0 + kG1 == 16, "one load per MFMA pair, 16 per tile");
   auto issue = [&](int kt, int q) {
     const uint32_t st = lwave + (uint32_t)(kt & 1) * kStage + (q >= 8 ? kTile : 0) + (q & 7) * 1024;
     const bool live = kt < nk;
@@ -492,11 +497,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dma(const __bf16* __restrict_
 #pragma unroll
   for (int q = 0; q < 8; ++q) read(0, 0, 0, q);
   for (int kt = 0; kt < nk; ++kt) {
-    // groups 0-2: k-steps 0-2, the next step's fragments read between the MFMAs
+    // groups 0-2: k-steps 0-2, the next step's fragments read between the MFMAs; groups 0 and 1 also issue
+    // the rest of tile kt+1's loads (tile 1 went out whole before the loop)
 #pragma unroll
     for (int kk = 0; kk < 3; ++kk) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
+        if (kk == 0 && q < kG0 && kt > 0) issue(kt + 1, kLast + q);
+        if (kk == 1 && q < kG1 && kt > 0) issue(kt + 1, kLast + kG0 + q);
         mfma(kk & 1, 2 * q);
         mfma(kk & 1, 2 * q + 1);
         read(kt, kk + 1, (kk + 1) & 1, q);
@@ -510,8 +518,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dma(const __bf16* __restrict_
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      issue(kt + 2, 2 * q);
-      issue(kt + 2, 2 * q + 1);
+      if (q < kLast) issue(kt + 2, q);
       mfma(1, 2 * q);
       mfma(1, 2 * q + 1);
       read(kt + 1, 0, 0, q);  // after the last tile: a stage's stale contents, never used
