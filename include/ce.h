@@ -355,8 +355,8 @@ ce_status ce_shard_combine_ex(const float* stats, int32_t S, int64_t d0, int64_t
  *                    calls, and FP32 heads, run on the GEMM library
  *   CE_GEMM_LIBRARY  hipBLASLt, ROCm's GEMM library, for every product
  *   CE_GEMM_AUTO     per product, the engine measured faster on gfx950 at the
- *                    head's shapes (currently the native kernel for dW and
- *                    the library for logits and dh)
+ *                    head's shapes (currently the native kernel for dh and
+ *                    dW, the library for the logits)
  * Both engines accumulate in FP32 and round the output once; their results
  * differ only in the summation order. */
 #define CE_GEMM_AUTO 0

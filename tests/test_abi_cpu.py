@@ -464,7 +464,7 @@ def test_device_build_contracts_within_expressions_only():
 
 def test_linear_gemm_plan(lib):
     """Which products run on the native MFMA kernel: every one for a BF16 head
-    with 16-byte rows under CE_GEMM_NATIVE, dW alone under CE_GEMM_AUTO; none
+    with 16-byte rows under CE_GEMM_NATIVE, dh and dW under CE_GEMM_AUTO; none
     under the library engine, for FP32 heads, or when D or a row stride is not
     a multiple of 8 or a base pointer not 16-byte aligned; -1 for an invalid
     descriptor."""
@@ -492,7 +492,7 @@ def test_linear_gemm_plan(lib):
     assert plan(D=0) == -1
     assert plan(h_ld=32) == -1
     assert lib.ce_linear_gemm_plan(None) == -1
-    # the automatic choice: the native kernel for dW only (bit 2), where it applies
-    assert plan(gemm=_abi.CE_GEMM_AUTO) == 4
+    # the automatic choice: the native kernel for dh and dW (bits 1 and 2), where it applies
+    assert plan(gemm=_abi.CE_GEMM_AUTO) == 6
     assert plan(gemm=_abi.CE_GEMM_AUTO, dtype=_abi.CE_F32) == 0
     assert plan(gemm=_abi.CE_GEMM_AUTO, h=hp + 2) == 0

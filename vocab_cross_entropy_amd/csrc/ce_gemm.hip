@@ -19,7 +19,9 @@
 //    first two groups) while the next tile's first fragments are read.  The loads are issued in asm: the compiler cannot tell the two stages
 //    of the LDS array apart and would otherwise wait for every load in flight before each LDS read.  BF16
 //    results leave through a per-wave LDS slice as 16-byte row chunks (the MFMA operands are swapped so
-//    that each lane holds 4 consecutive columns of one row).
+//    that each lane holds 4 consecutive columns of one row).  The BF16 products (an even k-tile count) run
+//    it in persistent form, k_gemm_dmap: one workgroup per CU walking its tiles, the load stream running
+//    on across tile boundaries.
 //  * k_gemm (shapes the first does not take: a K-contiguous operand whose K is not a multiple of 64, which
 //    must be masked on its way into LDS, or an M/N-contiguous operand whose k-extent exceeds a 31-bit byte
 //    range): every thread stages 8 chunks of 16 bytes of each operand per k-tile through registers, in two
@@ -573,6 +575,183 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dma(const __bf16* __restrict_
   }
 }
 
+// Persistent form of k_gemm_dma for BF16 outputs (an even k-tile count of at least 2): one workgroup per CU
+// walks its tiles in the order of tile_origin, the load stream runs on across tile boundaries (the next
+// tile's first k-tiles load during this tile's last two), and results leave through an LDS slice of their
+// own (160 KiB in all), so the next tile's loads are not held up by the epilogue.
+template <bool AK, bool BKC>
+__global__ __launch_bounds__(kThreads) void k_gemm_dmap(const __bf16* __restrict__ A, int64_t lda,
+                                                        const __bf16* __restrict__ B, int64_t ldb, __bf16* __restrict__ C,
+                                                        int64_t ldc, int M, int N, int K, int mblocks, int ntiles) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage + 4 * 8192];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  // tiles: with a multiple of 8 workgroups, XCD x = block % 8 owns the contiguous run [x per, (x+1) per) of
+  // the tile order and its G/8 workgroups take those tiles in turn; otherwise workgroup b takes b, b+G, ...
+  const int G = gridDim.x;
+  const bool xcd = (G & 7) == 0;
+  const int per = (ntiles + 7) / 8;
+  const int t_lo = xcd ? (int)(blockIdx.x & 7) * per : 0;
+  const int t_hi = xcd ? (t_lo + per < ntiles ? t_lo + per : ntiles) : ntiles;
+  const int first = xcd ? (int)(blockIdx.x >> 3) : (int)blockIdx.x, gstep = xcd ? G / 8 : G;
+  const int mine = t_hi - t_lo > first ? (t_hi - t_lo - first + gstep - 1) / gstep : 0;
+  if (mine == 0) return;
+  const int nblocks = ntiles / mblocks;
+  auto origin = [&](int i, int& m0, int& n0) {  // the i-th tile of this workgroup, in the order of tile_origin
+    const int L = t_lo + first + i * gstep;
+    constexpr int kGroup = 4;
+    const int grp = L / (kGroup * mblocks), f = grp * kGroup;
+    const int gsz = nblocks - f < kGroup ? nblocks - f : kGroup;
+    n0 = (f + (L - grp * kGroup * mblocks) % gsz) * kBN;
+    m0 = ((L - grp * kGroup * mblocks) / gsz) * kBM;
+  };
+  DmaOperand<AK> da;  // vo and kstep do not depend on the tile; d is set per tile below
+  DmaOperand<BKC> db;
+  da.init(A, lda, M, 0, K, wave, lane);
+  db.init(B, ldb, N, 0, K, wave, lane);
+  const u32x4 none = desc16(A, 0);
+  auto descs = [&](int i, u32x4& a, u32x4& b) {
+    if (i >= mine) {
+      a = none, b = none;
+      return;
+    }
+    int m0, n0;
+    origin(i, m0, n0);
+    DmaOperand<AK> ta;
+    DmaOperand<BKC> tb;
+    ta.init(A, lda, M, m0, K, wave, lane);
+    tb.init(B, ldb, N, n0, K, wave, lane);
+    a = ta.d, b = tb.d;
+  };
+  const Operand<AK> oa{};
+  const Operand<BKC> ob{};
+  const uint32_t lwave = (uint32_t)(uintptr_t)(lds_t*)smem + (uint32_t)wave * 8192u;
+  const int nk = (K + kBK - 1) / kBK;
+  u32x4 ca, cb, na, nb;  // this tile's and the next tile's buffers
+  descs(0, ca, cb);
+  descs(1, na, nb);
+  // load q of k-tile k (stage k % 2; nk is even, so every tile starts in stage 0) from buffers (a, b)
+  auto issue = [&](const u32x4& a, const u32x4& b, int k, int q) {
+    const uint32_t st = lwave + (uint32_t)(k & 1) * kStage + (q >= 8 ? kTile : 0) + (q & 7) * 1024;
+    if (q < 8) lds_dma16(a, st, da.vo[q], (uint32_t)k * da.kstep);
+    else lds_dma16(b, st, db.vo[q - 8], (uint32_t)k * db.kstep);
+  };
+  constexpr int kLast = 8, kG0 = 4, kG1 = 4;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+  bf16x8 fa[2][4], fb[2][4];
+  auto read = [&](int k, int kk, int s, int q) {
+    const unsigned char* as = smem + (k & 1) * kStage;
+    if (q == 0) fa[s][0] = oa.frag(as, wm * 128, kk, lane);
+    else if (q <= 4) fb[s][q - 1] = ob.frag(as + kTile, wn * 128 + (q - 1) * 32, kk, lane);
+    else fa[s][q - 4] = oa.frag(as, wm * 128 + (q - 4) * 32, kk, lane);
+  };
+  auto mfma = [&](int s, int n) {
+    const int i = n >> 2, j = n & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][j], fa[s][i], acc[i][j], 0, 0, 0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  // k-tile kt of this tile; WHERE: 0 kt+1 and kt+2 in this tile, 1 kt+2 is the next tile's k-tile 0,
+  // 2 (the last) kt+1 and kt+2 are the next tile's 0 and 1, and the next fragments are read after the
+  // epilogue
+  auto step = [&](int kt, auto where) {
+    constexpr int W = decltype(where)::value;
+    const u32x4& a1 = W == 2 ? na : ca;
+    const u32x4& b1 = W == 2 ? nb : cb;
+    const int k1 = W == 2 ? 0 : kt + 1;
+    const u32x4& a2 = W >= 1 ? na : ca;
+    const u32x4& b2 = W >= 1 ? nb : cb;
+    const int k2 = W == 2 ? 1 : (W == 1 ? 0 : kt + 2);
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (kk == 0 && q < kG0) issue(a1, b1, k1, kLast + q);
+        if (kk == 1 && q < kG1) issue(a1, b1, k1, kLast + kG0 + q);
+        mfma(kk & 1, 2 * q);
+        mfma(kk & 1, 2 * q + 1);
+        read(kt, kk + 1, (kk + 1) & 1, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    GEMM_WAIT_VM(0);
+    GEMM_WAIT_LGKM(0);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q < kLast) issue(a2, b2, k2, q);
+      mfma(1, 2 * q);
+      mfma(1, 2 * q + 1);
+      if (W != 2) read(kt + 1, 0, 0, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // k-tile 0 whole and k-tile 1's A loads; its B loads go out in k-tile 0's first groups like any other
+#pragma unroll
+  for (int q = 0; q < 16; ++q) issue(ca, cb, 0, q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) issue(ca, cb, 1, q);
+  GEMM_WAIT_VM(8);
+  __syncthreads();
+  unsigned char* slice = smem + 2 * kStage + wave * 8192;
+  const bool vec = ((uintptr_t)C & 15u) == 0 && (ldc & 7) == 0;
+  for (int ti = 0; ti < mine; ++ti) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) read(0, 0, 0, q);
+    for (int kt = 0; kt + 2 < nk; ++kt) step(kt, I0{});
+    step(nk - 2, I1{});
+    step(nk - 1, I2{});
+    // the tile out through this wave's slice (32 rows x 128 columns at a time), as 16-byte row chunks
+    int m0, n0;
+    origin(ti, m0, n0);
+    const int row0 = m0 + wm * 128, col0 = n0 + wn * 128;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x4 v = {(__bf16)acc[i][j][4 * q], (__bf16)acc[i][j][4 * q + 1], (__bf16)acc[i][j][4 * q + 2],
+                            (__bf16)acc[i][j][4 * q + 3]};
+          const int u = 8 * j + 2 * q + h;
+          *reinterpret_cast<bf16x4*>(slice + r * 256 + ((u ^ r) << 3)) = v;
+        }
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int rr = g * 4 + (lane >> 4), t = lane & 15;
+        u32x4 v = *reinterpret_cast<const u32x4*>(slice + rr * 256 + ((t ^ (rr >> 1)) << 4));
+        if (rr & 1) v = (u32x4){v[2], v[3], v[0], v[1]};
+        const int row = row0 + i * 32 + rr, col = col0 + t * 8;
+        if (row < M) {
+          __bf16* dst = C + (int64_t)row * ldc + col;
+          if (vec && col + 8 <= N) {
+            *reinterpret_cast<u32x4*>(dst) = v;
+          } else {
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (col + e < N) dst[e] = bv[e];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+    ca = na, cb = nb;
+    descs(ti + 2, na, nb);
+  }
+  GEMM_WAIT_VM(0);
+}
 }  // namespace
 
 namespace vce {
@@ -595,6 +774,17 @@ bool gemm_bf16_supported(const GemmBf16& g) {
 
 // Shapes k_gemm_dma takes: K-contiguous operands need K % 64 == 0 (their rows are not masked on the way
 // in), and an M/N-contiguous operand's k-extent must fit a 31-bit byte range from its first column.
+// Compute units of the current device (cached per device; 256 on an MI355X).
+static int cu_count() {
+  static int cached[64];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if ((n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED)) > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
+  return n;
+}
+
 static bool gemm_dma_ok(const GemmBf16& g) {
   const int64_t lim = (int64_t)1 << 31;
   auto mn_ok = [&](int64_t ld) { return ((int64_t)(g.K - 1) * ld + 256) * 2 < lim; };
@@ -607,6 +797,22 @@ hipError_t launch_gemm_bf16(const GemmBf16& g, hipStream_t stream) {
   const dim3 grid((unsigned)(mblocks * nblocks)), block(kThreads);
   const __bf16* A = static_cast<const __bf16*>(g.A);
   const __bf16* B = static_cast<const __bf16*>(g.B);
+  const int nk = (g.K + kBK - 1) / kBK;
+  if (gemm_dma_ok(g) && g.out == 0 && nk % 2 == 0) {
+    // persistent: one workgroup per CU (at most one per tile)
+    const int tiles = mblocks * nblocks, cus = cu_count();
+    const dim3 pgrid((unsigned)(tiles < cus ? tiles : cus));
+    __bf16* Cb = static_cast<__bf16*>(g.C);
+    if (g.a_kc && g.b_kc)
+      hipLaunchKernelGGL((k_gemm_dmap<true, true>), pgrid, block, 0, stream, A, g.lda, B, g.ldb, Cb, g.ldc, g.M, g.N,
+                         g.K, mblocks, tiles);
+    else if (g.a_kc && !g.b_kc)
+      hipLaunchKernelGGL((k_gemm_dmap<true, false>), pgrid, block, 0, stream, A, g.lda, B, g.ldb, Cb, g.ldc, g.M, g.N,
+                         g.K, mblocks, tiles);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (gemm_dma_ok(g)) {
 #define CE_GEMM_DMA(AKv, BKv, O)                                                                                 \
   hipLaunchKernelGGL((k_gemm_dma<AKv, BKv, O>), grid, block, 0, stream, A, g.lda, B, g.ldb, g.C, g.ldc, g.M, g.N, \

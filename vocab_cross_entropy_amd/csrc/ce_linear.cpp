@@ -307,11 +307,11 @@ ce_status chunk_plan_ok(const ce_linear* lin, const ce_params* p, int64_t rows) 
 // h_ld, w_ld and D multiples of 8), CE_GEMM_LIBRARY on hipBLASLt; CE_GEMM_AUTO
 // takes, per product, the engine measured faster on gfx950 at the head's
 // shapes (kAutoNative): at 8192 x 4096 x 128000 in chunks of 4096 rows the
-// native dW product takes 3.82 / 4.04 ms (written / added) against the
-// library's 4.25 / 4.46, while its logits and dh products take 3.41 ms
-// against the library's 2.90 and 3.16.
+// native products take 3.07 ms for dh and 3.45 / 3.67 ms for dW (written /
+// added) against the library's 3.11 and 4.21 / 4.45, and 3.22 ms for the
+// logits against the library's 2.87.
 enum Product { kLogits = 0, kDh = 1, kDw = 2 };
-constexpr bool kAutoNative[3] = {false, false, true};
+constexpr bool kAutoNative[3] = {false, true, true};
 
 bool native_layout_ok(const ce_linear* lin) {
   return lin->dtype == CE_BF16 && lin->h_ld % 8 == 0 && lin->w_ld % 8 == 0 && lin->D % 8 == 0 &&
