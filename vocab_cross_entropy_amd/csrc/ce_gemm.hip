@@ -200,18 +200,21 @@ struct DmaOperand {
   }
 };
 
-// The workgroup's output tile.  The 8 XCDs take blocks round-robin (block id mod 8); each gets a contiguous
-// run of tiles, which it walks in groups of 4 n-blocks, n fastest, so that the tiles resident on one XCD
-// share operand slabs in its L2.
-__device__ __forceinline__ void tile_origin(int mblocks, int& m0, int& n0) {
+// Tile L of the tile order: groups of 4 n-blocks, n fastest within a group, so that consecutive tiles
+// share operand slabs.
+__device__ __forceinline__ void tile_at(int L, int mblocks, int nblocks, int& m0, int& n0) {
   constexpr int kGroup = 4;
-  const int T = gridDim.x, per = (T + 7) / 8;
-  const int L = (T & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * per + (blockIdx.x >> 3));
-  const int nblocks = T / mblocks;
   const int grp = L / (kGroup * mblocks), first = grp * kGroup;
   const int gsz = nblocks - first < kGroup ? nblocks - first : kGroup;
   n0 = (first + (L - grp * kGroup * mblocks) % gsz) * kBN;
   m0 = ((L - grp * kGroup * mblocks) / gsz) * kBM;
+}
+// The workgroup's output tile.  The 8 XCDs take blocks round-robin (block id mod 8); each gets a contiguous
+// run of the tile order, so that the tiles resident on one XCD share operand slabs in its L2.
+__device__ __forceinline__ void tile_origin(int mblocks, int& m0, int& n0) {
+  const int T = gridDim.x, per = (T + 7) / 8;
+  const int L = (T & 7) ? (int)blockIdx.x : (int)((blockIdx.x & 7) * per + (blockIdx.x >> 3));
+  tile_at(L, mblocks, T / mblocks, m0, n0);
 }
 
 // FP32 results (OUT 1: written, 2: added) from the accumulator layout: lane l holds rows
@@ -598,14 +601,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dmap(const __bf16* __restrict
   const int mine = t_hi - t_lo > first ? (t_hi - t_lo - first + gstep - 1) / gstep : 0;
   if (mine == 0) return;
   const int nblocks = ntiles / mblocks;
-  auto origin = [&](int i, int& m0, int& n0) {  // the i-th tile of this workgroup, in the order of tile_origin
-    const int L = t_lo + first + i * gstep;
-    constexpr int kGroup = 4;
-    const int grp = L / (kGroup * mblocks), f = grp * kGroup;
-    const int gsz = nblocks - f < kGroup ? nblocks - f : kGroup;
-    n0 = (f + (L - grp * kGroup * mblocks) % gsz) * kBN;
-    m0 = ((L - grp * kGroup * mblocks) / gsz) * kBM;
-  };
+  auto origin = [&](int i, int& m0, int& n0) { tile_at(t_lo + first + i * gstep, mblocks, nblocks, m0, n0); };
   DmaOperand<AK> da;  // vo and kstep do not depend on the tile; d is set per tile below
   DmaOperand<BKC> db;
   da.init(A, lda, M, 0, K, wave, lane);
