@@ -205,6 +205,14 @@ def test_linear_tile_edges(gemm):
         check_linear(h, w, t, 0.1, "mean", chunk_rows=chunk, what=f"tile edges N={N} D={D} V={V}", gemm=gemm)
 
 
+def test_linear_many_tiles():
+    """More logits tiles than compute units, in a count that is not a multiple of 8: 3 x 157 = 471 tiles of
+    256 x 256 over 2 k-tiles, which the native kernel's persistent form deals to the 8 XCDs in runs of 59
+    and 58 tiles, each workgroup taking one or two; the dW product over 12 k-tiles and 157 row blocks."""
+    h, w, t = grid_inputs(768, 128, 40001, torch.bfloat16, seed=71)
+    check_linear(h, w, t, 0.1, "mean", chunk_rows=768, what="many tiles", gemm="native")
+
+
 def test_linear_no_rows():
     h = torch.empty((0, 32), dtype=torch.bfloat16, device="cuda")
     w = torch.ones((100, 32), dtype=torch.bfloat16, device="cuda")
