@@ -213,6 +213,14 @@ def test_linear_many_tiles():
     check_linear(h, w, t, 0.1, "mean", chunk_rows=768, what="many tiles", gemm="native")
 
 
+def test_linear_split_dh():
+    """dh of chunks with fewer output tiles than half the compute units: the native kernel splits the
+    vocabulary (K = 8192, 128 k-tiles) over FP32 partial planes in the head's GEMM scratch (2 tiles of 256 x
+    256 per chunk of 256 rows, so 128 splits of one k-tile) and sums them in a fixed order."""
+    h, w, t = grid_inputs(512, 512, 8192, torch.bfloat16, seed=73)
+    check_linear(h, w, t, 0.1, "sum", chunk_rows=256, what="split dh", gemm="native")
+
+
 def test_linear_no_rows():
     h = torch.empty((0, 32), dtype=torch.bfloat16, device="cuda")
     w = torch.ones((100, 32), dtype=torch.bfloat16, device="cuda")

@@ -440,11 +440,21 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const __bf16* __restrict__ A,
 // Both operands straight into LDS (shapes: gemm_dma_ok).  Same tile, LDS layouts and fragment reads as
 // k_gemm; k-tile kt's loads start with the last MFMA group of tile kt-2, right after the barrier that frees
 // that tile's stage, and finish in the first two groups of tile kt-1.
+// ksplit > 0: split K (gridDim.y splits): split y takes k-tiles [y ksplit, (y+1) ksplit) of K and writes its
+// FP32 partial product to plane y of C (cplane elements apart).
 template <bool AK, bool BKC, int OUT>
 __global__ __launch_bounds__(kThreads) void k_gemm_dma(const __bf16* __restrict__ A, int64_t lda,
                                                        const __bf16* __restrict__ B, int64_t ldb, void* __restrict__ C,
-                                                       int64_t ldc, int M, int N, int K, int mblocks) {
+                                                       int64_t ldc, int M, int N, int K, int mblocks, int ksplit,
+                                                       int64_t cplane) {
   constexpr bool BF16_OUT = OUT == 0;  // through LDS slices, from transposed accumulator blocks
+  if (ksplit > 0) {
+    const int k0 = (int)blockIdx.y * ksplit;
+    A += AK ? (int64_t)k0 : (int64_t)k0 * lda;
+    B += BKC ? (int64_t)k0 : (int64_t)k0 * ldb;
+    K = K - k0 < ksplit ? K - k0 : ksplit;
+    C = static_cast<float*>(C) + (int64_t)blockIdx.y * cplane;
+  }
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -575,6 +585,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dma(const __bf16* __restrict_
     }
   } else {
     store_acc_f32<OUT>(acc, smem, C, ldc, M, N, m0, n0, wm, wn, wave, lane);
+  }
+}
+
+// The S FP32 partial planes of a split product ([M][N] each, N a multiple of 4), summed in plane order and
+// rounded once to BF16 (out row stride ldo).
+__global__ __launch_bounds__(256) void k_sum_planes(const float* __restrict__ part, int S, int64_t plane, int M,
+                                                     int N, __bf16* __restrict__ out, int64_t ldo) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x, nq = (int64_t)M * (N / 4);
+  if (q >= nq) return;
+  const int64_t r = q / (N / 4), c = (q - r * (N / 4)) * 4;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + r * N + c);
+  for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(part + (int64_t)s * plane + r * N + c);
+  const bf16x4 v = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+  __bf16* dst = out + r * ldo + c;
+  if (((uintptr_t)dst & 7u) == 0) {
+    *reinterpret_cast<bf16x4*>(dst) = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = v[e];
   }
 }
 
@@ -794,6 +825,29 @@ hipError_t launch_gemm_bf16(const GemmBf16& g, hipStream_t stream) {
   const __bf16* A = static_cast<const __bf16*>(g.A);
   const __bf16* B = static_cast<const __bf16*>(g.B);
   const int nk = (g.K + kBK - 1) / kBK;
+  // dh with few output tiles (a short chunk): the K range split so that the tiles times the splits fill the
+  // compute units, each split's FP32 partial in a plane of the scratch, then the planes summed
+  if (g.out == 0 && g.a_kc && !g.b_kc && g.scratch && ((uintptr_t)g.scratch & 15u) == 0 && g.N % 4 == 0 &&
+      gemm_dma_ok(g)) {
+    const int tiles = mblocks * nblocks, cus = cu_count();
+    const int64_t plane = (int64_t)g.M * g.N;
+    int64_t S = (cus + tiles - 1) / tiles;
+    if (S > nk) S = nk;
+    if (S > (int64_t)(g.scratch_bytes / ((size_t)plane * 4))) S = (int64_t)(g.scratch_bytes / ((size_t)plane * 4));
+    if (tiles * 2 <= cus && S >= 2) {
+      const int per_split = (int)((nk + S - 1) / S);  // k-tiles a split
+      const int splits = (nk + per_split - 1) / per_split;
+      float* part = static_cast<float*>(g.scratch);
+      hipLaunchKernelGGL((k_gemm_dma<true, false, 1>), dim3((unsigned)tiles, (unsigned)splits), block, 0, stream, A,
+                         g.lda, B, g.ldb, (void*)part, (int64_t)g.N, g.M, g.N, g.K, mblocks, per_split * kBK, plane);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t nq = plane / 4;
+      hipLaunchKernelGGL(k_sum_planes, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, stream, part, splits, plane,
+                         g.M, g.N, static_cast<__bf16*>(g.C), g.ldc);
+      return hipGetLastError();
+    }
+  }
   if (gemm_dma_ok(g) && g.out == 0 && nk % 2 == 0) {
     // persistent: one workgroup per CU (at most one per tile)
     const int tiles = mblocks * nblocks, cus = cu_count();
@@ -812,7 +866,7 @@ hipError_t launch_gemm_bf16(const GemmBf16& g, hipStream_t stream) {
   if (gemm_dma_ok(g)) {
 #define CE_GEMM_DMA(AKv, BKv, O)                                                                                 \
   hipLaunchKernelGGL((k_gemm_dma<AKv, BKv, O>), grid, block, 0, stream, A, g.lda, B, g.ldb, g.C, g.ldc, g.M, g.N, \
-                     g.K, mblocks)
+                     g.K, mblocks, 0, (int64_t)0)
     if (g.a_kc && g.b_kc && g.out == 0) CE_GEMM_DMA(true, true, 0);
     else if (g.a_kc && !g.b_kc && g.out == 0) CE_GEMM_DMA(true, false, 0);
     else if (!g.a_kc && !g.b_kc && g.out == 1) CE_GEMM_DMA(false, false, 1);

@@ -196,6 +196,10 @@ struct GemmBf16 {
   int64_t ldc;
   int out;
   int M, N, K;
+  // optional device scratch (16-byte aligned): a BF16 product whose output tiles would leave most compute
+  // units idle splits its K range over FP32 partial planes here, summed in a fixed order afterwards
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
 };
 // Whether launch_gemm_bf16 takes g: M, N, K >= 1; lda and ldb multiples of 8 and at least the contiguous
 // extent; A and B 16-byte aligned (so no 16-byte chunk straddles a row's end); one of the head's layouts.

@@ -485,7 +485,9 @@ ce_status ce_linear_cross_entropy(const ce_linear* lin, const int64_t* targets, 
     if (dh) {
       char* dhc = static_cast<char*>(dh) + (size_t)r0 * (size_t)dh_ld * eb;
       Gemm g2{ab, ab, D, n, V, HIPBLAS_OP_N, HIPBLAS_OP_N, lin->w, lin->w_ld, logits, ldl, dhc, dh_ld, 0.f};
-      const vce::GemmBf16 n2{logits, ldl, true, lin->w, lin->w_ld, false, dhc, dh_ld, 0, (int)n, (int)D, (int)V};
+      vce::GemmBf16 n2{logits, ldl, true, lin->w, lin->w_ld, false, dhc, dh_ld, 0, (int)n, (int)D, (int)V};
+      n2.scratch = wsb + w.blas;  // for a split K range when the chunk has few output tiles
+      n2.scratch_bytes = kBlasWorkspace;
       if ((st = run_product(dev, lin, kDh, n2, g2, wsb + w.blas, stream))) return st;
     }
     // dW (+)= G_c^T h_c
