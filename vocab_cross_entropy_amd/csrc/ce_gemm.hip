@@ -21,7 +21,8 @@
 //    results leave through a per-wave LDS slice as 16-byte row chunks (the MFMA operands are swapped so
 //    that each lane holds 4 consecutive columns of one row).  The BF16 products (an even k-tile count) run
 //    it in persistent form, k_gemm_dmap: one workgroup per CU walking its tiles, the load stream running
-//    on across tile boundaries.
+//    on across tile boundaries.  A dh product whose output tiles fill at most half the CUs splits its K
+//    range instead (FP32 partial planes in a caller's scratch, summed in plane order by k_sum_planes).
 //  * k_gemm (shapes the first does not take: a K-contiguous operand whose K is not a multiple of 64, which
 //    must be masked on its way into LDS, or an M/N-contiguous operand whose k-extent exceeds a 31-bit byte
 //    range): every thread stages 8 chunks of 16 bytes of each operand per k-tile through registers, in two
