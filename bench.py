@@ -464,6 +464,24 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     inplace_gbps = 2 * flat.numel() * flat.element_size() / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+    # the library's reference pass over the same bytes (ce_stream_reference: a plain one-pass kernel with
+    # the fused kernel's own 16-byte non-temporal buffer loads and stores), in place and as a copy
+    def ref_rate(dst):
+        for _ in range(3):
+            vce.ce_stream_reference(flat, dst)
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record()
+        for _ in range(10):
+            vce.ce_stream_reference(flat, dst)
+        r1.record()
+        torch.cuda.synchronize()
+        return 2 * flat.numel() * flat.element_size() / (r0.elapsed_time(r1) / 10 * 1e-3) / 1e9
+    stream_inplace_gbps = stream_copy_gbps = None
+    if (flat.numel() * flat.element_size()) % 16 == 0:
+        stream_inplace_gbps = ref_rate(None)
+        dst = torch.empty_like(flat)
+        stream_copy_gbps = ref_rate(dst)
+        del dst
 
     # each call's main kernel: its average duration over the event pass and
     # the algorithmic bytes one launch moves (read + written, formula N*V*b
@@ -529,6 +547,9 @@ def main():
         "formula_bytes_per_step": formula_bytes,
         "copy_ref_GBps": round(copy_gbps, 1),
         "inplace_ref_GBps": round(inplace_gbps, 1),
+        "stream_ref_GBps": None if stream_inplace_gbps is None else {
+            "in_place": round(stream_inplace_gbps, 1), "copy": round(stream_copy_gbps, 1),
+            "frac_of_in_place": round(value / stream_inplace_gbps, 4)},
         "roofline": roofline,
         "kernels": kernel_summary,
         "cold_steps": {"median_us": round(1e3 * cold[len(cold) // 2], 2), "min_us": round(1e3 * cold[0], 2),

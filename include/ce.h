@@ -77,8 +77,9 @@ extern "C" {
  *    ce_backward_inplace_ex); a shard's statistic d leaves out the target
  * 5: ce_fwd_bwd_fused_noalloc
  * 6: ce_linear.gemm (was reserved): the chunked head's GEMM engine; the head's
- *    logits stride in the workspace rounded up to a multiple of 8 */
-#define CE_ABI_VERSION 6
+ *    logits stride in the workspace rounded up to a multiple of 8
+ * 7: ce_stream_reference */
+#define CE_ABI_VERSION 7
 
 typedef enum ce_status {
   CE_OK = 0,
@@ -425,10 +426,26 @@ ce_status ce_linear_tune(const ce_linear* lin, const ce_params* p, void* dh, int
 ce_status ce_workspace_check(void* ws, hipStream_t stream);
 
 /*
+ * Reference streaming pass for benchmarks (not a step of the method): a
+ * plain one-pass kernel moving the bytes a fused call moves, whose rate is
+ * reported beside that call's.  `bytes` (a multiple of 16; 0 does nothing) of device
+ * memory are read once and written once with the same 16-byte non-temporal
+ * buffer loads and stores as the fused kernel streams logits with, in
+ * 64 KiB workgroup spans.  src == dst: every 32-bit word is XORed with
+ * 0x80008000 in place (the sign of each BF16 half flips, so two passes restore
+ * the buffer); otherwise src is copied to dst, which must not overlap it.  Both
+ * 16-byte aligned.  Asynchronous on `stream`; ce_profile_start times it like
+ * the calls listed there.  CE_EINVAL for a bad size, NULL, misaligned or
+ * partly overlapping buffers, before any launch.
+ */
+ce_status ce_stream_reference(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
+/*
  * Kernel timing for benchmarks.  After ce_profile_start(capacity), each of
- * the next `capacity` calls of ce_forward, ce_backward_inplace,
- * ce_fwd_bwd_fused or ce_shard_partial_stats records a pair of HIP events on
- * its stream around its main (bandwidth-dominant) kernel.
+ * the next `capacity` calls of ce_forward(_ex), ce_backward_inplace(_ex),
+ * ce_fwd_bwd_fused(_noalloc), ce_shards_fwd_bwd_fused, ce_shard_partial_stats,
+ * ce_scale_grad_inplace or ce_stream_reference that launch work records a pair
+ * of HIP events on its stream around its main (bandwidth-dominant) kernel.
  * ce_profile_stop(ms, cap, count) waits for those events, writes up to `cap`
  * durations in milliseconds to host array `ms`, the number recorded to
  * *count, and releases the events.  Not thread-safe; adds no synchronisation

@@ -279,6 +279,24 @@ def test_scale_grad_validates(lib):
     assert h.untouched()
 
 
+def test_stream_reference_validates(lib):
+    # rejected before any HIP call (the pointers are never dereferenced on the host): a size that is
+    # not a multiple of 16, NULL, misaligned and partly overlapping buffers; no bytes is a no-op
+    a, b = 0x100000, 0x200000
+    vp = ctypes.c_void_p
+    assert lib.ce_stream_reference(vp(a), vp(b), 0, None) == _abi.CE_OK
+    assert lib.ce_stream_reference(None, None, 0, None) == _abi.CE_OK
+    assert lib.ce_stream_reference(vp(a), vp(b), 24, None) == _abi.CE_EINVAL
+    assert lib.ce_stream_reference(vp(a), vp(b), -16, None) == _abi.CE_EINVAL
+    assert lib.ce_stream_reference(None, vp(b), 32, None) == _abi.CE_EINVAL
+    assert lib.ce_stream_reference(vp(a), None, 32, None) == _abi.CE_EINVAL
+    assert lib.ce_stream_reference(vp(a + 8), vp(b), 32, None) == _abi.CE_EINVAL
+    assert lib.ce_stream_reference(vp(a), vp(b + 4), 32, None) == _abi.CE_EINVAL
+    assert lib.ce_stream_reference(vp(a), vp(a + 16), 32, None) == _abi.CE_EINVAL
+    assert lib.ce_stream_reference(vp(a + 16), vp(a), 32, None) == _abi.CE_EINVAL
+    assert b"overlap" in lib.ce_last_error()
+
+
 def _linear_host(N=16, D=8, V=32):
     h = np.zeros((N, D), np.uint16)
     w = np.zeros((V, D), np.uint16)

@@ -37,6 +37,7 @@ __all__ = [
     "ce_shard_combine", "ce_shards_fwd_bwd_fused", "ce_shards_workspace_bytes",
     "ce_workspace_bytes", "ce_combine_workspace_bytes", "ce_workspace_init", "ce_workspace_check",
     "ce_linear_workspace_bytes", "ce_linear_cross_entropy", "ce_linear_tune", "ce_linear_gemm_plan",
+    "ce_stream_reference",
     "parallel_cross_entropy", "linear_cross_entropy",
     "Profiler", "CeError", "CeArgumentError", "lib", "ShardedCrossEntropy", "sharded_cross_entropy",
 ]
@@ -392,6 +393,24 @@ def ce_scale_grad_inplace(x, grad_out: torch.Tensor, per_row: bool):
     _need(dev, "grad_out", g, torch.float32, x.shape[0] * x.shape[1] if per_row else 1)
     _check(lib.ce_scale_grad_inplace(ctypes.byref(logits_desc(x)), _ptr(g), int(bool(per_row)), _stream(dev)))
     return x
+
+
+def ce_stream_reference(src: torch.Tensor, dst: torch.Tensor | None = None):
+    """The library's reference streaming pass over ``src``'s bytes (a benchmark
+    aid): with ``dst`` None every 32-bit word is XORed with 0x80008000 in
+    place, else ``src`` is copied into ``dst`` (same byte count, no overlap).
+    Contiguous tensors on one GPU, a multiple of 16 bytes, 16-byte aligned."""
+    dev = _device_of(src, "src")
+    if not src.is_contiguous():
+        raise CeArgumentError(_abi.CE_EINVAL, "src must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if dst is not None:
+        if _device_of(dst, "dst") != dev or not dst.is_contiguous():
+            raise CeArgumentError(_abi.CE_EINVAL, "dst must be contiguous on src's device")
+        if dst.numel() * dst.element_size() != nbytes:
+            raise CeArgumentError(_abi.CE_EINVAL, "dst must hold as many bytes as src")
+    _check(lib.ce_stream_reference(_ptr(src), _ptr(src if dst is None else dst), nbytes, _stream(dev)))
+    return src if dst is None else dst
 
 
 def ce_shard_partial_stats(shard, t, vocab_start, vocab_total, ignore_idx=-100, *, stats=None):

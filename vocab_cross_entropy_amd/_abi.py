@@ -19,7 +19,7 @@ CE_F32, CE_BF16 = 0, 1
 CE_REDUCE_NONE, CE_REDUCE_MEAN, CE_REDUCE_SUM = 0, 1, 2
 CE_SMOOTH_ALL, CE_SMOOTH_OTHERS = 0, 1
 CE_GEMM_AUTO, CE_GEMM_NATIVE, CE_GEMM_LIBRARY = 0, 1, 2
-CE_ABI_VERSION = 6
+CE_ABI_VERSION = 7
 
 
 class CeLogits(ctypes.Structure):
@@ -85,6 +85,7 @@ SIGNATURES = {
     "ce_shards_fwd_bwd_fused": (ctypes.c_int, [_P(CeLogits), ctypes.c_int32, _P(CeTargets), _P(CeParams), _vp, _vp,
                                                _vp, _vp, ctypes.c_size_t, _vp]),
     "ce_scale_grad_inplace": (ctypes.c_int, [_P(CeLogits), _vp, ctypes.c_int32, _vp]),
+    "ce_stream_reference": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp]),
     "ce_shard_partial_stats": (ctypes.c_int, [_P(CeLogits), _P(CeTargets), _P(CeParams), _vp, _vp]),
     "ce_shard_combine": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                         _P(CeTargets), _P(CeParams), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),

@@ -60,9 +60,11 @@ def build(verbose: bool = False, variant: str = "") -> str:
     aobj = os.path.join(bdir, "ce_api.o")
     lobj = os.path.join(bdir, "ce_linear.o")
     gobj = os.path.join(bdir, "ce_gemm.o")
+    robj = os.path.join(bdir, "ce_stream_ref.o")
     steps = [
         [HIPCC, *DEVICE, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_kernels.hip"), "-o", kobj],
         [HIPCC, *DEVICE, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_gemm.hip"), "-o", gobj],
+        [HIPCC, *DEVICE, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_stream_ref.hip"), "-o", robj],
         [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_api.cpp"), "-o", aobj],
         [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, "ce_linear.cpp"), "-o", lobj],
     ]
@@ -73,7 +75,7 @@ def build(verbose: bool = False, variant: str = "") -> str:
     tmp = lib + ".tmp"
     # the chunked linear call's products run on the library's MFMA kernel (ce_gemm.hip) or on hipBLASLt
     # (ROCm's matrix-core GEMM library), per ce_linear.gemm
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, gobj, aobj, lobj, "-L/opt/rocm/lib",
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, gobj, robj, aobj, lobj, "-L/opt/rocm/lib",
           "-lhipblaslt", "-o", tmp])
     os.replace(tmp, lib)
     return lib

@@ -631,6 +631,22 @@ ce_status ce_scale_grad_inplace(const ce_logits* x, const float* grad_out, int32
   return CE_OK;
 }
 
+ce_status ce_stream_reference(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  if (bytes < 0 || bytes % 16 != 0) return fail(CE_EINVAL, "bytes must be a non-negative multiple of 16");
+  if (bytes == 0) return CE_OK;
+  if (!src || !dst) return fail(CE_EINVAL, "src or dst is NULL");
+  if (((uintptr_t)src & 15u) || ((uintptr_t)dst & 15u)) return fail(CE_EINVAL, "src and dst must be 16-byte aligned");
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 != d0 && s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes)
+    return fail(CE_EINVAL, "src and dst overlap without being the same buffer");
+  hipEvent_t e0, e1;
+  prof_next(&e0, &e1);
+  hipError_t e;
+  if ((e = vce::launch_stream_ref(src, dst, bytes, s0 == d0 ? 0x80008000u : 0u, stream, e0, e1)))
+    return hip_fail(e, "reference stream launch");
+  return CE_OK;
+}
+
 ce_status ce_shard_partial_stats(const ce_logits* shard, const ce_targets* t, const ce_params* p, float* stats,
                                  hipStream_t stream) {
   ce_status st;

@@ -171,6 +171,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_mean(const float* row_loss, int64_t N, const int32_t* n_valid, float* out, hipStream_t stream);
 hipError_t launch_ws_init(void* ws, size_t bytes, hipStream_t stream);
 hipError_t launch_scale(const ScaleArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_stream_ref(const void* src, void* dst, int64_t bytes, uint32_t flip, hipStream_t stream,
+                             hipEvent_t ev0, hipEvent_t ev1);
 // chunked linear + cross-entropy: n over all N rows (row r's target at tgt[r * ts]) into n_out, and
 // with the mean scale[0] = g / n; then loss[0] = sum of parts (index order, FP64), / n for the mean
 hipError_t launch_linear_prep(const int64_t* tgt, int64_t ts, int64_t N, int64_t ignore_idx, int32_t reduce,
